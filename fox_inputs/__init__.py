@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for Forgetting Attention, shared by the tests, the bench and smoke().
+
+This module is the only code that both the oracle side and the HIP side consume. It holds no
+step of the attention path: it draws random numbers, rounds them to the storage type, and hands
+back plain NumPy arrays. Both sides then receive identical bits.
+
+Input recipes follow the workloads of the Forgetting Transformer pages (arXiv 2503.02130):
+16,384-token context, head dim 64/128, 12 heads, d_model 1536, and forget-gate logits whose
+per-head mean sets a memory horizon. The log forget gate handed to the path is drawn as
+log f = log sigmoid(z) of a normally distributed logit z; that is the distribution of the input,
+evaluated once here in fp64 and rounded to fp32, and both sides read the same fp32 values.
+The gate step itself (x -> log f, Pro block Step 4) is not done here: that workload hands x,
+w_f and b_f to each side, which compute log f independently.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+__all__ = [
+    "bf16_bits", "bf16_round", "bits_to_f32", "FoxCase", "make_case", "CONFIGS",
+    "config_case", "logsigmoid_input",
+]
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (round to nearest, ties to even); return the uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    rounding_bias = ((u >> 16) & 1) + 0x7FFF
+    r = ((u + rounding_bias) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bits (uint16) to the fp32 values they encode (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 array holding the bfloat16-rounded values of x (exactly representable in bf16)."""
+    return bits_to_f32(bf16_bits(x))
+
+
+def logsigmoid_input(z: np.ndarray) -> np.ndarray:
+    """fp32 log-forget-gate input values drawn as log sigmoid(z): fp64 evaluation, one rounding."""
+    z = np.asarray(z, dtype=np.float64)
+    return (-np.logaddexp(0.0, -z)).astype(np.float32)
+
+
+@dataclasses.dataclass
+class FoxCase:
+    """One synthetic batch. Float arrays hold the exact values both sides see.
+
+    q, k, v, do: fp32 arrays [B,H,L,D]; when dtype == "bf16" every value is bf16-representable
+    and *_bits holds the uint16 encoding to upload. log_f: fp32 [B,H,L] (None for the Pro
+    workload, which supplies x / w_f / b_f instead). x: [B,L,d_model] bf16 values; w_f: fp32
+    [H,d_model]; b_f: fp32 [H].
+    """
+    name: str
+    B: int
+    H: int
+    L: int
+    D: int
+    dtype: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    log_f: np.ndarray | None = None
+    do: np.ndarray | None = None
+    x: np.ndarray | None = None
+    w_f: np.ndarray | None = None
+    b_f: np.ndarray | None = None
+    qk_norm: bool = False
+    seed: int = 0
+
+    def bits(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return bf16_bits(a)
+
+
+def _qkv(rng: np.random.Generator, shape, dtype: str):
+    out = []
+    for _ in range(3):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        out.append(bf16_round(a) if dtype == "bf16" else a)
+    return out
+
+
+def make_case(B: int, H: int, L: int, D: int, dtype: str = "bf16", *, seed: int = 0,
+              gate: str = "normal", gate_mean: float = 3.0, gate_std: float = 1.5,
+              head_mean_range: tuple[float, float] = (1.0, 6.0), with_do: bool = False,
+              name: str = "custom") -> FoxCase:
+    """Generic recipe: q, k, v ~ N(0,1); log f = log sigmoid(z).
+
+    gate = "normal": z ~ N(gate_mean, gate_std^2) per (b, h, t).
+    gate = "per_head": mu_h ~ U[head_mean_range] per head, z ~ N(mu_h, 1) per (b, h, t).
+    gate = "zero": log f = 0 (f = 1, plain causal attention).
+    """
+    assert dtype in ("bf16", "f32")
+    rng = np.random.default_rng(seed)
+    q, k, v = _qkv(rng, (B, H, L, D), dtype)
+    if gate == "normal":
+        z = rng.normal(gate_mean, gate_std, size=(B, H, L))
+        log_f = logsigmoid_input(z)
+    elif gate == "per_head":
+        mu = rng.uniform(head_mean_range[0], head_mean_range[1], size=(H,))
+        z = mu[None, :, None] + rng.standard_normal((B, H, L))
+        log_f = logsigmoid_input(z)
+    elif gate == "zero":
+        log_f = np.zeros((B, H, L), np.float32)
+    else:
+        raise ValueError(gate)
+    do = None
+    if with_do:
+        r2 = np.random.default_rng(seed + 1000)
+        do = r2.standard_normal((B, H, L, D), dtype=np.float32)
+        do = bf16_round(do) if dtype == "bf16" else do
+    return FoxCase(name, B, H, L, D, dtype, q, k, v, log_f=log_f, do=do, seed=seed)
+
+
+def make_pro_case(B: int, H: int, L: int, D: int, d_model: int, *, seed: int = 4,
+                  name: str = "pro") -> FoxCase:
+    """Pro-block workload: x ~ N(0,1) bf16 [B,L,d_model]; q, k, v ~ N(0,1) bf16;
+    w_f ~ N(0, 0.02^2) fp32 [H,d_model]; b_f ~ U[1,6] fp32 [H]; QK-norm with unit weights."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _qkv(rng, (B, H, L, D), "bf16")
+    x = bf16_round(rng.standard_normal((B, L, d_model), dtype=np.float32))
+    w_f = (0.02 * rng.standard_normal((H, d_model))).astype(np.float32)
+    b_f = rng.uniform(1.0, 6.0, size=(H,)).astype(np.float32)
+    return FoxCase(name, B, H, L, D, "bf16", q, k, v, x=x, w_f=w_f, b_f=b_f, qk_norm=True,
+                   seed=seed)
+
+
+# The five workloads. Sizes and distributions follow the pages' setting (16K context,
+# d_head 128, 12 heads, d_model 1536); config 1 is the small fp32 case.
+CONFIGS = {
+    1: dict(kind="fwd", B=1, H=2, L=256, D=64, dtype="f32", seed=1, gate="normal"),
+    2: dict(kind="fwd", B=4, H=12, L=2048, D=128, dtype="bf16", seed=2, gate="normal"),
+    3: dict(kind="fwd", B=1, H=12, L=16384, D=128, dtype="bf16", seed=3, gate="per_head"),
+    4: dict(kind="pro", B=1, H=12, L=16384, D=128, d_model=1536, dtype="bf16", seed=4),
+    5: dict(kind="bwd", B=1, H=12, L=16384, D=128, dtype="bf16", seed=3, gate="per_head"),
+}
+
+
+def config_case(n: int, L: int | None = None, B: int | None = None, H: int | None = None) -> FoxCase:
+    """Inputs of workload n; L/B/H may be overridden to shrink a case with the same recipe."""
+    c = dict(CONFIGS[n])
+    kind = c.pop("kind")
+    if L is not None:
+        c["L"] = L
+    if B is not None:
+        c["B"] = B
+    if H is not None:
+        c["H"] = H
+    if kind == "pro":
+        return make_pro_case(c["B"], c["H"], c["L"], c["D"], c["d_model"], seed=c["seed"],
+                             name=f"config{n}")
+    return make_case(c["B"], c["H"], c["L"], c["D"], c["dtype"], seed=c["seed"], gate=c["gate"],
+                     with_do=(kind == "bwd"), name=f"config{n}")

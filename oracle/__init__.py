@@ -1,0 +1,10 @@
+"""fp64 CPU oracle of Forgetting Attention — test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this package.
+It shares no code with the HIP library and imports nothing from it.
+"""
+from .fox_oracle import (  # noqa: F401
+    log_sigmoid, gate_logf, rms_norm, fixed_gate_logf, cumsum_logf, reverse_cumsum,
+    decay_bias_bruteforce, attn_probs_bruteforce, attn_fwd_bruteforce, attn_bwd_bruteforce,
+    attn_fwd, attn_fwd_rows, attn_bwd,
+)

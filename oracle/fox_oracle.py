@@ -1,0 +1,282 @@
+"""CPU fp64 oracle of Forgetting Attention.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of
+bench.py may import or call anything in this package; the library path never does.
+
+Each function writes out the plain definition of one step of the method, in float64, with no
+tiling, fusion or reordering beyond what the definition states. Sources (cited by page and
+section; the pages summarise arXiv 2503.02130, "Forgetting Transformer: Softmax Attention with
+a Forget Gate"):
+
+  [FoX-pg]  paper-graph-ui.vercel.app summary, section 3.4 "Detailed, Sentence-Based Technical
+            Breakdown" with its parts "The Mathematical Form of Forgetting Attention",
+            "Forget Gate Computation", "Hardware-Aware Implementation (Modified FlashAttention)",
+            "Connection to ALiBi" and "The Pro Block Architecture".
+  [FoX-pl]  paperlayer.ai summary (abs/2503.02130v2), sections "3 FORGETTING TRANSFORMER",
+            "D DATA-INDEPENDENT FORGET GATE INITIALIZATION" and "E HARDWARE-AWARE
+            IMPLEMENTATION OF FORGETTING ATTENTION".
+
+Two independent tiers compute attention:
+  T1 (``*_bruteforce``): explicit range sums D_ij = sum_{l=j+1..i} log f_l and per-row loops;
+      supports log f = -inf (f = 0). For tiny L only.
+  T2 (``attn_fwd`` / ``attn_bwd`` / ``attn_fwd_rows``): D_ij = c_i - c_j with c = cumsum(log f),
+      vectorised over blocks of query rows (the blocking only groups rows; every row still sees
+      all of its keys at once).
+
+Conventions (readings of the pages, each listed in the design doc): positions are 0-indexed and
+c is the inclusive prefix sum; the softmax scale multiplies q.k only, never the bias; the
+causal mask keeps j <= i (D_ii = 0); LSE is the natural-log log-sum-exp of the biased, scaled
+logits.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a):
+    return np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------------------------
+# Forget gate  ([FoX-pg] "Forget Gate Computation"; Pro block Step 4)
+# ----------------------------------------------------------------------------------------------
+def log_sigmoid(z):
+    """log sigma(z) in fp64, evaluated stably: -log1p(exp(-z)) for z >= 0, z - log1p(exp(z)) else.
+
+    The gate is f = sigma(w_f . x + b_f) in (0,1); the path only ever needs log f.
+    """
+    z = _f64(z)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = -np.log1p(np.exp(-z[pos]))
+    out[~pos] = z[~pos] - np.log1p(np.exp(z[~pos]))
+    return out
+
+
+def gate_logf(x, w_f, b_f):
+    """Per-head scalar forget gate in log space.
+
+    x: [B, L, d_model] layer input; w_f: [H, d_model]; b_f: [H]  ->  log f: [B, H, L].
+    z[b,h,t] = sum_d x[b,t,d] w_f[h,d] + b_f[h]; log f = log sigma(z).
+    One (w_f, b_f) pair per head ([FoX-pg] "Forget Gate Computation", multi-head treatment).
+    """
+    x, w_f, b_f = _f64(x), _f64(w_f), _f64(b_f)
+    z = np.matmul(x, w_f.T)                        # [B, L, H]
+    z = np.transpose(z, (0, 2, 1)) + b_f[None, :, None]
+    return log_sigmoid(z)
+
+
+def rms_norm(x, eps, weight=None):
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) [* weight].
+
+    Used for QK-norm in the Pro block (Step 1 for queries, Step 2 for keys); unit weights
+    when ``weight`` is None.
+    """
+    x = _f64(x)
+    y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    if weight is not None:
+        y = y * _f64(weight)
+    return y
+
+
+def fixed_gate_logf(t_min, t_max, H):
+    """Data-independent gate initialisation ([FoX-pl] D; [FoX-pg] "Connection to ALiBi").
+
+    The decay horizons T_h are geometrically spaced from t_min to t_max; the bias is
+    b_h = logit(exp(-1/T_h)), so sigma(b_h)^T_h = 1/e. Returns (T_h, b_h, log f_h = log sigma(b_h)).
+    Used only to build structured test inputs (a fixed gate is ALiBi with slope 1/T_h).
+    """
+    if H == 1:
+        T = np.array([float(t_min)])
+    else:
+        T = float(t_min) * (float(t_max) / float(t_min)) ** (np.arange(H, dtype=F64) / (H - 1))
+    f = np.exp(-1.0 / T)
+    b = np.log(f) - np.log1p(-f)
+    return T, b, log_sigmoid(b)
+
+
+# ----------------------------------------------------------------------------------------------
+# Cumulative log decay  ([FoX-pg] "Hardware-Aware Implementation": c = cumsum(log f))
+# ----------------------------------------------------------------------------------------------
+def cumsum_logf(log_f):
+    """c_i = sum_{l <= i} log f_l (inclusive, 0-indexed), fp64, along the last axis."""
+    return np.cumsum(_f64(log_f), axis=-1)
+
+
+def reverse_cumsum(dc):
+    """d log f_l = sum_{t >= l} dc_t: the adjoint of the inclusive prefix sum."""
+    dc = _f64(dc)
+    return np.flip(np.cumsum(np.flip(dc, axis=-1), axis=-1), axis=-1)
+
+
+# ----------------------------------------------------------------------------------------------
+# T1: brute force from the definition  ([FoX-pg] "The Mathematical Form of Forgetting Attention")
+# ----------------------------------------------------------------------------------------------
+def decay_bias_bruteforce(log_f_row):
+    """D[i, j] = sum_{l=j+1..i} log f_l for j <= i (so D_ii = 0), -inf for j > i.
+
+    Explicit range sums; log f may hold -inf (f = 0, log 0 = -inf cuts off every key before it).
+    """
+    lf = _f64(log_f_row)
+    L = lf.shape[0]
+    D = np.full((L, L), -np.inf)
+    for i in range(L):
+        for j in range(i + 1):
+            D[i, j] = lf[j + 1:i + 1].sum() if i > j else 0.0
+    return D
+
+
+def attn_probs_bruteforce(q, k, log_f, scale):
+    """P[i, :] = softmax_j(scale * q_i . k_j + D_ij) for one (b, h): [L, L], zeros above the diagonal."""
+    q, k = _f64(q), _f64(k)
+    L = q.shape[0]
+    D = decay_bias_bruteforce(log_f)
+    P = np.zeros((L, L))
+    for i in range(L):
+        s = scale * (k[:i + 1] @ q[i]) + D[i, :i + 1]
+        m = np.max(s)
+        p = np.exp(s - m)
+        P[i, :i + 1] = p / p.sum()
+    return P
+
+
+def attn_fwd_bruteforce(q, k, v, log_f, scale):
+    """T1 forward. q, k, v: [B, H, L, D]; log_f: [B, H, L]  ->  (O [B,H,L,D], LSE [B,H,L]).
+
+    Per row: s_j = scale q_i.k_j + D_ij (j <= i); m = max s; p = exp(s - m); l = sum p;
+    O_i = sum_j p_j v_j / l; LSE_i = m + log l.
+    """
+    q, k, v, log_f = _f64(q), _f64(k), _f64(v), _f64(log_f)
+    B, H, L, Dh = q.shape
+    O = np.zeros((B, H, L, Dh))
+    LSE = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            D = decay_bias_bruteforce(log_f[b, h])
+            for i in range(L):
+                s = scale * (k[b, h, :i + 1] @ q[b, h, i]) + D[i, :i + 1]
+                m = np.max(s)
+                p = np.exp(s - m)
+                ell = p.sum()
+                O[b, h, i] = (p @ v[b, h, :i + 1]) / ell
+                LSE[b, h, i] = m + np.log(ell)
+    return O, LSE
+
+
+def attn_bwd_bruteforce(q, k, v, log_f, do, scale):
+    """T1 backward for the loss sum(dO * O): returns (dQ, dK, dV, dlog_f).
+
+    P from attn_probs_bruteforce; dV = P^T dO; dP = dO V^T; dS = P * (dP - rowsum(dP * P));
+    dQ = scale dS K; dK = scale dS^T Q. The log-gate gradient is taken straight from the
+    definition: log f_l enters D_ij exactly when j < l <= i, so d log f_l = sum_{i >= l} sum_{j < l} dS_ij.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, L, Dh = q.shape
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    dlf = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            P = attn_probs_bruteforce(q[b, h], k[b, h], log_f[b, h], scale)
+            dV[b, h] = P.T @ do[b, h]
+            dP = do[b, h] @ v[b, h].T
+            dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+            dQ[b, h] = scale * (dS @ k[b, h])
+            dK[b, h] = scale * (dS.T @ q[b, h])
+            for l in range(L):
+                dlf[b, h, l] = dS[l:, :l].sum()
+    return dQ, dK, dV, dlf
+
+
+# ----------------------------------------------------------------------------------------------
+# T2: the c_i - c_j form  ([FoX-pg] "Hardware-Aware Implementation"; [FoX-pl] E)
+# ----------------------------------------------------------------------------------------------
+def _rows_logits(q_rows, k_keys, c_rows, c_keys, rows, scale):
+    """s[r, j] = scale q_r . k_j + c_r - c_j for the given query rows; -inf where j > row."""
+    s = scale * (q_rows @ k_keys.T) + (c_rows[:, None] - c_keys[None, :])
+    j = np.arange(k_keys.shape[0])
+    s[j[None, :] > rows[:, None]] = -np.inf
+    return s
+
+
+def attn_fwd(q, k, v, log_f=None, *, c=None, scale, block=512):
+    """T2 forward. Either log_f or c ([B, H, L]) gives the decay. Returns (O, LSE) in fp64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    c = cumsum_logf(log_f) if c is None else _f64(c)
+    B, H, L, Dh = q.shape
+    O = np.zeros((B, H, L, Dh))
+    LSE = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            for i0 in range(0, L, block):
+                i1 = min(L, i0 + block)
+                rows = np.arange(i0, i1)
+                s = _rows_logits(q[b, h, i0:i1], k[b, h, :i1], c[b, h, i0:i1], c[b, h, :i1], rows,
+                                 scale)
+                m = s.max(axis=1)
+                p = np.exp(s - m[:, None])
+                ell = p.sum(axis=1)
+                O[b, h, i0:i1] = (p @ v[b, h, :i1]) / ell[:, None]
+                LSE[b, h, i0:i1] = m + np.log(ell)
+    return O, LSE
+
+
+def attn_fwd_rows(q, k, v, c, rows, *, scale):
+    """O and LSE of selected rows of one (b, h): q, k, v [L, D], c [L] -> (O [n, D], LSE [n]).
+
+    Each listed row i sees keys 0..i only; the cost is O(i * D) per row, so full-length
+    sequences can be checked on a sample of rows.
+    """
+    q, k, v, c = _f64(q), _f64(k), _f64(v), _f64(c)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.zeros((rows.size, q.shape[1]))
+    LSE = np.zeros(rows.size)
+    for n, i in enumerate(rows):
+        s = scale * (k[:i + 1] @ q[i]) + (c[i] - c[:i + 1])
+        m = s.max()
+        p = np.exp(s - m)
+        ell = p.sum()
+        O[n] = (p @ v[:i + 1]) / ell
+        LSE[n] = m + np.log(ell)
+    return O, LSE
+
+
+def attn_bwd(q, k, v, log_f=None, do=None, *, c=None, scale, O=None, LSE=None, block=512):
+    """T2 backward for the loss sum(dO * O). Returns (dQ, dK, dV, dlog_f, dc_q, dc_k).
+
+    Recompute P_ij = exp(s_ij - LSE_i) with the same bias; Delta_i = dO_i . O_i;
+    dV_j = sum_i P_ij dO_i; dP_ij = dO_i . v_j; dS_ij = P_ij (dP_ij - Delta_i);
+    dQ_i = scale sum_j dS_ij k_j; dK_j = scale sum_i dS_ij q_i;
+    dc^q_i = sum_j dS_ij; dc^k_j = -sum_i dS_ij; dc = dc^q + dc^k; d log f = reverse cumsum(dc).
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    c = cumsum_logf(log_f) if c is None else _f64(c)
+    if O is None or LSE is None:
+        O, LSE = attn_fwd(q, k, v, c=c, scale=scale, block=block)
+    B, H, L, Dh = q.shape
+    dQ = np.zeros_like(q)
+    dK = np.zeros_like(k)
+    dV = np.zeros_like(v)
+    dcq = np.zeros((B, H, L))
+    dck = np.zeros((B, H, L))
+    Delta = np.sum(do * O, axis=-1)
+    for b in range(B):
+        for h in range(H):
+            for i0 in range(0, L, block):
+                i1 = min(L, i0 + block)
+                rows = np.arange(i0, i1)
+                s = _rows_logits(q[b, h, i0:i1], k[b, h, :i1], c[b, h, i0:i1], c[b, h, :i1], rows,
+                                 scale)
+                P = np.exp(s - LSE[b, h, i0:i1, None])
+                dV[b, h, :i1] += P.T @ do[b, h, i0:i1]
+                dP = do[b, h, i0:i1] @ v[b, h, :i1].T
+                dS = P * (dP - Delta[b, h, i0:i1, None])
+                dQ[b, h, i0:i1] = scale * (dS @ k[b, h, :i1])
+                dK[b, h, :i1] += scale * (dS.T @ q[b, h, i0:i1])
+                dcq[b, h, i0:i1] = dS.sum(axis=1)
+                dck[b, h, :i1] -= dS.sum(axis=0)
+    dlf = reverse_cumsum(dcq + dck)
+    return dQ, dK, dV, dlf, dcq, dck

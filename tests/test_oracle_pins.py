@@ -1,0 +1,320 @@
+"""Pins of the fp64 oracle against facts fixed outside it (CPU only).
+
+Every check compares the oracle with something it does not compute itself: a library routine
+(torch's causal scaled-dot-product attention, torch autograd, scipy's log_expit), a closed form
+the pages state (ALiBi as a constant gate, the hard reset of log 0 = -inf, the printed gate
+initialisation), an invariant of softmax attention, or central finite differences. The last
+block plants mistakes into a copy of the oracle's source and checks that some pin catches each.
+"""
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import fox_inputs as fi
+import oracle
+from oracle import fox_oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def _case(B=2, H=2, L=64, D=32, seed=50, gate="normal"):
+    return fi.make_case(B, H, L, D, "f32", seed=seed, gate=gate, with_do=True)
+
+
+def _t(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+def _sdpa_causal(q, k, v, scale, bias=None):
+    """torch's scaled_dot_product_attention (fp64, CPU) with causal masking and optional float bias."""
+    L = q.shape[-2]
+    mask = torch.full((L, L), -math.inf, dtype=torch.float64).triu(1)
+    if bias is not None:
+        mask = mask + _t(bias)
+    return F.scaled_dot_product_attention(_t(q), _t(k), _t(v), attn_mask=mask, scale=scale).numpy()
+
+
+def _lse_ref(q, k, scale, bias):
+    L = q.shape[-2]
+    s = torch.matmul(_t(q), _t(k).transpose(-1, -2).contiguous()) * scale + _t(bias)
+    s = s + torch.full((L, L), -math.inf, dtype=torch.float64).triu(1)
+    return torch.logsumexp(s, dim=-1).numpy()
+
+
+# ---------------------------------------------------------------- two independent tiers agree
+def test_t1_equals_t2_forward():
+    c = _case()
+    s = 1 / math.sqrt(c.D)
+    O1, L1 = oracle.attn_fwd_bruteforce(c.q, c.k, c.v, c.log_f, s)
+    O2, L2 = oracle.attn_fwd(c.q, c.k, c.v, c.log_f, scale=s, block=16)
+    assert np.abs(O1 - O2).max() < 1e-12 and np.abs(L1 - L2).max() < 1e-12
+
+
+def test_t1_equals_t2_backward():
+    c = _case()
+    s = 1 / math.sqrt(c.D)
+    g1 = oracle.attn_bwd_bruteforce(c.q, c.k, c.v, c.log_f, c.do, s)
+    g2 = oracle.attn_bwd(c.q, c.k, c.v, c.log_f, c.do, scale=s, block=16)
+    for a, b in zip(g1, g2[:4]):
+        assert np.abs(a - b).max() < 1e-11 * max(1.0, np.abs(a).max())
+
+
+def test_range_sum_is_difference_of_prefix_sums():
+    lf = fi.make_case(1, 1, 40, 4, "f32", seed=3).log_f[0, 0]
+    D = oracle.decay_bias_bruteforce(lf)
+    c = oracle.cumsum_logf(lf)
+    ii, jj = np.tril_indices(40)
+    assert np.abs(D[ii, jj] - (c[ii] - c[jj])).max() < 1e-12
+    assert np.all(np.isneginf(D[np.triu_indices(40, 1)]))
+    assert np.all(np.diag(D) == 0.0)
+
+
+def test_rows_match_full_forward():
+    c = _case(B=1, H=1, L=300, D=16, seed=7)
+    s = 0.25
+    O, LSE = oracle.attn_fwd(c.q, c.k, c.v, c.log_f, scale=s, block=64)
+    cc = oracle.cumsum_logf(c.log_f)
+    rows = np.array([0, 1, 63, 64, 200, 299])
+    Or, Lr = oracle.attn_fwd_rows(c.q[0, 0], c.k[0, 0], c.v[0, 0], cc[0, 0], rows, scale=s)
+    assert np.abs(Or - O[0, 0, rows]).max() < 1e-12 and np.abs(Lr - LSE[0, 0, rows]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- closed forms and library routines
+def test_all_gates_open_is_causal_softmax_attention():
+    c = _case(gate="zero")
+    s = 1 / math.sqrt(c.D)
+    O, LSE = oracle.attn_fwd(c.q, c.k, c.v, c.log_f, scale=s, block=16)
+    ref = _sdpa_causal(c.q, c.k, c.v, s)
+    assert np.abs(O - ref).max() < 1e-12
+    assert np.abs(LSE - _lse_ref(c.q, c.k, s, np.zeros((c.L, c.L)))).max() < 1e-12
+
+
+@pytest.mark.parametrize("tier", ["T1", "T2"])
+def test_constant_gate_is_alibi(tier):
+    """log f = -m_h at every position gives the bias -m_h (i - j) exactly."""
+    B, H, L, D = 1, 4, 48, 16
+    c = fi.make_case(B, H, L, D, "f32", seed=11)
+    m = 2.0 ** (-8.0 * np.arange(1, H + 1) / H)
+    log_f = np.broadcast_to(-m[None, :, None], (B, H, L)).astype(np.float64)
+    s = 1 / math.sqrt(D)
+    if tier == "T1":
+        O, LSE = oracle.attn_fwd_bruteforce(c.q, c.k, c.v, log_f, s)
+    else:
+        O, LSE = oracle.attn_fwd(c.q, c.k, c.v, log_f, scale=s, block=16)
+    i = np.arange(L)
+    for h in range(H):
+        bias = -m[h] * (i[:, None] - i[None, :])
+        bias = np.where(i[None, :] <= i[:, None], bias, 0.0)
+        ref = _sdpa_causal(c.q[:, h:h + 1], c.k[:, h:h + 1], c.v[:, h:h + 1], s, bias)
+        assert np.abs(O[:, h:h + 1] - ref).max() < 1e-12
+        assert np.abs(LSE[0, h] - _lse_ref(c.q[0, h], c.k[0, h], s, bias)).max() < 1e-11
+
+
+def test_fixed_gate_init_matches_printed_values():
+    g = json.load(open(os.path.join(GOLDEN, "fixed_gate_init.json")))
+    T, b, log_f = oracle.fixed_gate_logf(g["t_min"], g["t_max"], g["H"])
+    assert np.allclose(T, g["horizons"], rtol=1e-12)
+    f = np.exp(log_f)
+    # the pages give three decimals without saying whether they round or truncate: allow one unit
+    tol = 10.0 ** -g["printed_decimals"]
+    assert abs(f[0] - g["f_at_t_min_approx"]) <= tol
+    assert abs(f[-1] - g["f_at_t_max_approx"]) <= tol
+    assert np.allclose(f ** T, math.exp(-1.0), rtol=1e-12)
+    # a fixed gate is ALiBi with slope 1/T_h
+    assert np.allclose(-log_f, 1.0 / T, rtol=1e-12)
+
+
+@pytest.mark.parametrize("cut", [1, 17, 40])
+def test_hard_reset_cuts_off_the_past(cut):
+    """log f_l = -inf (f = 0): rows i >= l attend only to keys l..i (T1); -1e4 does the same in T2."""
+    B, H, L, D = 1, 1, 48, 8
+    c = fi.make_case(B, H, L, D, "f32", seed=5)
+    s = 1 / math.sqrt(D)
+    for val, tier in ((-np.inf, "T1"), (-1e4, "T2")):
+        lf = c.log_f.astype(np.float64).copy()
+        lf[..., cut] = val
+        if tier == "T1":
+            O, LSE = oracle.attn_fwd_bruteforce(c.q, c.k, c.v, lf, s)
+        else:
+            O, LSE = oracle.attn_fwd(c.q, c.k, c.v, lf, scale=s, block=16)
+        lf_tail = lf[..., cut:].copy()
+        lf_tail[..., 0] = 0.0
+        O_tail, LSE_tail = oracle.attn_fwd_bruteforce(c.q[..., cut:, :], c.k[..., cut:, :],
+                                                      c.v[..., cut:, :], lf_tail, s)
+        assert np.abs(O[..., cut:, :] - O_tail).max() < 1e-12
+        assert np.abs(LSE[..., cut:] - LSE_tail).max() < 1e-12
+
+
+def test_first_row_sees_only_itself():
+    c = _case()
+    s = 0.3
+    O, LSE = oracle.attn_fwd(c.q, c.k, c.v, c.log_f, scale=s)
+    assert np.abs(O[..., 0, :] - c.v[..., 0, :]).max() < 1e-15
+    assert np.abs(LSE[..., 0] - s * np.sum(c.q[..., 0, :].astype(np.float64) * c.k[..., 0, :], -1)).max() < 1e-12
+
+
+def test_rows_are_distributions():
+    c = _case(B=1, H=1, L=40)
+    P = oracle.attn_probs_bruteforce(c.q[0, 0], c.k[0, 0], c.log_f[0, 0], 0.2)
+    assert np.abs(P.sum(1) - 1).max() < 1e-14
+    assert np.all(P >= 0) and np.all(np.triu(P, 1) == 0)
+
+
+def test_shift_and_first_gate_invariance():
+    c = _case()
+    s = 1 / math.sqrt(c.D)
+    cc = oracle.cumsum_logf(c.log_f)
+    O, LSE = oracle.attn_fwd(c.q, c.k, c.v, c=cc, scale=s)
+    O2, LSE2 = oracle.attn_fwd(c.q, c.k, c.v, c=cc + 123.25, scale=s)
+    assert np.abs(O - O2).max() < 1e-12 and np.abs(LSE - LSE2).max() < 1e-10
+    lf = c.log_f.astype(np.float64).copy()
+    lf[..., 0] -= 7.0
+    O3, LSE3 = oracle.attn_fwd(c.q, c.k, c.v, lf, scale=s)
+    assert np.abs(O - O3).max() < 1e-12 and np.abs(LSE - LSE3).max() < 1e-10
+
+
+def test_log_sigmoid_against_scipy():
+    z = np.concatenate([np.linspace(-60, 60, 2001), [-800.0, -40.0, 0.0, 40.0, 800.0]])
+    ref = scipy.special.log_expit(z)
+    got = oracle.log_sigmoid(z)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - ref).max() <= 1e-15 * np.maximum(1.0, np.abs(ref)).max()
+    assert oracle.log_sigmoid(np.array([0.0]))[0] == -math.log(2.0)
+
+
+def test_gate_against_torch():
+    c = fi.make_pro_case(2, 3, 40, 8, 96, seed=9)
+    got = oracle.gate_logf(c.x, c.w_f, c.b_f)
+    z = torch.einsum("bld,hd->bhl", _t(c.x), _t(c.w_f)) + _t(c.b_f)[None, :, None]
+    assert np.abs(got - F.logsigmoid(z).numpy()).max() < 1e-13
+
+
+def test_rms_norm_against_torch():
+    x = np.random.default_rng(0).standard_normal((5, 7, 128))
+    got = oracle.rms_norm(x, 1e-6)
+    ref = F.rms_norm(_t(x), (128,), eps=1e-6).numpy()
+    assert np.abs(got - ref).max() < 1e-13
+
+
+def test_reverse_cumsum_is_adjoint_of_cumsum():
+    rng = np.random.default_rng(1)
+    a, b = rng.standard_normal(57), rng.standard_normal(57)
+    assert abs(np.dot(oracle.cumsum_logf(a), b) - np.dot(a, oracle.reverse_cumsum(b))) < 1e-12
+
+
+# ---------------------------------------------------------------- gradients
+def _torch_grads(c, scale):
+    """Gradients of sum(dO * O) through torch autograd, bias built as c_i - c_j in torch."""
+    q, k, v = (_t(a).requires_grad_(True) for a in (c.q, c.k, c.v))
+    lf = _t(c.log_f).requires_grad_(True)
+    cc = torch.cumsum(lf, dim=-1)
+    bias = cc[..., :, None] - cc[..., None, :]
+    L = c.L
+    bias = bias + torch.full((L, L), -math.inf, dtype=torch.float64).triu(1)
+    O = F.scaled_dot_product_attention(q, k, v, attn_mask=bias, scale=scale)
+    (O * _t(c.do)).sum().backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy(), lf.grad.numpy()
+
+
+def test_gradients_against_torch_autograd():
+    c = _case()
+    s = 1 / math.sqrt(c.D)
+    ref = _torch_grads(c, s)
+    got = oracle.attn_bwd(c.q, c.k, c.v, c.log_f, c.do, scale=s, block=16)
+    for g, r in zip(got[:4], ref):
+        assert np.abs(g - r).max() < 1e-11 * max(1.0, np.abs(r).max())
+
+
+def test_gradients_against_finite_differences():
+    """Central differences along random directions, loss = sum(dO * O), fp64."""
+    c = _case()
+    s = 1 / math.sqrt(c.D)
+    grads = oracle.attn_bwd(c.q, c.k, c.v, c.log_f, c.do, scale=s, block=32)[:4]
+    base = [c.q.astype(np.float64), c.k.astype(np.float64), c.v.astype(np.float64),
+            c.log_f.astype(np.float64)]
+    rng = np.random.default_rng(123)
+
+    def loss(args):
+        O, _ = oracle.attn_fwd(args[0], args[1], args[2], args[3], scale=s, block=32)
+        return float(np.sum(O * c.do))
+
+    h = 1e-5
+    for which in range(4):
+        for _ in range(3):
+            u = rng.standard_normal(base[which].shape)
+            plus = list(base)
+            minus = list(base)
+            plus[which] = base[which] + h * u
+            minus[which] = base[which] - h * u
+            fd = (loss(plus) - loss(minus)) / (2 * h)
+            an = float(np.sum(grads[which] * u))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
+
+
+def test_gradient_invariants():
+    c = _case()
+    s = 1 / math.sqrt(c.D)
+    dQ, dK, dV, dlf, dcq, dck = oracle.attn_bwd(c.q, c.k, c.v, c.log_f, c.do, scale=s)
+    # adding a constant vector to every key shifts each row's logits by a constant
+    assert np.abs(dK.sum(axis=2)).max() < 1e-12
+    # rows of P sum to one, so the total value gradient is the total output gradient
+    assert np.abs(dV.sum(axis=2) - c.do.astype(np.float64).sum(axis=2)).max() < 1e-12
+    # each row of dS sums to zero, and log f_0 never reaches an output
+    assert np.abs(dcq).max() < 1e-12
+    assert np.abs(dlf[..., 0]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- planted mistakes are caught
+MUTATIONS = {
+    "bias_sign": ("(c_rows[:, None] - c_keys[None, :])", "(c_keys[None, :] - c_rows[:, None])"),
+    "scaled_bias": ("s = scale * (q_rows @ k_keys.T) + (c_rows[:, None] - c_keys[None, :])",
+                    "s = scale * (q_rows @ k_keys.T + (c_rows[:, None] - c_keys[None, :]))"),
+    "mask_diagonal": ("s[j[None, :] > rows[:, None]] = -np.inf",
+                      "s[j[None, :] >= rows[:, None]] = -1e30"),
+    # (dropping dc^q is not a mistake in exact arithmetic: every row of dS sums to zero)
+    "dck_sign": ("dlf = reverse_cumsum(dcq + dck)", "dlf = reverse_cumsum(dcq - dck)"),
+    "exclusive_reverse_scan": ("dlf = reverse_cumsum(dcq + dck)",
+                               "dlf = reverse_cumsum(dcq + dck) - (dcq + dck)"),
+    "dk_transpose": ("dK[b, h, :i1] += scale * (dS.T @ q[b, h, i0:i1])",
+                     "dK[b, h, :i1] += scale * (P.T @ q[b, h, i0:i1])"),
+    "forward_scan": ("return np.flip(np.cumsum(np.flip(dc, axis=-1), axis=-1), axis=-1)",
+                     "return np.cumsum(dc, axis=-1)"),
+}
+
+
+def _mutant(name):
+    src = open(fox_oracle.__file__).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_hold(mod):
+    c = _case(B=1, H=2, L=48, D=16)
+    s = 1 / math.sqrt(c.D)
+    O, LSE = mod.attn_fwd(c.q, c.k, c.v, c.log_f, scale=s, block=16)
+    O1, L1 = oracle.attn_fwd_bruteforce(c.q, c.k, c.v, c.log_f, s)
+    if np.abs(O - O1).max() > 1e-10 or np.abs(LSE - L1).max() > 1e-10:
+        return False
+    got = mod.attn_bwd(c.q, c.k, c.v, c.log_f, c.do, scale=s, block=16)[:4]
+    ref = _torch_grads(c, s)
+    return all(np.abs(g - r).max() < 1e-9 for g, r in zip(got, ref))
+
+
+def test_unmutated_oracle_passes_the_pin_harness():
+    assert _pins_hold(fox_oracle)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    assert not _pins_hold(_mutant(name))
