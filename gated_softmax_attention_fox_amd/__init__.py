@@ -1,0 +1,308 @@
+"""Forgetting Attention on MI355X (gfx950): Python binding of libfox.so.
+
+Argument marshalling only. Every function below checks the tensors it is given, allocates the
+outputs with torch (device memory is PyTorch's plumbing here), and calls the C entry point of
+the same name in libfox.so on the current HIP stream; all arithmetic runs in the library's
+kernels. If libfox.so is missing, importing the binding raises: there is no fallback path.
+
+C entry points (include/fox.h) and their wrappers:
+    fox_logf_cumsum(log_f)                         -> c
+    fox_gate_logf(x, w_f, b_f)                     -> log_f
+    fox_qk_rmsnorm(x, eps, weight)                 -> y
+    fox_attn_fwd(q, k, v, c, o_dtype, scale)       -> (o, lse)
+    fox_attn_bwd(q, k, v, c, o, lse, dO, scale)    -> (dq, dk, dv, dlog_f)
+    fox_attn_bwd_delta(dO, o)                      -> delta
+    fox_attn_bwd_dq(q, k, v, c, lse, dO, delta)    -> (dq, dc_q, delta_refined)
+    fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta_refined) -> (dk, dv, dc_k)
+    fox_dlogf_from_dc(dc_q, dc_k)                  -> dlog_f
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+__all__ = [
+    "FoxError", "LIB_PATH", "HEADER_PATH", "load_library", "header_functions",
+    "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_bwd",
+    "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
+    "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID",
+    "FOX_E_UNSUPPORTED", "FOX_E_LAUNCH", "FOX_F32", "FOX_BF16", "FOX_CAUSAL",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfox.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fox.h")
+
+FOX_OK, FOX_E_INVALID, FOX_E_UNSUPPORTED, FOX_E_LAUNCH = 0, 1, 2, 3
+FOX_F32, FOX_BF16 = 0, 1
+FOX_CAUSAL = 1
+
+_c_i64, _c_u32, _c_f32, _c_vp, _c_sz = (ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
+                                         ctypes.c_void_p, ctypes.c_size_t)
+_SIGS = {
+    "fox_logf_cumsum": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_gate_logf": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                     _c_i64, _c_i64, _c_vp]),
+    "fox_qk_rmsnorm": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int, _c_i64, _c_i64, _c_f32, _c_vp,
+                                      _c_vp]),
+    "fox_attn_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int,
+                                    _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, _c_u32, _c_vp]),
+    "fox_attn_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "fox_attn_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64,
+                                    _c_i64, _c_i64, _c_f32, _c_u32, _c_vp]),
+    "fox_attn_bwd_delta": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_attn_bwd_dkv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                        _c_f32, _c_u32, _c_vp]),
+    "fox_attn_bwd_dq": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                       _c_f32, _c_u32, _c_vp]),
+    "fox_dlogf_from_dc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "fox_last_error": (ctypes.c_char_p, []),
+    "fox_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class FoxError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {detail}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfox.so and declare the C signatures. Raises if the library is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m gated_softmax_attention_fox_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/fox.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fox_[a-z0-9_]+)\s*\(", text)))
+
+
+def fox_version() -> str:
+    return load_library().fox_version().decode()
+
+
+def _check(status: int, fn: str):
+    if status != FOX_OK:
+        lib = load_library()
+        raise FoxError(status, fn, lib.fox_last_error().decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {t.dim()})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _code(dt: torch.dtype) -> int:
+    return FOX_BF16 if dt == torch.bfloat16 else FOX_F32
+
+
+def fox_logf_cumsum(log_f: torch.Tensor, c: torch.Tensor | None = None) -> torch.Tensor:
+    """c = inclusive prefix sum of log_f along the last axis (fp32 in, fp32 out)."""
+    lib = load_library()
+    pl = _dev(log_f, "log_f", (torch.float32,))
+    if c is None:
+        c = torch.empty_like(log_f)
+    pc = _dev(c, "c", (torch.float32,))
+    L = log_f.shape[-1]
+    _check(lib.fox_logf_cumsum(pl, pc, log_f.numel() // max(L, 1), L, _stream(log_f)),
+           "fox_logf_cumsum")
+    return c
+
+
+def fox_gate_logf(x: torch.Tensor, w_f: torch.Tensor, b_f: torch.Tensor) -> torch.Tensor:
+    """log_f [B, H, L] = log sigmoid(x . w_f^T + b_f) from x [B, L, d_model]."""
+    lib = load_library()
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
+    pw = _dev(w_f, "w_f", (torch.float32,), 2)
+    pb = _dev(b_f, "b_f", (torch.float32,), 1)
+    B, L, dm = x.shape
+    H = w_f.shape[0]
+    if w_f.shape[1] != dm or b_f.shape[0] != H:
+        raise ValueError("w_f must be [H, d_model] and b_f [H]")
+    out = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
+    _check(lib.fox_gate_logf(px, _code(x.dtype), pw, pb, ctypes.c_void_p(out.data_ptr()), B, L, dm,
+                             H, _stream(x)), "fox_gate_logf")
+    return out
+
+
+def fox_qk_rmsnorm(x: torch.Tensor, eps: float = 1e-6, weight: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """RMSNorm over the last axis (D = 64 or 128) of every row; same dtype in and out."""
+    lib = load_library()
+    px = _dev(x, "x", (torch.bfloat16, torch.float32))
+    D = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    po = _dev(out, "out", (x.dtype,))
+    pw = ctypes.c_void_p(0)
+    if weight is not None:
+        pw = _dev(weight, "weight", (torch.float32,), 1)
+    _check(lib.fox_qk_rmsnorm(px, po, _code(x.dtype), x.numel() // D, D, eps, pw, _stream(x)),
+           "fox_qk_rmsnorm")
+    return out
+
+
+def _bhld(q, k, v):
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one shape [B, H, L, D]")
+    return q.shape
+
+
+def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | None = None,
+                 want_lse: bool = True):
+    """(O, LSE) of causal Forgetting Attention with bias c_i - c_j (c: [B, H, L] fp32)."""
+    lib = load_library()
+    B, H, L, D = _bhld(q, k, v)
+    dts = (torch.bfloat16, torch.float32)
+    pq, pk, pv = _dev(q, "q", dts), _dev(k, "k", (q.dtype,)), _dev(v, "v", (q.dtype,))
+    pc = _dev(c, "c", (torch.float32,), 3)
+    if tuple(c.shape) != (B, H, L):
+        raise ValueError("c must be [B, H, L]")
+    o_dtype = o_dtype or q.dtype
+    o = torch.empty((B, H, L, D), dtype=o_dtype, device=q.device)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if want_lse else None
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_fwd(pq, pk, pv, _code(q.dtype), pc, ctypes.c_void_p(o.data_ptr()),
+                            _code(o_dtype), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                            B, H, L, D, scale, FOX_CAUSAL, _stream(q)), "fox_attn_fwd")
+    return o, lse
+
+
+def fox_attn_bwd_workspace_bytes(B: int, H: int, L: int, D: int) -> int:
+    return int(load_library().fox_attn_bwd_workspace_bytes(B, H, L, D))
+
+
+def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=None):
+    """(dQ, dK, dV, d log f) for the loss sum(dO * O); o must be the fp32 forward output."""
+    lib = load_library()
+    B, H, L, D = _bhld(q, k, v)
+    pq = _dev(q, "q", (torch.bfloat16, torch.float32))
+    pk, pv = _dev(k, "k", (q.dtype,)), _dev(v, "v", (q.dtype,))
+    pdo = _dev(dO, "dO", (q.dtype,))
+    pc = _dev(c, "c", (torch.float32,), 3)
+    po = _dev(o, "o", (torch.float32,), 4)
+    pl = _dev(lse, "lse", (torch.float32,), 3)
+    dq = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    dlf = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    need = fox_attn_bwd_workspace_bytes(B, H, L, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace", (torch.uint8,))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_bwd(pq, pk, pv, _code(q.dtype), pc, po, pl, pdo,
+                            ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()),
+                            ctypes.c_void_p(dv.data_ptr()), ctypes.c_void_p(dlf.data_ptr()), pw,
+                            workspace.numel(), B, H, L, D, scale, FOX_CAUSAL, _stream(q)),
+           "fox_attn_bwd")
+    return dq, dk, dv, dlf
+
+
+def fox_attn_bwd_delta(dO: torch.Tensor, o: torch.Tensor) -> torch.Tensor:
+    """Delta = rowsum(dO * O) over the last axis; dO bf16, o fp32."""
+    lib = load_library()
+    pd = _dev(dO, "dO", (torch.bfloat16,))
+    po = _dev(o, "o", (torch.float32,))
+    if dO.shape != o.shape:
+        raise ValueError("dO and o must have the same shape")
+    D = o.shape[-1]
+    delta = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
+    _check(lib.fox_attn_bwd_delta(pd, FOX_BF16, po, ctypes.c_void_p(delta.data_ptr()),
+                                  o.numel() // D, D, _stream(o)), "fox_attn_bwd_delta")
+    return delta
+
+
+def _bwd_inputs(q, k, v, c, lse, dO, delta):
+    B, H, L, D = _bhld(q, k, v)
+    ptrs = (_dev(q, "q", (torch.bfloat16,)), _dev(k, "k", (torch.bfloat16,)),
+            _dev(v, "v", (torch.bfloat16,)), _dev(c, "c", (torch.float32,), 3),
+            _dev(lse, "lse", (torch.float32,), 3), _dev(dO, "dO", (torch.bfloat16,), 4),
+            _dev(delta, "delta", (torch.float32,), 3))
+    return (B, H, L, D), ptrs
+
+
+def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None):
+    """(dK, dV, dc_k) of the key-stationary backward step; delta = fox_attn_bwd_dq's refined one."""
+    lib = load_library()
+    (B, H, L, D), (pq, pk, pv, pc, pl, pdo, pdl) = _bwd_inputs(q, k, v, c, lse, dO, delta)
+    dk = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    dck = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_bwd_dkv(pq, pk, pv, FOX_BF16, pc, pl, pdo, pdl,
+                                ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
+                                ctypes.c_void_p(dck.data_ptr()), B, H, L, D, scale, FOX_CAUSAL,
+                                _stream(q)), "fox_attn_bwd_dkv")
+    return dk, dv, dck
+
+
+def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
+                    delta_out: torch.Tensor | None = None):
+    """(dQ, dc_q, refined delta) of the query-stationary backward step (run before dkv).
+
+    delta_out may be `delta` itself to refine it in place."""
+    lib = load_library()
+    (B, H, L, D), (pq, pk, pv, pc, pl, pdo, pdl) = _bwd_inputs(q, k, v, c, lse, dO, delta)
+    dq = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
+    dcq = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if delta_out is None:
+        delta_out = torch.empty_like(delta)
+    pdn = _dev(delta_out, "delta_out", (torch.float32,), 3)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_bwd_dq(pq, pk, pv, FOX_BF16, pc, pl, pdo, pdl,
+                               ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dcq.data_ptr()), pdn,
+                               B, H, L, D, scale, FOX_CAUSAL, _stream(q)), "fox_attn_bwd_dq")
+    return dq, dcq, delta_out
+
+
+def fox_dlogf_from_dc(dc_q: torch.Tensor, dc_k: torch.Tensor) -> torch.Tensor:
+    """d log f = reverse cumulative sum of dc_q + dc_k along the last axis."""
+    lib = load_library()
+    pa = _dev(dc_q, "dc_q", (torch.float32,))
+    pb = _dev(dc_k, "dc_k", (torch.float32,))
+    if dc_q.shape != dc_k.shape:
+        raise ValueError("dc_q and dc_k must have the same shape")
+    out = torch.empty_like(dc_q)
+    L = dc_q.shape[-1]
+    _check(lib.fox_dlogf_from_dc(pa, pb, ctypes.c_void_p(out.data_ptr()), dc_q.numel() // L, L,
+                                 _stream(dc_q)), "fox_dlogf_from_dc")
+    return out

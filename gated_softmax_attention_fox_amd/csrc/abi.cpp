@@ -1,0 +1,274 @@
+// abi.cpp — the C ABI of libfox (declared in include/fox.h).
+//
+// Each entry point validates its arguments on the host, returns FOX_E_INVALID /
+// FOX_E_UNSUPPORTED before touching the GPU when they are wrong, and otherwise enqueues the
+// kernels on the caller's stream and maps a failed launch to FOX_E_LAUNCH. Nothing here
+// allocates device memory or synchronises the host with the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fox.h"
+#include "fox_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fox_status fail(fox_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+fox_status ok() {
+  g_last_error.clear();
+  return FOX_OK;
+}
+
+fox_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FOX_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest sizes the kernels index with 32-bit integers.
+constexpr int64_t kMaxL = int64_t(1) << 26;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+#define FOX_REQUIRE(cond, ...)                                   \
+  do {                                                           \
+    if (!(cond)) return fail(FOX_E_INVALID, __VA_ARGS__);        \
+  } while (0)
+
+#define FOX_REQUIRE_PTR(p)                                                          \
+  do {                                                                              \
+    FOX_REQUIRE((p) != nullptr, "%s must not be NULL", #p);                         \
+    FOX_REQUIRE(aligned16(p), "%s must be 16-byte aligned", #p);                    \
+  } while (0)
+
+fox_status check_bhld(int64_t B, int64_t H, int64_t L, int64_t D) {
+  FOX_REQUIRE(B >= 1 && H >= 1, "B and H must be >= 1 (got B=%lld H=%lld)", (long long)B,
+              (long long)H);
+  FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, %lld] (got %lld)", (long long)kMaxL,
+              (long long)L);
+  FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
+  FOX_REQUIRE(B * H <= (int64_t(1) << 31) / 1024 && B * H * L * D <= kMaxElems,
+              "B*H*L*D too large");
+  return FOX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fox_version(void) { return "0.1.0"; }
+
+const char* fox_status_str(fox_status s) {
+  switch (s) {
+    case FOX_OK: return "ok";
+    case FOX_E_INVALID: return "invalid argument";
+    case FOX_E_UNSUPPORTED: return "unsupported request";
+    case FOX_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* fox_last_error(void) { return g_last_error.c_str(); }
+
+fox_status fox_logf_cumsum(const float* log_f, float* c, int64_t BH, int64_t L, void* stream) {
+  FOX_REQUIRE_PTR(log_f);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE(log_f != c, "c must not alias log_f");
+  FOX_REQUIRE(BH >= 1 && BH < (int64_t(1) << 31), "BH must be in [1, 2^31) (got %lld)",
+              (long long)BH);
+  FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, %lld] (got %lld)", (long long)kMaxL,
+              (long long)L);
+  return launched(fox::launch_cumsum(log_f, c, BH, L, (hipStream_t)stream), "fox_logf_cumsum");
+}
+
+fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
+                         float* log_f, int64_t B, int64_t L, int64_t d_model, int64_t H,
+                         void* stream) {
+  FOX_REQUIRE_PTR(x);
+  FOX_REQUIRE_PTR(w_f);
+  FOX_REQUIRE(b_f != nullptr, "b_f must not be NULL");
+  FOX_REQUIRE_PTR(log_f);
+  FOX_REQUIRE(x_dt == FOX_BF16 || x_dt == FOX_F32, "x_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(B >= 1 && L >= 1 && L <= kMaxL, "B >= 1 and 1 <= L <= 2^26 required");
+  FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
+  FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
+              "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
+  FOX_REQUIRE(B * ((L + 63) / 64) < (int64_t(1) << 31), "B*L too large");
+  return launched(fox::launch_gate(x, x_dt == FOX_BF16, w_f, b_f, log_f, B, L, d_model, H,
+                                   (hipStream_t)stream),
+                  "fox_gate_logf");
+}
+
+fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, int64_t D, float eps,
+                          const float* weight, void* stream) {
+  FOX_REQUIRE_PTR(x);
+  FOX_REQUIRE_PTR(y);
+  FOX_REQUIRE(dt == FOX_BF16 || dt == FOX_F32, "dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(rows >= 1 && rows * (D / 8) / 256 < (int64_t(1) << 31), "rows out of range");
+  FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
+  FOX_REQUIRE(eps >= 0.f, "eps must be >= 0");
+  return launched(fox::launch_rmsnorm(x, y, dt == FOX_BF16, rows, D, eps, weight,
+                                      (hipStream_t)stream),
+                  "fox_qk_rmsnorm");
+}
+
+fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                        const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B, int64_t H,
+                        int64_t L, int64_t D, float scale, uint32_t flags, void* stream) {
+  FOX_REQUIRE_PTR(q);
+  FOX_REQUIRE_PTR(k);
+  FOX_REQUIRE_PTR(v);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE_PTR(o);
+  if (lse) FOX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+  fox_status st = check_bhld(B, H, L, D);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(!(in_dt == FOX_F32 && o_dt != FOX_F32), "fp32 inputs require an fp32 output");
+  FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+  if (!(flags & FOX_CAUSAL))
+    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
+  if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  const hipStream_t s = (hipStream_t)stream;
+  if (in_dt == FOX_F32)
+    return launched(fox::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, c,
+                                        (float*)o, lse, B * H, L, D, scale, s),
+                    "fox_attn_fwd");
+  return launched(fox::launch_fwd_bf16(q, k, v, c, o, o_dt == FOX_F32, lse, B * H, L, D, scale, s),
+                  "fox_attn_fwd");
+}
+
+size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D) {
+  (void)D;
+  if (B < 1 || H < 1 || L < 1) return 0;
+  return fox::bwd_workspace_bytes(B * H, L);
+}
+
+fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                        const float* c, const float* o, const float* lse, const void* dO,
+                        float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
+                        size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
+                        float scale, uint32_t flags, void* stream) {
+  FOX_REQUIRE_PTR(q);
+  FOX_REQUIRE_PTR(k);
+  FOX_REQUIRE_PTR(v);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE_PTR(o);
+  FOX_REQUIRE_PTR(lse);
+  FOX_REQUIRE_PTR(dO);
+  FOX_REQUIRE_PTR(dq);
+  FOX_REQUIRE_PTR(dk);
+  FOX_REQUIRE_PTR(dv);
+  FOX_REQUIRE_PTR(dlog_f);
+  FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL");
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+              "workspace must be 256-byte aligned");
+  fox_status st = check_bhld(B, H, L, D);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+  if (!(flags & FOX_CAUSAL))
+    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
+  if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (in_dt != FOX_BF16)
+    return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
+                "the backward takes bf16 q/k/v/dO (in_dt = FOX_BF16)");
+  const size_t need = fox::bwd_workspace_bytes(B * H, L);
+  FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
+              workspace_bytes, need);
+  return launched(fox::launch_bwd_bf16(q, k, v, c, o, lse, dO, dq, dk, dv, dlog_f, workspace,
+                                       B * H, L, D, scale, (hipStream_t)stream),
+                  "fox_attn_bwd");
+}
+
+namespace {
+fox_status check_bwd_common(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                            const float* c, const float* lse, const void* dO, const float* delta,
+                            int64_t B, int64_t H, int64_t L, int64_t D, float scale,
+                            uint32_t flags) {
+  FOX_REQUIRE_PTR(q);
+  FOX_REQUIRE_PTR(k);
+  FOX_REQUIRE_PTR(v);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE_PTR(lse);
+  FOX_REQUIRE_PTR(dO);
+  FOX_REQUIRE_PTR(delta);
+  fox_status st = check_bhld(B, H, L, D);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+  if (!(flags & FOX_CAUSAL))
+    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
+  if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (in_dt != FOX_BF16)
+    return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
+                "the backward takes bf16 q/k/v/dO (in_dt = FOX_BF16)");
+  return FOX_OK;
+}
+}  // namespace
+
+fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, float* delta,
+                              int64_t rows, int64_t D, void* stream) {
+  FOX_REQUIRE_PTR(dO);
+  FOX_REQUIRE_PTR(o);
+  FOX_REQUIRE_PTR(delta);
+  FOX_REQUIRE(dO_dt == FOX_BF16, "dO must be bf16 (dO_dt = FOX_BF16)");
+  FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
+  FOX_REQUIRE(rows >= 1 && rows * (D / 8) / 256 < (int64_t(1) << 31), "rows out of range");
+  return launched(fox::launch_bwd_delta(dO, o, delta, rows, D, (hipStream_t)stream),
+                  "fox_attn_bwd_delta");
+}
+
+fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                            const float* c, const float* lse, const void* dO, const float* delta,
+                            float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
+                            int64_t D, float scale, uint32_t flags, void* stream) {
+  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, delta, B, H, L, D, scale, flags);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(dk);
+  FOX_REQUIRE_PTR(dv);
+  FOX_REQUIRE_PTR(dc_k);
+  return launched(fox::launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dc_k, B * H, L, D, scale,
+                                      (hipStream_t)stream),
+                  "fox_attn_bwd_dkv");
+}
+
+fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                           const float* c, const float* lse, const void* dO, const float* delta,
+                           float* dq, float* dc_q, float* delta_out, int64_t B, int64_t H,
+                           int64_t L, int64_t D, float scale, uint32_t flags, void* stream) {
+  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, delta, B, H, L, D, scale, flags);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(dq);
+  FOX_REQUIRE_PTR(dc_q);
+  FOX_REQUIRE_PTR(delta_out);
+  return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dc_q, delta_out, B * H, L, D,
+                                     scale, (hipStream_t)stream),
+                  "fox_attn_bwd_dq");
+}
+
+fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f, int64_t BH,
+                             int64_t L, void* stream) {
+  FOX_REQUIRE_PTR(dc_q);
+  FOX_REQUIRE_PTR(dc_k);
+  FOX_REQUIRE_PTR(dlog_f);
+  FOX_REQUIRE(dlog_f != dc_q && dlog_f != dc_k, "dlog_f must not alias dc_q or dc_k");
+  FOX_REQUIRE(BH >= 1 && BH < (int64_t(1) << 31), "BH must be in [1, 2^31)");
+  FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, 2^26]");
+  return launched(fox::launch_rev_cumsum2(dc_q, dc_k, dlog_f, BH, L, (hipStream_t)stream),
+                  "fox_dlogf_from_dc");
+}
+
+}  // extern "C"

@@ -1,0 +1,334 @@
+// attn_fwd.hip — Forgetting Attention forward on gfx950.
+//
+// Computes, for every (b, h) and query i,
+//   O_i = sum_{j<=i} softmax_j(scale q_i.k_j + c_i - c_j) v_j,  LSE_i = log sum_j exp(...),
+// tile by tile, without materialising the L x L bias (paper-graph-ui summary of arXiv 2503.02130,
+// section 3.4, "Hardware-Aware Implementation (Modified FlashAttention)", the forward pass: load
+// the c slices with the Q and K/V blocks, add the rank-1 bias c^q 1^T - 1 c^k^T to the logit
+// block on chip, mask causally, run the online softmax, normalise at the end; paperlayer.ai
+// summary, section E).
+//
+// bf16 path (MFMA). A workgroup owns 128 queries of one (b, h); each of its 4 waves owns 32 of
+// them. The score block is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so
+// that every lane holds one query's column of scores: the row max and row sum of the online
+// softmax are then in-lane reductions plus one exchange with the partner half-wave. The
+// probabilities stay in registers and feed O^T += V^T P^T directly as the B operand; V^T comes
+// from a column read of the row-major V tile in LDS. K, V and the bias slice are staged in LDS
+// per 64-key tile. Only the diagonal tiles evaluate the causal mask; tiles entirely above a
+// wave's last query are skipped by that wave. Workgroups are issued longest-first (the last
+// query tiles, which see the most keys, start first) to even out the causal triangle.
+//
+// Bias and precision: the softmax runs in base 2 on x = scale*log2(e)*(q.k) - log2(e)*(c_j - c_r),
+// with c_r = c at the workgroup's first query. The row constant c_i - c_r cancels in the softmax
+// and is added back only to LSE, and keeping c relative to a nearby reference makes c_j - c_r
+// exact for the keys that carry weight.
+//
+// fp32 path (vector ALU, no down-conversion): one wave owns 32 queries, two lanes per query
+// (each half of the head dimension), K/V tiles of 32 keys in LDS; the logit is
+// scale*(q.k) + (c_i - c_j) in fp32 and the softmax uses expf.
+#include <cstdlib>
+
+#include "fox_device.h"
+#include "fox_launch.h"
+
+namespace fox {
+namespace {
+
+constexpr int kFwdBN = 64;  // keys per LDS tile
+
+// NW waves, 32 queries each. K/V/bias tiles are double-buffered in LDS: the global loads of
+// tile t+1 are issued into registers before tile t is computed and stored to the other buffer
+// after it, so one barrier per tile suffices.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const float* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE, int L, int BH,
+    int n_qt, float sl2e, int o_f32) {
+  constexpr int BM = NW * 32;
+  constexpr int NT = NW * 64;
+  constexpr int TILE = kFwdBN * D;
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int CPT = TILE / 8 / NT;      // chunks per thread per tensor
+  static_assert(CPT >= 1 && CPT * 8 * NT == TILE, "tile must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) bf16_t k_s[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t v_s[2][TILE];
+  __shared__ __attribute__((aligned(16))) float ck_s[2][kFwdBN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int qt = n_qt - 1 - bid / BH;  // longest-first
+  const int q0 = qt * BM;
+  const size_t base = (size_t)bh * L * D;
+  Q += base;
+  K += base;
+  V += base;
+  C += (size_t)bh * L;
+  const float c_ref = C[q0];
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (qi < L) {
+      qf[c] = ld8(Q + (size_t)qi * D + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.f;
+    }
+  }
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) oacc[d] = zero16();
+  float m = -INFINITY, lsum = 0.f;
+
+  u32x4 kreg[CPT], vreg[CPT];
+  float creg = 0.f;
+  // (always_inline: an outlined lambda would keep kreg/vreg in scratch memory)
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kFwdBN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      const int key = k0 + idx / CPR, cc = idx % CPR;
+      kreg[i] = ld16_or_zero<D>(K, key, L, cc * 8);  // within one (b, h): L * D < 2^31
+      vreg[i] = ld16_or_zero<D>(V, key, L, cc * 8);
+    }
+    if (tid < kFwdBN) creg = (k0 + tid) < L ? (C[k0 + tid] - c_ref) * kLog2e : 0.f;
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      lds_store8<D>(k_s[buf], idx / CPR, (idx % CPR) * 8, kreg[i]);
+      lds_store8<D>(v_s[buf], idx / CPR, (idx % CPR) * 8, vreg[i]);
+    }
+    if (tid < kFwdBN) ck_s[buf][tid] = creg;
+  };
+
+  const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
+  const int kt_last = q_last / kFwdBN;
+  // Key tiles are walked from the diagonal backwards. The first tile a wave processes holds its
+  // largest biases (c is non-increasing, so the bias shrinks with distance) and fixes a running
+  // max that later tiles rarely beat; the max is therefore only raised when a tile exceeds it by
+  // more than kLazy (in log2 units), which bounds every probability by 2^kLazy and skips the
+  // rescaling of O on almost every tile. Only that first tile needs the causal mask: it starts
+  // at or before the wave's first query, so every row already has a finite max after it.
+  constexpr float kLazy = 8.0f;
+  gload(kt_last);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it <= kt_last; ++it) {
+    const int kt = kt_last - it;
+    const int buf = it & 1;
+    const int k0 = kt * kFwdBN;
+    if (kt > 0) gload(kt - 1);
+    if (k0 <= qw + 31) {  // else every key of this tile lies after every query of this wave
+      const bool diag = k0 + kFwdBN - 1 > qw;
+      const bf16_t* ks = k_s[buf];
+      const bf16_t* vs = v_s[buf];
+      f32x16 s[kFwdBN / 32];
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+        s[kb] = zero16();
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+          s[kb] = mfma32(lds_row8<D>(ks, kb * 32 + l32, 16 * c + 8 * h), qf[c], s[kb]);
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 ck = *reinterpret_cast<const f32x4*>(&ck_s[buf][kb * 32 + 8 * i + 4 * h]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x = fmaf(s[kb][4 * i + j], sl2e, -ck[j]);
+            if (diag && (k0 + kb * 32 + 8 * i + 4 * h + j) > qi) x = -INFINITY;
+            s[kb][4 * i + j] = x;
+            mx = fmaxf(mx, x);
+          }
+        }
+      }
+      mx = xhalf_max(mx);
+      const bool raise = mx > m + kLazy;
+      if (__any(raise)) {  // wave-uniform: rescale only when some row's max moved
+        const float mnew = raise ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(s[kb][e] - m);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 pb = pack_c_half(s[kb], t);
+          lsum = rowsum_bf16x8(pb, lsum);  // l sums the same rounded P that meets V
+#pragma unroll
+          for (int d = 0; d < D / 32; ++d)
+            oacc[d] = mfma32(lds_col8<D>(vs, kb * 32 + 16 * t, d * 32, lane), pb, oacc[d]);
+        }
+      }
+    }
+    if (kt > 0) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float ltot = xhalf_sum(lsum);
+  const float inv = 1.0f / ltot;
+  if (qi < L) {
+    const size_t orow = base + (size_t)qi * D;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = d * 32 + 8 * i + 4 * h;
+        const float y0 = oacc[d][4 * i] * inv, y1 = oacc[d][4 * i + 1] * inv;
+        const float y2 = oacc[d][4 * i + 2] * inv, y3 = oacc[d][4 * i + 3] * inv;
+        if (o_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + col) = make_float4(y0, y1, y2, y3);
+        } else {
+          const uint32_t lo = (uint32_t)f2bf(y0) | ((uint32_t)f2bf(y1) << 16);
+          const uint32_t hi = (uint32_t)f2bf(y2) | ((uint32_t)f2bf(y3) << 16);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(O) + orow + col) = make_uint2(lo, hi);
+        }
+      }
+    }
+    if (h == 0 && LSE) LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + (C[qi] - c_ref);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+constexpr int kF32BM = 32;  // queries per workgroup (one wave, two lanes per query)
+constexpr int kF32BN = 32;  // keys per LDS tile
+
+template <int D>
+__global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q,
+                                                     const float* __restrict__ K,
+                                                     const float* __restrict__ V,
+                                                     const float* __restrict__ C,
+                                                     float* __restrict__ O, float* __restrict__ LSE,
+                                                     int L, float scale) {
+  constexpr int DH = D / 2;
+  __shared__ float k_s[kF32BN][D];
+  __shared__ float v_s[kF32BN][D];
+  __shared__ float c_s[kF32BN];
+  const int tid = threadIdx.x;
+  const int half = tid >> 5;
+  const int bh = blockIdx.y;
+  const int q0 = blockIdx.x * kF32BM;
+  const int qi = q0 + (tid & 31);
+  const size_t base = (size_t)bh * L * D;
+  Q += base;
+  K += base;
+  V += base;
+  C += (size_t)bh * L;
+  const bool qok = qi < L;
+  const float ci = qok ? C[qi] : 0.f;
+  float q[DH], o[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) {
+    q[d] = qok ? Q[(size_t)qi * D + half * DH + d] : 0.f;
+    o[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int q_last = (q0 + kF32BM - 1 < L - 1) ? q0 + kF32BM - 1 : L - 1;
+  for (int k0 = 0; k0 <= q_last; k0 += kF32BN) {
+    __syncthreads();
+    for (int idx = tid; idx < kF32BN * D; idx += 64) {
+      const int r = idx / D, d = idx % D;
+      const int key = k0 + r;
+      k_s[r][d] = key < L ? K[(size_t)key * D + d] : 0.f;
+      v_s[r][d] = key < L ? V[(size_t)key * D + d] : 0.f;
+    }
+    if (tid < kF32BN) c_s[tid] = (k0 + tid) < L ? C[k0 + tid] : 0.f;
+    __syncthreads();
+    float s[kF32BN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kF32BN; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < DH; ++d) dot = fmaf(q[d], k_s[j][half * DH + d], dot);
+      dot += __shfl_xor(dot, 32, 64);
+      const float x = (k0 + j <= qi) ? fmaf(dot, scale, ci - c_s[j]) : -INFINITY;
+      s[j] = x;
+      mx = fmaxf(mx, x);
+    }
+    const float mnew = fmaxf(m, mx);
+    const float alpha = expf(m - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < kF32BN; ++j) {
+      s[j] = expf(s[j] - mnew);
+      ps += s[j];
+    }
+    l = l * alpha + ps;
+    m = mnew;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) {
+      float acc = o[d] * alpha;
+#pragma unroll
+      for (int j = 0; j < kF32BN; ++j) acc = fmaf(s[j], v_s[j][half * DH + d], acc);
+      o[d] = acc;
+    }
+  }
+  if (!qok) return;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) O[base + (size_t)qi * D + half * DH + d] = o[d] * inv;
+  if (half == 0 && LSE) LSE[(size_t)bh * L + qi] = m + logf(l);
+}
+
+}  // namespace
+
+template <int D, int NW>
+void fwd_bf16_go(const void* q, const void* k, const void* v, const float* c, void* o, bool o_f32,
+                 float* lse, int64_t BH, int64_t L, float scale, hipStream_t s) {
+  const int n_qt = (int)((L + NW * 32 - 1) / (NW * 32));
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)(n_qt * BH)), dim3(NW * 64), 0, s,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L,
+                     (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const float* c, void* o,
+                           bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
+                           hipStream_t s) {
+  // waves per workgroup (32 queries each): 8 (256-query workgroups) unless FOX_FWD_WAVES=4
+  static const int nw = [] {
+    const char* e = getenv("FOX_FWD_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  if (D == 64) {
+    if (nw == 8) fwd_bf16_go<64, 8>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
+    else fwd_bf16_go<64, 4>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
+  } else {
+    if (nw == 8) fwd_bf16_go<128, 8>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
+    else fwd_bf16_go<128, 4>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, const float* c, float* o,
+                          float* lse, int64_t BH, int64_t L, int64_t D, float scale, hipStream_t s) {
+  const dim3 grid((unsigned)((L + kF32BM - 1) / kF32BM), (unsigned)BH);
+  if (D == 64)
+    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, c, o, lse, (int)L, scale);
+  else
+    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, c, o, lse, (int)L, scale);
+  return hipGetLastError();
+}
+
+}  // namespace fox

@@ -1,0 +1,144 @@
+// fox_device.h — device-side building blocks shared by the gfx950 kernels of libfox.
+//
+// Matrix-core conventions (CDNA4, wave64). For v_mfma_f32_32x32x16_bf16, lane l with
+// h = l / 32 supplies
+//   A[m = l % 32][k = 8h .. 8h+7]     (8 bf16)
+//   B[k = 8h .. 8h+7][n = l % 32]     (8 bf16)
+// and receives the fp32 accumulator values
+//   C[m = 8i + 4h + j][n = l % 32]    in slot 4i + j   (i, j = 0..3).
+// Only two facts are relied on: A and B pair their k slots identically, and the C layout above.
+// A C tile therefore already sits in B-operand form with k = its row index: the 8 values of
+// slots 8t .. 8t+7 (t = 0, 1) are B's k slots for rows {16t + 4h + 0..3, 16t + 8 + 4h + 0..3}.
+// Any A operand paired with such a B must present the same rows in the same slots; the
+// helpers below read exactly that row set.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fox {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bf16_t;  // storage type of bfloat16 in global memory and LDS
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// bf16 <-> fp32 (round to nearest even on the way down, via the gfx950 convert instruction).
+__device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, h);
+}
+
+// 8 consecutive bf16 from memory (global or LDS) as an MFMA operand.
+__device__ __forceinline__ bf16x8 ld8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Pack slots 8t .. 8t+7 of a C tile into a bf16 B operand.
+__device__ __forceinline__ bf16x8 pack_c_half(const f32x16& c, int t) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[8 * t + e];
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// LDS tiles of D bf16 columns (D = 64 or 128), unpadded and XOR-swizzled in 16-byte chunks:
+// logical chunk c of row r lives at physical chunk c ^ swz_key(r). The key is chosen so that
+// both access patterns the kernels use are free of bank conflicts:
+//   row reads   - 16 lanes read the same 16-byte chunk of 16 consecutive rows (ds_read_b128);
+//   column reads - 32 lanes read a 4-row x 64-byte block in 8-byte pieces (ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// Element offset of logical (row, col) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz_key<D>(row))) << 3) + (col & 7);
+}
+
+// 8 consecutive elements of one row (col a multiple of 8): an A/B operand read along k = column.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row8(const bf16_t* base, int row, int col) {
+  return *reinterpret_cast<const bf16x8*>(base + swz<D>(row, col));
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// A operand whose k slots are the rows {r0 + 4h + 0..3, r0 + 8 + 4h + 0..3} of a swizzled LDS
+// tile at column cbase + (lane % 32) (cbase a multiple of 32): the transpose of a row read.
+// Matches pack_c_half(., t) when r0 = 16t relative to the C tile's first row.
+//
+// ds_read_b64_tr_b16 works on groups of 16 lanes: lane 4a + b of a group receives element b of
+// the 8-byte pieces read by the group's lanes a, a + 4, a + 8, a + 12 (in that order). So when
+// group lane s reads columns col0 + 4(s % 4) .. +3 of row row0 + s / 4, group lane i receives
+// column col0 + i of rows row0 .. row0 + 3.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col8(const bf16_t* base, int r0, int cbase, int lane) {
+  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = cbase + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + swz<D>(row, col)));
+  const i16x4 b =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + swz<D>(row + 8, col)));
+  // Whole-vector shuffle and bit cast only: a __builtin_bit_cast of a single element of a
+  // __bf16 vector is miscompiled by this toolchain (every element reads element 0).
+  const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+// 16-byte register chunk. A native vector (not HIP's uint4 struct): selects between two chunks
+// then stay in registers instead of going through scratch memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Row `row` (0-based, < rows) of a dense [rows x D] bf16 matrix, 8 elements from column col,
+// or zeros when row >= rows. The load itself is clamped to the last row, so it is always in
+// bounds, and the zero fill is a value select.
+template <int D>
+__device__ __forceinline__ u32x4 ld16_or_zero(const bf16_t* m, int row, int rows, int col) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(m + (row < rows ? row : rows - 1) * D + col);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  return row < rows ? v : z;
+}
+
+// Store 16 bytes (8 elements, col a multiple of 8) into a swizzled tile.
+template <int D>
+__device__ __forceinline__ void lds_store8(bf16_t* base, int row, int col, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(base + swz<D>(row, col)) = v;
+}
+
+// acc + sum of the 8 bf16 values of v, with v_dot2_f32_bf16 against packed ones (fp32 sums).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float rowsum_bf16x8(const bf16x8& v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
+// Sum / max across the two half-waves (lanes l and l ^ 32).
+__device__ __forceinline__ float xhalf_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+__device__ __forceinline__ float xhalf_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+
+}  // namespace fox

@@ -1,0 +1,128 @@
+// gate.hip — the scalar per-head forget gate in log space.
+//
+// log f[b, h, t] = log sigmoid(z), z = sum_d x[b, t, d] w_f[h, d] + b_f[h]  (paper-graph-ui summary
+// of arXiv 2503.02130, section 3.4, "Forget Gate Computation": one weight vector and one bias per
+// head applied to the layer input; Pro block Step 4 keeps the same gate).
+//
+// HBM-bound contraction with H (~12) outputs per token, done on the vector ALU: a workgroup owns
+// 64 tokens, stages x through LDS in coalesced 256-column slabs, and each of its 4 waves walks a
+// quarter of every slab with one token per lane. The gate weights are read with wave-uniform
+// addresses (scalar loads), so the inner loop is one FMA per (token, head, column). The four
+// per-wave partial sums meet in LDS and lane t writes log f for token t, evaluated stably as
+// -log1p(exp(-z)) for z >= 0 and z - log1p(exp(z)) otherwise.
+#include "fox_device.h"
+#include "fox_launch.h"
+
+namespace fox {
+namespace {
+
+constexpr int kGateTok = 64;       // tokens per workgroup
+constexpr int kGateSlab = 256;     // x columns staged per step
+constexpr int kGatePitch = kGateSlab + 8;
+constexpr int kGateHeads = 16;     // heads handled per workgroup (blockIdx.y walks head groups)
+
+__device__ __forceinline__ float log_sigmoid(float z) {
+  return z >= 0.f ? -log1pf(expf(-z)) : z - log1pf(expf(z));
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
+                                                   const float* __restrict__ w_f,
+                                                   const float* __restrict__ b_f,
+                                                   float* __restrict__ log_f, int L, int dm, int H,
+                                                   int tok_blocks) {
+  __shared__ bf16_t xs_b[kBf16 ? kGateTok * kGatePitch : 1];
+  __shared__ float xs_f[kBf16 ? 1 : kGateTok * kGatePitch];
+  __shared__ float red[4][kGateHeads][kGateTok];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x / tok_blocks;
+  const int t0 = (blockIdx.x % tok_blocks) * kGateTok;
+  const int h0 = blockIdx.y * kGateHeads;
+  const int nh = H - h0 < kGateHeads ? H - h0 : kGateHeads;
+
+  float acc[kGateHeads];
+#pragma unroll
+  for (int h = 0; h < kGateHeads; ++h) acc[h] = 0.f;
+
+  for (int d0 = 0; d0 < dm; d0 += kGateSlab) {
+    const int width = dm - d0 < kGateSlab ? dm - d0 : kGateSlab;  // multiple of 8
+    __syncthreads();
+    // stage x[b, t0 .. t0+63, d0 .. d0+width) into LDS, 8 columns per thread-step
+    for (int idx = tid; idx < kGateTok * (kGateSlab / 8); idx += 256) {
+      const int r = idx / (kGateSlab / 8), c8 = (idx % (kGateSlab / 8)) * 8;
+      const int t = t0 + r;
+      const bool ok = t < L && c8 < width;
+      const size_t g = ((size_t)b * L + t) * dm + d0 + c8;
+      if (kBf16) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (ok) v = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(xv) + g);
+        *reinterpret_cast<uint4*>(&xs_b[r * kGatePitch + c8]) = v;
+      } else {
+        float4 v0 = make_float4(0, 0, 0, 0), v1 = v0;
+        if (ok) {
+          v0 = *reinterpret_cast<const float4*>(static_cast<const float*>(xv) + g);
+          v1 = *reinterpret_cast<const float4*>(static_cast<const float*>(xv) + g + 4);
+        }
+        *reinterpret_cast<float4*>(&xs_f[r * kGatePitch + c8]) = v0;
+        *reinterpret_cast<float4*>(&xs_f[r * kGatePitch + c8 + 4]) = v1;
+      }
+    }
+    __syncthreads();
+    // wave w covers columns [64w, 64w+64) of the slab; lane = token
+    const int cw0 = wave * 64;
+    for (int c8 = 0; c8 < 64; c8 += 8) {
+      const int col = cw0 + c8;
+      if (col >= width) break;  // wave-uniform
+      float xv8[8];
+      if (kBf16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(&xs_b[lane * kGatePitch + col]);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv8[2 * e] = __uint_as_float(w4[e] << 16);
+          xv8[2 * e + 1] = __uint_as_float(w4[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv8[e] = xs_f[lane * kGatePitch + col + e];
+      }
+#pragma unroll
+      for (int h = 0; h < kGateHeads; ++h) {
+        if (h < nh) {
+          const float* wr = w_f + (size_t)(h0 + h) * dm + d0 + col;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h] = fmaf(xv8[e], wr[e], acc[h]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kGateHeads; ++h) red[wave][h][lane] = acc[h];
+  __syncthreads();
+  if (wave == 0) {
+    const int t = t0 + lane;
+    for (int h = 0; h < nh; ++h) {
+      const float z = ((red[0][h][lane] + red[1][h][lane]) + (red[2][h][lane] + red[3][h][lane])) +
+                      b_f[h0 + h];
+      if (t < L) log_f[((size_t)b * H + h0 + h) * L + t] = log_sigmoid(z);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* log_f,
+                       int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
+  const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
+  const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
+  if (x_bf16)
+    hipLaunchKernelGGL(gate_kernel<true>, grid, dim3(256), 0, s, x, w_f, b_f, log_f, (int)L,
+                       (int)d_model, (int)H, tok_blocks);
+  else
+    hipLaunchKernelGGL(gate_kernel<false>, grid, dim3(256), 0, s, x, w_f, b_f, log_f, (int)L,
+                       (int)d_model, (int)H, tok_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace fox

@@ -1,0 +1,161 @@
+/*
+ * fox.h — C ABI of the Forgetting Attention library (libfox.so, gfx950 / MI355X).
+ *
+ * Forgetting Attention is causal softmax attention whose logits carry the bias
+ * D_ij = c_i - c_j, with c the per-head prefix sum of log forget gates
+ * (arXiv 2503.02130, "Forgetting Transformer: Softmax Attention with a Forget Gate";
+ * paper-graph-ui summary, section 3.4, parts "The Mathematical Form of Forgetting
+ * Attention" and "Hardware-Aware Implementation (Modified FlashAttention)").
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller. The library never
+ *     allocates, frees or keeps a pointer after the call returns; the caller keeps the
+ *     buffers alive until the queued work on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call only
+ *     enqueues kernels on it: no host synchronisation, no host<->device copies.
+ *   - Layouts are dense and row-major, last index fastest:
+ *       q, k, v, o, dO, dq, dk, dv : [B, H, L, D]
+ *       log_f, c, lse, dlog_f       : [B, H, L]
+ *       x (gate input)              : [B, L, d_model];  w_f: [H, d_model];  b_f: [H]
+ *     Positions are 0-indexed; c is the inclusive prefix sum c_i = sum_{l<=i} log f_l.
+ *   - Every pointer must be 16-byte aligned. D must be 64 or 128; L >= 1; B, H >= 1.
+ *   - Arguments are validated on the host before anything is launched. A bad argument
+ *     returns FOX_E_INVALID (or FOX_E_UNSUPPORTED for a well-formed request this library does
+ *     not implement) and enqueues nothing; fox_last_error() then describes it. A failed
+ *     launch returns FOX_E_LAUNCH. No C++ exception or abort crosses this boundary.
+ *   - Preconditions not checked on the device: log f must be finite (the pages' log 0 = -inf
+ *     would make c_i - c_j undefined; a hard reset is a large finite negative value such as
+ *     -1e4); NaN inputs propagate to NaN outputs.
+ *   - Calls are reentrant: the library holds no mutable global state apart from the
+ *     thread-local error message.
+ */
+#ifndef FOX_H
+#define FOX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fox_status {
+  FOX_OK = 0,
+  FOX_E_INVALID = 1,      /* bad pointer, size, alignment, dtype combination or workspace */
+  FOX_E_UNSUPPORTED = 2,  /* valid request outside what is implemented (e.g. non-causal) */
+  FOX_E_LAUNCH = 3        /* the HIP runtime rejected a kernel launch */
+} fox_status;
+
+typedef enum fox_dtype { FOX_F32 = 0, FOX_BF16 = 1 } fox_dtype;
+
+/* Flags of fox_attn_fwd / fox_attn_bwd. FOX_CAUSAL is required: the method is defined for
+ * causal sequence modelling only (paperlayer.ai summary, section 6 "CONCLUSION", limitations:
+ * the non-causal case is future work). */
+enum { FOX_CAUSAL = 1u };
+
+/* Cumulative log decay (paper-graph-ui summary, "Hardware-Aware Implementation": c is the
+ * cumulative sum of log f, computed once per head before attention and kept in HBM).
+ *   log_f : [BH, L] fp32 input;  c : [BH, L] fp32 output, c[r, i] = sum_{l<=i} log_f[r, l].
+ * Accumulates in fp64 and rounds once to fp32. c may not alias log_f. */
+fox_status fox_logf_cumsum(const float* log_f, float* c, int64_t BH, int64_t L, void* stream);
+
+/* Scalar per-head forget gate in log space (paper-graph-ui summary, "Forget Gate Computation";
+ * Pro block Step 4): log_f[b, h, t] = log sigmoid(sum_d x[b, t, d] * w_f[h, d] + b_f[h]).
+ *   x   : [B, L, d_model], dtype x_dt (FOX_BF16 or FOX_F32)
+ *   w_f : [H, d_model] fp32;  b_f : [H] fp32;  log_f : [B, H, L] fp32 output.
+ * fp32 accumulation; log sigmoid is evaluated stably (never as log of a rounded sigmoid).
+ * d_model must be a multiple of 8 and at most 8192; H at most 64. */
+fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
+                         float* log_f, int64_t B, int64_t L, int64_t d_model, int64_t H,
+                         void* stream);
+
+/* QK-norm (Pro block Steps 1-2: RMSNorm over the head dimension of each query and key):
+ *   y[r, :] = x[r, :] / sqrt(mean_d x[r, d]^2 + eps) * (weight ? weight[:] : 1)
+ *   x, y : [rows, D] in dtype dt (same dtype in and out; y may equal x for in-place);
+ *   weight : [D] fp32 or NULL for unit weights. fp32 arithmetic, one rounding on output.
+ * Call once for q and once for k ([B*H*L, D] each). */
+fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, int64_t D,
+                          float eps, const float* weight, void* stream);
+
+/* Forward (paper-graph-ui summary, "Hardware-Aware Implementation", the forward pass;
+ * paperlayer.ai summary, section E):
+ *   O[i]   = sum_{j<=i} softmax_j(scale * q_i . k_j + c_i - c_j) v_j
+ *   lse[i] = log sum_{j<=i} exp(scale * q_i . k_j + c_i - c_j)     (natural log, fp32)
+ * The scale multiplies q.k only; the bias is added unscaled. Only differences of c matter,
+ * so any per-(b,h) constant offset in c leaves O and lse unchanged.
+ *   q, k, v : in_dt (FOX_BF16, or FOX_F32 for the full-fp32 path);  c : fp32
+ *   o       : o_dt (FOX_BF16 or FOX_F32; must be FOX_F32 when in_dt is FOX_F32)
+ *   lse     : fp32, may be NULL if not wanted.
+ * bf16 inputs run on bf16 MFMA with fp32 accumulation and an fp32 online softmax; fp32
+ * inputs run fully in fp32. flags must contain FOX_CAUSAL. */
+fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                        const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
+                        int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
+                        void* stream);
+
+/* Bytes of device workspace fox_attn_bwd needs for these sizes (caller-allocated). */
+size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
+
+/* Backward of the loss sum(dO * O) (paper-graph-ui summary, "Hardware-Aware Implementation",
+ * the backward pass; paperlayer.ai summary, section E): recomputes P from lse with the same
+ * bias, and returns
+ *   dq, dk, dv : [B, H, L, D] fp32
+ *   dlog_f     : [B, H, L] fp32, the reverse cumulative sum of dc = dc^q + dc^k with
+ *                dc^q_i = sum_j dS_ij and dc^k_j = -sum_i dS_ij.
+ * Inputs: q, k, v, dO in in_dt (FOX_BF16 only); c and lse as given to / returned by
+ * fox_attn_fwd; o is the forward output in fp32 (the row term Delta_i = dO_i . O_i is formed
+ * from the fp32 output). workspace: device memory of at least
+ * fox_attn_bwd_workspace_bytes(B, H, L, D) bytes, 256-byte aligned, contents ignored on
+ * entry and clobbered. Deterministic: identical inputs give bit-identical outputs. */
+fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                        const float* c, const float* o, const float* lse, const void* dO,
+                        float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
+                        size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
+                        float scale, uint32_t flags, void* stream);
+
+/* The four steps of fox_attn_bwd as separate calls, for callers that schedule them
+ * themselves. Running them in this order with the same arguments gives exactly fox_attn_bwd's
+ * results.
+ *
+ * Step 1, Delta_i = sum_d dO[i, d] * O[i, d] (the FlashAttention row term that dS needs):
+ *   dO : [rows, D] in dO_dt (FOX_BF16);  o : [rows, D] fp32;  delta : [rows] fp32. */
+fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, float* delta,
+                              int64_t rows, int64_t D, void* stream);
+
+/* Step 2, query-stationary: dq ([B,H,L,D] fp32), dc_q[i] = sum_j dS_ij ([B,H,L] fp32), and
+ * delta_out ([B,H,L] fp32, may equal delta): the row term refined so that each row of dS sums to
+ * zero under the P and dP this library recomputes. The forward rounds P to bf16 before the PV
+ * product, so dO . O matches sum_j P_ij dP_ij only to ~1e-3 relative; d log f sums that
+ * residual over every row that attends across a position, hence the refinement. */
+fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                           const float* c, const float* lse, const void* dO, const float* delta,
+                           float* dq, float* dc_q, float* delta_out, int64_t B, int64_t H,
+                           int64_t L, int64_t D, float scale, uint32_t flags, void* stream);
+
+/* Step 3, key-stationary: dk, dv ([B,H,L,D] fp32) and dc_k[j] = -sum_i dS_ij ([B,H,L] fp32).
+ * delta must be step 2's delta_out; the other inputs as for fox_attn_bwd. */
+fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                            const float* c, const float* lse, const void* dO, const float* delta,
+                            float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
+                            int64_t D, float scale, uint32_t flags, void* stream);
+
+/* Step 4, d log f[r, l] = sum_{t>=l} (dc_q[r, t] + dc_k[r, t]): the gradient of the prefix sum
+ * fox_logf_cumsum computes, applied to dc = dc^q + dc^k ([BH, L] fp32 each; fp64 accumulation,
+ * one rounding). dlog_f may not alias dc_q or dc_k. */
+fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f, int64_t BH,
+                             int64_t L, void* stream);
+
+/* Static description of a status code. */
+const char* fox_status_str(fox_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
+const char* fox_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* fox_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOX_H */

@@ -1,0 +1,65 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, compare against the oracle."""
+import math
+import sys
+
+import numpy as np
+import torch
+
+import fox_inputs as fi
+
+# Tolerances of the path (bf16 inputs with fp32 accumulation / the fp32 workload).
+BF16_MAXABS = 2e-2
+BF16_RELL2 = 5e-3
+F32_MAXABS = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Upload the exact values of a (bf16-representable for dtype == 'bf16')."""
+    if dtype == "bf16":
+        return torch.from_numpy(fi.bf16_bits(a)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = got - ref
+    maxabs = float(np.abs(d).max()) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-30)) if d.size else 0.0
+    return maxabs, rel
+
+
+def check(name, got, ref, maxabs=BF16_MAXABS, rel_l2=BF16_RELL2):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    m, r = errors(got, ref)
+    # relative L2 is meaningless for a reference that is (numerically) zero, e.g. dQ at L = 1
+    if rel_l2 is not None and np.linalg.norm(np.asarray(ref, np.float64)) < 1e-6:
+        rel_l2 = None
+    rl = "n/a" if rel_l2 is None else f"{rel_l2:g}"
+    say(f"  {name}: max-abs {m:.3e} (<= {maxabs:g})  rel-L2 {r:.3e} (<= {rl})")
+    assert m <= maxabs, f"{name}: max-abs {m:.3e} > {maxabs:g}"
+    if rel_l2 is not None:
+        assert r <= rel_l2, f"{name}: rel-L2 {r:.3e} > {rel_l2:g}"
+
+
+def sample_rows(L, n, seed, tile=64):
+    """Rows that cover the start, tile edges, the end and random interior rows."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, L - 1, L - 2, min(L - 1, tile - 1), min(L - 1, tile), min(L - 1, 2 * tile + 3),
+             L // 2}
+    rnd = set(rng.integers(0, L, size=n).tolist())
+    return np.array(sorted(r for r in fixed | rnd if 0 <= r < L))
+
+
+def default_scale(D):
+    return 1.0 / math.sqrt(D)

@@ -1,0 +1,115 @@
+"""Host-side tests of the C ABI (CPU only: nothing here launches a kernel).
+
+The library must load, export every function include/fox.h declares, and reject bad arguments
+with the documented status codes before touching the GPU. The argument-validation cases pass
+fake (never dereferenced) device addresses; they run only where no GPU is visible, so a
+validation bug can never turn into a launch on fake pointers.
+"""
+import ctypes
+import os
+
+import pytest
+import torch
+
+import gated_softmax_attention_fox_amd as fox
+
+NO_GPU = not torch.cuda.is_available()
+host_only = pytest.mark.skipif(not NO_GPU, reason="fake-pointer validation cases run without a GPU")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fox.LIB_PATH):
+        import gated_softmax_attention_fox_amd.build as b
+        b.build()
+    return fox.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = fox.header_functions()
+    for n in ("fox_logf_cumsum", "fox_attn_fwd", "fox_attn_bwd", "fox_attn_bwd_workspace_bytes",
+              "fox_gate_logf", "fox_qk_rmsnorm", "fox_status_str", "fox_last_error", "fox_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in fox.header_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.fox_status_str(0) == b"ok"
+    assert lib.fox_status_str(1) == b"invalid argument"
+    assert lib.fox_status_str(2) == b"unsupported request"
+    assert lib.fox_status_str(3) == b"kernel launch failed"
+    assert lib.fox_version().decode().count(".") == 2
+
+
+def test_workspace_size(lib):
+    # three fp32 [B*H*L] regions, each rounded up to 256 bytes
+    assert lib.fox_attn_bwd_workspace_bytes(1, 12, 16384, 128) == 3 * 12 * 16384 * 4
+    assert lib.fox_attn_bwd_workspace_bytes(1, 1, 1, 64) == 3 * 256
+    assert lib.fox_attn_bwd_workspace_bytes(0, 1, 1, 64) == 0
+
+
+P = 0x7f0000000000  # fake, 16-byte aligned, never dereferenced
+
+
+def _fwd(lib, q=P, k=P, v=P, in_dt=1, c=P, o=P, o_dt=1, lse=P, B=1, H=2, L=64, D=128, scale=0.1,
+         flags=1):
+    return lib.fox_attn_fwd(q, k, v, in_dt, c, o, o_dt, lse, B, H, L, D, scale, flags, None)
+
+
+def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o=P):
+    return lib.fox_attn_bwd(P, P, P, in_dt, P, o, P, P, P, P, P, P, ws, ws_bytes, B, H, L, D, 0.1,
+                            flags, None)
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(k=P + 8), 1), (dict(c=0), 1), (dict(o=0), 1), (dict(lse=P + 4), 1),
+    (dict(D=96), 1), (dict(D=256), 1), (dict(L=0), 1), (dict(B=0), 1), (dict(H=-1), 1),
+    (dict(in_dt=7), 1), (dict(o_dt=3), 1), (dict(in_dt=0, o_dt=1), 1), (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1), (dict(flags=0), 2), (dict(flags=3), 2),
+])
+def test_forward_rejects(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.fox_last_error().decode() != ""
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=0), 1), (dict(ws=P + 16), 1), (dict(ws_bytes=100), 1), (dict(in_dt=0), 2),
+    (dict(in_dt=5), 1), (dict(flags=0), 2), (dict(D=32), 1), (dict(o=0), 1),
+])
+def test_backward_rejects(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+    msg = lib.fox_last_error().decode()
+    assert msg
+    if kw.get("ws_bytes") == 100:
+        assert "workspace too small" in msg
+
+
+@host_only
+def test_scan_gate_norm_reject(lib):
+    assert lib.fox_logf_cumsum(0, P, 1, 8, None) == 1
+    assert lib.fox_logf_cumsum(P, P, 1, 8, None) == 1          # aliasing
+    assert lib.fox_logf_cumsum(P, P + 16, 0, 8, None) == 1
+    assert lib.fox_logf_cumsum(P, P + 16, 1, 0, None) == 1
+    assert lib.fox_gate_logf(P, 1, P, P, P, 1, 8, 12, 2, None) == 1   # d_model % 8
+    assert lib.fox_gate_logf(P, 1, P, P, P, 1, 8, 16, 65, None) == 1  # H > 64
+    assert lib.fox_gate_logf(P, 2, P, P, P, 1, 8, 16, 2, None) == 1   # dtype
+    assert lib.fox_qk_rmsnorm(P, P, 1, 10, 96, ctypes.c_float(1e-6), None, None) == 1
+    assert lib.fox_qk_rmsnorm(P, P, 1, 10, 128, ctypes.c_float(-1.0), None, None) == 1
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        fox.load_library(str(tmp_path / "missing.so"))
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    c = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        fox.fox_attn_fwd(x, x, x, c)
