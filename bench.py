@@ -9,10 +9,18 @@ A step runs, on one HIP stream:
 
 Prints ONE JSON line. value = causal fwd+bwd TFLOP/s with the FlashAttention convention:
 fwd = 4*B*H*D*L^2/2 FLOPs (two causal contractions), bwd = 2.5 x fwd (five contractions).
+Every launch in the timed loop is bracketed by events on the stream it runs on, so the
+per-kernel averages and the step time come from the same K steps.
+
+The roofline object covers the kernel with the longest average duration. Its "traffic" (HBM bytes
+per launch) is read from profiles/hbm_traffic.txt, which holds FETCH_SIZE / WRITE_SIZE counter
+readings scaled by a copy kernel of known size; it is null when the kernel's source has changed
+since the counters were taken (the file records a hash of the sources).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +36,17 @@ if ROOT not in sys.path:
 METRIC = "Forgetting-attn fwd(+bwd) causal TFLOP/s @L=16384,D=128; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "gated_softmax_attention_fox_amd", "csrc")
+# sources that define each timed kernel (a change to any of them invalidates its counter data)
+KERNEL_SOURCES = {
+    "fwd": ["attn_fwd.hip", "fox_device.h"],
+    "dq": ["attn_bwd.hip", "fox_device.h"],
+    "dkv": ["attn_bwd.hip", "fox_device.h"],
+    "delta": ["attn_bwd.hip"],
+    "scan": ["scan.hip"],
+    "dlogf": ["scan.hip"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def log(*a):
@@ -39,8 +58,33 @@ def contraction_flops(B, H, L, D):
     return B * H * D * L * L
 
 
-def cpu_baseline(case, seconds_hint=True):
-    """Time the fp64 oracle on one head of the workload (fwd + bwd) on this host's cores."""
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the counter file, or None if absent or stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sec, vals = None, {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line.startswith("[") and line.endswith("]"):
+            sec = line[1:-1]
+        elif "=" in line and not line.startswith("#") and sec == kernel:
+            k, v = (s.strip() for s in line.split("=", 1))
+            vals[k] = v
+    if not vals or vals.get("source_sha256") != source_hash(kernel):
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(case, heads: int):
+    """Time the fp64 oracle (fwd + bwd) on the first `heads` heads of the workload."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -48,16 +92,16 @@ def cpu_baseline(case, seconds_hint=True):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the affinity set numpy's BLAS sees
         threads = len(os.sched_getaffinity(0))
-    sl = (slice(0, 1), slice(0, 1))
+    sl = (slice(0, 1), slice(0, heads))
     s = 1.0 / math.sqrt(case.D)
     t0 = time.perf_counter()
     oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl], scale=s,
                     block=1024)
     dt = time.perf_counter() - t0
-    flops = 7 * contraction_flops(1, 1, case.L, case.D)  # fwd (2) + bwd (5), as for the GPU
+    flops = 7 * contraction_flops(1, heads, case.L, case.D)  # fwd (2) + bwd (5), as for the GPU
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one head (b=0, h=0) of the workload, fwd+bwd in fp64 NumPy: {dt:.2f} s",
-            "seconds": dt}
+            "sample": f"{heads} of the workload's 12 heads (b=0, h=0..{heads - 1}), fwd+bwd in "
+                      f"fp64 NumPy: {dt:.2f} s"}
 
 
 def main():
@@ -66,6 +110,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8,
+                    help="heads of the workload the oracle is timed on (about 1.5 s each)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run 3 device copies of this many MiB (a known-size kernel "
+                         "that scales HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -95,59 +144,53 @@ def main():
     torch.cuda.synchronize()
 
     names = ["scan", "fwd", "delta", "dq", "dkv", "dlogf"]
-    ev = {n: [] for n in names}
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.current_stream(dev)  # the library launches on this stream
 
-    def step(record):
-        def timed(n, fn):
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                r = fn()
-                e1.record(stream)
-                ev[n].append((e0, e1))
-                return r
-            return fn()
-        c = timed("scan", lambda: fox.fox_logf_cumsum(log_f))
-        o, lse = timed("fwd", lambda: fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32))
-        delta = timed("delta", lambda: fox.fox_attn_bwd_delta(do, o))
-        dq, dcq, delta = timed("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta,
-                                                                  delta_out=delta))
-        dk, dv, dck = timed("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta))
-        dlf = timed("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
+    def step(events):
+        def run(n, fn):
+            if events is None:
+                return fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r = fn()
+            e1.record(stream)
+            events.append((n, e0, e1))
+            return r
+        c = run("scan", lambda: fox.fox_logf_cumsum(log_f))
+        o, lse = run("fwd", lambda: fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32))
+        delta = run("delta", lambda: fox.fox_attn_bwd_delta(do, o))
+        dq, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta,
+                                                                delta_out=delta))
+        dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta))
+        dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
         return dq, dk, dv, dlf
 
     for _ in range(args.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
 
-    # timed region 1: the plain step loop (this is `value`)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # the timed region: exactly K steps, every launch bracketed by events on its stream
+    events = []
     torch.cuda.synchronize()
-    t_start.record(stream)
+    t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
-    t_end.record(stream)
+        step(events)
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-
-    # timed region 2: the same steps with an event pair around every launch, per-kernel times
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    kern_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = events[0][1].elapsed_time(events[-1][2]) / args.steps
+    kern_ms = {n: float(np.mean([a.elapsed_time(b) for m, a, b in events if m == n]))
+               for n in names}
 
     unit = contraction_flops(B, H, L, D)
     fwd_flops, bwd_flops = 2 * unit, 5 * unit
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
-    # algorithmic work of each MFMA kernel per launch (causal contractions it must perform)
+    # algorithmic work of each MFMA kernel per launch (the causal contractions it performs)
     kernel_flops = {"fwd": 2 * unit, "dkv": 4 * unit, "dq": 3 * unit}
     dom = max(kernel_flops, key=lambda n: kern_ms[n])
     ach = kernel_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     fwd_tf = kernel_flops["fwd"] / (kern_ms["fwd"] * 1e-3) / 1e12
     fwd_path_tf = fwd_flops / ((kern_ms["fwd"] + kern_ms["scan"]) * 1e-3) / 1e12
+    bwd_ms = sum(kern_ms[n] for n in ("delta", "dq", "dkv", "dlogf"))
 
     out = {
         "metric": METRIC,
@@ -168,17 +211,28 @@ def main():
                    "grad_dtype": "fp32"},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(dom)},
         "fwd": {"kernel_ms": round(kern_ms["fwd"], 4), "tflops": round(fwd_tf, 2),
                 "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                "scan_plus_fwd_tflops": round(fwd_path_tf, 2)},
+                "scan_plus_fwd_tflops": round(fwd_path_tf, 2),
+                "traffic": read_traffic("fwd")},
+        "bwd": {"ms": round(bwd_ms, 4),
+                "tflops_credited": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)},
         "kernel_ms": {n: round(kern_ms[n], 4) for n in names},
+        "host_wall_ms_per_step": round(wall_ms, 4),
     }
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):  # an elementwise kernel that reads n bytes and writes n bytes
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
-        log("timing the oracle on one head (CPU) ...")
-        cb = cpu_baseline(case)
-        cb.pop("seconds")
-        out["cpu_baseline"] = cb
+        log(f"timing the oracle on {args.cpu_heads} heads (CPU) ...")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_heads)
     print(json.dumps(out), flush=True)
 
 
