@@ -35,6 +35,9 @@ namespace fox {
 namespace {
 
 constexpr int kFwdBN = 64;  // keys per LDS tile
+constexpr float kFwdLazy = 8.0f;  // rescale O only when a row max rises by more than this (log2)
+struct First { static constexpr bool value = true; };   // tag: a wave's first (diagonal) tile
+struct Rest { static constexpr bool value = false; };   // tag: every later tile
 
 // NW waves, 32 queries each. K/V/bias tiles are double-buffered in LDS: the global loads of
 // tile t+1 are issued into registers before tile t is computed and stored to the other buffer
@@ -211,6 +214,271 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
+// Software-pipelined variant. Same numerics as fwd_bf16_kernel (8 waves x 32 queries, keys walked
+// from the diagonal backwards, lazy rescaling), but each wave overlaps three 32-key sub-tiles:
+// while it turns the scores of sub-tile j into probabilities (VALU), the matrix cores work on
+// O += V(j-1)^T P(j-1)^T and on S(j+1)^T = K(j+1) Q^T. Sub-tile j is key block
+// (2 kt_last + 1 - j) of 32 keys; LDS holds 64-key tiles (tile t = key tile kt_last - t = sub-tiles
+// 2t and 2t + 1) in rings, one barrier per tile. During iteration t (sub-steps 2t, 2t + 1) the
+// waves read K of tiles t and t + 1, V of tiles t - 1 and t and the bias of tile t, while the
+// copies of K(t + 2), V(t + 1) and the bias of tile t + 1 go global -> LDS (buffer loads straight
+// into LDS, no registers) into buffers nobody reads in iteration t. Tile 0 (the one holding the
+// sequence end, possibly partial) is staged through registers with zero fill instead. A wave's
+// first sub-tile is exactly its diagonal 32-key block, the only one that evaluates the mask.
+template <int D>
+__global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const float* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE, int L, int BH,
+    int n_qt, float sl2e, int o_f32) {
+  constexpr int NW = 8, BM = NW * 32, NT = NW * 64, BN = kFwdBN;
+  constexpr int TILE = BN * D;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = TILE / 8 / NT;         // 16-byte chunks per thread per tensor (register path)
+  constexpr int BLK = TILE * 2 / 1024 / NW;  // 1 KiB DMA blocks per wave per tensor
+  static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) bf16_t k_s[3][TILE];  // K of tile t in k_s[t % 3]
+  __shared__ __attribute__((aligned(16))) bf16_t v_s[3][TILE];  // V of tile t in v_s[t % 3]
+  __shared__ __attribute__((aligned(16))) float ck_s[2][BN];    // bias of tile t in ck_s[t & 1]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int qt = n_qt - 1 - bid / BH;  // longest-first
+  const int q0 = qt * BM;
+  const size_t base = (size_t)bh * L * D;
+  Q += base;
+  K += base;
+  V += base;
+  C += (size_t)bh * L;
+  const float c_ref = C[q0];
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+  const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
+  const int kt_last = q_last / BN;
+  const int n_t = kt_last + 1;             // tiles this workgroup visits
+  const int n_j = 2 * n_t;                 // sub-tiles
+  const bool active = qw <= q_last;        // the wave holds at least one real query
+  const int j0 = 2 * kt_last + 1 - qw / 32;  // the wave's diagonal sub-tile
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(K, (uint32_t)(L * D * 2));
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(V, (uint32_t)(L * D * 2));
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (qi < L) {
+      qf[c] = ld8(Q + (size_t)qi * D + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.f;
+    }
+  }
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) oacc[d] = zero16();
+  float m = 0.f, lsum = 0.f;
+  bf16x8 pb[2];  // P of the previous sub-tile as B operands (two 16-key halves)
+
+  // Tile 0 (keys from kt_last * BN; may run past the sequence end) through registers, zero-filled.
+  {
+    const int k0 = kt_last * BN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      const int key = k0 + idx / CPR, cc = idx % CPR;
+      lds_store8<D>(k_s[0], idx / CPR, cc * 8, ld16_or_zero<D>(K, key, L, cc * 8));
+      lds_store8<D>(v_s[0], idx / CPR, cc * 8, ld16_or_zero<D>(V, key, L, cc * 8));
+    }
+  }
+
+  // Sub-tile j sits in tile j / 2 at rows 32 * (1 - j % 2) of that tile.
+  auto krows = [&](int j) __attribute__((always_inline)) {
+    return &k_s[(j >> 1) % 3][(1 - (j & 1)) * 32 * D];
+  };
+  auto vrows = [&](int j) __attribute__((always_inline)) {
+    return &v_s[(j >> 1) % 3][(1 - (j & 1)) * 32 * D];
+  };
+  auto qk = [&](f32x16& sacc, int j) __attribute__((always_inline)) {
+    const bf16_t* ks = krows(j);
+    sacc = zero16();
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) sacc = mfma32(lds_row8<D>(ks, l32, 16 * c + 8 * h), qf[c], sacc);
+  };
+  auto pv = [&](int j) __attribute__((always_inline)) {
+    const bf16_t* vs = vrows(j);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d)
+        oacc[d] = mfma32(lds_col8<D>(vs, 16 * t, d * 32, lane), pb[t], oacc[d]);
+    }
+  };
+  // Scores of sub-tile j -> P (bf16 B operands) and the running max / sum. First: the wave's
+  // diagonal sub-tile, which is also its first: mask keys after the query, set m from scratch.
+  auto softmax = [&](f32x16& sacc, int j, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool kFirst = decltype(first_tag)::value;
+    const float* cks = &ck_s[(j >> 1) & 1][(1 - (j & 1)) * 32];
+    const int key0 = (2 * kt_last + 1 - j) * 32;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 ck = *reinterpret_cast<const f32x4*>(&cks[8 * i + 4 * h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x;
+        if constexpr (kFirst) {
+          x = fmaf(sacc[4 * i + e], sl2e, -ck[e]);
+          if ((key0 + 8 * i + 4 * h + e) > qi) x = -INFINITY;
+        } else {
+          x = fmaf(sacc[4 * i + e], sl2e, -ck[e]) - m;
+        }
+        sacc[4 * i + e] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = xhalf_max(mx);
+    if constexpr (kFirst) {
+      m = mx;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] -= mx;
+    } else {
+      // scores are already relative to m; raise m only when a row exceeds it by kFwdLazy
+      const bool raise = mx > kFwdLazy;
+      if (__any(raise)) {
+        const float dm = raise ? mx : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-dm);
+        m += dm;
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] -= dm;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[e] = __builtin_amdgcn_exp2f(sacc[e]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      pb[t] = pack_c_half(sacc, t);
+      lsum = rowsum_bf16x8(pb[t], lsum);  // l sums the same rounded P that meets V
+    }
+  };
+
+  auto dma_k = [&](int t) __attribute__((always_inline)) {  // K of (full) tile t
+#pragma unroll
+    for (int b = 0; b < BLK; ++b)
+      dma_tile_block<D>(k_rsrc, k_s[t % 3], (kt_last - t) * BN, wave * BLK + b, lane);
+  };
+  auto dma_v = [&](int t) __attribute__((always_inline)) {  // V of (full) tile t
+#pragma unroll
+    for (int b = 0; b < BLK; ++b)
+      dma_tile_block<D>(v_rsrc, v_s[t % 3], (kt_last - t) * BN, wave * BLK + b, lane);
+  };
+  auto load_bias = [&](int t) __attribute__((always_inline)) {  // bias of tile t, one per thread
+    float creg = 0.f;
+    if (t < n_t && tid < BN) {
+      const int key = (kt_last - t) * BN + tid;
+      creg = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
+    }
+    return creg;
+  };
+  auto publish = [&](int t, float creg) __attribute__((always_inline)) {  // bias of tile t + barrier
+    if (t < n_t && tid < BN) ck_s[t & 1][tid] = creg;
+    wait_dma();
+    __syncthreads();
+  };
+
+  // Phase A, the diagonal band (tiles 0..3, sub-tiles 0..7): every wave's diagonal sub-tile
+  // j0 = 7 - wave (for a full workgroup) lies here, so the waves' pipelines start at different
+  // points; each wave simply runs P(j-1)V, S(j), softmax(j) in order for its sub-tiles j >= j0.
+  // The last P stays in pb for phase B. Iteration t reads K(t), V(t-1), V(t) and the bias of
+  // tile t, and copies K(t+1), V(t+1), the bias of tile t+1 (and at t = 3 also K(5), which phase
+  // B's first iteration needs).
+  f32x16 sa, sb;
+  publish(0, load_bias(0));
+  const int n_a = n_t < 4 ? n_t : 4;
+  for (int t = 0; t < n_a; ++t) {
+    if (t + 1 < n_t) {
+      dma_k(t + 1);
+      dma_v(t + 1);
+    }
+    if (t == 3 && 5 < n_t) dma_k(5);
+    const float creg = load_bias(t + 1);
+    if (active) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int j = 2 * t + s;
+        if (j > j0) pv(j - 1);
+        if (j >= j0) {
+          qk(sa, j);
+          if (j == j0) softmax(sa, j, First{});
+          else softmax(sa, j, Rest{});
+        }
+      }
+    }
+    publish(t + 1, creg);
+  }
+
+  // Phase B, tiles 4..n_t-1: every wave is past its diagonal, and in sub-step j runs
+  // P(j-1)V, softmax(j) and S(j+1) with no branches. Iteration t reads K(t), K(t+1), V(t-1), V(t)
+  // and the bias of tile t, and copies K(t+2), V(t+1) and the bias of tile t+1.
+  if (n_t > 4) {
+    if (active) qk(sa, 8);
+    int t = 4;
+    for (; t + 1 < n_t; ++t) {
+      if (t + 2 < n_t) dma_k(t + 2);
+      dma_v(t + 1);
+      const float creg = load_bias(t + 1);
+      if (active) {
+        pv(2 * t - 1);
+        softmax(sa, 2 * t, Rest{});
+        qk(sb, 2 * t + 1);
+        pv(2 * t);
+        softmax(sb, 2 * t + 1, Rest{});
+        qk(sa, 2 * t + 2);
+      }
+      publish(t + 1, creg);
+    }
+    // last tile: no further scores to start
+    if (active) {
+      pv(2 * t - 1);
+      softmax(sa, 2 * t, Rest{});
+      qk(sb, 2 * t + 1);
+      pv(2 * t);
+      softmax(sb, 2 * t + 1, Rest{});
+    }
+  }
+  if (active) pv(n_j - 1);
+
+  if (!active) return;
+  const float ltot = xhalf_sum(lsum);
+  const float inv = 1.0f / ltot;
+  if (qi < L) {
+    const size_t orow = base + (size_t)qi * D;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = d * 32 + 8 * i + 4 * h;
+        const float y0 = oacc[d][4 * i] * inv, y1 = oacc[d][4 * i + 1] * inv;
+        const float y2 = oacc[d][4 * i + 2] * inv, y3 = oacc[d][4 * i + 3] * inv;
+        if (o_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + col) = make_float4(y0, y1, y2, y3);
+        } else {
+          const uint32_t lo = (uint32_t)f2bf(y0) | ((uint32_t)f2bf(y1) << 16);
+          const uint32_t hi = (uint32_t)f2bf(y2) | ((uint32_t)f2bf(y3) << 16);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(O) + orow + col) = make_uint2(lo, hi);
+        }
+      }
+    }
+    if (h == 0 && LSE) LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + (C[qi] - c_ref);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 constexpr int kF32BM = 32;  // queries per workgroup (one wave, two lanes per query)
 constexpr int kF32BN = 32;  // keys per LDS tile
 
@@ -311,6 +579,22 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const fl
     const char* e = getenv("FOX_FWD_WAVES");
     return (e && atoi(e) == 4) ? 4 : 8;
   }();
+  static const bool pipe = [] {
+    const char* e = getenv("FOX_FWD_IMPL");
+    return !(e && atoi(e) == 0);
+  }();
+  if (pipe) {
+    const int n_qt = (int)((L + 255) / 256);
+    if (D == 64)
+      hipLaunchKernelGGL(fwd_bf16_pipe_kernel<64>, dim3((unsigned)(n_qt * BH)), dim3(512), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L,
+                         (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+    else
+      hipLaunchKernelGGL(fwd_bf16_pipe_kernel<128>, dim3((unsigned)(n_qt * BH)), dim3(512), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L,
+                         (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+    return hipGetLastError();
+  }
   if (D == 64) {
     if (nw == 8) fwd_bf16_go<64, 8>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
     else fwd_bf16_go<64, 4>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);

@@ -137,8 +137,45 @@ __device__ __forceinline__ float rowsum_bf16x8(const bf16x8& v, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
 }
 
-// Sum / max across the two half-waves (lanes l and l ^ 32).
-__device__ __forceinline__ float xhalf_sum(float v) { return v + __shfl_xor(v, 32, 64); }
-__device__ __forceinline__ float xhalf_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+// Sum / max across the two half-waves (lanes l and l ^ 32). v_permlane32_swap on two copies of
+// v returns, in every lane, the pair {v[l % 32], v[l % 32 + 32]}.
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// ---------------------------------------------------------------------------------------------
+// Global -> LDS tile copies that bypass registers (buffer_load_dwordx4 ... lds). A buffer
+// resource spans `bytes` bytes from `base`; reads at or past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave copies 1 KiB of a swizzled [rows x D] bf16 tile: the 1 KiB block `blk` (rows
+// blk * 512 / D onward) of the tile whose first row is global row `row0` of the matrix behind
+// `rsrc`. Lane l fills LDS bytes blk * 1024 + 16 l, which is physical chunk l % (D / 8) of
+// tile row blk * 512 / D + l / (D / 8); it therefore reads logical chunk
+// (l % (D / 8)) ^ swz_key(row) of that row, so the LDS image is the swizzled layout above.
+template <int D>
+__device__ __forceinline__ void dma_tile_block(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, int row0,
+                                               int blk, int lane) {
+  constexpr int CPR = D / 8;
+  const int r = blk * (512 / D) + lane / CPR;
+  const int lc = (lane % CPR) ^ swz_key<D>(r);
+  const int voff = ((row0 + r) * D + lc * 8) * 2;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + blk * 512), 16, voff, 0, 0, 0);
+}
+
+// Wait until every global -> LDS copy this wave issued has landed.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fox
