@@ -27,6 +27,7 @@
 // (each half of the head dimension), K/V tiles of 32 keys in LDS; the logit is
 // scale*(q.k) + (c_i - c_j) in fp32 and the softmax uses expf.
 #include <cstdlib>
+#include <type_traits>
 
 #include "fox_device.h"
 #include "fox_launch.h"
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
   __shared__ __attribute__((aligned(16))) bf16_t k_s[3][TILE];  // K of tile t in k_s[t % 3]
   __shared__ __attribute__((aligned(16))) bf16_t v_s[3][TILE];  // V of tile t in v_s[t % 3]
-  __shared__ __attribute__((aligned(16))) float ck_s[2][BN];    // bias of tile t in ck_s[t & 1]
+  __shared__ __attribute__((aligned(16))) float ck_s[3][BN];    // bias of tile t in ck_s[t % 3]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -291,21 +292,22 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
   }
 
-  // Sub-tile j sits in tile j / 2 at rows 32 * (1 - j % 2) of that tile.
+  // Sub-tile j sits in tile j / 2 at rows 32 * (1 - j % 2) of that tile (odd j: rows 0..31).
   auto krows = [&](int j) __attribute__((always_inline)) {
     return &k_s[(j >> 1) % 3][(1 - (j & 1)) * 32 * D];
   };
   auto vrows = [&](int j) __attribute__((always_inline)) {
     return &v_s[(j >> 1) % 3][(1 - (j & 1)) * 32 * D];
   };
-  auto qk = [&](f32x16& sacc, int j) __attribute__((always_inline)) {
-    const bf16_t* ks = krows(j);
+  auto crows = [&](int j) __attribute__((always_inline)) {
+    return &ck_s[(j >> 1) % 3][(1 - (j & 1)) * 32];
+  };
+  auto qk = [&](f32x16& sacc, const bf16_t* ks) __attribute__((always_inline)) {
     sacc = zero16();
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) sacc = mfma32(lds_row8<D>(ks, l32, 16 * c + 8 * h), qf[c], sacc);
   };
-  auto pv = [&](int j) __attribute__((always_inline)) {
-    const bf16_t* vs = vrows(j);
+  auto pv = [&](const bf16_t* vs) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -313,12 +315,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
         oacc[d] = mfma32(lds_col8<D>(vs, 16 * t, d * 32, lane), pb[t], oacc[d]);
     }
   };
-  // Scores of sub-tile j -> P (bf16 B operands) and the running max / sum. First: the wave's
-  // diagonal sub-tile, which is also its first: mask keys after the query, set m from scratch.
-  auto softmax = [&](f32x16& sacc, int j, auto first_tag) __attribute__((always_inline)) {
+  // Scores of one sub-tile (bias slice cks, first key key0) -> P (bf16 B operands) and the
+  // running max / sum. First: the wave's diagonal sub-tile, which is also its first: mask keys
+  // after the query and set m from scratch.
+  auto softmax = [&](f32x16& sacc, const float* cks, int key0, auto first_tag)
+      __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value;
-    const float* cks = &ck_s[(j >> 1) & 1][(1 - (j & 1)) * 32];
-    const int key0 = (2 * kt_last + 1 - j) * 32;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -367,15 +369,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
   };
 
-  auto dma_k = [&](int t) __attribute__((always_inline)) {  // K of (full) tile t
+  auto dma_k = [&](int t, int slot) __attribute__((always_inline)) {  // K of (full) tile t
 #pragma unroll
     for (int b = 0; b < BLK; ++b)
-      dma_tile_block<D>(k_rsrc, k_s[t % 3], (kt_last - t) * BN, wave * BLK + b, lane);
+      dma_tile_block<D>(k_rsrc, k_s[slot], (kt_last - t) * BN, wave * BLK + b, lane);
   };
-  auto dma_v = [&](int t) __attribute__((always_inline)) {  // V of (full) tile t
+  auto dma_v = [&](int t, int slot) __attribute__((always_inline)) {  // V of (full) tile t
 #pragma unroll
     for (int b = 0; b < BLK; ++b)
-      dma_tile_block<D>(v_rsrc, v_s[t % 3], (kt_last - t) * BN, wave * BLK + b, lane);
+      dma_tile_block<D>(v_rsrc, v_s[slot], (kt_last - t) * BN, wave * BLK + b, lane);
   };
   auto load_bias = [&](int t) __attribute__((always_inline)) {  // bias of tile t, one per thread
     float creg = 0.f;
@@ -385,8 +387,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
     return creg;
   };
-  auto publish = [&](int t, float creg) __attribute__((always_inline)) {  // bias of tile t + barrier
-    if (t < n_t && tid < BN) ck_s[t & 1][tid] = creg;
+  auto publish = [&](int t, int slot, float creg) __attribute__((always_inline)) {
+    if (t < n_t && tid < BN) ck_s[slot][tid] = creg;  // bias of tile t, then the barrier
     wait_dma();
     __syncthreads();
   };
@@ -398,60 +400,77 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   // tile t, and copies K(t+1), V(t+1), the bias of tile t+1 (and at t = 3 also K(5), which phase
   // B's first iteration needs).
   f32x16 sa, sb;
-  publish(0, load_bias(0));
+  publish(0, 0, load_bias(0));
   const int n_a = n_t < 4 ? n_t : 4;
   for (int t = 0; t < n_a; ++t) {
     if (t + 1 < n_t) {
-      dma_k(t + 1);
-      dma_v(t + 1);
+      dma_k(t + 1, (t + 1) % 3);
+      dma_v(t + 1, (t + 1) % 3);
     }
-    if (t == 3 && 5 < n_t) dma_k(5);
+    if (t == 3 && 5 < n_t) dma_k(5, 2);
     const float creg = load_bias(t + 1);
     if (active) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int j = 2 * t + s;
-        if (j > j0) pv(j - 1);
+        if (j > j0) pv(vrows(j - 1));
         if (j >= j0) {
-          qk(sa, j);
-          if (j == j0) softmax(sa, j, First{});
-          else softmax(sa, j, Rest{});
+          qk(sa, krows(j));
+          const int key0 = (2 * kt_last + 1 - j) * 32;
+          if (j == j0) softmax(sa, crows(j), key0, First{});
+          else softmax(sa, crows(j), key0, Rest{});
         }
       }
     }
-    publish(t + 1, creg);
+    publish(t + 1, (t + 1) % 3, creg);
   }
 
   // Phase B, tiles 4..n_t-1: every wave is past its diagonal, and in sub-step j runs
   // P(j-1)V, softmax(j) and S(j+1) with no branches. Iteration t reads K(t), K(t+1), V(t-1), V(t)
-  // and the bias of tile t, and copies K(t+2), V(t+1) and the bias of tile t+1.
+  // and the bias of tile t, and copies K(t+2), V(t+1) and the bias of tile t+1. Slot S = t % 3
+  // holds tile t in every ring; the main loop is unrolled over three tiles so that every slot,
+  // and with it every LDS address, is a compile-time offset from a per-lane pattern.
+  auto tile_step = [&](int t, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    constexpr int S1 = (S + 1) % 3, S2 = (S + 2) % 3;
+    if (t + 2 < n_t) dma_k(t + 2, S2);
+    dma_v(t + 1, S1);
+    const float creg = load_bias(t + 1);
+    if (active) {
+      pv(&v_s[S2][0]);                       // sub-tile 2t - 1: tile t - 1, rows 0..31
+      softmax(sa, &ck_s[S][32], 0, Rest{});  // sub-tile 2t: tile t, rows 32..63
+      qk(sb, &k_s[S][0]);                    // sub-tile 2t + 1: tile t, rows 0..31
+      pv(&v_s[S][32 * D]);                   // sub-tile 2t
+      softmax(sb, &ck_s[S][0], 0, Rest{});   // sub-tile 2t + 1
+      qk(sa, &k_s[S1][32 * D]);              // sub-tile 2t + 2: tile t + 1, rows 32..63
+    }
+    publish(t + 1, S1, creg);
+  };
   if (n_t > 4) {
-    if (active) qk(sa, 8);
+    if (active) qk(sa, &k_s[1][32 * D]);  // sub-tile 8: tile 4 (slot 1), rows 32..63
     int t = 4;
-    for (; t + 1 < n_t; ++t) {
-      if (t + 2 < n_t) dma_k(t + 2);
-      dma_v(t + 1);
+    for (; t + 3 < n_t; t += 3) {  // t % 3 == 1 here
+      tile_step(t, std::integral_constant<int, 1>{});
+      tile_step(t + 1, std::integral_constant<int, 2>{});
+      tile_step(t + 2, std::integral_constant<int, 0>{});
+    }
+    // the last one to three tiles, with run-time slots; the very last starts no new scores
+    for (; t < n_t; ++t) {
+      if (t + 2 < n_t) dma_k(t + 2, (t + 2) % 3);
+      if (t + 1 < n_t) dma_v(t + 1, (t + 1) % 3);
       const float creg = load_bias(t + 1);
       if (active) {
-        pv(2 * t - 1);
-        softmax(sa, 2 * t, Rest{});
-        qk(sb, 2 * t + 1);
-        pv(2 * t);
-        softmax(sb, 2 * t + 1, Rest{});
-        qk(sa, 2 * t + 2);
+        pv(vrows(2 * t - 1));
+        softmax(sa, crows(2 * t), 0, Rest{});
+        qk(sb, krows(2 * t + 1));
+        pv(vrows(2 * t));
+        softmax(sb, crows(2 * t + 1), 0, Rest{});
+        if (t + 1 < n_t) qk(sa, krows(2 * t + 2));
       }
-      publish(t + 1, creg);
-    }
-    // last tile: no further scores to start
-    if (active) {
-      pv(2 * t - 1);
-      softmax(sa, 2 * t, Rest{});
-      qk(sb, 2 * t + 1);
-      pv(2 * t);
-      softmax(sb, 2 * t + 1, Rest{});
+      publish(t + 1, (t + 1) % 3, creg);
     }
   }
-  if (active) pv(n_j - 1);
+  if (active) pv(vrows(n_j - 1));
 
   if (!active) return;
   const float ltot = xhalf_sum(lsum);
