@@ -219,13 +219,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
 // from the diagonal backwards, lazy rescaling), but each wave overlaps three 32-key sub-tiles:
 // while it turns the scores of sub-tile j into probabilities (VALU), the matrix cores work on
 // O += V(j-1)^T P(j-1)^T and on S(j+1)^T = K(j+1) Q^T. Sub-tile j is key block
-// (2 kt_last + 1 - j) of 32 keys; LDS holds 64-key tiles (tile t = key tile kt_last - t = sub-tiles
-// 2t and 2t + 1) in rings, one barrier per tile. During iteration t (sub-steps 2t, 2t + 1) the
-// waves read K of tiles t and t + 1, V of tiles t - 1 and t and the bias of tile t, while the
-// copies of K(t + 2), V(t + 1) and the bias of tile t + 1 go global -> LDS (buffer loads straight
-// into LDS, no registers) into buffers nobody reads in iteration t. Tile 0 (the one holding the
-// sequence end, possibly partial) is staged through registers with zero fill instead. A wave's
-// first sub-tile is exactly its diagonal 32-key block, the only one that evaluates the mask.
+// (2 kt_last + 1 - j) of 32 keys; tile t (64 keys, key tile kt_last - t) holds sub-tiles 2t and
+// 2t + 1.
+//
+// Memory pipeline. K, V and the raw c values of tile t live in LDS ring slot t % 4 (the bias
+// slice of tile t, (c_j - c_ref) log2 e, in slot t % 2). Iteration t reads K(t), K(t + 1),
+// V(t - 1), V(t) and the bias of tile t; it starts the global -> LDS copies of K(t + 3),
+// V(t + 2) and c(t + 3), converts c(t + 1) into the bias of tile t + 1, and ends with a barrier
+// that waits only for the copies started one iteration earlier, so every copy has two
+// iterations to land. The copies are inline-assembly buffer loads the compiler does not track
+// (fox_device.h), which keeps it from stalling the first LDS read after each copy. Tile 0 (the
+// one holding the sequence end, possibly partial) goes through registers with zero fill.
+//
+// Phases. Every wave's diagonal 32-key block lies in tiles 0..3 (the diagonal band); there the
+// waves run P(j-1)V, S(j), softmax(j) one after another from their own first sub-tile, which is
+// the only one that evaluates the causal mask. From tile 4 on all waves are in step and run the
+// pipelined body; its main loop is unrolled over four tiles so that every ring slot is a
+// compile-time constant and every LDS address is a per-lane base register plus an immediate.
 template <int D>
 __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
@@ -235,13 +245,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   constexpr int TILE = BN * D;
   constexpr int CPR = D / 8;
   constexpr int CPT = TILE / 8 / NT;         // 16-byte chunks per thread per tensor (register path)
-  constexpr int BLK = TILE * 2 / 1024 / NW;  // 1 KiB DMA blocks per wave per tensor
+  constexpr int BLK = TILE * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor and tile
+  constexpr int NCOPY = 2 * BLK + 1;         // copies a wave starts per iteration (K, V, c)
   static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
-  __shared__ __attribute__((aligned(16))) bf16_t k_s[3][TILE];  // K of tile t in k_s[t % 3]
-  __shared__ __attribute__((aligned(16))) bf16_t v_s[3][TILE];  // V of tile t in v_s[t % 3]
-  __shared__ __attribute__((aligned(16))) float ck_s[3][BN];    // bias of tile t in ck_s[t % 3]
+  constexpr uint32_t TB = TILE * 2;  // bytes of one K or V tile
+  constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 6 * BN * 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses need it
   const int h = lane >> 5, l32 = lane & 31;
   const int bid = blockIdx.x;
   const int bh = bid % BH;
@@ -257,12 +269,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   const int qi = qw + l32;
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
   const int kt_last = q_last / BN;
-  const int n_t = kt_last + 1;             // tiles this workgroup visits
-  const int n_j = 2 * n_t;                 // sub-tiles
-  const bool active = qw <= q_last;        // the wave holds at least one real query
+  const int n_t = kt_last + 1;               // tiles this workgroup visits
+  const int n_j = 2 * n_t;                   // sub-tiles
+  const bool active = qw <= q_last;          // the wave holds at least one real query
   const int j0 = 2 * kt_last + 1 - qw / 32;  // the wave's diagonal sub-tile
-  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(K, (uint32_t)(L * D * 2));
-  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(V, (uint32_t)(L * D * 2));
+  const i32x4 k_rs = buffer_words(K, (uint32_t)(L * D * 2));
+  const i32x4 v_rs = buffer_words(V, (uint32_t)(L * D * 2));
+  const i32x4 c_rs = buffer_words(C, (uint32_t)(L * 4));
+  const uint32_t sbase = lds_addr(smem);
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -280,51 +294,83 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   float m = 0.f, lsum = 0.f;
   bf16x8 pb[2];  // P of the previous sub-tile as B operands (two 16-key halves)
 
-  // Tile 0 (keys from kt_last * BN; may run past the sequence end) through registers, zero-filled.
-  {
-    const int k0 = kt_last * BN;
+  // ---- copies -------------------------------------------------------------------------------
+  auto copy_kv = [&](const i32x4& rs, uint32_t region, int t, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      const int key = k0 + idx / CPR, cc = idx % CPR;
-      lds_store8<D>(k_s[0], idx / CPR, cc * 8, ld16_or_zero<D>(K, key, L, cc * 8));
-      lds_store8<D>(v_s[0], idx / CPR, cc * 8, ld16_or_zero<D>(V, key, L, cc * 8));
+    for (int b = 0; b < BLK; ++b) {
+      const int blk = wave * BLK + b;
+      const int r = blk * (512 / D) + lane / CPR;
+      const int lc = (lane % CPR) ^ swz_key<D>(r);
+      const uint32_t voff = (uint32_t)(((kt_last - t) * BN + r) * D + lc * 8) * 2;
+      copy16_to_lds(sbase + region + slot * TB + blk * 1024, voff, rs);
     }
-  }
+  };
+  auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {  // 8 values per wave
+    if (lane < 8) {
+      const uint32_t voff = (uint32_t)((kt_last - t) * BN + wave * 8 + lane) * 4;
+      copy4_to_lds(sbase + R_OFF + slot * BN * 4 + wave * 32, voff, c_rs);
+    }
+  };
+  // Iteration t's copies: K(t + 3), V(t + 2), c(t + 3) (full tiles only: t >= 1).
+  auto start_copies = [&](int t, int sk, int sv, int sc) __attribute__((always_inline)) {
+    if (t + 3 < n_t) {
+      copy_kv(k_rs, K_OFF, t + 3, sk);
+      copy_c(t + 3, sc);
+    }
+    if (t + 2 < n_t) copy_kv(v_rs, V_OFF, t + 2, sv);
+  };
+  // Bias slice of tile t + 1 from its raw c values (wave 0).
+  auto convert_c = [&](int t, int sr, int sb) __attribute__((always_inline)) {
+    if (wave == 0 && t + 1 < n_t) {
+      const float cj = *(const __attribute__((address_space(3))) float*)(uintptr_t)(
+          sbase + R_OFF + sr * BN * 4 + lane * 4);
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(sbase + C_OFF + sb * BN * 4 + lane * 4) =
+          (cj - c_ref) * kLog2e;
+    }
+  };
 
-  // Sub-tile j sits in tile j / 2 at rows 32 * (1 - j % 2) of that tile (odd j: rows 0..31).
-  auto krows = [&](int j) __attribute__((always_inline)) {
-    return &k_s[(j >> 1) % 3][(1 - (j & 1)) * 32 * D];
+  // ---- compute stages -----------------------------------------------------------------------
+  uint32_t kp[D / 16], vp[D / 32][2];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) kp[c] = opaque(sbase + K_OFF + row8_off<D>(lane, 16 * c + 8 * h));
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    vp[d][0] = opaque(sbase + V_OFF + col8_off<D>(lane, d * 32, 0));
+    vp[d][1] = opaque(sbase + V_OFF + col8_off<D>(lane, d * 32, 1));
+  }
+  const uint32_t cp = opaque(sbase + C_OFF + 16 * h);
+
+  // Byte offsets of sub-tile j's rows (K and V share the layout) and bias slice.
+  auto kofs = [&](int j) __attribute__((always_inline)) {
+    return (uint32_t)((j >> 1) & 3) * TB + (uint32_t)(1 - (j & 1)) * 32 * D * 2;
   };
-  auto vrows = [&](int j) __attribute__((always_inline)) {
-    return &v_s[(j >> 1) % 3][(1 - (j & 1)) * 32 * D];
+  auto cofs = [&](int j) __attribute__((always_inline)) {
+    return (uint32_t)((j >> 1) & 1) * BN * 4 + (uint32_t)(1 - (j & 1)) * 32 * 4;
   };
-  auto crows = [&](int j) __attribute__((always_inline)) {
-    return &ck_s[(j >> 1) % 3][(1 - (j & 1)) * 32];
-  };
-  auto qk = [&](f32x16& sacc, const bf16_t* ks) __attribute__((always_inline)) {
+  auto qk = [&](f32x16& sacc, uint32_t ko) __attribute__((always_inline)) {
     sacc = zero16();
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) sacc = mfma32(lds_row8<D>(ks, l32, 16 * c + 8 * h), qf[c], sacc);
+    for (int c = 0; c < D / 16; ++c) sacc = mfma32(lds_ld16(kp[c] + ko), qf[c], sacc);
   };
-  auto pv = [&](const bf16_t* vs) __attribute__((always_inline)) {
+  auto pv = [&](uint32_t vo) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int d = 0; d < D / 32; ++d)
-        oacc[d] = mfma32(lds_col8<D>(vs, 16 * t, d * 32, lane), pb[t], oacc[d]);
+        oacc[d] = mfma32(lds_tr8(vp[d][0] + vo + t * 16 * D * 2, vp[d][1] + vo + t * 16 * D * 2),
+                         pb[t], oacc[d]);
     }
   };
-  // Scores of one sub-tile (bias slice cks, first key key0) -> P (bf16 B operands) and the
+  // Scores of one sub-tile (bias slice at co, first key key0) -> P (bf16 B operands) and the
   // running max / sum. First: the wave's diagonal sub-tile, which is also its first: mask keys
   // after the query and set m from scratch.
-  auto softmax = [&](f32x16& sacc, const float* cks, int key0, auto first_tag)
+  auto softmax = [&](f32x16& sacc, uint32_t co, int key0, auto first_tag)
       __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 ck = *reinterpret_cast<const f32x4*>(&cks[8 * i + 4 * h]);
+      const f32x4 ck = lds_ldf4(cp + co + 32 * i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x;
@@ -369,108 +415,90 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
   };
 
-  auto dma_k = [&](int t, int slot) __attribute__((always_inline)) {  // K of (full) tile t
+  // ---- prologue: tile 0 through registers; copies of K(1), K(2), V(1), c(1), c(2) -------------
+  {
+    const int k0 = kt_last * BN;
 #pragma unroll
-    for (int b = 0; b < BLK; ++b)
-      dma_tile_block<D>(k_rsrc, k_s[slot], (kt_last - t) * BN, wave * BLK + b, lane);
-  };
-  auto dma_v = [&](int t, int slot) __attribute__((always_inline)) {  // V of (full) tile t
-#pragma unroll
-    for (int b = 0; b < BLK; ++b)
-      dma_tile_block<D>(v_rsrc, v_s[slot], (kt_last - t) * BN, wave * BLK + b, lane);
-  };
-  auto load_bias = [&](int t) __attribute__((always_inline)) {  // bias of tile t, one per thread
-    float creg = 0.f;
-    if (t < n_t && tid < BN) {
-      const int key = (kt_last - t) * BN + tid;
-      creg = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      const int key = k0 + idx / CPR, cc = idx % CPR;
+      lds_store8<D>((bf16_t*)(smem + K_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(K, key, L, cc * 8));
+      lds_store8<D>((bf16_t*)(smem + V_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(V, key, L, cc * 8));
     }
-    return creg;
-  };
-  auto publish = [&](int t, int slot, float creg) __attribute__((always_inline)) {
-    if (t < n_t && tid < BN) ck_s[slot][tid] = creg;  // bias of tile t, then the barrier
-    wait_dma();
-    __syncthreads();
-  };
+    if (tid < BN) {
+      const int key = k0 + tid;
+      ((float*)(smem + C_OFF))[tid] = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
+    }
+    if (1 < n_t) {
+      copy_kv(k_rs, K_OFF, 1, 1);
+      copy_kv(v_rs, V_OFF, 1, 1);
+      copy_c(1, 1);
+    }
+    if (2 < n_t) {
+      copy_kv(k_rs, K_OFF, 2, 2);
+      copy_c(2, 2);
+    }
+    bar_vm<0>();
+  }
 
-  // Phase A, the diagonal band (tiles 0..3, sub-tiles 0..7): every wave's diagonal sub-tile
-  // j0 = 7 - wave (for a full workgroup) lies here, so the waves' pipelines start at different
-  // points; each wave simply runs P(j-1)V, S(j), softmax(j) in order for its sub-tiles j >= j0.
-  // The last P stays in pb for phase B. Iteration t reads K(t), V(t-1), V(t) and the bias of
-  // tile t, and copies K(t+1), V(t+1), the bias of tile t+1 (and at t = 3 also K(5), which phase
-  // B's first iteration needs).
+  // ---- phase A: the diagonal band, tiles 0..3 -----------------------------------------------
   f32x16 sa, sb;
-  publish(0, 0, load_bias(0));
   const int n_a = n_t < 4 ? n_t : 4;
   for (int t = 0; t < n_a; ++t) {
-    if (t + 1 < n_t) {
-      dma_k(t + 1, (t + 1) % 3);
-      dma_v(t + 1, (t + 1) % 3);
-    }
-    if (t == 3 && 5 < n_t) dma_k(5, 2);
-    const float creg = load_bias(t + 1);
+    start_copies(t, (t + 3) & 3, (t + 2) & 3, (t + 3) & 3);
+    convert_c(t, (t + 1) & 3, (t + 1) & 1);
     if (active) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int j = 2 * t + s;
-        if (j > j0) pv(vrows(j - 1));
+        if (j > j0) pv(kofs(j - 1));
         if (j >= j0) {
-          qk(sa, krows(j));
+          qk(sa, kofs(j));
           const int key0 = (2 * kt_last + 1 - j) * 32;
-          if (j == j0) softmax(sa, crows(j), key0, First{});
-          else softmax(sa, crows(j), key0, Rest{});
+          if (j == j0) softmax(sa, cofs(j), key0, First{});
+          else softmax(sa, cofs(j), key0, Rest{});
         }
       }
     }
-    publish(t + 1, (t + 1) % 3, creg);
+    bar_vm<0>();
   }
 
-  // Phase B, tiles 4..n_t-1: every wave is past its diagonal, and in sub-step j runs
-  // P(j-1)V, softmax(j) and S(j+1) with no branches. Iteration t reads K(t), K(t+1), V(t-1), V(t)
-  // and the bias of tile t, and copies K(t+2), V(t+1) and the bias of tile t+1. Slot S = t % 3
-  // holds tile t in every ring; the main loop is unrolled over three tiles so that every slot,
-  // and with it every LDS address, is a compile-time offset from a per-lane pattern.
-  auto tile_step = [&](int t, auto slot_tag) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot_tag)::value;
-    constexpr int S1 = (S + 1) % 3, S2 = (S + 2) % 3;
-    if (t + 2 < n_t) dma_k(t + 2, S2);
-    dma_v(t + 1, S1);
-    const float creg = load_bias(t + 1);
-    if (active) {
-      pv(&v_s[S2][0]);                       // sub-tile 2t - 1: tile t - 1, rows 0..31
-      softmax(sa, &ck_s[S][32], 0, Rest{});  // sub-tile 2t: tile t, rows 32..63
-      qk(sb, &k_s[S][0]);                    // sub-tile 2t + 1: tile t, rows 0..31
-      pv(&v_s[S][32 * D]);                   // sub-tile 2t
-      softmax(sb, &ck_s[S][0], 0, Rest{});   // sub-tile 2t + 1
-      qk(sa, &k_s[S1][32 * D]);              // sub-tile 2t + 2: tile t + 1, rows 32..63
-    }
-    publish(t + 1, S1, creg);
+  // ---- phase B: tiles 4..n_t-1, every wave past its diagonal --------------------------------
+  // Iteration t: P(2t-1)V, softmax(2t), S(2t+1), P(2t)V, softmax(2t+1), S(2t+2).
+  auto tile_body = [&](uint32_t ko_t, uint32_t ko_t1, uint32_t vo_tm1, uint32_t co_t, bool next)
+      __attribute__((always_inline)) {
+    pv(vo_tm1);                                  // sub-tile 2t - 1: tile t - 1, rows 0..31
+    softmax(sa, co_t + 32 * 4, 0, Rest{});       // sub-tile 2t: tile t, rows 32..63
+    qk(sb, ko_t);                                // sub-tile 2t + 1: tile t, rows 0..31
+    pv(ko_t + 32 * D * 2);                       // sub-tile 2t
+    softmax(sb, co_t, 0, Rest{});                // sub-tile 2t + 1
+    if (next) qk(sa, ko_t1 + 32 * D * 2);        // sub-tile 2t + 2: tile t + 1, rows 32..63
+  };
+  auto steady = [&](int t, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;  // t % 4
+    start_copies(t, (S + 3) & 3, (S + 2) & 3, (S + 3) & 3);
+    convert_c(t, (S + 1) & 3, (S + 1) & 1);
+    if (active) tile_body(S * TB, ((S + 1) & 3) * TB, ((S + 3) & 3) * TB, (S & 1) * BN * 4, true);
+    bar_vm<NCOPY>();
   };
   if (n_t > 4) {
-    if (active) qk(sa, &k_s[1][32 * D]);  // sub-tile 8: tile 4 (slot 1), rows 32..63
+    if (active) qk(sa, kofs(8));
     int t = 4;
-    for (; t + 3 < n_t; t += 3) {  // t % 3 == 1 here
-      tile_step(t, std::integral_constant<int, 1>{});
-      tile_step(t + 1, std::integral_constant<int, 2>{});
-      tile_step(t + 2, std::integral_constant<int, 0>{});
+    for (; t + 6 < n_t; t += 4) {  // all copies of the four iterations exist; t % 4 == 0
+      steady(t, std::integral_constant<int, 0>{});
+      steady(t + 1, std::integral_constant<int, 1>{});
+      steady(t + 2, std::integral_constant<int, 2>{});
+      steady(t + 3, std::integral_constant<int, 3>{});
     }
-    // the last one to three tiles, with run-time slots; the very last starts no new scores
-    for (; t < n_t; ++t) {
-      if (t + 2 < n_t) dma_k(t + 2, (t + 2) % 3);
-      if (t + 1 < n_t) dma_v(t + 1, (t + 1) % 3);
-      const float creg = load_bias(t + 1);
-      if (active) {
-        pv(vrows(2 * t - 1));
-        softmax(sa, crows(2 * t), 0, Rest{});
-        qk(sb, krows(2 * t + 1));
-        pv(vrows(2 * t));
-        softmax(sb, crows(2 * t + 1), 0, Rest{});
-        if (t + 1 < n_t) qk(sa, krows(2 * t + 2));
-      }
-      publish(t + 1, (t + 1) % 3, creg);
+    for (; t < n_t; ++t) {  // the last few tiles, run-time slots
+      start_copies(t, (t + 3) & 3, (t + 2) & 3, (t + 3) & 3);
+      convert_c(t, (t + 1) & 3, (t + 1) & 1);
+      if (active)
+        tile_body(kofs(2 * t + 1), kofs(2 * t + 3), kofs(2 * t - 1), cofs(2 * t + 1), t + 1 < n_t);
+      bar_vm<0>();
     }
   }
-  if (active) pv(vrows(n_j - 1));
+  if (active) pv(kofs(n_j - 1));
 
   if (!active) return;
   const float ltot = xhalf_sum(lsum);

@@ -175,7 +175,93 @@ __device__ __forceinline__ void dma_tile_block(__amdgpu_buffer_rsrc_t rsrc, bf16
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + blk * 512), 16, voff, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------------------------
+// LDS reads from a per-lane base address plus a compile-time offset. A kernel computes each
+// lane's swizzled byte address once, hides it from the optimiser with opaque(), and adds only
+// constants inside its loops: the constant then folds into the 16-bit offset field of the DS
+// instruction, so a read costs no address arithmetic.
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {  // LDS byte address of a __shared__ object
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+__device__ __forceinline__ bf16x8 lds_ld16(uint32_t a) { return *(const lds_bf16x8*)(uintptr_t)a; }
+__device__ __forceinline__ f32x4 lds_ldf4(uint32_t a) { return *(const lds_f32x4*)(uintptr_t)a; }
+// Two transposed 8-byte reads (rows r and r + 8 of a lds_col8 pattern) as one B-layout operand.
+__device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
+  const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+// Byte offsets inside a swizzled tile of the reads lds_row8(base, row = lane % 32, col) and
+// lds_col8(base, r0 = 0, cbase, lane) issue (the second of the latter at row + 8). Adding
+// 32 * D * 2 * k (row8) or 16 * D * 2 * k (col8) moves them k row blocks down.
+template <int D>
+__device__ __forceinline__ uint32_t row8_off(int lane, int col) {
+  return (uint32_t)swz<D>(lane & 31, col) * 2;
+}
+template <int D>
+__device__ __forceinline__ uint32_t col8_off(int lane, int cbase, int second) {
+  const int row = 4 * (lane >> 5) + ((lane & 15) >> 2) + 8 * second;
+  const int col = cbase + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return (uint32_t)swz<D>(row, col) * 2;
+}
+
 // Wait until every global -> LDS copy this wave issued has landed.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------------
+// Global -> LDS copies issued as inline assembly. The compiler does not track them, so it never
+// inserts the conservative vmcnt(0) it would place before every LDS read that might alias a
+// tracked copy; the kernel instead waits explicitly with bar_vm<N>(), which lets the N most
+// recently issued copies stay in flight across the barrier (vector memory loads complete in
+// issue order). A kernel using these must issue no compiler-visible vector memory load between
+// a copy and the wait that covers it.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: `bytes` bytes from `base`, reads at or past the end return zero.
+__device__ __forceinline__ i32x4 buffer_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = (int)(uint32_t)a;
+  r[1] = (int)(uint32_t)(a >> 32);  // stride 0
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+// Each active lane copies 16 bytes from byte offset voff of the buffer to LDS byte address
+// lds + 16 * lane (lds must be wave-uniform). M0 is saved and restored.
+__device__ __forceinline__ void copy16_to_lds(uint32_t lds, uint32_t voff, i32x4 rs) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+// Same with 4 bytes per lane (LDS byte address lds + 4 * lane).
+__device__ __forceinline__ void copy4_to_lds(uint32_t lds, uint32_t voff, i32x4 rs) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+// Workgroup barrier after this wave's LDS accesses have completed and all but its N most recent
+// copies have landed.
+template <int N>
+__device__ __forceinline__ void bar_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 }  // namespace fox
