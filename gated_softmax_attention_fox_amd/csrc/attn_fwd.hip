@@ -361,35 +361,48 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
                          pb[t], oacc[d]);
     }
   };
-  // Scores of one sub-tile (bias slice at co, first key key0) -> P (bf16 B operands) and the
-  // running max / sum. First: the wave's diagonal sub-tile, which is also its first: mask keys
-  // after the query and set m from scratch.
-  auto softmax = [&](f32x16& sacc, uint32_t co, int key0, auto first_tag)
+  // The bias values a lane needs for one sub-tile (keys 8i + 4h + e of its bias slice at co).
+  auto bias_vals = [&](f32x4 (&ck)[4], uint32_t co) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ck[i] = lds_ldf4(cp + co + 32 * i);
+  };
+  // Scores of one sub-tile (bias values ck, first key key0) -> P (bf16 B operands) and the
+  // running max / sum, in log2 units relative to m: y = scale log2(e) q.k - (ck + m). The bias
+  // and m are added first: both can be large when c_ref lies far from the row's own c (a
+  // sequence of strongly closed gates), and for every key that carries weight they nearly
+  // cancel, so their sum is exact and the fma rounds only the small result. First: the wave's
+  // diagonal sub-tile, which is also its first: mask keys after the query, set m from scratch.
+  auto softmax = [&](f32x16& sacc, const f32x4 (&ck)[4], int key0, auto first_tag)
       __attribute__((always_inline)) {
     constexpr bool kFirst = decltype(first_tag)::value;
     float mx = -INFINITY;
+    if constexpr (kFirst) {  // a rough pass for the row max, then the exact form below
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = fmaf(sacc[4 * i + e], sl2e, -ck[i][e]);
+          if ((key0 + 8 * i + 4 * h + e) > qi) x = -INFINITY;
+          mx = fmaxf(mx, x);
+        }
+      }
+      m = xhalf_max(mx);
+      mx = -INFINITY;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 ck = lds_ldf4(cp + co + 32 * i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x;
+        float x = fmaf(sacc[4 * i + e], sl2e, -(ck[i][e] + m));
         if constexpr (kFirst) {
-          x = fmaf(sacc[4 * i + e], sl2e, -ck[e]);
           if ((key0 + 8 * i + 4 * h + e) > qi) x = -INFINITY;
-        } else {
-          x = fmaf(sacc[4 * i + e], sl2e, -ck[e]) - m;
         }
         sacc[4 * i + e] = x;
         mx = fmaxf(mx, x);
       }
     }
     mx = xhalf_max(mx);
-    if constexpr (kFirst) {
-      m = mx;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[e] -= mx;
-    } else {
+    if constexpr (!kFirst) {
       // scores are already relative to m; raise m only when a row exceeds it by kFwdLazy
       const bool raise = mx > kFwdLazy;
       if (__any(raise)) {
@@ -453,10 +466,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
         const int j = 2 * t + s;
         if (j > j0) pv(kofs(j - 1));
         if (j >= j0) {
+          f32x4 ck[4];
+          bias_vals(ck, cofs(j));
           qk(sa, kofs(j));
           const int key0 = (2 * kt_last + 1 - j) * 32;
-          if (j == j0) softmax(sa, cofs(j), key0, First{});
-          else softmax(sa, cofs(j), key0, Rest{});
+          if (j == j0) softmax(sa, ck, key0, First{});
+          else softmax(sa, ck, key0, Rest{});
         }
       }
     }
@@ -467,11 +482,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   // Iteration t: P(2t-1)V, softmax(2t), S(2t+1), P(2t)V, softmax(2t+1), S(2t+2).
   auto tile_body = [&](uint32_t ko_t, uint32_t ko_t1, uint32_t vo_tm1, uint32_t co_t, bool next)
       __attribute__((always_inline)) {
+    f32x4 ck[4];
+    bias_vals(ck, co_t + 32 * 4);                // bias reads ahead of the MFMAs that hide them
     pv(vo_tm1);                                  // sub-tile 2t - 1: tile t - 1, rows 0..31
-    softmax(sa, co_t + 32 * 4, 0, Rest{});       // sub-tile 2t: tile t, rows 32..63
+    softmax(sa, ck, 0, Rest{});                  // sub-tile 2t: tile t, rows 32..63
+    bias_vals(ck, co_t);
     qk(sb, ko_t);                                // sub-tile 2t + 1: tile t, rows 0..31
     pv(ko_t + 32 * D * 2);                       // sub-tile 2t
-    softmax(sb, co_t, 0, Rest{});                // sub-tile 2t + 1
+    softmax(sb, ck, 0, Rest{});                  // sub-tile 2t + 1
     if (next) qk(sa, ko_t1 + 32 * D * 2);        // sub-tile 2t + 2: tile t + 1, rows 32..63
   };
   auto steady = [&](int t, auto slot_tag) __attribute__((always_inline)) {
