@@ -26,6 +26,9 @@
 // one lane, so the backward is deterministic. The C-tile / operand conventions are those of
 // fox_device.h: in dkv_kernel the C tiles are [query x key] with one key per lane, so P and dS
 // are B operands of products that contract over queries; in dq_kernel they are [key x query].
+#include <cstdlib>
+#include <type_traits>
+
 #include "fox_device.h"
 #include "fox_launch.h"
 
@@ -318,6 +321,292 @@ __global__ __launch_bounds__(256) void dq_kernel(
   }
 }
 
+// Query-stationary step with the forward kernel's memory pipeline. 4 waves, one per SIMD (up
+// to 512 registers each), 64 queries per wave as two 32-query blocks that share every K / V
+// operand read; keys are walked from the diagonal backwards in 64-key tiles (two 32-key
+// sub-tiles, sub-tile j = key block 2 kt_last + 1 - j). K, V and raw c of tile t sit in LDS
+// ring slot t % 4 (the bias slice (c_j - c_ref) log2 e of tile t in slot t % 2); iteration t
+// reads K(t), V(t) and the bias of tile t, starts the untracked copies of K(t + 2), V(t + 2)
+// and c(t + 3), converts c(t + 1) into the bias of tile t + 1, and its barrier waits only for
+// the copies started one iteration earlier. Tile 0 (holding the sequence end) goes through
+// registers with zero fill. Per 32-key sub-tile and query block a wave computes S^T = K Q^T
+// and dP^T = V dO^T, then P = exp2(scale log2(e) s - (bias_j + m_i)) with
+// m_i = (LSE_i - (c_i - c_ref)) log2 e (bias and m added first, as in the forward),
+// dS = P (dP - Delta_i), and dQ^T += K^T dS^T with K^T from transposed reads of the K tile.
+// Tiles 0..3 hold every wave's diagonal and evaluate the causal mask; from tile 4 on the loop
+// is unrolled over four tiles so that every LDS address is a per-lane base plus an immediate.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dq_pipe_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
+    const float* Delta, float* __restrict__ dQ, float* __restrict__ dcq_out, float* delta_out,
+    int L, int BH, int n_qt, float sl2e, float scale) {
+  constexpr int NW = 4, BM = NW * 64, NT = NW * 64, BN = 64;
+  constexpr int TILE = BN * D;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = TILE / 8 / NT;
+  constexpr int BLK = TILE * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor and tile
+  constexpr int CW = BN / NW;                // c values each wave copies per tile
+  constexpr int NCOPY = 2 * BLK + 1;
+  static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
+  constexpr uint32_t TB = TILE * 2;
+  constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 6 * BN * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int qt = n_qt - 1 - bid / BH;  // longest-first
+  const int q0 = qt * BM;
+  const size_t base = (size_t)bh * L * D;
+  Q += base;
+  K += base;
+  V += base;
+  dO += base;
+  C += (size_t)bh * L;
+  const float c_ref = C[q0];
+  const int qw = q0 + wave * 64;
+  const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
+  const int kt_last = q_last / BN;
+  const int n_t = kt_last + 1;
+  const bool active = qw <= q_last;
+  const int j0 = max(2 * kt_last - qw / 32, 0);  // first sub-tile with a key <= a query of the wave
+  const i32x4 k_rs = buffer_words(K, (uint32_t)(L * D * 2));
+  const i32x4 v_rs = buffer_words(V, (uint32_t)(L * D * 2));
+  const i32x4 c_rs = buffer_words(C, (uint32_t)(L * 4));
+  const uint32_t sbase = lds_addr(smem);
+
+  int qi[2];
+  bool qok[2];
+  bf16x8 qf[2][D / 16], dof[2][D / 16];
+  float mrow[2], dl[2], dcq[2], psum[2];
+  f32x16 dqacc[2][D / 32];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    qi[b] = qw + 32 * b + l32;
+    qok[b] = qi[b] < L;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      if (qok[b]) {
+        qf[b][c] = ld8(Q + (size_t)qi[b] * D + 16 * c + 8 * h);
+        dof[b][c] = ld8(dO + (size_t)qi[b] * D + 16 * c + 8 * h);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qf[b][c][e] = (__bf16)0.f;
+          dof[b][c][e] = (__bf16)0.f;
+        }
+      }
+    }
+    // rows past the end get P = 0 through an infinite row offset
+    mrow[b] = qok[b] ? (LSE[(size_t)bh * L + qi[b]] - (C[qi[b]] - c_ref)) * kLog2e : INFINITY;
+    dl[b] = qok[b] ? Delta[(size_t)bh * L + qi[b]] : 0.f;
+    dcq[b] = 0.f;
+    psum[b] = 0.f;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) dqacc[b][d] = zero16();
+  }
+
+  auto copy_kv = [&](const i32x4& rs, uint32_t region, int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      const int blk = wave * BLK + k;
+      const int r = blk * (512 / D) + lane / CPR;
+      const int lc = (lane % CPR) ^ swz_key<D>(r);
+      const uint32_t voff = (uint32_t)(((kt_last - t) * BN + r) * D + lc * 8) * 2;
+      copy16_to_lds(sbase + region + slot * TB + blk * 1024, voff, rs);
+    }
+  };
+  auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {
+    if (lane < CW) {
+      const uint32_t voff = (uint32_t)((kt_last - t) * BN + wave * CW + lane) * 4;
+      copy4_to_lds(sbase + R_OFF + slot * BN * 4 + wave * CW * 4, voff, c_rs);
+    }
+  };
+  auto start_copies = [&](int t, int skv, int sc) __attribute__((always_inline)) {
+    if (t + 2 < n_t) {
+      copy_kv(k_rs, K_OFF, t + 2, skv);
+      copy_kv(v_rs, V_OFF, t + 2, skv);
+    }
+    if (t + 3 < n_t) copy_c(t + 3, sc);
+  };
+  auto convert_c = [&](int t, int sr, int sb) __attribute__((always_inline)) {
+    if (wave == 0 && t + 1 < n_t) {
+      const float cj = *(const __attribute__((address_space(3))) float*)(uintptr_t)(
+          sbase + R_OFF + sr * BN * 4 + lane * 4);
+      *(__attribute__((address_space(3))) float*)(uintptr_t)(sbase + C_OFF + sb * BN * 4 + lane * 4) =
+          (cj - c_ref) * kLog2e;
+    }
+  };
+
+  uint32_t kp[D / 16], vq[D / 16], kt[D / 32][2];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    kp[c] = opaque(sbase + K_OFF + row8_off<D>(lane, 16 * c + 8 * h));
+    vq[c] = opaque(sbase + V_OFF + row8_off<D>(lane, 16 * c + 8 * h));
+  }
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    kt[d][0] = opaque(sbase + K_OFF + col8_off<D>(lane, d * 32, 0));
+    kt[d][1] = opaque(sbase + K_OFF + col8_off<D>(lane, d * 32, 1));
+  }
+  const uint32_t cp = opaque(sbase + C_OFF + 16 * h);
+
+  // One 32-key sub-tile for both query blocks: rows at byte offset ro of a K / V slot, bias
+  // slice at co, first key key0 (masking only with kMask).
+  auto sub_tile = [&](uint32_t ro, uint32_t co, int key0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = zero16();
+      dp[b] = zero16();
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 a = lds_ld16(kp[c] + ro);
+      s[0] = mfma32(a, qf[0][c], s[0]);
+      s[1] = mfma32(a, qf[1][c], s[1]);
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const bf16x8 a = lds_ld16(vq[c] + ro);
+      dp[0] = mfma32(a, dof[0][c], dp[0]);
+      dp[1] = mfma32(a, dof[1][c], dp[1]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {  // the VALU reads these: keep them in VGPRs
+      pin_vgpr(s[b]);
+      pin_vgpr(dp[b]);
+    }
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 ck = lds_ldf4(cp + co + 32 * i);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = fmaf(s[b][4 * i + e], sl2e, -(ck[e] + mrow[b]));
+          if constexpr (kMask) {
+            if ((key0 + 8 * i + 4 * h + e) > qi[b]) x = -INFINITY;
+          }
+          const float p = __builtin_amdgcn_exp2f(x);
+          const float ds = p * (dp[b][4 * i + e] - dl[b]);
+          dcq[b] += ds;
+          psum[b] += p;
+          s[b][4 * i + e] = ds;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      sb[b][0] = pack_c_half(s[b], 0);
+      sb[b][1] = pack_c_half(s[b], 1);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        const bf16x8 a = lds_tr8(kt[d][0] + ro + t * 16 * D * 2, kt[d][1] + ro + t * 16 * D * 2);
+        dqacc[0][d] = mfma32(a, sb[0][t], dqacc[0][d]);
+        dqacc[1][d] = mfma32(a, sb[1][t], dqacc[1][d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {  // only the matrix cores touch these until the end
+      pin_agpr(dqacc[0][d]);
+      pin_agpr(dqacc[1][d]);
+    }
+  };
+
+  // prologue: tile 0 through registers (zero fill past the end), copies of K(1), V(1), c(1), c(2)
+  {
+    const int k0 = kt_last * BN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      const int key = k0 + idx / CPR, cc = idx % CPR;
+      lds_store8<D>((bf16_t*)(smem + K_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(K, key, L, cc * 8));
+      lds_store8<D>((bf16_t*)(smem + V_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(V, key, L, cc * 8));
+    }
+    if (tid < BN) {
+      const int key = k0 + tid;
+      ((float*)(smem + C_OFF))[tid] = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
+    }
+    if (1 < n_t) {
+      copy_kv(k_rs, K_OFF, 1, 1);
+      copy_kv(v_rs, V_OFF, 1, 1);
+      copy_c(1, 1);
+    }
+    if (2 < n_t) copy_c(2, 2);
+    bar_vm<0>();
+  }
+
+  // tiles 0..3 (the diagonal band, masked) and the last few tiles: run-time slots
+  auto generic_tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    start_copies(t, (t + 2) & 3, (t + 3) & 3);
+    convert_c(t, (t + 1) & 3, (t + 1) & 1);
+    if (active) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int j = 2 * t + sub;
+        const uint32_t ro = (uint32_t)(t & 3) * TB + (uint32_t)(1 - sub) * 32 * D * 2;
+        const uint32_t co = (uint32_t)(t & 1) * BN * 4 + (uint32_t)(1 - sub) * 32 * 4;
+        if (j >= j0) sub_tile(ro, co, (2 * kt_last + 1 - j) * 32, mask_tag);
+      }
+    }
+    bar_vm<0>();
+  };
+  auto steady_tile = [&](int t, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;  // t % 4
+    start_copies(t, (S + 2) & 3, (S + 3) & 3);
+    convert_c(t, (S + 1) & 3, (S + 1) & 1);
+    if (active) {
+      sub_tile(S * TB + 32 * D * 2, (S & 1) * BN * 4 + 32 * 4, 0, std::false_type{});
+      sub_tile(S * TB, (S & 1) * BN * 4, 0, std::false_type{});
+    }
+    bar_vm<NCOPY>();
+  };
+  int t = 0;
+  for (; t < n_t && t < 4; ++t) generic_tile(t, std::true_type{});
+  for (; t + 6 < n_t; t += 4) {  // t % 4 == 0; every copy of the four iterations exists
+    steady_tile(t, std::integral_constant<int, 0>{});
+    steady_tile(t + 1, std::integral_constant<int, 1>{});
+    steady_tile(t + 2, std::integral_constant<int, 2>{});
+    steady_tile(t + 3, std::integral_constant<int, 3>{});
+  }
+  for (; t < n_t; ++t) generic_tile(t, std::false_type{});
+
+  // Row term consistent with this kernel's own P and dP (see dq_kernel).
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float eps = xhalf_sum(dcq[b]);
+    const float ptot = xhalf_sum(psum[b]);
+    const float dl_new = dl[b] + eps / ptot;
+    const float dcq_tot = eps - (dl_new - dl[b]) * ptot;
+    if (qok[b]) {
+      const size_t row = base + (size_t)qi[b] * D;
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = d * 32 + 8 * i + 4 * h;
+          *reinterpret_cast<float4*>(dQ + row + col) =
+              make_float4(dqacc[b][d][4 * i] * scale, dqacc[b][d][4 * i + 1] * scale,
+                          dqacc[b][d][4 * i + 2] * scale, dqacc[b][d][4 * i + 3] * scale);
+        }
+      }
+      if (h == 0) {
+        dcq_out[(size_t)bh * L + qi[b]] = dcq_tot;
+        delta_out[(size_t)bh * L + qi[b]] = dl_new;
+      }
+    }
+  }
+}
+
 inline size_t region_floats(int64_t BH, int64_t L) {
   return (size_t)((BH * L + 63) / 64 * 64);  // 256-byte granules
 }
@@ -341,6 +630,17 @@ template <int D>
 void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
            const bf16_t* dO, const float* delta, float* dq, float* dcq, float* delta_out,
            int64_t BH, int64_t L, float scale, hipStream_t s) {
+  static const bool pipe = [] {
+    const char* e = getenv("FOX_BWD_IMPL");
+    return !(e && atoi(e) == 0);
+  }();
+  if (pipe) {
+    const int n_qt = (int)((L + 255) / 256);
+    hipLaunchKernelGGL(dq_pipe_kernel<D>, dim3((unsigned)(n_qt * BH)), dim3(256), 0, s, q, k, v,
+                       dO, c, lse, delta, dq, dcq, delta_out, (int)L, (int)BH, n_qt,
+                       scale * kLog2e, scale);
+    return;
+  }
   const int n_qt = (int)((L + kQBM - 1) / kQBM);
   hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(n_qt * BH)), dim3(256), 0, s, q, k, v, dO, c,
                      lse, delta, dq, dcq, delta_out, (int)L, (int)BH, n_qt, scale * kLog2e, scale);

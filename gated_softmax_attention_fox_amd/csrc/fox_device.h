@@ -214,6 +214,12 @@ __device__ __forceinline__ uint32_t col8_off(int lane, int cbase, int second) {
   return (uint32_t)swz<D>(row, col) * 2;
 }
 
+// Register-file hints for the allocator (no instruction is emitted): accumulators only the
+// matrix cores touch stay in AGPRs, MFMA results the vector ALU reads stay in VGPRs, so no
+// v_accvgpr moves are needed between them.
+__device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
+__device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
+
 // Wait until every global -> LDS copy this wave issued has landed.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
