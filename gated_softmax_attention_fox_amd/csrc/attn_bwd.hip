@@ -321,6 +321,258 @@ __global__ __launch_bounds__(256) void dq_kernel(
   }
 }
 
+// Key-stationary step with the forward kernel's memory pipeline. 4 waves, one per SIMD, 32 keys
+// per wave (K^T and V^T held as MFMA operands, dK^T and dV^T accumulated in registers), 128 keys
+// per workgroup. Queries are walked upwards from the diagonal in 64-query tiles (tile t =
+// queries k0 + 64 t .., two 32-query sub-tiles). Q and dO of tile t and its raw c, LSE and
+// Delta values sit in LDS ring slot t % 4, the converted row terms m_i =
+// (LSE_i - (c_i - c_ref)) log2 e and Delta_i in slot t % 2; iteration t reads tile t, starts the
+// untracked copies of Q(t + 2), dO(t + 2) and the raw row values of tile t + 3, converts those of
+// tile t + 1, and its barrier waits only for the copies started one iteration earlier. Past the
+// sequence end the copies read zeros and m_i is +inf, so P is zero there. Per 32-query sub-tile
+// a wave computes S = Q K^T and dP = dO V^T (one key per lane), P = exp2(scale log2(e) s -
+// (k_j + m_i)) with k_j = (c_j - c_ref) log2 e (the two terms added first), dS = P (dP - Delta_i),
+// dc^k_j -= sum_i dS_ij from the fp32 dS, and dV^T += dO^T P, dK^T += Q^T dS with the transposes
+// read from the row-major tiles. Tiles 0 and 1 hold every wave's diagonal and evaluate the
+// causal mask; from tile 2 on the loop is unrolled over four tiles for compile-time slots.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkv_pipe_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
+    const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV,
+    float* __restrict__ dck_out, int L, int BH, float sl2e, float scale) {
+  constexpr int NW = 4, BK = NW * 32, BQ = 64;
+  constexpr int TILE = BQ * D;
+  constexpr int CPR = D / 8;
+  constexpr int BLK = TILE * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor and tile
+  constexpr int RW = BQ / NW;                // row values each wave copies per array and tile
+  constexpr int NCOPY = 2 * BLK + 3;
+  static_assert(BLK >= 1, "tile must split evenly over the waves");
+  constexpr uint32_t TB = TILE * 2;
+  constexpr uint32_t Q_OFF = 0, O_OFF = 4 * TB, R_OFF = 8 * TB, M_OFF = 8 * TB + 4 * 3 * BQ * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 4 * 3 * BQ * 4 + 2 * 2 * BQ * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int kt = bid / BH;  // key tile 0 sees every query tile: issued first
+  const int k0 = kt * BK;
+  const size_t base = (size_t)bh * L * D;
+  Q += base;
+  K += base;
+  V += base;
+  dO += base;
+  C += (size_t)bh * L;
+  LSE += (size_t)bh * L;
+  Delta += (size_t)bh * L;
+  const float c_ref = C[k0];
+  const int kw = k0 + wave * 32;
+  const int kj = kw + l32;
+  const bool kok = kj < L;
+  const bool active = kw < L;
+  const int n_t = (L - k0 + BQ - 1) / BQ;  // query tiles from the diagonal to the end
+  const int j0 = wave;                     // the wave's diagonal sub-tile (queries kw .. kw + 31)
+  const i32x4 q_rs = buffer_words(Q, (uint32_t)(L * D * 2));
+  const i32x4 o_rs = buffer_words(dO, (uint32_t)(L * D * 2));
+  const i32x4 c_rs = buffer_words(C, (uint32_t)(L * 4));
+  const i32x4 l_rs = buffer_words(LSE, (uint32_t)(L * 4));
+  const i32x4 d_rs = buffer_words(Delta, (uint32_t)(L * 4));
+  const uint32_t sbase = lds_addr(smem);
+
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (kok) {
+      kf[c] = ld8(K + (size_t)kj * D + 16 * c + 8 * h);
+      vf[c] = ld8(V + (size_t)kj * D + 16 * c + 8 * h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        kf[c][e] = (__bf16)0.f;
+        vf[c][e] = (__bf16)0.f;
+      }
+    }
+  }
+  const float kterm = kok ? (C[kj] - c_ref) * kLog2e : 0.f;
+  f32x16 dvacc[D / 32], dkacc[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    dvacc[d] = zero16();
+    dkacc[d] = zero16();
+  }
+  float dck = 0.f;
+
+  auto copy_tile = [&](const i32x4& rs, uint32_t region, int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      const int blk = wave * BLK + k;
+      const int r = blk * (512 / D) + lane / CPR;
+      const int lc = (lane % CPR) ^ swz_key<D>(r);
+      const uint32_t voff = (uint32_t)((k0 + t * BQ + r) * D + lc * 8) * 2;
+      copy16_to_lds(sbase + region + slot * TB + blk * 1024, voff, rs);
+    }
+  };
+  auto copy_rows = [&](int t, int slot) __attribute__((always_inline)) {  // raw c, LSE, Delta
+    if (lane < RW) {
+      const uint32_t voff = (uint32_t)(k0 + t * BQ + wave * RW + lane) * 4;
+      const uint32_t dst = sbase + R_OFF + slot * 3 * BQ * 4 + wave * RW * 4;
+      copy4_to_lds(dst, voff, c_rs);
+      copy4_to_lds(dst + BQ * 4, voff, l_rs);
+      copy4_to_lds(dst + 2 * BQ * 4, voff, d_rs);
+    }
+  };
+  auto start_copies = [&](int t, int sqo, int sr) __attribute__((always_inline)) {
+    if (t + 2 < n_t) {
+      copy_tile(q_rs, Q_OFF, t + 2, sqo);
+      copy_tile(o_rs, O_OFF, t + 2, sqo);
+    }
+    if (t + 3 < n_t) copy_rows(t + 3, sr);
+  };
+  // Row terms of tile t + 1 from its raw values (wave 0, one query per lane).
+  auto convert_rows = [&](int t, int sr, int sm) __attribute__((always_inline)) {
+    if (wave == 0 && t + 1 < n_t) {
+      typedef __attribute__((address_space(3))) float lds_f;
+      const uint32_t src = sbase + R_OFF + sr * 3 * BQ * 4 + lane * 4;
+      const float ci = *(const lds_f*)(uintptr_t)src;
+      const float li = *(const lds_f*)(uintptr_t)(src + BQ * 4);
+      const float di = *(const lds_f*)(uintptr_t)(src + 2 * BQ * 4);
+      const bool ok = k0 + (t + 1) * BQ + lane < L;
+      const uint32_t dst = sbase + M_OFF + sm * 2 * BQ * 4 + lane * 4;
+      *(lds_f*)(uintptr_t)dst = ok ? (li - (ci - c_ref)) * kLog2e : INFINITY;
+      *(lds_f*)(uintptr_t)(dst + BQ * 4) = ok ? di : 0.f;
+    }
+  };
+
+  uint32_t qp[D / 16], op[D / 16], qtp[D / 32][2], otp[D / 32][2];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    qp[c] = opaque(sbase + Q_OFF + row8_off<D>(lane, 16 * c + 8 * h));
+    op[c] = opaque(sbase + O_OFF + row8_off<D>(lane, 16 * c + 8 * h));
+  }
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    qtp[d][0] = opaque(sbase + Q_OFF + col8_off<D>(lane, d * 32, 0));
+    qtp[d][1] = opaque(sbase + Q_OFF + col8_off<D>(lane, d * 32, 1));
+    otp[d][0] = opaque(sbase + O_OFF + col8_off<D>(lane, d * 32, 0));
+    otp[d][1] = opaque(sbase + O_OFF + col8_off<D>(lane, d * 32, 1));
+  }
+  const uint32_t mp = opaque(sbase + M_OFF + 16 * h);
+
+  // One 32-query sub-tile: rows at byte offset ro of a Q / dO slot, row terms at mo, first
+  // query q0s (masking only with kMask).
+  auto sub_tile = [&](uint32_t ro, uint32_t mo, int q0s, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) s = mfma32(lds_ld16(qp[c] + ro), kf[c], s);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) dp = mfma32(lds_ld16(op[c] + ro), vf[c], dp);
+    pin_vgpr(s);
+    pin_vgpr(dp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 m4 = lds_ldf4(mp + mo + 32 * i);
+      const f32x4 d4 = lds_ldf4(mp + mo + BQ * 4 + 32 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = fmaf(s[4 * i + e], sl2e, -(kterm + m4[e]));
+        if constexpr (kMask) {
+          if (kj > q0s + 8 * i + 4 * h + e) x = -INFINITY;
+        }
+        const float p = __builtin_amdgcn_exp2f(x);
+        const float ds = p * (dp[4 * i + e] - d4[e]);
+        dck -= ds;
+        s[4 * i + e] = p;
+        dp[4 * i + e] = ds;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 pb = pack_c_half(s, t);
+      const bf16x8 sb = pack_c_half(dp, t);
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        dvacc[d] = mfma32(lds_tr8(otp[d][0] + ro + t * 16 * D * 2, otp[d][1] + ro + t * 16 * D * 2),
+                          pb, dvacc[d]);
+        dkacc[d] = mfma32(lds_tr8(qtp[d][0] + ro + t * 16 * D * 2, qtp[d][1] + ro + t * 16 * D * 2),
+                          sb, dkacc[d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+      pin_agpr(dvacc[d]);
+      pin_agpr(dkacc[d]);
+    }
+  };
+
+  // prologue: copies of Q(0), dO(0), Q(1), dO(1) and the raw rows of tiles 0..2; convert tile 0
+  copy_tile(q_rs, Q_OFF, 0, 0);
+  copy_tile(o_rs, O_OFF, 0, 0);
+  copy_rows(0, 0);
+  if (1 < n_t) {
+    copy_tile(q_rs, Q_OFF, 1, 1);
+    copy_tile(o_rs, O_OFF, 1, 1);
+    copy_rows(1, 1);
+  }
+  if (2 < n_t) copy_rows(2, 2);
+  bar_vm<0>();
+  convert_rows(-1, 0, 0);
+  bar_vm<0>();
+
+  auto generic_tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    start_copies(t, (t + 2) & 3, (t + 3) & 3);
+    convert_rows(t, (t + 1) & 3, (t + 1) & 1);
+    if (active) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int j = 2 * t + sub;
+        const uint32_t ro = (uint32_t)(t & 3) * TB + (uint32_t)sub * 32 * D * 2;
+        const uint32_t mo = (uint32_t)(t & 1) * 2 * BQ * 4 + (uint32_t)sub * 32 * 4;
+        if (j >= j0) sub_tile(ro, mo, k0 + 32 * j, mask_tag);
+      }
+    }
+    bar_vm<0>();
+  };
+  auto steady_tile = [&](int t, auto slot_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;  // t % 4
+    start_copies(t, (S + 2) & 3, (S + 3) & 3);
+    convert_rows(t, (S + 1) & 3, (S + 1) & 1);
+    if (active) {
+      sub_tile(S * TB, (S & 1) * 2 * BQ * 4, 0, std::false_type{});
+      sub_tile(S * TB + 32 * D * 2, (S & 1) * 2 * BQ * 4 + 32 * 4, 0, std::false_type{});
+    }
+    bar_vm<NCOPY>();
+  };
+  int t = 0;
+  for (; t < n_t && t < 2; ++t) generic_tile(t, std::true_type{});
+  for (; t + 6 < n_t; t += 4) {  // t % 4 == 2; every copy of the four iterations exists
+    steady_tile(t, std::integral_constant<int, 2>{});
+    steady_tile(t + 1, std::integral_constant<int, 3>{});
+    steady_tile(t + 2, std::integral_constant<int, 0>{});
+    steady_tile(t + 3, std::integral_constant<int, 1>{});
+  }
+  for (; t < n_t; ++t) generic_tile(t, std::false_type{});
+
+  const float dck_tot = xhalf_sum(dck);
+  if (!kok) return;
+  const size_t row = base + (size_t)kj * D;
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = d * 32 + 8 * i + 4 * h;
+      *reinterpret_cast<float4*>(dV + row + col) =
+          make_float4(dvacc[d][4 * i], dvacc[d][4 * i + 1], dvacc[d][4 * i + 2], dvacc[d][4 * i + 3]);
+      *reinterpret_cast<float4*>(dK + row + col) =
+          make_float4(dkacc[d][4 * i] * scale, dkacc[d][4 * i + 1] * scale,
+                      dkacc[d][4 * i + 2] * scale, dkacc[d][4 * i + 3] * scale);
+    }
+  }
+  if (h == 0) dck_out[(size_t)bh * L + kj] = dck_tot;
+}
+
 // Query-stationary step with the forward kernel's memory pipeline. 4 waves, one per SIMD (up
 // to 512 registers each), 64 queries per wave as two 32-query blocks that share every K / V
 // operand read; keys are walked from the diagonal backwards in 64-key tiles (two 32-key
@@ -621,6 +873,16 @@ template <int D>
 void go_dkv(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
             const bf16_t* dO, const float* delta, float* dk, float* dv, float* dck, int64_t BH,
             int64_t L, float scale, hipStream_t s) {
+  static const bool pipe = [] {
+    const char* e = getenv("FOX_BWD_IMPL");
+    return !(e && atoi(e) == 0);
+  }();
+  if (pipe) {
+    const int n_kt = (int)((L + 127) / 128);
+    hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v,
+                       dO, c, lse, delta, dk, dv, dck, (int)L, (int)BH, scale * kLog2e, scale);
+    return;
+  }
   const int n_kt = (int)((L + kKvBN - 1) / kKvBN);
   hipLaunchKernelGGL(dkv_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v, dO, c,
                      lse, delta, dk, dv, dck, (int)L, (int)BH, scale * kLog2e, scale);
