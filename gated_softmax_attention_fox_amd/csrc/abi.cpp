@@ -39,8 +39,9 @@ fox_status launched(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Largest sizes the kernels index with 32-bit integers.
-constexpr int64_t kMaxL = int64_t(1) << 26;
+// Largest sequence length: the attention kernels address one (b, h) slab of L x D bf16 values
+// with 32-bit byte offsets (buffer descriptors cover L * D * 2 bytes), so L * 128 * 2 < 2^32.
+constexpr int64_t kMaxL = int64_t(1) << 23;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
 #define FOX_REQUIRE(cond, ...)                                   \
@@ -102,7 +103,7 @@ fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const 
   FOX_REQUIRE(b_f != nullptr, "b_f must not be NULL");
   FOX_REQUIRE_PTR(log_f);
   FOX_REQUIRE(x_dt == FOX_BF16 || x_dt == FOX_F32, "x_dt must be FOX_BF16 or FOX_F32");
-  FOX_REQUIRE(B >= 1 && L >= 1 && L <= kMaxL, "B >= 1 and 1 <= L <= 2^26 required");
+  FOX_REQUIRE(B >= 1 && L >= 1 && L <= kMaxL, "B >= 1 and 1 <= L <= 2^23 required");
   FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
   FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
               "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
@@ -266,7 +267,7 @@ fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f
   FOX_REQUIRE_PTR(dlog_f);
   FOX_REQUIRE(dlog_f != dc_q && dlog_f != dc_k, "dlog_f must not alias dc_q or dc_k");
   FOX_REQUIRE(BH >= 1 && BH < (int64_t(1) << 31), "BH must be in [1, 2^31)");
-  FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, 2^26]");
+  FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, 2^23]");
   return launched(fox::launch_rev_cumsum2(dc_q, dc_k, dlog_f, BH, L, (hipStream_t)stream),
                   "fox_dlogf_from_dc");
 }

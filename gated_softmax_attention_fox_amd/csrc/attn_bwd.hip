@@ -8,25 +8,26 @@
 // note the work may be split over two kernels; here it is split so that no output needs atomics:
 //
 //   1. delta_kernel : Delta_i = dO_i . O_i from the fp32 forward output.
-//   2. dq_kernel    : query-stationary. A workgroup owns 128 queries (32 per wave) and walks the
-//                     key tiles up to its diagonal: S^T = K Q^T, P, dP^T = V dO^T,
-//                     dS = P (dP - Delta_i), dQ^T += K^T dS^T. It also sums P and dS along each
-//                     row and replaces Delta_i by the value that makes the row of dS sum to zero
-//                     under this P and dP; dc^q_i is that row sum.
-//   3. dkv_kernel   : key-stationary. A workgroup owns 128 keys (32 per wave, held in registers
-//                     as MFMA operands) and walks the query tiles at or after its diagonal:
-//                     S = Q K^T, P = exp(S*scale + c_i - c_j - LSE_i), dP = dO V^T,
-//                     dS = P (dP - Delta'_i), dV^T += dO^T P, dK^T += Q^T dS, dc^k_j -= sum_i dS_ij.
+//   2. dq_pipe_kernel  : query-stationary. A workgroup owns 256 queries (64 per wave) and walks
+//                        the key tiles from its diagonal backwards: S^T = K Q^T, P,
+//                        dP^T = V dO^T, dS = P (dP - Delta_i), dQ^T += K^T dS^T. It also sums P
+//                        and dS along each row and replaces Delta_i by the value that makes the
+//                        row of dS sum to zero under this P and dP; dc^q_i is that row sum.
+//   3. dkv_pipe_kernel : key-stationary. A workgroup owns 128 keys (32 per wave, held in
+//                        registers as MFMA operands) and walks the query tiles from its diagonal
+//                        to the end: S = Q K^T, P = exp(S*scale + c_i - c_j - LSE_i), dP = dO V^T,
+//                        dS = P (dP - Delta'_i), dV^T += dO^T P, dK^T += Q^T dS,
+//                        dc^k_j -= sum_i dS_ij.
 //   4. reverse scan : d log f_l = sum_{t>=l} (dc^q_t + dc^k_t), fp64 accumulation.
 //
 // d log f_l telescopes to the sum of dS over rows >= l and columns < l, so the row and column
 // sums must come from one consistent dS: both are taken in fp32 before dS is rounded to bf16 for
 // the MFMA, and both kernels use the refined row term (a Delta from the forward's O, whose P
-// was rounded to bf16, leaves a per-row residual that the reverse scan would accumulate). Every output element is written by exactly
-// one lane, so the backward is deterministic. The C-tile / operand conventions are those of
-// fox_device.h: in dkv_kernel the C tiles are [query x key] with one key per lane, so P and dS
-// are B operands of products that contract over queries; in dq_kernel they are [key x query].
-#include <cstdlib>
+// was rounded to bf16, leaves a per-row residual that the reverse scan would accumulate).
+// Every output element is written by exactly one lane, so the backward is deterministic. The C-tile / operand conventions are those of
+// fox_device.h: in dkv_pipe_kernel the C tiles are [query x key] with one key per lane, so P
+// and dS are B operands of products that contract over queries; in dq_pipe_kernel they are
+// [key x query].
 #include <type_traits>
 
 #include "fox_device.h"
@@ -34,11 +35,6 @@
 
 namespace fox {
 namespace {
-
-constexpr int kKvBN = 128;  // keys per workgroup in dkv_kernel
-constexpr int kKvBM = 64;   // queries per LDS tile in dkv_kernel
-constexpr int kQBM = 128;   // queries per workgroup in dq_kernel
-constexpr int kQBN = 64;    // keys per LDS tile in dq_kernel
 
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const bf16_t* __restrict__ dO,
@@ -65,260 +61,6 @@ __global__ __launch_bounds__(256) void delta_kernel(const bf16_t* __restrict__ d
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) acc += __shfl_xor(acc, m, 64);
   if (row < rows && part == 0) delta[row] = acc;
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void dkv_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
-    const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV,
-    float* __restrict__ dck_out, int L, int BH, float sl2e, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t q_s[kKvBM * D];
-  __shared__ __attribute__((aligned(16))) bf16_t do_s[kKvBM * D];
-  __shared__ __attribute__((aligned(16))) float qt_s[kKvBM];
-  __shared__ __attribute__((aligned(16))) float dl_s[kKvBM];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int kt = bid / BH;  // key tile 0 sees every query tile: issued first
-  const int k0 = kt * kKvBN;
-  const size_t base = (size_t)bh * L * D;
-  Q += base;
-  K += base;
-  V += base;
-  dO += base;
-  C += (size_t)bh * L;
-  LSE += (size_t)bh * L;
-  Delta += (size_t)bh * L;
-  const float c_ref = C[k0];
-  const int kw = k0 + wave * 32;
-  const int kj = kw + l32;
-  const bool kok = kj < L;
-
-  bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (kok) {
-      kf[c] = ld8(K + (size_t)kj * D + 16 * c + 8 * h);
-      vf[c] = ld8(V + (size_t)kj * D + 16 * c + 8 * h);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kf[c][e] = (__bf16)0.f;
-        vf[c][e] = (__bf16)0.f;
-      }
-    }
-  }
-  const float kterm = kok ? (C[kj] - c_ref) * kLog2e : 0.f;
-  f32x16 dvacc[D / 32], dkacc[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
-    dvacc[d] = zero16();
-    dkacc[d] = zero16();
-  }
-  float dck = 0.f;
-
-  for (int q0 = k0; q0 < L; q0 += kKvBM) {
-    __syncthreads();
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < kKvBM * CH; idx += 256) {
-      const int r = idx / CH, cc = idx % CH;
-      lds_store8<D>(q_s, r, cc * 8, ld16_or_zero<D>(Q, q0 + r, L, cc * 8));
-      lds_store8<D>(do_s, r, cc * 8, ld16_or_zero<D>(dO, q0 + r, L, cc * 8));
-    }
-    if (tid < kKvBM) {
-      const int qq = q0 + tid;
-      // rows past the end get P = 0 through an infinitely negative row term
-      qt_s[tid] = qq < L ? ((C[qq] - c_ref) - LSE[qq]) * kLog2e : -INFINITY;
-      dl_s[tid] = qq < L ? Delta[qq] : 0.f;
-    }
-    __syncthreads();
-    if (q0 + kKvBM - 1 < kw) continue;  // every query of this tile precedes every key of this wave
-    const bool diag = q0 < kw + 31;
-
-#pragma unroll
-    for (int qb = 0; qb < kKvBM / 32; ++qb) {
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s = mfma32(lds_row8<D>(q_s, qb * 32 + l32, 16 * c + 8 * h), kf[c], s);
-        dp = mfma32(lds_row8<D>(do_s, qb * 32 + l32, 16 * c + 8 * h), vf[c], dp);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&qt_s[qb * 32 + 8 * i + 4 * h]);
-        const f32x4 dl4 = *reinterpret_cast<const f32x4*>(&dl_s[qb * 32 + 8 * i + 4 * h]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * i + j;
-          float x = fmaf(s[e], sl2e, qt4[j]) - kterm;
-          if (diag && kj > q0 + qb * 32 + 8 * i + 4 * h + j) x = -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(x);
-          const float ds = p * (dp[e] - dl4[j]);
-          dck -= ds;
-          s[e] = p;
-          dp[e] = ds;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 pb = pack_c_half(s, t);
-        const bf16x8 sb = pack_c_half(dp, t);
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d) {
-          dvacc[d] = mfma32(lds_col8<D>(do_s, qb * 32 + 16 * t, d * 32, lane), pb, dvacc[d]);
-          dkacc[d] = mfma32(lds_col8<D>(q_s, qb * 32 + 16 * t, d * 32, lane), sb, dkacc[d]);
-        }
-      }
-    }
-  }
-
-  const float dck_tot = xhalf_sum(dck);
-  if (!kok) return;
-  const size_t row = base + (size_t)kj * D;
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = d * 32 + 8 * i + 4 * h;
-      *reinterpret_cast<float4*>(dV + row + col) =
-          make_float4(dvacc[d][4 * i], dvacc[d][4 * i + 1], dvacc[d][4 * i + 2], dvacc[d][4 * i + 3]);
-      *reinterpret_cast<float4*>(dK + row + col) =
-          make_float4(dkacc[d][4 * i] * scale, dkacc[d][4 * i + 1] * scale,
-                      dkacc[d][4 * i + 2] * scale, dkacc[d][4 * i + 3] * scale);
-    }
-  }
-  if (h == 0) dck_out[(size_t)bh * L + kj] = dck_tot;
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void dq_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
-    const float* Delta, float* __restrict__ dQ, float* __restrict__ dcq_out, float* delta_out,
-    int L, int BH, int n_qt, float sl2e, float scale) {
-  __shared__ __attribute__((aligned(16))) bf16_t k_s[kQBN * D];
-  __shared__ __attribute__((aligned(16))) bf16_t v_s[kQBN * D];
-  __shared__ __attribute__((aligned(16))) float kt_s[kQBN];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = n_qt - 1 - bid / BH;  // longest-first
-  const int q0 = qt * kQBM;
-  const size_t base = (size_t)bh * L * D;
-  Q += base;
-  K += base;
-  V += base;
-  dO += base;
-  C += (size_t)bh * L;
-  const float c_ref = C[q0];
-  const int qw = q0 + wave * 32;
-  const int qi = qw + l32;
-  const bool qok = qi < L;
-
-  bf16x8 qf[D / 16], dof[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (qok) {
-      qf[c] = ld8(Q + (size_t)qi * D + 16 * c + 8 * h);
-      dof[c] = ld8(dO + (size_t)qi * D + 16 * c + 8 * h);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qf[c][e] = (__bf16)0.f;
-        dof[c][e] = (__bf16)0.f;
-      }
-    }
-  }
-  const float qterm = qok ? ((C[qi] - c_ref) - LSE[(size_t)bh * L + qi]) * kLog2e : -INFINITY;
-  const float dl = qok ? Delta[(size_t)bh * L + qi] : 0.f;
-  f32x16 dqacc[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) dqacc[d] = zero16();
-  float dcq = 0.f, psum = 0.f;
-
-  const int q_last = (q0 + kQBM - 1 < L - 1) ? q0 + kQBM - 1 : L - 1;
-  const int kt_last = q_last / kQBN;
-  for (int kt = 0; kt <= kt_last; ++kt) {
-    const int k0 = kt * kQBN;
-    __syncthreads();
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < kQBN * CH; idx += 256) {
-      const int r = idx / CH, cc = idx % CH;
-      lds_store8<D>(k_s, r, cc * 8, ld16_or_zero<D>(K, k0 + r, L, cc * 8));
-      lds_store8<D>(v_s, r, cc * 8, ld16_or_zero<D>(V, k0 + r, L, cc * 8));
-    }
-    if (tid < kQBN) {
-      const int key = k0 + tid;
-      kt_s[tid] = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
-    }
-    __syncthreads();
-    if (k0 > qw + 31) continue;
-    const bool diag = k0 + kQBN - 1 > qw;
-
-#pragma unroll
-    for (int kb = 0; kb < kQBN / 32; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s = mfma32(lds_row8<D>(k_s, kb * 32 + l32, 16 * c + 8 * h), qf[c], s);
-        dp = mfma32(lds_row8<D>(v_s, kb * 32 + l32, 16 * c + 8 * h), dof[c], dp);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 kt4 = *reinterpret_cast<const f32x4*>(&kt_s[kb * 32 + 8 * i + 4 * h]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * i + j;
-          float x = fmaf(s[e], sl2e, qterm) - kt4[j];
-          if (diag && (k0 + kb * 32 + 8 * i + 4 * h + j) > qi) x = -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(x);
-          const float ds = p * (dp[e] - dl);
-          dcq += ds;
-          psum += p;
-          dp[e] = ds;
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 sb = pack_c_half(dp, t);
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d)
-          dqacc[d] = mfma32(lds_col8<D>(k_s, kb * 32 + 16 * t, d * 32, lane), sb, dqacc[d]);
-      }
-    }
-  }
-
-  // Row term consistent with this kernel's own P and dP: the forward's O was built from P
-  // rounded to bf16, so dO.O differs from sum_j P_ij dP_ij by ~1e-3 relative, and that residual
-  // would accumulate in d log f over every row that still attends across a position. With
-  // eps = sum_j P_ij (dP_ij - Delta_i) and S = sum_j P_ij, Delta'_i = Delta_i + eps / S makes
-  // sum_j P_ij (dP_ij - Delta'_i) vanish; the key-stationary step uses Delta', and dc^q is that
-  // (rounding-level) row sum. dQ keeps Delta: its error from the residual is ~scale*eps*|k|.
-  const float eps = xhalf_sum(dcq);
-  const float ptot = xhalf_sum(psum);
-  const float dl_new = dl + eps / ptot;
-  const float dcq_tot = eps - (dl_new - dl) * ptot;
-  if (!qok) return;
-  const size_t row = base + (size_t)qi * D;
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int col = d * 32 + 8 * i + 4 * h;
-      *reinterpret_cast<float4*>(dQ + row + col) =
-          make_float4(dqacc[d][4 * i] * scale, dqacc[d][4 * i + 1] * scale,
-                      dqacc[d][4 * i + 2] * scale, dqacc[d][4 * i + 3] * scale);
-    }
-  }
-  if (h == 0) {
-    dcq_out[(size_t)bh * L + qi] = dcq_tot;
-    delta_out[(size_t)bh * L + qi] = dl_new;
-  }
 }
 
 // Key-stationary step with the forward kernel's memory pipeline. 4 waves, one per SIMD, 32 keys
@@ -832,7 +574,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   for (; t < n_t; ++t) generic_tile(t, std::false_type{});
 
-  // Row term consistent with this kernel's own P and dP (see dq_kernel).
+  // Row term consistent with this kernel's own P and dP: the forward's O was built from P
+  // rounded to bf16, so dO.O differs from sum_j P_ij dP_ij by ~1e-3 relative, and that residual
+  // would accumulate in d log f over every row that still attends across a position. With
+  // eps = sum_j P_ij (dP_ij - Delta_i) and S = sum_j P_ij, Delta'_i = Delta_i + eps / S makes
+  // sum_j P_ij (dP_ij - Delta'_i) vanish; the key-stationary step uses Delta', and dc^q is that
+  // (rounding-level) row sum. dQ keeps Delta: its error from the residual is ~scale*eps*|k|.
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const float eps = xhalf_sum(dcq[b]);
@@ -873,39 +620,19 @@ template <int D>
 void go_dkv(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
             const bf16_t* dO, const float* delta, float* dk, float* dv, float* dck, int64_t BH,
             int64_t L, float scale, hipStream_t s) {
-  static const bool pipe = [] {
-    const char* e = getenv("FOX_BWD_IMPL");
-    return !(e && atoi(e) == 0);
-  }();
-  if (pipe) {
-    const int n_kt = (int)((L + 127) / 128);
-    hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v,
-                       dO, c, lse, delta, dk, dv, dck, (int)L, (int)BH, scale * kLog2e, scale);
-    return;
-  }
-  const int n_kt = (int)((L + kKvBN - 1) / kKvBN);
-  hipLaunchKernelGGL(dkv_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v, dO, c,
-                     lse, delta, dk, dv, dck, (int)L, (int)BH, scale * kLog2e, scale);
+  const int n_kt = (int)((L + 127) / 128);
+  hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v, dO,
+                     c, lse, delta, dk, dv, dck, (int)L, (int)BH, scale * kLog2e, scale);
 }
 
 template <int D>
 void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
            const bf16_t* dO, const float* delta, float* dq, float* dcq, float* delta_out,
            int64_t BH, int64_t L, float scale, hipStream_t s) {
-  static const bool pipe = [] {
-    const char* e = getenv("FOX_BWD_IMPL");
-    return !(e && atoi(e) == 0);
-  }();
-  if (pipe) {
-    const int n_qt = (int)((L + 255) / 256);
-    hipLaunchKernelGGL(dq_pipe_kernel<D>, dim3((unsigned)(n_qt * BH)), dim3(256), 0, s, q, k, v,
-                       dO, c, lse, delta, dq, dcq, delta_out, (int)L, (int)BH, n_qt,
-                       scale * kLog2e, scale);
-    return;
-  }
-  const int n_qt = (int)((L + kQBM - 1) / kQBM);
-  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(n_qt * BH)), dim3(256), 0, s, q, k, v, dO, c,
-                     lse, delta, dq, dcq, delta_out, (int)L, (int)BH, n_qt, scale * kLog2e, scale);
+  const int n_qt = (int)((L + 255) / 256);
+  hipLaunchKernelGGL(dq_pipe_kernel<D>, dim3((unsigned)(n_qt * BH)), dim3(256), 0, s, q, k, v, dO,
+                     c, lse, delta, dq, dcq, delta_out, (int)L, (int)BH, n_qt, scale * kLog2e,
+                     scale);
 }
 
 }  // namespace

@@ -8,25 +8,28 @@
 // block on chip, mask causally, run the online softmax, normalise at the end; paperlayer.ai
 // summary, section E).
 //
-// bf16 path (MFMA). A workgroup owns 128 queries of one (b, h); each of its 4 waves owns 32 of
+// bf16 path (MFMA). A workgroup owns 256 queries of one (b, h); each of its 8 waves owns 32 of
 // them. The score block is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 so
 // that every lane holds one query's column of scores: the row max and row sum of the online
 // softmax are then in-lane reductions plus one exchange with the partner half-wave. The
 // probabilities stay in registers and feed O^T += V^T P^T directly as the B operand; V^T comes
-// from a column read of the row-major V tile in LDS. K, V and the bias slice are staged in LDS
-// per 64-key tile. Only the diagonal tiles evaluate the causal mask; tiles entirely above a
-// wave's last query are skipped by that wave. Workgroups are issued longest-first (the last
-// query tiles, which see the most keys, start first) to even out the causal triangle.
+// from transposed reads (ds_read_b64_tr_b16) of the row-major V tile in LDS. Keys are walked
+// from the diagonal backwards: the first tile fixes a running max that the decaying bias
+// rarely lets later tiles beat, so O is rescaled only when a row max rises by more than
+// kFwdLazy. Workgroups are issued longest-first (the last query tiles, which see the most keys,
+// start first) to even out the causal triangle. The memory pipeline, the three-stage software
+// pipeline per wave and the phases are described at the kernel.
 //
-// Bias and precision: the softmax runs in base 2 on x = scale*log2(e)*(q.k) - log2(e)*(c_j - c_r),
-// with c_r = c at the workgroup's first query. The row constant c_i - c_r cancels in the softmax
-// and is added back only to LSE, and keeping c relative to a nearby reference makes c_j - c_r
-// exact for the keys that carry weight.
+// Bias and precision: the softmax runs in base 2 on
+//   y = scale*log2(e)*(q.k) - (ck_j + m_i),  ck_j = log2(e)*(c_j - c_r),
+// with c_r = c at the workgroup's first query and m_i the row's running reference. The row
+// constant c_i - c_r cancels in the softmax and is added back only to LSE. ck_j and m_i are
+// summed before the fma: both grow large when c_r is far from the row's own c, and for every
+// key with weight they nearly cancel, so the sum is exact.
 //
 // fp32 path (vector ALU, no down-conversion): one wave owns 32 queries, two lanes per query
 // (each half of the head dimension), K/V tiles of 32 keys in LDS; the logit is
 // scale*(q.k) + (c_i - c_j) in fp32 and the softmax uses expf.
-#include <cstdlib>
 #include <type_traits>
 
 #include "fox_device.h"
@@ -40,183 +43,10 @@ constexpr float kFwdLazy = 8.0f;  // rescale O only when a row max rises by more
 struct First { static constexpr bool value = true; };   // tag: a wave's first (diagonal) tile
 struct Rest { static constexpr bool value = false; };   // tag: every later tile
 
-// NW waves, 32 queries each. K/V/bias tiles are double-buffered in LDS: the global loads of
-// tile t+1 are issued into registers before tile t is computed and stored to the other buffer
-// after it, so one barrier per tile suffices.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const float* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE, int L, int BH,
-    int n_qt, float sl2e, int o_f32) {
-  constexpr int BM = NW * 32;
-  constexpr int NT = NW * 64;
-  constexpr int TILE = kFwdBN * D;
-  constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int CPT = TILE / 8 / NT;      // chunks per thread per tensor
-  static_assert(CPT >= 1 && CPT * 8 * NT == TILE, "tile must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) bf16_t k_s[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t v_s[2][TILE];
-  __shared__ __attribute__((aligned(16))) float ck_s[2][kFwdBN];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, l32 = lane & 31;
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = n_qt - 1 - bid / BH;  // longest-first
-  const int q0 = qt * BM;
-  const size_t base = (size_t)bh * L * D;
-  Q += base;
-  K += base;
-  V += base;
-  C += (size_t)bh * L;
-  const float c_ref = C[q0];
-  const int qw = q0 + wave * 32;
-  const int qi = qw + l32;
-
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (qi < L) {
-      qf[c] = ld8(Q + (size_t)qi * D + 16 * c + 8 * h);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.f;
-    }
-  }
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) oacc[d] = zero16();
-  float m = -INFINITY, lsum = 0.f;
-
-  u32x4 kreg[CPT], vreg[CPT];
-  float creg = 0.f;
-  // (always_inline: an outlined lambda would keep kreg/vreg in scratch memory)
-  auto gload = [&](int kt) __attribute__((always_inline)) {
-    const int k0 = kt * kFwdBN;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      const int key = k0 + idx / CPR, cc = idx % CPR;
-      kreg[i] = ld16_or_zero<D>(K, key, L, cc * 8);  // within one (b, h): L * D < 2^31
-      vreg[i] = ld16_or_zero<D>(V, key, L, cc * 8);
-    }
-    if (tid < kFwdBN) creg = (k0 + tid) < L ? (C[k0 + tid] - c_ref) * kLog2e : 0.f;
-  };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      lds_store8<D>(k_s[buf], idx / CPR, (idx % CPR) * 8, kreg[i]);
-      lds_store8<D>(v_s[buf], idx / CPR, (idx % CPR) * 8, vreg[i]);
-    }
-    if (tid < kFwdBN) ck_s[buf][tid] = creg;
-  };
-
-  const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
-  const int kt_last = q_last / kFwdBN;
-  // Key tiles are walked from the diagonal backwards. The first tile a wave processes holds its
-  // largest biases (c is non-increasing, so the bias shrinks with distance) and fixes a running
-  // max that later tiles rarely beat; the max is therefore only raised when a tile exceeds it by
-  // more than kLazy (in log2 units), which bounds every probability by 2^kLazy and skips the
-  // rescaling of O on almost every tile. Only that first tile needs the causal mask: it starts
-  // at or before the wave's first query, so every row already has a finite max after it.
-  constexpr float kLazy = 8.0f;
-  gload(kt_last);
-  lstore(0);
-  __syncthreads();
-  for (int it = 0; it <= kt_last; ++it) {
-    const int kt = kt_last - it;
-    const int buf = it & 1;
-    const int k0 = kt * kFwdBN;
-    if (kt > 0) gload(kt - 1);
-    if (k0 <= qw + 31) {  // else every key of this tile lies after every query of this wave
-      const bool diag = k0 + kFwdBN - 1 > qw;
-      const bf16_t* ks = k_s[buf];
-      const bf16_t* vs = v_s[buf];
-      f32x16 s[kFwdBN / 32];
-#pragma unroll
-      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
-        s[kb] = zero16();
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          s[kb] = mfma32(lds_row8<D>(ks, kb * 32 + l32, 16 * c + 8 * h), qf[c], s[kb]);
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 ck = *reinterpret_cast<const f32x4*>(&ck_s[buf][kb * 32 + 8 * i + 4 * h]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float x = fmaf(s[kb][4 * i + j], sl2e, -ck[j]);
-            if (diag && (k0 + kb * 32 + 8 * i + 4 * h + j) > qi) x = -INFINITY;
-            s[kb][4 * i + j] = x;
-            mx = fmaxf(mx, x);
-          }
-        }
-      }
-      mx = xhalf_max(mx);
-      const bool raise = mx > m + kLazy;
-      if (__any(raise)) {  // wave-uniform: rescale only when some row's max moved
-        const float mnew = raise ? mx : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(s[kb][e] - m);
-      }
-#pragma unroll
-      for (int kb = 0; kb < kFwdBN / 32; ++kb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 pb = pack_c_half(s[kb], t);
-          lsum = rowsum_bf16x8(pb, lsum);  // l sums the same rounded P that meets V
-#pragma unroll
-          for (int d = 0; d < D / 32; ++d)
-            oacc[d] = mfma32(lds_col8<D>(vs, kb * 32 + 16 * t, d * 32, lane), pb, oacc[d]);
-        }
-      }
-    }
-    if (kt > 0) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  const float ltot = xhalf_sum(lsum);
-  const float inv = 1.0f / ltot;
-  if (qi < L) {
-    const size_t orow = base + (size_t)qi * D;
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int col = d * 32 + 8 * i + 4 * h;
-        const float y0 = oacc[d][4 * i] * inv, y1 = oacc[d][4 * i + 1] * inv;
-        const float y2 = oacc[d][4 * i + 2] * inv, y3 = oacc[d][4 * i + 3] * inv;
-        if (o_f32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(O) + orow + col) = make_float4(y0, y1, y2, y3);
-        } else {
-          const uint32_t lo = (uint32_t)f2bf(y0) | ((uint32_t)f2bf(y1) << 16);
-          const uint32_t hi = (uint32_t)f2bf(y2) | ((uint32_t)f2bf(y3) << 16);
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(O) + orow + col) = make_uint2(lo, hi);
-        }
-      }
-    }
-    if (h == 0 && LSE) LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + (C[qi] - c_ref);
-  }
-}
-
 // ---------------------------------------------------------------------------------------------
-// Software-pipelined variant. Same numerics as fwd_bf16_kernel (8 waves x 32 queries, keys walked
-// from the diagonal backwards, lazy rescaling), but each wave overlaps three 32-key sub-tiles:
+// bf16 kernel: 8 waves x 32 queries (256 queries of one (b, h) per workgroup), keys walked from the
+// diagonal backwards with lazy rescaling (see the head of this file). Each wave overlaps three
+// 32-key sub-tiles:
 // while it turns the scores of sub-tile j into probabilities (VALU), the matrix cores work on
 // O += V(j-1)^T P(j-1)^T and on S(j+1)^T = K(j+1) Q^T. Sub-tile j is key block
 // (2 kt_last + 1 - j) of 32 keys; tile t (64 keys, key tile kt_last - t) holds sub-tiles 2t and
@@ -627,46 +457,19 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 
 }  // namespace
 
-template <int D, int NW>
-void fwd_bf16_go(const void* q, const void* k, const void* v, const float* c, void* o, bool o_f32,
-                 float* lse, int64_t BH, int64_t L, float scale, hipStream_t s) {
-  const int n_qt = (int)((L + NW * 32 - 1) / (NW * 32));
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3((unsigned)(n_qt * BH)), dim3(NW * 64), 0, s,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L,
-                     (int)BH, n_qt, scale * kLog2e, (int)o_f32);
-}
-
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const float* c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
                            hipStream_t s) {
-  // waves per workgroup (32 queries each): 8 (256-query workgroups) unless FOX_FWD_WAVES=4
-  static const int nw = [] {
-    const char* e = getenv("FOX_FWD_WAVES");
-    return (e && atoi(e) == 4) ? 4 : 8;
-  }();
-  static const bool pipe = [] {
-    const char* e = getenv("FOX_FWD_IMPL");
-    return !(e && atoi(e) == 0);
-  }();
-  if (pipe) {
-    const int n_qt = (int)((L + 255) / 256);
-    if (D == 64)
-      hipLaunchKernelGGL(fwd_bf16_pipe_kernel<64>, dim3((unsigned)(n_qt * BH)), dim3(512), 0, s,
-                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L,
-                         (int)BH, n_qt, scale * kLog2e, (int)o_f32);
-    else
-      hipLaunchKernelGGL(fwd_bf16_pipe_kernel<128>, dim3((unsigned)(n_qt * BH)), dim3(512), 0, s,
-                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L,
-                         (int)BH, n_qt, scale * kLog2e, (int)o_f32);
-    return hipGetLastError();
-  }
-  if (D == 64) {
-    if (nw == 8) fwd_bf16_go<64, 8>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
-    else fwd_bf16_go<64, 4>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
-  } else {
-    if (nw == 8) fwd_bf16_go<128, 8>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
-    else fwd_bf16_go<128, 4>(q, k, v, c, o, o_f32, lse, BH, L, scale, s);
-  }
+  const int n_qt = (int)((L + 255) / 256);
+  const dim3 grid((unsigned)(n_qt * BH)), block(512);
+  if (D == 64)
+    hipLaunchKernelGGL(fwd_bf16_pipe_kernel<64>, grid, block, 0, s, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L, (int)BH, n_qt,
+                       scale * kLog2e, (int)o_f32);
+  else
+    hipLaunchKernelGGL(fwd_bf16_pipe_kernel<128>, grid, block, 0, s, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L, (int)BH, n_qt,
+                       scale * kLog2e, (int)o_f32);
   return hipGetLastError();
 }
 

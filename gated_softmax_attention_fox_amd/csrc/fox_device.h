@@ -78,34 +78,7 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * D + ((((col >> 3) ^ swz_key<D>(row))) << 3) + (col & 7);
 }
 
-// 8 consecutive elements of one row (col a multiple of 8): an A/B operand read along k = column.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row8(const bf16_t* base, int row, int col) {
-  return *reinterpret_cast<const bf16x8*>(base + swz<D>(row, col));
-}
-
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// A operand whose k slots are the rows {r0 + 4h + 0..3, r0 + 8 + 4h + 0..3} of a swizzled LDS
-// tile at column cbase + (lane % 32) (cbase a multiple of 32): the transpose of a row read.
-// Matches pack_c_half(., t) when r0 = 16t relative to the C tile's first row.
-//
-// ds_read_b64_tr_b16 works on groups of 16 lanes: lane 4a + b of a group receives element b of
-// the 8-byte pieces read by the group's lanes a, a + 4, a + 8, a + 12 (in that order). So when
-// group lane s reads columns col0 + 4(s % 4) .. +3 of row row0 + s / 4, group lane i receives
-// column col0 + i of rows row0 .. row0 + 3.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_col8(const bf16_t* base, int r0, int cbase, int lane) {
-  const int row = r0 + 4 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = cbase + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + swz<D>(row, col)));
-  const i16x4 b =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + swz<D>(row + 8, col)));
-  // Whole-vector shuffle and bit cast only: a __builtin_bit_cast of a single element of a
-  // __bf16 vector is miscompiled by this toolchain (every element reads element 0).
-  const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, ab);
-}
 
 // 16-byte register chunk. A native vector (not HIP's uint4 struct): selects between two chunks
 // then stay in registers instead of going through scratch memory.
@@ -151,31 +124,6 @@ __device__ __forceinline__ float xhalf_max(float v) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Global -> LDS tile copies that bypass registers (buffer_load_dwordx4 ... lds). A buffer
-// resource spans `bytes` bytes from `base`; reads at or past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wave copies 1 KiB of a swizzled [rows x D] bf16 tile: the 1 KiB block `blk` (rows
-// blk * 512 / D onward) of the tile whose first row is global row `row0` of the matrix behind
-// `rsrc`. Lane l fills LDS bytes blk * 1024 + 16 l, which is physical chunk l % (D / 8) of
-// tile row blk * 512 / D + l / (D / 8); it therefore reads logical chunk
-// (l % (D / 8)) ^ swz_key(row) of that row, so the LDS image is the swizzled layout above.
-template <int D>
-__device__ __forceinline__ void dma_tile_block(__amdgpu_buffer_rsrc_t rsrc, bf16_t* tile, int row0,
-                                               int blk, int lane) {
-  constexpr int CPR = D / 8;
-  const int r = blk * (512 / D) + lane / CPR;
-  const int lc = (lane % CPR) ^ swz_key<D>(r);
-  const int voff = ((row0 + r) * D + lc * 8) * 2;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + blk * 512), 16, voff, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------------------------------------
 // LDS reads from a per-lane base address plus a compile-time offset. A kernel computes each
 // lane's swizzled byte address once, hides it from the optimiser with opaque(), and adds only
 // constants inside its loops: the constant then folds into the 16-bit offset field of the DS
@@ -193,16 +141,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {  // LDS byte addre
 }
 __device__ __forceinline__ bf16x8 lds_ld16(uint32_t a) { return *(const lds_bf16x8*)(uintptr_t)a; }
 __device__ __forceinline__ f32x4 lds_ldf4(uint32_t a) { return *(const lds_f32x4*)(uintptr_t)a; }
-// Two transposed 8-byte reads (rows r and r + 8 of a lds_col8 pattern) as one B-layout operand.
-__device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
-  const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, ab);
-}
-// Byte offsets inside a swizzled tile of the reads lds_row8(base, row = lane % 32, col) and
-// lds_col8(base, r0 = 0, cbase, lane) issue (the second of the latter at row + 8). Adding
-// 32 * D * 2 * k (row8) or 16 * D * 2 * k (col8) moves them k row blocks down.
+// Per-lane byte offsets inside a swizzled tile, relative to its first row (adding 2 D bytes per
+// row moves them down; row blocks of 16 keep the swizzle key, so whole blocks can be added):
+//
+// row8_off(lane, col): 8 consecutive elements of row lane % 32 from column col (a multiple of
+// 8), read with ds_read_b128 - an A operand with m = row and k = column, or a B operand with
+// n = row.
+//
+// col8_off(lane, cbase, second): the two ds_read_b64_tr_b16 reads (second = 0, 1) that form an
+// A operand whose k slots are the rows {4h + 0..3, 8 + 4h + 0..3} of the tile at column
+// cbase + lane % 32 (cbase a multiple of 32): the transpose of a row read. It pairs with
+// pack_c_half(., t) of a C tile whose rows are the tile rows 16 t ... ds_read_b64_tr_b16 works on
+// groups of 16 lanes: lane 4a + b of a group receives element b of the 8-byte pieces read by the
+// group's lanes a, a + 4, a + 8, a + 12 (in that order). So when group lane s reads columns
+// col0 + 4 (s % 4) .. + 3 of row row0 + s / 4, group lane i receives column col0 + i of rows
+// row0 .. row0 + 3.
 template <int D>
 __device__ __forceinline__ uint32_t row8_off(int lane, int col) {
   return (uint32_t)swz<D>(lane & 31, col) * 2;
@@ -213,15 +166,21 @@ __device__ __forceinline__ uint32_t col8_off(int lane, int cbase, int second) {
   const int col = cbase + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   return (uint32_t)swz<D>(row, col) * 2;
 }
+// The two col8 reads as one operand. Whole-vector shuffle and bit cast only: a
+// __builtin_bit_cast of a single element of a __bf16 vector is miscompiled by this toolchain
+// (every element reads element 0).
+__device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
+  const i16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
 
 // Register-file hints for the allocator (no instruction is emitted): accumulators only the
 // matrix cores touch stay in AGPRs, MFMA results the vector ALU reads stay in VGPRs, so no
 // v_accvgpr moves are needed between them.
 __device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
 __device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
-
-// Wait until every global -> LDS copy this wave issued has landed.
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------------
 // Global -> LDS copies issued as inline assembly. The compiler does not track them, so it never

@@ -18,7 +18,7 @@
  *       log_f, c, lse, dlog_f       : [B, H, L]
  *       x (gate input)              : [B, L, d_model];  w_f: [H, d_model];  b_f: [H]
  *     Positions are 0-indexed; c is the inclusive prefix sum c_i = sum_{l<=i} log f_l.
- *   - Every pointer must be 16-byte aligned. D must be 64 or 128; L >= 1; B, H >= 1.
+ *   - Every pointer must be 16-byte aligned. D must be 64 or 128; 1 <= L <= 2^23; B, H >= 1.
  *   - Arguments are validated on the host before anything is launched. A bad argument
  *     returns FOX_E_INVALID (or FOX_E_UNSUPPORTED for a well-formed request this library does
  *     not implement) and enqueues nothing; fox_last_error() then describes it. A failed

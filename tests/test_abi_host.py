@@ -68,8 +68,8 @@ def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o
 @host_only
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), 1), (dict(k=P + 8), 1), (dict(c=0), 1), (dict(o=0), 1), (dict(lse=P + 4), 1),
-    (dict(D=96), 1), (dict(D=256), 1), (dict(L=0), 1), (dict(B=0), 1), (dict(H=-1), 1),
-    (dict(in_dt=7), 1), (dict(o_dt=3), 1), (dict(in_dt=0, o_dt=1), 1), (dict(scale=0.0), 1),
+    (dict(D=96), 1), (dict(D=256), 1), (dict(L=0), 1), (dict(L=(1 << 23) + 1), 1), (dict(B=0), 1),
+    (dict(H=-1), 1), (dict(in_dt=7), 1), (dict(o_dt=3), 1), (dict(in_dt=0, o_dt=1), 1), (dict(scale=0.0), 1),
     (dict(scale=float("nan")), 1), (dict(flags=0), 2), (dict(flags=3), 2),
 ])
 def test_forward_rejects(lib, kw, status):
@@ -81,6 +81,7 @@ def test_forward_rejects(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(ws=0), 1), (dict(ws=P + 16), 1), (dict(ws_bytes=100), 1), (dict(in_dt=0), 2),
     (dict(in_dt=5), 1), (dict(flags=0), 2), (dict(D=32), 1), (dict(o=0), 1),
+    (dict(L=(1 << 23) + 1), 1),
 ])
 def test_backward_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
