@@ -181,6 +181,7 @@ __device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
 // v_accvgpr moves are needed between them.
 __device__ __forceinline__ void pin_agpr(f32x16& x) { asm volatile("" : "+a"(x)); }
 __device__ __forceinline__ void pin_vgpr(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x)); }
 
 // ---------------------------------------------------------------------------------------------
 // Global -> LDS copies issued as inline assembly. The compiler does not track them, so it never
