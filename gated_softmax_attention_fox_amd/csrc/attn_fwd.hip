@@ -309,18 +309,70 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   }
 
   // ---- phase B: tiles 4..n_t-1, every wave past its diagonal --------------------------------
-  // Iteration t: P(2t-1)V, softmax(2t), S(2t+1), P(2t)V, softmax(2t+1), S(2t+2).
+  // One step: P(j-1)V into O, softmax of sub-tile j (scores in sc, bias values ck), S(j+1) into
+  // sn. The exponentials are taken against the current m before the lazy-raise test; only when a
+  // row max rose by more than kFwdLazy (rare) are they taken again after the raise. The common
+  // path is one straight-line block, so the scheduler can interleave the softmax arithmetic with
+  // the step's matrix products.
+  auto step = [&](f32x16& sc, f32x16& sn, const f32x4 (&ck)[4], uint32_t vo, uint32_t ko, bool next)
+      __attribute__((always_inline)) {
+    pv(vo);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = fmaf(sc[4 * i + e], sl2e, -(ck[i][e] + m));
+        sc[4 * i + e] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = xhalf_max(mx);
+    f32x16 p;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(sc[e]);
+    bf16x8 nb[2];
+    float ln = lsum;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      nb[t] = pack_c_half(p, t);
+      ln = rowsum_bf16x8(nb[t], ln);
+    }
+    if (next) qk(sn, ko);
+    // Keep the common-path exponentials above the branch (the compiler would otherwise sink them
+    // into the fall-through path, which splits the block again).
+    asm volatile("" : "+v"(nb[0]), "+v"(nb[1]), "+v"(ln));
+    const bool raise = mx > kFwdLazy;
+    if (__any(raise)) {
+      const float dm = raise ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-dm);
+      m += dm;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(sc[e] - dm);
+      ln = lsum * alpha;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        nb[t] = pack_c_half(p, t);
+        ln = rowsum_bf16x8(nb[t], ln);
+      }
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+      }
+    }
+    pb[0] = nb[0];
+    pb[1] = nb[1];
+    lsum = ln;
+  };
+  // Iteration t: sub-tiles 2t (rows 32..63 of tile t) and 2t + 1 (rows 0..31).
   auto tile_body = [&](uint32_t ko_t, uint32_t ko_t1, uint32_t vo_tm1, uint32_t co_t, bool next)
       __attribute__((always_inline)) {
     f32x4 ck[4];
-    bias_vals(ck, co_t + 32 * 4);                // bias reads ahead of the MFMAs that hide them
-    pv(vo_tm1);                                  // sub-tile 2t - 1: tile t - 1, rows 0..31
-    softmax(sa, ck, 0, Rest{});                  // sub-tile 2t: tile t, rows 32..63
+    bias_vals(ck, co_t + 32 * 4);
+    step(sa, sb, ck, vo_tm1, ko_t, true);
     bias_vals(ck, co_t);
-    qk(sb, ko_t);                                // sub-tile 2t + 1: tile t, rows 0..31
-    pv(ko_t + 32 * D * 2);                       // sub-tile 2t
-    softmax(sb, ck, 0, Rest{});                  // sub-tile 2t + 1
-    if (next) qk(sa, ko_t1 + 32 * D * 2);        // sub-tile 2t + 2: tile t + 1, rows 32..63
+    step(sb, sa, ck, ko_t + 32 * D * 2, ko_t1 + 32 * D * 2, next);
   };
   auto steady = [&](int t, auto slot_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;  // t % 4
