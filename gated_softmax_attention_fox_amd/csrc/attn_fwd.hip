@@ -13,10 +13,11 @@
 // that every lane holds one query's column of scores: the row max and row sum of the online
 // softmax are then in-lane reductions plus one exchange with the partner half-wave. The
 // probabilities stay in registers and feed O^T += V^T P^T directly as the B operand; V^T comes
-// from transposed reads (ds_read_b64_tr_b16) of the row-major V tile in LDS. Keys are walked
-// from the diagonal backwards: the first tile fixes a running max that the decaying bias
-// rarely lets later tiles beat, so O is rescaled only when a row max rises by more than
-// kFwdLazy. Workgroups are issued longest-first (the last query tiles, which see the most keys,
+// from transposed reads (ds_read_b64_tr_b16) of the row-major V tile in LDS. The diagonal band
+// of keys is visited first: it fixes a running max that the decaying bias rarely lets older keys
+// beat, so O is rescaled only when a row max rises by more than kFwdLazy; the older keys then
+// follow in ascending order, which keeps the workgroups of one head on the same K and V tiles at
+// the same time. Workgroups are issued longest-first (the last query tiles, which see the most keys,
 // start first) to even out the causal triangle. The memory pipeline, the three-stage software
 // pipeline per wave and the phases are described at the kernel.
 //
@@ -31,6 +32,7 @@
 // (each half of the head dimension), K/V tiles of 32 keys in LDS; the logit is
 // scale*(q.k) + (c_i - c_j) in fp32 and the softmax uses expf.
 #include <type_traits>
+#include <utility>
 
 #include "fox_device.h"
 #include "fox_launch.h"
@@ -43,14 +45,32 @@ constexpr float kFwdLazy = 8.0f;  // rescale O only when a row max rises by more
 struct First { static constexpr bool value = true; };   // tag: a wave's first (diagonal) tile
 struct Rest { static constexpr bool value = false; };   // tag: every later tile
 
+// Instruction order of one pipelined step (scheduler groups, filled in this order): kD0 LDS reads,
+// then each of the step's 16 matrix products followed by kDs LDS reads (for the first kNd
+// products) and kV vector instructions.
+template <int I, int kDs, int kV, int kNd>
+__device__ __forceinline__ void interleave_one() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (I < kNd) __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+}
+template <int kD0, int kDs, int kV, int kNd, int... I>
+__device__ __forceinline__ void interleave_all(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, kD0, 0);
+  (interleave_one<I, kDs, kV, kNd>(), ...);
+}
+template <int kD0, int kDs, int kV, int kNd>
+__device__ __forceinline__ void interleave_step() {
+  interleave_all<kD0, kDs, kV, kNd>(std::make_integer_sequence<int, 16>{});
+}
+
 // ---------------------------------------------------------------------------------------------
-// bf16 kernel: 8 waves x 32 queries (256 queries of one (b, h) per workgroup), keys walked from the
-// diagonal backwards with lazy rescaling (see the head of this file). Each wave overlaps three
-// 32-key sub-tiles:
+// bf16 kernel: 8 waves x 32 queries (256 queries of one (b, h) per workgroup), diagonal band first
+// with lazy rescaling (see the head of this file). Each wave overlaps three 32-key sub-tiles:
 // while it turns the scores of sub-tile j into probabilities (VALU), the matrix cores work on
-// O += V(j-1)^T P(j-1)^T and on S(j+1)^T = K(j+1) Q^T. Sub-tile j is key block
-// (2 kt_last + 1 - j) of 32 keys; tile t (64 keys, key tile kt_last - t) holds sub-tiles 2t and
-// 2t + 1.
+// O += V(j-1)^T P(j-1)^T and on S(j+1)^T = K(j+1) Q^T. The workgroup visits n_t 64-key tiles:
+// visit t < 4 is key tile kt_last - t (the band), visit t >= 4 is key tile t - 4; visit t holds
+// sub-tiles 2t (its rows 32..63) and 2t + 1 (rows 0..31).
 //
 // Memory pipeline. K, V and the raw c values of tile t live in LDS ring slot t % 4 (the bias
 // slice of tile t, (c_j - c_ref) log2 e, in slot t % 2). Iteration t reads K(t), K(t + 1),
@@ -125,19 +145,23 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   bf16x8 pb[2];  // P of the previous sub-tile as B operands (two 16-key halves)
 
   // ---- copies -------------------------------------------------------------------------------
+  // Key tile of visit t: the diagonal band (the last four key tiles) first, from the diagonal
+  // backwards; then every earlier key tile in ascending order, so that the workgroups of one head
+  // that run at the same time stream the same K and V tiles through the cache.
+  auto key_tile = [&](int t) __attribute__((always_inline)) { return t < 4 ? kt_last - t : t - 4; };
   auto copy_kv = [&](const i32x4& rs, uint32_t region, int t, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < BLK; ++b) {
       const int blk = wave * BLK + b;
       const int r = blk * (512 / D) + lane / CPR;
       const int lc = (lane % CPR) ^ swz_key<D>(r);
-      const uint32_t voff = (uint32_t)(((kt_last - t) * BN + r) * D + lc * 8) * 2;
+      const uint32_t voff = (uint32_t)((key_tile(t) * BN + r) * D + lc * 8) * 2;
       copy16_to_lds(sbase + region + slot * TB + blk * 1024, voff, rs);
     }
   };
   auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {  // 8 values per wave
     if (lane < 8) {
-      const uint32_t voff = (uint32_t)((kt_last - t) * BN + wave * 8 + lane) * 4;
+      const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * 8 + lane) * 4;
       copy4_to_lds(sbase + R_OFF + slot * BN * 4 + wave * 32, voff, c_rs);
     }
   };
@@ -342,6 +366,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     // Keep the common-path exponentials above the branch (the compiler would otherwise sink them
     // into the fall-through path, which splits the block again).
     asm volatile("" : "+v"(nb[0]), "+v"(nb[1]), "+v"(ln));
+    interleave_step<8, 2, 5, 10>();
     const bool raise = mx > kFwdLazy;
     if (__any(raise)) {
       const float dm = raise ? mx : 0.f;

@@ -149,6 +149,33 @@ def test_forward_config3_full_length(fox):
     check("LSE sampled rows", np.concatenate(gl), np.concatenate(rl))
 
 
+@pytest.mark.parametrize("per_wg", [2, 3, 4, 5])
+def test_forward_balanced_schedule(fox, per_wg):
+    """Head counts that give every compute unit the same number of (head, 256-query tile) items,
+    so the forward walks its balanced item lists; L = 300 leaves the second query tile partial
+    (waves past the end idle). Two rows of every item are checked against the oracle."""
+    P = torch.cuda.get_device_properties(0).multi_processor_count
+    if P % 2:
+        pytest.skip("balanced lists need an even number of compute units")
+    L, D = 300, 128
+    H = per_wg * P // 2  # n_qt = 2 query tiles per head
+    case = fi.make_case(1, H, L, D, "bf16", seed=40 + per_wg, gate="per_head")
+    say(f"fwd balanced schedule: {per_wg} items per workgroup, H={H}, L={L}")
+    c, o, lse = _run_fwd(fox, case, torch.float32)
+    s = default_scale(D)
+    cc = oracle.cumsum_logf(case.log_f)
+    rng = np.random.default_rng(per_wg)
+    got, ref, gl, rl = [], [], [], []
+    for h in range(H):
+        rows = np.array(sorted({int(rng.integers(0, 256)), 255, 256, L - 1,
+                                int(rng.integers(256, L))}))
+        O, LSE = oracle.attn_fwd_rows(case.q[0, h], case.k[0, h], case.v[0, h], cc[0, h], rows,
+                                      scale=s)
+        got.append(o[0, h, rows]); ref.append(O); gl.append(lse[0, h, rows]); rl.append(LSE)
+    check("O rows of every item", np.concatenate(got), np.concatenate(ref))
+    check("LSE rows of every item", np.concatenate(gl), np.concatenate(rl))
+
+
 def test_forward_deterministic(fox):
     case = fi.make_case(2, 3, 1500, 128, "bf16", seed=5)
     q, k, v = (dev(getattr(case, n), "bf16") for n in "qkv")
