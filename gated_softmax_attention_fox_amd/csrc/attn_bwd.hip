@@ -29,6 +29,7 @@
 // and dS are B operands of products that contract over queries; in dq_pipe_kernel they are
 // [key x query].
 #include <type_traits>
+#include <utility>
 
 #include "fox_device.h"
 #include "fox_launch.h"
@@ -61,6 +62,41 @@ __global__ __launch_bounds__(256) void delta_kernel(const bf16_t* __restrict__ d
 #pragma unroll
   for (int m = 1; m < G; m <<= 1) acc += __shfl_xor(acc, m, 64);
   if (row < rows && part == 0) delta[row] = acc;
+}
+
+// Instruction order of one software-pipelined step (scheduler groups, filled in this order): kD0
+// LDS reads, then each of the step's kNM matrix products followed by kDs LDS reads (for the
+// first kNd products) and kV vector instructions.
+template <int I, int kDs, int kV, int kNd>
+__device__ __forceinline__ void interleave_bwd_one() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  if constexpr (I < kNd) __builtin_amdgcn_sched_group_barrier(0x100, kDs, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+}
+template <int kD0, int kDs, int kV, int kNd, int... I>
+__device__ __forceinline__ void interleave_bwd_all(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, kD0, 0);
+  (interleave_bwd_one<I, kDs, kV, kNd>(), ...);
+}
+template <int kD0, int kDs, int kV, int kNd, int kNM>
+__device__ __forceinline__ void interleave_bwd() {
+  interleave_bwd_all<kD0, kDs, kV, kNd>(std::make_integer_sequence<int, kNM>{});
+}
+// A block of kNM matrix products fed by one LDS read each: kD0 reads first, then one read after
+// each product, so that every operand is read kD0 products ahead.
+template <int I>
+__device__ __forceinline__ void readahead_one() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+}
+template <int kD0, int... I>
+__device__ __forceinline__ void readahead_all(std::integer_sequence<int, I...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, kD0, 0);
+  (readahead_one<I>(), ...);
+}
+template <int kD0, int kNM>
+__device__ __forceinline__ void readahead() {
+  readahead_all<kD0>(std::make_integer_sequence<int, kNM - kD0>{});
 }
 
 // Key-stationary step with the forward kernel's memory pipeline. 4 waves, one per SIMD, 32 keys
@@ -202,29 +238,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   const uint32_t mp = opaque(sbase + M_OFF + 16 * h);
 
-  // One 32-query sub-tile: rows at byte offset ro of a Q / dO slot, row terms at mo, first
-  // query q0s (masking only with kMask).
-  auto sub_tile = [&](uint32_t ro, uint32_t mo, int q0s, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    f32x16 s = zero16(), dp = zero16();
+  // The three parts of one 32-query sub-tile (Q / dO rows at byte offset ro of a slot, row terms
+  // at mo, first query q0s, masking only with kMask):
+  //   sd   : S = Q K^T and dP = dO V^T (one key per lane);
+  //   grad : P = exp2(scale log2(e) s - (k_j + m_i)), dS = P (dP - Delta_i), dc^k_j -= sum_i dS_ij,
+  //          and P, dS as bf16 B operands;
+  //   dvdk : dV^T += dO^T P, dK^T += Q^T dS.
+  auto sd = [&](f32x16& s, f32x16& dp, uint32_t ro) __attribute__((always_inline)) {
+    s = zero16();
+    dp = zero16();
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) s = mfma32(lds_ld16(qp[c] + ro), kf[c], s);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) dp = mfma32(lds_ld16(op[c] + ro), vf[c], dp);
     pin_vgpr(s);
     pin_vgpr(dp);
+  };
+  auto rows = [&](f32x4 (&m4)[4], f32x4 (&d4)[4], uint32_t mo) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x4 m4 = lds_ldf4(mp + mo + 32 * i);
-      const f32x4 d4 = lds_ldf4(mp + mo + BQ * 4 + 32 * i);
+      m4[i] = lds_ldf4(mp + mo + 32 * i);
+      d4[i] = lds_ldf4(mp + mo + BQ * 4 + 32 * i);
+    }
+  };
+  auto grad = [&](f32x16& s, f32x16& dp, const f32x4 (&m4)[4], const f32x4 (&d4)[4], int q0s,
+                  auto mask_tag, bf16x8 (&pb)[2], bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = fmaf(s[4 * i + e], sl2e, -(kterm + m4[e]));
+        float x = fmaf(s[4 * i + e], sl2e, -(kterm + m4[i][e]));
         if constexpr (kMask) {
           if (kj > q0s + 8 * i + 4 * h + e) x = -INFINITY;
         }
         const float p = __builtin_amdgcn_exp2f(x);
-        const float ds = p * (dp[4 * i + e] - d4[e]);
+        const float ds = p * (dp[4 * i + e] - d4[i][e]);
         dck -= ds;
         s[4 * i + e] = p;
         dp[4 * i + e] = ds;
@@ -232,14 +281,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bf16x8 pb = pack_c_half(s, t);
-      const bf16x8 sb = pack_c_half(dp, t);
+      pb[t] = pack_c_half(s, t);
+      sb[t] = pack_c_half(dp, t);
+    }
+  };
+  auto dvdk = [&](uint32_t ro, const bf16x8 (&pb)[2], const bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) {
         dvacc[d] = mfma32(lds_tr8(otp[d][0] + ro + t * 16 * D * 2, otp[d][1] + ro + t * 16 * D * 2),
-                          pb, dvacc[d]);
+                          pb[t], dvacc[d]);
         dkacc[d] = mfma32(lds_tr8(qtp[d][0] + ro + t * 16 * D * 2, qtp[d][1] + ro + t * 16 * D * 2),
-                          sb, dkacc[d]);
+                          sb[t], dkacc[d]);
       }
     }
 #pragma unroll
@@ -247,6 +301,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       pin_agpr(dvacc[d]);
       pin_agpr(dkacc[d]);
     }
+  };
+  auto sub_tile = [&](uint32_t ro, uint32_t mo, int q0s, auto mask_tag) __attribute__((always_inline)) {
+    f32x16 s, dp;
+    bf16x8 pb[2], sb[2];
+    f32x4 m4[4], d4[4];
+    rows(m4, d4, mo);
+    sd(s, dp, ro);
+    readahead<8, 16>();
+    __builtin_amdgcn_sched_barrier(0);
+    grad(s, dp, m4, d4, q0s, mask_tag, pb, sb);
+    dvdk(ro, pb, sb);
   };
 
   // prologue: copies of Q(0), dO(0), Q(1), dO(1) and the raw rows of tiles 0..2; convert tile 0
@@ -277,13 +342,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     bar_vm<0>();
   };
+  // Steady tile t (slot S = t % 4), software-pipelined so that the vector work of one sub-tile runs
+  // under the matrix products of its neighbours: S, dP of sub-tile 2t; then (step A) the gradient
+  // arithmetic of 2t under dV, dK of 2t - 1 (carried from the previous tile in pc, sc) and S, dP
+  // of 2t + 1; then (step B) the gradient arithmetic of 2t + 1 under dV, dK of 2t. The P and dS of
+  // 2t + 1 are carried to the next tile. Every tile read here (t - 1 and t) has landed.
+  bf16x8 pc[2], sc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pc[i][e] = (__bf16)0.f;
+      sc[i][e] = (__bf16)0.f;
+    }
+  }
   auto steady_tile = [&](int t, auto slot_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;  // t % 4
+    constexpr uint32_t cur = S * TB, prev = ((S + 3) & 3) * TB, half = 32 * D * 2;
+    constexpr uint32_t mo0 = (S & 1) * 2 * BQ * 4, mo1 = mo0 + 32 * 4;
     start_copies(t, (S + 2) & 3, (S + 3) & 3);
     convert_rows(t, (S + 1) & 3, (S + 1) & 1);
     if (active) {
-      sub_tile(S * TB, (S & 1) * 2 * BQ * 4, 0, std::false_type{});
-      sub_tile(S * TB + 32 * D * 2, (S & 1) * 2 * BQ * 4 + 32 * 4, 0, std::false_type{});
+      f32x16 s0, dp0, s1, dp1;
+      bf16x8 p0[2], q0[2];
+      f32x4 m4[4], d4[4];
+      sd(s0, dp0, cur);
+      readahead<8, 16>();
+      __builtin_amdgcn_sched_barrier(0);
+      rows(m4, d4, mo0);
+      dvdk(prev + half, pc, sc);
+      sd(s1, dp1, cur + half);
+      grad(s0, dp0, m4, d4, 0, std::false_type{}, p0, q0);
+      interleave_bwd<14, 2, 4, 21, 32>();
+      __builtin_amdgcn_sched_barrier(0);
+      rows(m4, d4, mo1);
+      dvdk(cur, p0, q0);
+      grad(s1, dp1, m4, d4, 0, std::false_type{}, pc, sc);
+      interleave_bwd<14, 2, 7, 13, 16>();
     }
     bar_vm<NCOPY>();
   };
@@ -295,6 +390,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     steady_tile(t + 2, std::integral_constant<int, 0>{});
     steady_tile(t + 3, std::integral_constant<int, 1>{});
   }
+  // the last steady tile's carried sub-tile (zero operands when the loop did not run)
+  if (active) dvdk((uint32_t)((t + 3) & 3) * TB + 32 * D * 2, pc, sc);
   for (; t < n_t; ++t) generic_tile(t, std::false_type{});
 
   const float dck_tot = xhalf_sum(dck);
