@@ -81,6 +81,45 @@ def rms_norm(x, eps, weight=None):
     return y
 
 
+def gate_logf_bwd(x, w_f, b_f, dlog_f):
+    """Gradients of the gate through log sigma and the per-head GEMV.
+
+    Given the upstream gradient dlog_f [B, H, L] of log f = log sigma(z),
+    z[b,h,t] = sum_d x[b,t,d] w_f[h,d] + b_f[h]:
+      dz   = dlog_f * d(log sigma)/dz = dlog_f * sigma(-z)        (1 - sigma(z) = sigma(-z))
+      db_f = sum_{b,t} dz[b,h,t]
+      dw_f = sum_{b,t} dz[b,h,t] x[b,t,:]
+      dx   = sum_h dz[b,h,t] w_f[h,:]
+    Returns (dx [B, L, d_model], dw_f [H, d_model], db_f [H]). sigma(-z) is taken as
+    exp(log sigma(-z)), so it never rounds to 0 or 1 before the product.
+    ([FoX-pg] "Forget Gate Computation"; Pro block Step 4.)
+    """
+    x, w_f, b_f, g = _f64(x), _f64(w_f), _f64(b_f), _f64(dlog_f)
+    z = np.transpose(np.matmul(x, w_f.T), (0, 2, 1)) + b_f[None, :, None]   # [B, H, L]
+    dz = g * np.exp(log_sigmoid(-z))
+    db_f = dz.sum(axis=(0, 2))
+    dw_f = np.einsum("bhl,bld->hd", dz, x)
+    dx = np.einsum("bhl,hd->bld", dz, w_f)
+    return dx, dw_f, db_f
+
+
+def rms_norm_bwd(x, dy, eps, weight=None):
+    """Gradients of y = x / r * w, r = sqrt(mean(x^2) + eps), over the last axis.
+
+    With xh = x / r and g = dy * w (g = dy for unit weights):
+      dx = (g - xh * mean(g * xh)) / r
+      dw = sum over rows of dy * xh          (None for unit weights)
+    Returns (dx, dw). ([FoX-pg] "The Pro Block Architecture", Steps 1-2, QK-norm.)
+    """
+    x, dy = _f64(x), _f64(dy)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xh = x / r
+    g = dy if weight is None else dy * _f64(weight)
+    dx = (g - xh * np.mean(g * xh, axis=-1, keepdims=True)) / r
+    dw = None if weight is None else (dy * xh).reshape(-1, x.shape[-1]).sum(axis=0)
+    return dx, dw
+
+
 def fixed_gate_logf(t_min, t_max, H):
     """Data-independent gate initialisation ([FoX-pl] D; [FoX-pg] "Connection to ALiBi").
 

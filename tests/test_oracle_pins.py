@@ -318,3 +318,111 @@ def test_unmutated_oracle_passes_the_pin_harness():
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name):
     assert not _pins_hold(_mutant(name))
+
+
+# ---------------------------------------------------------------- Pro block backward (gate, QK-norm)
+def _pro_small(seed=11):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((2, 7, 24))
+    w = 0.3 * rng.standard_normal((3, 24))
+    b = rng.uniform(1, 6, size=3) * np.array([1.0, -1.0, 1.0])  # both signs of z
+    g = rng.standard_normal((2, 3, 7))
+    return x, w, b, g
+
+
+def _fd_dir(f, args, which, u, h=1e-6):
+    p = list(args)
+    m = list(args)
+    p[which] = args[which] + h * u
+    m[which] = args[which] - h * u
+    return (f(*p) - f(*m)) / (2 * h)
+
+
+def _gate_pins_hold(mod):
+    """Finite differences of sum(g * log f) for x, w_f, b_f, and torch autograd."""
+    x, w, b, g = _pro_small()
+    dx, dw, db = mod.gate_logf_bwd(x, w, b, g)
+    loss = lambda x_, w_, b_: float(np.sum(g * oracle.gate_logf(x_, w_, b_)))
+    rng = np.random.default_rng(5)
+    for which, grad in enumerate((dx, dw, db)):
+        for _ in range(2):
+            u = rng.standard_normal(grad.shape)
+            fd = _fd_dir(loss, (x, w, b), which, u)
+            if abs(fd - float(np.sum(grad * u))) > 1e-7 * max(1.0, abs(fd)):
+                return False
+    xt, wt, bt = (_t(a).requires_grad_(True) for a in (x, w, b))
+    z = torch.einsum("bld,hd->bhl", xt, wt) + bt[None, :, None]
+    (F.logsigmoid(z) * _t(g)).sum().backward()
+    return all(np.abs(a - r.grad.numpy()).max() < 1e-12 for a, r in ((dx, xt), (dw, wt), (db, bt)))
+
+
+def _rms_pins_hold(mod):
+    """Finite differences of sum(dy * rms_norm(x)) for x and the weights, and torch autograd."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 32)) * rng.uniform(0.1, 3.0, size=(5, 1))
+    dy = rng.standard_normal((5, 32))
+    wgt = rng.uniform(0.5, 1.5, size=32)
+    for weight in (None, wgt):
+        dx, dw = mod.rms_norm_bwd(x, dy, 1e-3, weight)
+        loss = lambda x_, w_: float(np.sum(dy * oracle.rms_norm(x_, 1e-3, w_)))
+        u = rng.standard_normal(x.shape)
+        fd = _fd_dir(loss, (x, weight), 0, u)
+        if abs(fd - float(np.sum(dx * u))) > 1e-7 * max(1.0, abs(fd)):
+            return False
+        if weight is not None:
+            u = rng.standard_normal(32)
+            fd = _fd_dir(loss, (x, weight), 1, u)
+            if abs(fd - float(np.sum(dw * u))) > 1e-7 * max(1.0, abs(fd)):
+                return False
+    xt = _t(x).requires_grad_(True)
+    wt = _t(wgt).requires_grad_(True)
+    (F.rms_norm(xt, (32,), weight=wt, eps=1e-3) * _t(dy)).sum().backward()
+    dx, dw = mod.rms_norm_bwd(x, dy, 1e-3, wgt)
+    return np.abs(dx - xt.grad.numpy()).max() < 1e-12 and np.abs(dw - wt.grad.numpy()).max() < 1e-12
+
+
+def test_gate_backward_pins():
+    assert _gate_pins_hold(fox_oracle)
+
+
+def test_rms_norm_backward_pins():
+    assert _rms_pins_hold(fox_oracle)
+
+
+def test_gate_backward_linear_and_zero():
+    x, w, b, g = _pro_small()
+    a = oracle.gate_logf_bwd(x, w, b, g)
+    a2 = oracle.gate_logf_bwd(x, w, b, -2.5 * g)
+    for p, q in zip(a, a2):
+        assert np.abs(q + 2.5 * p).max() < 1e-12
+    for z in oracle.gate_logf_bwd(x, w, b, 0 * g):
+        assert np.abs(z).max() == 0.0
+
+
+def test_rms_norm_backward_scale_invariance():
+    """With eps = 0 and unit weights the output ignores the row's scale, so x . dx = 0."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((9, 64))
+    dx, dw = oracle.rms_norm_bwd(x, rng.standard_normal((9, 64)), 0.0)
+    assert dw is None
+    assert np.abs(np.sum(x * dx, axis=-1)).max() < 1e-12
+
+
+PRO_MUTATIONS = {
+    "gate_sigmoid_sign": ("dz = g * np.exp(log_sigmoid(-z))", "dz = g * np.exp(log_sigmoid(z))"),
+    "gate_dx_transpose": ('dx = np.einsum("bhl,hd->bld", dz, w_f)', 'dx = np.einsum("bhl,hd->bld", g, w_f)'),
+    "gate_db_axis": ("db_f = dz.sum(axis=(0, 2))", "db_f = g.sum(axis=(0, 2))"),
+    "rms_mean_term": ("dx = (g - xh * np.mean(g * xh, axis=-1, keepdims=True)) / r", "dx = g / r"),
+    "rms_dw_unnormalised": ("dw = None if weight is None else (dy * xh).reshape(-1, x.shape[-1]).sum(axis=0)",
+                            "dw = None if weight is None else (dy * x).reshape(-1, x.shape[-1]).sum(axis=0)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PRO_MUTATIONS))
+def test_planted_pro_backward_mistake_is_caught(name):
+    src = open(fox_oracle.__file__).read()
+    old, new = PRO_MUTATIONS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle_pro_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    assert not (_gate_pins_hold(mod) and _rms_pins_hold(mod))
