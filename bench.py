@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--paper-shape", action="store_true",
                     help="the FoX paper's own head shape instead: B=1, H=24, L=16384, D=64 "
                          "(same input recipe); a second measurement, not the headline line")
+    ap.add_argument("--pro", action="store_true",
+                    help="the Pro block's whole attention step instead (workload 4 plus dO): gate, "
+                         "scan, QK-norm, attention forward and backward, QK-norm and gate backward")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run 3 device copies of this many MiB (a known-size kernel "
                          "that scales HBM byte counters)")
@@ -133,6 +136,8 @@ def main():
     fox.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.pro:
+        return pro_step(args, torch, fi, fox, dev)
     if args.paper_shape:
         case = fi.make_case(1, 24, 16384, 64, "bf16", seed=6, gate="per_head", with_do=True,
                             name="paper_shape")
@@ -245,6 +250,89 @@ def main():
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_heads} heads (CPU) ...")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+def pro_step(args, torch, fi, fox, dev):
+    """One training step of the Pro block's attention path (workload 4 plus a seeded dO)."""
+    case = fi.config_case(4)
+    B, H, L, D, dm = case.B, case.H, case.L, case.D, case.x.shape[-1]
+    up = lambda a, dt: (torch.from_numpy(fi.bf16_bits(a)).view(torch.bfloat16) if dt == "bf16"
+                        else torch.from_numpy(np.ascontiguousarray(a, np.float32))).to(dev)
+    x, q, k, v = up(case.x, "bf16"), up(case.q, "bf16"), up(case.k, "bf16"), up(case.v, "bf16")
+    w_f, b_f = up(case.w_f, "f32"), up(case.b_f, "f32")
+    do = up(fi.bf16_round(np.random.default_rng(45).standard_normal((B, H, L, D),
+                                                                    dtype=np.float32)), "bf16")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    names = ["gate", "scan", "qnorm", "knorm", "fwd", "delta", "dq", "dkv", "dlogf", "qnorm_bwd",
+             "knorm_bwd", "gate_bwd"]
+
+    def step(events):
+        def run(n, fn):
+            if events is None:
+                return fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r = fn()
+            e1.record(stream)
+            events.append((n, e0, e1))
+            return r
+        lf = run("gate", lambda: fox.fox_gate_logf(x, w_f, b_f))
+        c = run("scan", lambda: fox.fox_logf_cumsum(lf))
+        qn = run("qnorm", lambda: fox.fox_qk_rmsnorm(q, eps=1e-6))
+        kn = run("knorm", lambda: fox.fox_qk_rmsnorm(k, eps=1e-6))
+        o, lse = run("fwd", lambda: fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32))
+        delta = run("delta", lambda: fox.fox_attn_bwd_delta(do, o))
+        dqn, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(qn, kn, v, c, lse, do, delta,
+                                                                 delta_out=delta))
+        dkn, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(qn, kn, v, c, lse, do, delta))
+        dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
+        dq, _ = run("qnorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(q, dqn, eps=1e-6))
+        dk, _ = run("knorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(k, dkn, eps=1e-6))
+        dx, dw, db = run("gate_bwd", lambda: fox.fox_gate_logf_bwd(x, w_f, b_f, dlf))
+        return dq, dk, dv, dx, dw, db
+
+    for _ in range(args.warmup):
+        step(None)
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = events[0][1].elapsed_time(events[-1][2]) / args.steps
+    kern_ms = {n: float(np.mean([a.elapsed_time(b) for m, a, b in events if m == n])) for n in names}
+    unit = contraction_flops(B, H, L, D)
+    value = 7 * unit / (ms_per_step * 1e-3) / 1e12
+    n_tok, n_qk = B * L, B * H * L * D
+    # algorithmic bytes: every input read once, every output written once
+    hbm_bytes = {
+        "gate": n_tok * dm * 2 + B * H * L * 4,
+        "qnorm": n_qk * 2 * 2, "knorm": n_qk * 2 * 2,
+        "qnorm_bwd": n_qk * (2 + 4 + 4), "knorm_bwd": n_qk * (2 + 4 + 4),
+        "gate_bwd": n_tok * dm * (2 + 4) + B * H * L * 4,
+    }
+    hbm = {n: {"ms": round(kern_ms[n], 4), "bytes": int(b),
+               "GB_per_s": round(b / (kern_ms[n] * 1e-3) / 1e9, 1),
+               "frac_of_8TBps": round(b / (kern_ms[n] * 1e-3) / 8e12, 4)} for n, b in hbm_bytes.items()}
+    fwd_tf = 2 * unit / (kern_ms["fwd"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "pro_block_attention_step B=1 H=12 L=16384 D=128 d_model=1536 "
+                               "(gate, scan, QK-norm, attention fwd+bwd, QK-norm and gate "
+                               "backward; bf16 x/q/k/v/dO; 7 contractions credited)",
+                   "B": B, "H": H, "L": L, "D": D, "d_model": dm, "causal": True},
+        "fwd": {"kernel_ms": round(kern_ms["fwd"], 4), "tflops": round(fwd_tf, 2),
+                "frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "hbm_kernels": hbm,
+        "kernel_ms": {n: round(kern_ms[n], 4) for n in names},
+        "host_wall_ms_per_step": round(wall_ms, 4),
+    }
     print(json.dumps(out), flush=True)
 
 

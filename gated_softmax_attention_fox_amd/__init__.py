@@ -49,6 +49,13 @@ _SIGS = {
                                      _c_i64, _c_i64, _c_vp]),
     "fox_qk_rmsnorm": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int, _c_i64, _c_i64, _c_f32, _c_vp,
                                       _c_vp]),
+    "fox_gate_logf_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "fox_gate_logf_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                         _c_vp, _c_vp, _c_sz, _c_i64, _c_i64, _c_i64, _c_i64,
+                                         _c_vp]),
+    "fox_qk_rmsnorm_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
+    "fox_qk_rmsnorm_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                          _c_sz, _c_i64, _c_i64, _c_f32, _c_vp]),
     "fox_attn_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int,
                                     _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, _c_u32, _c_vp]),
     "fox_attn_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
@@ -178,6 +185,58 @@ def fox_qk_rmsnorm(x: torch.Tensor, eps: float = 1e-6, weight: torch.Tensor | No
     _check(lib.fox_qk_rmsnorm(px, po, _code(x.dtype), x.numel() // D, D, eps, pw, _stream(x)),
            "fox_qk_rmsnorm")
     return out
+
+
+def fox_gate_logf_bwd(x: torch.Tensor, w_f: torch.Tensor, b_f: torch.Tensor,
+                      dlog_f: torch.Tensor):
+    """(dx [B, L, d_model], dw_f [H, d_model], db_f [H]), all fp32, given dlog_f [B, H, L]."""
+    lib = load_library()
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
+    pw = _dev(w_f, "w_f", (torch.float32,), 2)
+    pb = _dev(b_f, "b_f", (torch.float32,), 1)
+    pg = _dev(dlog_f, "dlog_f", (torch.float32,), 3)
+    B, L, dm = x.shape
+    H = w_f.shape[0]
+    if w_f.shape[1] != dm or b_f.shape[0] != H or tuple(dlog_f.shape) != (B, H, L):
+        raise ValueError("w_f must be [H, d_model], b_f [H] and dlog_f [B, H, L]")
+    dx = torch.empty((B, L, dm), dtype=torch.float32, device=x.device)
+    dw = torch.empty((H, dm), dtype=torch.float32, device=x.device)
+    db = torch.empty((H,), dtype=torch.float32, device=x.device)
+    need = int(lib.fox_gate_logf_bwd_workspace_bytes(B, L, dm, H))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(lib.fox_gate_logf_bwd(px, _code(x.dtype), pw, pb, pg, ctypes.c_void_p(dx.data_ptr()),
+                                 ctypes.c_void_p(dw.data_ptr()), ctypes.c_void_p(db.data_ptr()),
+                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), B, L, dm, H,
+                                 _stream(x)), "fox_gate_logf_bwd")
+    return dx, dw, db
+
+
+def fox_qk_rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, eps: float = 1e-6,
+                       weight: torch.Tensor | None = None, want_dweight: bool = False):
+    """(dx fp32, dweight fp32 or None) of the QK-norm, given its input x and dy (fp32)."""
+    lib = load_library()
+    px = _dev(x, "x", (torch.bfloat16, torch.float32))
+    pdy = _dev(dy, "dy", (torch.float32,))
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    D = x.shape[-1]
+    rows = x.numel() // D
+    dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    pw = ctypes.c_void_p(0)
+    if weight is not None:
+        pw = _dev(weight, "weight", (torch.float32,), 1)
+    dwt, pdw, ws, nws = None, ctypes.c_void_p(0), ctypes.c_void_p(0), 0
+    if want_dweight:
+        if weight is None:
+            raise ValueError("want_dweight needs weight")
+        dwt = torch.empty((D,), dtype=torch.float32, device=x.device)
+        pdw = ctypes.c_void_p(dwt.data_ptr())
+        need = int(lib.fox_qk_rmsnorm_bwd_workspace_bytes(rows, D))
+        wst = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+        ws, nws = ctypes.c_void_p(wst.data_ptr()), wst.numel()
+    _check(lib.fox_qk_rmsnorm_bwd(px, _code(x.dtype), pdy, ctypes.c_void_p(dx.data_ptr()), pw, pdw,
+                                  ws, nws, rows, D, eps, _stream(x)), "fox_qk_rmsnorm_bwd")
+    return dx, dwt
 
 
 def _bhld(q, k, v):

@@ -126,6 +126,70 @@ fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, in
                   "fox_qk_rmsnorm");
 }
 
+size_t fox_gate_logf_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H) {
+  if (B < 1 || L < 1 || d_model < 1 || H < 1) return 0;
+  return fox::gate_bwd_workspace_bytes(B, L, d_model, H);
+}
+
+fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
+                             const float* dlog_f, float* dx, float* dw_f, float* db_f,
+                             void* workspace, size_t workspace_bytes, int64_t B, int64_t L,
+                             int64_t d_model, int64_t H, void* stream) {
+  FOX_REQUIRE_PTR(x);
+  FOX_REQUIRE_PTR(w_f);
+  FOX_REQUIRE(b_f != nullptr, "b_f must not be NULL");
+  FOX_REQUIRE_PTR(dlog_f);
+  FOX_REQUIRE_PTR(dx);
+  FOX_REQUIRE_PTR(dw_f);
+  FOX_REQUIRE(db_f != nullptr, "db_f must not be NULL");
+  FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL");
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+              "workspace must be 256-byte aligned");
+  FOX_REQUIRE(x_dt == FOX_BF16 || x_dt == FOX_F32, "x_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(B >= 1 && L >= 1 && L <= kMaxL, "B >= 1 and 1 <= L <= 2^23 required");
+  FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
+  FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
+              "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
+  FOX_REQUIRE(B * L <= (int64_t(1) << 31) / 64 && B * L * d_model <= kMaxElems,
+              "B*L*d_model too large");
+  const size_t need = fox::gate_bwd_workspace_bytes(B, L, d_model, H);
+  FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
+              workspace_bytes, need);
+  return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w_f, b_f, dlog_f, dx, dw_f, db_f,
+                                       workspace, B, L, d_model, H, (hipStream_t)stream),
+                  "fox_gate_logf_bwd");
+}
+
+size_t fox_qk_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D) {
+  if (rows < 1 || !(D == 64 || D == 128)) return 0;
+  return fox::rmsnorm_bwd_workspace_bytes(rows, D);
+}
+
+fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, float* dx,
+                              const float* weight, float* dweight, void* workspace,
+                              size_t workspace_bytes, int64_t rows, int64_t D, float eps,
+                              void* stream) {
+  FOX_REQUIRE_PTR(x);
+  FOX_REQUIRE_PTR(dy);
+  FOX_REQUIRE_PTR(dx);
+  FOX_REQUIRE(dt == FOX_BF16 || dt == FOX_F32, "dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
+  FOX_REQUIRE(rows >= 1 && rows * D <= kMaxElems, "rows out of range");
+  FOX_REQUIRE(eps >= 0.f, "eps must be >= 0");
+  FOX_REQUIRE(!(dweight && !weight), "dweight needs the weight it is the gradient of");
+  if (dweight) {
+    FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL when dweight is wanted");
+    FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+                "workspace must be 256-byte aligned");
+    const size_t need = fox::rmsnorm_bwd_workspace_bytes(rows, D);
+    FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  }
+  return launched(fox::launch_rmsnorm_bwd(x, dt == FOX_BF16, dy, weight, dx, dweight, workspace,
+                                          rows, D, eps, (hipStream_t)stream),
+                  "fox_qk_rmsnorm_bwd");
+}
+
 fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
                         const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B, int64_t H,
                         int64_t L, int64_t D, float scale, uint32_t flags, void* stream) {

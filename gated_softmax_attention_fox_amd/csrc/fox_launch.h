@@ -17,6 +17,20 @@ hipError_t launch_rev_cumsum2(const float* a, const float* b, float* out, int64_
 // log_f[b, h, t] = log sigmoid(x[b, t, :] . w_f[h, :] + b_f[h]).
 hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* log_f,
                        int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s);
+// Backward of the gate: dz[b, t, h] = dlog_f[b, h, t] * sigma(-z) (token-major).
+hipError_t launch_gate_dz(const void* x, bool x_bf16, const float* w_f, const float* b_f,
+                          const float* dlog_f, float* dz, int64_t B, int64_t L, int64_t d_model,
+                          int64_t H, hipStream_t s);
+// Backward of the gate: dx, dw_f, db_f (workspace: gate_bwd_workspace_bytes).
+size_t gate_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H);
+hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const float* b_f,
+                           const float* dlog_f, float* dx, float* dw_f, float* db_f, void* ws,
+                           int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s);
+// Backward of the QK-norm: dx and, when dw is not null, the weight gradient.
+size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D);
+hipError_t launch_rmsnorm_bwd(const void* x, bool bf16, const float* dy, const float* w, float* dx,
+                              float* dw, void* ws, int64_t rows, int64_t D, float eps,
+                              hipStream_t s);
 // y = x / sqrt(mean(x^2) + eps) * w over rows of length D.
 hipError_t launch_rmsnorm(const void* x, void* y, bool bf16, int64_t rows, int64_t D, float eps,
                           const float* w, hipStream_t s);

@@ -10,6 +10,10 @@
 // addresses (scalar loads), so the inner loop is one FMA per (token, head, column). The four
 // per-wave partial sums meet in LDS and lane t writes log f for token t, evaluated stably as
 // -log1p(exp(-z)) for z >= 0 and z - log1p(exp(z)) otherwise.
+//
+// The same kernel serves the backward (kBwd): it recomputes z and writes, token-major,
+// dz[b, t, h] = dlog_f[b, h, t] * sigma(-z), since d log sigma(z) / dz = 1 - sigma(z) = sigma(-z);
+// sigma(-z) = 1 / (1 + exp(z)) goes to 0 or 1 in the limits without a NaN.
 #include "fox_device.h"
 #include "fox_launch.h"
 
@@ -25,11 +29,12 @@ __device__ __forceinline__ float log_sigmoid(float z) {
   return z >= 0.f ? -log1pf(expf(-z)) : z - log1pf(expf(z));
 }
 
-template <bool kBf16>
+template <bool kBf16, bool kBwd>
 __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w_f,
                                                    const float* __restrict__ b_f,
-                                                   float* __restrict__ log_f, int L, int dm, int H,
+                                                   const float* __restrict__ dlog_f,
+                                                   float* __restrict__ out, int L, int dm, int H,
                                                    int tok_blocks) {
   __shared__ bf16_t xs_b[kBf16 ? kGateTok * kGatePitch : 1];
   __shared__ float xs_f[kBf16 ? 1 : kGateTok * kGatePitch];
@@ -105,7 +110,14 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     for (int h = 0; h < nh; ++h) {
       const float z = ((red[0][h][lane] + red[1][h][lane]) + (red[2][h][lane] + red[3][h][lane])) +
                       b_f[h0 + h];
-      if (t < L) log_f[((size_t)b * H + h0 + h) * L + t] = log_sigmoid(z);
+      if (t < L) {
+        if constexpr (kBwd) {
+          const float g = dlog_f[((size_t)b * H + h0 + h) * L + t];
+          out[((size_t)b * L + t) * H + h0 + h] = g / (1.0f + expf(z));
+        } else {
+          out[((size_t)b * H + h0 + h) * L + t] = log_sigmoid(z);
+        }
+      }
     }
   }
 }
@@ -117,11 +129,25 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float
   const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
   const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
   if (x_bf16)
-    hipLaunchKernelGGL(gate_kernel<true>, grid, dim3(256), 0, s, x, w_f, b_f, log_f, (int)L,
-                       (int)d_model, (int)H, tok_blocks);
+    hipLaunchKernelGGL((gate_kernel<true, false>), grid, dim3(256), 0, s, x, w_f, b_f, nullptr,
+                       log_f, (int)L, (int)d_model, (int)H, tok_blocks);
   else
-    hipLaunchKernelGGL(gate_kernel<false>, grid, dim3(256), 0, s, x, w_f, b_f, log_f, (int)L,
-                       (int)d_model, (int)H, tok_blocks);
+    hipLaunchKernelGGL((gate_kernel<false, false>), grid, dim3(256), 0, s, x, w_f, b_f, nullptr,
+                       log_f, (int)L, (int)d_model, (int)H, tok_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_dz(const void* x, bool x_bf16, const float* w_f, const float* b_f,
+                          const float* dlog_f, float* dz, int64_t B, int64_t L, int64_t d_model,
+                          int64_t H, hipStream_t s) {
+  const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
+  const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
+  if (x_bf16)
+    hipLaunchKernelGGL((gate_kernel<true, true>), grid, dim3(256), 0, s, x, w_f, b_f, dlog_f, dz,
+                       (int)L, (int)d_model, (int)H, tok_blocks);
+  else
+    hipLaunchKernelGGL((gate_kernel<false, true>), grid, dim3(256), 0, s, x, w_f, b_f, dlog_f, dz,
+                       (int)L, (int)d_model, (int)H, tok_blocks);
   return hipGetLastError();
 }
 

@@ -1,0 +1,255 @@
+// pro_bwd.hip — backward of the Pro block's preprocessing: the forget gate's GEMV and the
+// QK-norm (paper-graph-ui summary of arXiv 2503.02130, section 3.4, "Forget Gate Computation" and
+// "The Pro Block Architecture", Steps 1-2 and 4). Both are HBM-bound; every reduction runs in a
+// fixed order (per-chunk partials, then a second pass), so the results are deterministic.
+//
+// Gate: given dz[b, t, h] (gate.hip, backward mode),
+//   dx[b, t, :] = sum_h dz[b, t, h] w_f[h, :]        (one pass over the tokens)
+//   dw_f[h, :]  = sum_{b,t} dz[b, t, h] x[b, t, :]   (partials per 256-token chunk, then a sum)
+//   db_f[h]     = sum_{b,t} dz[b, t, h]
+// QK-norm: with r = 1 / sqrt(mean x^2 + eps), xh = x r and g = dy w (w = 1 when absent),
+//   dx = r (g - xh mean(g xh)),  dw = sum over rows of dy xh  (partials per workgroup, then a sum).
+#include "fox_device.h"
+#include "fox_launch.h"
+
+namespace fox {
+namespace {
+
+constexpr int kChunk = 256;   // tokens per dw_f partial
+constexpr int kHGroup = 16;   // heads per dw_f partial workgroup
+constexpr int kRmsBlocks = 1024;
+
+__device__ __forceinline__ float load_x(const void* x, bool bf16, size_t i) {
+  return bf16 ? bf2f(static_cast<const bf16_t*>(x)[i]) : static_cast<const float*>(x)[i];
+}
+
+// dx[r, d .. d+7] for token r (one thread per 8 columns).
+__global__ __launch_bounds__(256) void gate_dx_kernel(const float* __restrict__ dz,
+                                                      const float* __restrict__ w_f,
+                                                      float* __restrict__ dx, int64_t rows, int dm,
+                                                      int H) {
+  const int groups = dm / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= rows * groups) return;
+  const int64_t r = gid / groups;
+  const int d = (int)(gid % groups) * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int h = 0; h < H; ++h) {
+    const float g = dz[r * H + h];
+    const float4 w0 = *reinterpret_cast<const float4*>(w_f + (size_t)h * dm + d);
+    const float4 w1 = *reinterpret_cast<const float4*>(w_f + (size_t)h * dm + d + 4);
+    acc[0] = fmaf(g, w0.x, acc[0]); acc[1] = fmaf(g, w0.y, acc[1]);
+    acc[2] = fmaf(g, w0.z, acc[2]); acc[3] = fmaf(g, w0.w, acc[3]);
+    acc[4] = fmaf(g, w1.x, acc[4]); acc[5] = fmaf(g, w1.y, acc[5]);
+    acc[6] = fmaf(g, w1.z, acc[6]); acc[7] = fmaf(g, w1.w, acc[7]);
+  }
+  *reinterpret_cast<float4*>(dx + r * dm + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *reinterpret_cast<float4*>(dx + r * dm + d + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// Partial dw_f and db_f of one 256-token chunk, one 256-column slab and up to 16 heads: thread c
+// owns column slab * 256 + c and walks the chunk's tokens (coalesced rows of x).
+template <bool kBf16>
+__global__ __launch_bounds__(256) void gate_dw_partial_kernel(const void* __restrict__ x,
+                                                              const float* __restrict__ dz,
+                                                              float* __restrict__ part,
+                                                              float* __restrict__ part_db,
+                                                              int64_t rows, int dm, int H) {
+  __shared__ float dzs[kChunk][kHGroup];
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x, slab = blockIdx.y, h0 = blockIdx.z * kHGroup;
+  const int nh = H - h0 < kHGroup ? H - h0 : kHGroup;
+  const int64_t r0 = (int64_t)chunk * kChunk;
+  const int n = rows - r0 < kChunk ? (int)(rows - r0) : kChunk;
+  for (int i = tid; i < kChunk * kHGroup; i += 256) {
+    const int r = i / kHGroup, h = i % kHGroup;
+    dzs[r][h] = (r < n && h < nh) ? dz[(r0 + r) * H + h0 + h] : 0.f;
+  }
+  __syncthreads();
+  const int d = slab * 256 + tid;
+  if (d < dm) {
+    float acc[kHGroup];
+#pragma unroll
+    for (int h = 0; h < kHGroup; ++h) acc[h] = 0.f;
+    for (int r = 0; r < n; ++r) {
+      const float xv = load_x(x, kBf16, (size_t)(r0 + r) * dm + d);
+#pragma unroll
+      for (int h = 0; h < kHGroup; ++h) acc[h] = fmaf(dzs[r][h], xv, acc[h]);
+    }
+    for (int h = 0; h < nh; ++h) part[((size_t)chunk * H + h0 + h) * dm + d] = acc[h];
+  }
+  if (slab == 0 && tid < nh) {
+    float sum = 0.f;
+    for (int r = 0; r < n; ++r) sum += dzs[r][tid];
+    part_db[(size_t)chunk * H + h0 + tid] = sum;
+  }
+}
+
+// dw_f[h, d] and db_f[h] as the chunk partials summed in chunk order.
+__global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __restrict__ part,
+                                                             const float* __restrict__ part_db,
+                                                             float* __restrict__ dw_f,
+                                                             float* __restrict__ db_f, int n_chunk,
+                                                             int dm, int H) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n_w = (int64_t)H * dm;
+  if (gid < n_w) {
+    float s = 0.f;
+    for (int c = 0; c < n_chunk; ++c) s += part[(size_t)c * n_w + gid];
+    dw_f[gid] = s;
+  } else if (gid < n_w + H) {
+    const int h = (int)(gid - n_w);
+    float s = 0.f;
+    for (int c = 0; c < n_chunk; ++c) s += part_db[(size_t)c * H + h];
+    db_f[h] = s;
+  }
+}
+
+// QK-norm backward, D / 8 lanes per row, grid-stride over rows; with kDw each workgroup also sums
+// dy * xh over its rows into one partial row of length D.
+template <int D, bool kBf16, bool kDw>
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const void* __restrict__ x,
+                                                          const float* __restrict__ dy,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ dx,
+                                                          float* __restrict__ part, int64_t rows,
+                                                          float eps) {
+  constexpr int G = D / 8, RPB = 256 / G;
+  __shared__ float red[kDw ? RPB : 1][kDw ? D : 1];
+  const int tid = threadIdx.x, sub = tid / G, pc = (tid % G) * 8;
+  float wv[8], dwp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    wv[e] = w ? w[pc + e] : 1.0f;
+    dwp[e] = 0.f;
+  }
+  for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row < rows; row += (int64_t)gridDim.x * RPB) {
+    // the G lanes of a row are consecutive in one wave and share `row`, so they stay together
+    const size_t off = (size_t)row * D + pc;
+    float v[8], g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = load_x(x, kBf16, off + e);
+    const float4 d0 = *reinterpret_cast<const float4*>(dy + off);
+    const float4 d1 = *reinterpret_cast<const float4*>(dy + off + 4);
+    const float dyv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    float sg = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] *= r;  // xh
+      g[e] = dyv[e] * wv[e];
+      sg = fmaf(g[e], v[e], sg);
+    }
+#pragma unroll
+    for (int m = 1; m < G; m <<= 1) sg += __shfl_xor(sg, m, 64);
+    const float mean = sg / (float)D;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[e] = r * (g[e] - v[e] * mean);
+      if (kDw) dwp[e] = fmaf(dyv[e], v[e], dwp[e]);
+    }
+    *reinterpret_cast<float4*>(dx + off) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(dx + off + 4) = make_float4(o[4], o[5], o[6], o[7]);
+  }
+  if constexpr (kDw) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[sub][pc + e] = dwp[e];
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.f;
+      for (int i = 0; i < RPB; ++i) s += red[i][tid];
+      part[(size_t)blockIdx.x * D + tid] = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(128) void rmsnorm_dw_reduce_kernel(const float* __restrict__ part,
+                                                                float* __restrict__ dw, int nblk,
+                                                                int D) {
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  float s = 0.f;
+  for (int b = 0; b < nblk; ++b) s += part[(size_t)b * D + d];
+  dw[d] = s;
+}
+
+size_t granule(size_t floats) { return (floats + 63) / 64 * 64; }  // 256-byte granules
+
+template <int D, bool kBf16>
+hipError_t go_rms_bwd(const void* x, const float* dy, const float* w, float* dx, float* dw,
+                      float* part, int64_t rows, float eps, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t need = (rows + RPB - 1) / RPB;
+  if (dw) {
+    const int nblk = (int)(need < kRmsBlocks ? need : kRmsBlocks);
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<D, kBf16, true>), dim3((unsigned)nblk), dim3(256), 0, s,
+                       x, dy, w, dx, part, rows, eps);
+    hipLaunchKernelGGL(rmsnorm_dw_reduce_kernel, dim3(1), dim3(128), 0, s, part, dw, nblk, D);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_bwd_kernel<D, kBf16, false>), dim3((unsigned)need), dim3(256), 0,
+                       s, x, dy, w, dx, nullptr, rows, eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gate_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H) {
+  const int64_t rows = B * L;
+  const int64_t n_chunk = (rows + kChunk - 1) / kChunk;
+  return 4 * (granule((size_t)(rows * H)) + granule((size_t)(n_chunk * H * d_model)) +
+              granule((size_t)(n_chunk * H)));
+}
+
+hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const float* b_f,
+                           const float* dlog_f, float* dx, float* dw_f, float* db_f, void* ws,
+                           int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
+  const int64_t rows = B * L;
+  const int n_chunk = (int)((rows + kChunk - 1) / kChunk);
+  float* dz = static_cast<float*>(ws);
+  float* part = dz + granule((size_t)(rows * H));
+  float* part_db = part + granule((size_t)((int64_t)n_chunk * H * d_model));
+  hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dlog_f, dz, B, L, d_model, H, s);
+  if (e != hipSuccess) return e;
+  const int64_t dx_threads = rows * (d_model / 8);
+  hipLaunchKernelGGL(gate_dx_kernel, dim3((unsigned)((dx_threads + 255) / 256)), dim3(256), 0, s,
+                     dz, w_f, dx, rows, (int)d_model, (int)H);
+  const dim3 pg((unsigned)n_chunk, (unsigned)((d_model + 255) / 256),
+                (unsigned)((H + kHGroup - 1) / kHGroup));
+  if (x_bf16)
+    hipLaunchKernelGGL((gate_dw_partial_kernel<true>), pg, dim3(256), 0, s, x, dz, part, part_db,
+                       rows, (int)d_model, (int)H);
+  else
+    hipLaunchKernelGGL((gate_dw_partial_kernel<false>), pg, dim3(256), 0, s, x, dz, part, part_db,
+                       rows, (int)d_model, (int)H);
+  const int64_t red = H * d_model + H;
+  hipLaunchKernelGGL(gate_dw_reduce_kernel, dim3((unsigned)((red + 255) / 256)), dim3(256), 0, s,
+                     part, part_db, dw_f, db_f, n_chunk, (int)d_model, (int)H);
+  return hipGetLastError();
+}
+
+size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D) {
+  (void)rows;
+  return 4 * granule((size_t)kRmsBlocks * (size_t)D);
+}
+
+hipError_t launch_rmsnorm_bwd(const void* x, bool bf16, const float* dy, const float* w, float* dx,
+                              float* dw, void* ws, int64_t rows, int64_t D, float eps,
+                              hipStream_t s) {
+  float* part = static_cast<float*>(ws);
+  if (D == 64)
+    return bf16 ? go_rms_bwd<64, true>(x, dy, w, dx, dw, part, rows, eps, s)
+                : go_rms_bwd<64, false>(x, dy, w, dx, dw, part, rows, eps, s);
+  return bf16 ? go_rms_bwd<128, true>(x, dy, w, dx, dw, part, rows, eps, s)
+              : go_rms_bwd<128, false>(x, dy, w, dx, dw, part, rows, eps, s);
+}
+
+}  // namespace fox

@@ -77,6 +77,34 @@ fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const 
 fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, int64_t D,
                           float eps, const float* weight, void* stream);
 
+/* Backward of the gate (paper-graph-ui summary, "Forget Gate Computation"; Pro block Step 4),
+ * for the loss whose gradient with respect to log_f is dlog_f ([B, H, L] fp32):
+ *   dz[b, h, t] = dlog_f[b, h, t] * sigmoid(-z[b, h, t])   (z recomputed from x, w_f, b_f)
+ *   dx[b, t, :] = sum_h dz[b, h, t] w_f[h, :]              [B, L, d_model] fp32 output
+ *   dw_f[h, :]  = sum_{b,t} dz[b, h, t] x[b, t, :]         [H, d_model] fp32 output
+ *   db_f[h]     = sum_{b,t} dz[b, h, t]                    [H] fp32 output
+ * x, w_f, b_f, shapes and limits as for fox_gate_logf. workspace: device memory of at least
+ * fox_gate_logf_bwd_workspace_bytes(B, L, d_model, H) bytes, 256-byte aligned, contents ignored.
+ * fp32 arithmetic; sums over tokens run in a fixed order (deterministic, no atomics). */
+size_t fox_gate_logf_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H);
+fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
+                             const float* dlog_f, float* dx, float* dw_f, float* db_f,
+                             void* workspace, size_t workspace_bytes, int64_t B, int64_t L,
+                             int64_t d_model, int64_t H, void* stream);
+
+/* Backward of the QK-norm (Pro block Steps 1-2), y = x / sqrt(mean x^2 + eps) * weight:
+ *   x  : [rows, D] in dtype dt (the norm's input);  dy : [rows, D] fp32 (gradient of y)
+ *   dx : [rows, D] fp32 output, dx = r (g - xh mean(g xh)) with r = 1 / sqrt(mean x^2 + eps),
+ *        xh = x r, g = dy * weight (weight NULL: unit weights)
+ *   dweight : [D] fp32 output sum_rows dy * xh, or NULL if not wanted (needs weight != NULL);
+ *        then workspace must hold fox_qk_rmsnorm_bwd_workspace_bytes(rows, D) bytes, 256-byte
+ *        aligned (it may be NULL when dweight is NULL). Deterministic (fixed-order sums). */
+size_t fox_qk_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D);
+fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, float* dx,
+                              const float* weight, float* dweight, void* workspace,
+                              size_t workspace_bytes, int64_t rows, int64_t D, float eps,
+                              void* stream);
+
 /* Forward (paper-graph-ui summary, "Hardware-Aware Implementation", the forward pass;
  * paperlayer.ai summary, section E):
  *   O[i]   = sum_{j<=i} softmax_j(scale * q_i . k_j + c_i - c_j) v_j

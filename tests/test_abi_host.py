@@ -114,3 +114,22 @@ def test_binding_rejects_cpu_tensors(lib):
     c = torch.zeros(1, 2, 8)
     with pytest.raises(ValueError):
         fox.fox_attn_fwd(x, x, x, c)
+
+
+def test_pro_backward_rejects(lib):
+    ws = 256 * 1024  # a 256-aligned stand-in address, never dereferenced
+    f = lib.fox_gate_logf_bwd
+    # d_model % 8, H > 64, dtype, unaligned workspace, short workspace
+    assert f(P, 1, P, P, P, P, P, P, ws, 1 << 30, 1, 8, 12, 2, None) == 1
+    assert f(P, 1, P, P, P, P, P, P, ws, 1 << 30, 1, 8, 16, 65, None) == 1
+    assert f(P, 2, P, P, P, P, P, P, ws, 1 << 30, 1, 8, 16, 2, None) == 1
+    assert f(P, 1, P, P, P, P, P, P, ws + 16, 1 << 30, 1, 8, 16, 2, None) == 1
+    assert f(P, 1, P, P, P, P, P, P, ws, 16, 1, 8, 16, 2, None) == 1
+    assert lib.fox_gate_logf_bwd_workspace_bytes(1, 16384, 1536, 12) >= 4 * 16384 * 12
+    assert lib.fox_gate_logf_bwd_workspace_bytes(0, 8, 16, 2) == 0
+    g = lib.fox_qk_rmsnorm_bwd
+    assert g(P, 1, P, P, None, None, None, 0, 10, 96, ctypes.c_float(1e-6), None) == 1  # D
+    assert g(P, 1, P, P, None, P, ws, 1 << 20, 10, 128, ctypes.c_float(1e-6), None) == 1  # dweight without weight
+    assert g(P, 1, P, P, P, P, None, 0, 10, 128, ctypes.c_float(1e-6), None) == 1  # no workspace
+    assert g(P, 1, P, P, None, None, None, 0, 10, 128, ctypes.c_float(-1.0), None) == 1  # eps
+    assert lib.fox_qk_rmsnorm_bwd_workspace_bytes(10, 128) >= 1024 * 128 * 4

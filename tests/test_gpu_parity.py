@@ -242,6 +242,68 @@ def test_pro_pipeline_config4(fox):
     check("LSE sampled rows", np.concatenate(gl), np.concatenate(rl))
 
 
+# ------------------------------------------------------------------------------------- Pro backward
+def _check_tight(name, got, ref, rel=1e-5):
+    """The bf16 bar, plus a relative-L2 bound that fp32 arithmetic on these inputs must meet."""
+    check(name, got, ref)
+    g, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    rl = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    assert rl <= rel, f"{name}: relative L2 {rl:.3e} > {rel:g} (fp32 arithmetic)"
+
+
+@pytest.mark.parametrize("x_dt", ["bf16", "f32"])
+def test_gate_backward_config4(fox, x_dt):
+    """dx, dw_f, db_f of the gate at config 4's shape (x [1, 16384, 1536], 12 heads)."""
+    case = fi.config_case(4)
+    x = case.x if x_dt == "bf16" else case.x.astype(np.float32)
+    g = np.random.default_rng(44).standard_normal((case.B, case.H, case.L)).astype(np.float32)
+    say(f"gate backward config4 x={x_dt}")
+    dx, dw, db = fox.fox_gate_logf_bwd(dev(x, x_dt), dev(case.w_f, "f32"), dev(case.b_f, "f32"),
+                                       dev(g, "f32"))
+    torch.cuda.synchronize()
+    rdx, rdw, rdb = oracle.gate_logf_bwd(x, case.w_f, case.b_f, g)
+    _check_tight("dx", host(dx), rdx)
+    _check_tight("dw_f", host(dw), rdw)
+    _check_tight("db_f", host(db), rdb)
+
+
+@pytest.mark.parametrize("B,L,dm,H", [(2, 1, 8, 1), (1, 77, 40, 3), (3, 300, 264, 17)])
+def test_gate_backward_ragged(fox, B, L, dm, H):
+    rng = np.random.default_rng(B * 1000 + L)
+    x = fi.bf16_round(rng.standard_normal((B, L, dm)).astype(np.float32))
+    w = (0.1 * rng.standard_normal((H, dm))).astype(np.float32)
+    b = rng.uniform(-6, 6, size=H).astype(np.float32)
+    g = rng.standard_normal((B, H, L)).astype(np.float32)
+    dx, dw, db = fox.fox_gate_logf_bwd(dev(x, "bf16"), dev(w, "f32"), dev(b, "f32"), dev(g, "f32"))
+    torch.cuda.synchronize()
+    rdx, rdw, rdb = oracle.gate_logf_bwd(x, w, b, g)
+    _check_tight("dx", host(dx), rdx)
+    _check_tight("dw_f", host(dw), rdw)
+    _check_tight("db_f", host(db), rdb)
+
+
+@pytest.mark.parametrize("rows,D,dt,weighted", [(1, 64, "bf16", False), (37, 128, "f32", True),
+                                                (1000, 64, "bf16", True),
+                                                (12 * 16384, 128, "bf16", False),
+                                                (12 * 16384, 128, "bf16", True)])
+def test_qk_rmsnorm_backward(fox, rows, D, dt, weighted):
+    rng = np.random.default_rng(rows + D)
+    x = (rng.standard_normal((rows, D)) * rng.uniform(0.2, 3.0, size=(rows, 1))).astype(np.float32)
+    if dt == "bf16":
+        x = fi.bf16_round(x)
+    dy = rng.standard_normal((rows, D)).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, size=D).astype(np.float32) if weighted else None
+    say(f"qk-norm backward rows={rows} D={D} {dt} weighted={weighted}")
+    dx, dwt = fox.fox_qk_rmsnorm_bwd(dev(x, dt), dev(dy, "f32"), eps=1e-6,
+                                     weight=None if w is None else dev(w, "f32"),
+                                     want_dweight=weighted)
+    torch.cuda.synchronize()
+    rdx, rdw = oracle.rms_norm_bwd(x, dy, 1e-6, w)
+    _check_tight("dx", host(dx), rdx)
+    if weighted:
+        _check_tight("dweight", host(dwt), rdw)
+
+
 # ------------------------------------------------------------------------------------- backward
 def _run_bwd(fox, case):
     q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
