@@ -122,10 +122,91 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   }
 }
 
+// bf16 x on the matrix cores: z[16 tokens][16 heads] = x[16 tokens][:] . w_f[16 heads][:]^T with
+// v_mfma_f32_16x16x32_bf16, one workgroup per tile of 16 tokens of one batch row (blockIdx.y picks
+// the group of 16 heads); its 4 waves take every 4th 32-column step and their partial sums meet
+// in LDS. Lane l supplies A = x[token l % 16][8 (l / 16) .. +7] of each 32-column step
+// straight from HBM and B = w_f[head l % 16][same columns]; w_f is split into bf16 hi and lo
+// parts (hi = bf16(w), lo = bf16(w - hi)) and both are multiplied, so z keeps about 16
+// significant bits of w on top of exact products and fp32 accumulation. Lane l receives z for
+// head l % 16 and tokens 4 (l / 16) .. +3. Needs d_model % 32 == 0.
+template <bool kBwd>
+__global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict__ x,
+                                                        const float* __restrict__ w_f,
+                                                        const float* __restrict__ b_f,
+                                                        const float* __restrict__ dlog_f,
+                                                        float* __restrict__ out, int L, int dm,
+                                                        int H, int tiles_per_b, int n_tiles) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  __shared__ f32x4v part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x;
+  const int b = tile / tiles_per_b, t0 = (tile % tiles_per_b) * 16;
+  const int r = lane & 15, grp = lane >> 4;
+  const int h0 = blockIdx.y * 16;
+  const int t = t0 + r, hh = h0 + r;
+  const bool tok_ok = t < L, head_ok = hh < H;
+  const bf16_t* xr = x + ((size_t)b * L + (tok_ok ? t : L - 1)) * dm + 8 * grp;
+  const float* wr = w_f + (size_t)(head_ok ? hh : 0) * dm + 8 * grp;
+  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+#pragma unroll 2
+  for (int d0 = 32 * wave; d0 < dm; d0 += 128) {
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(xr + d0);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok ? xa : zero4);
+    const float4 w0 = *reinterpret_cast<const float4*>(wr + d0);
+    const float4 w1 = *reinterpret_cast<const float4*>(wr + d0 + 4);
+    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    bf16x8 bh, bl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float w = head_ok ? wv[e] : 0.f;
+      const __bf16 hi = (__bf16)w;
+      bh[e] = hi;
+      bl[e] = (__bf16)(w - (float)hi);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  acc = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+  const int hc = h0 + r;  // the head of this lane's output column
+  if (hc >= H) return;
+  const float bias = b_f[hc];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tt = t0 + 4 * grp + j;
+    if (tt >= L) break;
+    const float z = acc[j] + bias;
+    if constexpr (kBwd) {
+      out[((size_t)b * L + tt) * H + hc] = dlog_f[((size_t)b * H + hc) * L + tt] / (1.0f + expf(z));
+    } else {
+      out[((size_t)b * H + hc) * L + tt] = log_sigmoid(z);
+    }
+  }
+}
+
+template <bool kBwd>
+void go_gate_mfma(const void* x, const float* w_f, const float* b_f, const float* dlog_f,
+                  float* out, int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
+  const int tiles_per_b = (int)((L + 15) / 16);
+  const int64_t n_tiles = B * tiles_per_b;
+  const dim3 grid((unsigned)n_tiles, (unsigned)((H + 15) / 16));
+  hipLaunchKernelGGL((gate_mfma_kernel<kBwd>), grid, dim3(256), 0, s,
+                     static_cast<const bf16_t*>(x), w_f, b_f, dlog_f, out, (int)L, (int)d_model,
+                     (int)H, tiles_per_b, (int)n_tiles);
+}
+
 }  // namespace
 
 hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* log_f,
                        int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
+  if (x_bf16 && d_model % 32 == 0) {
+    go_gate_mfma<false>(x, w_f, b_f, nullptr, log_f, B, L, d_model, H, s);
+    return hipGetLastError();
+  }
   const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
   const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
   if (x_bf16)
@@ -140,6 +221,10 @@ hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float
 hipError_t launch_gate_dz(const void* x, bool x_bf16, const float* w_f, const float* b_f,
                           const float* dlog_f, float* dz, int64_t B, int64_t L, int64_t d_model,
                           int64_t H, hipStream_t s) {
+  if (x_bf16 && d_model % 32 == 0) {
+    go_gate_mfma<true>(x, w_f, b_f, dlog_f, dz, B, L, d_model, H, s);
+    return hipGetLastError();
+  }
   const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
   const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
   if (x_bf16)

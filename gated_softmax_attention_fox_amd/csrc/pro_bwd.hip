@@ -49,6 +49,46 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(const float* __restrict__ 
   *reinterpret_cast<float4*>(dx + r * dm + d + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
+// dx for up to 16 heads: a workgroup owns 16 tokens and thread c the columns 8c .. 8c + 7 of all
+// of them, so its slice of w_f (16 heads x 8 columns) is read once and stays in registers.
+__global__ __launch_bounds__(256) void gate_dx16_kernel(const float* __restrict__ dz,
+                                                        const float* __restrict__ w_f,
+                                                        float* __restrict__ dx, int64_t rows,
+                                                        int dm, int H) {
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  for (int grp = threadIdx.x; grp < dm / 8; grp += 256) {
+    const int d = grp * 8;
+    float w[16][8];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+      if (h < H) {
+        a = *reinterpret_cast<const float4*>(w_f + (size_t)h * dm + d);
+        c = *reinterpret_cast<const float4*>(w_f + (size_t)h * dm + d + 4);
+      }
+      w[h][0] = a.x; w[h][1] = a.y; w[h][2] = a.z; w[h][3] = a.w;
+      w[h][4] = c.x; w[h][5] = c.y; w[h][6] = c.z; w[h][7] = c.w;
+    }
+    for (int i = 0; i < 16; ++i) {
+      const int64_t r = r0 + i;
+      if (r >= rows) break;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int h = 0; h < 16; ++h) {
+        if (h < H) {
+          const float g = dz[r * H + h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(g, w[h][e], acc[e]);
+        }
+      }
+      *reinterpret_cast<float4*>(dx + r * dm + d) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(dx + r * dm + d + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
 // Partial dw_f and db_f of one 256-token chunk, one 256-column slab and up to 16 heads: thread c
 // owns column slab * 256 + c and walks the chunk's tokens (coalesced rows of x).
 template <bool kBf16>
@@ -219,9 +259,14 @@ hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const f
   float* part_db = part + granule((size_t)((int64_t)n_chunk * H * d_model));
   hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dlog_f, dz, B, L, d_model, H, s);
   if (e != hipSuccess) return e;
-  const int64_t dx_threads = rows * (d_model / 8);
-  hipLaunchKernelGGL(gate_dx_kernel, dim3((unsigned)((dx_threads + 255) / 256)), dim3(256), 0, s,
-                     dz, w_f, dx, rows, (int)d_model, (int)H);
+  if (H <= 16) {
+    hipLaunchKernelGGL(gate_dx16_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, dz,
+                       w_f, dx, rows, (int)d_model, (int)H);
+  } else {
+    const int64_t dx_threads = rows * (d_model / 8);
+    hipLaunchKernelGGL(gate_dx_kernel, dim3((unsigned)((dx_threads + 255) / 256)), dim3(256), 0,
+                       s, dz, w_f, dx, rows, (int)d_model, (int)H);
+  }
   const dim3 pg((unsigned)n_chunk, (unsigned)((d_model + 255) / 256),
                 (unsigned)((H + kHGroup - 1) / kHGroup));
   if (x_bf16)

@@ -195,7 +195,8 @@ def test_gate_matches_oracle(fox):
     check("log f", lf, ref, maxabs=F32_MAXABS, rel_l2=None)
 
 
-@pytest.mark.parametrize("B,L,dm,H", [(2, 100, 96, 3), (1, 65, 264, 17), (1, 1, 8, 1)])
+@pytest.mark.parametrize("B,L,dm,H", [(2, 100, 96, 3), (1, 65, 264, 17), (1, 1, 8, 1), (2, 37, 64, 20),
+                                     (3, 17, 32, 16)])
 def test_gate_ragged(fox, B, L, dm, H):
     rng = np.random.default_rng(B * L + dm)
     x = fi.bf16_round(rng.standard_normal((B, L, dm), dtype=np.float32))
@@ -267,7 +268,8 @@ def test_gate_backward_config4(fox, x_dt):
     _check_tight("db_f", host(db), rdb)
 
 
-@pytest.mark.parametrize("B,L,dm,H", [(2, 1, 8, 1), (1, 77, 40, 3), (3, 300, 264, 17)])
+@pytest.mark.parametrize("B,L,dm,H", [(2, 1, 8, 1), (1, 77, 40, 3), (3, 300, 264, 17), (2, 45, 96, 20),
+                                     (2, 45, 96, 7), (1, 1, 32, 16)])
 def test_gate_backward_ragged(fox, B, L, dm, H):
     rng = np.random.default_rng(B * 1000 + L)
     x = fi.bf16_round(rng.standard_normal((B, L, dm)).astype(np.float32))
