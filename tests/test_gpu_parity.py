@@ -368,6 +368,39 @@ def test_backward_config5_full_length(fox):
     assert np.abs(dlf[..., 0]).max() <= BF16_MAXABS
 
 
+def test_paper_head_shape_full_length(fox):
+    """The FoX paper's head shape, B=1, H=24, L=16384, D=64, as the benchmark's paper-shape run
+    builds it: forward on sampled rows of every head, backward on the shortest- and
+    longest-memory heads whole, plus the column-sum invariants for every head."""
+    case = fi.make_case(1, 24, 16384, 64, "bf16", seed=6, gate="per_head", with_do=True,
+                        name="paper_shape")
+    say("fwd+bwd paper shape (H=24, L=16384, D=64)")
+    s = default_scale(case.D)
+    _, o, lse = _run_fwd(fox, case, torch.bfloat16)
+    cc = oracle.cumsum_logf(case.log_f)
+    got, ref, gl, rl = [], [], [], []
+    for h in range(case.H):
+        rows = sample_rows(case.L, 24, seed=500 + h, tile=128)
+        O, LSE = oracle.attn_fwd_rows(case.q[0, h], case.k[0, h], case.v[0, h], cc[0, h], rows,
+                                      scale=s)
+        got.append(o[0, h, rows]); ref.append(O); gl.append(lse[0, h, rows]); rl.append(LSE)
+    check("O sampled rows", np.concatenate(got), np.concatenate(ref))
+    check("LSE sampled rows", np.concatenate(gl), np.concatenate(rl))
+    grads = _run_bwd(fox, case)
+    mu = case.log_f[0].mean(axis=-1)
+    for h in (int(np.argmin(mu)), int(np.argmax(mu))):
+        sl = (slice(0, 1), slice(h, h + 1))
+        ref = oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl],
+                              scale=s, block=1024)[:4]
+        _check_grads([g[sl] for g in grads], ref, f" (h{h})")
+    _, dk, dv, dlf = grads
+    dk_norm = np.linalg.norm(dk, axis=2)
+    assert np.all(np.abs(dk.sum(axis=2)) <= 6 * BF16_RELL2 * dk_norm)
+    dv_err = np.abs(dv.sum(axis=2) - case.do.astype(np.float64).sum(axis=2))
+    assert np.all(dv_err <= 6 * BF16_RELL2 * np.linalg.norm(dv, axis=2))
+    assert np.abs(dlf[..., 0]).max() <= BF16_MAXABS
+
+
 def test_backward_deterministic(fox):
     case = fi.make_case(1, 3, 700, 128, "bf16", seed=8, with_do=True)
     a = _run_bwd(fox, case)
