@@ -319,3 +319,91 @@ def attn_bwd(q, k, v, log_f=None, do=None, *, c=None, scale, O=None, LSE=None, b
                 dck[b, h, :i1] -= dS.sum(axis=0)
     dlf = reverse_cumsum(dcq + dck)
     return dQ, dK, dV, dlf, dcq, dck
+
+
+# ----------------------------------------------------------------------------------------------
+# Exact tile skipping  ([FoX-pl] section 6 "CONCLUSION", limitations and future work: pruning
+# computation by the forget-gate values; [FoX-pg] "Follow-Up Research": eviction of tokens
+# before sharp forget gates). The pages leave the method open; the reading here skips only work
+# that contributes exact zeros, so the attention output is unchanged.
+# ----------------------------------------------------------------------------------------------
+def _group_max_norms(x, g):
+    """Largest row norm |x_r| of every g-row group, [..., L, D] -> [..., ceil(L / g)]."""
+    x = _f64(x)
+    L = x.shape[-2]
+    n = np.sqrt(np.sum(x * x, axis=-1))
+    pad = (-L) % g
+    n = np.concatenate([n, np.zeros(n.shape[:-1] + (pad,))], axis=-1)
+    return n.reshape(n.shape[:-1] + (-1, g)).max(axis=-1)
+
+
+def skip_bounds(q, k, c, *, scale, g=64):
+    """Upper bounds, in log2 units, on the weight of every key of a key tile for every query of
+    a query tile, relative to the query's diagonal logit scale q_i.k_i.
+
+    For a query i and an earlier key j the logit difference is
+        scale q_i.(k_j - k_i) - (c_j - c_i) <= scale |q_i| (|k_j| + |k_i|) - (c_j - c_i)
+    (Cauchy-Schwarz), and over a query range starting at qa and a key range ending at kb < qa,
+    c_j - c_i >= c_kb - c_qa because c does not increase. With Qmax, Kmax and Kdiag the largest
+    |q_i|, |k_j| and |k_i| of the ranges (taken over g-row groups):
+        bound = log2(e) (scale Qmax (Kmax + Kdiag) - (c_kb - c_qa)).
+
+    Two tilings, both in g-row groups:
+      fwd[b, h, t, T] : query tile t of 4g rows, key tile T of g rows, for the key tiles before
+                        the tile's four diagonal key tiles (T < (last query of t) // g - 3);
+                        +inf elsewhere.
+      kv[b, h, kb, u] : key block kb of 2g rows, query tile u of g rows counted from the block's
+                        first row, for u >= 2 (entirely after the block); +inf elsewhere.
+    """
+    q, k, c = _f64(q), _f64(k), _f64(c)
+    B, H, L, _ = q.shape
+    qn, kn = _group_max_norms(q, g), _group_max_norms(k, g)
+    n_qt, n_g, n_kb = -(-L // (4 * g)), -(-L // g), -(-L // (2 * g))
+    fwd = np.full((B, H, n_qt, n_g), np.inf)
+    kv = np.full((B, H, n_kb, n_g), np.inf)
+    for t in range(n_qt):
+        qa, qb = 4 * g * t, min(4 * g * t + 4 * g - 1, L - 1)
+        groups = slice(qa // g, qb // g + 1)
+        qmax, kdiag = qn[..., groups].max(axis=-1), kn[..., groups].max(axis=-1)
+        for T in range(qb // g - 3):
+            kb = g * T + g - 1
+            fwd[..., t, T] = np.log2(np.e) * (scale * qmax * (kn[..., T] + kdiag)
+                                              - (c[..., kb] - c[..., qa]))
+    for blk in range(n_kb):
+        ka, kb = 2 * g * blk, min(2 * g * blk + 2 * g - 1, L - 1)
+        kmax = kn[..., ka // g:kb // g + 1].max(axis=-1)
+        for u in range(2, -(-(L - ka) // g)):
+            qa = ka + g * u
+            grp = qa // g
+            kv[..., blk, u] = np.log2(np.e) * (scale * qn[..., grp] * (kmax + kn[..., grp])
+                                               - (c[..., kb] - c[..., qa]))
+    return fwd, kv
+
+
+def skip_plan(q, k, c, *, scale, threshold_log2=-160.0, g=64):
+    """The tiles whose bound (skip_bounds) lies below threshold_log2.
+
+    q_skip[b, h, t]    : the number of leading key tiles (from key 0) a query tile skips: the
+                         longest prefix of its candidate tiles that all lie below the threshold.
+    kv_tiles[b, h, kb] : the number of query tiles a key block walks from its first row: one more
+                         than its last tile not below the threshold (at least 2, the diagonal),
+                         capped at the tiles up to the sequence end.
+    """
+    fwd, kv = skip_bounds(q, k, c, scale=scale, g=g)
+    B, H, L, _ = _f64(q).shape
+    n_qt, n_kb = fwd.shape[2], kv.shape[2]
+    q_skip = np.zeros((B, H, n_qt), np.int64)
+    kv_tiles = np.zeros((B, H, n_kb), np.int64)
+    for b in range(B):
+        for h in range(H):
+            for t in range(n_qt):
+                qb = min(4 * g * t + 4 * g - 1, L - 1)
+                n = 0
+                while n < qb // g - 3 and fwd[b, h, t, n] < threshold_log2:
+                    n += 1
+                q_skip[b, h, t] = n
+            for blk in range(n_kb):
+                n_full = -(-(L - 2 * g * blk) // g)
+                keep = [u for u in range(2, n_full) if not kv[b, h, blk, u] < threshold_log2]
+                kv_tiles[b, h, blk] = min(n_full, max(keep, default=1) + 1)
+    return q_skip, kv_tiles

@@ -426,3 +426,122 @@ def test_planted_pro_backward_mistake_is_caught(name):
     mod = types.ModuleType("oracle_pro_mutant_" + name)
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
     assert not (_gate_pins_hold(mod) and _rms_pins_hold(mod))
+
+
+# ------------------------------------------------------------------------- exact tile skipping
+# The skip bound is checked against brute force (it may never lie below the largest logit
+# difference of a tile), against a construction where Cauchy-Schwarz is tight (it must equal
+# it), against hand-derived plans for that construction, and against the real attention weights
+# (every weight in a skipped tile is below the threshold).
+def _skip_case(seed, L=150, D=8, lam=(5.0, 20.0)):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(1, 2, L, D)) * rng.uniform(0.5, 3.0, size=(1, 2, L, 1))
+    k = rng.normal(size=(1, 2, L, D)) * rng.uniform(0.5, 3.0, size=(1, 2, L, 1))
+    log_f = -rng.uniform(*lam, size=(1, 2, L)) * np.array([1.0, 0.05])[None, :, None]
+    return q, k, log_f
+
+
+def _exact_tile_max(q, k, c, scale, g):
+    """max over each candidate tile of log2(e) (logit_ij - logit_ii), by brute force."""
+    B, H, L, _ = q.shape
+    diag = scale * np.einsum("bhld,bhld->bhl", q, k)
+    lg = scale * np.einsum("bhid,bhjd->bhij", q, k) + c[..., :, None] - c[..., None, :]
+    diff = (lg - diag[..., :, None]) * math.log2(math.e)
+    n_qt, n_g, n_kb = -(-L // (4 * g)), -(-L // g), -(-L // (2 * g))
+    fwd = np.full((B, H, n_qt, n_g), -np.inf)
+    kv = np.full((B, H, n_kb, n_g), -np.inf)
+    for t in range(n_qt):
+        qa, qb = 4 * g * t, min(4 * g * t + 4 * g - 1, L - 1)
+        for T in range(qb // g - 3):
+            fwd[..., t, T] = diff[..., qa:qb + 1, g * T:g * T + g].max(axis=(-1, -2))
+    for blk in range(n_kb):
+        ka, kb = 2 * g * blk, min(2 * g * blk + 2 * g - 1, L - 1)
+        for u in range(2, -(-(L - ka) // g)):
+            qa = ka + g * u
+            kv[..., blk, u] = diff[..., qa:min(qa + g, L), ka:kb + 1].max(axis=(-1, -2))
+    return fwd, kv
+
+
+def _tight_case(g=4, D=8, lam=20.0):
+    """All queries a u, keys a u before row 4g and -a u from it on (u a unit vector), constant
+    gate log f = -lam: for query rows >= 4g and keys < 4g, q_i.(k_j - k_i) = |q_i| (|k_j| + |k_i|)
+    and the bound is attained at the tile's first query and last key."""
+    L = 8 * g
+    scale = 1.0 / math.sqrt(D)
+    a = math.sqrt(10.0 / scale)  # scale a^2 = 10
+    u = np.zeros(D)
+    u[0] = 1.0
+    q = np.broadcast_to(a * u, (1, 1, L, D)).copy()
+    k = q.copy()
+    k[..., 4 * g:, :] *= -1.0
+    c = np.cumsum(np.full((1, 1, L), -lam), axis=-1)
+    return q, k, c, scale
+
+
+def _skip_pins_hold(mod):
+    ok = True
+    g = 4
+    for seed in (1, 2, 3):
+        q, k, log_f = _skip_case(seed)
+        c = np.cumsum(log_f, axis=-1)
+        s = 1.0 / math.sqrt(q.shape[-1])
+        fb, kb = mod.skip_bounds(q, k, c, scale=s, g=g)
+        fe, ke = _exact_tile_max(q, k, c, s, g)
+        ok &= bool(np.all(np.isfinite(fb) == np.isfinite(fe)))
+        ok &= bool(np.all(np.isfinite(kb) == np.isfinite(ke)))
+        ok &= bool(np.all(fb[np.isfinite(fb)] >= fe[np.isfinite(fe)] - 1e-9))
+        ok &= bool(np.all(kb[np.isfinite(kb)] >= ke[np.isfinite(ke)] - 1e-9))
+        # every weight of a skipped tile lies below the threshold
+        q_skip, kv_tiles = mod.skip_plan(q, k, c, scale=s, threshold_log2=-60.0, g=g)
+        n_full = -(-(150 - 8 * np.arange(kv_tiles.shape[-1])) // 4)  # tiles up to the end
+        ok &= bool(q_skip.sum() > 0 and np.any(kv_tiles < n_full))  # the case does skip
+        for h in range(2):
+            P = fox_oracle.attn_probs_bruteforce(q[0, h], k[0, h], log_f[0, h], s)
+            lp = np.log2(np.maximum(P, 1e-300))
+            for t, n in enumerate(q_skip[0, h]):
+                rows = slice(16 * t, min(16 * t + 16, 150))
+                if n:
+                    ok &= bool(lp[rows, :4 * n].max() < -60.0)
+            for blk, n in enumerate(kv_tiles[0, h]):
+                if 8 * blk + 4 * n < 150:
+                    ok &= bool(lp[8 * blk + 4 * n:, 8 * blk:8 * blk + 8].max() < -60.0)
+    # tight construction: equality, and the plans derived by hand. Bounds (log2 e times
+    # 20 - lam (qa - kb)) put qa - kb >= 9 below -160 and qa - kb <= 5 above it.
+    q, k, c, s = _tight_case(g=g)
+    fb, kb = mod.skip_bounds(q, k, c, scale=s, g=g)
+    fe, ke = _exact_tile_max(q, k, c, s, g)
+    ok &= bool(np.allclose(fb[0, 0, 1, :4], fe[0, 0, 1, :4], rtol=0, atol=1e-9))
+    ok &= bool(np.allclose(kb[0, 0, 0, 4:8], ke[0, 0, 0, 4:8], rtol=0, atol=1e-9))
+    ok &= bool(np.allclose(kb[0, 0, 1, 2:6], ke[0, 0, 1, 2:6], rtol=0, atol=1e-9))
+    q_skip, kv_tiles = mod.skip_plan(q, k, c, scale=s, g=g)
+    ok &= q_skip[0, 0].tolist() == [0, 2]
+    ok &= kv_tiles[0, 0].tolist() == [4, 4, 4, 2]
+    # no decay: nothing is skipped
+    q_skip, kv_tiles = mod.skip_plan(q, k, np.zeros_like(c), scale=s, g=g)
+    ok &= q_skip[0, 0].tolist() == [0, 0] and kv_tiles[0, 0].tolist() == [8, 6, 4, 2]
+    return ok
+
+
+def test_skip_bound_pins():
+    assert _skip_pins_hold(fox_oracle)
+
+
+SKIP_MUTATIONS = {
+    "skip_drop_diag_norm": ("(kn[..., T] + kdiag)", "(kn[..., T])"),
+    "skip_first_key_of_tile": ("kb = g * T + g - 1", "kb = g * T"),
+    "skip_last_query_of_tile": ("- (c[..., kb] - c[..., qa]))\n    for blk",
+                                "- (c[..., kb] - c[..., qb]))\n    for blk"),
+    "skip_kv_walk_short": ("max(keep, default=1) + 1", "max(keep, default=1)"),
+    "skip_prefix_too_long": ("while n < qb // g - 3 and fwd[b, h, t, n] < threshold_log2:",
+                             "while n < qb // g - 3 and fwd[b, h, t, n] < threshold_log2 + 100:"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SKIP_MUTATIONS))
+def test_planted_skip_mistake_is_caught(name):
+    src = open(fox_oracle.__file__).read()
+    old, new = SKIP_MUTATIONS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle_skip_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    assert not _skip_pins_hold(mod)
