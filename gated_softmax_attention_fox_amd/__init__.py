@@ -9,8 +9,9 @@ C entry points (include/fox.h) and their wrappers:
     fox_logf_cumsum(log_f)                         -> c
     fox_gate_logf(x, w_f, b_f)                     -> log_f
     fox_qk_rmsnorm(x, eps, weight)                 -> y
-    fox_attn_fwd(q, k, v, c, o_dtype, scale)       -> (o, lse)
-    fox_attn_bwd(q, k, v, c, o, lse, dO, scale)    -> (dq, dk, dv, dlog_f)
+    fox_attn_skip_plan(q, k, c, scale)             -> plan (uint8 device tensor)
+    fox_attn_fwd(q, k, v, c, o_dtype, scale, skip_plan=None)        -> (o, lse)
+    fox_attn_bwd(q, k, v, c, o, lse, dO, scale, skip_plan=None)     -> (dq, dk, dv, dlog_f)
     fox_attn_bwd_delta(dO, o)                      -> delta
     fox_attn_bwd_dq(q, k, v, c, lse, dO, delta)    -> (dq, dc_q, delta_refined)
     fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta_refined) -> (dk, dv, dc_k)
@@ -28,6 +29,7 @@ import torch
 __all__ = [
     "FoxError", "LIB_PATH", "HEADER_PATH", "load_library", "header_functions",
     "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_bwd",
+    "fox_attn_skip_plan_bytes", "fox_attn_skip_plan", "skip_plan_arrays",
     "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
     "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID",
     "FOX_E_UNSUPPORTED", "FOX_E_LAUNCH", "FOX_F32", "FOX_BF16", "FOX_CAUSAL",
@@ -56,19 +58,23 @@ _SIGS = {
     "fox_qk_rmsnorm_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "fox_qk_rmsnorm_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                           _c_sz, _c_i64, _c_i64, _c_f32, _c_vp]),
+    "fox_attn_skip_plan_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "fox_attn_skip_plan": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_sz, _c_i64,
+                                          _c_i64, _c_i64, _c_i64, _c_f32, _c_vp]),
     "fox_attn_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int,
-                                    _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, _c_u32, _c_vp]),
+                                    _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, _c_u32, _c_vp,
+                                    _c_vp]),
     "fox_attn_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "fox_attn_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64,
-                                    _c_i64, _c_i64, _c_f32, _c_u32, _c_vp]),
+                                    _c_i64, _c_i64, _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_attn_bwd_delta": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_attn_bwd_dkv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
-                                        _c_f32, _c_u32, _c_vp]),
+                                        _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_attn_bwd_dq": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
-                                       _c_f32, _c_u32, _c_vp]),
+                                       _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_dlogf_from_dc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "fox_last_error": (ctypes.c_char_p, []),
@@ -245,9 +251,55 @@ def _bhld(q, k, v):
     return q.shape
 
 
+def fox_attn_skip_plan_bytes(B: int, H: int, L: int, D: int) -> int:
+    return int(load_library().fox_attn_skip_plan_bytes(B, H, L, D))
+
+
+def fox_attn_skip_plan(q, k, c, scale: float | None = None) -> torch.Tensor:
+    """The exact tile-skipping plan of (q, k, c, scale), as a uint8 device tensor to pass as
+    skip_plan to fox_attn_fwd and the backward calls made with the same inputs."""
+    lib = load_library()
+    B, H, L, D = _bhld(q, k, k)
+    pq, pk = _dev(q, "q", (torch.bfloat16,)), _dev(k, "k", (torch.bfloat16,))
+    pc = _dev(c, "c", (torch.float32,), 3)
+    if tuple(c.shape) != (B, H, L):
+        raise ValueError("c must be [B, H, L]")
+    need = fox_attn_skip_plan_bytes(B, H, L, D)
+    plan = torch.empty(need, dtype=torch.uint8, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_skip_plan(pq, pk, FOX_BF16, pc, ctypes.c_void_p(plan.data_ptr()), need,
+                                  B, H, L, D, scale, _stream(q)), "fox_attn_skip_plan")
+    return plan
+
+
+def skip_plan_arrays(plan: torch.Tensor, B: int, H: int, L: int):
+    """Views (q_skip, kv_tiles, qn, kn, q_order, kv_order) of a plan, in the layout
+    include/fox.h documents."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    BH, n_qt, n_kb, n64 = B * H, -(-L // 256), -(-L // 128), -(-L // 64)
+    o_kv = a256(4 * BH * n_qt)
+    o_qn = a256(o_kv + 4 * BH * n_kb)
+    o_kn = a256(o_qn + 4 * BH * n64)
+    o_qo = a256(o_kn + 4 * BH * n64)
+    o_ko = a256(o_qo + 4 * BH * n_qt)
+    view = lambda off, n, dt, cols: plan[off:off + 4 * n].view(dt).view(-1, cols)
+    return (view(0, BH * n_qt, torch.int32, n_qt), view(o_kv, BH * n_kb, torch.int32, n_kb),
+            view(o_qn, BH * n64, torch.float32, n64), view(o_kn, BH * n64, torch.float32, n64),
+            view(o_qo, BH * n_qt, torch.int32, BH * n_qt)[0],
+            view(o_ko, BH * n_kb, torch.int32, BH * n_kb)[0])
+
+
+def _plan_ptr(skip_plan) -> ctypes.c_void_p:
+    if skip_plan is None:
+        return ctypes.c_void_p(0)
+    return _dev(skip_plan, "skip_plan", (torch.uint8,))
+
+
 def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | None = None,
-                 want_lse: bool = True):
-    """(O, LSE) of causal Forgetting Attention with bias c_i - c_j (c: [B, H, L] fp32)."""
+                 want_lse: bool = True, skip_plan: torch.Tensor | None = None):
+    """(O, LSE) of causal Forgetting Attention with bias c_i - c_j (c: [B, H, L] fp32).
+
+    skip_plan: fox_attn_skip_plan(q, k, c, scale), or None to visit every tile."""
     lib = load_library()
     B, H, L, D = _bhld(q, k, v)
     dts = (torch.bfloat16, torch.float32)
@@ -261,7 +313,8 @@ def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | 
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.fox_attn_fwd(pq, pk, pv, _code(q.dtype), pc, ctypes.c_void_p(o.data_ptr()),
                             _code(o_dtype), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
-                            B, H, L, D, scale, FOX_CAUSAL, _stream(q)), "fox_attn_fwd")
+                            B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan), _stream(q)),
+           "fox_attn_fwd")
     return o, lse
 
 
@@ -269,7 +322,8 @@ def fox_attn_bwd_workspace_bytes(B: int, H: int, L: int, D: int) -> int:
     return int(load_library().fox_attn_bwd_workspace_bytes(B, H, L, D))
 
 
-def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=None):
+def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=None,
+                 skip_plan: torch.Tensor | None = None):
     """(dQ, dK, dV, d log f) for the loss sum(dO * O); o must be the fp32 forward output."""
     lib = load_library()
     B, H, L, D = _bhld(q, k, v)
@@ -291,7 +345,8 @@ def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=N
     _check(lib.fox_attn_bwd(pq, pk, pv, _code(q.dtype), pc, po, pl, pdo,
                             ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()),
                             ctypes.c_void_p(dv.data_ptr()), ctypes.c_void_p(dlf.data_ptr()), pw,
-                            workspace.numel(), B, H, L, D, scale, FOX_CAUSAL, _stream(q)),
+                            workspace.numel(), B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan),
+                            _stream(q)),
            "fox_attn_bwd")
     return dq, dk, dv, dlf
 
@@ -319,7 +374,8 @@ def _bwd_inputs(q, k, v, c, lse, dO, delta):
     return (B, H, L, D), ptrs
 
 
-def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None):
+def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None,
+                     skip_plan: torch.Tensor | None = None):
     """(dK, dV, dc_k) of the key-stationary backward step; delta = fox_attn_bwd_dq's refined one."""
     lib = load_library()
     (B, H, L, D), (pq, pk, pv, pc, pl, pdo, pdl) = _bwd_inputs(q, k, v, c, lse, dO, delta)
@@ -330,12 +386,12 @@ def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None):
     _check(lib.fox_attn_bwd_dkv(pq, pk, pv, FOX_BF16, pc, pl, pdo, pdl,
                                 ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
                                 ctypes.c_void_p(dck.data_ptr()), B, H, L, D, scale, FOX_CAUSAL,
-                                _stream(q)), "fox_attn_bwd_dkv")
+                                _plan_ptr(skip_plan), _stream(q)), "fox_attn_bwd_dkv")
     return dk, dv, dck
 
 
 def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
-                    delta_out: torch.Tensor | None = None):
+                    delta_out: torch.Tensor | None = None, skip_plan: torch.Tensor | None = None):
     """(dQ, dc_q, refined delta) of the query-stationary backward step (run before dkv).
 
     delta_out may be `delta` itself to refine it in place."""
@@ -349,7 +405,8 @@ def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.fox_attn_bwd_dq(pq, pk, pv, FOX_BF16, pc, pl, pdo, pdl,
                                ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dcq.data_ptr()), pdn,
-                               B, H, L, D, scale, FOX_CAUSAL, _stream(q)), "fox_attn_bwd_dq")
+                               B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan), _stream(q)),
+           "fox_attn_bwd_dq")
     return dq, dcq, delta_out
 
 

@@ -190,9 +190,36 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
                   "fox_qk_rmsnorm_bwd");
 }
 
+size_t fox_attn_skip_plan_bytes(int64_t B, int64_t H, int64_t L, int64_t D) {
+  (void)D;
+  if (B < 1 || H < 1 || L < 1) return 0;
+  return fox::skip_plan_layout(B * H, L).bytes;
+}
+
+fox_status fox_attn_skip_plan(const void* q, const void* k, fox_dtype in_dt, const float* c,
+                              void* plan, size_t plan_bytes, int64_t B, int64_t H, int64_t L,
+                              int64_t D, float scale, void* stream) {
+  FOX_REQUIRE_PTR(q);
+  FOX_REQUIRE_PTR(k);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE(plan != nullptr, "plan must not be NULL");
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(plan) & 255u) == 0, "plan must be 256-byte aligned");
+  fox_status st = check_bhld(B, H, L, D);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+  if (in_dt != FOX_BF16)
+    return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
+                "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+  const size_t need = fox::skip_plan_layout(B * H, L).bytes;
+  FOX_REQUIRE(plan_bytes >= need, "plan too small: %zu bytes given, %zu needed", plan_bytes, need);
+  return launched(fox::launch_skip_plan(q, k, c, plan, B * H, L, D, scale, (hipStream_t)stream),
+                  "fox_attn_skip_plan");
+}
+
 fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
                         const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B, int64_t H,
-                        int64_t L, int64_t D, float scale, uint32_t flags, void* stream) {
+                        int64_t L, int64_t D, float scale, uint32_t flags, const void* skip_plan,
+                        void* stream) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k);
   FOX_REQUIRE_PTR(v);
@@ -208,12 +235,17 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
   if (!(flags & FOX_CAUSAL))
     return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
   if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
+              "skip_plan must be 256-byte aligned");
+  if (skip_plan && in_dt != FOX_BF16)
+    return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
   const hipStream_t s = (hipStream_t)stream;
   if (in_dt == FOX_F32)
     return launched(fox::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, c,
                                         (float*)o, lse, B * H, L, D, scale, s),
                     "fox_attn_fwd");
-  return launched(fox::launch_fwd_bf16(q, k, v, c, o, o_dt == FOX_F32, lse, B * H, L, D, scale, s),
+  return launched(fox::launch_fwd_bf16(q, k, v, c, o, o_dt == FOX_F32, lse, B * H, L, D, scale,
+                                       fox::skip_args(skip_plan, B * H, L), s),
                   "fox_attn_fwd");
 }
 
@@ -227,7 +259,7 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
                         const float* c, const float* o, const float* lse, const void* dO,
                         float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
                         size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
-                        float scale, uint32_t flags, void* stream) {
+                        float scale, uint32_t flags, const void* skip_plan, void* stream) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k);
   FOX_REQUIRE_PTR(v);
@@ -254,8 +286,10 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
   const size_t need = fox::bwd_workspace_bytes(B * H, L);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
+              "skip_plan must be 256-byte aligned");
   return launched(fox::launch_bwd_bf16(q, k, v, c, o, lse, dO, dq, dk, dv, dlog_f, workspace,
-                                       B * H, L, D, scale, (hipStream_t)stream),
+                                       B * H, L, D, scale, skip_plan, (hipStream_t)stream),
                   "fox_attn_bwd");
 }
 
@@ -299,28 +333,34 @@ fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, f
 fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dtype in_dt,
                             const float* c, const float* lse, const void* dO, const float* delta,
                             float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
-                            int64_t D, float scale, uint32_t flags, void* stream) {
+                            int64_t D, float scale, uint32_t flags, const void* skip_plan,
+                            void* stream) {
   fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, delta, B, H, L, D, scale, flags);
   if (st != FOX_OK) return st;
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
+              "skip_plan must be 256-byte aligned");
   FOX_REQUIRE_PTR(dk);
   FOX_REQUIRE_PTR(dv);
   FOX_REQUIRE_PTR(dc_k);
   return launched(fox::launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dc_k, B * H, L, D, scale,
-                                      (hipStream_t)stream),
+                                      fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dkv");
 }
 
 fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
                            const float* c, const float* lse, const void* dO, const float* delta,
                            float* dq, float* dc_q, float* delta_out, int64_t B, int64_t H,
-                           int64_t L, int64_t D, float scale, uint32_t flags, void* stream) {
+                           int64_t L, int64_t D, float scale, uint32_t flags,
+                           const void* skip_plan, void* stream) {
   fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, delta, B, H, L, D, scale, flags);
   if (st != FOX_OK) return st;
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
+              "skip_plan must be 256-byte aligned");
   FOX_REQUIRE_PTR(dq);
   FOX_REQUIRE_PTR(dc_q);
   FOX_REQUIRE_PTR(delta_out);
   return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dc_q, delta_out, B * H, L, D,
-                                     scale, (hipStream_t)stream),
+                                     scale, fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dq");
 }
 

@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV,
-    float* __restrict__ dck_out, int L, int BH, float sl2e, float scale) {
+    float* __restrict__ dck_out, const int32_t* __restrict__ kv_tiles,
+    const int32_t* __restrict__ kv_order, int L, int BH, float sl2e, float scale) {
   constexpr int NW = 4, BK = NW * 32, BQ = 64;
   constexpr int TILE = BQ * D;
   constexpr int CPR = D / 8;
@@ -133,9 +134,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
+  // Key tile 0 sees every query tile and is issued first, or a skip plan's order of decreasing
+  // work.
   const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int kt = bid / BH;  // key tile 0 sees every query tile: issued first
+  const int n_kb = (L + BK - 1) / BK;
+  const int item = kv_order ? kv_order[bid] : 0;
+  const int bh = kv_order ? item / n_kb : bid % BH;
+  const int kt = kv_order ? item % n_kb : bid / BH;
   const int k0 = kt * BK;
   const size_t base = (size_t)bh * L * D;
   Q += base;
@@ -150,7 +155,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int kj = kw + l32;
   const bool kok = kj < L;
   const bool active = kw < L;
-  const int n_t = (L - k0 + BQ - 1) / BQ;  // query tiles from the diagonal to the end
+  // Query tiles walked from the diagonal: to the sequence end, or to the last tile whose weights
+  // a skip plan could not rule out (the later ones would add exact zeros).
+  const int n_t = kv_tiles ? kv_tiles[(size_t)bh * n_kb + kt] : (L - k0 + BQ - 1) / BQ;
   const int j0 = wave;                     // the wave's diagonal sub-tile (queries kw .. kw + 31)
   const i32x4 q_rs = buffer_words(Q, (uint32_t)(L * D * 2));
   const i32x4 o_rs = buffer_words(dO, (uint32_t)(L * D * 2));
@@ -431,7 +438,8 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
     const float* Delta, float* __restrict__ dQ, float* __restrict__ dcq_out, float* delta_out,
-    int L, int BH, int n_qt, float sl2e, float scale) {
+    const int32_t* __restrict__ q_skip, const int32_t* __restrict__ q_order, int L, int BH,
+    int n_qt, float sl2e, float scale) {
   constexpr int NW = 8 / NB, BM = 256, NT = NW * 64, BN = 64;
   constexpr int TILE = BN * D;
   constexpr int CPR = D / 8;
@@ -447,9 +455,11 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, l32 = lane & 31;
+  // Longest-first: by query tile, or in a skip plan's order of decreasing work.
   const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = n_qt - 1 - bid / BH;  // longest-first
+  const int item = q_order ? q_order[bid] : 0;
+  const int bh = q_order ? item / n_qt : bid % BH;
+  const int qt = q_order ? item % n_qt : n_qt - 1 - bid / BH;
   const int q0 = qt * BM;
   const size_t base = (size_t)bh * L * D;
   Q += base;
@@ -461,7 +471,8 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   const int qw = q0 + wave * 32 * NB;
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
   const int kt_last = q_last / BN;
-  const int n_t = kt_last + 1;
+  // Key tiles kt_last down to the oldest one a skip plan could not rule out.
+  const int n_t = kt_last + 1 - (q_skip ? q_skip[(size_t)bh * n_qt + qt] : 0);
   const bool active = qw <= q_last;
   const int j0 = max(2 * kt_last + 2 - NB - qw / 32, 0);  // first sub-tile with a key <= a query of the wave
   const i32x4 k_rs = buffer_words(K, (uint32_t)(L * D * 2));
@@ -716,22 +727,23 @@ void go_delta(const bf16_t* dO, const float* o, float* delta, int64_t rows, hipS
 template <int D>
 void go_dkv(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
             const bf16_t* dO, const float* delta, float* dk, float* dv, float* dck, int64_t BH,
-            int64_t L, float scale, hipStream_t s) {
+            int64_t L, float scale, const SkipArgs& skip, hipStream_t s) {
   const int n_kt = (int)((L + 127) / 128);
   hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v, dO,
-                     c, lse, delta, dk, dv, dck, (int)L, (int)BH, scale * kLog2e, scale);
+                     c, lse, delta, dk, dv, dck, skip.kv_tiles, skip.kv_order, (int)L, (int)BH,
+                     scale * kLog2e, scale);
 }
 
 template <int D>
 void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
            const bf16_t* dO, const float* delta, float* dq, float* dcq, float* delta_out,
-           int64_t BH, int64_t L, float scale, hipStream_t s) {
+           int64_t BH, int64_t L, float scale, const SkipArgs& skip, hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
   // one 32-query block per wave, 8 waves (two per SIMD): measured 18% faster than 4 waves with
   // two blocks each, whose halved LDS traffic does not make up for the lost latency hiding
   hipLaunchKernelGGL((dq_pipe_kernel<D, 1>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s, q, k, v,
-                     dO, c, lse, delta, dq, dcq, delta_out, (int)L, (int)BH, n_qt, scale * kLog2e,
-                     scale);
+                     dO, c, lse, delta, dq, dcq, delta_out, skip.q_skip, skip.q_order, (int)L,
+                     (int)BH, n_qt, scale * kLog2e, scale);
 }
 
 }  // namespace
@@ -748,43 +760,44 @@ hipError_t launch_bwd_delta(const void* dO, const float* o, float* delta, int64_
 hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const float* c,
                           const float* lse, const void* dO, const float* delta, float* dk,
                           float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
-                          hipStream_t s) {
+                          const SkipArgs& skip, hipStream_t s) {
   if (D == 64)
     go_dkv<64>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-               delta, dk, dv, dck, BH, L, scale, s);
+               delta, dk, dv, dck, BH, L, scale, skip, s);
   else
     go_dkv<128>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-                delta, dk, dv, dck, BH, L, scale, s);
+                delta, dk, dv, dck, BH, L, scale, skip, s);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* c,
                          const float* lse, const void* dO, const float* delta, float* dq,
                          float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
-                         float scale, hipStream_t s) {
+                         float scale, const SkipArgs& skip, hipStream_t s) {
   if (D == 64)
     go_dq<64>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-              delta, dq, dcq, delta_out, BH, L, scale, s);
+              delta, dq, dcq, delta_out, BH, L, scale, skip, s);
   else
     go_dq<128>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-               delta, dq, dcq, delta_out, BH, L, scale, s);
+               delta, dq, dcq, delta_out, BH, L, scale, skip, s);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,
                            const float* o, const float* lse, const void* dO, float* dq, float* dk,
                            float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
-                           float scale, hipStream_t s) {
+                           float scale, const void* plan, hipStream_t s) {
   const size_t R = region_floats(BH, L);
+  const SkipArgs skip = skip_args(plan, BH, L);
   float* delta = (float*)ws;
   float* dcq = delta + R;
   float* dck = delta + 2 * R;
   hipError_t e = launch_bwd_delta(dO, o, delta, BH * L, D, s);
   if (e != hipSuccess) return e;
   // the query-stationary step refines delta in place; the key-stationary step reads the result
-  e = launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dcq, delta, BH, L, D, scale, s);
+  e = launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dcq, delta, BH, L, D, scale, skip, s);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dck, BH, L, D, scale, s);
+  e = launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dck, BH, L, D, scale, skip, s);
   if (e != hipSuccess) return e;
   return launch_rev_cumsum2(dcq, dck, dlog_f, BH, L, s);
 }

@@ -89,7 +89,8 @@ __device__ __forceinline__ void interleave_step() {
 template <int D>
 __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const float* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE, int L, int BH,
+    const float* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE,
+    const int32_t* __restrict__ q_skip, const int32_t* __restrict__ q_order, int L, int BH,
     int n_qt, float sl2e, int o_f32) {
   constexpr int NW = 8, BM = NW * 32, NT = NW * 64, BN = kFwdBN;
   constexpr int TILE = BN * D;
@@ -105,9 +106,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses need it
   const int h = lane >> 5, l32 = lane & 31;
+  // Longest-first: by query tile, or in a skip plan's order of decreasing work.
   const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int qt = n_qt - 1 - bid / BH;  // longest-first
+  const int item = q_order ? q_order[bid] : 0;
+  const int bh = q_order ? item / n_qt : bid % BH;
+  const int qt = q_order ? item % n_qt : n_qt - 1 - bid / BH;
   const int q0 = qt * BM;
   const size_t base = (size_t)bh * L * D;
   Q += base;
@@ -119,7 +122,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   const int qi = qw + l32;
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
   const int kt_last = q_last / BN;
-  const int n_t = kt_last + 1;               // tiles this workgroup visits
+  // Leading key tiles a skip plan rules out (every weight in them underflows to zero).
+  const int kt_skip = q_skip ? q_skip[(size_t)bh * n_qt + qt] : 0;
+  const int n_t = kt_last + 1 - kt_skip;     // tiles this workgroup visits
   const int n_j = 2 * n_t;                   // sub-tiles
   const bool active = qw <= q_last;          // the wave holds at least one real query
   const int j0 = 2 * kt_last + 1 - qw / 32;  // the wave's diagonal sub-tile
@@ -146,9 +151,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
 
   // ---- copies -------------------------------------------------------------------------------
   // Key tile of visit t: the diagonal band (the last four key tiles) first, from the diagonal
-  // backwards; then every earlier key tile in ascending order, so that the workgroups of one head
-  // that run at the same time stream the same K and V tiles through the cache.
-  auto key_tile = [&](int t) __attribute__((always_inline)) { return t < 4 ? kt_last - t : t - 4; };
+  // backwards; then every earlier key tile not skipped, in ascending order, so that the
+  // workgroups of one head that run at the same time stream the same K and V tiles through the
+  // cache.
+  auto key_tile = [&](int t) __attribute__((always_inline)) {
+    return t < 4 ? kt_last - t : t - 4 + kt_skip;
+  };
   auto copy_kv = [&](const i32x4& rs, uint32_t region, int t, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < BLK; ++b) {
@@ -536,16 +544,18 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const float* c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
-                           hipStream_t s) {
+                           const SkipArgs& skip, hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
   const dim3 grid((unsigned)(n_qt * BH)), block(512);
   if (D == 64)
     hipLaunchKernelGGL(fwd_bf16_pipe_kernel<64>, grid, block, 0, s, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L, (int)BH, n_qt,
+                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, skip.q_skip, skip.q_order, (int)L,
+                       (int)BH, n_qt,
                        scale * kLog2e, (int)o_f32);
   else
     hipLaunchKernelGGL(fwd_bf16_pipe_kernel<128>, grid, block, 0, s, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, (int)L, (int)BH, n_qt,
+                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, skip.q_skip, skip.q_order, (int)L,
+                       (int)BH, n_qt,
                        scale * kLog2e, (int)o_f32);
   return hipGetLastError();
 }

@@ -34,10 +34,31 @@ hipError_t launch_rmsnorm_bwd(const void* x, bool bf16, const float* dy, const f
 // y = x / sqrt(mean(x^2) + eps) * w over rows of length D.
 hipError_t launch_rmsnorm(const void* x, void* y, bool bf16, int64_t rows, int64_t D, float eps,
                           const float* w, hipStream_t s);
+// Skip plan (skip_plan.hip): byte offsets of its four arrays and its size.
+//   q_skip   : int32 [BH, ceil(L / 256)]  leading key tiles a 256-query tile skips
+//   kv_tiles : int32 [BH, ceil(L / 128)]  64-query tiles a 128-key block walks
+//   qn, kn   : fp32  [BH, ceil(L / 64)]   largest row norm of q / k per 64-row group
+//   q_order  : int32 [BH * ceil(L / 256)] launch order of the query tiles (index bh n_qt + qt),
+//                                         most work first
+//   kv_order : int32 [BH * ceil(L / 128)] the same for the key blocks (index bh n_kb + kb)
+struct SkipPlanLayout {
+  size_t q_skip, kv_tiles, qn, kn, q_order, kv_order, bytes;
+};
+SkipPlanLayout skip_plan_layout(int64_t BH, int64_t L);
+hipError_t launch_skip_plan(const void* q, const void* k, const float* c, void* plan, int64_t BH,
+                            int64_t L, int64_t D, float scale, hipStream_t s);
+// The plan's arrays the kernels read (all null without a plan).
+struct SkipArgs {
+  const int32_t* q_skip = nullptr;
+  const int32_t* q_order = nullptr;
+  const int32_t* kv_tiles = nullptr;
+  const int32_t* kv_order = nullptr;
+};
+SkipArgs skip_args(const void* plan, int64_t BH, int64_t L);
 // Forward, bf16 inputs on MFMA; O in bf16 or fp32.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const float* c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
-                           hipStream_t s);
+                           const SkipArgs& skip, hipStream_t s);
 // Forward, fp32 inputs and outputs, fp32 arithmetic throughout.
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, const float* c, float* o,
                           float* lse, int64_t BH, int64_t L, int64_t D, float scale, hipStream_t s);
@@ -50,15 +71,16 @@ hipError_t launch_bwd_delta(const void* dO, const float* o, float* delta, int64_
 hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const float* c,
                           const float* lse, const void* dO, const float* delta, float* dk,
                           float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
-                          hipStream_t s);
+                          const SkipArgs& skip, hipStream_t s);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* c,
                          const float* lse, const void* dO, const float* delta, float* dq,
                          float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
-                         float scale, hipStream_t s);
-// Backward, bf16 inputs, fp32 O / gradients: the four steps in order.
+                         float scale, const SkipArgs& skip, hipStream_t s);
+// Backward, bf16 inputs, fp32 O / gradients: the four steps in order (plan: a skip plan or
+// null).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,
                            const float* o, const float* lse, const void* dO, float* dq, float* dk,
                            float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
-                           float scale, hipStream_t s);
+                           float scale, const void* plan, hipStream_t s);
 
 }  // namespace fox

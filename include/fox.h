@@ -105,6 +105,41 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
                               size_t workspace_bytes, int64_t rows, int64_t D, float eps,
                               void* stream);
 
+/* Exact skipping of fully decayed tiles. The forget gate makes a key's weight decay with its
+ * distance from the query; the pages name pruning of computation by the gate values as future
+ * work (paperlayer.ai summary, section 6 "CONCLUSION", limitations and future work;
+ * paper-graph-ui summary, "Follow-Up Research", KV-cache eviction). A plan records, for the
+ * given q, k, c and scale, the tiles of the bf16 attention kernels in which every weight is
+ * provably below 2^-160 of the row's largest, so that the kernels' exp2 already returns exactly
+ * zero there; with the plan the kernels do not visit those tiles. For finite inputs the
+ * results are bit-identical to those without a plan.
+ * The bound: for a query i and an earlier key j,
+ *   scale q_i.k_j + c_i - c_j - (scale q_i.k_i) <= scale |q_i| (|k_j| + |k_i|) - (c_j - c_i),
+ * evaluated per tile with the largest row norms of q and k in each 64-row group and with c at
+ * the tile ends (c does not increase), plus a slack for the fp32 rounding of c. The forward's
+ * running maximum and the backward's LSE are never below the diagonal logit scale q_i.k_i.
+ *   fox_attn_skip_plan_bytes : bytes of device memory a plan takes for these sizes.
+ *   fox_attn_skip_plan       : fills `plan` (256-byte aligned, at least that many bytes) from
+ *                              q, k (bf16, [B, H, L, D]), c and scale. Reads q and k once.
+ * Plan layout (four arrays, each starting at the next 256-byte boundary, BH = B * H):
+ *   int32 q_skip[BH][ceil(L / 256)]   key tiles of 64 keys, counted from key 0, that the
+ *                                     256-query tile skips (the forward and dq steps);
+ *   int32 kv_tiles[BH][ceil(L / 128)] 64-query tiles, counted from the block's first key, that
+ *                                     the 128-key block walks (the dk/dv step);
+ *   fp32 qn[BH][ceil(L / 64)], kn[...] largest row norm of q and k in each 64-row group;
+ *   int32 q_order[BH * ceil(L / 256)]  launch order of the query tiles (entry bh * ceil(L / 256)
+ *                                     + tile), most work first; entries of equal work may come
+ *                                     in a different order on each call (results do not depend
+ *                                     on it);
+ *   int32 kv_order[BH * ceil(L / 128)] the same for the key blocks.
+ * Pass the plan as skip_plan to fox_attn_fwd and the backward calls made with the same q, k,
+ * c, sizes and scale; a plan for other inputs gives wrong results. skip_plan = NULL visits
+ * every tile. */
+size_t fox_attn_skip_plan_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
+fox_status fox_attn_skip_plan(const void* q, const void* k, fox_dtype in_dt, const float* c,
+                              void* plan, size_t plan_bytes, int64_t B, int64_t H, int64_t L,
+                              int64_t D, float scale, void* stream);
+
 /* Forward (paper-graph-ui summary, "Hardware-Aware Implementation", the forward pass;
  * paperlayer.ai summary, section E):
  *   O[i]   = sum_{j<=i} softmax_j(scale * q_i . k_j + c_i - c_j) v_j
@@ -115,11 +150,12 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
  *   o       : o_dt (FOX_BF16 or FOX_F32; must be FOX_F32 when in_dt is FOX_F32)
  *   lse     : fp32, may be NULL if not wanted.
  * bf16 inputs run on bf16 MFMA with fp32 accumulation and an fp32 online softmax; fp32
- * inputs run fully in fp32. flags must contain FOX_CAUSAL. */
+ * inputs run fully in fp32. flags must contain FOX_CAUSAL. skip_plan: NULL, or a plan from
+ * fox_attn_skip_plan for these q, k, c and scale (bf16 inputs only). */
 fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
                         const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
                         int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
-                        void* stream);
+                        const void* skip_plan, void* stream);
 
 /* Bytes of device workspace fox_attn_bwd needs for these sizes (caller-allocated). */
 size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
@@ -134,12 +170,13 @@ size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
  * fox_attn_fwd; o is the forward output in fp32 (the row term Delta_i = dO_i . O_i is formed
  * from the fp32 output). workspace: device memory of at least
  * fox_attn_bwd_workspace_bytes(B, H, L, D) bytes, 256-byte aligned, contents ignored on
- * entry and clobbered. Deterministic: identical inputs give bit-identical outputs. */
+ * entry and clobbered. Deterministic: identical inputs give bit-identical outputs. skip_plan:
+ * NULL, or the plan of these q, k, c and scale (see fox_attn_skip_plan). */
 fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
                         const float* c, const float* o, const float* lse, const void* dO,
                         float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
                         size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
-                        float scale, uint32_t flags, void* stream);
+                        float scale, uint32_t flags, const void* skip_plan, void* stream);
 
 /* The four steps of fox_attn_bwd as separate calls, for callers that schedule them
  * themselves. Running them in this order with the same arguments gives exactly fox_attn_bwd's
@@ -154,18 +191,21 @@ fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, f
  * delta_out ([B,H,L] fp32, may equal delta): the row term refined so that each row of dS sums to
  * zero under the P and dP this library recomputes. The forward rounds P to bf16 before the PV
  * product, so dO . O matches sum_j P_ij dP_ij only to ~1e-3 relative; d log f sums that
- * residual over every row that attends across a position, hence the refinement. */
+ * residual over every row that attends across a position, hence the refinement. skip_plan as
+ * for fox_attn_bwd. */
 fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
                            const float* c, const float* lse, const void* dO, const float* delta,
                            float* dq, float* dc_q, float* delta_out, int64_t B, int64_t H,
-                           int64_t L, int64_t D, float scale, uint32_t flags, void* stream);
+                           int64_t L, int64_t D, float scale, uint32_t flags,
+                           const void* skip_plan, void* stream);
 
 /* Step 3, key-stationary: dk, dv ([B,H,L,D] fp32) and dc_k[j] = -sum_i dS_ij ([B,H,L] fp32).
- * delta must be step 2's delta_out; the other inputs as for fox_attn_bwd. */
+ * delta must be step 2's delta_out; the other inputs (skip_plan too) as for fox_attn_bwd. */
 fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dtype in_dt,
                             const float* c, const float* lse, const void* dO, const float* delta,
                             float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
-                            int64_t D, float scale, uint32_t flags, void* stream);
+                            int64_t D, float scale, uint32_t flags, const void* skip_plan,
+                            void* stream);
 
 /* Step 4, d log f[r, l] = sum_{t>=l} (dc_q[r, t] + dc_k[r, t]): the gradient of the prefix sum
  * fox_logf_cumsum computes, applied to dc = dc^q + dc^k ([BH, L] fp32 each; fp64 accumulation,

@@ -56,13 +56,13 @@ P = 0x7f0000000000  # fake, 16-byte aligned, never dereferenced
 
 
 def _fwd(lib, q=P, k=P, v=P, in_dt=1, c=P, o=P, o_dt=1, lse=P, B=1, H=2, L=64, D=128, scale=0.1,
-         flags=1):
-    return lib.fox_attn_fwd(q, k, v, in_dt, c, o, o_dt, lse, B, H, L, D, scale, flags, None)
+         flags=1, plan=None):
+    return lib.fox_attn_fwd(q, k, v, in_dt, c, o, o_dt, lse, B, H, L, D, scale, flags, plan, None)
 
 
-def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o=P):
+def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o=P, plan=None):
     return lib.fox_attn_bwd(P, P, P, in_dt, P, o, P, P, P, P, P, P, ws, ws_bytes, B, H, L, D, 0.1,
-                            flags, None)
+                            flags, plan, None)
 
 
 @host_only
@@ -71,6 +71,7 @@ def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o
     (dict(D=96), 1), (dict(D=256), 1), (dict(L=0), 1), (dict(L=(1 << 23) + 1), 1), (dict(B=0), 1),
     (dict(H=-1), 1), (dict(in_dt=7), 1), (dict(o_dt=3), 1), (dict(in_dt=0, o_dt=1), 1), (dict(scale=0.0), 1),
     (dict(scale=float("nan")), 1), (dict(flags=0), 2), (dict(flags=3), 2),
+    (dict(plan=P + 16), 1), (dict(in_dt=0, o_dt=0, plan=P), 2),
 ])
 def test_forward_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
@@ -81,7 +82,7 @@ def test_forward_rejects(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(ws=0), 1), (dict(ws=P + 16), 1), (dict(ws_bytes=100), 1), (dict(in_dt=0), 2),
     (dict(in_dt=5), 1), (dict(flags=0), 2), (dict(D=32), 1), (dict(o=0), 1),
-    (dict(L=(1 << 23) + 1), 1),
+    (dict(L=(1 << 23) + 1), 1), (dict(plan=P + 64), 1),
 ])
 def test_backward_rejects(lib, kw, status):
     assert _bwd(lib, **kw) == status
@@ -102,6 +103,28 @@ def test_scan_gate_norm_reject(lib):
     assert lib.fox_gate_logf(P, 2, P, P, P, 1, 8, 16, 2, None) == 1   # dtype
     assert lib.fox_qk_rmsnorm(P, P, 1, 10, 96, ctypes.c_float(1e-6), None, None) == 1
     assert lib.fox_qk_rmsnorm(P, P, 1, 10, 128, ctypes.c_float(-1.0), None, None) == 1
+
+
+def test_skip_plan_size(lib):
+    # int32 [12, 64] + int32 [12, 128] + 2 x fp32 [12, 256] + int32 [768] + int32 [1536], each
+    # rounded up to 256 bytes
+    assert lib.fox_attn_skip_plan_bytes(1, 12, 16384, 128) == 4 * 12 * (64 + 128 + 256 + 256 + 64 + 128)
+    assert lib.fox_attn_skip_plan_bytes(1, 1, 1, 64) == 6 * 256
+    assert lib.fox_attn_skip_plan_bytes(1, 0, 1, 64) == 0
+
+
+@host_only
+def test_skip_plan_rejects(lib):
+    def plan(q=P, k=P, in_dt=1, c=P, out=P, nbytes=1 << 20, L=300, scale=0.1):
+        return lib.fox_attn_skip_plan(q, k, in_dt, c, out, nbytes, 1, 2, L, 128, scale, None)
+    assert plan(q=0) == 1
+    assert plan(out=0) == 1
+    assert plan(out=P + 16) == 1
+    assert plan(nbytes=100) == 1
+    assert "plan too small" in lib.fox_last_error().decode()
+    assert plan(in_dt=0) == 2
+    assert plan(scale=-1.0) == 1
+    assert plan(L=0) == 1
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -13,6 +13,7 @@ import torch
 
 import fox_inputs as fi
 import oracle
+from oracle import fox_oracle
 from tests.fox_testlib import (BF16_MAXABS, BF16_RELL2, F32_MAXABS, check, default_scale, dev,
                                host, sample_rows, say)
 
@@ -407,3 +408,111 @@ def test_backward_deterministic(fox):
     b = _run_bwd(fox, case)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+# ------------------------------------------------------------------------------ exact tile skipping
+def _skip_case(L, D, kind, H=4, seed=0):
+    if kind == "strong":  # log f averaging about -0.7 per token: most old tiles carry no weight
+        case = fi.make_case(1, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=0.0,
+                            with_do=True)
+    elif kind == "mixed":  # per-head gates from strongly to barely forgetting
+        case = fi.make_case(1, H, L, D, "bf16", seed=seed, gate="per_head",
+                            head_mean_range=(-2.0, 6.0), with_do=True)
+    else:  # hard resets inside otherwise open gates
+        case = fi.make_case(1, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=6.0,
+                            with_do=True)
+        case.log_f[..., L // 3] = -1e4
+        case.log_f[..., (2 * L) // 3 + 5] = -1e4
+    return case
+
+
+def _plan_and_inputs(fox, case):
+    q, k, v = (dev(getattr(case, n), "bf16") for n in "qkv")
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    plan = fox.fox_attn_skip_plan(q, k, c)
+    return q, k, v, c, plan
+
+
+def _check_plan_against_oracle(fox, case, plan, c):
+    """The plan lies between the oracle's plans at thresholds -175 and -150 (log2): the kernel
+    tests -160 with a slack of about 1.5 for the fp32 rounding of c, so any index or term error
+    moves it outside that band. The group norms match the oracle's, and the launch orders list
+    every item once, most work first."""
+    B, H, L, D = case.B, case.H, case.L, case.D
+    q_skip, kv_tiles, qn, kn, q_order, kv_order = (host(a) for a in
+                                                   fox.skip_plan_arrays(plan, B, H, L))
+    n_qt, n_kb = q_skip.shape[1], kv_tiles.shape[1]
+    q_work = np.minimum(np.arange(n_qt) * 256 + 255, L - 1) // 64 + 1 - q_skip  # [BH, n_qt]
+    for order, work in ((q_order, q_work.reshape(-1)), (kv_order, kv_tiles.reshape(-1))):
+        assert np.array_equal(np.sort(order), np.arange(order.size))
+        assert np.all(np.diff(work[order.astype(np.int64)]) <= 0)
+    s = default_scale(D)
+    cc = host(c).astype(np.float64)
+    lo_q, hi_kv = oracle.skip_plan(case.q, case.k, cc, scale=s, threshold_log2=-175.0)
+    hi_q, lo_kv = oracle.skip_plan(case.q, case.k, cc, scale=s, threshold_log2=-150.0)
+    assert np.all(lo_q.reshape(B * H, -1) <= q_skip) and np.all(q_skip <= hi_q.reshape(B * H, -1))
+    assert np.all(lo_kv.reshape(B * H, -1) <= kv_tiles)
+    assert np.all(kv_tiles <= hi_kv.reshape(B * H, -1))
+    for got, x in ((qn, case.q), (kn, case.k)):
+        ref = fox_oracle._group_max_norms(x, 64).reshape(B * H, -1)
+        assert np.all(got >= ref * (1 - 1e-6)) and np.all(got <= ref * (1 + 1e-4) + 1e-30)
+    return q_skip, kv_tiles
+
+
+@pytest.mark.parametrize("L,D,kind", [(3000, 128, "strong"), (1000, 64, "strong"),
+                                      (2500, 128, "mixed"), (1500, 64, "reset"), (100, 128, "strong"),
+                                      (4097, 128, "reset")])
+def test_skip_plan_matches_oracle(fox, L, D, kind):
+    case = _skip_case(L, D, kind, seed=L)
+    say(f"skip plan L={L} D={D} {kind}")
+    q, k, v, c, plan = _plan_and_inputs(fox, case)
+    torch.cuda.synchronize()
+    q_skip, kv_tiles = _check_plan_against_oracle(fox, case, plan, c)
+    if L >= 1000 and kind != "mixed":
+        assert q_skip.sum() > 0 and kv_tiles.sum() < case.H * sum(
+            -(-(L - 128 * b) // 64) for b in range(-(-L // 128)))
+
+
+@pytest.mark.parametrize("L,D,kind", [(3000, 128, "strong"), (1000, 64, "strong"),
+                                      (2500, 128, "mixed"), (1500, 64, "reset"), (100, 128, "strong"),
+                                      (4097, 128, "reset")])
+def test_skip_is_exact(fox, L, D, kind):
+    """With the plan, the forward (bf16 and fp32 O) and the backward return bit-identical results."""
+    case = _skip_case(L, D, kind, seed=L + 1)
+    say(f"skip exact L={L} D={D} {kind}")
+    q, k, v, c, plan = _plan_and_inputs(fox, case)
+    for o_dt in (torch.bfloat16, torch.float32):
+        o0, l0 = fox.fox_attn_fwd(q, k, v, c, o_dtype=o_dt)
+        o1, l1 = fox.fox_attn_fwd(q, k, v, c, o_dtype=o_dt, skip_plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), o_dt
+    do = dev(case.do, "bf16")
+    o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    g0 = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
+    g1 = fox.fox_attn_bwd(q, k, v, c, o, lse, do, skip_plan=plan)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dlog f"), g0, g1):
+        assert torch.equal(a, b), name
+
+
+def test_skip_config5_full_length(fox):
+    """The benchmark's workload (L = 16384, 12 heads with per-head gates): the plan against the
+    oracle's, and bit-identical forward and backward results with it."""
+    case = fi.config_case(5)
+    say("skip config5 (L=16384)")
+    q, k, v, c, plan = _plan_and_inputs(fox, case)
+    torch.cuda.synchronize()
+    q_skip, kv_tiles = _check_plan_against_oracle(fox, case, plan, c)
+    n_old = np.array([max(min(256 * t + 255, case.L - 1) // 64 - 3, 0) for t in range(64)])
+    say(f"  skipped key tiles: {q_skip.sum()} of {case.H * n_old.sum()} candidates")
+    assert q_skip.sum() > 0
+    do = dev(case.do, "bf16")
+    o0, l0 = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    o1, l1 = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32, skip_plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    g0 = fox.fox_attn_bwd(q, k, v, c, o0, l0, do)
+    g1 = fox.fox_attn_bwd(q, k, v, c, o0, l0, do, skip_plan=plan)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv", "dlog f"), g0, g1):
+        assert torch.equal(a, b), name
