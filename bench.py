@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--pro", action="store_true",
                     help="the Pro block's whole attention step instead (workload 4 plus dO): gate, "
                          "scan, QK-norm, attention forward and backward, QK-norm and gate backward")
+    ap.add_argument("--no-skip", action="store_true",
+                    help="leave out the second measurement with exact tile skipping")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run 3 device copies of this many MiB (a known-size kernel "
                          "that scales HBM byte counters)")
@@ -164,7 +166,7 @@ def main():
     names = ["scan", "fwd", "delta", "dq", "dkv", "dlogf"]
     stream = torch.cuda.current_stream(dev)  # the library launches on this stream
 
-    def step(events):
+    def step(events, skip=False):
         def run(n, fn):
             if events is None:
                 return fn()
@@ -175,13 +177,16 @@ def main():
             events.append((n, e0, e1))
             return r
         c = run("scan", lambda: fox.fox_logf_cumsum(log_f))
-        o, lse = run("fwd", lambda: fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32))
+        plan = run("plan", lambda: fox.fox_attn_skip_plan(q, k, c)) if skip else None
+        o, lse = run("fwd", lambda: fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32,
+                                                     skip_plan=plan))
         delta = run("delta", lambda: fox.fox_attn_bwd_delta(do, o))
         dq, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta,
-                                                                delta_out=delta))
-        dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta))
+                                                                delta_out=delta, skip_plan=plan))
+        dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta,
+                                                              skip_plan=plan))
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
-        return dq, dk, dv, dlf
+        return dq, dk, dv, dlf, plan
 
     for _ in range(args.warmup):
         step(None)
@@ -238,6 +243,9 @@ def main():
         "kernel_ms": {n: round(kern_ms[n], 4) for n in names},
         "host_wall_ms_per_step": round(wall_ms, 4),
     }
+    if not args.no_skip:
+        out["skip_decayed"] = skip_measurement(args, torch, fox, step, names, ms_per_step,
+                                               fwd_flops + bwd_flops, (B, H, L))
     if args.copy_mib > 0:
         n = args.copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -251,6 +259,41 @@ def main():
         log(f"timing the oracle on {args.cpu_heads} heads (CPU) ...")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_heads)
     print(json.dumps(out), flush=True)
+
+
+def skip_measurement(args, torch, fox, step, names, dense_ms, dense_flops, bhl):
+    """The same step with exact tile skipping (a skip plan made inside every step from q, k, c):
+    a separate measurement, credited with the dense FLOPs ("effective"), never the headline."""
+    B, H, L = bhl
+    ref = step(None)
+    got = step(None, skip=True)
+    torch.cuda.synchronize()
+    identical = all(torch.equal(a, b) for a, b in zip(ref[:4], got[:4]))
+    q_skip, kv_tiles = (a.cpu().numpy().astype(np.int64)
+                        for a in fox.skip_plan_arrays(got[4], B, H, L)[:2])
+    n_qt, n_kb = q_skip.shape[1], kv_tiles.shape[1]
+    q_dense = np.minimum(np.arange(n_qt) * 256 + 255, L - 1) // 64 + 1
+    kv_dense = -(-(L - 128 * np.arange(n_kb)) // 64)
+    for _ in range(args.warmup):
+        step(None, skip=True)
+    events = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(events, skip=True)
+    torch.cuda.synchronize()
+    ms = events[0][1].elapsed_time(events[-1][2]) / args.steps
+    kern = {n: float(np.mean([a.elapsed_time(b) for m, a, b in events if m == n]))
+            for n in ["plan"] + names}
+    return {
+        "ms_per_step": round(ms, 4),
+        "effective_tflops": round(dense_flops / (ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(dense_ms / ms, 3),
+        "bit_identical_to_dense": bool(identical),
+        "fwd_dq_key_tiles_walked_frac": round(
+            float((q_dense - q_skip).sum() / (B * H * q_dense.sum())), 4),
+        "dkv_query_tiles_walked_frac": round(float(kv_tiles.sum() / (B * H * kv_dense.sum())), 4),
+        "kernel_ms": {n: round(kern[n], 4) for n in kern},
+    }
 
 
 def pro_step(args, torch, fi, fox, dev):
