@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--pro", action="store_true",
                     help="the Pro block's whole attention step instead (workload 4 plus dO): gate, "
                          "scan, QK-norm, attention forward and backward, QK-norm and gate backward")
+    ap.add_argument("--decode", action="store_true",
+                    help="single-token decode against a full KV cache instead: B=8 sequences of "
+                         "12 heads, 16384 cached positions, D=128 (a separate, HBM-bound line)")
     ap.add_argument("--no-skip", action="store_true",
                     help="leave out the second measurement with exact tile skipping")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -140,6 +143,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.pro:
         return pro_step(args, torch, fi, fox, dev)
+    if args.decode:
+        return decode_step(args, torch, fi, fox, dev)
     if args.paper_shape:
         case = fi.make_case(1, 24, 16384, 64, "bf16", seed=6, gate="per_head", with_do=True,
                             name="paper_shape")
@@ -246,15 +251,7 @@ def main():
     if not args.no_skip:
         out["skip_decayed"] = skip_measurement(args, torch, fox, step, names, ms_per_step,
                                                fwd_flops + bwd_flops, (B, H, L))
-    if args.copy_mib > 0:
-        n = args.copy_mib << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):  # an elementwise kernel that reads n bytes and writes n bytes
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = n
+    copy_calibration(args, torch, dev, out)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_heads} heads (CPU) ...")
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_heads)
@@ -294,6 +291,80 @@ def skip_measurement(args, torch, fox, step, names, dense_ms, dense_flops, bhl):
         "dkv_query_tiles_walked_frac": round(float(kv_tiles.sum() / (B * H * kv_dense.sum())), 4),
         "kernel_ms": {n: round(kern[n], 4) for n in kern},
     }
+
+
+def copy_calibration(args, torch, dev, out):
+    """After timing: 3 elementwise kernels that read and write --copy-mib MiB each (a kernel of
+    known traffic that scales the HBM byte counters)."""
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+
+
+def decode_step(args, torch, fi, fox, dev):
+    """Single-token decode: one new query per sequence against a full cache of the bench's
+    sequence length (every cached K and V row read once; bound by HBM)."""
+    B, H, T, D = 8, 12, 16384, 128
+    case = fi.make_case(B, H, T, D, "bf16", seed=8, gate="per_head", name="decode")
+    rng = np.random.default_rng(88)
+    qn = fi.bf16_round(rng.standard_normal((B, H, D), dtype=np.float32))
+    up = lambda a: torch.from_numpy(fi.bf16_bits(a)).view(torch.bfloat16).to(dev)
+    q, k, v = up(qn), up(case.k), up(case.v)
+    c = fox.fox_logf_cumsum(torch.from_numpy(case.log_f).to(dev))
+    lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+    ws = torch.empty(fox.fox_attn_decode_workspace_bytes(B, H, T, D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(max(args.warmup, 3)):
+        fox.fox_attn_decode(q, k, v, c, lens, workspace=ws)
+    torch.cuda.synchronize()
+    steps = args.steps * 10  # a decode step is about 0.2 ms
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fox.fox_attn_decode(q, k, v, c, lens, workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = B * H * T * (2 * D * 2 + 4)  # K and V rows (bf16) and c (fp32), each read once
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "Forgetting-attn single-token decode, KV-cache read bandwidth",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(args.warmup, 3), "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"fox_attn_decode B={B} H={H} T={T} D={D} (full caches, bf16 "
+                               "K/V, per-head gates mu_h~U[1,6], z~N(mu_h,1))",
+                   "B": B, "H": H, "T": T, "D": D},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        cc = oracle.cumsum_logf(case.log_f[:1])
+        n = 0
+        for h in range(H):
+            qf = np.zeros((T, D), np.float32)
+            qf[T - 1] = qn[0, h]
+            oracle.attn_fwd_rows(qf, case.k[0, h], case.v[0, h], cc[0, h], np.array([T - 1]),
+                                 scale=1.0 / math.sqrt(D))
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n * T * (2 * D * 2 + 4) / dt / 1e9, 3),
+                               "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle",
+                               "sample": f"sequence 0, all {H} heads, one decode row each in fp64 "
+                                         f"NumPy: {dt:.2f} s"}
+    copy_calibration(args, torch, dev, out)
+    print(json.dumps(out), flush=True)
 
 
 def pro_step(args, torch, fi, fox, dev):

@@ -16,6 +16,8 @@ C entry points (include/fox.h) and their wrappers:
     fox_attn_bwd_dq(q, k, v, c, lse, dO, delta)    -> (dq, dc_q, delta_refined)
     fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta_refined) -> (dk, dv, dc_k)
     fox_dlogf_from_dc(dc_q, dc_k)                  -> dlog_f
+    fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype, scale) -> (o, lse)
+    fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, lens) (in place)
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ __all__ = [
     "FoxError", "LIB_PATH", "HEADER_PATH", "load_library", "header_functions",
     "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_bwd",
     "fox_attn_skip_plan_bytes", "fox_attn_skip_plan", "skip_plan_arrays",
+    "fox_attn_decode_workspace_bytes", "fox_attn_decode", "fox_attn_decode_append",
     "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
     "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID",
     "FOX_E_UNSUPPORTED", "FOX_E_LAUNCH", "FOX_F32", "FOX_BF16", "FOX_CAUSAL",
@@ -76,6 +79,13 @@ _SIGS = {
                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                        _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_dlogf_from_dc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_attn_decode_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "fox_attn_decode": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                       ctypes.c_int, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64, _c_i64,
+                                       _c_i64, _c_f32, _c_u32, _c_vp]),
+    "fox_attn_decode_append": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                              _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                              _c_vp]),
     "fox_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "fox_last_error": (ctypes.c_char_p, []),
     "fox_version": (ctypes.c_char_p, []),
@@ -422,3 +432,56 @@ def fox_dlogf_from_dc(dc_q: torch.Tensor, dc_k: torch.Tensor) -> torch.Tensor:
     _check(lib.fox_dlogf_from_dc(pa, pb, ctypes.c_void_p(out.data_ptr()), dc_q.numel() // L, L,
                                  _stream(dc_q)), "fox_dlogf_from_dc")
     return out
+
+
+def fox_attn_decode_workspace_bytes(B: int, H: int, T_max: int, D: int) -> int:
+    return int(load_library().fox_attn_decode_workspace_bytes(B, H, T_max, D))
+
+
+def fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype: torch.dtype = torch.float32,
+                    scale: float | None = None, workspace=None):
+    """(o [B, H, D], lse [B, H]) of the newest position of each sequence against the cache.
+
+    q: [B, H, D] bf16; k_cache, v_cache: [B, H, T_max, D] bf16; c_cache: [B, H, T_max] fp32;
+    lens: [B] int32 device tensor of cached lengths (the query sits at lens[b] - 1)."""
+    lib = load_library()
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share one shape [B, H, T_max, D]")
+    B, H, T, D = k_cache.shape
+    if tuple(q.shape) != (B, H, D) or tuple(c_cache.shape) != (B, H, T):
+        raise ValueError("q must be [B, H, D] and c_cache [B, H, T_max]")
+    if tuple(lens.shape) != (B,):
+        raise ValueError("lens must be [B]")
+    pq = _dev(q, "q", (torch.bfloat16,), 3)
+    pk, pv = _dev(k_cache, "k_cache", (torch.bfloat16,), 4), _dev(v_cache, "v_cache", (torch.bfloat16,), 4)
+    pc = _dev(c_cache, "c_cache", (torch.float32,), 3)
+    pl = _dev(lens, "lens", (torch.int32,), 1)
+    o = torch.empty((B, H, D), dtype=o_dtype, device=q.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = fox_attn_decode_workspace_bytes(B, H, T, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace", (torch.uint8,))
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_decode(pq, pk, pv, FOX_BF16, pc, pl, ctypes.c_void_p(o.data_ptr()),
+                               _code(o_dtype), ctypes.c_void_p(lse.data_ptr()), pw,
+                               workspace.numel(), B, H, T, D, scale, FOX_CAUSAL, _stream(q)),
+           "fox_attn_decode")
+    return o, lse
+
+
+def fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, lens):
+    """Append one position per sequence to the cache in place (k, v, c), then lens += 1."""
+    lib = load_library()
+    B, H, T, D = k_cache.shape
+    if tuple(k_new.shape) != (B, H, D) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [B, H, D]")
+    if tuple(log_f_new.shape) != (B, H) or tuple(lens.shape) != (B,):
+        raise ValueError("log_f_new must be [B, H] and lens [B]")
+    args = (_dev(k_new, "k_new", (torch.bfloat16,), 3), _dev(v_new, "v_new", (torch.bfloat16,), 3),
+            FOX_BF16, _dev(log_f_new, "log_f_new", (torch.float32,), 2),
+            _dev(k_cache, "k_cache", (torch.bfloat16,), 4),
+            _dev(v_cache, "v_cache", (torch.bfloat16,), 4),
+            _dev(c_cache, "c_cache", (torch.float32,), 3), _dev(lens, "lens", (torch.int32,), 1))
+    _check(lib.fox_attn_decode_append(*args, B, H, T, D, _stream(k_cache)),
+           "fox_attn_decode_append")

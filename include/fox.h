@@ -213,6 +213,39 @@ fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dty
 fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f, int64_t BH,
                              int64_t L, void* stream);
 
+/* Single-token decode against a KV cache. The last position t of a sequence attends to all of
+ * its cached positions: o_t = sum_{j<=t} softmax_j(scale q_t.k_j + c_t - c_j) v_j, the forward's
+ * row t (paper-graph-ui summary, section 3.4, "The Mathematical Form of Forgetting Attention"),
+ * and appending a token extends c by the recurrence c_t = c_{t-1} + log f_t of the prefix sum
+ * ("Hardware-Aware Implementation"). The cache has the forward's layout, so a prefill with
+ * fox_logf_cumsum and fox_attn_fwd over the prompt leaves k, v, c ready for decoding.
+ *   q       : [B, H, D] bf16, the query of the newest position of each sequence
+ *   k_cache, v_cache : [B, H, T_max, D] bf16;  c_cache : [B, H, T_max] fp32
+ *   lens    : [B] int32 on the device, the number of cached positions of each sequence
+ *             (1 <= lens[b] <= T_max; the query sits at position lens[b] - 1, whose key and
+ *             value must already be in the cache). A length above T_max is read as T_max; a
+ *             sequence with lens[b] < 1 gets zeros and lse = -inf.
+ *   o       : [B, H, D] in o_dt (FOX_BF16 or FOX_F32);  lse : [B, H] fp32 or NULL
+ *   workspace : at least fox_attn_decode_workspace_bytes(B, H, T_max, D) bytes, 256-byte
+ *             aligned, contents ignored and clobbered.
+ * fp32 logits, exponentials and sums; no rounding of the weights. flags must contain
+ * FOX_CAUSAL. Reads every cached key and value once (bound by HBM). */
+size_t fox_attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t T_max, int64_t D);
+fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           fox_dtype in_dt, const float* c_cache, const int32_t* lens, void* o,
+                           fox_dtype o_dt, float* lse, void* workspace, size_t workspace_bytes,
+                           int64_t B, int64_t H, int64_t T_max, int64_t D, float scale,
+                           uint32_t flags, void* stream);
+
+/* Append one position to every sequence of the cache: at index p = lens[b], copy k_new and
+ * v_new ([B, H, D] bf16) and set c_cache[b, h, p] = c_cache[b, h, p - 1] + log_f_new[b, h]
+ * (log_f_new : [B, H] fp32; c starts at log f for p = 0), then lens[b] += 1, all on the device.
+ * A sequence with lens[b] >= T_max (a full cache) is left unchanged, lens included. */
+fox_status fox_attn_decode_append(const void* k_new, const void* v_new, fox_dtype in_dt,
+                                  const float* log_f_new, void* k_cache, void* v_cache,
+                                  float* c_cache, int32_t* lens, int64_t B, int64_t H,
+                                  int64_t T_max, int64_t D, void* stream);
+
 /* Static description of a status code. */
 const char* fox_status_str(fox_status s);
 

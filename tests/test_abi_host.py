@@ -127,6 +127,40 @@ def test_skip_plan_rejects(lib):
     assert plan(L=0) == 1
 
 
+def test_decode_workspace_size(lib):
+    # fp32 [B*H, ceil(T / chunk), D + 2], rounded up to 256 bytes; chunk = 512 positions here
+    # (the largest power of two that keeps at least 1536 workgroups)
+    assert lib.fox_attn_decode_workspace_bytes(4, 12, 16384, 128) == 4 * 12 * 32 * 130 * 4
+    assert lib.fox_attn_decode_workspace_bytes(1, 1, 1, 64) == 512
+    assert lib.fox_attn_decode_workspace_bytes(1, 1, 1, 96) == 0
+
+
+@host_only
+def test_decode_rejects(lib):
+    def dec(q=P, lens=P, o=P, in_dt=1, o_dt=1, ws=P, ws_bytes=1 << 30, T=64, D=128, flags=1):
+        return lib.fox_attn_decode(q, P, P, in_dt, P, lens, o, o_dt, None, ws, ws_bytes, 2, 3, T,
+                                   D, 0.1, flags, None)
+    assert dec(q=0) == 1
+    assert dec(lens=0) == 1
+    assert dec(o=P + 8) == 1
+    assert dec(in_dt=0) == 2
+    assert dec(o_dt=4) == 1
+    assert dec(ws=P + 16) == 1
+    assert dec(ws_bytes=100) == 1
+    assert "workspace too small" in lib.fox_last_error().decode()
+    assert dec(T=0) == 1
+    assert dec(D=96) == 1
+    assert dec(flags=0) == 2
+
+    def app(k_new=P, lens=P, in_dt=1, T=64, D=128):
+        return lib.fox_attn_decode_append(k_new, P, in_dt, P, P, P, P, lens, 2, 3, T, D, None)
+    assert app(k_new=0) == 1
+    assert app(lens=P + 4) == 1
+    assert app(in_dt=0) == 2
+    assert app(D=32) == 1
+    assert app(T=0) == 1
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         fox.load_library(str(tmp_path / "missing.so"))

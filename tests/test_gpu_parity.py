@@ -516,3 +516,117 @@ def test_skip_config5_full_length(fox):
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv", "dlog f"), g0, g1):
         assert torch.equal(a, b), name
+
+
+# ---------------------------------------------------------------------------- single-token decode
+def _decode_ref(q, k, v, log_f, lens, scale):
+    """Oracle rows: the query of sequence b sits at position lens[b] - 1 of its cache."""
+    B, H, D = q.shape
+    cc = oracle.cumsum_logf(log_f)
+    O = np.zeros((B, H, D))
+    LSE = np.zeros((B, H))
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(H):
+            qf = np.zeros((n, D), np.float32)
+            qf[n - 1] = q[b, h]
+            o, l = oracle.attn_fwd_rows(qf, k[b, h, :n], v[b, h, :n], cc[b, h, :n],
+                                        np.array([n - 1]), scale=scale)
+            O[b, h], LSE[b, h] = o[0], l[0]
+    return O, LSE
+
+
+def _check_decode(name, got, ref, log_f):
+    """The bf16 bar, plus the bound fp32 arithmetic meets given the fp32 rounding of c: each c
+    is within an ulp of the exact prefix sum, so every bias c_t - c_j, and with it every weight,
+    is off by at most 2 ulp(max |c|) relative (at least the fp32 floor of 1e-5)."""
+    cmax = float(np.abs(oracle.cumsum_logf(log_f)).max())
+    _check_tight(name, got, ref, rel=max(1e-5, 4 * 2.0 ** -23 * cmax))
+
+
+def _decode_case(B, H, T, D, seed):
+    case = fi.make_case(B, H, T, D, "bf16", seed=seed, gate="per_head",
+                        head_mean_range=(0.0, 6.0))
+    q = fi.bf16_round(np.random.default_rng(seed + 7).standard_normal((B, H, D), dtype=np.float32))
+    return case, q
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("o_dt", ["bf16", "f32"])
+def test_decode_matches_oracle(fox, D, o_dt):
+    """Ragged lengths, including a one-position cache and a full one."""
+    B, H, T = 3, 2, 1100
+    lens = np.array([1, 300, 1100], np.int32)
+    case, q = _decode_case(B, H, T, D, seed=D)
+    say(f"decode D={D} o={o_dt} lens={lens.tolist()}")
+    kc, vc = dev(case.k, "bf16"), dev(case.v, "bf16")
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    o_torch = torch.bfloat16 if o_dt == "bf16" else torch.float32
+    o, lse = fox.fox_attn_decode(dev(q, "bf16"), kc, vc, c, torch.from_numpy(lens).cuda(),
+                                 o_dtype=o_torch)
+    torch.cuda.synchronize()
+    O, LSE = _decode_ref(q, case.k, case.v, case.log_f, lens, default_scale(D))
+    if o_dt == "f32":
+        _check_decode("decode O", host(o), O, case.log_f)
+    else:
+        check("decode O", host(o), O)
+    _check_decode("decode LSE", host(lse), LSE, case.log_f)
+
+
+def test_decode_full_length(fox):
+    """Four sequences of 12 heads in a 16384-position cache (D = 128), lengths 16384, 9000, 1
+    and 5000, at the bench's decode shape."""
+    B, H, T, D = 4, 12, 16384, 128
+    lens = np.array([16384, 9000, 1, 5000], np.int32)
+    case, q = _decode_case(B, H, T, D, seed=77)
+    say("decode full length")
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    o, lse = fox.fox_attn_decode(dev(q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16"), c,
+                                 torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    O, LSE = _decode_ref(q, case.k, case.v, case.log_f, lens, default_scale(D))
+    _check_decode("decode O", host(o), O, case.log_f)
+    _check_decode("decode LSE", host(lse), LSE, case.log_f)
+
+
+def test_decode_append_after_prefill(fox):
+    """A prefill of 500 positions (scan + cache), then 20 appended tokens, each followed by a
+    decode step compared with the oracle's row; the cache holds the appended k, v exactly and
+    c within fp32 rounding of the prefix sum. A full cache is left unchanged."""
+    B, H, T, D, L0, N = 2, 3, 520, 64, 500, 20
+    case, _ = _decode_case(B, H, T, D, seed=5)
+    rng = np.random.default_rng(9)
+    qs = fi.bf16_round(rng.standard_normal((N, B, H, D), dtype=np.float32))
+    say("decode append after prefill")
+    kc, vc = dev(case.k, "bf16"), dev(case.v, "bf16")
+    kc[:, :, L0:].zero_()
+    vc[:, :, L0:].zero_()
+    c = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    c[:, :, :L0] = fox.fox_logf_cumsum(dev(np.ascontiguousarray(case.log_f[:, :, :L0]), "f32"))
+    lens = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    for n in range(N):
+        p = L0 + n
+        fox.fox_attn_decode_append(dev(np.ascontiguousarray(case.k[:, :, p]), "bf16"),
+                                   dev(np.ascontiguousarray(case.v[:, :, p]), "bf16"),
+                                   dev(np.ascontiguousarray(case.log_f[:, :, p]), "f32"),
+                                   kc, vc, c, lens)
+        o, lse = fox.fox_attn_decode(dev(qs[n], "bf16"), kc, vc, c, lens)
+        torch.cuda.synchronize()
+        assert host(lens).tolist() == [p + 1] * B
+        O, LSE = _decode_ref(qs[n], case.k, case.v, case.log_f, np.full(B, p + 1), default_scale(D))
+        _check_decode(f"decode O after {n + 1} appends", host(o), O, case.log_f[:, :, :p + 1])
+        _check_decode(f"decode LSE after {n + 1} appends", host(lse), LSE, case.log_f[:, :, :p + 1])
+    assert np.array_equal(host(kc.float())[:, :, :L0 + N], case.k[:, :, :L0 + N])
+    assert np.array_equal(host(vc.float())[:, :, :L0 + N], case.v[:, :, :L0 + N])
+    ref_c = oracle.cumsum_logf(case.log_f[:, :, :L0 + N])
+    assert np.all(np.abs(host(c)[:, :, :L0 + N] - ref_c) <= 1e-5 * (1 + np.abs(ref_c)))
+    # a full cache: nothing is written and lens stays at T
+    lens.fill_(T)
+    before = (kc.clone(), vc.clone(), c.clone())
+    fox.fox_attn_decode_append(dev(np.ascontiguousarray(case.k[:, :, 0]), "bf16"),
+                               dev(np.ascontiguousarray(case.v[:, :, 0]), "bf16"),
+                               dev(np.ascontiguousarray(case.log_f[:, :, 0]), "f32"),
+                               kc, vc, c, lens)
+    torch.cuda.synchronize()
+    assert host(lens).tolist() == [T] * B
+    assert all(torch.equal(a, b) for a, b in zip(before, (kc, vc, c)))
