@@ -411,15 +411,15 @@ def test_backward_deterministic(fox):
 
 
 # ------------------------------------------------------------------------------ exact tile skipping
-def _skip_case(L, D, kind, H=4, seed=0):
+def _skip_case(L, D, kind, H=4, seed=0, B=1):
     if kind == "strong":  # log f averaging about -0.7 per token: most old tiles carry no weight
-        case = fi.make_case(1, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=0.0,
+        case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=0.0,
                             with_do=True)
     elif kind == "mixed":  # per-head gates from strongly to barely forgetting
-        case = fi.make_case(1, H, L, D, "bf16", seed=seed, gate="per_head",
+        case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="per_head",
                             head_mean_range=(-2.0, 6.0), with_do=True)
     else:  # hard resets inside otherwise open gates
-        case = fi.make_case(1, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=6.0,
+        case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=6.0,
                             with_do=True)
         case.log_f[..., L // 3] = -1e4
         case.log_f[..., (2 * L) // 3 + 5] = -1e4
@@ -459,26 +459,27 @@ def _check_plan_against_oracle(fox, case, plan, c):
     return q_skip, kv_tiles
 
 
-@pytest.mark.parametrize("L,D,kind", [(3000, 128, "strong"), (1000, 64, "strong"),
-                                      (2500, 128, "mixed"), (1500, 64, "reset"), (100, 128, "strong"),
-                                      (4097, 128, "reset")])
-def test_skip_plan_matches_oracle(fox, L, D, kind):
-    case = _skip_case(L, D, kind, seed=L)
+SKIP_CASES = [(3000, 128, "strong", 1), (1000, 64, "strong", 1), (2500, 128, "mixed", 1),
+              (1500, 64, "reset", 1), (100, 128, "strong", 1), (4097, 128, "reset", 1),
+              (2000, 128, "mixed", 2), (1300, 64, "strong", 3)]
+
+
+@pytest.mark.parametrize("L,D,kind,B", SKIP_CASES)
+def test_skip_plan_matches_oracle(fox, L, D, kind, B):
+    case = _skip_case(L, D, kind, seed=L, B=B)
     say(f"skip plan L={L} D={D} {kind}")
     q, k, v, c, plan = _plan_and_inputs(fox, case)
     torch.cuda.synchronize()
     q_skip, kv_tiles = _check_plan_against_oracle(fox, case, plan, c)
     if L >= 1000 and kind != "mixed":
-        assert q_skip.sum() > 0 and kv_tiles.sum() < case.H * sum(
+        assert q_skip.sum() > 0 and kv_tiles.sum() < B * case.H * sum(
             -(-(L - 128 * b) // 64) for b in range(-(-L // 128)))
 
 
-@pytest.mark.parametrize("L,D,kind", [(3000, 128, "strong"), (1000, 64, "strong"),
-                                      (2500, 128, "mixed"), (1500, 64, "reset"), (100, 128, "strong"),
-                                      (4097, 128, "reset")])
-def test_skip_is_exact(fox, L, D, kind):
+@pytest.mark.parametrize("L,D,kind,B", SKIP_CASES)
+def test_skip_is_exact(fox, L, D, kind, B):
     """With the plan, the forward (bf16 and fp32 O) and the backward return bit-identical results."""
-    case = _skip_case(L, D, kind, seed=L + 1)
+    case = _skip_case(L, D, kind, seed=L + 1, B=B)
     say(f"skip exact L={L} D={D} {kind}")
     q, k, v, c, plan = _plan_and_inputs(fox, case)
     for o_dt in (torch.bfloat16, torch.float32):
