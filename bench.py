@@ -382,7 +382,7 @@ def pro_step(args, torch, fi, fox, dev):
     names = ["gate", "scan", "qnorm", "knorm", "fwd", "delta", "dq", "dkv", "dlogf", "qnorm_bwd",
              "knorm_bwd", "gate_bwd"]
 
-    def step(events):
+    def step(events, skip=False):
         def run(n, fn):
             if events is None:
                 return fn()
@@ -396,11 +396,14 @@ def pro_step(args, torch, fi, fox, dev):
         c = run("scan", lambda: fox.fox_logf_cumsum(lf))
         qn = run("qnorm", lambda: fox.fox_qk_rmsnorm(q, eps=1e-6))
         kn = run("knorm", lambda: fox.fox_qk_rmsnorm(k, eps=1e-6))
-        o, lse = run("fwd", lambda: fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32))
+        plan = run("plan", lambda: fox.fox_attn_skip_plan(qn, kn, c)) if skip else None
+        o, lse = run("fwd", lambda: fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32,
+                                                     skip_plan=plan))
         delta = run("delta", lambda: fox.fox_attn_bwd_delta(do, o))
         dqn, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(qn, kn, v, c, lse, do, delta,
-                                                                 delta_out=delta))
-        dkn, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(qn, kn, v, c, lse, do, delta))
+                                                                 delta_out=delta, skip_plan=plan))
+        dkn, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(qn, kn, v, c, lse, do, delta,
+                                                               skip_plan=plan))
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
         dq, _ = run("qnorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(q, dqn, eps=1e-6))
         dk, _ = run("knorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(k, dkn, eps=1e-6))
@@ -447,6 +450,27 @@ def pro_step(args, torch, fi, fox, dev):
         "kernel_ms": {n: round(kern_ms[n], 4) for n in names},
         "host_wall_ms_per_step": round(wall_ms, 4),
     }
+    if not args.no_skip:  # the same step with exact tile skipping, a separate measurement
+        ref = step(None)
+        got = step(None, skip=True)
+        torch.cuda.synchronize()
+        identical = all(torch.equal(a, b) for a, b in zip(ref, got))
+        for _ in range(args.warmup):
+            step(None, skip=True)
+        ev = []
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            step(ev, skip=True)
+        torch.cuda.synchronize()
+        ms = ev[0][1].elapsed_time(ev[-1][2]) / args.steps
+        out["skip_decayed"] = {
+            "ms_per_step": round(ms, 4),
+            "effective_tflops": round(7 * unit / (ms * 1e-3) / 1e12, 2),
+            "speedup_vs_dense": round(ms_per_step / ms, 3),
+            "bit_identical_to_dense": bool(identical),
+            "kernel_ms": {n: round(float(np.mean([a.elapsed_time(b) for m, a, b in ev if m == n])), 4)
+                          for n in ["plan"] + names},
+        }
     print(json.dumps(out), flush=True)
 
 
