@@ -120,6 +120,58 @@ def rms_norm_bwd(x, dy, eps, weight=None):
     return dx, dw
 
 
+# ----------------------------------------------------------------------------------------------
+# Pro block: KV-shift and output norm + gate  ([FoX-pg] "The Pro Block Architecture", Steps 2,
+# 3, 5 and 7). The equations of these steps are missing from the page; the readings below take
+# the plainest form its words support (see the readings table of the design notes).
+# ----------------------------------------------------------------------------------------------
+def shift_gate(x, w):
+    """Shift gate alpha[b, h, t] = sigma(x[b, t, :] . w[h, :]) in (0, 1), one learned vector per
+    head and no bias (Step 2: "an additional learned vector for the shift gate")."""
+    z = np.transpose(np.matmul(_f64(x), _f64(w).T), (0, 2, 1))
+    return np.exp(log_sigmoid(z))
+
+
+def kv_shift(x_cand, alpha):
+    """Data-dependent token shift over positions (Steps 2-3): the shift gate interpolates between
+    the previous position's candidate and the current one,
+        y_t = alpha_t x_{t-1} + (1 - alpha_t) x_t,   x_{-1} = 0,
+    with alpha_t weighting the carried-forward previous candidate. x_cand [..., L, D],
+    alpha [..., L]."""
+    x, a = _f64(x_cand), _f64(alpha)[..., None]
+    prev = np.concatenate([np.zeros_like(x[..., :1, :]), x[..., :-1, :]], axis=-2)
+    return a * prev + (1.0 - a) * x
+
+
+def kv_shift_bwd(x_cand, alpha, dy):
+    """Gradients of kv_shift: dx_t = (1 - alpha_t) dy_t + alpha_{t+1} dy_{t+1} (the last
+    position has no successor) and dalpha_t = sum_d dy_t (x_{t-1} - x_t)."""
+    x, a, g = _f64(x_cand), _f64(alpha), _f64(dy)
+    prev = np.concatenate([np.zeros_like(x[..., :1, :]), x[..., :-1, :]], axis=-2)
+    nxt = np.concatenate([(a[..., 1:, None] * g[..., 1:, :]), np.zeros_like(g[..., :1, :])], axis=-2)
+    dx = (1.0 - a[..., None]) * g + nxt
+    da = np.sum(g * (prev - x), axis=-1)
+    return dx, da
+
+
+def out_norm_gate(o, g_lin, eps, weight=None):
+    """Output normalisation and gating (Steps 5 and 7): y = RMSNorm(o) [* weight] * sigma(g_lin),
+    the per-dimension output gate sigma(W_g x) applied to the normalised attention output
+    before the output projection."""
+    return rms_norm(o, eps, weight) * np.exp(log_sigmoid(_f64(g_lin)))
+
+
+def out_norm_gate_bwd(o, g_lin, eps, dy, weight=None):
+    """Gradients of out_norm_gate: with n = RMSNorm(o) [* weight] and s = sigma(g_lin),
+    dg_lin = dy n s (1 - s) and do = RMSNorm backward of dy s (rms_norm_bwd)."""
+    gl, dy = _f64(g_lin), _f64(dy)
+    s = np.exp(log_sigmoid(gl))
+    n = rms_norm(o, eps, weight)
+    dg = dy * n * s * np.exp(log_sigmoid(-gl))
+    do, _ = rms_norm_bwd(o, dy * s, eps, weight)
+    return do, dg
+
+
 def fixed_gate_logf(t_min, t_max, H):
     """Data-independent gate initialisation ([FoX-pl] D; [FoX-pg] "Connection to ALiBi").
 

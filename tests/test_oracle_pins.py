@@ -545,3 +545,83 @@ def test_planted_skip_mistake_is_caught(name):
     mod = types.ModuleType("oracle_skip_mutant_" + name)
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
     assert not _skip_pins_hold(mod)
+
+
+# ------------------------------------------------------- Pro block: KV-shift and output norm + gate
+# Forward pins: torch's sigmoid and matmul for the shift gate; special gate values where the
+# shift is the identity, a pure one-position shift, or the mean of neighbours; the output gate
+# saturated open (RMSNorm, pinned above against torch) and half open. Backward pins: central
+# finite differences of the oracle's own forward, in every input.
+def _pro_shift_pins_hold(mod):
+    rng = np.random.default_rng(31)
+    B, H, L, D, dm = 2, 3, 9, 8, 16
+    x = rng.standard_normal((B, L, dm))
+    w = rng.standard_normal((H, dm)) * 0.3
+    a = mod.shift_gate(x, w)
+    ref = torch.sigmoid(_t(x) @ _t(w).T).permute(0, 2, 1).numpy()
+    if np.abs(a - ref).max() > 1e-14:
+        return False
+    xc = rng.standard_normal((B, H, L, D))
+    zero, one = np.zeros((B, H, L)), np.ones((B, H, L))
+    shifted = np.concatenate([np.zeros((B, H, 1, D)), xc[:, :, :-1]], axis=2)
+    if not (np.allclose(mod.kv_shift(xc, zero), xc, rtol=0, atol=1e-15)
+            and np.allclose(mod.kv_shift(xc, one), shifted, rtol=0, atol=1e-15)
+            and np.allclose(mod.kv_shift(xc, one / 2), (xc + shifted) / 2, rtol=0, atol=1e-15)):
+        return False
+    dy = rng.standard_normal((B, H, L, D))
+    al = rng.uniform(0.05, 0.95, size=(B, H, L))
+    dx, da = mod.kv_shift_bwd(xc, al, dy)
+    loss = lambda x_, a_: float(np.sum(dy * oracle.kv_shift(x_, a_)))
+    for which, grad in ((0, dx), (1, da)):
+        u = rng.standard_normal(xc.shape if which == 0 else al.shape)
+        fd = _fd_dir(loss, (xc, al), which, u)
+        if abs(fd - float(np.sum(grad * u))) > 1e-7 * max(1.0, abs(fd)):
+            return False
+    return True
+
+
+def _pro_out_pins_hold(mod):
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((6, 16)) * rng.uniform(0.1, 3.0, size=(6, 1))
+    g = rng.standard_normal((6, 16))
+    wgt = rng.uniform(0.5, 1.5, size=16)
+    for weight in (None, wgt):
+        if not np.allclose(mod.out_norm_gate(o, np.full_like(g, 60.0), 1e-3, weight),
+                           oracle.rms_norm(o, 1e-3, weight), rtol=1e-15, atol=1e-15):
+            return False
+        if not np.allclose(mod.out_norm_gate(o, np.zeros_like(g), 1e-3, weight),
+                           0.5 * oracle.rms_norm(o, 1e-3, weight), rtol=1e-15, atol=1e-15):
+            return False
+        dy = rng.standard_normal(o.shape)
+        do, dg = mod.out_norm_gate_bwd(o, g, 1e-3, dy, weight)
+        loss = lambda o_, g_: float(np.sum(dy * oracle.out_norm_gate(o_, g_, 1e-3, weight)))
+        for which, grad in ((0, do), (1, dg)):
+            u = rng.standard_normal(o.shape)
+            fd = _fd_dir(loss, (o, g), which, u)
+            if abs(fd - float(np.sum(grad * u))) > 1e-7 * max(1.0, abs(fd)):
+                return False
+    return True
+
+
+def test_pro_shift_and_output_pins():
+    assert _pro_shift_pins_hold(fox_oracle)
+    assert _pro_out_pins_hold(fox_oracle)
+
+
+PRO2_MUTATIONS = {
+    "shift_gate_sides_swapped": ("return a * prev + (1.0 - a) * x", "return (1.0 - a) * prev + a * x"),
+    "shift_bwd_next_gate": ("(a[..., 1:, None] * g[..., 1:, :])", "(a[..., :-1, None] * g[..., 1:, :])"),
+    "shift_bwd_dalpha_sign": ("da = np.sum(g * (prev - x), axis=-1)", "da = np.sum(g * (x - prev), axis=-1)"),
+    "out_gate_derivative": ("dg = dy * n * s * np.exp(log_sigmoid(-gl))", "dg = dy * n * s"),
+    "out_norm_bwd_ungated": ("do, _ = rms_norm_bwd(o, dy * s, eps, weight)", "do, _ = rms_norm_bwd(o, dy, eps, weight)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PRO2_MUTATIONS))
+def test_planted_pro_shift_output_mistake_is_caught(name):
+    src = open(fox_oracle.__file__).read()
+    old, new = PRO2_MUTATIONS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle_pro2_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    assert not (_pro_shift_pins_hold(mod) and _pro_out_pins_hold(mod))
