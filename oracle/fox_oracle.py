@@ -132,6 +132,15 @@ def shift_gate(x, w):
     return np.exp(log_sigmoid(z))
 
 
+def shift_gate_bwd(x, w, dalpha):
+    """Gradients of shift_gate for the upstream gradient dalpha [B, H, L]:
+    dz = dalpha sigma(z) sigma(-z), dw = sum_{b,t} dz x, dx = sum_h dz w. Returns (dx, dw)."""
+    x, w, g = _f64(x), _f64(w), _f64(dalpha)
+    z = np.transpose(np.matmul(x, w.T), (0, 2, 1))
+    dz = g * np.exp(log_sigmoid(z) + log_sigmoid(-z))
+    return np.einsum("bhl,hd->bld", dz, w), np.einsum("bhl,bld->hd", dz, x)
+
+
 def kv_shift(x_cand, alpha):
     """Data-dependent token shift over positions (Steps 2-3): the shift gate interpolates between
     the previous position's candidate and the current one,

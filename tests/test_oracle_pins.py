@@ -561,6 +561,14 @@ def _pro_shift_pins_hold(mod):
     ref = torch.sigmoid(_t(x) @ _t(w).T).permute(0, 2, 1).numpy()
     if np.abs(a - ref).max() > 1e-14:
         return False
+    da = rng.standard_normal((B, H, L))
+    gx, gw = mod.shift_gate_bwd(x, w, da)
+    loss = lambda x_, w_: float(np.sum(da * oracle.shift_gate(x_, w_)))
+    for which, grad in ((0, gx), (1, gw)):
+        u = rng.standard_normal(x.shape if which == 0 else w.shape)
+        fd = _fd_dir(loss, (x, w), which, u)
+        if abs(fd - float(np.sum(grad * u))) > 1e-7 * max(1.0, abs(fd)):
+            return False
     xc = rng.standard_normal((B, H, L, D))
     zero, one = np.zeros((B, H, L)), np.ones((B, H, L))
     shifted = np.concatenate([np.zeros((B, H, 1, D)), xc[:, :, :-1]], axis=2)
@@ -610,6 +618,8 @@ def test_pro_shift_and_output_pins():
 
 PRO2_MUTATIONS = {
     "shift_gate_sides_swapped": ("return a * prev + (1.0 - a) * x", "return (1.0 - a) * prev + a * x"),
+    "shift_gate_bwd_derivative": ("dz = g * np.exp(log_sigmoid(z) + log_sigmoid(-z))",
+                                  "dz = g * np.exp(log_sigmoid(-z))"),
     "shift_bwd_next_gate": ("(a[..., 1:, None] * g[..., 1:, :])", "(a[..., :-1, None] * g[..., 1:, :])"),
     "shift_bwd_dalpha_sign": ("da = np.sum(g * (prev - x), axis=-1)", "da = np.sum(g * (x - prev), axis=-1)"),
     "out_gate_derivative": ("dg = dy * n * s * np.exp(log_sigmoid(-gl))", "dg = dy * n * s"),
