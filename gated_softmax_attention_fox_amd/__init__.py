@@ -18,6 +18,10 @@ C entry points (include/fox.h) and their wrappers:
     fox_dlogf_from_dc(dc_q, dc_k)                  -> dlog_f
     fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype, scale) -> (o, lse)
     fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, lens) (in place)
+    fox_shift_gate(x, w) -> alpha;  fox_shift_gate_bwd(x, w, dalpha) -> (dx, dw)
+    fox_kv_shift(x, alpha, normalize, eps, weight) -> y
+    fox_kv_shift_bwd(x, alpha, dy, normalize, eps, weight) -> (dx, dalpha)
+    fox_out_norm_gate(o, g, eps, weight) -> y;  fox_out_norm_gate_bwd(o, g, dy, eps, weight) -> (do, dg)
 """
 from __future__ import annotations
 
@@ -33,6 +37,8 @@ __all__ = [
     "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_bwd",
     "fox_attn_skip_plan_bytes", "fox_attn_skip_plan", "skip_plan_arrays",
     "fox_attn_decode_workspace_bytes", "fox_attn_decode", "fox_attn_decode_append",
+    "fox_shift_gate", "fox_shift_gate_bwd", "fox_kv_shift", "fox_kv_shift_bwd", "fox_out_norm_gate",
+    "fox_out_norm_gate_bwd",
     "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
     "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID",
     "FOX_E_UNSUPPORTED", "FOX_E_LAUNCH", "FOX_F32", "FOX_BF16", "FOX_CAUSAL",
@@ -79,6 +85,18 @@ _SIGS = {
                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                        _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_dlogf_from_dc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_shift_gate": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                      _c_i64, _c_vp]),
+    "fox_shift_gate_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                          _c_sz, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp]),
+    "fox_kv_shift": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int, _c_f32, _c_vp,
+                                    _c_i64, _c_i64, _c_i64, _c_vp]),
+    "fox_kv_shift_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                        ctypes.c_int, _c_f32, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp]),
+    "fox_out_norm_gate": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, ctypes.c_int, _c_vp, _c_f32,
+                                         _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_out_norm_gate_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, ctypes.c_int, _c_vp,
+                                             _c_f32, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_attn_decode_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "fox_attn_decode": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
                                        ctypes.c_int, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64, _c_i64,
@@ -485,3 +503,111 @@ def fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, l
             _dev(c_cache, "c_cache", (torch.float32,), 3), _dev(lens, "lens", (torch.int32,), 1))
     _check(lib.fox_attn_decode_append(*args, B, H, T, D, _stream(k_cache)),
            "fox_attn_decode_append")
+
+
+def _wptr(weight, D):
+    if weight is None:
+        return ctypes.c_void_p(0)
+    if tuple(weight.shape) != (D,):
+        raise ValueError(f"weight must be [{D}]")
+    return _dev(weight, "weight", (torch.float32,), 1)
+
+
+def fox_shift_gate(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """Shift gate alpha [B, H, L] = sigmoid(x . w^T) (x [B, L, d_model], w [H, d_model] fp32)."""
+    lib = load_library()
+    B, L, dm = x.shape
+    H = w.shape[0]
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
+    pw = _dev(w, "w", (torch.float32,), 2)
+    alpha = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
+    _check(lib.fox_shift_gate(px, _code(x.dtype), pw, ctypes.c_void_p(alpha.data_ptr()), B, L, dm,
+                              H, _stream(x)), "fox_shift_gate")
+    return alpha
+
+
+def fox_shift_gate_bwd(x: torch.Tensor, w: torch.Tensor, dalpha: torch.Tensor):
+    """(dx, dw) of the shift gate for the upstream gradient dalpha [B, H, L]."""
+    lib = load_library()
+    B, L, dm = x.shape
+    H = w.shape[0]
+    px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
+    pw = _dev(w, "w", (torch.float32,), 2)
+    pd = _dev(dalpha, "dalpha", (torch.float32,), 3)
+    dx = torch.empty((B, L, dm), dtype=torch.float32, device=x.device)
+    dw = torch.empty((H, dm), dtype=torch.float32, device=x.device)
+    need = int(lib.fox_gate_logf_bwd_workspace_bytes(B, L, dm, H))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _check(lib.fox_shift_gate_bwd(px, _code(x.dtype), pw, pd, ctypes.c_void_p(dx.data_ptr()),
+                                  ctypes.c_void_p(dw.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                  ws.numel(), B, L, dm, H, _stream(x)), "fox_shift_gate_bwd")
+    return dx, dw
+
+
+def fox_kv_shift(x: torch.Tensor, alpha: torch.Tensor, normalize: bool = False, eps: float = 1e-6,
+                 weight: torch.Tensor | None = None) -> torch.Tensor:
+    """Token shift y_t = alpha_t x_{t-1} + (1 - alpha_t) x_t over [..., L, D], RMS-normalised when
+    normalize (keys); alpha [..., L] fp32."""
+    lib = load_library()
+    L, D = x.shape[-2], x.shape[-1]
+    BH = x.numel() // (L * D)
+    if tuple(alpha.shape) != tuple(x.shape[:-1]):
+        raise ValueError("alpha must have x's shape without the last axis")
+    px = _dev(x, "x", (torch.bfloat16, torch.float32))
+    pa = _dev(alpha, "alpha", (torch.float32,))
+    y = torch.empty_like(x)
+    _check(lib.fox_kv_shift(px, _code(x.dtype), pa, ctypes.c_void_p(y.data_ptr()), int(normalize),
+                            float(eps), _wptr(weight, D), BH, L, D, _stream(x)), "fox_kv_shift")
+    return y
+
+
+def fox_kv_shift_bwd(x, alpha, dy, normalize: bool = False, eps: float = 1e-6, weight=None):
+    """(dx, dalpha) of fox_kv_shift for the upstream gradient dy (fp32, x's shape)."""
+    lib = load_library()
+    L, D = x.shape[-2], x.shape[-1]
+    BH = x.numel() // (L * D)
+    if dy.shape != x.shape:
+        raise ValueError("dy must have x's shape")
+    px = _dev(x, "x", (torch.bfloat16, torch.float32))
+    pa = _dev(alpha, "alpha", (torch.float32,))
+    pd = _dev(dy, "dy", (torch.float32,))
+    dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    da = torch.empty(alpha.shape, dtype=torch.float32, device=x.device)
+    _check(lib.fox_kv_shift_bwd(px, _code(x.dtype), pa, pd, ctypes.c_void_p(dx.data_ptr()),
+                                ctypes.c_void_p(da.data_ptr()), int(normalize), float(eps),
+                                _wptr(weight, D), BH, L, D, _stream(x)), "fox_kv_shift_bwd")
+    return dx, da
+
+
+def fox_out_norm_gate(o: torch.Tensor, g: torch.Tensor, eps: float = 1e-6,
+                      weight: torch.Tensor | None = None) -> torch.Tensor:
+    """y = RMSNorm(o) [* weight] * sigmoid(g) over the last axis; y has g's dtype."""
+    lib = load_library()
+    if o.shape != g.shape:
+        raise ValueError("o and g must have the same shape")
+    D = o.shape[-1]
+    po = _dev(o, "o", (torch.bfloat16, torch.float32))
+    pg = _dev(g, "g", (torch.bfloat16, torch.float32))
+    y = torch.empty_like(g)
+    _check(lib.fox_out_norm_gate(po, _code(o.dtype), pg, _code(g.dtype), _wptr(weight, D),
+                                 float(eps), ctypes.c_void_p(y.data_ptr()), o.numel() // D, D,
+                                 _stream(o)), "fox_out_norm_gate")
+    return y
+
+
+def fox_out_norm_gate_bwd(o, g, dy, eps: float = 1e-6, weight=None):
+    """(d_o, dg) of fox_out_norm_gate for the upstream gradient dy (fp32)."""
+    lib = load_library()
+    if o.shape != g.shape or dy.shape != o.shape:
+        raise ValueError("o, g and dy must have the same shape")
+    D = o.shape[-1]
+    po = _dev(o, "o", (torch.bfloat16, torch.float32))
+    pg = _dev(g, "g", (torch.bfloat16, torch.float32))
+    pd = _dev(dy, "dy", (torch.float32,))
+    d_o = torch.empty(o.shape, dtype=torch.float32, device=o.device)
+    dg = torch.empty(o.shape, dtype=torch.float32, device=o.device)
+    _check(lib.fox_out_norm_gate_bwd(po, _code(o.dtype), pg, _code(g.dtype), _wptr(weight, D),
+                                     float(eps), pd, ctypes.c_void_p(d_o.data_ptr()),
+                                     ctypes.c_void_p(dg.data_ptr()), o.numel() // D, D, _stream(o)),
+           "fox_out_norm_gate_bwd")
+    return d_o, dg

@@ -109,7 +109,7 @@ fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const 
               "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
   FOX_REQUIRE(B * ((L + 63) / 64) < (int64_t(1) << 31), "B*L too large");
   return launched(fox::launch_gate(x, x_dt == FOX_BF16, w_f, b_f, log_f, B, L, d_model, H,
-                                   (hipStream_t)stream),
+                                   fox::GateKind::kLogSigmoid, (hipStream_t)stream),
                   "fox_gate_logf");
 }
 
@@ -156,7 +156,8 @@ fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, co
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
   return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w_f, b_f, dlog_f, dx, dw_f, db_f,
-                                       workspace, B, L, d_model, H, (hipStream_t)stream),
+                                       workspace, B, L, d_model, H, fox::GateKind::kLogSigmoid,
+                                       (hipStream_t)stream),
                   "fox_gate_logf_bwd");
 }
 
@@ -362,6 +363,124 @@ fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtyp
   return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dc_q, delta_out, B * H, L, D,
                                      scale, fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dq");
+}
+
+namespace {
+fox_status check_shift_gate(const void* x, fox_dtype x_dt, const float* w, int64_t B, int64_t L,
+                            int64_t d_model, int64_t H) {
+  FOX_REQUIRE_PTR(x);
+  FOX_REQUIRE_PTR(w);
+  FOX_REQUIRE(x_dt == FOX_BF16 || x_dt == FOX_F32, "x_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(B >= 1 && L >= 1 && L <= kMaxL, "B >= 1 and 1 <= L <= 2^23 required");
+  FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
+  FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
+              "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
+  FOX_REQUIRE(B * L <= (int64_t(1) << 31) / 64 && B * L * d_model <= kMaxElems,
+              "B*L*d_model too large");
+  return FOX_OK;
+}
+
+fox_status check_rows(const void* x, int64_t rows, int64_t D, float eps) {
+  FOX_REQUIRE_PTR(x);
+  FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
+  FOX_REQUIRE(rows >= 1 && rows * D <= kMaxElems, "rows out of range");
+  FOX_REQUIRE(eps >= 0.f, "eps must be >= 0");
+  return FOX_OK;
+}
+}  // namespace
+
+fox_status fox_shift_gate(const void* x, fox_dtype x_dt, const float* w, float* alpha, int64_t B,
+                          int64_t L, int64_t d_model, int64_t H, void* stream) {
+  fox_status st = check_shift_gate(x, x_dt, w, B, L, d_model, H);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(alpha);
+  return launched(fox::launch_gate(x, x_dt == FOX_BF16, w, nullptr, alpha, B, L, d_model, H,
+                                   fox::GateKind::kSigmoid, (hipStream_t)stream),
+                  "fox_shift_gate");
+}
+
+fox_status fox_shift_gate_bwd(const void* x, fox_dtype x_dt, const float* w, const float* dalpha,
+                              float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                              int64_t B, int64_t L, int64_t d_model, int64_t H, void* stream) {
+  fox_status st = check_shift_gate(x, x_dt, w, B, L, d_model, H);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(dalpha);
+  FOX_REQUIRE_PTR(dx);
+  FOX_REQUIRE_PTR(dw);
+  FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL");
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+              "workspace must be 256-byte aligned");
+  const size_t need = fox::gate_bwd_workspace_bytes(B, L, d_model, H);
+  FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
+              workspace_bytes, need);
+  return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w, nullptr, dalpha, dx, dw, nullptr,
+                                       workspace, B, L, d_model, H, fox::GateKind::kSigmoid,
+                                       (hipStream_t)stream),
+                  "fox_shift_gate_bwd");
+}
+
+fox_status fox_kv_shift(const void* x, fox_dtype dt, const float* alpha, void* y, int normalize,
+                        float eps, const float* weight, int64_t BH, int64_t L, int64_t D,
+                        void* stream) {
+  fox_status st = check_rows(x, BH * L, D, eps);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(alpha);
+  FOX_REQUIRE_PTR(y);
+  FOX_REQUIRE(dt == FOX_BF16 || dt == FOX_F32, "dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(BH >= 1 && L >= 1 && L <= kMaxL, "BH >= 1 and 1 <= L <= 2^23 required");
+  FOX_REQUIRE(y != x, "y must not alias x (each row reads its predecessor)");
+  return launched(fox::launch_kv_shift(x, dt == FOX_BF16, alpha, y, normalize != 0, eps, weight,
+                                       BH * L, L, D, (hipStream_t)stream),
+                  "fox_kv_shift");
+}
+
+fox_status fox_kv_shift_bwd(const void* x, fox_dtype dt, const float* alpha, const float* dy,
+                            float* dx, float* dalpha, int normalize, float eps,
+                            const float* weight, int64_t BH, int64_t L, int64_t D, void* stream) {
+  fox_status st = check_rows(x, BH * L, D, eps);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(alpha);
+  FOX_REQUIRE_PTR(dy);
+  FOX_REQUIRE_PTR(dx);
+  FOX_REQUIRE_PTR(dalpha);
+  FOX_REQUIRE(dt == FOX_BF16 || dt == FOX_F32, "dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(BH >= 1 && L >= 1 && L <= kMaxL, "BH >= 1 and 1 <= L <= 2^23 required");
+  FOX_REQUIRE(static_cast<const void*>(dx) != static_cast<const void*>(dy),
+              "dx must not alias dy (each row reads its successor's gradient)");
+  return launched(fox::launch_kv_shift_bwd(x, dt == FOX_BF16, alpha, dy, dx, dalpha,
+                                           normalize != 0, eps, weight, BH * L, L, D,
+                                           (hipStream_t)stream),
+                  "fox_kv_shift_bwd");
+}
+
+fox_status fox_out_norm_gate(const void* o, fox_dtype o_dt, const void* g, fox_dtype g_dt,
+                             const float* weight, float eps, void* y, int64_t rows, int64_t D,
+                             void* stream) {
+  fox_status st = check_rows(o, rows, D, eps);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(g);
+  FOX_REQUIRE_PTR(y);
+  FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(g_dt == FOX_BF16 || g_dt == FOX_F32, "g_dt must be FOX_BF16 or FOX_F32");
+  return launched(fox::launch_out_norm_gate(o, o_dt == FOX_BF16, g, g_dt == FOX_BF16, weight, eps,
+                                            y, rows, D, (hipStream_t)stream),
+                  "fox_out_norm_gate");
+}
+
+fox_status fox_out_norm_gate_bwd(const void* o, fox_dtype o_dt, const void* g, fox_dtype g_dt,
+                                 const float* weight, float eps, const float* dy, float* d_o,
+                                 float* dg, int64_t rows, int64_t D, void* stream) {
+  fox_status st = check_rows(o, rows, D, eps);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(g);
+  FOX_REQUIRE_PTR(dy);
+  FOX_REQUIRE_PTR(d_o);
+  FOX_REQUIRE_PTR(dg);
+  FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(g_dt == FOX_BF16 || g_dt == FOX_F32, "g_dt must be FOX_BF16 or FOX_F32");
+  return launched(fox::launch_out_norm_gate_bwd(o, o_dt == FOX_BF16, g, g_dt == FOX_BF16, weight,
+                                                eps, dy, d_o, dg, rows, D, (hipStream_t)stream),
+                  "fox_out_norm_gate_bwd");
 }
 
 size_t fox_attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t T_max, int64_t D) {

@@ -14,18 +14,23 @@ hipError_t launch_cumsum(const float* x, float* c, int64_t rows, int64_t L, hipS
 // out[r, l] = sum_{t >= l} (a[r, t] + b[r, t]) (fp64 accumulation, fp32 out).
 hipError_t launch_rev_cumsum2(const float* a, const float* b, float* out, int64_t rows, int64_t L,
                               hipStream_t s);
-// log_f[b, h, t] = log sigmoid(x[b, t, :] . w_f[h, :] + b_f[h]).
-hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* log_f,
-                       int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s);
-// Backward of the gate: dz[b, t, h] = dlog_f[b, h, t] * sigma(-z) (token-major).
+// What a per-head gate GEMV z = x . w^T + b (b may be null) returns: log sigma(z) (the forget
+// gate) or sigma(z) (the Pro block's shift gates).
+enum class GateKind { kLogSigmoid, kSigmoid };
+// out[b, h, t] = log sigmoid(z) or sigmoid(z), z = x[b, t, :] . w_f[h, :] + b_f[h].
+hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* out,
+                       int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
+                       hipStream_t s);
+// Backward of the gate's output: dz[b, t, h] = dout[b, h, t] * (d out / dz) (token-major).
 hipError_t launch_gate_dz(const void* x, bool x_bf16, const float* w_f, const float* b_f,
-                          const float* dlog_f, float* dz, int64_t B, int64_t L, int64_t d_model,
-                          int64_t H, hipStream_t s);
-// Backward of the gate: dx, dw_f, db_f (workspace: gate_bwd_workspace_bytes).
+                          const float* dout, float* dz, int64_t B, int64_t L, int64_t d_model,
+                          int64_t H, GateKind kind, hipStream_t s);
+// Backward of the gate: dx, dw_f and (when not null) db_f (workspace: gate_bwd_workspace_bytes).
 size_t gate_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H);
 hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const float* b_f,
-                           const float* dlog_f, float* dx, float* dw_f, float* db_f, void* ws,
-                           int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s);
+                           const float* dout, float* dx, float* dw_f, float* db_f, void* ws,
+                           int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
+                           hipStream_t s);
 // Backward of the QK-norm: dx and, when dw is not null, the weight gradient.
 size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D);
 hipError_t launch_rmsnorm_bwd(const void* x, bool bf16, const float* dy, const float* w, float* dx,
@@ -34,6 +39,19 @@ hipError_t launch_rmsnorm_bwd(const void* x, bool bf16, const float* dy, const f
 // y = x / sqrt(mean(x^2) + eps) * w over rows of length D.
 hipError_t launch_rmsnorm(const void* x, void* y, bool bf16, int64_t rows, int64_t D, float eps,
                           const float* w, hipStream_t s);
+// Pro block token shift (optionally RMS-normalised) and output norm + gate (pro_fuse.hip).
+hipError_t launch_kv_shift(const void* x, bool bf16, const float* alpha, void* y, bool norm,
+                           float eps, const float* w, int64_t rows, int64_t L, int64_t D,
+                           hipStream_t s);
+hipError_t launch_kv_shift_bwd(const void* x, bool bf16, const float* alpha, const float* dy,
+                               float* dx, float* dalpha, bool norm, float eps, const float* w,
+                               int64_t rows, int64_t L, int64_t D, hipStream_t s);
+hipError_t launch_out_norm_gate(const void* o, bool o_bf16, const void* g, bool g_bf16,
+                                const float* w, float eps, void* y, int64_t rows, int64_t D,
+                                hipStream_t s);
+hipError_t launch_out_norm_gate_bwd(const void* o, bool o_bf16, const void* g, bool g_bf16,
+                                    const float* w, float eps, const float* dy, float* d_o,
+                                    float* dg, int64_t rows, int64_t D, hipStream_t s);
 // Skip plan (skip_plan.hip): byte offsets of its four arrays and its size.
 //   q_skip   : int32 [BH, ceil(L / 256)]  leading key tiles a 256-query tile skips
 //   kv_tiles : int32 [BH, ceil(L / 128)]  64-query tiles a 128-key block walks

@@ -14,6 +14,9 @@
 // The same kernel serves the backward (kBwd): it recomputes z and writes, token-major,
 // dz[b, t, h] = dlog_f[b, h, t] * sigma(-z), since d log sigma(z) / dz = 1 - sigma(z) = sigma(-z);
 // sigma(-z) = 1 / (1 + exp(z)) goes to 0 or 1 in the limits without a NaN.
+//
+// With kSig the output is sigma(z) itself and the bias may be absent: the Pro block's shift gates
+// (Steps 2-3, one learned vector per head), whose backward takes dz = dalpha sigma(z) sigma(-z).
 #include "fox_device.h"
 #include "fox_launch.h"
 
@@ -29,7 +32,9 @@ __device__ __forceinline__ float log_sigmoid(float z) {
   return z >= 0.f ? -log1pf(expf(-z)) : z - log1pf(expf(z));
 }
 
-template <bool kBf16, bool kBwd>
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+template <bool kBf16, bool kBwd, bool kSig>
 __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    const float* __restrict__ w_f,
                                                    const float* __restrict__ b_f,
@@ -109,13 +114,14 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
     const int t = t0 + lane;
     for (int h = 0; h < nh; ++h) {
       const float z = ((red[0][h][lane] + red[1][h][lane]) + (red[2][h][lane] + red[3][h][lane])) +
-                      b_f[h0 + h];
+                      (b_f ? b_f[h0 + h] : 0.f);
       if (t < L) {
         if constexpr (kBwd) {
           const float g = dlog_f[((size_t)b * H + h0 + h) * L + t];
-          out[((size_t)b * L + t) * H + h0 + h] = g / (1.0f + expf(z));
+          out[((size_t)b * L + t) * H + h0 + h] =
+              kSig ? g * sigmoid(z) / (1.0f + expf(z)) : g / (1.0f + expf(z));
         } else {
-          out[((size_t)b * H + h0 + h) * L + t] = log_sigmoid(z);
+          out[((size_t)b * H + h0 + h) * L + t] = kSig ? sigmoid(z) : log_sigmoid(z);
         }
       }
     }
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 // parts (hi = bf16(w), lo = bf16(w - hi)) and both are multiplied, so z keeps about 16
 // significant bits of w on top of exact products and fp32 accumulation. Lane l receives z for
 // head l % 16 and tokens 4 (l / 16) .. +3. Needs d_model % 32 == 0.
-template <bool kBwd>
+template <bool kBwd, bool kSig>
 __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict__ x,
                                                         const float* __restrict__ w_f,
                                                         const float* __restrict__ b_f,
@@ -174,66 +180,70 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict
   acc = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
   const int hc = h0 + r;  // the head of this lane's output column
   if (hc >= H) return;
-  const float bias = b_f[hc];
+  const float bias = b_f ? b_f[hc] : 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tt = t0 + 4 * grp + j;
     if (tt >= L) break;
     const float z = acc[j] + bias;
     if constexpr (kBwd) {
-      out[((size_t)b * L + tt) * H + hc] = dlog_f[((size_t)b * H + hc) * L + tt] / (1.0f + expf(z));
+      const float g = dlog_f[((size_t)b * H + hc) * L + tt];
+      out[((size_t)b * L + tt) * H + hc] =
+          kSig ? g * sigmoid(z) / (1.0f + expf(z)) : g / (1.0f + expf(z));
     } else {
-      out[((size_t)b * H + hc) * L + tt] = log_sigmoid(z);
+      out[((size_t)b * H + hc) * L + tt] = kSig ? sigmoid(z) : log_sigmoid(z);
     }
   }
 }
 
-template <bool kBwd>
+template <bool kBwd, bool kSig>
 void go_gate_mfma(const void* x, const float* w_f, const float* b_f, const float* dlog_f,
                   float* out, int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
   const int tiles_per_b = (int)((L + 15) / 16);
   const int64_t n_tiles = B * tiles_per_b;
   const dim3 grid((unsigned)n_tiles, (unsigned)((H + 15) / 16));
-  hipLaunchKernelGGL((gate_mfma_kernel<kBwd>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((gate_mfma_kernel<kBwd, kSig>), grid, dim3(256), 0, s,
                      static_cast<const bf16_t*>(x), w_f, b_f, dlog_f, out, (int)L, (int)d_model,
                      (int)H, tiles_per_b, (int)n_tiles);
 }
 
 }  // namespace
 
-hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* log_f,
-                       int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
+namespace {
+template <bool kBwd, bool kSig>
+hipError_t go_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f,
+                   const float* dlog_f, float* out, int64_t B, int64_t L, int64_t d_model,
+                   int64_t H, hipStream_t s) {
   if (x_bf16 && d_model % 32 == 0) {
-    go_gate_mfma<false>(x, w_f, b_f, nullptr, log_f, B, L, d_model, H, s);
+    go_gate_mfma<kBwd, kSig>(x, w_f, b_f, dlog_f, out, B, L, d_model, H, s);
     return hipGetLastError();
   }
   const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
   const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
   if (x_bf16)
-    hipLaunchKernelGGL((gate_kernel<true, false>), grid, dim3(256), 0, s, x, w_f, b_f, nullptr,
-                       log_f, (int)L, (int)d_model, (int)H, tok_blocks);
+    hipLaunchKernelGGL((gate_kernel<true, kBwd, kSig>), grid, dim3(256), 0, s, x, w_f, b_f,
+                       dlog_f, out, (int)L, (int)d_model, (int)H, tok_blocks);
   else
-    hipLaunchKernelGGL((gate_kernel<false, false>), grid, dim3(256), 0, s, x, w_f, b_f, nullptr,
-                       log_f, (int)L, (int)d_model, (int)H, tok_blocks);
+    hipLaunchKernelGGL((gate_kernel<false, kBwd, kSig>), grid, dim3(256), 0, s, x, w_f, b_f,
+                       dlog_f, out, (int)L, (int)d_model, (int)H, tok_blocks);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* out,
+                       int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
+                       hipStream_t s) {
+  return kind == GateKind::kSigmoid
+             ? go_gate<false, true>(x, x_bf16, w_f, b_f, nullptr, out, B, L, d_model, H, s)
+             : go_gate<false, false>(x, x_bf16, w_f, b_f, nullptr, out, B, L, d_model, H, s);
 }
 
 hipError_t launch_gate_dz(const void* x, bool x_bf16, const float* w_f, const float* b_f,
-                          const float* dlog_f, float* dz, int64_t B, int64_t L, int64_t d_model,
-                          int64_t H, hipStream_t s) {
-  if (x_bf16 && d_model % 32 == 0) {
-    go_gate_mfma<true>(x, w_f, b_f, dlog_f, dz, B, L, d_model, H, s);
-    return hipGetLastError();
-  }
-  const int tok_blocks = (int)((L + kGateTok - 1) / kGateTok);
-  const dim3 grid((unsigned)(B * tok_blocks), (unsigned)((H + kGateHeads - 1) / kGateHeads));
-  if (x_bf16)
-    hipLaunchKernelGGL((gate_kernel<true, true>), grid, dim3(256), 0, s, x, w_f, b_f, dlog_f, dz,
-                       (int)L, (int)d_model, (int)H, tok_blocks);
-  else
-    hipLaunchKernelGGL((gate_kernel<false, true>), grid, dim3(256), 0, s, x, w_f, b_f, dlog_f, dz,
-                       (int)L, (int)d_model, (int)H, tok_blocks);
-  return hipGetLastError();
+                          const float* dout, float* dz, int64_t B, int64_t L, int64_t d_model,
+                          int64_t H, GateKind kind, hipStream_t s) {
+  return kind == GateKind::kSigmoid
+             ? go_gate<true, true>(x, x_bf16, w_f, b_f, dout, dz, B, L, d_model, H, s)
+             : go_gate<true, false>(x, x_bf16, w_f, b_f, dout, dz, B, L, d_model, H, s);
 }
 
 }  // namespace fox

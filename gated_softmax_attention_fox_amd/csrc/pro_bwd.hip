@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __rest
     const int h = (int)(gid - n_w);
     float s = 0.f;
     for (int c = 0; c < n_chunk; ++c) s += part_db[(size_t)c * H + h];
-    db_f[h] = s;
+    if (db_f) db_f[h] = s;
   }
 }
 
@@ -250,14 +250,15 @@ size_t gate_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H
 }
 
 hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const float* b_f,
-                           const float* dlog_f, float* dx, float* dw_f, float* db_f, void* ws,
-                           int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
+                           const float* dout, float* dx, float* dw_f, float* db_f, void* ws,
+                           int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
+                           hipStream_t s) {
   const int64_t rows = B * L;
   const int n_chunk = (int)((rows + kChunk - 1) / kChunk);
   float* dz = static_cast<float*>(ws);
   float* part = dz + granule((size_t)(rows * H));
   float* part_db = part + granule((size_t)((int64_t)n_chunk * H * d_model));
-  hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dlog_f, dz, B, L, d_model, H, s);
+  hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dout, dz, B, L, d_model, H, kind, s);
   if (e != hipSuccess) return e;
   if (H <= 16) {
     hipLaunchKernelGGL(gate_dx16_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, dz,

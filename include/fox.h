@@ -140,6 +140,50 @@ fox_status fox_attn_skip_plan(const void* q, const void* k, fox_dtype in_dt, con
                               void* plan, size_t plan_bytes, int64_t B, int64_t H, int64_t L,
                               int64_t D, float scale, void* stream);
 
+/* The Pro block's token shift and output normalisation + gate (paper-graph-ui summary, section
+ * 3.4, "The Pro Block Architecture", Steps 2-3, 5 and 7). The page's equations are missing;
+ * these entry points take the plainest reading of its words:
+ *   shift gate   alpha[b, h, t] = sigmoid(x[b, t, :] . w[h, :])  (one learned vector per head,
+ *                no bias), in (0, 1);
+ *   token shift  y_t = alpha_t x_{t-1} + (1 - alpha_t) x_t  (x_{-1} = 0; alpha weights the
+ *                carried-forward previous candidate), then RMSNorm for keys (normalize = 1),
+ *                none for values;
+ *   output       y = RMSNorm(o) [* weight] * sigmoid(g)  (g = W_g x, the per-dimension output
+ *                gate pre-activation), before the output projection.
+ * The projections W_k x, W_v x, W_g x and W_o are plain GEMMs outside this library.
+ *
+ * fox_shift_gate: x [B, L, d_model] (x_dt FOX_BF16 or FOX_F32), w [H, d_model] fp32 ->
+ *   alpha [B, H, L] fp32; limits as for fox_gate_logf.
+ * fox_shift_gate_bwd: dalpha [B, H, L] fp32 -> dx [B, L, d_model], dw [H, d_model] (fp32);
+ *   workspace of fox_gate_logf_bwd_workspace_bytes(B, L, d_model, H) bytes, 256-byte aligned.
+ *   Deterministic (fixed-order sums).
+ * fox_kv_shift: x, y [BH, L, D] in dt (FOX_BF16 or FOX_F32; y may not alias x); alpha [BH, L]
+ *   fp32; with normalize != 0 the shifted rows are RMS-normalised with eps and weight ([D] fp32,
+ *   or NULL for unit weights). fp32 arithmetic, one rounding on output.
+ * fox_kv_shift_bwd: dy [BH, L, D] fp32, the gradient of fox_kv_shift's output -> dx [BH, L, D]
+ *   fp32 (may not alias dy) and dalpha [BH, L] fp32, with the same x, alpha, normalize, eps
+ *   and weight (the weight is a constant here: no weight gradient).
+ * fox_out_norm_gate: o [rows, D] (o_dt), g [rows, D] (g_dt), weight [D] fp32 or NULL -> y
+ *   [rows, D] in g_dt.
+ * fox_out_norm_gate_bwd: dy [rows, D] fp32 -> d_o and dg [rows, D] fp32 (no weight gradient). */
+fox_status fox_shift_gate(const void* x, fox_dtype x_dt, const float* w, float* alpha, int64_t B,
+                          int64_t L, int64_t d_model, int64_t H, void* stream);
+fox_status fox_shift_gate_bwd(const void* x, fox_dtype x_dt, const float* w, const float* dalpha,
+                              float* dx, float* dw, void* workspace, size_t workspace_bytes,
+                              int64_t B, int64_t L, int64_t d_model, int64_t H, void* stream);
+fox_status fox_kv_shift(const void* x, fox_dtype dt, const float* alpha, void* y, int normalize,
+                        float eps, const float* weight, int64_t BH, int64_t L, int64_t D,
+                        void* stream);
+fox_status fox_kv_shift_bwd(const void* x, fox_dtype dt, const float* alpha, const float* dy,
+                            float* dx, float* dalpha, int normalize, float eps,
+                            const float* weight, int64_t BH, int64_t L, int64_t D, void* stream);
+fox_status fox_out_norm_gate(const void* o, fox_dtype o_dt, const void* g, fox_dtype g_dt,
+                             const float* weight, float eps, void* y, int64_t rows, int64_t D,
+                             void* stream);
+fox_status fox_out_norm_gate_bwd(const void* o, fox_dtype o_dt, const void* g, fox_dtype g_dt,
+                                 const float* weight, float eps, const float* dy, float* d_o,
+                                 float* dg, int64_t rows, int64_t D, void* stream);
+
 /* Forward (paper-graph-ui summary, "Hardware-Aware Implementation", the forward pass;
  * paperlayer.ai summary, section E):
  *   O[i]   = sum_{j<=i} softmax_j(scale * q_i . k_j + c_i - c_j) v_j

@@ -161,6 +161,23 @@ def test_decode_rejects(lib):
     assert app(T=0) == 1
 
 
+@host_only
+def test_pro_shift_and_output_reject(lib):
+    f = ctypes.c_float
+    assert lib.fox_shift_gate(0, 1, P, P, 1, 8, 16, 2, None) == 1
+    assert lib.fox_shift_gate(P, 1, P, P, 1, 8, 12, 2, None) == 1      # d_model % 8
+    assert lib.fox_shift_gate(P, 3, P, P, 1, 8, 16, 2, None) == 1      # dtype
+    assert lib.fox_shift_gate_bwd(P, 1, P, P, P, P, P, 100, 1, 8, 16, 2, None) == 1
+    assert "workspace too small" in lib.fox_last_error().decode()
+    assert lib.fox_kv_shift(P, 1, P, P, 1, f(1e-6), None, 2, 8, 96, None) == 1   # D
+    assert lib.fox_kv_shift(P, 1, P, P, 1, f(-1.0), None, 2, 8, 64, None) == 1   # eps
+    assert lib.fox_kv_shift(P, 1, P, P + 16, 0, f(1e-6), None, 2, 0, 64, None) == 1  # L = 0
+    assert lib.fox_kv_shift(P, 1, P, P, 0, f(1e-6), None, 2, 8, 64, None) == 1   # y aliases x
+    assert lib.fox_kv_shift_bwd(P, 1, P, P, P, P + 16, 1, f(1e-6), None, 2, 8, 64, None) == 1
+    assert lib.fox_out_norm_gate(P, 1, P, 7, None, f(1e-6), P, 4, 128, None) == 1
+    assert lib.fox_out_norm_gate_bwd(P, 1, P, 1, None, f(1e-6), P, P, 0, 4, 128, None) == 1
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         fox.load_library(str(tmp_path / "missing.so"))

@@ -631,3 +631,96 @@ def test_decode_append_after_prefill(fox):
     torch.cuda.synchronize()
     assert host(lens).tolist() == [T] * B
     assert all(torch.equal(a, b) for a, b in zip(before, (kc, vc, c)))
+
+
+# ------------------------------------------------------ Pro block: shift gate, KV-shift, output gate
+@pytest.mark.parametrize("x_dt,dm", [("bf16", 1536), ("f32", 1536), ("bf16", 40)])
+def test_shift_gate_forward_backward(fox, x_dt, dm):
+    """alpha = sigmoid(x . w^T) and its backward (dx, dw), against the oracle; d_model = 1536
+    takes the matrix-core path for bf16, 40 the vector-ALU path."""
+    rng = np.random.default_rng(dm)
+    B, L, H = 2, 300, 12
+    x = rng.standard_normal((B, L, dm)).astype(np.float32)
+    x = fi.bf16_round(x) if x_dt == "bf16" else x
+    w = (0.05 * rng.standard_normal((H, dm))).astype(np.float32)
+    da = rng.standard_normal((B, H, L)).astype(np.float32)
+    say(f"shift gate x={x_dt} d_model={dm}")
+    xt = dev(x, x_dt)
+    alpha = fox.fox_shift_gate(xt, dev(w, "f32"))
+    dx, dw = fox.fox_shift_gate_bwd(xt, dev(w, "f32"), dev(da, "f32"))
+    torch.cuda.synchronize()
+    _check_tight("alpha", host(alpha), oracle.shift_gate(x, w))
+    rdx, rdw = oracle.shift_gate_bwd(x, w, da)
+    _check_tight("dx", host(dx), rdx)
+    _check_tight("dw", host(dw), rdw)
+
+
+@pytest.mark.parametrize("D,dt,normalize,weighted,L", [(128, "bf16", True, False, 16384),
+                                                       (128, "f32", True, True, 77),
+                                                       (64, "bf16", False, False, 300),
+                                                       (64, "f32", True, True, 1),
+                                                       (128, "bf16", False, False, 5)])
+def test_kv_shift_forward_backward(fox, D, dt, normalize, weighted, L):
+    """Token shift (keys: then RMSNorm; values: none) and its backward against the oracle; the
+    first row of each sequence has no predecessor and L = 1 has no successor."""
+    rng = np.random.default_rng(D + L)
+    BH = 12 if L == 16384 else 5
+    x = rng.standard_normal((BH, L, D)).astype(np.float32)
+    x = fi.bf16_round(x) if dt == "bf16" else x
+    a = rng.uniform(0.0, 1.0, size=(BH, L)).astype(np.float32)
+    dy = rng.standard_normal((BH, L, D)).astype(np.float32)
+    wgt = rng.uniform(0.5, 1.5, size=D).astype(np.float32) if weighted else None
+    say(f"kv shift D={D} {dt} norm={normalize} weighted={weighted} L={L}")
+    wt = dev(wgt, "f32") if weighted else None
+    y = fox.fox_kv_shift(dev(x, dt), dev(a, "f32"), normalize=normalize, eps=1e-6, weight=wt)
+    dx, da = fox.fox_kv_shift_bwd(dev(x, dt), dev(a, "f32"), dev(dy, "f32"), normalize=normalize,
+                                  eps=1e-6, weight=wt)
+    torch.cuda.synchronize()
+    v = oracle.kv_shift(x, a)
+    ref = oracle.rms_norm(v, 1e-6, wgt) if normalize else v
+    gv = oracle.rms_norm_bwd(v, dy, 1e-6, wgt)[0] if normalize else dy
+    rdx, rda = oracle.kv_shift_bwd(x, a, gv)
+    if dt == "bf16":
+        check("y", host(y), ref)
+    else:
+        _check_tight("y", host(y), ref)
+    _check_tight("dx", host(dx), rdx)
+    if normalize and L == 1:
+        # every row is a first row: v = (1 - alpha) x, which RMSNorm makes independent of alpha
+        # up to eps, so dalpha = -sum_d g_d x_d nearly cancels (g is orthogonal to x but for eps);
+        # the fp32 result then differs by cancellation noise of a few ulp of the terms'
+        # magnitude sum_d |g_d x_d|, which is the bound here
+        scale = np.sum(np.abs(gv * x), axis=-1)
+        err = np.abs(host(da) - rda)
+        assert np.all(err <= 1e-5 * scale), float(np.max(err / scale))
+    else:
+        _check_tight("dalpha", host(da), rda)
+
+
+@pytest.mark.parametrize("D,o_dt,g_dt,weighted,rows", [(128, "f32", "bf16", False, 196608),
+                                                       (128, "bf16", "f32", True, 37),
+                                                       (64, "f32", "f32", True, 1000),
+                                                       (64, "bf16", "bf16", False, 1)])
+def test_out_norm_gate_forward_backward(fox, D, o_dt, g_dt, weighted, rows):
+    """y = RMSNorm(o) [* w] * sigmoid(g) and its backward (d_o, dg) against the oracle."""
+    rng = np.random.default_rng(D + rows)
+    o = (rng.standard_normal((rows, D)) * rng.uniform(0.1, 3.0, size=(rows, 1))).astype(np.float32)
+    g = (2 * rng.standard_normal((rows, D))).astype(np.float32)
+    o = fi.bf16_round(o) if o_dt == "bf16" else o
+    g = fi.bf16_round(g) if g_dt == "bf16" else g
+    dy = rng.standard_normal((rows, D)).astype(np.float32)
+    wgt = rng.uniform(0.5, 1.5, size=D).astype(np.float32) if weighted else None
+    say(f"out norm gate D={D} o={o_dt} g={g_dt} weighted={weighted} rows={rows}")
+    wt = dev(wgt, "f32") if weighted else None
+    y = fox.fox_out_norm_gate(dev(o, o_dt), dev(g, g_dt), eps=1e-6, weight=wt)
+    d_o, dg = fox.fox_out_norm_gate_bwd(dev(o, o_dt), dev(g, g_dt), dev(dy, "f32"), eps=1e-6,
+                                        weight=wt)
+    torch.cuda.synchronize()
+    ref = oracle.out_norm_gate(o, g, 1e-6, wgt)
+    rdo, rdg = oracle.out_norm_gate_bwd(o, g, 1e-6, dy, wgt)
+    if g_dt == "bf16":
+        check("y", host(y), ref)
+    else:
+        _check_tight("y", host(y), ref)
+    _check_tight("d_o", host(d_o), rdo)
+    _check_tight("dg", host(dg), rdg)
