@@ -367,6 +367,51 @@ def decode_step(args, torch, fi, fox, dev):
     print(json.dumps(out), flush=True)
 
 
+def pro_extra_kernels(torch, fox, x, k, v, stream):
+    """The Pro block's shift gates, token shift (keys with RMSNorm, values without) and output
+    norm + gate, forward and backward, at the workload's shape: each timed alone, 20 calls,
+    with its algorithmic HBM bytes (every input read once, every output written once)."""
+    B, L, dm = x.shape
+    H, D = k.shape[1], k.shape[3]
+    rng = torch.Generator(device=x.device).manual_seed(46)
+    w_k = 0.02 * torch.randn(H, dm, device=x.device, generator=rng)
+    alpha = fox.fox_shift_gate(x, w_k)
+    g = torch.randn(B, H, L, D, device=x.device, generator=rng).to(torch.bfloat16)
+    dy = torch.randn(B, H, L, D, device=x.device, generator=rng)
+    dal = torch.randn(B, H, L, device=x.device, generator=rng)
+    o_prev = torch.randn(B, H, L, D, device=x.device, generator=rng)  # an fp32 attention output
+    n_row, n_tok = B * H * L * D, B * L
+    cases = {
+        "shift_gate": (lambda: fox.fox_shift_gate(x, w_k), n_tok * dm * 2 + B * H * L * 4),
+        "shift_gate_bwd": (lambda: fox.fox_shift_gate_bwd(x, w_k, dal),
+                           n_tok * dm * (2 + 4) + B * H * L * 4),
+        "k_shift_norm": (lambda: fox.fox_kv_shift(k, alpha, normalize=True),
+                         n_row * (2 + 2) + B * H * L * 4),
+        "v_shift": (lambda: fox.fox_kv_shift(v, alpha), n_row * (2 + 2) + B * H * L * 4),
+        "k_shift_norm_bwd": (lambda: fox.fox_kv_shift_bwd(k, alpha, dy, normalize=True),
+                             n_row * (2 + 4 + 4) + B * H * L * 8),
+        "out_norm_gate": (lambda: fox.fox_out_norm_gate(o_prev, g), n_row * (4 + 2 + 2)),
+        "out_norm_gate_bwd": (lambda: fox.fox_out_norm_gate_bwd(o_prev, g, dy),
+                              n_row * (4 + 2 + 4 + 4 + 4)),
+    }
+    res = {}
+    for name, (fn, nbytes) in cases.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        res[name] = {"ms": round(ms, 4), "bytes": int(nbytes),
+                     "GB_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_8TBps": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+    return res
+
+
 def pro_step(args, torch, fi, fox, dev):
     """One training step of the Pro block's attention path (workload 4 plus a seeded dO)."""
     case = fi.config_case(4)
@@ -450,6 +495,7 @@ def pro_step(args, torch, fi, fox, dev):
         "kernel_ms": {n: round(kern_ms[n], 4) for n in names},
         "host_wall_ms_per_step": round(wall_ms, 4),
     }
+    out["pro_shift_output_kernels"] = pro_extra_kernels(torch, fox, x, k, v, stream)
     if not args.no_skip:  # the same step with exact tile skipping, a separate measurement
         ref = step(None)
         got = step(None, skip=True)
