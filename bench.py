@@ -346,6 +346,25 @@ def decode_step(args, torch, fi, fox, dev):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None},
     }
+    if not args.no_skip:  # the same decode with the cache's key norms (exact chunk skipping)
+        kn = fox.fox_attn_decode_key_norms(k, lens)
+        o0, l0 = fox.fox_attn_decode(q, k, v, c, lens, workspace=ws)
+        o1, l1 = fox.fox_attn_decode(q, k, v, c, lens, workspace=ws, k_norms=kn)
+        torch.cuda.synchronize()
+        identical = torch.equal(o0, o1) and torch.equal(l0, l1)
+        for _ in range(3):
+            fox.fox_attn_decode(q, k, v, c, lens, workspace=ws, k_norms=kn)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fox.fox_attn_decode(q, k, v, c, lens, workspace=ws, k_norms=kn)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_s = e0.elapsed_time(e1) / steps
+        out["skip_decayed"] = {"ms_per_step": round(ms_s, 4),
+                               "effective_GB_per_s": round(nbytes / (ms_s * 1e-3) / 1e9, 1),
+                               "speedup_vs_dense": round(ms / ms_s, 3),
+                               "bit_identical_to_dense": bool(identical)}
     if not args.no_cpu_baseline:
         import oracle
         t0 = time.perf_counter()

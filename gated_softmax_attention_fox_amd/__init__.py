@@ -37,6 +37,7 @@ __all__ = [
     "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_bwd",
     "fox_attn_skip_plan_bytes", "fox_attn_skip_plan", "skip_plan_arrays",
     "fox_attn_decode_workspace_bytes", "fox_attn_decode", "fox_attn_decode_append",
+    "fox_attn_decode_key_norms",
     "fox_shift_gate", "fox_shift_gate_bwd", "fox_kv_shift", "fox_kv_shift_bwd", "fox_out_norm_gate",
     "fox_out_norm_gate_bwd",
     "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
@@ -99,10 +100,12 @@ _SIGS = {
                                              _c_f32, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_attn_decode_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "fox_attn_decode": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
-                                       ctypes.c_int, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64, _c_i64,
-                                       _c_i64, _c_f32, _c_u32, _c_vp]),
+                                       _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64,
+                                       _c_i64, _c_i64, _c_f32, _c_u32, _c_vp]),
+    "fox_attn_decode_key_norms": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64,
+                                                 _c_i64, _c_i64, _c_i64, _c_vp]),
     "fox_attn_decode_append": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
-                                              _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                              _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                               _c_vp]),
     "fox_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "fox_last_error": (ctypes.c_char_p, []),
@@ -457,11 +460,14 @@ def fox_attn_decode_workspace_bytes(B: int, H: int, T_max: int, D: int) -> int:
 
 
 def fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype: torch.dtype = torch.float32,
-                    scale: float | None = None, workspace=None):
+                    scale: float | None = None, workspace=None,
+                    k_norms: torch.Tensor | None = None):
     """(o [B, H, D], lse [B, H]) of the newest position of each sequence against the cache.
 
     q: [B, H, D] bf16; k_cache, v_cache: [B, H, T_max, D] bf16; c_cache: [B, H, T_max] fp32;
-    lens: [B] int32 device tensor of cached lengths (the query sits at lens[b] - 1)."""
+    lens: [B] int32 device tensor of cached lengths (the query sits at lens[b] - 1).
+    k_norms: fox_attn_decode_key_norms(...) kept current by the appends, or None; with it the
+    chunks whose weights all underflow are not read (bit-identical results)."""
     lib = load_library()
     if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("k_cache and v_cache must share one shape [B, H, T_max, D]")
@@ -481,15 +487,30 @@ def fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype: torch.dtype = t
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", (torch.uint8,))
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib.fox_attn_decode(pq, pk, pv, FOX_BF16, pc, pl, ctypes.c_void_p(o.data_ptr()),
+    pn = ctypes.c_void_p(0) if k_norms is None else _dev(k_norms, "k_norms", (torch.float32,), 3)
+    _check(lib.fox_attn_decode(pq, pk, pv, FOX_BF16, pc, pl, pn, ctypes.c_void_p(o.data_ptr()),
                                _code(o_dtype), ctypes.c_void_p(lse.data_ptr()), pw,
                                workspace.numel(), B, H, T, D, scale, FOX_CAUSAL, _stream(q)),
            "fox_attn_decode")
     return o, lse
 
 
-def fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, lens):
-    """Append one position per sequence to the cache in place (k, v, c), then lens += 1."""
+def fox_attn_decode_key_norms(k_cache: torch.Tensor, lens: torch.Tensor) -> torch.Tensor:
+    """The largest key norm of every 64 cached positions: [B, H, ceil(T_max / 64)] fp32."""
+    lib = load_library()
+    B, H, T, D = k_cache.shape
+    kn = torch.empty((B, H, -(-T // 64)), dtype=torch.float32, device=k_cache.device)
+    _check(lib.fox_attn_decode_key_norms(_dev(k_cache, "k_cache", (torch.bfloat16,), 4), FOX_BF16,
+                                         _dev(lens, "lens", (torch.int32,), 1),
+                                         ctypes.c_void_p(kn.data_ptr()), B, H, T, D,
+                                         _stream(k_cache)), "fox_attn_decode_key_norms")
+    return kn
+
+
+def fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, lens,
+                           k_norms: torch.Tensor | None = None):
+    """Append one position per sequence to the cache in place (k, v, c and, when given, the key
+    norms), then lens += 1."""
     lib = load_library()
     B, H, T, D = k_cache.shape
     if tuple(k_new.shape) != (B, H, D) or k_new.shape != v_new.shape:
@@ -500,7 +521,9 @@ def fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, l
             FOX_BF16, _dev(log_f_new, "log_f_new", (torch.float32,), 2),
             _dev(k_cache, "k_cache", (torch.bfloat16,), 4),
             _dev(v_cache, "v_cache", (torch.bfloat16,), 4),
-            _dev(c_cache, "c_cache", (torch.float32,), 3), _dev(lens, "lens", (torch.int32,), 1))
+            _dev(c_cache, "c_cache", (torch.float32,), 3),
+            ctypes.c_void_p(0) if k_norms is None else _dev(k_norms, "k_norms", (torch.float32,), 3),
+            _dev(lens, "lens", (torch.int32,), 1))
     _check(lib.fox_attn_decode_append(*args, B, H, T, D, _stream(k_cache)),
            "fox_attn_decode_append")
 

@@ -489,10 +489,10 @@ size_t fox_attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t T_max, int6
 }
 
 fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                           fox_dtype in_dt, const float* c_cache, const int32_t* lens, void* o,
-                           fox_dtype o_dt, float* lse, void* workspace, size_t workspace_bytes,
-                           int64_t B, int64_t H, int64_t T_max, int64_t D, float scale,
-                           uint32_t flags, void* stream) {
+                           fox_dtype in_dt, const float* c_cache, const int32_t* lens,
+                           const float* k_norms, void* o, fox_dtype o_dt, float* lse,
+                           void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t T_max, int64_t D, float scale, uint32_t flags, void* stream) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k_cache);
   FOX_REQUIRE_PTR(v_cache);
@@ -500,6 +500,7 @@ fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cac
   FOX_REQUIRE_PTR(lens);
   FOX_REQUIRE_PTR(o);
   if (lse) FOX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+  if (k_norms) FOX_REQUIRE(aligned16(k_norms), "k_norms must be 16-byte aligned");
   FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL");
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
               "workspace must be 256-byte aligned");
@@ -516,15 +517,32 @@ fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cac
   const size_t need = fox::decode_workspace_bytes(B * H, T_max, D);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
-  return launched(fox::launch_decode(q, k_cache, v_cache, c_cache, lens, o, o_dt == FOX_F32, lse,
-                                     workspace, B, H, T_max, D, scale, (hipStream_t)stream),
+  return launched(fox::launch_decode(q, k_cache, v_cache, c_cache, lens, k_norms, o,
+                                     o_dt == FOX_F32, lse, workspace, B, H, T_max, D, scale,
+                                     (hipStream_t)stream),
                   "fox_attn_decode");
+}
+
+fox_status fox_attn_decode_key_norms(const void* k_cache, fox_dtype in_dt, const int32_t* lens,
+                                     float* k_norms, int64_t B, int64_t H, int64_t T_max,
+                                     int64_t D, void* stream) {
+  FOX_REQUIRE_PTR(k_cache);
+  FOX_REQUIRE_PTR(lens);
+  FOX_REQUIRE_PTR(k_norms);
+  fox_status st = check_bhld(B, H, T_max, D);
+  if (st != FOX_OK) return st;
+  if (in_dt != FOX_BF16)
+    return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
+                "the decode cache is bf16 (in_dt = FOX_BF16)");
+  return launched(fox::launch_decode_key_norms(k_cache, lens, k_norms, B, H, T_max, D,
+                                               (hipStream_t)stream),
+                  "fox_attn_decode_key_norms");
 }
 
 fox_status fox_attn_decode_append(const void* k_new, const void* v_new, fox_dtype in_dt,
                                   const float* log_f_new, void* k_cache, void* v_cache,
-                                  float* c_cache, int32_t* lens, int64_t B, int64_t H,
-                                  int64_t T_max, int64_t D, void* stream) {
+                                  float* c_cache, float* k_norms, int32_t* lens, int64_t B,
+                                  int64_t H, int64_t T_max, int64_t D, void* stream) {
   FOX_REQUIRE_PTR(k_new);
   FOX_REQUIRE_PTR(v_new);
   FOX_REQUIRE_PTR(log_f_new);
@@ -532,13 +550,14 @@ fox_status fox_attn_decode_append(const void* k_new, const void* v_new, fox_dtyp
   FOX_REQUIRE_PTR(v_cache);
   FOX_REQUIRE_PTR(c_cache);
   FOX_REQUIRE_PTR(lens);
+  if (k_norms) FOX_REQUIRE(aligned16(k_norms), "k_norms must be 16-byte aligned");
   fox_status st = check_bhld(B, H, T_max, D);
   if (st != FOX_OK) return st;
   if (in_dt != FOX_BF16)
     return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
                 "the decode cache is bf16 (in_dt = FOX_BF16)");
   return launched(fox::launch_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache,
-                                            lens, B, H, T_max, D, (hipStream_t)stream),
+                                            k_norms, lens, B, H, T_max, D, (hipStream_t)stream),
                   "fox_attn_decode_append");
 }
 

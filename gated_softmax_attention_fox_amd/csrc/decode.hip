@@ -13,6 +13,13 @@
 // with an online softmax, double-buffering its K and V rows in registers (decode_partial_kernel).
 // The chunk writes (o, m, l) to the workspace; a second kernel combines the chunks of each
 // (b, h) (m = max over chunks, l and o rescaled by exp2(m_c - m)) and normalises.
+//
+// Exact skipping (optional). With the largest key norm of every 64 cached positions at hand
+// (kept beside the cache), a chunk whose every weight is provably below 2^-160 of the query's
+// own-key weight is not read: for a key j of the chunk, scale q_t.(k_j - k_t) - (c_j - c_t)
+// <= scale |q_t| (|k_j| + |k_t|) - (c_end - c_t), c_end the chunk's last c (c does not
+// increase). The combine would scale such a chunk by exp2(m_c - m) with m at least the
+// own-key logit, which is exactly 0 in fp32, so skipping it changes no bit of the result.
 #include "fox_device.h"
 #include "fox_launch.h"
 
@@ -38,11 +45,11 @@ int decode_chunk(int64_t BH, int64_t T, int64_t D) {
 // m, sum l, weighted values acc), reading the next step's K and V rows into a second register
 // buffer while it computes on the current one. D / 8 lanes share a row, so each load
 // instruction reads whole rows (1 KiB contiguous). The waves are combined once at the end.
-template <int D>
+template <int D, bool kSkip>
 __global__ __launch_bounds__(256) void decode_partial_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const float* __restrict__ C, const int32_t* __restrict__ lens, float* __restrict__ part,
-    int H, int T, int n_ch, int chunk, float sl2e) {
+    const float* __restrict__ C, const int32_t* __restrict__ lens, const float* __restrict__ KN,
+    float* __restrict__ part, int H, int T, int n_ch, int chunk, float sl2e) {
   constexpr int CPR = D / 8;          // lanes per row (16 bytes each)
   constexpr int RPI = 64 / CPR;       // rows per load instruction
   constexpr int IT = kDecRows;        // load instructions per tensor and step
@@ -66,6 +73,31 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   const float* Cb = C + rows;
   const float ct = Cb[t];
   const bf16x8 qv = ld8(Q + (size_t)bh * D + col);
+  float* out = part + ((size_t)bh * n_ch + ch) * (D + 2);
+
+  // A separate instantiation: the bound's code in the dense kernel measured 9% slower even
+  // when not taken.
+  if constexpr (kSkip) {  // the bound of this chunk; every thread evaluates the same values
+    const int n64 = (T + 63) / 64;
+    const float* kn = KN + (size_t)bh * n64;
+    float qq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qq = fmaf((float)qv[e], (float)qv[e], qq);
+#pragma unroll
+    for (int mk = 1; mk < CPR; mk <<= 1) qq += __shfl_xor(qq, mk, 64);
+    const int g0 = j0 / 64, g1 = (min(j0 + chunk, len) - 1) / 64;
+    float km = 0.f;
+    for (int g = g0 + lane; g <= g1; g += 64) km = fmaxf(km, kn[g]);
+#pragma unroll
+    for (int mk = 1; mk < 64; mk <<= 1) km = fmaxf(km, __shfl_xor(km, mk, 64));
+    const float ce = Cb[min(j0 + chunk, len) - 1];
+    const float slack = 1e-6f * (fabsf(ce) + fabsf(ct)) + 1.f;
+    const float bound = sl2e * sqrtf(qq) * 1.00001f * (km + kn[t / 64]) + (slack - (ce - ct)) * kLog2e;
+    if (bound < -160.f) {  // nothing in this chunk can carry weight: an empty partial
+      for (int d = threadIdx.x; d < D + 2; d += 256) out[d] = d == D ? -INFINITY : 0.f;
+      return;
+    }
+  }
 
   auto load = [&](bf16x8 (&kr)[IT], bf16x8 (&vr)[IT], int step) __attribute__((always_inline)) {
 #pragma unroll
@@ -145,7 +177,6 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
   float mt = red[0][D];
 #pragma unroll
   for (int w = 1; w < kDecWaves; ++w) mt = fmaxf(mt, red[w][D]);  // wave 0 is never empty
-  float* out = part + ((size_t)bh * n_ch + ch) * (D + 2);
   for (int d = threadIdx.x; d < D + 2; d += 256) {
     if (d == D) {
       out[d] = mt;
@@ -180,7 +211,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
 #pragma unroll 8
   for (int c = 0; c < n; ++c) {
     const float* pc = p + (size_t)c * (D + 2);
-    const float a = __builtin_amdgcn_exp2f(pc[D] - mt);
+    const float a = __builtin_amdgcn_exp2f(pc[D] - mt);  // 0 for a skipped chunk (m = -inf)
     l = fmaf(a, pc[D + 1], l);
     o = fmaf(a, pc[d], o);
   }
@@ -198,18 +229,64 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_append_kernel(
     const bf16_t* __restrict__ k_new, const bf16_t* __restrict__ v_new,
     const float* __restrict__ logf_new, bf16_t* __restrict__ K, bf16_t* __restrict__ V,
-    float* __restrict__ C, const int32_t* __restrict__ lens, int H, int T) {
+    float* __restrict__ C, float* __restrict__ KN, const int32_t* __restrict__ lens, int H,
+    int T) {
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int pos = lens[bh / H];
-  if (pos < 0 || pos >= T) return;  // a full cache is left unchanged
+  if (pos < 0 || pos >= T) return;  // a full cache is left unchanged (uniform: one wave)
   const size_t row = (size_t)bh * T + pos;
+  float ss = 0.f;
   if (tid < D / 8) {
-    *reinterpret_cast<uint4*>(K + row * D + tid * 8) =
-        *reinterpret_cast<const uint4*>(k_new + (size_t)bh * D + tid * 8);
+    const uint4 kw = *reinterpret_cast<const uint4*>(k_new + (size_t)bh * D + tid * 8);
+    *reinterpret_cast<uint4*>(K + row * D + tid * 8) = kw;
     *reinterpret_cast<uint4*>(V + row * D + tid * 8) =
         *reinterpret_cast<const uint4*>(v_new + (size_t)bh * D + tid * 8);
+    const bf16x8 kv = __builtin_bit_cast(bf16x8, kw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf((float)kv[e], (float)kv[e], ss);
   }
-  if (tid == 0) C[row] = (pos > 0 ? C[row - 1] : 0.f) + logf_new[bh];
+#pragma unroll
+  for (int mk = 1; mk < 64; mk <<= 1) ss += __shfl_xor(ss, mk, 64);
+  if (tid == 0) {
+    C[row] = (pos > 0 ? C[row - 1] : 0.f) + logf_new[bh];
+    if (KN) {  // the group's largest key norm, restarted at a group's first position
+      float* kn = KN + (size_t)bh * ((T + 63) / 64) + pos / 64;
+      const float nk = sqrtf(ss) * 1.00001f;
+      *kn = pos % 64 == 0 ? nk : fmaxf(*kn, nk);
+    }
+  }
+}
+
+// Largest key norm of every 64 cached positions (positions at or past the length count as 0).
+template <int D>
+__global__ __launch_bounds__(256) void decode_key_norms_kernel(const bf16_t* __restrict__ K,
+                                                               const int32_t* __restrict__ lens,
+                                                               float* __restrict__ KN, int H,
+                                                               int T) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int lane = threadIdx.x & 63;
+  const int n64 = (T + 63) / 64;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int bh = blockIdx.y;
+  if (g >= n64) return;  // a whole wave; the kernel has no barrier
+  const int len = min(lens[bh / H], T);
+  const bf16_t* Kb = K + (size_t)bh * T * D;
+  float mx = 0.f;
+  for (int it = 0; it < 64 / RPI; ++it) {
+    const int row = g * 64 + it * RPI + lane / CPR;
+    float ss = 0.f;
+    if (row < len) {
+      const bf16x8 v = ld8(Kb + (size_t)row * D + (lane % CPR) * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)v[e], (float)v[e], ss);
+    }
+#pragma unroll
+    for (int mk = 1; mk < CPR; mk <<= 1) ss += __shfl_xor(ss, mk, 64);
+    mx = fmaxf(mx, sqrtf(ss));
+  }
+#pragma unroll
+  for (int mk = CPR; mk < 64; mk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, mk, 64));
+  if (lane == 0) KN[(size_t)bh * n64 + g] = mx * 1.00001f;  // rounded up
 }
 
 __global__ void decode_advance_kernel(int32_t* __restrict__ lens, int B, int T) {
@@ -226,39 +303,63 @@ size_t decode_workspace_bytes(int64_t BH, int64_t T, int64_t D) {
 }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* c,
-                         const int32_t* lens, void* o, bool o_f32, float* lse, void* ws,
-                         int64_t B, int64_t H, int64_t T, int64_t D, float scale, hipStream_t s) {
+                         const int32_t* lens, const float* k_norms, void* o, bool o_f32,
+                         float* lse, void* ws, int64_t B, int64_t H, int64_t T, int64_t D,
+                         float scale, hipStream_t s) {
   const int chunk = decode_chunk(B * H, T, D);
   const int n_ch = (int)((T + chunk - 1) / chunk);
   const dim3 g1((unsigned)n_ch, (unsigned)(B * H));
   float* part = static_cast<float*>(ws);
   if (D == 64) {
-    hipLaunchKernelGGL(decode_partial_kernel<64>, g1, dim3(256), 0, s, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, c, lens, part, (int)H, (int)T, n_ch,
-                       chunk, scale * kLog2e);
+    if (k_norms)
+      hipLaunchKernelGGL((decode_partial_kernel<64, true>), g1, dim3(256), 0, s, (const bf16_t*)q,
+                         (const bf16_t*)k, (const bf16_t*)v, c, lens, k_norms, part, (int)H,
+                         (int)T, n_ch, chunk, scale * kLog2e);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<64, false>), g1, dim3(256), 0, s, (const bf16_t*)q,
+                         (const bf16_t*)k, (const bf16_t*)v, c, lens, k_norms, part, (int)H,
+                         (int)T, n_ch, chunk, scale * kLog2e);
     hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)(B * H)), dim3(64), 0, s, part,
                        lens, o, (int)o_f32, lse, (int)H, (int)T, n_ch, chunk);
   } else {
-    hipLaunchKernelGGL(decode_partial_kernel<128>, g1, dim3(256), 0, s, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, c, lens, part, (int)H, (int)T, n_ch,
-                       chunk, scale * kLog2e);
+    if (k_norms)
+      hipLaunchKernelGGL((decode_partial_kernel<128, true>), g1, dim3(256), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lens, k_norms,
+                         part, (int)H, (int)T, n_ch, chunk, scale * kLog2e);
+    else
+      hipLaunchKernelGGL((decode_partial_kernel<128, false>), g1, dim3(256), 0, s,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lens, k_norms,
+                         part, (int)H, (int)T, n_ch, chunk, scale * kLog2e);
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)(B * H)), dim3(128), 0, s,
                        part, lens, o, (int)o_f32, lse, (int)H, (int)T, n_ch, chunk);
   }
   return hipGetLastError();
 }
 
+hipError_t launch_decode_key_norms(const void* k, const int32_t* lens, float* k_norms, int64_t B,
+                                   int64_t H, int64_t T, int64_t D, hipStream_t s) {
+  const int n64 = (int)((T + 63) / 64);
+  const dim3 grid((unsigned)((n64 + 3) / 4), (unsigned)(B * H));
+  if (D == 64)
+    hipLaunchKernelGGL(decode_key_norms_kernel<64>, grid, dim3(256), 0, s, (const bf16_t*)k, lens,
+                       k_norms, (int)H, (int)T);
+  else
+    hipLaunchKernelGGL(decode_key_norms_kernel<128>, grid, dim3(256), 0, s, (const bf16_t*)k,
+                       lens, k_norms, (int)H, (int)T);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_append(const void* k_new, const void* v_new, const float* logf_new,
-                                void* k, void* v, float* c, int32_t* lens, int64_t B, int64_t H,
-                                int64_t T, int64_t D, hipStream_t s) {
+                                void* k, void* v, float* c, float* k_norms, int32_t* lens,
+                                int64_t B, int64_t H, int64_t T, int64_t D, hipStream_t s) {
   if (D == 64)
     hipLaunchKernelGGL(decode_append_kernel<64>, dim3((unsigned)(B * H)), dim3(64), 0, s,
                        (const bf16_t*)k_new, (const bf16_t*)v_new, logf_new, (bf16_t*)k,
-                       (bf16_t*)v, c, lens, (int)H, (int)T);
+                       (bf16_t*)v, c, k_norms, lens, (int)H, (int)T);
   else
     hipLaunchKernelGGL(decode_append_kernel<128>, dim3((unsigned)(B * H)), dim3(64), 0, s,
                        (const bf16_t*)k_new, (const bf16_t*)v_new, logf_new, (bf16_t*)k,
-                       (bf16_t*)v, c, lens, (int)H, (int)T);
+                       (bf16_t*)v, c, k_norms, lens, (int)H, (int)T);
   hipLaunchKernelGGL(decode_advance_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
                      lens, (int)B, (int)T);
   return hipGetLastError();

@@ -96,14 +96,20 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          float scale, const SkipArgs& skip, hipStream_t s);
 // Single-token decode against a KV cache [BH, T, D] (bf16) with c [BH, T] and per-sequence
 // lengths lens [B]: o [BH, D] (bf16 or fp32) and lse [BH]; workspace decode_workspace_bytes.
+// k_norms [BH, ceil(T / 64)] (largest key norm per 64 positions) or null: with it, chunks
+// whose weights all underflow are not read.
 size_t decode_workspace_bytes(int64_t BH, int64_t T, int64_t D);
 hipError_t launch_decode(const void* q, const void* k, const void* v, const float* c,
-                         const int32_t* lens, void* o, bool o_f32, float* lse, void* ws,
-                         int64_t B, int64_t H, int64_t T, int64_t D, float scale, hipStream_t s);
-// Append one position per sequence at lens[b] (k, v, and c = c_prev + log f), then lens += 1.
+                         const int32_t* lens, const float* k_norms, void* o, bool o_f32,
+                         float* lse, void* ws, int64_t B, int64_t H, int64_t T, int64_t D,
+                         float scale, hipStream_t s);
+hipError_t launch_decode_key_norms(const void* k, const int32_t* lens, float* k_norms, int64_t B,
+                                   int64_t H, int64_t T, int64_t D, hipStream_t s);
+// Append one position per sequence at lens[b] (k, v, c = c_prev + log f and, when k_norms is not
+// null, the group's key norm), then lens += 1.
 hipError_t launch_decode_append(const void* k_new, const void* v_new, const float* logf_new,
-                                void* k, void* v, float* c, int32_t* lens, int64_t B, int64_t H,
-                                int64_t T, int64_t D, hipStream_t s);
+                                void* k, void* v, float* c, float* k_norms, int32_t* lens,
+                                int64_t B, int64_t H, int64_t T, int64_t D, hipStream_t s);
 // Backward, bf16 inputs, fp32 O / gradients: the four steps in order (plan: a skip plan or
 // null).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,

@@ -269,6 +269,13 @@ fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f
  *             (1 <= lens[b] <= T_max; the query sits at position lens[b] - 1, whose key and
  *             value must already be in the cache). A length above T_max is read as T_max; a
  *             sequence with lens[b] < 1 gets zeros and lse = -inf.
+ *   k_norms : [B, H, ceil(T_max / 64)] fp32, the largest key norm of every 64 cached positions
+ *             (fox_attn_decode_key_norms, kept current by fox_attn_decode_append), or NULL.
+ *             With it, chunks of the cache whose every weight is provably below 2^-160 of the
+ *             query's own-key weight (scale q.(k_j - k_t) - (c_j - c_t) <= scale |q| (|k_j| +
+ *             |k_t|) - (c_end - c_t)) are not read; the result is bit-identical, since such a
+ *             chunk would enter the combination scaled by exactly 0 in fp32. A stale k_norms
+ *             gives wrong results.
  *   o       : [B, H, D] in o_dt (FOX_BF16 or FOX_F32);  lse : [B, H] fp32 or NULL
  *   workspace : at least fox_attn_decode_workspace_bytes(B, H, T_max, D) bytes, 256-byte
  *             aligned, contents ignored and clobbered.
@@ -276,19 +283,27 @@ fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f
  * FOX_CAUSAL. Reads every cached key and value once (bound by HBM). */
 size_t fox_attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t T_max, int64_t D);
 fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                           fox_dtype in_dt, const float* c_cache, const int32_t* lens, void* o,
-                           fox_dtype o_dt, float* lse, void* workspace, size_t workspace_bytes,
-                           int64_t B, int64_t H, int64_t T_max, int64_t D, float scale,
-                           uint32_t flags, void* stream);
+                           fox_dtype in_dt, const float* c_cache, const int32_t* lens,
+                           const float* k_norms, void* o, fox_dtype o_dt, float* lse,
+                           void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                           int64_t T_max, int64_t D, float scale, uint32_t flags, void* stream);
+
+/* The largest key norm of every 64 positions of a bf16 cache (positions at or past lens[b]
+ * count as 0), rounded up: k_norms [B, H, ceil(T_max / 64)] fp32. Call it after filling a cache
+ * by other means (a prefill); fox_attn_decode_append keeps it current afterwards. */
+fox_status fox_attn_decode_key_norms(const void* k_cache, fox_dtype in_dt, const int32_t* lens,
+                                     float* k_norms, int64_t B, int64_t H, int64_t T_max,
+                                     int64_t D, void* stream);
 
 /* Append one position to every sequence of the cache: at index p = lens[b], copy k_new and
  * v_new ([B, H, D] bf16) and set c_cache[b, h, p] = c_cache[b, h, p - 1] + log_f_new[b, h]
- * (log_f_new : [B, H] fp32; c starts at log f for p = 0), then lens[b] += 1, all on the device.
- * A sequence with lens[b] >= T_max (a full cache) is left unchanged, lens included. */
+ * (log_f_new : [B, H] fp32; c starts at log f for p = 0), updates k_norms (or NULL) for the
+ * group of p, then lens[b] += 1, all on the device. A sequence with lens[b] >= T_max (a full
+ * cache) is left unchanged, lens included. */
 fox_status fox_attn_decode_append(const void* k_new, const void* v_new, fox_dtype in_dt,
                                   const float* log_f_new, void* k_cache, void* v_cache,
-                                  float* c_cache, int32_t* lens, int64_t B, int64_t H,
-                                  int64_t T_max, int64_t D, void* stream);
+                                  float* c_cache, float* k_norms, int32_t* lens, int64_t B,
+                                  int64_t H, int64_t T_max, int64_t D, void* stream);
 
 /* Static description of a status code. */
 const char* fox_status_str(fox_status s);

@@ -138,8 +138,8 @@ def test_decode_workspace_size(lib):
 @host_only
 def test_decode_rejects(lib):
     def dec(q=P, lens=P, o=P, in_dt=1, o_dt=1, ws=P, ws_bytes=1 << 30, T=64, D=128, flags=1):
-        return lib.fox_attn_decode(q, P, P, in_dt, P, lens, o, o_dt, None, ws, ws_bytes, 2, 3, T,
-                                   D, 0.1, flags, None)
+        return lib.fox_attn_decode(q, P, P, in_dt, P, lens, None, o, o_dt, None, ws, ws_bytes, 2,
+                                   3, T, D, 0.1, flags, None)
     assert dec(q=0) == 1
     assert dec(lens=0) == 1
     assert dec(o=P + 8) == 1
@@ -153,12 +153,16 @@ def test_decode_rejects(lib):
     assert dec(flags=0) == 2
 
     def app(k_new=P, lens=P, in_dt=1, T=64, D=128):
-        return lib.fox_attn_decode_append(k_new, P, in_dt, P, P, P, P, lens, 2, 3, T, D, None)
+        return lib.fox_attn_decode_append(k_new, P, in_dt, P, P, P, P, None, lens, 2, 3, T, D,
+                                          None)
     assert app(k_new=0) == 1
     assert app(lens=P + 4) == 1
     assert app(in_dt=0) == 2
     assert app(D=32) == 1
     assert app(T=0) == 1
+    assert lib.fox_attn_decode_key_norms(P, 1, 0, P, 2, 3, 64, 128, None) == 1   # lens NULL
+    assert lib.fox_attn_decode_key_norms(P, 0, P, P, 2, 3, 64, 128, None) == 2   # fp32 cache
+    assert lib.fox_attn_decode_key_norms(P, 1, P, P + 8, 2, 3, 64, 128, None) == 1
 
 
 @host_only

@@ -724,3 +724,56 @@ def test_out_norm_gate_forward_backward(fox, D, o_dt, g_dt, weighted, rows):
         _check_tight("y", host(y), ref)
     _check_tight("d_o", host(d_o), rdo)
     _check_tight("dg", host(dg), rdg)
+
+
+@pytest.mark.parametrize("D,gate_mean,T", [(128, 0.0, 3000), (64, 1.0, 2000), (128, 4.0, 16384)])
+def test_decode_skip_is_exact(fox, D, gate_mean, T):
+    """With the cache's key norms, decode skips chunks whose weights all underflow: outputs and
+    LSE are bit-identical to the dense decode. The norms match the oracle's group maxima."""
+    B, H = 3, 4
+    lens = np.array([T, T // 3, 1], np.int32)
+    case = fi.make_case(B, H, T, D, "bf16", seed=T + D, gate="normal", gate_mean=gate_mean)
+    q = fi.bf16_round(np.random.default_rng(T).standard_normal((B, H, D), dtype=np.float32))
+    say(f"decode skip D={D} gate_mean={gate_mean} T={T}")
+    kc, vc = dev(case.k, "bf16"), dev(case.v, "bf16")
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    lt = torch.from_numpy(lens).cuda()
+    kn = fox.fox_attn_decode_key_norms(kc, lt)
+    o0, l0 = fox.fox_attn_decode(dev(q, "bf16"), kc, vc, c, lt)
+    o1, l1 = fox.fox_attn_decode(dev(q, "bf16"), kc, vc, c, lt, k_norms=kn)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    got = host(kn)
+    for b in range(B):
+        kk = case.k[b].copy()
+        kk[:, lens[b]:] = 0.0
+        ref = fox_oracle._group_max_norms(kk, 64)
+        assert np.all(got[b] >= ref * (1 - 1e-6)) and np.all(got[b] <= ref * (1 + 1e-4) + 1e-30)
+
+
+def test_decode_append_keeps_key_norms(fox):
+    """Appends that update the key norms leave them equal (to rounding) to norms recomputed from
+    the cache, and decode with them stays bit-identical to the dense decode."""
+    B, H, T, D, L0, N = 2, 3, 400, 128, 250, 70
+    case = fi.make_case(B, H, T, D, "bf16", seed=71, gate="normal", gate_mean=0.5)
+    rng = np.random.default_rng(72)
+    qs = fi.bf16_round(rng.standard_normal((N, B, H, D), dtype=np.float32))
+    say("decode append with key norms")
+    kc, vc = dev(case.k, "bf16"), dev(case.v, "bf16")
+    c = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    c[:, :, :L0] = fox.fox_logf_cumsum(dev(np.ascontiguousarray(case.log_f[:, :, :L0]), "f32"))
+    lens = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    kn = fox.fox_attn_decode_key_norms(kc, lens)
+    for n in range(N):
+        p = L0 + n
+        fox.fox_attn_decode_append(dev(np.ascontiguousarray(case.k[:, :, p]), "bf16"),
+                                   dev(np.ascontiguousarray(case.v[:, :, p]), "bf16"),
+                                   dev(np.ascontiguousarray(case.log_f[:, :, p]), "f32"),
+                                   kc, vc, c, lens, k_norms=kn)
+        o0, l0 = fox.fox_attn_decode(dev(qs[n], "bf16"), kc, vc, c, lens)
+        o1, l1 = fox.fox_attn_decode(dev(qs[n], "bf16"), kc, vc, c, lens, k_norms=kn)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), n
+    fresh = fox.fox_attn_decode_key_norms(kc, lens)
+    torch.cuda.synchronize()
+    assert np.allclose(host(kn), host(fresh), rtol=1e-6, atol=0)
