@@ -53,13 +53,26 @@ def test_scan_matches_oracle(fox, n):
     assert np.all(np.abs(c - ref) <= ulp + 1e-30), float(np.max(np.abs(c - ref) / ulp))
 
 
-@pytest.mark.parametrize("L", [1, 2, 255, 256, 257, 5000])
+@pytest.mark.parametrize("L", [1, 2, 255, 256, 257, 5000, 16385, 40000])
 def test_scan_ragged_lengths(fox, L):
     lf = fi.make_case(2, 3, L, 64, "f32", seed=L).log_f
     c = host(fox.fox_logf_cumsum(dev(lf, "f32")))
     ref = oracle.cumsum_logf(lf)
     ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
     assert np.all(np.abs(c - ref) <= ulp + 1e-30)
+
+
+@pytest.mark.parametrize("L", [1, 300, 16384, 40001])
+def test_reverse_scan_of_dc(fox, L):
+    """d log f = reverse cumulative sum of dc_q + dc_k (fp64 accumulation, one rounding), across
+    more than one 16384-element tile for the longer rows."""
+    rng = np.random.default_rng(L)
+    a = rng.standard_normal((3, L)).astype(np.float32)
+    b = rng.standard_normal((3, L)).astype(np.float32)
+    got = host(fox.fox_dlogf_from_dc(dev(a, "f32"), dev(b, "f32")))
+    ref = oracle.reverse_cumsum(a.astype(np.float64) + b.astype(np.float64))
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= ulp + 1e-30), float(np.max(np.abs(got - ref) / ulp))
 
 
 # ------------------------------------------------------------------------------------- forward
