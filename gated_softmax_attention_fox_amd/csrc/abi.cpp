@@ -211,6 +211,10 @@ fox_status fox_attn_skip_plan(const void* q, const void* k, fox_dtype in_dt, con
   if (in_dt != FOX_BF16)
     return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
                 "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+  // the plan's kernels put B*H on the second grid axis and count items in 32-bit integers
+  if (B * H > 65535 || B * H * ((L + 127) / 128 + (L + 255) / 256) > (int64_t(1) << 29))
+    return fail(FOX_E_UNSUPPORTED, "tile skipping supports B*H <= 65535 and B*H*ceil(L/128) "
+                "below 2^29 (got B*H=%lld, L=%lld)", (long long)(B * H), (long long)L);
   const size_t need = fox::skip_plan_layout(B * H, L).bytes;
   FOX_REQUIRE(plan_bytes >= need, "plan too small: %zu bytes given, %zu needed", plan_bytes, need);
   return launched(fox::launch_skip_plan(q, k, c, plan, B * H, L, D, scale, (hipStream_t)stream),
@@ -514,6 +518,8 @@ fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cac
   if (in_dt != FOX_BF16)
     return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
                 "the decode step takes a bf16 cache (in_dt = FOX_BF16)");
+  if (B * H > 65535)  // the second grid axis
+    return fail(FOX_E_UNSUPPORTED, "decode supports B*H <= 65535 (got %lld)", (long long)(B * H));
   const size_t need = fox::decode_workspace_bytes(B * H, T_max, D);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
@@ -534,6 +540,8 @@ fox_status fox_attn_decode_key_norms(const void* k_cache, fox_dtype in_dt, const
   if (in_dt != FOX_BF16)
     return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
                 "the decode cache is bf16 (in_dt = FOX_BF16)");
+  if (B * H > 65535)  // the second grid axis
+    return fail(FOX_E_UNSUPPORTED, "decode supports B*H <= 65535 (got %lld)", (long long)(B * H));
   return launched(fox::launch_decode_key_norms(k_cache, lens, k_norms, B, H, T_max, D,
                                                (hipStream_t)stream),
                   "fox_attn_decode_key_norms");

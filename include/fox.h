@@ -121,6 +121,7 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
  *   fox_attn_skip_plan_bytes : bytes of device memory a plan takes for these sizes.
  *   fox_attn_skip_plan       : fills `plan` (256-byte aligned, at least that many bytes) from
  *                              q, k (bf16, [B, H, L, D]), c and scale. Reads q and k once.
+ *                              Supports B*H <= 65535 (FOX_E_UNSUPPORTED beyond).
  * Plan layout (four arrays, each starting at the next 256-byte boundary, BH = B * H):
  *   int32 q_skip[BH][ceil(L / 256)]   key tiles of 64 keys, counted from key 0, that the
  *                                     256-query tile skips (the forward and dq steps);
@@ -280,7 +281,8 @@ fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f
  *   workspace : at least fox_attn_decode_workspace_bytes(B, H, T_max, D) bytes, 256-byte
  *             aligned, contents ignored and clobbered.
  * fp32 logits, exponentials and sums; no rounding of the weights. flags must contain
- * FOX_CAUSAL. Reads every cached key and value once (bound by HBM). */
+ * FOX_CAUSAL. Reads every cached key and value once (bound by HBM). Supports B*H <= 65535
+ * (FOX_E_UNSUPPORTED beyond). */
 size_t fox_attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t T_max, int64_t D);
 fox_status fox_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                            fox_dtype in_dt, const float* c_cache, const int32_t* lens,

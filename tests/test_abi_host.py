@@ -125,6 +125,7 @@ def test_skip_plan_rejects(lib):
     assert plan(in_dt=0) == 2
     assert plan(scale=-1.0) == 1
     assert plan(L=0) == 1
+    assert lib.fox_attn_skip_plan(P, P, 1, P, P, 1 << 40, 300, 300, 64, 128, 0.1, None) == 2  # B*H
 
 
 def test_decode_workspace_size(lib):
@@ -151,6 +152,8 @@ def test_decode_rejects(lib):
     assert dec(T=0) == 1
     assert dec(D=96) == 1
     assert dec(flags=0) == 2
+    assert lib.fox_attn_decode(P, P, P, 1, P, P, None, P, 1, None, P, 1 << 40, 300, 300, 64, 128,
+                               0.1, 1, None) == 2  # B*H above the grid limit
 
     def app(k_new=P, lens=P, in_dt=1, T=64, D=128):
         return lib.fox_attn_decode_append(k_new, P, in_dt, P, P, P, P, None, lens, 2, 3, T, D,
