@@ -50,7 +50,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(const float* __
   double carry = 0.0;
   for (int64_t t0 = 0; t0 < L; t0 += kScanTile) {
     const int n = L - t0 < kScanTile ? (int)(L - t0) : kScanTile;
-    // coalesced loads in scan order (i = t0 + k), scattered into padded segments
+    // coalesced loads in scan order (i = t0 + k), scattered into padded segments; unrolled so
+    // that many loads are in flight at once (the inputs usually come cold from HBM)
+#pragma unroll 16
     for (int k = tid; k < n; k += kScanThreads)
       tile[(k / kScanPer) * kScanPad + k % kScanPer] = scan_load<kReverse>(a, b, L, t0 + k);
     __syncthreads();
@@ -80,6 +82,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(const float* __
     }
     carry += tile_tot;
     __syncthreads();
+#pragma unroll 16
     for (int k = tid; k < n; k += kScanThreads) {
       const int64_t i = t0 + k;
       out[kReverse ? (L - 1 - i) : i] = (float)tile[(k / kScanPer) * kScanPad + k % kScanPer];
