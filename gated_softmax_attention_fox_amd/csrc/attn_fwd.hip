@@ -42,6 +42,7 @@ namespace {
 
 constexpr int kFwdBN = 64;  // keys per LDS tile
 constexpr float kFwdLazy = 8.0f;  // rescale O only when a row max rises by more than this (log2)
+constexpr float kFwdLazyW = 256.0f;  // 2^kFwdLazy: the weight a row max above kFwdLazy exceeds
 struct First { static constexpr bool value = true; };   // tag: a wave's first (diagonal) tile
 struct Rest { static constexpr bool value = false; };   // tag: every later tile
 
@@ -349,44 +350,50 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   auto step = [&](f32x16& sc, f32x16& sn, const f32x4 (&ck)[4], uint32_t vo, uint32_t ko, bool next)
       __attribute__((always_inline)) {
     pv(vo);
-    float mx = -INFINITY;
+    f32x16 p;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = fmaf(sc[4 * i + e], sl2e, -(ck[i][e] + m));
         sc[4 * i + e] = x;
-        mx = fmaxf(mx, x);
+        p[4 * i + e] = __builtin_amdgcn_exp2f(x);
       }
     }
-    mx = xhalf_max(mx);
-    f32x16 p;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(sc[e]);
     bf16x8 nb[2];
-    float ln = lsum;
+    float ps = 0.f;  // this lane's sum of the step's rounded weights
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       nb[t] = pack_c_half(p, t);
-      ln = rowsum_bf16x8(nb[t], ln);
+      ps = rowsum_bf16x8(nb[t], ps);
     }
     if (next) qk(sn, ko);
     // Keep the common-path exponentials above the branch (the compiler would otherwise sink them
     // into the fall-through path, which splits the block again).
-    asm volatile("" : "+v"(nb[0]), "+v"(nb[1]), "+v"(ln));
-    interleave_step<8, 2, 5, 10>();
-    const bool raise = mx > kFwdLazy;
-    if (__any(raise)) {
+    asm volatile("" : "+v"(nb[0]), "+v"(nb[1]), "+v"(ps));
+    interleave_step<6, 2, 4, 11>();
+    // The lazy-raise test without a row max: a weight above 2^kFwdLazy (x > kFwdLazy) rounds to
+    // at least 2^kFwdLazy in bf16, and a sum of non-negative terms is at least each term, so a
+    // lane whose row needs a raise always has ps >= 2^kFwdLazy. The branch then takes the exact
+    // row max and raises only the rows whose max exceeds kFwdLazy, as the max test would; a
+    // lane let through by the sum alone gets dm = 0, which leaves its values unchanged.
+    if (__any(ps >= kFwdLazyW)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+      mx = xhalf_max(mx);
+      const bool raise = mx > kFwdLazy;
       const float dm = raise ? mx : 0.f;
       const float alpha = __builtin_amdgcn_exp2f(-dm);
       m += dm;
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(sc[e] - dm);
-      ln = lsum * alpha;
+      lsum *= alpha;
+      ps = 0.f;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         nb[t] = pack_c_half(p, t);
-        ln = rowsum_bf16x8(nb[t], ln);
+        ps = rowsum_bf16x8(nb[t], ps);
       }
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) {
@@ -396,7 +403,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
     pb[0] = nb[0];
     pb[1] = nb[1];
-    lsum = ln;
+    lsum += ps;
   };
   // Iteration t: sub-tiles 2t (rows 32..63 of tile t) and 2t + 1 (rows 0..31).
   auto tile_body = [&](uint32_t ko_t, uint32_t ko_t1, uint32_t vo_tm1, uint32_t co_t, bool next)
