@@ -179,6 +179,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         vf[c][e] = (__bf16)0.f;
       }
     }
+    // Only the matrix cores read K^T and V^T: AGPRs, which leaves the vector registers free.
+    pin_agpr(kf[c]);
+    pin_agpr(vf[c]);
   }
   const float kterm = kok ? (C[kj] - c_ref) * kLog2e : 0.f;
   f32x16 dvacc[D / 32], dkacc[D / 32];
@@ -472,7 +475,8 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
   const int kt_last = q_last / BN;
   // Key tiles kt_last down to the oldest one a skip plan could not rule out.
-  const int n_t = kt_last + 1 - (q_skip ? q_skip[(size_t)bh * n_qt + qt] : 0);
+  const int kt_skip = q_skip ? q_skip[(size_t)bh * n_qt + qt] : 0;
+  const int n_t = kt_last + 1 - kt_skip;
   const bool active = qw <= q_last;
   const int j0 = max(2 * kt_last + 2 - NB - qw / 32, 0);  // first sub-tile with a key <= a query of the wave
   const i32x4 k_rs = buffer_words(K, (uint32_t)(L * D * 2));
@@ -511,19 +515,25 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
     for (int d = 0; d < D / 32; ++d) dqacc[b][d] = zero16();
   }
 
+  // Key tile of visit t: the diagonal band (the last four key tiles) from the diagonal
+  // backwards, then the older tiles in ascending order, so that the workgroups of one head that
+  // run at the same time stream the same K and V tiles through the cache.
+  auto key_tile = [&](int t) __attribute__((always_inline)) {
+    return t < 4 ? kt_last - t : t - 4 + kt_skip;
+  };
   auto copy_kv = [&](const i32x4& rs, uint32_t region, int t, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < BLK; ++k) {
       const int blk = wave * BLK + k;
       const int r = blk * (512 / D) + lane / CPR;
       const int lc = (lane % CPR) ^ swz_key<D>(r);
-      const uint32_t voff = (uint32_t)(((kt_last - t) * BN + r) * D + lc * 8) * 2;
+      const uint32_t voff = (uint32_t)((key_tile(t) * BN + r) * D + lc * 8) * 2;
       copy16_to_lds(sbase + region + slot * TB + blk * 1024, voff, rs);
     }
   };
   auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {
     if (lane < CW) {
-      const uint32_t voff = (uint32_t)((kt_last - t) * BN + wave * CW + lane) * 4;
+      const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * CW + lane) * 4;
       copy4_to_lds(sbase + R_OFF + slot * BN * 4 + wave * CW * 4, voff, c_rs);
     }
   };
@@ -578,11 +588,6 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
 #pragma unroll
       for (int b = 0; b < NB; ++b) dp[b] = mfma32(a, dof[b][c], dp[b]);
     }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {  // the VALU reads these: keep them in VGPRs
-      pin_vgpr(s[b]);
-      pin_vgpr(dp[b]);
-    }
     bf16x8 sb[NB][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -616,11 +621,6 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
 #pragma unroll
         for (int b = 0; b < NB; ++b) dqacc[b][d] = mfma32(a, sb[b][t], dqacc[b][d]);
       }
-    }
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d) {  // only the matrix cores touch these until the end
-#pragma unroll
-      for (int b = 0; b < NB; ++b) pin_agpr(dqacc[b][d]);
     }
   };
 
