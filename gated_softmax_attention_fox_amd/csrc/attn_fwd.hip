@@ -109,9 +109,16 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   const int h = lane >> 5, l32 = lane & 31;
   // Longest-first: by query tile, or in a skip plan's order of decreasing work.
   const int bid = blockIdx.x;
-  const int item = q_order ? q_order[bid] : 0;
-  const int bh = q_order ? item / n_qt : bid % BH;
-  const int qt = q_order ? item % n_qt : n_qt - 1 - bid / BH;
+  int bh, qt;
+  if (q_order) {
+    const int item = q_order[bid];
+    bh = item / n_qt;
+    qt = item % n_qt;
+  } else {  // query tiles from the last, each head kept to one XCD where possible
+    int level;
+    xcd_item(bid, BH, bh, level);
+    qt = n_qt - 1 - level;
+  }
   const int q0 = qt * BM;
   const size_t base = (size_t)bh * L * D;
   Q += base;

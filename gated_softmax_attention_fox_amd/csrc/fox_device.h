@@ -230,4 +230,47 @@ __device__ __forceinline__ void bar_vm() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// ---------------------------------------------------------------------------------------------
+// XCD-aware work order. The hardware places workgroup `bid` on XCD bid % 8, and each XCD has its
+// own L2. A grid of n_levels x BH items (levels issued one after another, most work first; a level
+// holds one item per (b, h)) is mapped so that every head keeps to one XCD where the level's
+// positions allow it: head h's home XCD is h % 8; a level position on XCD x takes the next head
+// at home on x, and the positions left over (when BH is not a multiple of 8) take the heads left
+// over, both in order. Within each level this is a bijection between positions and heads, so the
+// grid covers every item once whatever the placement; only the cache reuse depends on it. With
+// 12 heads, heads 0..7 stay on their XCD and heads 8..11 alternate between two XCDs level by level
+// (instead of every head alternating and every XCD streaming three heads).
+__device__ __forceinline__ void xcd_item(int bid, int BH, int& bh, int& level) {
+  constexpr int NX = 8;
+  level = bid / BH;
+  const int p = bid - level * BH;  // position within the level
+  const int b8 = (level * BH) % NX;  // XCD of the level's first position
+  auto first_pos = [&](int y) { return (y - b8 + NX) % NX; };  // first position on XCD y
+  auto n_pos = [&](int y) { const int q = first_pos(y); return BH > q ? (BH - q + NX - 1) / NX : 0; };
+  auto n_home = [&](int y) { return y < BH ? (BH - 1 - y) / NX + 1 : 0; };
+  const int x = (b8 + p) % NX;
+  const int k = (p - first_pos(x)) / NX;  // rank of p among the level's positions on XCD x
+  if (k < n_home(x)) {
+    bh = x + NX * k;
+    return;
+  }
+  int r = 0;  // rank of p among the left-over positions before it
+  for (int y = 0; y < NX; ++y) {
+    const int q = first_pos(y);
+    const int before = p > q ? (p - q + NX - 1) / NX : 0;
+    r += before > n_home(y) ? before - n_home(y) : 0;
+  }
+  for (int y = 0; y < NX; ++y) {  // the r-th left-over head: y + NX j for n_pos(y) <= j < n_home(y)
+    const int extra = n_home(y) - n_pos(y);
+    if (extra > 0) {
+      if (r < extra) {
+        bh = y + NX * (n_pos(y) + r);
+        return;
+      }
+      r -= extra;
+    }
+  }
+  bh = p;  // not reached: the left-over positions and heads are equal in number
+}
+
 }  // namespace fox

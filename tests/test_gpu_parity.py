@@ -344,6 +344,23 @@ def test_backward_small(fox, L, D):
     _check_grads(got, ref)
 
 
+@pytest.mark.parametrize("B,H,L,D", [(1, 3, 600, 128), (1, 5, 300, 64), (1, 12, 520, 128),
+                                     (1, 13, 260, 64), (3, 7, 280, 128), (1, 17, 140, 64)])
+def test_head_counts_off_the_xcd_grid(fox, B, H, L, D):
+    """Forward and backward at head counts that are not multiples of 8, over several query and
+    key tiles: the kernels' XCD-aware work order must still visit every (b, h, tile) once."""
+    case = fi.make_case(B, H, L, D, "bf16", seed=700 + 10 * H + B, with_do=True)
+    say(f"head counts B={B} H={H} L={L} D={D}")
+    s = default_scale(D)
+    _, o, lse = _run_fwd(fox, case, torch.float32)
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
+    check("O", o, O)
+    check("LSE", lse, LSE)
+    got = _run_bwd(fox, case)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s)[:4]
+    _check_grads(got, ref)
+
+
 def test_backward_config2_shape(fox):
     """B=4, H=12, L=2048 with config-5 statistics: 6 whole heads compared."""
     case = fi.make_case(4, 12, 2048, 128, "bf16", seed=3, gate="per_head", with_do=True)
