@@ -5,7 +5,8 @@
 //
 // Gate: given dz[b, t, h] (gate.hip, backward mode),
 //   dx[b, t, :] = sum_h dz[b, t, h] w_f[h, :]        (one pass over the tokens)
-//   dw_f[h, :]  = sum_{b,t} dz[b, t, h] x[b, t, :]   (partials per 256-token chunk, then a sum)
+//   dw_f[h, :]  = sum_{b,t} dz[b, t, h] x[b, t, :]   (partials per 256-token chunk, then a sum;
+//                                                    on the matrix cores for bf16 x)
 //   db_f[h]     = sum_{b,t} dz[b, t, h]
 // QK-norm: with r = 1 / sqrt(mean x^2 + eps), xh = x r and g = dy w (w = 1 when absent),
 //   dx = r (g - xh mean(g xh)),  dw = sum over rows of dy xh  (partials per workgroup, then a sum).
@@ -128,6 +129,108 @@ __global__ __launch_bounds__(256) void gate_dw_partial_kernel(const void* __rest
 }
 
 // dw_f[h, d] and db_f[h] as the chunk partials summed in chunk order.
+// dw_f partials on the matrix cores (bf16 x, d_model a multiple of 128; heads in groups of 32).
+// Workgroup (chunk, slab, head group) accumulates dw_f^T[128 columns x 32 heads] over the chunk's
+// kChunk tokens, staging 64 tokens of x and dz at a time in LDS (the next stage's x is already in
+// flight in registers while the current one is multiplied). Each wave owns 32 columns:
+// v_mfma_f32_32x32x16_bf16 with A = x^T from transposed reads of the swizzled x tile (k = token)
+// and B = dz of the same 16 tokens for head n = lane % 32, split into three bf16 parts
+// (hi + mid + lo carries all 24 bits of the fp32 value), so every product is exact and only the
+// fp32 accumulation rounds. The partials have gate_dw_partial_kernel's layout.
+__global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restrict__ x,
+                                                           const float* __restrict__ dz,
+                                                           float* __restrict__ part,
+                                                           float* __restrict__ part_db,
+                                                           int64_t rows, int dm, int H) {
+  constexpr int TS = 64;  // tokens per LDS stage
+  constexpr int HG = 32;  // heads per workgroup (the MFMA's n dimension)
+  constexpr int XV = TS * 16 / 256;  // 16-byte pieces of x per thread and stage
+  constexpr int DV = TS * HG / 256;  // dz values per thread and stage
+  __shared__ __attribute__((aligned(16))) bf16_t xs[TS * 128];
+  __shared__ float dzs[TS][HG];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
+  const int chunk = blockIdx.x, slab = blockIdx.y, h0 = blockIdx.z * HG;
+  const int nh = H - h0 < HG ? H - h0 : HG;
+  const int64_t r0 = (int64_t)chunk * kChunk;
+  const int n = rows - r0 < kChunk ? (int)(rows - r0) : kChunk;
+  const int n_st = (n + TS - 1) / TS;
+  const uint32_t xb = lds_addr(xs);
+  const uint32_t a0 = xb + col8_off<128>(lane, 32 * wave, 0);
+  const uint32_t a1 = xb + col8_off<128>(lane, 32 * wave, 1);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  u32x4 xv[XV];
+  float dv[DV];
+  auto load_stage = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const int i = tid + 256 * q, row = i >> 4, c = i & 15;
+      const int tok = st * TS + row;
+      const bool ok = tok < n;  // rows past the chunk read token r0 and are zeroed
+      const u32x4 v = *reinterpret_cast<const u32x4*>(x + (size_t)(ok ? r0 + tok : r0) * dm +
+                                                      slab * 128 + c * 8);
+      xv[q] = ok ? v : zero4;
+    }
+#pragma unroll
+    for (int q = 0; q < DV; ++q) {
+      const int i = tid + 256 * q, row = i / HG, hh = i % HG;
+      const int tok = st * TS + row;
+      dv[q] = (tok < n && hh < nh) ? dz[(r0 + tok) * H + h0 + hh] : 0.f;
+    }
+  };
+
+  f32x16 acc = zero16();
+  float db = 0.f;
+  load_stage(0);
+  for (int st = 0; st < n_st; ++st) {
+#pragma unroll
+    for (int q = 0; q < XV; ++q) {
+      const int i = tid + 256 * q;
+      lds_store8<128>(xs, i >> 4, (i & 15) * 8, xv[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < DV; ++q) {
+      const int i = tid + 256 * q;
+      dzs[i / HG][i % HG] = dv[q];
+    }
+    __syncthreads();
+    if (st + 1 < n_st) load_stage(st + 1);
+    if (slab == 0 && tid < HG) {
+      for (int row = 0; row < TS; ++row) db += dzs[row][tid];
+    }
+#pragma unroll
+    for (int ks = 0; ks < TS / 16; ++ks) {
+      const uint32_t ro = (uint32_t)ks * 16 * 128 * 2;  // 16-row blocks keep the swizzle key
+      const bf16x8 a = lds_tr8(a0 + ro, a1 + ro);
+      bf16x8 bh, bm, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // the token of B's k slot e matches A's (transposed read)
+        const float v = dzs[16 * ks + (e < 4 ? 4 * hl + e : 8 + 4 * hl + (e - 4))][lane & 31];
+        const __bf16 p1 = (__bf16)v;
+        const float r1 = v - (float)p1;
+        const __bf16 p2 = (__bf16)r1;
+        bh[e] = p1;
+        bm[e] = p2;
+        bl[e] = (__bf16)(r1 - (float)p2);
+      }
+      acc = mfma32(a, bh, acc);
+      acc = mfma32(a, bm, acc);
+      acc = mfma32(a, bl, acc);
+    }
+    __syncthreads();
+  }
+  const int head = lane & 31;  // C[m = 8 i + 4 hl + j][n = head] sits in slot 4 i + j
+  if (head < nh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = slab * 128 + 32 * wave + 8 * i + 4 * hl;
+      *reinterpret_cast<float4*>(part + ((size_t)chunk * H + h0 + head) * dm + d) =
+          make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    }
+  }
+  if (slab == 0 && tid < nh) part_db[(size_t)chunk * H + h0 + tid] = db;
+}
+
 __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __restrict__ part,
                                                              const float* __restrict__ part_db,
                                                              float* __restrict__ dw_f,
@@ -270,7 +373,12 @@ hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const f
   }
   const dim3 pg((unsigned)n_chunk, (unsigned)((d_model + 255) / 256),
                 (unsigned)((H + kHGroup - 1) / kHGroup));
-  if (x_bf16)
+  if (x_bf16 && d_model % 128 == 0)
+    hipLaunchKernelGGL(gate_dw_mfma_kernel,
+                       dim3((unsigned)n_chunk, (unsigned)(d_model / 128), (unsigned)((H + 31) / 32)),
+                       dim3(256), 0, s, static_cast<const bf16_t*>(x), dz, part, part_db, rows,
+                       (int)d_model, (int)H);
+  else if (x_bf16)
     hipLaunchKernelGGL((gate_dw_partial_kernel<true>), pg, dim3(256), 0, s, x, dz, part, part_db,
                        rows, (int)d_model, (int)H);
   else

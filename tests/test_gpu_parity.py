@@ -283,7 +283,10 @@ def test_gate_backward_config4(fox, x_dt):
 
 
 @pytest.mark.parametrize("B,L,dm,H", [(2, 1, 8, 1), (1, 77, 40, 3), (3, 300, 264, 17), (2, 45, 96, 20),
-                                     (2, 45, 96, 7), (1, 1, 32, 16)])
+                                     (2, 45, 96, 7), (1, 1, 32, 16),
+                                     # d_model a multiple of 128: the matrix-core dw_f pass
+                                     (2, 77, 128, 3), (1, 300, 256, 17), (3, 45, 384, 33),
+                                     (1, 1, 128, 1), (1, 513, 128, 32)])
 def test_gate_backward_ragged(fox, B, L, dm, H):
     rng = np.random.default_rng(B * 1000 + L)
     x = fi.bf16_round(rng.standard_normal((B, L, dm)).astype(np.float32))
