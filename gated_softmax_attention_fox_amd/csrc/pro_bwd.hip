@@ -4,7 +4,8 @@
 // fixed order (per-chunk partials, then a second pass), so the results are deterministic.
 //
 // Gate: given dz[b, t, h] (gate.hip, backward mode),
-//   dx[b, t, :] = sum_h dz[b, t, h] w_f[h, :]        (one pass over the tokens)
+//   dx[b, t, :] = sum_h dz[b, t, h] w_f[h, :]        (one pass over the tokens; on the matrix
+//                                                    cores when H <= 16, d_model % 128 == 0)
 //   dw_f[h, :]  = sum_{b,t} dz[b, t, h] x[b, t, :]   (partials per 256-token chunk, then a sum;
 //                                                    on the matrix cores for bf16 x)
 //   db_f[h]     = sum_{b,t} dz[b, t, h]
@@ -92,6 +93,68 @@ __global__ __launch_bounds__(256) void gate_dx16_kernel(const float* __restrict_
 
 // Partial dw_f and db_f of one 256-token chunk, one 256-column slab and up to 16 heads: thread c
 // owns column slab * 256 + c and walks the chunk's tokens (coalesced rows of x).
+// dx on the matrix cores (d_model a multiple of 128, H <= 16): workgroup (token block, slab) owns
+// 128 tokens x 128 columns, each wave 32 columns. dx^T[32 columns x 32 tokens] is one
+// v_mfma_f32_32x32x16_bf16 per operand pair, k = the (zero-padded) 16 heads: A = w_f^T (the
+// wave's columns, loaded once), B = dz^T of 32 tokens. Both are split into three bf16 parts and
+// the six products that reach fp32 accuracy are summed smallest first; the hi x hi product is
+// exact, so the result matches an fp32 dot product of 16 terms to its rounding.
+__global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const float* __restrict__ dz,
+                                                           const float* __restrict__ w_f,
+                                                           float* __restrict__ dx, int64_t rows,
+                                                           int dm, int H) {
+  constexpr int TB = 128;  // tokens per workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hl = lane >> 5, l32 = lane & 31;
+  const int64_t t_blk = (int64_t)blockIdx.x * TB;
+  const int d0 = blockIdx.y * 128 + 32 * wave;
+  auto split3 = [](const float (&v)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 a = (__bf16)v[e];
+      const float r1 = v[e] - (float)a;
+      const __bf16 b = (__bf16)r1;
+      p0[e] = a;
+      p1[e] = b;
+      p2[e] = (__bf16)(r1 - (float)b);
+    }
+  };
+  // A[m = column d0 + l32][k = head 8 hl + e]
+  bf16x8 wa0, wa1, wa2;
+  {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int h = 8 * hl + e;
+      v[e] = h < H ? w_f[(size_t)h * dm + d0 + l32] : 0.f;
+    }
+    split3(v, wa0, wa1, wa2);
+  }
+  for (int tb = 0; tb < TB; tb += 32) {
+    const int64_t t = t_blk + tb + l32;  // B[k = head 8 hl + e][n = token t]
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int h = 8 * hl + e;
+      v[e] = (t < rows && h < H) ? dz[t * H + h] : 0.f;
+    }
+    bf16x8 b0, b1, b2;
+    split3(v, b0, b1, b2);
+    f32x16 acc = zero16();
+    acc = mfma32(wa2, b0, acc);
+    acc = mfma32(wa1, b1, acc);
+    acc = mfma32(wa0, b2, acc);
+    acc = mfma32(wa1, b0, acc);
+    acc = mfma32(wa0, b1, acc);
+    acc = mfma32(wa0, b0, acc);
+    if (t < rows) {  // C[m = 8 i + 4 hl + j][n = l32] in slot 4 i + j: 4 consecutive columns
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(dx + t * dm + d0 + 8 * i + 4 * hl) =
+            make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    }
+  }
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(256) void gate_dw_partial_kernel(const void* __restrict__ x,
                                                               const float* __restrict__ dz,
@@ -240,7 +303,8 @@ __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __rest
   const int64_t n_w = (int64_t)H * dm;
   if (gid < n_w) {
     float s = 0.f;
-    for (int c = 0; c < n_chunk; ++c) s += part[(size_t)c * n_w + gid];
+#pragma unroll 8
+    for (int c = 0; c < n_chunk; ++c) s += part[(size_t)c * n_w + gid];  // 8 loads in flight
     dw_f[gid] = s;
   } else if (gid < n_w + H) {
     const int h = (int)(gid - n_w);
@@ -363,7 +427,10 @@ hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const f
   float* part_db = part + granule((size_t)((int64_t)n_chunk * H * d_model));
   hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dout, dz, B, L, d_model, H, kind, s);
   if (e != hipSuccess) return e;
-  if (H <= 16) {
+  if (H <= 16 && d_model % 128 == 0) {
+    hipLaunchKernelGGL(gate_dx_mfma_kernel, dim3((unsigned)((rows + 127) / 128), (unsigned)(d_model / 128)),
+                       dim3(256), 0, s, dz, w_f, dx, rows, (int)d_model, (int)H);
+  } else if (H <= 16) {
     hipLaunchKernelGGL(gate_dx16_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, dz,
                        w_f, dx, rows, (int)d_model, (int)H);
   } else {
