@@ -429,8 +429,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // Query-stationary step with the forward kernel's memory pipeline. NB 32-query blocks per wave
 // share every K / V operand read; 8 / NB waves cover 256 queries (NB = 1: 8 waves, two per
-// SIMD, within 256 registers each; NB = 2: 4 waves, one per SIMD, up to 512). Keys are walked from the diagonal backwards in 64-key tiles (two 32-key
-// sub-tiles, sub-tile j = key block 2 kt_last + 1 - j). K, V and raw c of tile t sit in LDS
+// SIMD, within 256 registers each; NB = 2: 4 waves, one per SIMD, up to 512). Keys are walked in 64-key tiles (two 32-key sub-tiles): the diagonal band (the
+// last four key tiles, where sub-tile j is key block 2 kt_last + 1 - j) from the diagonal
+// backwards, then the older tiles in ascending order. K, V and raw c of tile t sit in LDS
 // ring slot t % 4 (the bias slice (c_j - c_ref) log2 e of tile t in slot t % 2); iteration t
 // reads K(t), V(t) and the bias of tile t, starts the untracked copies of K(t + 2), V(t + 2)
 // and c(t + 3), converts c(t + 1) into the bias of tile t + 1, and its barrier waits only for
