@@ -383,24 +383,24 @@ def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=N
 
 
 def fox_attn_bwd_delta(dO: torch.Tensor, o: torch.Tensor) -> torch.Tensor:
-    """Delta = rowsum(dO * O) over the last axis; dO bf16, o fp32."""
+    """Delta = rowsum(dO * O) over the last axis; dO bf16 or fp32, o fp32."""
     lib = load_library()
-    pd = _dev(dO, "dO", (torch.bfloat16,))
+    pd = _dev(dO, "dO", (torch.bfloat16, torch.float32))
     po = _dev(o, "o", (torch.float32,))
     if dO.shape != o.shape:
         raise ValueError("dO and o must have the same shape")
     D = o.shape[-1]
     delta = torch.empty(o.shape[:-1], dtype=torch.float32, device=o.device)
-    _check(lib.fox_attn_bwd_delta(pd, FOX_BF16, po, ctypes.c_void_p(delta.data_ptr()),
+    _check(lib.fox_attn_bwd_delta(pd, _code(dO.dtype), po, ctypes.c_void_p(delta.data_ptr()),
                                   o.numel() // D, D, _stream(o)), "fox_attn_bwd_delta")
     return delta
 
 
 def _bwd_inputs(q, k, v, c, lse, dO, delta):
     B, H, L, D = _bhld(q, k, v)
-    ptrs = (_dev(q, "q", (torch.bfloat16,)), _dev(k, "k", (torch.bfloat16,)),
-            _dev(v, "v", (torch.bfloat16,)), _dev(c, "c", (torch.float32,), 3),
-            _dev(lse, "lse", (torch.float32,), 3), _dev(dO, "dO", (torch.bfloat16,), 4),
+    ptrs = (_dev(q, "q", (torch.bfloat16, torch.float32)), _dev(k, "k", (q.dtype,)),
+            _dev(v, "v", (q.dtype,)), _dev(c, "c", (torch.float32,), 3),
+            _dev(lse, "lse", (torch.float32,), 3), _dev(dO, "dO", (q.dtype,), 4),
             _dev(delta, "delta", (torch.float32,), 3))
     return (B, H, L, D), ptrs
 
@@ -414,7 +414,7 @@ def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None,
     dv = torch.empty_like(dk)
     dck = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib.fox_attn_bwd_dkv(pq, pk, pv, FOX_BF16, pc, pl, pdo, pdl,
+    _check(lib.fox_attn_bwd_dkv(pq, pk, pv, _code(q.dtype), pc, pl, pdo, pdl,
                                 ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
                                 ctypes.c_void_p(dck.data_ptr()), B, H, L, D, scale, FOX_CAUSAL,
                                 _plan_ptr(skip_plan), _stream(q)), "fox_attn_bwd_dkv")
@@ -434,7 +434,7 @@ def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
         delta_out = torch.empty_like(delta)
     pdn = _dev(delta_out, "delta_out", (torch.float32,), 3)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib.fox_attn_bwd_dq(pq, pk, pv, FOX_BF16, pc, pl, pdo, pdl,
+    _check(lib.fox_attn_bwd_dq(pq, pk, pv, _code(q.dtype), pc, pl, pdo, pdl,
                                ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dcq.data_ptr()), pdn,
                                B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan), _stream(q)),
            "fox_attn_bwd_dq")

@@ -244,6 +244,8 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
               "skip_plan must be 256-byte aligned");
   if (skip_plan && in_dt != FOX_BF16)
     return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+  if (in_dt == FOX_F32 && B * H > 65535)
+    return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)", (long long)(B * H));
   const hipStream_t s = (hipStream_t)stream;
   if (in_dt == FOX_F32)
     return launched(fox::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, c,
@@ -285,14 +287,23 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
   if (!(flags & FOX_CAUSAL))
     return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
   if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
-  if (in_dt != FOX_BF16)
-    return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
-                "the backward takes bf16 q/k/v/dO (in_dt = FOX_BF16)");
+  FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
   const size_t need = fox::bwd_workspace_bytes(B * H, L);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
+  if (in_dt == FOX_F32) {
+    if (skip_plan)
+      return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+    if (B * H > 65535)
+      return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)",
+                  (long long)(B * H));
+    return launched(fox::launch_bwd_f32((const float*)q, (const float*)k, (const float*)v, c, o, lse,
+                                        (const float*)dO, dq, dk, dv, dlog_f, workspace, B * H, L,
+                                        D, scale, (hipStream_t)stream),
+                    "fox_attn_bwd");
+  }
   return launched(fox::launch_bwd_bf16(q, k, v, c, o, lse, dO, dq, dk, dv, dlog_f, workspace,
                                        B * H, L, D, scale, skip_plan, (hipStream_t)stream),
                   "fox_attn_bwd");
@@ -316,9 +327,9 @@ fox_status check_bwd_common(const void* q, const void* k, const void* v, fox_dty
   if (!(flags & FOX_CAUSAL))
     return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
   if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
-  if (in_dt != FOX_BF16)
-    return fail(in_dt == FOX_F32 ? FOX_E_UNSUPPORTED : FOX_E_INVALID,
-                "the backward takes bf16 q/k/v/dO (in_dt = FOX_BF16)");
+  FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
+  if (in_dt == FOX_F32 && B * H > 65535)
+    return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)", (long long)(B * H));
   return FOX_OK;
 }
 }  // namespace
@@ -328,9 +339,13 @@ fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, f
   FOX_REQUIRE_PTR(dO);
   FOX_REQUIRE_PTR(o);
   FOX_REQUIRE_PTR(delta);
-  FOX_REQUIRE(dO_dt == FOX_BF16, "dO must be bf16 (dO_dt = FOX_BF16)");
+  FOX_REQUIRE(dO_dt == FOX_BF16 || dO_dt == FOX_F32, "dO_dt must be FOX_BF16 or FOX_F32");
   FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
   FOX_REQUIRE(rows >= 1 && rows * (D / 8) / 256 < (int64_t(1) << 31), "rows out of range");
+  if (dO_dt == FOX_F32)
+    return launched(fox::launch_bwd_delta_f32((const float*)dO, o, delta, rows, D,
+                                              (hipStream_t)stream),
+                    "fox_attn_bwd_delta");
   return launched(fox::launch_bwd_delta(dO, o, delta, rows, D, (hipStream_t)stream),
                   "fox_attn_bwd_delta");
 }
@@ -347,6 +362,14 @@ fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dty
   FOX_REQUIRE_PTR(dk);
   FOX_REQUIRE_PTR(dv);
   FOX_REQUIRE_PTR(dc_k);
+  if (in_dt == FOX_F32) {
+    if (skip_plan)
+      return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+    return launched(fox::launch_bwd_dkv_f32((const float*)q, (const float*)k, (const float*)v, c, lse,
+                                            (const float*)dO, delta, dk, dv, dc_k, B * H, L, D,
+                                            scale, (hipStream_t)stream),
+                    "fox_attn_bwd_dkv");
+  }
   return launched(fox::launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dc_k, B * H, L, D, scale,
                                       fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dkv");
@@ -364,6 +387,14 @@ fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtyp
   FOX_REQUIRE_PTR(dq);
   FOX_REQUIRE_PTR(dc_q);
   FOX_REQUIRE_PTR(delta_out);
+  if (in_dt == FOX_F32) {
+    if (skip_plan)
+      return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+    return launched(fox::launch_bwd_dq_f32((const float*)q, (const float*)k, (const float*)v, c, lse,
+                                           (const float*)dO, delta, dq, dc_q, delta_out, B * H, L, D,
+                                           scale, (hipStream_t)stream),
+                    "fox_attn_bwd_dq");
+  }
   return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dc_q, delta_out, B * H, L, D,
                                      scale, fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dq");

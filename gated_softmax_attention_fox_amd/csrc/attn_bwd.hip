@@ -727,6 +727,179 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// fp32 path (vector ALU, no down-conversion; the counterpart of fwd_f32_kernel). A wave owns 16
+// rows (queries in f32_dq_kernel, keys in f32_dkv_kernel) with 4 lanes per row, each lane holding
+// a quarter of the head dimension; the other side's rows stream through LDS 32 at a time. Both
+// kernels form every dS element with the same instructions in the same order (f32_dot and
+// f32_ds), so the row sums dc^q and the column sums dc^k come from bit-identical dS and the
+// reverse scan telescopes, as in the bf16 path; those sums and the row-term refinement run in
+// fp64.
+constexpr int kF32Rows = 16;  // rows per wave (4 lanes each)
+constexpr int kF32Tile = 32;  // streamed rows per LDS tile
+
+// Dot product of a row quarter held by this lane with the matching quarter of b, summed over the
+// row's 4 lanes (lane bits 4 and 5) as (q0 + q1) + (q2 + q3) in every lane.
+template <int DQ>
+__device__ __forceinline__ float f32_dot(const float (&a)[DQ], const float* b) {
+  float s = 0.f;
+#pragma unroll
+  for (int d = 0; d < DQ; ++d) s = fmaf(a[d], b[d], s);
+  s += __shfl_xor(s, 16, 64);
+  return s + __shfl_xor(s, 32, 64);
+}
+// P_ij and dS_ij from the two dot products and the row / column terms.
+__device__ __forceinline__ void f32_ds(float qk, float dp, float scale, float ci, float cj,
+                                       float lse_i, float delta_i, float& p, float& ds) {
+  p = expf(fmaf(qk, scale, ci - cj) - lse_i);
+  ds = p * (dp - delta_i);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void delta_f32_kernel(const float* __restrict__ dO,
+                                                        const float* __restrict__ O,
+                                                        float* __restrict__ delta, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+  if (row < rows)
+    for (int d = lane; d < D; d += 64) acc = fmaf(dO[(size_t)row * D + d], O[(size_t)row * D + d], acc);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && lane == 0) delta[row] = acc;
+}
+
+// dQ, dc^q and the refined row term (as dq_pipe_kernel: Delta' makes the kernel's own row of dS
+// sum to zero; dc^q is the remaining rounding-level sum).
+template <int D>
+__global__ __launch_bounds__(64) void f32_dq_kernel(const float* __restrict__ Q,
+                                                    const float* __restrict__ K,
+                                                    const float* __restrict__ V,
+                                                    const float* __restrict__ dO,
+                                                    const float* __restrict__ C,
+                                                    const float* __restrict__ LSE,
+                                                    const float* Delta, float* __restrict__ dQ,
+                                                    float* __restrict__ dcq_out,
+                                                    float* delta_out, int L, float scale) {
+  constexpr int DQ = D / 4;
+  __shared__ float k_s[kF32Tile][D], v_s[kF32Tile][D], c_s[kF32Tile];
+  const int tid = threadIdx.x, part = tid >> 4;
+  const int64_t bh = blockIdx.y;
+  const int qi = blockIdx.x * kF32Rows + (tid & 15);
+  const bool qok = qi < L;
+  const size_t base = (size_t)bh * L * D, rbase = (size_t)bh * L;
+  float q[DQ], g[DQ], acc[DQ];
+#pragma unroll
+  for (int d = 0; d < DQ; ++d) {
+    q[d] = qok ? Q[base + (size_t)qi * D + part * DQ + d] : 0.f;
+    g[d] = qok ? dO[base + (size_t)qi * D + part * DQ + d] : 0.f;
+    acc[d] = 0.f;
+  }
+  const float ci = qok ? C[rbase + qi] : 0.f;
+  const float lse = qok ? LSE[rbase + qi] : 0.f;
+  const float dl = qok ? Delta[rbase + qi] : 0.f;
+  double eps = 0.0, ptot = 0.0;
+  const int q_last = min(blockIdx.x * kF32Rows + kF32Rows - 1, L - 1);
+  for (int k0 = 0; k0 <= q_last; k0 += kF32Tile) {
+    __syncthreads();
+    for (int i = tid; i < kF32Tile * D; i += 64) {
+      const int r = i / D, d = i % D, key = k0 + r;
+      k_s[r][d] = key < L ? K[base + (size_t)key * D + d] : 0.f;
+      v_s[r][d] = key < L ? V[base + (size_t)key * D + d] : 0.f;
+    }
+    if (tid < kF32Tile) c_s[tid] = k0 + tid < L ? C[rbase + k0 + tid] : 0.f;
+    __syncthreads();
+    for (int j = 0; j < kF32Tile; ++j) {
+      const float qk = f32_dot<DQ>(q, &k_s[j][part * DQ]);
+      const float dp = f32_dot<DQ>(g, &v_s[j][part * DQ]);
+      if (qok && k0 + j <= qi) {
+        float p, ds;
+        f32_ds(qk, dp, scale, ci, c_s[j], lse, dl, p, ds);
+        eps += (double)ds;
+        ptot += (double)p;
+#pragma unroll
+        for (int d = 0; d < DQ; ++d) acc[d] = fmaf(ds, k_s[j][part * DQ + d], acc[d]);
+      }
+    }
+  }
+  if (!qok) return;
+#pragma unroll
+  for (int d = 0; d < DQ; ++d) dQ[base + (size_t)qi * D + part * DQ + d] = acc[d] * scale;
+  if (part == 0) {
+    const double dl_new = (double)dl + eps / ptot;
+    dcq_out[rbase + qi] = (float)(eps - (dl_new - (double)dl) * ptot);
+    delta_out[rbase + qi] = (float)dl_new;
+  }
+}
+
+// dK, dV and dc^k (keys stationary; queries from the key's own onwards).
+template <int D>
+__global__ __launch_bounds__(64) void f32_dkv_kernel(const float* __restrict__ Q,
+                                                     const float* __restrict__ K,
+                                                     const float* __restrict__ V,
+                                                     const float* __restrict__ dO,
+                                                     const float* __restrict__ C,
+                                                     const float* __restrict__ LSE,
+                                                     const float* __restrict__ Delta,
+                                                     float* __restrict__ dK, float* __restrict__ dV,
+                                                     float* __restrict__ dck_out, int L,
+                                                     float scale) {
+  constexpr int DQ = D / 4;
+  __shared__ float q_s[kF32Tile][D], o_s[kF32Tile][D], c_s[kF32Tile], l_s[kF32Tile], d_s[kF32Tile];
+  const int tid = threadIdx.x, part = tid >> 4;
+  const int64_t bh = blockIdx.y;
+  const int k0 = blockIdx.x * kF32Rows;
+  const int kj = k0 + (tid & 15);
+  const bool kok = kj < L;
+  const size_t base = (size_t)bh * L * D, rbase = (size_t)bh * L;
+  float kr[DQ], vr[DQ], dk[DQ], dv[DQ];
+#pragma unroll
+  for (int d = 0; d < DQ; ++d) {
+    kr[d] = kok ? K[base + (size_t)kj * D + part * DQ + d] : 0.f;
+    vr[d] = kok ? V[base + (size_t)kj * D + part * DQ + d] : 0.f;
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  const float cj = kok ? C[rbase + kj] : 0.f;
+  double dck = 0.0;
+  for (int i0 = k0 / kF32Tile * kF32Tile; i0 < L; i0 += kF32Tile) {
+    __syncthreads();
+    for (int i = tid; i < kF32Tile * D; i += 64) {
+      const int r = i / D, d = i % D, qq = i0 + r;
+      q_s[r][d] = qq < L ? Q[base + (size_t)qq * D + d] : 0.f;
+      o_s[r][d] = qq < L ? dO[base + (size_t)qq * D + d] : 0.f;
+    }
+    if (tid < kF32Tile) {
+      const int qq = i0 + tid;
+      c_s[tid] = qq < L ? C[rbase + qq] : 0.f;
+      l_s[tid] = qq < L ? LSE[rbase + qq] : 0.f;
+      d_s[tid] = qq < L ? Delta[rbase + qq] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < kF32Tile; ++r) {
+      const float qk = f32_dot<DQ>(kr, &q_s[r][part * DQ]);
+      const float dp = f32_dot<DQ>(vr, &o_s[r][part * DQ]);
+      if (kok && i0 + r >= kj && i0 + r < L) {
+        float p, ds;
+        f32_ds(qk, dp, scale, c_s[r], cj, l_s[r], d_s[r], p, ds);
+        dck -= (double)ds;
+#pragma unroll
+        for (int d = 0; d < DQ; ++d) {
+          dv[d] = fmaf(p, o_s[r][part * DQ + d], dv[d]);
+          dk[d] = fmaf(ds, q_s[r][part * DQ + d], dk[d]);
+        }
+      }
+    }
+  }
+  if (!kok) return;
+#pragma unroll
+  for (int d = 0; d < DQ; ++d) {
+    dK[base + (size_t)kj * D + part * DQ + d] = dk[d] * scale;
+    dV[base + (size_t)kj * D + part * DQ + d] = dv[d];
+  }
+  if (part == 0) dck_out[rbase + kj] = (float)dck;
+}
+
 inline size_t region_floats(int64_t BH, int64_t L) {
   return (size_t)((BH * L + 63) / 64 * 64);  // 256-byte granules
 }
@@ -794,6 +967,59 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
     go_dq<128>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
                delta, dq, dcq, delta_out, BH, L, scale, skip, s);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta_f32(const float* dO, const float* o, float* delta, int64_t rows,
+                                int64_t D, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (D == 64) hipLaunchKernelGGL(delta_f32_kernel<64>, grid, dim3(256), 0, s, dO, o, delta, rows);
+  else hipLaunchKernelGGL(delta_f32_kernel<128>, grid, dim3(256), 0, s, dO, o, delta, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, const float* c,
+                             const float* lse, const float* dO, const float* delta, float* dq,
+                             float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
+                             float scale, hipStream_t s) {
+  const dim3 grid((unsigned)((L + kF32Rows - 1) / kF32Rows), (unsigned)BH);
+  if (D == 64)
+    hipLaunchKernelGGL(f32_dq_kernel<64>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dq, dcq,
+                       delta_out, (int)L, scale);
+  else
+    hipLaunchKernelGGL(f32_dq_kernel<128>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dq, dcq,
+                       delta_out, (int)L, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv_f32(const float* q, const float* k, const float* v, const float* c,
+                              const float* lse, const float* dO, const float* delta, float* dk,
+                              float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
+                              hipStream_t s) {
+  const dim3 grid((unsigned)((L + kF32Rows - 1) / kF32Rows), (unsigned)BH);
+  if (D == 64)
+    hipLaunchKernelGGL(f32_dkv_kernel<64>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dk, dv,
+                       dck, (int)L, scale);
+  else
+    hipLaunchKernelGGL(f32_dkv_kernel<128>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dk, dv,
+                       dck, (int)L, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* c,
+                          const float* o, const float* lse, const float* dO, float* dq, float* dk,
+                          float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
+                          float scale, hipStream_t s) {
+  const size_t R = region_floats(BH, L);
+  float* delta = (float*)ws;
+  float* dcq = delta + R;
+  float* dck = delta + 2 * R;
+  hipError_t e = launch_bwd_delta_f32(dO, o, delta, BH * L, D, s);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dq_f32(q, k, v, c, lse, dO, delta, dq, dcq, delta, BH, L, D, scale, s);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkv_f32(q, k, v, c, lse, dO, delta, dk, dv, dck, BH, L, D, scale, s);
+  if (e != hipSuccess) return e;
+  return launch_rev_cumsum2(dcq, dck, dlog_f, BH, L, s);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,

@@ -112,6 +112,21 @@ hipError_t launch_decode_append(const void* k_new, const void* v_new, const floa
                                 int64_t B, int64_t H, int64_t T, int64_t D, hipStream_t s);
 // Backward, bf16 inputs, fp32 O / gradients: the four steps in order (plan: a skip plan or
 // null).
+// The fp32 backward (vector ALU): the same four steps and workspace as the bf16 path.
+hipError_t launch_bwd_delta_f32(const float* dO, const float* o, float* delta, int64_t rows,
+                                int64_t D, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, const float* c,
+                             const float* lse, const float* dO, const float* delta, float* dq,
+                             float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
+                             float scale, hipStream_t s);
+hipError_t launch_bwd_dkv_f32(const float* q, const float* k, const float* v, const float* c,
+                              const float* lse, const float* dO, const float* delta, float* dk,
+                              float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
+                              hipStream_t s);
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* c,
+                          const float* o, const float* lse, const float* dO, float* dq, float* dk,
+                          float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
+                          float scale, hipStream_t s);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,
                            const float* o, const float* lse, const void* dO, float* dq, float* dk,
                            float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,

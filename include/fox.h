@@ -211,7 +211,8 @@ size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
  *   dq, dk, dv : [B, H, L, D] fp32
  *   dlog_f     : [B, H, L] fp32, the reverse cumulative sum of dc = dc^q + dc^k with
  *                dc^q_i = sum_j dS_ij and dc^k_j = -sum_i dS_ij.
- * Inputs: q, k, v, dO in in_dt (FOX_BF16 only); c and lse as given to / returned by
+ * Inputs: q, k, v, dO in in_dt (FOX_BF16 on the matrix cores; FOX_F32 for the full-fp32 path
+ * on the vector ALU, which takes no skip plan and B*H <= 65535); c and lse as given to / returned by
  * fox_attn_fwd; o is the forward output in fp32 (the row term Delta_i = dO_i . O_i is formed
  * from the fp32 output). workspace: device memory of at least
  * fox_attn_bwd_workspace_bytes(B, H, L, D) bytes, 256-byte aligned, contents ignored on
@@ -228,7 +229,7 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
  * results.
  *
  * Step 1, Delta_i = sum_d dO[i, d] * O[i, d] (the FlashAttention row term that dS needs):
- *   dO : [rows, D] in dO_dt (FOX_BF16);  o : [rows, D] fp32;  delta : [rows] fp32. */
+ *   dO : [rows, D] in dO_dt (FOX_BF16 or FOX_F32);  o : [rows, D] fp32;  delta : [rows] fp32. */
 fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, float* delta,
                               int64_t rows, int64_t D, void* stream);
 

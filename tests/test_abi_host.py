@@ -80,8 +80,8 @@ def test_forward_rejects(lib, kw, status):
 
 @host_only
 @pytest.mark.parametrize("kw,status", [
-    (dict(ws=0), 1), (dict(ws=P + 16), 1), (dict(ws_bytes=100), 1), (dict(in_dt=0), 2),
-    (dict(in_dt=5), 1), (dict(flags=0), 2), (dict(D=32), 1), (dict(o=0), 1),
+    (dict(ws=0), 1), (dict(ws=P + 16), 1), (dict(ws_bytes=100), 1), (dict(in_dt=0, plan=P), 2),
+    (dict(in_dt=0, H=70000), 2), (dict(in_dt=5), 1), (dict(flags=0), 2), (dict(D=32), 1), (dict(o=0), 1),
     (dict(L=(1 << 23) + 1), 1), (dict(plan=P + 64), 1),
 ])
 def test_backward_rejects(lib, kw, status):

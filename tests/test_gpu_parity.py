@@ -364,6 +364,57 @@ def test_head_counts_off_the_xcd_grid(fox, B, H, L, D):
     _check_grads(got, ref)
 
 
+def _run_bwd_f32(fox, case):
+    q, k, v, do = (dev(getattr(case, n), "f32") for n in ("q", "k", "v", "do"))
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    g = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
+    torch.cuda.synchronize()
+    return [host(t) for t in g]
+
+
+def test_backward_config1_fp32(fox):
+    """The full-fp32 backward at workload 1's shape and recipe, to the fp32 bar."""
+    case = fi.make_case(1, 2, 256, 64, "f32", seed=1, gate_mean=3.0, gate_std=1.5, with_do=True)
+    say("bwd config1 fp32")
+    got = _run_bwd_f32(fox, case)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=default_scale(64))[:4]
+    for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), got, ref):
+        check(name, a, b, maxabs=F32_MAXABS, rel_l2=None)
+
+
+@pytest.mark.parametrize("B,H,L,D", [(1, 1, 1, 64), (1, 2, 37, 128), (2, 3, 300, 64),
+                                     (1, 1, 700, 128)])
+def test_backward_fp32_shapes(fox, B, H, L, D):
+    """Ragged and single-position fp32 backward (one and several 16-row blocks and LDS tiles).
+
+    The fp32 bar is set relative to each output's size: d log f is a sum over the sequence and
+    grows with L, and the kernels see c rounded to fp32 (|c| ~ 0.1 L here), so the error of fp32
+    arithmetic is ~1e-6 of the largest value rather than a fixed 1e-5."""
+    case = fi.make_case(B, H, L, D, "f32", seed=900 + L, with_do=True)
+    say(f"bwd fp32 B={B} H={H} L={L} D={D}")
+    got = _run_bwd_f32(fox, case)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=default_scale(D))[:4]
+    for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), got, ref):
+        check(name, a, b, maxabs=F32_MAXABS * max(1.0, float(np.abs(b).max())), rel_l2=1e-5)
+
+
+def test_backward_fp32_steps_match(fox):
+    """The four fp32 step calls give exactly fox_attn_bwd's results."""
+    case = fi.make_case(1, 2, 200, 128, "f32", seed=41, with_do=True)
+    q, k, v, do = (dev(getattr(case, n), "f32") for n in ("q", "k", "v", "do"))
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    whole = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
+    delta = fox.fox_attn_bwd_delta(do, o)
+    dq, dcq, delta = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta, delta_out=delta)
+    dk, dv, dck = fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta)
+    dlf = fox.fox_dlogf_from_dc(dcq, dck)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), whole, (dq, dk, dv, dlf)):
+        assert torch.equal(a, b), f"{name}: step calls differ from fox_attn_bwd"
+
+
 def test_backward_config2_shape(fox):
     """B=4, H=12, L=2048 with config-5 statistics: 6 whole heads compared."""
     case = fi.make_case(4, 12, 2048, 128, "bf16", seed=3, gate="per_head", with_do=True)
