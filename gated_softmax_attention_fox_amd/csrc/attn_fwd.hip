@@ -331,7 +331,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     start_copies(t, (t + 3) & 3, (t + 2) & 3, (t + 3) & 3);
     convert_c(t, (t + 1) & 3, (t + 1) & 1);
     if (active) {
-#pragma unroll
+#pragma unroll 1
       for (int s = 0; s < 2; ++s) {
         const int j = 2 * t + s;
         if (j > j0) pv(kofs(j - 1));
