@@ -129,14 +129,14 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 }
 
 // bf16 x on the matrix cores: z[16 tokens][16 heads] = x[16 tokens][:] . w_f[16 heads][:]^T with
-// v_mfma_f32_16x16x32_bf16, one workgroup per tile of 16 tokens of one batch row (blockIdx.y picks
-// the group of 16 heads); its 4 waves take every 4th 32-column step and their partial sums meet
-// in LDS. Lane l supplies A = x[token l % 16][8 (l / 16) .. +7] of each 32-column step
+// v_mfma_f32_16x16x32_bf16. A workgroup takes NTT tiles of 16 tokens (blockIdx.y picks the group
+// of 16 heads); its 4 waves take every 4th 32-column step, load and split that step's w_f once
+// for all NTT tiles, and their partial sums meet in LDS. Lane l supplies A = x[token l % 16][8 (l / 16) .. +7] of each 32-column step
 // straight from HBM and B = w_f[head l % 16][same columns]; w_f is split into bf16 hi and lo
 // parts (hi = bf16(w), lo = bf16(w - hi)) and both are multiplied, so z keeps about 16
 // significant bits of w on top of exact products and fp32 accumulation. Lane l receives z for
 // head l % 16 and tokens 4 (l / 16) .. +3. Needs d_model % 32 == 0.
-template <bool kBwd, bool kSig>
+template <bool kBwd, bool kSig, int NTT>
 __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict__ x,
                                                         const float* __restrict__ w_f,
                                                         const float* __restrict__ b_f,
@@ -144,22 +144,30 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict
                                                         float* __restrict__ out, int L, int dm,
                                                         int H, int tiles_per_b, int n_tiles) {
   typedef float f32x4v __attribute__((ext_vector_type(4)));
-  __shared__ f32x4v part[4][64];
+  __shared__ f32x4v part[4][NTT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
-  const int b = tile / tiles_per_b, t0 = (tile % tiles_per_b) * 16;
   const int r = lane & 15, grp = lane >> 4;
   const int h0 = blockIdx.y * 16;
-  const int t = t0 + r, hh = h0 + r;
-  const bool tok_ok = t < L, head_ok = hh < H;
-  const bf16_t* xr = x + ((size_t)b * L + (tok_ok ? t : L - 1)) * dm + 8 * grp;
+  const int hh = h0 + r;
+  const bool head_ok = hh < H;
   const float* wr = w_f + (size_t)(head_ok ? hh : 0) * dm + 8 * grp;
-  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  // The workgroup's NTT token tiles (flattened over batch rows; tiles past the end are skipped).
+  const bf16_t* xr[NTT];
+  bool tok_ok[NTT];
+#pragma unroll
+  for (int u = 0; u < NTT; ++u) {
+    const int tile = blockIdx.x * NTT + u;
+    const int tl = tile < n_tiles ? tile : 0;
+    const int b = tl / tiles_per_b, t = (tl % tiles_per_b) * 16 + r;
+    tok_ok[u] = tile < n_tiles && t < L;
+    xr[u] = x + ((size_t)b * L + (t < L ? t : L - 1)) * dm + 8 * grp;
+  }
+  f32x4v acc[NTT];
+#pragma unroll
+  for (int u = 0; u < NTT; ++u) acc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 #pragma unroll 2
   for (int d0 = 32 * wave; d0 < dm; d0 += 128) {
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(xr + d0);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok ? xa : zero4);
     const float4 w0 = *reinterpret_cast<const float4*>(wr + d0);
     const float4 w1 = *reinterpret_cast<const float4*>(wr + d0 + 4);
     const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -171,38 +179,52 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict
       bh[e] = hi;
       bl[e] = (__bf16)(w - (float)hi);
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < NTT; ++u) {  // one load and split of w_f serves all the tiles
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xr[u] + d0);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok[u] ? xa : zero4);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[u], 0, 0, 0);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[u], 0, 0, 0);
+    }
   }
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int u = 0; u < NTT; ++u) part[wave][u][lane] = acc[u];
   __syncthreads();
   if (wave != 0) return;
-  acc = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
   const int hc = h0 + r;  // the head of this lane's output column
   if (hc >= H) return;
   const float bias = b_f ? b_f[hc] : 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tt = t0 + 4 * grp + j;
-    if (tt >= L) break;
-    const float z = acc[j] + bias;
-    if constexpr (kBwd) {
-      const float g = dlog_f[((size_t)b * H + hc) * L + tt];
-      out[((size_t)b * L + tt) * H + hc] =
-          kSig ? g * sigmoid(z) / (1.0f + expf(z)) : g / (1.0f + expf(z));
-    } else {
-      out[((size_t)b * H + hc) * L + tt] = kSig ? sigmoid(z) : log_sigmoid(z);
+  for (int u = 0; u < NTT; ++u) {
+    const int tile = blockIdx.x * NTT + u;
+    if (tile >= n_tiles) break;
+    const int b = tile / tiles_per_b, t0 = (tile % tiles_per_b) * 16;
+    const f32x4v z4 = (part[0][u][lane] + part[1][u][lane]) + (part[2][u][lane] + part[3][u][lane]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = t0 + 4 * grp + j;
+      if (tt >= L) break;
+      const float z = z4[j] + bias;
+      if constexpr (kBwd) {
+        const float g = dlog_f[((size_t)b * H + hc) * L + tt];
+        out[((size_t)b * L + tt) * H + hc] =
+            kSig ? g * sigmoid(z) / (1.0f + expf(z)) : g / (1.0f + expf(z));
+      } else {
+        out[((size_t)b * H + hc) * L + tt] = kSig ? sigmoid(z) : log_sigmoid(z);
+      }
     }
   }
 }
+
+constexpr int kGateTiles = 2;  // token tiles per workgroup of the matrix-core gate
 
 template <bool kBwd, bool kSig>
 void go_gate_mfma(const void* x, const float* w_f, const float* b_f, const float* dlog_f,
                   float* out, int64_t B, int64_t L, int64_t d_model, int64_t H, hipStream_t s) {
   const int tiles_per_b = (int)((L + 15) / 16);
   const int64_t n_tiles = B * tiles_per_b;
-  const dim3 grid((unsigned)n_tiles, (unsigned)((H + 15) / 16));
-  hipLaunchKernelGGL((gate_mfma_kernel<kBwd, kSig>), grid, dim3(256), 0, s,
+  const dim3 grid((unsigned)((n_tiles + kGateTiles - 1) / kGateTiles), (unsigned)((H + 15) / 16));
+  hipLaunchKernelGGL((gate_mfma_kernel<kBwd, kSig, kGateTiles>), grid, dim3(256), 0, s,
                      static_cast<const bf16_t*>(x), w_f, b_f, dlog_f, out, (int)L, (int)d_model,
                      (int)H, tiles_per_b, (int)n_tiles);
 }
