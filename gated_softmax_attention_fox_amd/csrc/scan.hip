@@ -6,24 +6,25 @@
 // Reverse: d log f_l = sum_{t>=l} dc_t, the adjoint of that sum, which turns the gradient of c
 // into the gradient of log f (same section, backward pass).
 //
-// One 256-thread workgroup per row, in tiles of 16384 elements staged through LDS. Each tile is
-// loaded with coalesced reads (in fp64; the reverse sum adds its two inputs exactly there) into
-// 256 contiguous segments of 64, padded by one slot so that the threads' segment walks do not
-// collide on a bank. Each thread sums its segment in fp64, the workgroup scans the 256 segment
-// totals with 64-wide wavefront shuffles plus one LDS step across the 4 waves, each thread
-// rewrites its segment with the running fp64 sum, and the tile is stored with coalesced writes,
-// rounded once to fp32; the tile total carries into the next tile. fp64 keeps c_i - c_j free
-// of accumulated rounding: the only error left is the single fp32 rounding of each c_i.
+// One 1024-thread workgroup per row, in tiles of 16384 elements. Each thread owns 16 consecutive
+// positions of the scan order and keeps them in registers as fp64 (the reverse sum adds its two
+// inputs exactly there); a row whose length is a multiple of 4 moves them as four 16-byte loads
+// and stores per thread. Each thread sums its 16 values, the workgroup scans the 1024 thread
+// totals with 64-wide wavefront shuffles plus one LDS step across the 16 waves, each thread
+// rewrites its values with the running fp64 sum, and the result is rounded once to fp32; the tile
+// total carries into the next tile. fp64 keeps c_i - c_j free of accumulated rounding: the only
+// error left is the single fp32 rounding of each c_i. The rows are short (a few hundred KB), so
+// the time is latency: the dependent chain per thread is 16 adds, not a full segment walk.
 #include "fox_device.h"
 #include "fox_launch.h"
 
 namespace fox {
 namespace {
 
-constexpr int kScanThreads = 256;
-constexpr int kScanPer = 64;                          // elements per thread segment
-constexpr int kScanTile = kScanThreads * kScanPer;    // elements per LDS tile
-constexpr int kScanPad = kScanPer + 1;                // LDS stride of a segment (bank spread)
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;                        // consecutive scan positions per thread
+constexpr int kScanTile = kScanThreads * kScanPer;  // positions per pass of the workgroup
+constexpr int kScanWaves = kScanThreads / 64;
 
 template <bool kReverse>
 __device__ __forceinline__ double scan_load(const float* __restrict__ a, const float* __restrict__ b,
@@ -35,59 +36,86 @@ __device__ __forceinline__ double scan_load(const float* __restrict__ a, const f
   return (double)a[i];
 }
 
+// Forward: out[i] = sum_{l<=i} a[l]. Reverse: out[l] = sum_{t>=l} (a[t] + b[t]). Scan position
+// k is memory position k (forward) or L-1-k (reverse).
 template <bool kReverse>
 __global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(const float* __restrict__ a,
                                                                  const float* __restrict__ b,
                                                                  float* __restrict__ out,
                                                                  int64_t L) {
-  __shared__ double tile[kScanThreads * kScanPad];
-  __shared__ double wave_tot[kScanThreads / 64];
+  __shared__ double wave_tot[2][kScanWaves];  // two copies: a pass never waits for the last reads
   const int64_t row = blockIdx.x;
   a += row * L;
   if (kReverse) b += row * L;
   out += row * L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // 16-byte moves where every row pointer is 16-byte aligned (then so is each thread's block)
+  const uintptr_t align = (uintptr_t)a | (uintptr_t)out | (kReverse ? (uintptr_t)b : (uintptr_t)0);
+  const bool vec = (L & 3) == 0 && (align & 15) == 0;
   double carry = 0.0;
-  for (int64_t t0 = 0; t0 < L; t0 += kScanTile) {
-    const int n = L - t0 < kScanTile ? (int)(L - t0) : kScanTile;
-    // coalesced loads in scan order (i = t0 + k), scattered into padded segments; unrolled so
-    // that many loads are in flight at once (the inputs usually come cold from HBM)
-#pragma unroll 16
-    for (int k = tid; k < n; k += kScanThreads)
-      tile[(k / kScanPer) * kScanPad + k % kScanPer] = scan_load<kReverse>(a, b, L, t0 + k);
-    __syncthreads();
-    const int cnt = n - tid * kScanPer < 0 ? 0 : (n - tid * kScanPer < kScanPer ? n - tid * kScanPer : kScanPer);
-    double* seg = tile + tid * kScanPad;
+  int par = 0;
+  for (int64_t t0 = 0; t0 < L; t0 += kScanTile, par ^= 1) {
+    const int64_t k0 = t0 + (int64_t)tid * kScanPer;  // this thread's first scan position
+    const int cnt = L - k0 <= 0 ? 0 : (L - k0 < kScanPer ? (int)(L - k0) : kScanPer);
+    const bool full = vec && cnt == kScanPer;
+    // memory position of this thread's block (the lowest address it touches when full)
+    const int64_t p0 = kReverse ? L - kScanPer - k0 : k0;
+    double v[kScanPer];
+    if (full) {
+#pragma unroll
+      for (int g = 0; g < kScanPer / 4; ++g) {
+        const float4 x = *reinterpret_cast<const float4*>(a + p0 + 4 * g);
+        float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kReverse) y = *reinterpret_cast<const float4*>(b + p0 + 4 * g);
+        const double m[4] = {(double)x.x + (double)y.x, (double)x.y + (double)y.y,
+                             (double)x.z + (double)y.z, (double)x.w + (double)y.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[kReverse ? kScanPer - 1 - (4 * g + e) : 4 * g + e] = m[e];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) v[j] = j < cnt ? scan_load<kReverse>(a, b, L, k0 + j) : 0.0;
+    }
     double tot = 0.0;
-    for (int j = 0; j < cnt; ++j) tot += seg[j];
-    // inclusive scan of segment totals inside the wave, then across the 4 waves
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) tot += v[j];
+    // inclusive scan of the thread totals inside the wave, then across the waves
     double x = tot;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double y = __shfl_up(x, off, 64);
       if (lane >= off) x += y;
     }
-    if (lane == 63) wave_tot[wave] = x;
+    if (lane == 63) wave_tot[par][wave] = x;
     __syncthreads();
     double before = carry, tile_tot = 0.0;
 #pragma unroll
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-      if (w < wave) before += wave_tot[w];
-      tile_tot += wave_tot[w];
+    for (int w = 0; w < kScanWaves; ++w) {
+      const double t = wave_tot[par][w];
+      if (w < wave) before += t;
+      tile_tot += t;
     }
-    double run = before + x - tot;  // exclusive prefix of this thread's segment
-    for (int j = 0; j < cnt; ++j) {
-      run += seg[j];
-      seg[j] = run;
+    double run = before + x - tot;  // exclusive prefix of this thread's block
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      run += v[j];
+      v[j] = run;
     }
     carry += tile_tot;
-    __syncthreads();
-#pragma unroll 16
-    for (int k = tid; k < n; k += kScanThreads) {
-      const int64_t i = t0 + k;
-      out[kReverse ? (L - 1 - i) : i] = (float)tile[(k / kScanPer) * kScanPad + k % kScanPer];
+    if (full) {
+#pragma unroll
+      for (int g = 0; g < kScanPer / 4; ++g) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = (float)v[kReverse ? kScanPer - 1 - (4 * g + e) : 4 * g + e];
+        *reinterpret_cast<float4*>(out + p0 + 4 * g) = make_float4(r[0], r[1], r[2], r[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) {
+        if (j < cnt) out[kReverse ? (L - 1 - (k0 + j)) : (k0 + j)] = (float)v[j];
+      }
     }
-    __syncthreads();  // the next tile reuses the LDS
   }
 }
 
