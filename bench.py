@@ -3,9 +3,9 @@
 Workload (the one the headline metric is quoted on): B=1, H=12, L=16384, D=128, bf16 q/k/v/dO,
 fp32 log forget gates drawn per head as log sigmoid(z), z ~ N(mu_h, 1), mu_h ~ U[1, 6].
 A step runs, on one HIP stream:
-    fox_logf_cumsum -> fox_attn_fwd (fp32 O + LSE) -> fox_attn_bwd_delta -> fox_attn_bwd_dq
-    -> fox_attn_bwd_dkv -> fox_dlogf_from_dc
-(the four backward calls are fox_attn_bwd's steps). Inputs are resident in HBM before timing.
+    fox_logf_cumsum -> fox_attn_fwd (fp32 O + LSE) -> fox_attn_bwd_dq (row term formed from O
+    inside) -> fox_attn_bwd_dkv -> fox_dlogf_from_dc
+(the backward calls are fox_attn_bwd's launches). Inputs are resident in HBM before timing.
 
 Prints ONE JSON line. value = causal fwd+bwd TFLOP/s with the FlashAttention convention:
 fwd = 4*B*H*D*L^2/2 FLOPs (two causal contractions), bwd = 2.5 x fwd (five contractions).
@@ -42,7 +42,6 @@ KERNEL_SOURCES = {
     "fwd": ["attn_fwd.hip", "fox_device.h"],
     "dq": ["attn_bwd.hip", "fox_device.h"],
     "dkv": ["attn_bwd.hip", "fox_device.h"],
-    "delta": ["attn_bwd.hip"],
     "scan": ["scan.hip"],
     "dlogf": ["scan.hip"],
 }
@@ -168,7 +167,7 @@ def main():
     log_f = up(case.log_f, "f32")
     torch.cuda.synchronize()
 
-    names = ["scan", "fwd", "delta", "dq", "dkv", "dlogf"]
+    names = ["scan", "fwd", "dq", "dkv", "dlogf"]
     stream = torch.cuda.current_stream(dev)  # the library launches on this stream
 
     def step(events, skip=False):
@@ -185,9 +184,8 @@ def main():
         plan = run("plan", lambda: fox.fox_attn_skip_plan(q, k, c)) if skip else None
         o, lse = run("fwd", lambda: fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32,
                                                      skip_plan=plan))
-        delta = run("delta", lambda: fox.fox_attn_bwd_delta(do, o))
-        dq, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta,
-                                                                delta_out=delta, skip_plan=plan))
+        dq, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, None, o=o,
+                                                                skip_plan=plan))
         dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta,
                                                               skip_plan=plan))
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
@@ -218,7 +216,7 @@ def main():
     ach = kernel_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
     fwd_tf = kernel_flops["fwd"] / (kern_ms["fwd"] * 1e-3) / 1e12
     fwd_path_tf = fwd_flops / ((kern_ms["fwd"] + kern_ms["scan"]) * 1e-3) / 1e12
-    bwd_ms = sum(kern_ms[n] for n in ("delta", "dq", "dkv", "dlogf"))
+    bwd_ms = sum(kern_ms[n] for n in ("dq", "dkv", "dlogf"))
 
     out = {
         "metric": METRIC,
@@ -443,7 +441,7 @@ def pro_step(args, torch, fi, fox, dev):
                                                                     dtype=np.float32)), "bf16")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    names = ["gate", "scan", "qnorm", "knorm", "fwd", "delta", "dq", "dkv", "dlogf", "qnorm_bwd",
+    names = ["gate", "scan", "qnorm", "knorm", "fwd", "dq", "dkv", "dlogf", "qnorm_bwd",
              "knorm_bwd", "gate_bwd"]
 
     def step(events, skip=False):
@@ -463,9 +461,8 @@ def pro_step(args, torch, fi, fox, dev):
         plan = run("plan", lambda: fox.fox_attn_skip_plan(qn, kn, c)) if skip else None
         o, lse = run("fwd", lambda: fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32,
                                                      skip_plan=plan))
-        delta = run("delta", lambda: fox.fox_attn_bwd_delta(do, o))
-        dqn, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(qn, kn, v, c, lse, do, delta,
-                                                                 delta_out=delta, skip_plan=plan))
+        dqn, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(qn, kn, v, c, lse, do, None, o=o,
+                                                                 skip_plan=plan))
         dkn, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(qn, kn, v, c, lse, do, delta,
                                                                skip_plan=plan))
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))

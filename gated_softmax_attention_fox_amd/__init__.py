@@ -14,6 +14,7 @@ C entry points (include/fox.h) and their wrappers:
     fox_attn_bwd(q, k, v, c, o, lse, dO, scale, skip_plan=None)     -> (dq, dk, dv, dlog_f)
     fox_attn_bwd_delta(dO, o)                      -> delta
     fox_attn_bwd_dq(q, k, v, c, lse, dO, delta)    -> (dq, dc_q, delta_refined)
+    fox_attn_bwd_dq(q, k, v, c, lse, dO, None, o=o) -> the same, with Delta formed from o inside
     fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta_refined) -> (dk, dv, dc_k)
     fox_dlogf_from_dc(dc_q, dc_k)                  -> dlog_f
     fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype, scale) -> (o, lse)
@@ -83,8 +84,8 @@ _SIGS = {
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_attn_bwd_dq": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
-                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
-                                       _c_f32, _c_u32, _c_vp, _c_vp]),
+                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
+                                       _c_i64, _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_dlogf_from_dc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_shift_gate": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                                       _c_i64, _c_vp]),
@@ -401,7 +402,7 @@ def _bwd_inputs(q, k, v, c, lse, dO, delta):
     ptrs = (_dev(q, "q", (torch.bfloat16, torch.float32)), _dev(k, "k", (q.dtype,)),
             _dev(v, "v", (q.dtype,)), _dev(c, "c", (torch.float32,), 3),
             _dev(lse, "lse", (torch.float32,), 3), _dev(dO, "dO", (q.dtype,), 4),
-            _dev(delta, "delta", (torch.float32,), 3))
+            None if delta is None else _dev(delta, "delta", (torch.float32,), 3))
     return (B, H, L, D), ptrs
 
 
@@ -422,19 +423,28 @@ def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None,
 
 
 def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
-                    delta_out: torch.Tensor | None = None, skip_plan: torch.Tensor | None = None):
+                    delta_out: torch.Tensor | None = None, skip_plan: torch.Tensor | None = None,
+                    o: torch.Tensor | None = None):
     """(dQ, dc_q, refined delta) of the query-stationary backward step (run before dkv).
 
-    delta_out may be `delta` itself to refine it in place."""
+    delta_out may be `delta` itself to refine it in place. With delta=None the step forms the
+    row term from o (the fp32 forward output) itself, bit-identical to fox_attn_bwd_delta."""
     lib = load_library()
     (B, H, L, D), (pq, pk, pv, pc, pl, pdo, pdl) = _bwd_inputs(q, k, v, c, lse, dO, delta)
+    po = None
+    if delta is None:
+        if o is None:
+            raise ValueError("fox_attn_bwd_dq needs delta or o")
+        po = _dev(o, "o", (torch.float32,), 4)
+        if tuple(o.shape) != (B, H, L, D):
+            raise ValueError(f"o must have shape {(B, H, L, D)}, got {tuple(o.shape)}")
     dq = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
     dcq = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     if delta_out is None:
-        delta_out = torch.empty_like(delta)
+        delta_out = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     pdn = _dev(delta_out, "delta_out", (torch.float32,), 3)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    _check(lib.fox_attn_bwd_dq(pq, pk, pv, _code(q.dtype), pc, pl, pdo, pdl,
+    _check(lib.fox_attn_bwd_dq(pq, pk, pv, _code(q.dtype), pc, pl, pdo, po, pdl,
                                ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dcq.data_ptr()), pdn,
                                B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan), _stream(q)),
            "fox_attn_bwd_dq")

@@ -311,8 +311,7 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
 
 namespace {
 fox_status check_bwd_common(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                            const float* c, const float* lse, const void* dO, const float* delta,
-                            int64_t B, int64_t H, int64_t L, int64_t D, float scale,
+                            const float* c, const float* lse, const void* dO, int64_t B, int64_t H, int64_t L, int64_t D, float scale,
                             uint32_t flags) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k);
@@ -320,7 +319,6 @@ fox_status check_bwd_common(const void* q, const void* k, const void* v, fox_dty
   FOX_REQUIRE_PTR(c);
   FOX_REQUIRE_PTR(lse);
   FOX_REQUIRE_PTR(dO);
-  FOX_REQUIRE_PTR(delta);
   fox_status st = check_bhld(B, H, L, D);
   if (st != FOX_OK) return st;
   FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
@@ -355,8 +353,9 @@ fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dty
                             float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
                             int64_t D, float scale, uint32_t flags, const void* skip_plan,
                             void* stream) {
-  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, delta, B, H, L, D, scale, flags);
+  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, B, H, L, D, scale, flags);
   if (st != FOX_OK) return st;
+  FOX_REQUIRE_PTR(delta);
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
   FOX_REQUIRE_PTR(dk);
@@ -376,27 +375,38 @@ fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dty
 }
 
 fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                           const float* c, const float* lse, const void* dO, const float* delta,
-                           float* dq, float* dc_q, float* delta_out, int64_t B, int64_t H,
-                           int64_t L, int64_t D, float scale, uint32_t flags,
-                           const void* skip_plan, void* stream) {
-  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, delta, B, H, L, D, scale, flags);
+                           const float* c, const float* lse, const void* dO, const float* o,
+                           const float* delta, float* dq, float* dc_q, float* delta_out,
+                           int64_t B, int64_t H, int64_t L, int64_t D, float scale,
+                           uint32_t flags, const void* skip_plan, void* stream) {
+  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, B, H, L, D, scale, flags);
   if (st != FOX_OK) return st;
+  FOX_REQUIRE(delta != nullptr || o != nullptr, "one of delta and o must be given");
+  if (delta) FOX_REQUIRE_PTR(delta);
+  else FOX_REQUIRE_PTR(o);
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
   FOX_REQUIRE_PTR(dq);
   FOX_REQUIRE_PTR(dc_q);
   FOX_REQUIRE_PTR(delta_out);
+  const float* o_used = delta ? nullptr : o;  // a given delta wins; o is then not read
   if (in_dt == FOX_F32) {
     if (skip_plan)
       return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+    if (o_used) {  // the vector-ALU path keeps the row term as its own launch, into delta_out
+      const hipError_t e = fox::launch_bwd_delta_f32((const float*)dO, o_used, delta_out, B * H * L,
+                                                     D, (hipStream_t)stream);
+      if (e != hipSuccess) return launched(e, "fox_attn_bwd_dq");
+      delta = delta_out;
+    }
     return launched(fox::launch_bwd_dq_f32((const float*)q, (const float*)k, (const float*)v, c, lse,
                                            (const float*)dO, delta, dq, dc_q, delta_out, B * H, L, D,
                                            scale, (hipStream_t)stream),
                     "fox_attn_bwd_dq");
   }
-  return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dc_q, delta_out, B * H, L, D,
-                                     scale, fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
+  return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, o_used, dq, dc_q, delta_out,
+                                     B * H, L, D, scale, fox::skip_args(skip_plan, B * H, L),
+                                     (hipStream_t)stream),
                   "fox_attn_bwd_dq");
 }
 

@@ -7,7 +7,9 @@
 // partial vectors dc^q and dc^k are summed and a reverse cumulative sum gives d log f. The pages
 // note the work may be split over two kernels; here it is split so that no output needs atomics:
 //
-//   1. delta_kernel : Delta_i = dO_i . O_i from the fp32 forward output.
+//   1. delta_kernel : Delta_i = dO_i . O_i from the fp32 forward output. Given O instead of
+//                     Delta, dq_pipe_kernel forms the same values (same bits) in its prologue,
+//                     which saves the launch and a second read of dO.
 //   2. dq_pipe_kernel  : query-stationary. A workgroup owns 256 queries (32 per wave) and walks
 //                        the key tiles from its diagonal backwards: S^T = K Q^T, P,
 //                        dP^T = V dO^T, dS = P (dP - Delta_i), dQ^T += K^T dS^T. It also sums P
@@ -446,9 +448,9 @@ template <int D, int NB>
 __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB))) void dq_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
-    const float* Delta, float* __restrict__ dQ, float* __restrict__ dcq_out, float* delta_out,
-    const int32_t* __restrict__ q_skip, const int32_t* __restrict__ q_order, int L, int BH,
-    int n_qt, float sl2e, float scale) {
+    const float* Delta, const float* __restrict__ O, float* __restrict__ dQ,
+    float* __restrict__ dcq_out, float* delta_out, const int32_t* __restrict__ q_skip,
+    const int32_t* __restrict__ q_order, int L, int BH, int n_qt, float sl2e, float scale) {
   constexpr int NW = 8 / NB, BM = 256, NT = NW * 64, BN = 64;
   constexpr int TILE = BN * D;
   constexpr int CPR = D / 8;
@@ -521,7 +523,36 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
     }
     // rows past the end get P = 0 through an infinite row offset
     mrow[b] = qok[b] ? (LSE[(size_t)bh * L + qi[b]] - (C[qi[b]] - c_ref)) * kLog2e : INFINITY;
-    dl[b] = qok[b] ? Delta[(size_t)bh * L + qi[b]] : 0.f;
+    if (O) {
+      // Delta_i = dO_i . O_i from the fp32 output, summed in delta_kernel's order: each group of
+      // eight consecutive elements in order, then the D/8 groups as a balanced pairwise tree
+      // (group 2c + h is this lane's chunk c; the partner half sits in lane ^ 32). The fused
+      // and the separate row term therefore agree bit for bit.
+      float g[D / 16];
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        float acc = 0.f;
+        if (qok[b]) {
+          const float* orow = O + base + (size_t)qi[b] * D + 16 * c + 8 * h;
+          const float4 x0 = *reinterpret_cast<const float4*>(orow);
+          const float4 x1 = *reinterpret_cast<const float4*>(orow + 4);
+          const float o8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf((float)dof[b][c][e], o8[e], acc);
+        }
+        g[c] = acc;
+      }
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) g[c] += __shfl_xor(g[c], 32, 64);
+#pragma unroll
+      for (int w = 1; w < D / 16; w <<= 1) {
+#pragma unroll
+        for (int c = 0; c < D / 16; c += 2 * w) g[c] += g[c + w];
+      }
+      dl[b] = g[0];  // 0 for rows past the end
+    } else {
+      dl[b] = qok[b] ? Delta[(size_t)bh * L + qi[b]] : 0.f;
+    }
     dcq[b] = 0.f;
     psum[b] = 0.f;
 #pragma unroll
@@ -922,13 +953,14 @@ void go_dkv(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, c
 
 template <int D>
 void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
-           const bf16_t* dO, const float* delta, float* dq, float* dcq, float* delta_out,
-           int64_t BH, int64_t L, float scale, const SkipArgs& skip, hipStream_t s) {
+           const bf16_t* dO, const float* delta, const float* o, float* dq, float* dcq,
+           float* delta_out, int64_t BH, int64_t L, float scale, const SkipArgs& skip,
+           hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
   // one 32-query block per wave, 8 waves (two per SIMD): measured 18% faster than 4 waves with
   // two blocks each, whose halved LDS traffic does not make up for the lost latency hiding
   hipLaunchKernelGGL((dq_pipe_kernel<D, 1>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s, q, k, v,
-                     dO, c, lse, delta, dq, dcq, delta_out, skip.q_skip, skip.q_order, (int)L,
+                     dO, c, lse, delta, o, dq, dcq, delta_out, skip.q_skip, skip.q_order, (int)L,
                      (int)BH, n_qt, scale * kLog2e, scale);
 }
 
@@ -957,15 +989,15 @@ hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const flo
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* c,
-                         const float* lse, const void* dO, const float* delta, float* dq,
-                         float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
-                         float scale, const SkipArgs& skip, hipStream_t s) {
+                         const float* lse, const void* dO, const float* delta, const float* o,
+                         float* dq, float* dcq, float* delta_out, int64_t BH, int64_t L,
+                         int64_t D, float scale, const SkipArgs& skip, hipStream_t s) {
   if (D == 64)
     go_dq<64>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-              delta, dq, dcq, delta_out, BH, L, scale, skip, s);
+              delta, o, dq, dcq, delta_out, BH, L, scale, skip, s);
   else
     go_dq<128>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-               delta, dq, dcq, delta_out, BH, L, scale, skip, s);
+               delta, o, dq, dcq, delta_out, BH, L, scale, skip, s);
   return hipGetLastError();
 }
 
@@ -1031,10 +1063,10 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const fl
   float* delta = (float*)ws;
   float* dcq = delta + R;
   float* dck = delta + 2 * R;
-  hipError_t e = launch_bwd_delta(dO, o, delta, BH * L, D, s);
-  if (e != hipSuccess) return e;
-  // the query-stationary step refines delta in place; the key-stationary step reads the result
-  e = launch_bwd_dq(q, k, v, c, lse, dO, delta, dq, dcq, delta, BH, L, D, scale, skip, s);
+  // the query-stationary step forms the row term from O itself and writes the refined value;
+  // the key-stationary step reads the result
+  hipError_t e = launch_bwd_dq(q, k, v, c, lse, dO, nullptr, o, dq, dcq, delta, BH, L, D, scale,
+                               skip, s);
   if (e != hipSuccess) return e;
   e = launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dck, BH, L, D, scale, skip, s);
   if (e != hipSuccess) return e;

@@ -83,7 +83,8 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, const 
 // Workspace bytes of the bf16 backward.
 size_t bwd_workspace_bytes(int64_t BH, int64_t L);
 // Backward steps: Delta = rowsum(dO * O); query-stationary dQ, dc^q and the refined Delta
-// (delta_out may equal delta); key-stationary dK, dV, dc^k from the refined Delta.
+// (delta_out may equal delta; with delta null the step forms Delta from o itself, bit-identical
+// to launch_bwd_delta); key-stationary dK, dV, dc^k from the refined Delta.
 hipError_t launch_bwd_delta(const void* dO, const float* o, float* delta, int64_t rows, int64_t D,
                             hipStream_t s);
 hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const float* c,
@@ -91,9 +92,9 @@ hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const flo
                           float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
                           const SkipArgs& skip, hipStream_t s);
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* c,
-                         const float* lse, const void* dO, const float* delta, float* dq,
-                         float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
-                         float scale, const SkipArgs& skip, hipStream_t s);
+                         const float* lse, const void* dO, const float* delta, const float* o,
+                         float* dq, float* dcq, float* delta_out, int64_t BH, int64_t L,
+                         int64_t D, float scale, const SkipArgs& skip, hipStream_t s);
 // Single-token decode against a KV cache [BH, T, D] (bf16) with c [BH, T] and per-sequence
 // lengths lens [B]: o [BH, D] (bf16 or fp32) and lse [BH]; workspace decode_workspace_bytes.
 // k_norms [BH, ceil(T / 64)] (largest key norm per 64 positions) or null: with it, chunks

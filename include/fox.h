@@ -226,7 +226,8 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
 
 /* The four steps of fox_attn_bwd as separate calls, for callers that schedule them
  * themselves. Running them in this order with the same arguments gives exactly fox_attn_bwd's
- * results.
+ * results. fox_attn_bwd itself runs step 1 inside step 2 (step 2 with delta = NULL and o
+ * given), which gives the same bits with one launch and one read of dO fewer.
  *
  * Step 1, Delta_i = sum_d dO[i, d] * O[i, d] (the FlashAttention row term that dS needs):
  *   dO : [rows, D] in dO_dt (FOX_BF16 or FOX_F32);  o : [rows, D] fp32;  delta : [rows] fp32. */
@@ -237,13 +238,17 @@ fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, f
  * delta_out ([B,H,L] fp32, may equal delta): the row term refined so that each row of dS sums to
  * zero under the P and dP this library recomputes. The forward rounds P to bf16 before the PV
  * product, so dO . O matches sum_j P_ij dP_ij only to ~1e-3 relative; d log f sums that
- * residual over every row that attends across a position, hence the refinement. skip_plan as
+ * residual over every row that attends across a position, hence the refinement.
+ * The row term comes from delta (step 1's output) when it is not NULL, and o is then not read.
+ * With delta = NULL, o ([B,H,L,D] fp32, the forward output) must be given and the step forms
+ * Delta_i = dO_i . O_i itself, bit-identical to step 1 (the bf16 path in the same kernel; the
+ * fp32 path as a launch of step 1 into delta_out first). Both NULL: FOX_E_INVALID. skip_plan as
  * for fox_attn_bwd. */
 fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                           const float* c, const float* lse, const void* dO, const float* delta,
-                           float* dq, float* dc_q, float* delta_out, int64_t B, int64_t H,
-                           int64_t L, int64_t D, float scale, uint32_t flags,
-                           const void* skip_plan, void* stream);
+                           const float* c, const float* lse, const void* dO, const float* o,
+                           const float* delta, float* dq, float* dc_q, float* delta_out,
+                           int64_t B, int64_t H, int64_t L, int64_t D, float scale,
+                           uint32_t flags, const void* skip_plan, void* stream);
 
 /* Step 3, key-stationary: dk, dv ([B,H,L,D] fp32) and dc_k[j] = -sum_i dS_ij ([B,H,L] fp32).
  * delta must be step 2's delta_out; the other inputs (skip_plan too) as for fox_attn_bwd. */

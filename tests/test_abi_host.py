@@ -92,6 +92,22 @@ def test_backward_rejects(lib, kw, status):
         assert "workspace too small" in msg
 
 
+def _bwd_dq(lib, o=P, delta=P, in_dt=1, plan=None):
+    return lib.fox_attn_bwd_dq(P, P, P, in_dt, P, P, P, o, delta, P, P, P, 1, 2, 64, 128, 0.1, 1,
+                               plan, None)
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=0, delta=0), 1),      # neither the row term nor the output it comes from
+    (dict(o=P + 4, delta=0), 1),  # o is read with 16-byte loads
+    (dict(delta=P + 4), 1), (dict(in_dt=0, plan=P), 2),
+])
+def test_backward_dq_step_rejects(lib, kw, status):
+    assert _bwd_dq(lib, **kw) == status
+    assert lib.fox_last_error().decode() != ""
+
+
 @host_only
 def test_scan_gate_norm_reject(lib):
     assert lib.fox_logf_cumsum(0, P, 1, 8, None) == 1

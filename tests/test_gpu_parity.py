@@ -415,6 +415,36 @@ def test_backward_fp32_steps_match(fox):
         assert torch.equal(a, b), f"{name}: step calls differ from fox_attn_bwd"
 
 
+@pytest.mark.parametrize("B,H,L,D,dtype,skip", [
+    (1, 2, 300, 128, "bf16", False), (2, 3, 1000, 64, "bf16", False), (1, 1, 1, 64, "bf16", False),
+    (1, 2, 4097, 128, "bf16", True), (1, 2, 200, 128, "f32", False), (1, 3, 77, 64, "f32", False)])
+def test_backward_row_term_from_o(fox, B, H, L, D, dtype, skip):
+    """The query-stationary step forming Delta from O itself (delta = None) returns the same bits
+    as the separate row-term call followed by the step, and fox_attn_bwd, which runs it that
+    way, the same bits as the four step calls."""
+    say(f"row term from O B={B} H={H} L={L} D={D} {dtype} skip={skip}")
+    if skip:
+        case = _skip_case(L, D, "reset", H=H, seed=L + 7, B=B)
+        q, k, v, c, plan = _plan_and_inputs(fox, case)
+    else:
+        case = fi.make_case(B, H, L, D, dtype, seed=500 + L, with_do=True, gate="per_head")
+        q, k, v = (dev(getattr(case, n), dtype) for n in ("q", "k", "v"))
+        c, plan = fox.fox_logf_cumsum(dev(case.log_f, "f32")), None
+    do = dev(case.do, dtype)
+    o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    delta = fox.fox_attn_bwd_delta(do, o)
+    sep = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta, skip_plan=plan)
+    fused = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, None, o=o, skip_plan=plan)
+    dk, dv, dck = fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, sep[2], skip_plan=plan)
+    dlf = fox.fox_dlogf_from_dc(sep[1], dck)
+    whole = fox.fox_attn_bwd(q, k, v, c, o, lse, do, skip_plan=plan)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dc_q", "delta_out"), sep, fused):
+        assert torch.equal(a, b), f"{name}: fused row term differs from the separate one"
+    for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), whole, (sep[0], dk, dv, dlf)):
+        assert torch.equal(a, b), f"{name}: fox_attn_bwd differs from the step calls"
+
+
 def test_backward_config2_shape(fox):
     """B=4, H=12, L=2048 with config-5 statistics: 6 whole heads compared."""
     case = fi.make_case(4, 12, 2048, 128, "bf16", seed=3, gate="per_head", with_do=True)
