@@ -23,7 +23,7 @@ Two independent tiers compute attention:
       vectorised over blocks of query rows (the blocking only groups rows; every row still sees
       all of its keys at once).
 
-Conventions (readings of the pages, each listed in the design doc): positions are 0-indexed and
+Conventions (readings taken where the pages are silent or ambiguous): positions are 0-indexed and
 c is the inclusive prefix sum; the softmax scale multiplies q.k only, never the bias; the
 causal mask keeps j <= i (D_ii = 0); LSE is the natural-log log-sum-exp of the biased, scaled
 logits.
