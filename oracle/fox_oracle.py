@@ -398,16 +398,31 @@ def _group_max_norms(x, g):
     return n.reshape(n.shape[:-1] + (-1, g)).max(axis=-1)
 
 
+def _group_extrema(c, g):
+    """Smallest and largest value of c in every g-position group, [..., L] -> two
+    [..., ceil(L / g)] arrays."""
+    c = _f64(c)
+    pad = (-c.shape[-1]) % g
+    lo = np.concatenate([c, np.full(c.shape[:-1] + (pad,), np.inf)], axis=-1)
+    hi = np.concatenate([c, np.full(c.shape[:-1] + (pad,), -np.inf)], axis=-1)
+    shape = c.shape[:-1] + (-1, g)
+    return lo.reshape(shape).min(axis=-1), hi.reshape(shape).max(axis=-1)
+
+
 def skip_bounds(q, k, c, *, scale, g=64):
     """Upper bounds, in log2 units, on the weight of every key of a key tile for every query of
     a query tile, relative to the query's diagonal logit scale q_i.k_i.
 
     For a query i and an earlier key j the logit difference is
         scale q_i.(k_j - k_i) - (c_j - c_i) <= scale |q_i| (|k_j| + |k_i|) - (c_j - c_i)
-    (Cauchy-Schwarz), and over a query range starting at qa and a key range ending at kb < qa,
-    c_j - c_i >= c_kb - c_qa because c does not increase. With Qmax, Kmax and Kdiag the largest
-    |q_i|, |k_j| and |k_i| of the ranges (taken over g-row groups):
-        bound = log2(e) (scale Qmax (Kmax + Kdiag) - (c_kb - c_qa)).
+    (Cauchy-Schwarz), and over a query range and an earlier key range
+    c_j - c_i >= Cmin_keys - Cmax_queries, the smallest c of the key range less the largest c
+    of the query range. With Qmax, Kmax and Kdiag the largest |q_i|, |k_j| and |k_i| of the
+    ranges (taken over g-row groups):
+        bound = log2(e) (scale Qmax (Kmax + Kdiag) - (Cmin_keys - Cmax_queries)).
+    The forget gate lies in (0, 1), so c does not increase and the extremes are c at the key
+    range's last position and at the query range's first; taking them over the groups keeps the
+    bound valid for any finite c.
 
     Two tilings, both in g-row groups:
       fwd[b, h, t, T] : query tile t of 4g rows, key tile T of g rows, for the key tiles before
@@ -419,6 +434,7 @@ def skip_bounds(q, k, c, *, scale, g=64):
     q, k, c = _f64(q), _f64(k), _f64(c)
     B, H, L, _ = q.shape
     qn, kn = _group_max_norms(q, g), _group_max_norms(k, g)
+    cmin, cmax = _group_extrema(c, g)
     n_qt, n_g, n_kb = -(-L // (4 * g)), -(-L // g), -(-L // (2 * g))
     fwd = np.full((B, H, n_qt, n_g), np.inf)
     kv = np.full((B, H, n_kb, n_g), np.inf)
@@ -426,18 +442,18 @@ def skip_bounds(q, k, c, *, scale, g=64):
         qa, qb = 4 * g * t, min(4 * g * t + 4 * g - 1, L - 1)
         groups = slice(qa // g, qb // g + 1)
         qmax, kdiag = qn[..., groups].max(axis=-1), kn[..., groups].max(axis=-1)
+        cq = cmax[..., groups].max(axis=-1)
         for T in range(qb // g - 3):
-            kb = g * T + g - 1
             fwd[..., t, T] = np.log2(np.e) * (scale * qmax * (kn[..., T] + kdiag)
-                                              - (c[..., kb] - c[..., qa]))
+                                              - (cmin[..., T] - cq))
     for blk in range(n_kb):
         ka, kb = 2 * g * blk, min(2 * g * blk + 2 * g - 1, L - 1)
-        kmax = kn[..., ka // g:kb // g + 1].max(axis=-1)
+        kgroups = slice(ka // g, kb // g + 1)
+        kmax, ck = kn[..., kgroups].max(axis=-1), cmin[..., kgroups].min(axis=-1)
         for u in range(2, -(-(L - ka) // g)):
-            qa = ka + g * u
-            grp = qa // g
+            grp = (ka + g * u) // g
             kv[..., blk, u] = np.log2(np.e) * (scale * qn[..., grp] * (kmax + kn[..., grp])
-                                               - (c[..., kb] - c[..., qa]))
+                                               - (ck - cmax[..., grp]))
     return fwd, kv
 
 

@@ -433,11 +433,14 @@ def test_planted_pro_backward_mistake_is_caught(name):
 # difference of a tile), against a construction where Cauchy-Schwarz is tight (it must equal
 # it), against hand-derived plans for that construction, and against the real attention weights
 # (every weight in a skipped tile is below the threshold).
-def _skip_case(seed, L=150, D=8, lam=(5.0, 20.0)):
+def _skip_case(seed, L=150, D=8, lam=(5.0, 20.0), rising=False):
     rng = np.random.default_rng(seed)
     q = rng.normal(size=(1, 2, L, D)) * rng.uniform(0.5, 3.0, size=(1, 2, L, 1))
     k = rng.normal(size=(1, 2, L, D)) * rng.uniform(0.5, 3.0, size=(1, 2, L, 1))
     log_f = -rng.uniform(*lam, size=(1, 2, L)) * np.array([1.0, 0.05])[None, :, None]
+    if rising:  # positive log f inside tiles: c rises there, so no tile end bounds its range
+        for a in (21, 70, 103):
+            log_f[..., a:a + 7] = rng.uniform(10.0, 40.0, size=(1, 2, 7))
     return q, k, log_f
 
 
@@ -481,8 +484,8 @@ def _tight_case(g=4, D=8, lam=20.0):
 def _skip_pins_hold(mod):
     ok = True
     g = 4
-    for seed in (1, 2, 3):
-        q, k, log_f = _skip_case(seed)
+    for seed in (1, 2, 3, 4, 5):
+        q, k, log_f = _skip_case(seed, rising=seed > 3)
         c = np.cumsum(log_f, axis=-1)
         s = 1.0 / math.sqrt(q.shape[-1])
         fb, kb = mod.skip_bounds(q, k, c, scale=s, g=g)
@@ -528,9 +531,11 @@ def test_skip_bound_pins():
 
 SKIP_MUTATIONS = {
     "skip_drop_diag_norm": ("(kn[..., T] + kdiag)", "(kn[..., T])"),
-    "skip_first_key_of_tile": ("kb = g * T + g - 1", "kb = g * T"),
-    "skip_last_query_of_tile": ("- (c[..., kb] - c[..., qa]))\n    for blk",
-                                "- (c[..., kb] - c[..., qb]))\n    for blk"),
+    "skip_largest_key_c": ("- (cmin[..., T] - cq))", "- (cmax[..., T] - cq))"),
+    "skip_smallest_query_c": ("cq = cmax[..., groups].max(axis=-1)",
+                              "cq = cmin[..., groups].min(axis=-1)"),
+    "skip_tile_ends_only": ("- (cmin[..., T] - cq))", "- (c[..., g * T + g - 1] - c[..., qa]))"),
+    "skip_kv_block_ends_only": ("- (ck - cmax[..., grp]))", "- (c[..., kb] - c[..., ka + g * u]))"),
     "skip_kv_walk_short": ("max(keep, default=1) + 1", "max(keep, default=1)"),
     "skip_prefix_too_long": ("while n < qb // g - 3 and fwd[b, h, t, n] < threshold_log2:",
                              "while n < qb // g - 3 and fwd[b, h, t, n] < threshold_log2 + 100:"),
