@@ -83,24 +83,38 @@ def read_traffic(kernel: str):
 
 
 def cpu_baseline(case, heads: int):
-    """Time the fp64 oracle (fwd + bwd) on the first `heads` heads of the workload."""
+    """Time the fp64 oracle (fwd + bwd) on the first `heads` heads of the workload, with the BLAS
+    threads pinned to the cores this process may run on."""
+    import contextlib
+
     import oracle
+    threads = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set numpy's BLAS sees
-        threads = len(os.sched_getaffinity(0))
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=threads, user_api="blas")
+    except Exception:  # threadpoolctl missing: BLAS keeps its own default
+        limit = contextlib.nullcontext()
     sl = (slice(0, 1), slice(0, heads))
     s = 1.0 / math.sqrt(case.D)
-    t0 = time.perf_counter()
-    oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl], scale=s,
-                    block=1024)
-    dt = time.perf_counter() - t0
+    with limit:
+        t0 = time.perf_counter()
+        oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl], scale=s,
+                        block=1024)
+        dt = time.perf_counter() - t0
     flops = 7 * contraction_flops(1, heads, case.L, case.D)  # fwd (2) + bwd (5), as for the GPU
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of the workload's {case.H} heads (b=0, h=0..{heads - 1}), fwd+bwd in "
                       f"fp64 NumPy: {dt:.2f} s"}
+
+
+def step_medians(events, names):
+    """Median per-kernel duration and median step duration (first launch to last) over the steps."""
+    per = {n: [a.elapsed_time(b) for m, a, b in events if m == n] for n in names}
+    starts = [a for m, a, b in events if m == names[0]]
+    ends = [b for m, a, b in events if m == names[-1]]
+    steps = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return ({n: round(float(np.median(v)), 4) for n, v in per.items() if v},
+            round(float(np.median(steps)), 4))
 
 
 def main():
@@ -184,9 +198,9 @@ def main():
         plan = run("plan", lambda: fox.fox_attn_skip_plan(q, k, c)) if skip else None
         o, lse = run("fwd", lambda: fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32,
                                                      skip_plan=plan))
-        dq, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, None, o=o,
-                                                                skip_plan=plan))
-        dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta,
+        dq, dcq, delta, lse2 = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, None,
+                                                                      o=o, skip_plan=plan))
+        dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse2, do, delta,
                                                               skip_plan=plan))
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
         return dq, dk, dv, dlf, plan
@@ -206,6 +220,7 @@ def main():
     ms_per_step = events[0][1].elapsed_time(events[-1][2]) / args.steps
     kern_ms = {n: float(np.mean([a.elapsed_time(b) for m, a, b in events if m == n]))
                for n in names}
+    kern_med, step_med = step_medians(events, names)
 
     unit = contraction_flops(B, H, L, D)
     fwd_flops, bwd_flops = 2 * unit, 5 * unit
@@ -244,6 +259,10 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4),
                 "tflops_credited": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2)},
         "kernel_ms": {n: round(kern_ms[n], 4) for n in names},
+        "kernel_ms_median": kern_med,
+        "ms_per_step_median": step_med,
+        "fwd_frac_of_peak_median": round(kernel_flops["fwd"] / (kern_med["fwd"] * 1e-3) / 1e12
+                                         / PEAK_BF16_TFLOPS, 4),
         "host_wall_ms_per_step": round(wall_ms, 4),
     }
     if not args.no_skip:
@@ -461,9 +480,9 @@ def pro_step(args, torch, fi, fox, dev):
         plan = run("plan", lambda: fox.fox_attn_skip_plan(qn, kn, c)) if skip else None
         o, lse = run("fwd", lambda: fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32,
                                                      skip_plan=plan))
-        dqn, dcq, delta = run("dq", lambda: fox.fox_attn_bwd_dq(qn, kn, v, c, lse, do, None, o=o,
-                                                                 skip_plan=plan))
-        dkn, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(qn, kn, v, c, lse, do, delta,
+        dqn, dcq, delta, lse2 = run("dq", lambda: fox.fox_attn_bwd_dq(qn, kn, v, c, lse, do, None,
+                                                                       o=o, skip_plan=plan))
+        dkn, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(qn, kn, v, c, lse2, do, delta,
                                                                skip_plan=plan))
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
         dq, _ = run("qnorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(q, dqn, eps=1e-6))

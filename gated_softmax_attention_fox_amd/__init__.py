@@ -42,7 +42,7 @@ __all__ = [
     "fox_shift_gate", "fox_shift_gate_bwd", "fox_kv_shift", "fox_kv_shift_bwd", "fox_out_norm_gate",
     "fox_out_norm_gate_bwd",
     "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
-    "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID",
+    "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID", "FOX_C_F64",
     "FOX_E_UNSUPPORTED", "FOX_E_LAUNCH", "FOX_F32", "FOX_BF16", "FOX_CAUSAL",
 ]
 
@@ -52,12 +52,13 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fox.h")
 
 FOX_OK, FOX_E_INVALID, FOX_E_UNSUPPORTED, FOX_E_LAUNCH = 0, 1, 2, 3
 FOX_F32, FOX_BF16 = 0, 1
-FOX_CAUSAL = 1
+FOX_CAUSAL, FOX_C_F64 = 1, 2
 
 _c_i64, _c_u32, _c_f32, _c_vp, _c_sz = (ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
 _SIGS = {
     "fox_logf_cumsum": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
+    "fox_logf_cumsum_f64": (ctypes.c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_gate_logf": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
                                      _c_i64, _c_i64, _c_vp]),
     "fox_qk_rmsnorm": (ctypes.c_int, [_c_vp, _c_vp, ctypes.c_int, _c_i64, _c_i64, _c_f32, _c_vp,
@@ -84,8 +85,8 @@ _SIGS = {
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                         _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_attn_bwd_dq": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
-                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
-                                       _c_i64, _c_f32, _c_u32, _c_vp, _c_vp]),
+                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                       _c_i64, _c_i64, _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_dlogf_from_dc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_shift_gate": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64,
                                       _c_i64, _c_vp]),
@@ -175,21 +176,35 @@ def _dev(t: torch.Tensor, name: str, dtypes, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    """Require an exact shape: the kernels index every element the sizes imply."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _code(dt: torch.dtype) -> int:
     return FOX_BF16 if dt == torch.bfloat16 else FOX_F32
 
 
-def fox_logf_cumsum(log_f: torch.Tensor, c: torch.Tensor | None = None) -> torch.Tensor:
-    """c = inclusive prefix sum of log_f along the last axis (fp32 in, fp32 out)."""
+def fox_logf_cumsum(log_f: torch.Tensor, c: torch.Tensor | None = None,
+                    dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """c = inclusive prefix sum of log_f along the last axis (fp32 in; fp32 out, or fp64 out
+    with dtype=torch.float64 or an fp64 c, for the attention calls' fp64-c mode)."""
     lib = load_library()
     pl = _dev(log_f, "log_f", (torch.float32,))
     if c is None:
-        c = torch.empty_like(log_f)
-    pc = _dev(c, "c", (torch.float32,))
+        c = torch.empty(log_f.shape, dtype=dtype, device=log_f.device)
+    pc = _dev(c, "c", (torch.float32, torch.float64))
+    _shape(c, "c", log_f.shape)
     L = log_f.shape[-1]
-    _check(lib.fox_logf_cumsum(pl, pc, log_f.numel() // max(L, 1), L, _stream(log_f)),
-           "fox_logf_cumsum")
+    fn = lib.fox_logf_cumsum_f64 if c.dtype == torch.float64 else lib.fox_logf_cumsum
+    _check(fn(pl, pc, log_f.numel() // max(L, 1), L, _stream(log_f)), "fox_logf_cumsum")
     return c
+
+
+def _cflags(c: torch.Tensor) -> int:
+    """FOX_CAUSAL, plus FOX_C_F64 when c holds fp64 values."""
+    return FOX_CAUSAL | (FOX_C_F64 if c.dtype == torch.float64 else 0)
 
 
 def fox_gate_logf(x: torch.Tensor, w_f: torch.Tensor, b_f: torch.Tensor) -> torch.Tensor:
@@ -217,9 +232,8 @@ def fox_qk_rmsnorm(x: torch.Tensor, eps: float = 1e-6, weight: torch.Tensor | No
     if out is None:
         out = torch.empty_like(x)
     po = _dev(out, "out", (x.dtype,))
-    pw = ctypes.c_void_p(0)
-    if weight is not None:
-        pw = _dev(weight, "weight", (torch.float32,), 1)
+    _shape(out, "out", x.shape)
+    pw = _wptr(weight, D)
     _check(lib.fox_qk_rmsnorm(px, po, _code(x.dtype), x.numel() // D, D, eps, pw, _stream(x)),
            "fox_qk_rmsnorm")
     return out
@@ -260,9 +274,7 @@ def fox_qk_rmsnorm_bwd(x: torch.Tensor, dy: torch.Tensor, eps: float = 1e-6,
     D = x.shape[-1]
     rows = x.numel() // D
     dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    pw = ctypes.c_void_p(0)
-    if weight is not None:
-        pw = _dev(weight, "weight", (torch.float32,), 1)
+    pw = _wptr(weight, D)
     dwt, pdw, ws, nws = None, ctypes.c_void_p(0), ctypes.c_void_p(0), 0
     if want_dweight:
         if weight is None:
@@ -305,26 +317,34 @@ def fox_attn_skip_plan(q, k, c, scale: float | None = None) -> torch.Tensor:
 
 
 def skip_plan_arrays(plan: torch.Tensor, B: int, H: int, L: int):
-    """Views (q_skip, kv_tiles, qn, kn, q_order, kv_order) of a plan, in the layout
+    """Views (q_skip, kv_tiles, qn, kn, cmin, cmax, q_order, kv_order) of a plan, in the layout
     include/fox.h documents."""
     a256 = lambda x: (x + 255) // 256 * 256
     BH, n_qt, n_kb, n64 = B * H, -(-L // 256), -(-L // 128), -(-L // 64)
     o_kv = a256(4 * BH * n_qt)
     o_qn = a256(o_kv + 4 * BH * n_kb)
     o_kn = a256(o_qn + 4 * BH * n64)
-    o_qo = a256(o_kn + 4 * BH * n64)
+    o_cmin = a256(o_kn + 4 * BH * n64)
+    o_cmax = a256(o_cmin + 4 * BH * n64)
+    o_qo = a256(o_cmax + 4 * BH * n64)
     o_ko = a256(o_qo + 4 * BH * n_qt)
     view = lambda off, n, dt, cols: plan[off:off + 4 * n].view(dt).view(-1, cols)
+    f64 = lambda off: view(off, BH * n64, torch.float32, n64)
     return (view(0, BH * n_qt, torch.int32, n_qt), view(o_kv, BH * n_kb, torch.int32, n_kb),
-            view(o_qn, BH * n64, torch.float32, n64), view(o_kn, BH * n64, torch.float32, n64),
+            f64(o_qn), f64(o_kn), f64(o_cmin), f64(o_cmax),
             view(o_qo, BH * n_qt, torch.int32, BH * n_qt)[0],
             view(o_ko, BH * n_kb, torch.int32, BH * n_kb)[0])
 
 
-def _plan_ptr(skip_plan) -> ctypes.c_void_p:
+def _plan_ptr(skip_plan, B: int, H: int, L: int, D: int) -> ctypes.c_void_p:
     if skip_plan is None:
         return ctypes.c_void_p(0)
-    return _dev(skip_plan, "skip_plan", (torch.uint8,))
+    p = _dev(skip_plan, "skip_plan", (torch.uint8,))
+    need = fox_attn_skip_plan_bytes(B, H, L, D)
+    if skip_plan.numel() < need:
+        raise ValueError(f"skip_plan holds {skip_plan.numel()} bytes; these sizes need {need} "
+                         "(fox_attn_skip_plan_bytes)")
+    return p
 
 
 def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | None = None,
@@ -336,7 +356,7 @@ def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | 
     B, H, L, D = _bhld(q, k, v)
     dts = (torch.bfloat16, torch.float32)
     pq, pk, pv = _dev(q, "q", dts), _dev(k, "k", (q.dtype,)), _dev(v, "v", (q.dtype,))
-    pc = _dev(c, "c", (torch.float32,), 3)
+    pc = _dev(c, "c", (torch.float32, torch.float64), 3)
     if tuple(c.shape) != (B, H, L):
         raise ValueError("c must be [B, H, L]")
     o_dtype = o_dtype or q.dtype
@@ -345,7 +365,8 @@ def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | 
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.fox_attn_fwd(pq, pk, pv, _code(q.dtype), pc, ctypes.c_void_p(o.data_ptr()),
                             _code(o_dtype), ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
-                            B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan), _stream(q)),
+                            B, H, L, D, scale, _cflags(c), _plan_ptr(skip_plan, B, H, L, D),
+                            _stream(q)),
            "fox_attn_fwd")
     return o, lse
 
@@ -362,9 +383,13 @@ def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=N
     pq = _dev(q, "q", (torch.bfloat16, torch.float32))
     pk, pv = _dev(k, "k", (q.dtype,)), _dev(v, "v", (q.dtype,))
     pdo = _dev(dO, "dO", (q.dtype,))
-    pc = _dev(c, "c", (torch.float32,), 3)
+    pc = _dev(c, "c", (torch.float32, torch.float64), 3)
     po = _dev(o, "o", (torch.float32,), 4)
     pl = _dev(lse, "lse", (torch.float32,), 3)
+    for t, name in ((dO, "dO"), (o, "o")):
+        _shape(t, name, (B, H, L, D))
+    for t, name in ((c, "c"), (lse, "lse")):
+        _shape(t, name, (B, H, L))
     dq = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
@@ -373,12 +398,14 @@ def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=N
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", (torch.uint8,))
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes; {need} needed")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.fox_attn_bwd(pq, pk, pv, _code(q.dtype), pc, po, pl, pdo,
                             ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()),
                             ctypes.c_void_p(dv.data_ptr()), ctypes.c_void_p(dlf.data_ptr()), pw,
-                            workspace.numel(), B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan),
-                            _stream(q)),
+                            workspace.numel(), B, H, L, D, scale, _cflags(c),
+                            _plan_ptr(skip_plan, B, H, L, D), _stream(q)),
            "fox_attn_bwd")
     return dq, dk, dv, dlf
 
@@ -399,8 +426,12 @@ def fox_attn_bwd_delta(dO: torch.Tensor, o: torch.Tensor) -> torch.Tensor:
 
 def _bwd_inputs(q, k, v, c, lse, dO, delta):
     B, H, L, D = _bhld(q, k, v)
+    _shape(dO, "dO", (B, H, L, D))
+    for t, name in ((c, "c"), (lse, "lse"), (delta, "delta")):
+        if t is not None:
+            _shape(t, name, (B, H, L))
     ptrs = (_dev(q, "q", (torch.bfloat16, torch.float32)), _dev(k, "k", (q.dtype,)),
-            _dev(v, "v", (q.dtype,)), _dev(c, "c", (torch.float32,), 3),
+            _dev(v, "v", (q.dtype,)), _dev(c, "c", (torch.float32, torch.float64), 3),
             _dev(lse, "lse", (torch.float32,), 3), _dev(dO, "dO", (q.dtype,), 4),
             None if delta is None else _dev(delta, "delta", (torch.float32,), 3))
     return (B, H, L, D), ptrs
@@ -408,7 +439,8 @@ def _bwd_inputs(q, k, v, c, lse, dO, delta):
 
 def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None,
                      skip_plan: torch.Tensor | None = None):
-    """(dK, dV, dc_k) of the key-stationary backward step; delta = fox_attn_bwd_dq's refined one."""
+    """(dK, dV, dc_k) of the key-stationary backward step; lse and delta are fox_attn_bwd_dq's
+    lse_out and refined delta."""
     lib = load_library()
     (B, H, L, D), (pq, pk, pv, pc, pl, pdo, pdl) = _bwd_inputs(q, k, v, c, lse, dO, delta)
     dk = torch.empty((B, H, L, D), dtype=torch.float32, device=q.device)
@@ -417,15 +449,17 @@ def fox_attn_bwd_dkv(q, k, v, c, lse, dO, delta, scale: float | None = None,
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.fox_attn_bwd_dkv(pq, pk, pv, _code(q.dtype), pc, pl, pdo, pdl,
                                 ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
-                                ctypes.c_void_p(dck.data_ptr()), B, H, L, D, scale, FOX_CAUSAL,
-                                _plan_ptr(skip_plan), _stream(q)), "fox_attn_bwd_dkv")
+                                ctypes.c_void_p(dck.data_ptr()), B, H, L, D, scale, _cflags(c),
+                                _plan_ptr(skip_plan, B, H, L, D), _stream(q)),
+           "fox_attn_bwd_dkv")
     return dk, dv, dck
 
 
 def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
                     delta_out: torch.Tensor | None = None, skip_plan: torch.Tensor | None = None,
                     o: torch.Tensor | None = None):
-    """(dQ, dc_q, refined delta) of the query-stationary backward step (run before dkv).
+    """(dQ, dc_q, refined delta, lse_out) of the query-stationary backward step (run before
+    dkv, which takes lse_out and the refined delta).
 
     delta_out may be `delta` itself to refine it in place. With delta=None the step forms the
     row term from o (the fp32 forward output) itself, bit-identical to fox_attn_bwd_delta."""
@@ -443,12 +477,15 @@ def fox_attn_bwd_dq(q, k, v, c, lse, dO, delta, scale: float | None = None,
     if delta_out is None:
         delta_out = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     pdn = _dev(delta_out, "delta_out", (torch.float32,), 3)
+    _shape(delta_out, "delta_out", (B, H, L))
+    lse_out = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     _check(lib.fox_attn_bwd_dq(pq, pk, pv, _code(q.dtype), pc, pl, pdo, po, pdl,
                                ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dcq.data_ptr()), pdn,
-                               B, H, L, D, scale, FOX_CAUSAL, _plan_ptr(skip_plan), _stream(q)),
+                               ctypes.c_void_p(lse_out.data_ptr()), B, H, L, D, scale, _cflags(c),
+                               _plan_ptr(skip_plan, B, H, L, D), _stream(q)),
            "fox_attn_bwd_dq")
-    return dq, dcq, delta_out
+    return dq, dcq, delta_out, lse_out
 
 
 def fox_dlogf_from_dc(dc_q: torch.Tensor, dc_k: torch.Tensor) -> torch.Tensor:
@@ -496,8 +533,13 @@ def fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype: torch.dtype = t
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", (torch.uint8,))
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes; {need} needed")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    pn = ctypes.c_void_p(0) if k_norms is None else _dev(k_norms, "k_norms", (torch.float32,), 3)
+    pn = ctypes.c_void_p(0)
+    if k_norms is not None:
+        pn = _dev(k_norms, "k_norms", (torch.float32,), 3)
+        _shape(k_norms, "k_norms", (B, H, -(-T // 64)))
     _check(lib.fox_attn_decode(pq, pk, pv, FOX_BF16, pc, pl, pn, ctypes.c_void_p(o.data_ptr()),
                                _code(o_dtype), ctypes.c_void_p(lse.data_ptr()), pw,
                                workspace.numel(), B, H, T, D, scale, FOX_CAUSAL, _stream(q)),
@@ -508,7 +550,10 @@ def fox_attn_decode(q, k_cache, v_cache, c_cache, lens, o_dtype: torch.dtype = t
 def fox_attn_decode_key_norms(k_cache: torch.Tensor, lens: torch.Tensor) -> torch.Tensor:
     """The largest key norm of every 64 cached positions: [B, H, ceil(T_max / 64)] fp32."""
     lib = load_library()
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, H, T_max, D]")
     B, H, T, D = k_cache.shape
+    _shape(lens, "lens", (B,))
     kn = torch.empty((B, H, -(-T // 64)), dtype=torch.float32, device=k_cache.device)
     _check(lib.fox_attn_decode_key_norms(_dev(k_cache, "k_cache", (torch.bfloat16,), 4), FOX_BF16,
                                          _dev(lens, "lens", (torch.int32,), 1),
@@ -522,7 +567,12 @@ def fox_attn_decode_append(k_new, v_new, log_f_new, k_cache, v_cache, c_cache, l
     """Append one position per sequence to the cache in place (k, v, c and, when given, the key
     norms), then lens += 1."""
     lib = load_library()
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share one shape [B, H, T_max, D]")
     B, H, T, D = k_cache.shape
+    _shape(c_cache, "c_cache", (B, H, T))
+    if k_norms is not None:
+        _shape(k_norms, "k_norms", (B, H, -(-T // 64)))
     if tuple(k_new.shape) != (B, H, D) or k_new.shape != v_new.shape:
         raise ValueError("k_new and v_new must be [B, H, D]")
     if tuple(log_f_new.shape) != (B, H) or tuple(lens.shape) != (B,):
@@ -553,6 +603,7 @@ def fox_shift_gate(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
     H = w.shape[0]
     px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
     pw = _dev(w, "w", (torch.float32,), 2)
+    _shape(w, "w", (H, dm))
     alpha = torch.empty((B, H, L), dtype=torch.float32, device=x.device)
     _check(lib.fox_shift_gate(px, _code(x.dtype), pw, ctypes.c_void_p(alpha.data_ptr()), B, L, dm,
                               H, _stream(x)), "fox_shift_gate")
@@ -567,6 +618,8 @@ def fox_shift_gate_bwd(x: torch.Tensor, w: torch.Tensor, dalpha: torch.Tensor):
     px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
     pw = _dev(w, "w", (torch.float32,), 2)
     pd = _dev(dalpha, "dalpha", (torch.float32,), 3)
+    _shape(w, "w", (H, dm))
+    _shape(dalpha, "dalpha", (B, H, L))
     dx = torch.empty((B, L, dm), dtype=torch.float32, device=x.device)
     dw = torch.empty((H, dm), dtype=torch.float32, device=x.device)
     need = int(lib.fox_gate_logf_bwd_workspace_bytes(B, L, dm, H))
@@ -601,6 +654,7 @@ def fox_kv_shift_bwd(x, alpha, dy, normalize: bool = False, eps: float = 1e-6, w
     BH = x.numel() // (L * D)
     if dy.shape != x.shape:
         raise ValueError("dy must have x's shape")
+    _shape(alpha, "alpha", x.shape[:-1])
     px = _dev(x, "x", (torch.bfloat16, torch.float32))
     pa = _dev(alpha, "alpha", (torch.float32,))
     pd = _dev(dy, "dy", (torch.float32,))

@@ -66,6 +66,25 @@ fox_status check_bhld(int64_t B, int64_t H, int64_t L, int64_t D) {
   return FOX_OK;
 }
 
+// Flags of the attention calls: FOX_CAUSAL is required; FOX_C_F64 says c holds fp64 values.
+// A skip plan is built from fp32 c, so it is not taken together with FOX_C_F64.
+fox_status check_flags(uint32_t flags, const void* skip_plan) {
+  if (!(flags & FOX_CAUSAL))
+    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
+  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64))
+    return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if ((flags & FOX_C_F64) && skip_plan)
+    return fail(FOX_E_UNSUPPORTED, "a skip plan is built from fp32 c; it is not taken with FOX_C_F64");
+  return FOX_OK;
+}
+
+fox::CPtr cptr(const void* c, uint32_t flags) {
+  fox::CPtr r;
+  r.p = c;
+  r.f64 = (flags & FOX_C_F64) != 0;
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,6 +112,18 @@ fox_status fox_logf_cumsum(const float* log_f, float* c, int64_t BH, int64_t L, 
   FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, %lld] (got %lld)", (long long)kMaxL,
               (long long)L);
   return launched(fox::launch_cumsum(log_f, c, BH, L, (hipStream_t)stream), "fox_logf_cumsum");
+}
+
+fox_status fox_logf_cumsum_f64(const float* log_f, double* c, int64_t BH, int64_t L, void* stream) {
+  FOX_REQUIRE_PTR(log_f);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE((const void*)log_f != (const void*)c, "c must not alias log_f");
+  FOX_REQUIRE(BH >= 1 && BH < (int64_t(1) << 31), "BH must be in [1, 2^31) (got %lld)",
+              (long long)BH);
+  FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, %lld] (got %lld)", (long long)kMaxL,
+              (long long)L);
+  return launched(fox::launch_cumsum64(log_f, c, BH, L, (hipStream_t)stream),
+                  "fox_logf_cumsum_f64");
 }
 
 fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
@@ -222,7 +253,7 @@ fox_status fox_attn_skip_plan(const void* q, const void* k, fox_dtype in_dt, con
 }
 
 fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                        const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B, int64_t H,
+                        const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B, int64_t H,
                         int64_t L, int64_t D, float scale, uint32_t flags, const void* skip_plan,
                         void* stream) {
   FOX_REQUIRE_PTR(q);
@@ -237,9 +268,8 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
   FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
   FOX_REQUIRE(!(in_dt == FOX_F32 && o_dt != FOX_F32), "fp32 inputs require an fp32 output");
   FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
-  if (!(flags & FOX_CAUSAL))
-    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
-  if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  st = check_flags(flags, skip_plan);
+  if (st != FOX_OK) return st;
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
   if (skip_plan && in_dt != FOX_BF16)
@@ -248,10 +278,11 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
     return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)", (long long)(B * H));
   const hipStream_t s = (hipStream_t)stream;
   if (in_dt == FOX_F32)
-    return launched(fox::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, c,
-                                        (float*)o, lse, B * H, L, D, scale, s),
+    return launched(fox::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v,
+                                        cptr(c, flags), (float*)o, lse, B * H, L, D, scale, s),
                     "fox_attn_fwd");
-  return launched(fox::launch_fwd_bf16(q, k, v, c, o, o_dt == FOX_F32, lse, B * H, L, D, scale,
+  return launched(fox::launch_fwd_bf16(q, k, v, cptr(c, flags), o, o_dt == FOX_F32, lse, B * H, L,
+                                       D, scale,
                                        fox::skip_args(skip_plan, B * H, L), s),
                   "fox_attn_fwd");
 }
@@ -262,11 +293,17 @@ size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D) 
   return fox::bwd_workspace_bytes(B * H, L);
 }
 
-fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                        const float* c, const float* o, const float* lse, const void* dO,
-                        float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
-                        size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
-                        float scale, uint32_t flags, const void* skip_plan, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fox_attn_bwd's validation and launches (named `what` in messages).
+fox_status attn_bwd_impl(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                         const void* c, const float* o, const float* lse, const void* dO,
+                         float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
+                         size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
+                         float scale, uint32_t flags, const void* skip_plan, void* stream,
+                         const char* what) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k);
   FOX_REQUIRE_PTR(v);
@@ -284,35 +321,51 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
   fox_status st = check_bhld(B, H, L, D);
   if (st != FOX_OK) return st;
   FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
-  if (!(flags & FOX_CAUSAL))
-    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
-  if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  st = check_flags(flags, skip_plan);
+  if (st != FOX_OK) return st;
   FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
   const size_t need = fox::bwd_workspace_bytes(B * H, L);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
+  if (in_dt == FOX_F32 && skip_plan)
+    return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
+  if (in_dt == FOX_F32 && B * H > 65535)
+    return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)",
+                (long long)(B * H));
   if (in_dt == FOX_F32) {
-    if (skip_plan)
-      return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
-    if (B * H > 65535)
-      return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)",
-                  (long long)(B * H));
-    return launched(fox::launch_bwd_f32((const float*)q, (const float*)k, (const float*)v, c, o, lse,
-                                        (const float*)dO, dq, dk, dv, dlog_f, workspace, B * H, L,
-                                        D, scale, (hipStream_t)stream),
-                    "fox_attn_bwd");
+    return launched(fox::launch_bwd_f32((const float*)q, (const float*)k, (const float*)v,
+                                        cptr(c, flags), o, lse, (const float*)dO, dq, dk, dv,
+                                        dlog_f, workspace, B * H, L, D, scale,
+                                        (hipStream_t)stream),
+                    what);
   }
-  return launched(fox::launch_bwd_bf16(q, k, v, c, o, lse, dO, dq, dk, dv, dlog_f, workspace,
+  return launched(fox::launch_bwd_bf16(q, k, v, cptr(c, flags), o, lse, dO, dq, dk, dv, dlog_f,
+                                       workspace,
                                        B * H, L, D, scale, skip_plan, (hipStream_t)stream),
-                  "fox_attn_bwd");
+                  what);
+}
+
+}  // namespace
+
+extern "C" {
+
+fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                        const void* c, const float* o, const float* lse, const void* dO,
+                        float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
+                        size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
+                        float scale, uint32_t flags, const void* skip_plan, void* stream) {
+  return attn_bwd_impl(q, k, v, in_dt, c, o, lse, dO, dq, dk, dv, dlog_f, workspace,
+                       workspace_bytes, B, H, L, D, scale, flags, skip_plan, stream,
+                       "fox_attn_bwd");
 }
 
 namespace {
 fox_status check_bwd_common(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                            const float* c, const float* lse, const void* dO, int64_t B, int64_t H, int64_t L, int64_t D, float scale,
-                            uint32_t flags) {
+                            const void* c, const float* lse, const void* dO, int64_t B, int64_t H,
+                            int64_t L, int64_t D, float scale, uint32_t flags,
+                            const void* skip_plan) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k);
   FOX_REQUIRE_PTR(v);
@@ -322,9 +375,8 @@ fox_status check_bwd_common(const void* q, const void* k, const void* v, fox_dty
   fox_status st = check_bhld(B, H, L, D);
   if (st != FOX_OK) return st;
   FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
-  if (!(flags & FOX_CAUSAL))
-    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
-  if (flags & ~uint32_t(FOX_CAUSAL)) return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  st = check_flags(flags, skip_plan);
+  if (st != FOX_OK) return st;
   FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
   if (in_dt == FOX_F32 && B * H > 65535)
     return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)", (long long)(B * H));
@@ -349,11 +401,11 @@ fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, f
 }
 
 fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                            const float* c, const float* lse, const void* dO, const float* delta,
+                            const void* c, const float* lse, const void* dO, const float* delta,
                             float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
                             int64_t D, float scale, uint32_t flags, const void* skip_plan,
                             void* stream) {
-  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, B, H, L, D, scale, flags);
+  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, B, H, L, D, scale, flags, skip_plan);
   if (st != FOX_OK) return st;
   FOX_REQUIRE_PTR(delta);
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
@@ -364,22 +416,23 @@ fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dty
   if (in_dt == FOX_F32) {
     if (skip_plan)
       return fail(FOX_E_UNSUPPORTED, "tile skipping serves the bf16 kernels (in_dt = FOX_BF16)");
-    return launched(fox::launch_bwd_dkv_f32((const float*)q, (const float*)k, (const float*)v, c, lse,
+    return launched(fox::launch_bwd_dkv_f32((const float*)q, (const float*)k, (const float*)v,
+                                            cptr(c, flags), lse,
                                             (const float*)dO, delta, dk, dv, dc_k, B * H, L, D,
                                             scale, (hipStream_t)stream),
                     "fox_attn_bwd_dkv");
   }
-  return launched(fox::launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dc_k, B * H, L, D, scale,
+  return launched(fox::launch_bwd_dkv(q, k, v, cptr(c, flags), lse, dO, delta, dk, dv, dc_k, B * H, L, D, scale,
                                       fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dkv");
 }
 
 fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                           const float* c, const float* lse, const void* dO, const float* o,
+                           const void* c, const float* lse, const void* dO, const float* o,
                            const float* delta, float* dq, float* dc_q, float* delta_out,
-                           int64_t B, int64_t H, int64_t L, int64_t D, float scale,
-                           uint32_t flags, const void* skip_plan, void* stream) {
-  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, B, H, L, D, scale, flags);
+                           float* lse_out, int64_t B, int64_t H, int64_t L, int64_t D,
+                           float scale, uint32_t flags, const void* skip_plan, void* stream) {
+  fox_status st = check_bwd_common(q, k, v, in_dt, c, lse, dO, B, H, L, D, scale, flags, skip_plan);
   if (st != FOX_OK) return st;
   FOX_REQUIRE(delta != nullptr || o != nullptr, "one of delta and o must be given");
   if (delta) FOX_REQUIRE_PTR(delta);
@@ -389,6 +442,8 @@ fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtyp
   FOX_REQUIRE_PTR(dq);
   FOX_REQUIRE_PTR(dc_q);
   FOX_REQUIRE_PTR(delta_out);
+  FOX_REQUIRE_PTR(lse_out);
+  FOX_REQUIRE((const void*)lse_out != (const void*)lse, "lse_out must not alias lse");
   const float* o_used = delta ? nullptr : o;  // a given delta wins; o is then not read
   if (in_dt == FOX_F32) {
     if (skip_plan)
@@ -399,14 +454,15 @@ fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtyp
       if (e != hipSuccess) return launched(e, "fox_attn_bwd_dq");
       delta = delta_out;
     }
-    return launched(fox::launch_bwd_dq_f32((const float*)q, (const float*)k, (const float*)v, c, lse,
-                                           (const float*)dO, delta, dq, dc_q, delta_out, B * H, L, D,
-                                           scale, (hipStream_t)stream),
+    return launched(fox::launch_bwd_dq_f32((const float*)q, (const float*)k, (const float*)v,
+                                           cptr(c, flags), lse, (const float*)dO, delta, dq, dc_q,
+                                           delta_out, lse_out, B * H, L, D, scale,
+                                           (hipStream_t)stream),
                     "fox_attn_bwd_dq");
   }
-  return launched(fox::launch_bwd_dq(q, k, v, c, lse, dO, delta, o_used, dq, dc_q, delta_out,
-                                     B * H, L, D, scale, fox::skip_args(skip_plan, B * H, L),
-                                     (hipStream_t)stream),
+  return launched(fox::launch_bwd_dq(q, k, v, cptr(c, flags), lse, dO, delta, o_used, dq, dc_q,
+                                     delta_out, lse_out, B * H, L, D, scale,
+                                     fox::skip_args(skip_plan, B * H, L), (hipStream_t)stream),
                   "fox_attn_bwd_dq");
 }
 

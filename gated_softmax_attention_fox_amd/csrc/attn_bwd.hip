@@ -115,10 +115,10 @@ __device__ __forceinline__ void readahead() {
 // dc^k_j -= sum_i dS_ij from the fp32 dS, and dV^T += dO^T P, dK^T += Q^T dS with the transposes
 // read from the row-major tiles. Tiles 0 and 1 hold every wave's diagonal and evaluate the
 // causal mask; from tile 2 on the loop is unrolled over four tiles for compile-time slots.
-template <int D>
+template <int D, typename CT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkv_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
+    const bf16_t* __restrict__ dO, const CT* __restrict__ C, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV,
     float* __restrict__ dck_out, const int32_t* __restrict__ kv_tiles,
     const int32_t* __restrict__ kv_order, int L, int BH, float sl2e, float scale) {
@@ -130,8 +130,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int NCOPY = 2 * BLK + 3;
   static_assert(BLK >= 1, "tile must split evenly over the waves");
   constexpr uint32_t TB = TILE * 2;
-  constexpr uint32_t Q_OFF = 0, O_OFF = 4 * TB, R_OFF = 8 * TB, M_OFF = 8 * TB + 4 * 3 * BQ * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 4 * 3 * BQ * 4 + 2 * 2 * BQ * 4];
+  constexpr uint32_t CS = sizeof(CT);        // bytes of one raw c value (fp32 or fp64)
+  constexpr uint32_t RS = BQ * (CS + 8);     // raw c, LSE and Delta of one tile (one ring slot)
+  constexpr uint32_t Q_OFF = 0, O_OFF = 4 * TB, R_OFF = 8 * TB, M_OFF = 8 * TB + 4 * RS;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 4 * RS + 2 * 2 * BQ * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   C += (size_t)bh * L;
   LSE += (size_t)bh * L;
   Delta += (size_t)bh * L;
-  const float c_ref = C[k0];
+  const CT c_ref = C[k0];
   const int kw = k0 + wave * 32;
   const int kj = kw + l32;
   const bool kok = kj < L;
@@ -166,11 +168,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // a skip plan could not rule out (the later ones would add exact zeros).
   const int n_t = kv_tiles ? kv_tiles[(size_t)bh * n_kb + kt] : (L - k0 + BQ - 1) / BQ;
   const int j0 = wave;                     // the wave's diagonal sub-tile (queries kw .. kw + 31)
-  const i32x4 q_rs = buffer_words(Q, (uint32_t)(L * D * 2));
-  const i32x4 o_rs = buffer_words(dO, (uint32_t)(L * D * 2));
-  const i32x4 c_rs = buffer_words(C, (uint32_t)(L * 4));
-  const i32x4 l_rs = buffer_words(LSE, (uint32_t)(L * 4));
-  const i32x4 d_rs = buffer_words(Delta, (uint32_t)(L * 4));
+  const i32x4 q_rs = buffer_words(Q, (uint32_t)L * (uint32_t)(D * 2));
+  const i32x4 o_rs = buffer_words(dO, (uint32_t)L * (uint32_t)(D * 2));
+  const i32x4 c_rs = buffer_words(C, (uint32_t)L * CS);
+  const i32x4 l_rs = buffer_words(LSE, (uint32_t)L * 4u);
+  const i32x4 d_rs = buffer_words(Delta, (uint32_t)L * 4u);
   const uint32_t sbase = lds_addr(smem);
 
   bf16x8 kf[D / 16], vf[D / 16];
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     pin_agpr(kf[c]);
     pin_agpr(vf[c]);
   }
-  const float kterm = kok ? (C[kj] - c_ref) * kLog2e : 0.f;
+  const float kterm = kok ? cbias(C[kj], c_ref) : 0.f;
   f32x16 dvacc[D / 32], dkacc[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) {
@@ -210,12 +212,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
   auto copy_rows = [&](int t, int slot) __attribute__((always_inline)) {  // raw c, LSE, Delta
+    const uint32_t row0 = (uint32_t)(k0 + t * BQ + wave * RW);
+    const uint32_t dst = sbase + R_OFF + slot * RS;
+    if (lane < RW * (int)CS / 4)  // c: one 4-byte word per lane
+      copy4_to_lds(dst + wave * RW * CS, row0 * CS + lane * 4, c_rs);
     if (lane < RW) {
-      const uint32_t voff = (uint32_t)(k0 + t * BQ + wave * RW + lane) * 4;
-      const uint32_t dst = sbase + R_OFF + slot * 3 * BQ * 4 + wave * RW * 4;
-      copy4_to_lds(dst, voff, c_rs);
-      copy4_to_lds(dst + BQ * 4, voff, l_rs);
-      copy4_to_lds(dst + 2 * BQ * 4, voff, d_rs);
+      copy4_to_lds(dst + BQ * CS + wave * RW * 4, (row0 + lane) * 4, l_rs);
+      copy4_to_lds(dst + BQ * (CS + 4) + wave * RW * 4, (row0 + lane) * 4, d_rs);
     }
   };
   auto start_copies = [&](int t, int sqo, int sr) __attribute__((always_inline)) {
@@ -229,13 +232,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   auto convert_rows = [&](int t, int sr, int sm) __attribute__((always_inline)) {
     if (wave == 0 && t + 1 < n_t) {
       typedef __attribute__((address_space(3))) float lds_f;
-      const uint32_t src = sbase + R_OFF + sr * 3 * BQ * 4 + lane * 4;
-      const float ci = *(const lds_f*)(uintptr_t)src;
-      const float li = *(const lds_f*)(uintptr_t)(src + BQ * 4);
-      const float di = *(const lds_f*)(uintptr_t)(src + 2 * BQ * 4);
+      typedef __attribute__((address_space(3))) CT lds_c;
+      const uint32_t src = sbase + R_OFF + sr * RS;
+      const CT ci = *(const lds_c*)(uintptr_t)(src + lane * CS);
+      const float li = *(const lds_f*)(uintptr_t)(src + BQ * CS + lane * 4);
+      const float di = *(const lds_f*)(uintptr_t)(src + BQ * (CS + 4) + lane * 4);
       const bool ok = k0 + (t + 1) * BQ + lane < L;
       const uint32_t dst = sbase + M_OFF + sm * 2 * BQ * 4 + lane * 4;
-      *(lds_f*)(uintptr_t)dst = ok ? (li - (ci - c_ref)) * kLog2e : INFINITY;
+      *(lds_f*)(uintptr_t)dst = ok ? (li - cdiff(ci, c_ref)) * kLog2e : INFINITY;
       *(lds_f*)(uintptr_t)(dst + BQ * 4) = ok ? di : 0.f;
     }
   };
@@ -444,12 +448,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // dS = P (dP - Delta_i), and dQ^T += K^T dS^T with K^T from transposed reads of the K tile.
 // Tiles 0..3 hold every wave's diagonal and evaluate the causal mask; from tile 4 on the loop
 // is unrolled over four tiles so that every LDS address is a per-lane base plus an immediate.
-template <int D, int NB>
+template <int D, int NB, typename CT>
 __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB))) void dq_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ C, const float* __restrict__ LSE,
+    const bf16_t* __restrict__ dO, const CT* __restrict__ C, const float* __restrict__ LSE,
     const float* Delta, const float* __restrict__ O, float* __restrict__ dQ,
-    float* __restrict__ dcq_out, float* delta_out, const int32_t* __restrict__ q_skip,
+    float* __restrict__ dcq_out, float* delta_out, float* lse_out,
+    const int32_t* __restrict__ q_skip,
     const int32_t* __restrict__ q_order, int L, int BH, int n_qt, float sl2e, float scale) {
   constexpr int NW = 8 / NB, BM = 256, NT = NW * 64, BN = 64;
   constexpr int TILE = BN * D;
@@ -460,8 +465,9 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   constexpr int NCOPY = 2 * BLK + 1;
   static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
   constexpr uint32_t TB = TILE * 2;
-  constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 6 * BN * 4];
+  constexpr uint32_t CS = sizeof(CT);  // bytes of one raw c value (fp32 or fp64)
+  constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * CS;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 4 * BN * CS + 2 * BN * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   V += base;
   dO += base;
   C += (size_t)bh * L;
-  const float c_ref = C[q0];
+  const CT c_ref = C[q0];
   const int qw = q0 + wave * 32 * NB;
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
   const int kt_last = q_last / BN;
@@ -494,9 +500,9 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   const int n_t = kt_last + 1 - kt_skip;
   const bool active = qw <= q_last;
   const int j0 = max(2 * kt_last + 2 - NB - qw / 32, 0);  // first sub-tile with a key <= a query of the wave
-  const i32x4 k_rs = buffer_words(K, (uint32_t)(L * D * 2));
-  const i32x4 v_rs = buffer_words(V, (uint32_t)(L * D * 2));
-  const i32x4 c_rs = buffer_words(C, (uint32_t)(L * 4));
+  const i32x4 k_rs = buffer_words(K, (uint32_t)L * (uint32_t)(D * 2));
+  const i32x4 v_rs = buffer_words(V, (uint32_t)L * (uint32_t)(D * 2));
+  const i32x4 c_rs = buffer_words(C, (uint32_t)L * CS);
   const uint32_t sbase = lds_addr(smem);
 
   int qi[NB];
@@ -522,7 +528,7 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
       }
     }
     // rows past the end get P = 0 through an infinite row offset
-    mrow[b] = qok[b] ? (LSE[(size_t)bh * L + qi[b]] - (C[qi[b]] - c_ref)) * kLog2e : INFINITY;
+    mrow[b] = qok[b] ? (LSE[(size_t)bh * L + qi[b]] - cdiff(C[qi[b]], c_ref)) * kLog2e : INFINITY;
     if (O) {
       // Delta_i = dO_i . O_i from the fp32 output, summed in delta_kernel's order: each group of
       // eight consecutive elements in order, then the D/8 groups as a balanced pairwise tree
@@ -576,9 +582,9 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
     }
   };
   auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {
-    if (lane < CW) {
-      const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * CW + lane) * 4;
-      copy4_to_lds(sbase + R_OFF + slot * BN * 4 + wave * CW * 4, voff, c_rs);
+    if (lane < CW * (int)CS / 4) {  // one 4-byte word per lane
+      const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * CW) * CS + lane * 4;
+      copy4_to_lds(sbase + R_OFF + slot * BN * CS + wave * CW * CS, voff, c_rs);
     }
   };
   auto start_copies = [&](int t, int skv, int sc) __attribute__((always_inline)) {
@@ -590,10 +596,10 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   };
   auto convert_c = [&](int t, int sr, int sb) __attribute__((always_inline)) {
     if (wave == 0 && t + 1 < n_t) {
-      const float cj = *(const __attribute__((address_space(3))) float*)(uintptr_t)(
-          sbase + R_OFF + sr * BN * 4 + lane * 4);
+      const CT cj = *(const __attribute__((address_space(3))) CT*)(uintptr_t)(
+          sbase + R_OFF + sr * BN * CS + lane * CS);
       *(__attribute__((address_space(3))) float*)(uintptr_t)(sbase + C_OFF + sb * BN * 4 + lane * 4) =
-          (cj - c_ref) * kLog2e;
+          cbias(cj, c_ref);
     }
   };
 
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
     }
     if (tid < BN) {
       const int key = k0 + tid;
-      ((float*)(smem + C_OFF))[tid] = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
+      ((float*)(smem + C_OFF))[tid] = key < L ? cbias(C[key], c_ref) : 0.f;
     }
     if (1 < n_t) {
       copy_kv(k_rs, K_OFF, 1, 1);
@@ -726,33 +732,45 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB
   }
   for (; t < n_t; ++t) generic_tile(t, std::false_type{});
 
-  // Row term consistent with this kernel's own P and dP: the forward's O was built from P
-  // rounded to bf16, so dO.O differs from sum_j P_ij dP_ij by ~1e-3 relative, and that residual
-  // would accumulate in d log f over every row that still attends across a position. With
-  // eps = sum_j P_ij (dP_ij - Delta_i) and S = sum_j P_ij, Delta'_i = Delta_i + eps / S makes
-  // sum_j P_ij (dP_ij - Delta'_i) vanish; the key-stationary step uses Delta', and dc^q is that
-  // (rounding-level) row sum. dQ keeps Delta: its error from the residual is ~scale*eps*|k|.
+  // Row terms consistent with this kernel's own P and dP.
+  // Normalisation: the forward's LSE is the log of the sum of the bf16-rounded weights that built
+  // O (and carries the rounding of c_i - c_ref), so exp(s - LSE) sums over a row to
+  // S = sum_j P_ij = 1 + O(2^-9), most off where a few keys dominate (after a hard reset). A
+  // row-constant error like that cancels in S: P_ij / S is the softmax to fp32 rounding. dQ and
+  // dc^q are scaled by 1 / S here, and LSE' = LSE + ln S goes to the key-stationary step, whose
+  // P then sums to one in every row; otherwise sum_i P_ij (...) in dc^k inherits the row errors
+  // and d log f accumulates them.
+  // Row term: the forward's O was built from P rounded to bf16, so dO.O differs from
+  // sum_j P_ij dP_ij by ~1e-3 relative, and that residual would accumulate in d log f over every
+  // row that still attends across a position. With eps = sum_j P_ij (dP_ij - Delta_i),
+  // Delta'_i = Delta_i + eps / S makes sum_j P_ij (dP_ij - Delta'_i) vanish; the key-stationary
+  // step uses Delta', and dc^q is that (rounding-level) row sum. dQ keeps Delta: its error from
+  // the residual is ~scale*eps*|k| / S.
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const float eps = xhalf_sum(dcq[b]);
     const float ptot = xhalf_sum(psum[b]);
     const float dl_new = dl[b] + eps / ptot;
-    const float dcq_tot = eps - (dl_new - dl[b]) * ptot;
+    const float inv = 1.0f / ptot;
+    const float dcq_tot = (eps - (dl_new - dl[b]) * ptot) * inv;
     if (qok[b]) {
       const size_t row = base + (size_t)qi[b] * D;
+      const float sc = scale * inv;
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int col = d * 32 + 8 * i + 4 * h;
           *reinterpret_cast<float4*>(dQ + row + col) =
-              make_float4(dqacc[b][d][4 * i] * scale, dqacc[b][d][4 * i + 1] * scale,
-                          dqacc[b][d][4 * i + 2] * scale, dqacc[b][d][4 * i + 3] * scale);
+              make_float4(dqacc[b][d][4 * i] * sc, dqacc[b][d][4 * i + 1] * sc,
+                          dqacc[b][d][4 * i + 2] * sc, dqacc[b][d][4 * i + 3] * sc);
         }
       }
       if (h == 0) {
-        dcq_out[(size_t)bh * L + qi[b]] = dcq_tot;
-        delta_out[(size_t)bh * L + qi[b]] = dl_new;
+        const size_t r = (size_t)bh * L + qi[b];
+        dcq_out[r] = dcq_tot;
+        delta_out[r] = dl_new;
+        lse_out[r] = LSE[r] + __logf(ptot);
       }
     }
   }
@@ -780,9 +798,10 @@ __device__ __forceinline__ float f32_dot(const float (&a)[DQ], const float* b) {
   return s + __shfl_xor(s, 32, 64);
 }
 // P_ij and dS_ij from the two dot products and the row / column terms.
-__device__ __forceinline__ void f32_ds(float qk, float dp, float scale, float ci, float cj,
+template <typename CT>
+__device__ __forceinline__ void f32_ds(float qk, float dp, float scale, CT ci, CT cj,
                                        float lse_i, float delta_i, float& p, float& ds) {
-  p = expf(fmaf(qk, scale, ci - cj) - lse_i);
+  p = expf(fmaf(qk, scale, cdiff(ci, cj)) - lse_i);
   ds = p * (dp - delta_i);
 }
 
@@ -802,18 +821,20 @@ __global__ __launch_bounds__(256) void delta_f32_kernel(const float* __restrict_
 
 // dQ, dc^q and the refined row term (as dq_pipe_kernel: Delta' makes the kernel's own row of dS
 // sum to zero; dc^q is the remaining rounding-level sum).
-template <int D>
+template <int D, typename CT>
 __global__ __launch_bounds__(64) void f32_dq_kernel(const float* __restrict__ Q,
                                                     const float* __restrict__ K,
                                                     const float* __restrict__ V,
                                                     const float* __restrict__ dO,
-                                                    const float* __restrict__ C,
+                                                    const CT* __restrict__ C,
                                                     const float* __restrict__ LSE,
                                                     const float* Delta, float* __restrict__ dQ,
                                                     float* __restrict__ dcq_out,
-                                                    float* delta_out, int L, float scale) {
+                                                    float* delta_out, float* lse_out, int L,
+                                                    float scale) {
   constexpr int DQ = D / 4;
-  __shared__ float k_s[kF32Tile][D], v_s[kF32Tile][D], c_s[kF32Tile];
+  __shared__ float k_s[kF32Tile][D], v_s[kF32Tile][D];
+  __shared__ CT c_s[kF32Tile];
   const int tid = threadIdx.x, part = tid >> 4;
   const int64_t bh = blockIdx.y;
   const int qi = blockIdx.x * kF32Rows + (tid & 15);
@@ -826,7 +847,7 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const float* __restrict__ Q,
     g[d] = qok ? dO[base + (size_t)qi * D + part * DQ + d] : 0.f;
     acc[d] = 0.f;
   }
-  const float ci = qok ? C[rbase + qi] : 0.f;
+  const CT ci = qok ? C[rbase + qi] : (CT)0;
   const float lse = qok ? LSE[rbase + qi] : 0.f;
   const float dl = qok ? Delta[rbase + qi] : 0.f;
   double eps = 0.0, ptot = 0.0;
@@ -838,7 +859,7 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const float* __restrict__ Q,
       k_s[r][d] = key < L ? K[base + (size_t)key * D + d] : 0.f;
       v_s[r][d] = key < L ? V[base + (size_t)key * D + d] : 0.f;
     }
-    if (tid < kF32Tile) c_s[tid] = k0 + tid < L ? C[rbase + k0 + tid] : 0.f;
+    if (tid < kF32Tile) c_s[tid] = k0 + tid < L ? C[rbase + k0 + tid] : (CT)0;
     __syncthreads();
     for (int j = 0; j < kF32Tile; ++j) {
       const float qk = f32_dot<DQ>(q, &k_s[j][part * DQ]);
@@ -860,23 +881,27 @@ __global__ __launch_bounds__(64) void f32_dq_kernel(const float* __restrict__ Q,
     const double dl_new = (double)dl + eps / ptot;
     dcq_out[rbase + qi] = (float)(eps - (dl_new - (double)dl) * ptot);
     delta_out[rbase + qi] = (float)dl_new;
+    // this path's forward sums the fp32 weights, so its rows already sum to one to fp32
+    // rounding: the row offset passes unchanged, and both steps form bit-identical dS
+    lse_out[rbase + qi] = lse;
   }
 }
 
 // dK, dV and dc^k (keys stationary; queries from the key's own onwards).
-template <int D>
+template <int D, typename CT>
 __global__ __launch_bounds__(64) void f32_dkv_kernel(const float* __restrict__ Q,
                                                      const float* __restrict__ K,
                                                      const float* __restrict__ V,
                                                      const float* __restrict__ dO,
-                                                     const float* __restrict__ C,
+                                                     const CT* __restrict__ C,
                                                      const float* __restrict__ LSE,
                                                      const float* __restrict__ Delta,
                                                      float* __restrict__ dK, float* __restrict__ dV,
                                                      float* __restrict__ dck_out, int L,
                                                      float scale) {
   constexpr int DQ = D / 4;
-  __shared__ float q_s[kF32Tile][D], o_s[kF32Tile][D], c_s[kF32Tile], l_s[kF32Tile], d_s[kF32Tile];
+  __shared__ float q_s[kF32Tile][D], o_s[kF32Tile][D], l_s[kF32Tile], d_s[kF32Tile];
+  __shared__ CT c_s[kF32Tile];
   const int tid = threadIdx.x, part = tid >> 4;
   const int64_t bh = blockIdx.y;
   const int k0 = blockIdx.x * kF32Rows;
@@ -891,7 +916,7 @@ __global__ __launch_bounds__(64) void f32_dkv_kernel(const float* __restrict__ Q
     dk[d] = 0.f;
     dv[d] = 0.f;
   }
-  const float cj = kok ? C[rbase + kj] : 0.f;
+  const CT cj = kok ? C[rbase + kj] : (CT)0;
   double dck = 0.0;
   for (int i0 = k0 / kF32Tile * kF32Tile; i0 < L; i0 += kF32Tile) {
     __syncthreads();
@@ -902,7 +927,7 @@ __global__ __launch_bounds__(64) void f32_dkv_kernel(const float* __restrict__ Q
     }
     if (tid < kF32Tile) {
       const int qq = i0 + tid;
-      c_s[tid] = qq < L ? C[rbase + qq] : 0.f;
+      c_s[tid] = qq < L ? C[rbase + qq] : (CT)0;
       l_s[tid] = qq < L ? LSE[rbase + qq] : 0.f;
       d_s[tid] = qq < L ? Delta[rbase + qq] : 0.f;
     }
@@ -941,32 +966,35 @@ void go_delta(const bf16_t* dO, const float* o, float* delta, int64_t rows, hipS
                      s, dO, o, delta, rows);
 }
 
-template <int D>
-void go_dkv(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
+template <int D, typename CT>
+void go_dkv(const bf16_t* q, const bf16_t* k, const bf16_t* v, const void* c, const float* lse,
             const bf16_t* dO, const float* delta, float* dk, float* dv, float* dck, int64_t BH,
             int64_t L, float scale, const SkipArgs& skip, hipStream_t s) {
   const int n_kt = (int)((L + 127) / 128);
-  hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k, v, dO,
-                     c, lse, delta, dk, dv, dck, skip.kv_tiles, skip.kv_order, (int)L, (int)BH,
-                     scale * kLog2e, scale);
+  hipLaunchKernelGGL((dkv_pipe_kernel<D, CT>), dim3((unsigned)(n_kt * BH)), dim3(256), 0, s, q, k,
+                     v, dO, (const CT*)c, lse, delta, dk, dv, dck, skip.kv_tiles, skip.kv_order,
+                     (int)L, (int)BH, scale * kLog2e, scale);
 }
 
-template <int D>
-void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* c, const float* lse,
+template <int D, typename CT>
+void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const void* c, const float* lse,
            const bf16_t* dO, const float* delta, const float* o, float* dq, float* dcq,
-           float* delta_out, int64_t BH, int64_t L, float scale, const SkipArgs& skip,
+           float* delta_out, float* lse_out, int64_t BH, int64_t L, float scale,
+           const SkipArgs& skip,
            hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
   // one 32-query block per wave, 8 waves (two per SIMD): measured 18% faster than 4 waves with
   // two blocks each, whose halved LDS traffic does not make up for the lost latency hiding
-  hipLaunchKernelGGL((dq_pipe_kernel<D, 1>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s, q, k, v,
-                     dO, c, lse, delta, o, dq, dcq, delta_out, skip.q_skip, skip.q_order, (int)L,
-                     (int)BH, n_qt, scale * kLog2e, scale);
+  hipLaunchKernelGGL((dq_pipe_kernel<D, 1, CT>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s, q, k,
+                     v, dO, (const CT*)c, lse, delta, o, dq, dcq, delta_out, lse_out, skip.q_skip,
+                     skip.q_order, (int)L, (int)BH, n_qt, scale * kLog2e, scale);
 }
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t BH, int64_t L) { return 3 * region_floats(BH, L) * sizeof(float); }
+// Four fp32 [BH, L] regions: the refined row term, dc^q, dc^k and the row offset LSE' that the
+// query-stationary step hands to the key-stationary one.
+size_t bwd_workspace_bytes(int64_t BH, int64_t L) { return 4 * region_floats(BH, L) * sizeof(float); }
 
 hipError_t launch_bwd_delta(const void* dO, const float* o, float* delta, int64_t rows, int64_t D,
                             hipStream_t s) {
@@ -975,29 +1003,48 @@ hipError_t launch_bwd_delta(const void* dO, const float* o, float* delta, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const float* c,
+hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, CPtr c,
                           const float* lse, const void* dO, const float* delta, float* dk,
                           float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
                           const SkipArgs& skip, hipStream_t s) {
-  if (D == 64)
-    go_dkv<64>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-               delta, dk, dv, dck, BH, L, scale, skip, s);
-  else
-    go_dkv<128>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-                delta, dk, dv, dck, BH, L, scale, skip, s);
+  const auto* Q = (const bf16_t*)q;
+  const auto* K = (const bf16_t*)k;
+  const auto* V = (const bf16_t*)v;
+  const auto* G = (const bf16_t*)dO;
+  if (D == 64) {
+    if (c.f64) go_dkv<64, double>(Q, K, V, c.p, lse, G, delta, dk, dv, dck, BH, L, scale, skip, s);
+    else go_dkv<64, float>(Q, K, V, c.p, lse, G, delta, dk, dv, dck, BH, L, scale, skip, s);
+  } else {
+    if (c.f64) go_dkv<128, double>(Q, K, V, c.p, lse, G, delta, dk, dv, dck, BH, L, scale, skip, s);
+    else go_dkv<128, float>(Q, K, V, c.p, lse, G, delta, dk, dv, dck, BH, L, scale, skip, s);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* c,
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, CPtr c,
                          const float* lse, const void* dO, const float* delta, const float* o,
-                         float* dq, float* dcq, float* delta_out, int64_t BH, int64_t L,
+                         float* dq, float* dcq, float* delta_out, float* lse_out, int64_t BH,
+                         int64_t L,
                          int64_t D, float scale, const SkipArgs& skip, hipStream_t s) {
-  if (D == 64)
-    go_dq<64>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-              delta, o, dq, dcq, delta_out, BH, L, scale, skip, s);
-  else
-    go_dq<128>((const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, c, lse, (const bf16_t*)dO,
-               delta, o, dq, dcq, delta_out, BH, L, scale, skip, s);
+  const auto* Q = (const bf16_t*)q;
+  const auto* K = (const bf16_t*)k;
+  const auto* V = (const bf16_t*)v;
+  const auto* G = (const bf16_t*)dO;
+  if (D == 64) {
+    if (c.f64)
+      go_dq<64, double>(Q, K, V, c.p, lse, G, delta, o, dq, dcq, delta_out, lse_out, BH, L, scale,
+                        skip, s);
+    else
+      go_dq<64, float>(Q, K, V, c.p, lse, G, delta, o, dq, dcq, delta_out, lse_out, BH, L, scale,
+                       skip, s);
+  } else {
+    if (c.f64)
+      go_dq<128, double>(Q, K, V, c.p, lse, G, delta, o, dq, dcq, delta_out, lse_out, BH, L, scale,
+                         skip, s);
+    else
+      go_dq<128, float>(Q, K, V, c.p, lse, G, delta, o, dq, dcq, delta_out, lse_out, BH, L, scale,
+                        skip, s);
+  }
   return hipGetLastError();
 }
 
@@ -1009,35 +1056,60 @@ hipError_t launch_bwd_delta_f32(const float* dO, const float* o, float* delta, i
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, const float* c,
-                             const float* lse, const float* dO, const float* delta, float* dq,
-                             float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
-                             float scale, hipStream_t s) {
+template <int D, typename CT>
+void go_dq_f32(const float* q, const float* k, const float* v, const void* c, const float* lse,
+               const float* dO, const float* delta, float* dq, float* dcq, float* delta_out,
+               float* lse_out, int64_t BH, int64_t L, float scale, hipStream_t s) {
   const dim3 grid((unsigned)((L + kF32Rows - 1) / kF32Rows), (unsigned)BH);
-  if (D == 64)
-    hipLaunchKernelGGL(f32_dq_kernel<64>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dq, dcq,
-                       delta_out, (int)L, scale);
-  else
-    hipLaunchKernelGGL(f32_dq_kernel<128>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dq, dcq,
-                       delta_out, (int)L, scale);
+  hipLaunchKernelGGL((f32_dq_kernel<D, CT>), grid, dim3(64), 0, s, q, k, v, dO, (const CT*)c, lse,
+                     delta, dq, dcq, delta_out, lse_out, (int)L, scale);
+}
+
+hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, CPtr c,
+                             const float* lse, const float* dO, const float* delta, float* dq,
+                             float* dcq, float* delta_out, float* lse_out, int64_t BH, int64_t L,
+                             int64_t D, float scale, hipStream_t s) {
+  if (D == 64) {
+    if (c.f64)
+      go_dq_f32<64, double>(q, k, v, c.p, lse, dO, delta, dq, dcq, delta_out, lse_out, BH, L, scale,
+                                     s);
+    else go_dq_f32<64, float>(q, k, v, c.p, lse, dO, delta, dq, dcq, delta_out, lse_out, BH, L, scale,
+                                     s);
+  } else {
+    if (c.f64)
+      go_dq_f32<128, double>(q, k, v, c.p, lse, dO, delta, dq, dcq, delta_out, lse_out, BH, L, scale,
+                                     s);
+    else go_dq_f32<128, float>(q, k, v, c.p, lse, dO, delta, dq, dcq, delta_out, lse_out, BH, L, scale,
+                                     s);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkv_f32(const float* q, const float* k, const float* v, const float* c,
+template <int D, typename CT>
+void go_dkv_f32(const float* q, const float* k, const float* v, const void* c, const float* lse,
+                const float* dO, const float* delta, float* dk, float* dv, float* dck, int64_t BH,
+                int64_t L, float scale, hipStream_t s) {
+  const dim3 grid((unsigned)((L + kF32Rows - 1) / kF32Rows), (unsigned)BH);
+  hipLaunchKernelGGL((f32_dkv_kernel<D, CT>), grid, dim3(64), 0, s, q, k, v, dO, (const CT*)c, lse,
+                     delta, dk, dv, dck, (int)L, scale);
+}
+
+hipError_t launch_bwd_dkv_f32(const float* q, const float* k, const float* v, CPtr c,
                               const float* lse, const float* dO, const float* delta, float* dk,
                               float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
                               hipStream_t s) {
-  const dim3 grid((unsigned)((L + kF32Rows - 1) / kF32Rows), (unsigned)BH);
-  if (D == 64)
-    hipLaunchKernelGGL(f32_dkv_kernel<64>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dk, dv,
-                       dck, (int)L, scale);
-  else
-    hipLaunchKernelGGL(f32_dkv_kernel<128>, grid, dim3(64), 0, s, q, k, v, dO, c, lse, delta, dk, dv,
-                       dck, (int)L, scale);
+  if (D == 64) {
+    if (c.f64) go_dkv_f32<64, double>(q, k, v, c.p, lse, dO, delta, dk, dv, dck, BH, L, scale, s);
+    else go_dkv_f32<64, float>(q, k, v, c.p, lse, dO, delta, dk, dv, dck, BH, L, scale, s);
+  } else {
+    if (c.f64)
+      go_dkv_f32<128, double>(q, k, v, c.p, lse, dO, delta, dk, dv, dck, BH, L, scale, s);
+    else go_dkv_f32<128, float>(q, k, v, c.p, lse, dO, delta, dk, dv, dck, BH, L, scale, s);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* c,
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, CPtr c,
                           const float* o, const float* lse, const float* dO, float* dq, float* dk,
                           float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
                           float scale, hipStream_t s) {
@@ -1045,16 +1117,17 @@ hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const 
   float* delta = (float*)ws;
   float* dcq = delta + R;
   float* dck = delta + 2 * R;
+  float* lse2 = delta + 3 * R;
   hipError_t e = launch_bwd_delta_f32(dO, o, delta, BH * L, D, s);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dq_f32(q, k, v, c, lse, dO, delta, dq, dcq, delta, BH, L, D, scale, s);
+  e = launch_bwd_dq_f32(q, k, v, c, lse, dO, delta, dq, dcq, delta, lse2, BH, L, D, scale, s);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkv_f32(q, k, v, c, lse, dO, delta, dk, dv, dck, BH, L, D, scale, s);
+  e = launch_bwd_dkv_f32(q, k, v, c, lse2, dO, delta, dk, dv, dck, BH, L, D, scale, s);
   if (e != hipSuccess) return e;
   return launch_rev_cumsum2(dcq, dck, dlog_f, BH, L, s);
 }
 
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, CPtr c,
                            const float* o, const float* lse, const void* dO, float* dq, float* dk,
                            float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
                            float scale, const void* plan, hipStream_t s) {
@@ -1063,12 +1136,13 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const fl
   float* delta = (float*)ws;
   float* dcq = delta + R;
   float* dck = delta + 2 * R;
-  // the query-stationary step forms the row term from O itself and writes the refined value;
-  // the key-stationary step reads the result
-  hipError_t e = launch_bwd_dq(q, k, v, c, lse, dO, nullptr, o, dq, dcq, delta, BH, L, D, scale,
-                               skip, s);
+  float* lse2 = delta + 3 * R;
+  // the query-stationary step forms the row term from O itself and writes the refined value and
+  // the normalised row offset; the key-stationary step reads both
+  hipError_t e = launch_bwd_dq(q, k, v, c, lse, dO, nullptr, o, dq, dcq, delta, lse2, BH, L, D,
+                               scale, skip, s);
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkv(q, k, v, c, lse, dO, delta, dk, dv, dck, BH, L, D, scale, skip, s);
+  e = launch_bwd_dkv(q, k, v, c, lse2, dO, delta, dk, dv, dck, BH, L, D, scale, skip, s);
   if (e != hipSuccess) return e;
   return launch_rev_cumsum2(dcq, dck, dlog_f, BH, L, s);
 }

@@ -87,10 +87,10 @@ __device__ __forceinline__ void interleave_step() {
 // the only one that evaluates the causal mask. From tile 4 on all waves are in step and run the
 // pipelined body; its main loop is unrolled over four tiles so that every ring slot is a
 // compile-time constant and every LDS address is a per-lane base register plus an immediate.
-template <int D>
+template <int D, typename CT>
 __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const float* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE,
+    const CT* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE,
     const int32_t* __restrict__ q_skip, const int32_t* __restrict__ q_order, int L, int BH,
     int n_qt, float sl2e, int o_f32) {
   constexpr int NW = 8, BM = NW * 32, NT = NW * 64, BN = kFwdBN;
@@ -101,8 +101,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   constexpr int NCOPY = 2 * BLK + 1;         // copies a wave starts per iteration (K, V, c)
   static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
   constexpr uint32_t TB = TILE * 2;  // bytes of one K or V tile
-  constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * 4;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 6 * BN * 4];
+  constexpr uint32_t CS = sizeof(CT);  // bytes of one raw c value (fp32 or fp64)
+  constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * CS;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 4 * BN * CS + 2 * BN * 4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses need it
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   K += base;
   V += base;
   C += (size_t)bh * L;
-  const float c_ref = C[q0];
+  const CT c_ref = C[q0];
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
@@ -136,9 +137,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   const int n_j = 2 * n_t;                   // sub-tiles
   const bool active = qw <= q_last;          // the wave holds at least one real query
   const int j0 = 2 * kt_last + 1 - qw / 32;  // the wave's diagonal sub-tile
-  const i32x4 k_rs = buffer_words(K, (uint32_t)(L * D * 2));
-  const i32x4 v_rs = buffer_words(V, (uint32_t)(L * D * 2));
-  const i32x4 c_rs = buffer_words(C, (uint32_t)(L * 4));
+  const i32x4 k_rs = buffer_words(K, (uint32_t)L * (uint32_t)(D * 2));
+  const i32x4 v_rs = buffer_words(V, (uint32_t)L * (uint32_t)(D * 2));
+  const i32x4 c_rs = buffer_words(C, (uint32_t)L * CS);
   const uint32_t sbase = lds_addr(smem);
 
   bf16x8 qf[D / 16];
@@ -176,9 +177,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
   };
   auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {  // 8 values per wave
-    if (lane < 8) {
-      const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * 8 + lane) * 4;
-      copy4_to_lds(sbase + R_OFF + slot * BN * 4 + wave * 32, voff, c_rs);
+    if (lane < 2 * (int)CS) {  // one 4-byte word per lane
+      const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * 8) * CS + lane * 4;
+      copy4_to_lds(sbase + R_OFF + slot * BN * CS + wave * 8 * CS, voff, c_rs);
     }
   };
   // Iteration t's copies: K(t + 3), V(t + 2), c(t + 3) (full tiles only: t >= 1).
@@ -192,10 +193,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   // Bias slice of tile t + 1 from its raw c values (wave 0).
   auto convert_c = [&](int t, int sr, int sb) __attribute__((always_inline)) {
     if (wave == 0 && t + 1 < n_t) {
-      const float cj = *(const __attribute__((address_space(3))) float*)(uintptr_t)(
-          sbase + R_OFF + sr * BN * 4 + lane * 4);
+      const CT cj = *(const __attribute__((address_space(3))) CT*)(uintptr_t)(
+          sbase + R_OFF + sr * BN * CS + lane * CS);
       *(__attribute__((address_space(3))) float*)(uintptr_t)(sbase + C_OFF + sb * BN * 4 + lane * 4) =
-          (cj - c_ref) * kLog2e;
+          cbias(cj, c_ref);
     }
   };
 
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
     if (tid < BN) {
       const int key = k0 + tid;
-      ((float*)(smem + C_OFF))[tid] = key < L ? (C[key] - c_ref) * kLog2e : 0.f;
+      ((float*)(smem + C_OFF))[tid] = key < L ? cbias(C[key], c_ref) : 0.f;
     }
     if (1 < n_t) {
       copy_kv(k_rs, K_OFF, 1, 1);
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
         }
       }
     }
-    if (h == 0 && LSE) LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + (C[qi] - c_ref);
+    if (h == 0 && LSE) LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + cdiff(C[qi], c_ref);
   }
 }
 
@@ -476,17 +477,17 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
 constexpr int kF32BM = 32;  // queries per workgroup (one wave, two lanes per query)
 constexpr int kF32BN = 32;  // keys per LDS tile
 
-template <int D>
+template <int D, typename CT>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q,
                                                      const float* __restrict__ K,
                                                      const float* __restrict__ V,
-                                                     const float* __restrict__ C,
+                                                     const CT* __restrict__ C,
                                                      float* __restrict__ O, float* __restrict__ LSE,
                                                      int L, float scale) {
   constexpr int DH = D / 2;
   __shared__ float k_s[kF32BN][D];
   __shared__ float v_s[kF32BN][D];
-  __shared__ float c_s[kF32BN];
+  __shared__ CT c_s[kF32BN];
   const int tid = threadIdx.x;
   const int half = tid >> 5;
   const int bh = blockIdx.y;
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   V += base;
   C += (size_t)bh * L;
   const bool qok = qi < L;
-  const float ci = qok ? C[qi] : 0.f;
+  const CT ci = qok ? C[qi] : (CT)0;
   float q[DH], o[DH];
 #pragma unroll
   for (int d = 0; d < DH; ++d) {
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
       k_s[r][d] = key < L ? K[(size_t)key * D + d] : 0.f;
       v_s[r][d] = key < L ? V[(size_t)key * D + d] : 0.f;
     }
-    if (tid < kF32BN) c_s[tid] = (k0 + tid) < L ? C[k0 + tid] : 0.f;
+    if (tid < kF32BN) c_s[tid] = (k0 + tid) < L ? C[k0 + tid] : (CT)0;
     __syncthreads();
     float s[kF32BN];
     float mx = -INFINITY;
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 #pragma unroll
       for (int d = 0; d < DH; ++d) dot = fmaf(q[d], k_s[j][half * DH + d], dot);
       dot += __shfl_xor(dot, 32, 64);
-      const float x = (k0 + j <= qi) ? fmaf(dot, scale, ci - c_s[j]) : -INFINITY;
+      const float x = (k0 + j <= qi) ? fmaf(dot, scale, cdiff(ci, c_s[j])) : -INFINITY;
       s[j] = x;
       mx = fmaxf(mx, x);
     }
@@ -554,33 +555,48 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
   if (half == 0 && LSE) LSE[(size_t)bh * L + qi] = m + logf(l);
 }
 
+template <int D, typename CT>
+void go_fwd_bf16(const void* q, const void* k, const void* v, const void* c, void* o, bool o_f32,
+                 float* lse, int64_t BH, int64_t L, float scale, const SkipArgs& skip,
+                 hipStream_t s) {
+  const int n_qt = (int)((L + 255) / 256);
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)c, o, lse,
+                     skip.q_skip, skip.q_order, (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+}
+
+template <int D, typename CT>
+void go_fwd_f32(const float* q, const float* k, const float* v, const void* c, float* o,
+                float* lse, int64_t BH, int64_t L, float scale, hipStream_t s) {
+  const dim3 grid((unsigned)((L + kF32BM - 1) / kF32BM), (unsigned)BH);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CT>), grid, dim3(64), 0, s, q, k, v, (const CT*)c, o, lse,
+                     (int)L, scale);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const float* c, void* o,
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
                            const SkipArgs& skip, hipStream_t s) {
-  const int n_qt = (int)((L + 255) / 256);
-  const dim3 grid((unsigned)(n_qt * BH)), block(512);
-  if (D == 64)
-    hipLaunchKernelGGL(fwd_bf16_pipe_kernel<64>, grid, block, 0, s, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, skip.q_skip, skip.q_order, (int)L,
-                       (int)BH, n_qt,
-                       scale * kLog2e, (int)o_f32);
-  else
-    hipLaunchKernelGGL(fwd_bf16_pipe_kernel<128>, grid, block, 0, s, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, c, o, lse, skip.q_skip, skip.q_order, (int)L,
-                       (int)BH, n_qt,
-                       scale * kLog2e, (int)o_f32);
+  if (D == 64) {
+    if (c.f64) go_fwd_bf16<64, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+    else go_fwd_bf16<64, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+  } else {
+    if (c.f64) go_fwd_bf16<128, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+    else go_fwd_bf16<128, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, const float* c, float* o,
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, CPtr c, float* o,
                           float* lse, int64_t BH, int64_t L, int64_t D, float scale, hipStream_t s) {
-  const dim3 grid((unsigned)((L + kF32BM - 1) / kF32BM), (unsigned)BH);
-  if (D == 64)
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, c, o, lse, (int)L, scale);
-  else
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, c, o, lse, (int)L, scale);
+  if (D == 64) {
+    if (c.f64) go_fwd_f32<64, double>(q, k, v, c.p, o, lse, BH, L, scale, s);
+    else go_fwd_f32<64, float>(q, k, v, c.p, o, lse, BH, L, scale, s);
+  } else {
+    if (c.f64) go_fwd_f32<128, double>(q, k, v, c.p, o, lse, BH, L, scale, s);
+    else go_fwd_f32<128, float>(q, k, v, c.p, o, lse, BH, L, scale, s);
+  }
   return hipGetLastError();
 }
 

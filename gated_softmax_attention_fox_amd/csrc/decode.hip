@@ -17,9 +17,11 @@
 // Exact skipping (optional). With the largest key norm of every 64 cached positions at hand
 // (kept beside the cache), a chunk whose every weight is provably below 2^-160 of the query's
 // own-key weight is not read: for a key j of the chunk, scale q_t.(k_j - k_t) - (c_j - c_t)
-// <= scale |q_t| (|k_j| + |k_t|) - (c_end - c_t), c_end the chunk's last c (c does not
-// increase). The combine would scale such a chunk by exp2(m_c - m) with m at least the
-// own-key logit, which is exactly 0 in fp32, so skipping it changes no bit of the result.
+// <= scale |q_t| (|k_j| + |k_t|) - (c_min - c_t), c_min the chunk's smallest c (its last one
+// when the gates lie in (0, 1); the chunk's c values are read to find it, 4 bytes per position
+// against the 4 D bytes of its key and value rows, so the test holds for any finite c). The
+// combine would scale such a chunk by exp2(m_c - m) with m at least the own-key logit, which is
+// exactly 0 in fp32, so skipping it changes no bit of the result.
 #include "fox_device.h"
 #include "fox_launch.h"
 
@@ -90,7 +92,12 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(
     for (int g = g0 + lane; g <= g1; g += 64) km = fmaxf(km, kn[g]);
 #pragma unroll
     for (int mk = 1; mk < 64; mk <<= 1) km = fmaxf(km, __shfl_xor(km, mk, 64));
-    const float ce = Cb[min(j0 + chunk, len) - 1];
+    const int j_end = min(j0 + chunk, len);
+    float ce = INFINITY;  // the chunk's smallest c; 16 loads in flight per lane
+#pragma unroll 16
+    for (int j = j0 + lane; j < j_end; j += 64) ce = fminf(ce, Cb[j]);
+#pragma unroll
+    for (int mk = 1; mk < 64; mk <<= 1) ce = fminf(ce, __shfl_xor(ce, mk, 64));
     const float slack = 1e-6f * (fabsf(ce) + fabsf(ct)) + 1.f;
     const float bound = sl2e * sqrtf(qq) * 1.00001f * (km + kn[t / 64]) + (slack - (ce - ct)) * kLog2e;
     if (bound < -160.f) {  // nothing in this chunk can carry weight: an empty partial

@@ -40,6 +40,16 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// c_a - c_b, and log2(e) (c_a - c_b), from the cumulative log decay in fp32 or fp64: the fp64
+// form subtracts exactly and rounds once, so the difference keeps its precision however large
+// |c| has grown (hard resets drive c to -1e5 and beyond, where fp32 values are 2^-6 apart).
+__device__ __forceinline__ float cdiff(float a, float b) { return a - b; }
+__device__ __forceinline__ float cdiff(double a, double b) { return (float)(a - b); }
+__device__ __forceinline__ float cbias(float a, float b) { return (a - b) * kLog2e; }
+__device__ __forceinline__ float cbias(double a, double b) {
+  return (float)((a - b) * 1.4426950408889634);
+}
+
 // bf16 <-> fp32 (round to nearest even on the way down, via the gfx950 convert instruction).
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 __device__ __forceinline__ bf16_t f2bf(float f) {

@@ -9,8 +9,14 @@
 
 namespace fox {
 
-// c[r, i] = sum_{l <= i} x[r, l] (fp64 accumulation, fp32 out).
+// c[r, i] = sum_{l <= i} x[r, l] (fp64 accumulation, fp32 out; fp64 out for launch_cumsum64).
 hipError_t launch_cumsum(const float* x, float* c, int64_t rows, int64_t L, hipStream_t s);
+hipError_t launch_cumsum64(const float* x, double* c, int64_t rows, int64_t L, hipStream_t s);
+// The cumulative log decay c as the attention kernels take it: fp32, or fp64 (FOX_C_F64).
+struct CPtr {
+  const void* p = nullptr;
+  bool f64 = false;
+};
 // out[r, l] = sum_{t >= l} (a[r, t] + b[r, t]) (fp64 accumulation, fp32 out).
 hipError_t launch_rev_cumsum2(const float* a, const float* b, float* out, int64_t rows, int64_t L,
                               hipStream_t s);
@@ -60,7 +66,7 @@ hipError_t launch_out_norm_gate_bwd(const void* o, bool o_bf16, const void* g, b
 //                                         most work first
 //   kv_order : int32 [BH * ceil(L / 128)] the same for the key blocks (index bh n_kb + kb)
 struct SkipPlanLayout {
-  size_t q_skip, kv_tiles, qn, kn, q_order, kv_order, bytes;
+  size_t q_skip, kv_tiles, qn, kn, cmin, cmax, q_order, kv_order, bytes;
 };
 SkipPlanLayout skip_plan_layout(int64_t BH, int64_t L);
 hipError_t launch_skip_plan(const void* q, const void* k, const float* c, void* plan, int64_t BH,
@@ -74,27 +80,28 @@ struct SkipArgs {
 };
 SkipArgs skip_args(const void* plan, int64_t BH, int64_t L);
 // Forward, bf16 inputs on MFMA; O in bf16 or fp32.
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, const float* c, void* o,
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
                            const SkipArgs& skip, hipStream_t s);
 // Forward, fp32 inputs and outputs, fp32 arithmetic throughout.
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, const float* c, float* o,
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, CPtr c, float* o,
                           float* lse, int64_t BH, int64_t L, int64_t D, float scale, hipStream_t s);
 // Workspace bytes of the bf16 backward.
 size_t bwd_workspace_bytes(int64_t BH, int64_t L);
-// Backward steps: Delta = rowsum(dO * O); query-stationary dQ, dc^q and the refined Delta
+// Backward steps: Delta = rowsum(dO * O); query-stationary dQ, dc^q, the refined Delta
 // (delta_out may equal delta; with delta null the step forms Delta from o itself, bit-identical
-// to launch_bwd_delta); key-stationary dK, dV, dc^k from the refined Delta.
+// to launch_bwd_delta) and the normalised row offset lse_out; key-stationary dK, dV, dc^k from
+// the refined Delta and lse_out.
 hipError_t launch_bwd_delta(const void* dO, const float* o, float* delta, int64_t rows, int64_t D,
                             hipStream_t s);
-hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, const float* c,
+hipError_t launch_bwd_dkv(const void* q, const void* k, const void* v, CPtr c,
                           const float* lse, const void* dO, const float* delta, float* dk,
                           float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
                           const SkipArgs& skip, hipStream_t s);
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* c,
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, CPtr c,
                          const float* lse, const void* dO, const float* delta, const float* o,
-                         float* dq, float* dcq, float* delta_out, int64_t BH, int64_t L,
-                         int64_t D, float scale, const SkipArgs& skip, hipStream_t s);
+                         float* dq, float* dcq, float* delta_out, float* lse_out, int64_t BH,
+                         int64_t L, int64_t D, float scale, const SkipArgs& skip, hipStream_t s);
 // Single-token decode against a KV cache [BH, T, D] (bf16) with c [BH, T] and per-sequence
 // lengths lens [B]: o [BH, D] (bf16 or fp32) and lse [BH]; workspace decode_workspace_bytes.
 // k_norms [BH, ceil(T / 64)] (largest key norm per 64 positions) or null: with it, chunks
@@ -116,19 +123,19 @@ hipError_t launch_decode_append(const void* k_new, const void* v_new, const floa
 // The fp32 backward (vector ALU): the same four steps and workspace as the bf16 path.
 hipError_t launch_bwd_delta_f32(const float* dO, const float* o, float* delta, int64_t rows,
                                 int64_t D, hipStream_t s);
-hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, const float* c,
+hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, CPtr c,
                              const float* lse, const float* dO, const float* delta, float* dq,
-                             float* dcq, float* delta_out, int64_t BH, int64_t L, int64_t D,
-                             float scale, hipStream_t s);
-hipError_t launch_bwd_dkv_f32(const float* q, const float* k, const float* v, const float* c,
+                             float* dcq, float* delta_out, float* lse_out, int64_t BH, int64_t L,
+                             int64_t D, float scale, hipStream_t s);
+hipError_t launch_bwd_dkv_f32(const float* q, const float* k, const float* v, CPtr c,
                               const float* lse, const float* dO, const float* delta, float* dk,
                               float* dv, float* dck, int64_t BH, int64_t L, int64_t D, float scale,
                               hipStream_t s);
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* c,
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, CPtr c,
                           const float* o, const float* lse, const float* dO, float* dq, float* dk,
                           float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
                           float scale, hipStream_t s);
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const float* c,
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, CPtr c,
                            const float* o, const float* lse, const void* dO, float* dq, float* dk,
                            float* dv, float* dlog_f, void* ws, int64_t BH, int64_t L, int64_t D,
                            float scale, const void* plan, hipStream_t s);

@@ -11,10 +11,11 @@
 // inputs exactly there); a row whose length is a multiple of 4 moves them as four 16-byte loads
 // and stores per thread. Each thread sums its 16 values, the workgroup scans the 1024 thread
 // totals with 64-wide wavefront shuffles plus one LDS step across the 16 waves, each thread
-// rewrites its values with the running fp64 sum, and the result is rounded once to fp32; the tile
-// total carries into the next tile. fp64 keeps c_i - c_j free of accumulated rounding: the only
-// error left is the single fp32 rounding of each c_i. The rows are short (a few hundred KB), so
-// the time is latency: the dependent chain per thread is 16 adds, not a full segment walk.
+// rewrites its values with the running fp64 sum, and the result is rounded once to fp32 (or kept
+// in fp64 for the fp64 form of c); the tile total carries into the next tile. fp64 keeps
+// c_i - c_j free of accumulated rounding: the only error left is the single rounding of each
+// c_i to the output type. The rows are short (a few hundred KB), so the time is latency: the
+// dependent chain per thread is 16 adds, not a full segment walk.
 #include "fox_device.h"
 #include "fox_launch.h"
 
@@ -36,12 +37,21 @@ __device__ __forceinline__ double scan_load(const float* __restrict__ a, const f
   return (double)a[i];
 }
 
+// 16-byte store of four consecutive outputs (two for fp64 values, done twice).
+__device__ __forceinline__ void store4(float* p, const float (&r)[4]) {
+  *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
+}
+__device__ __forceinline__ void store4(double* p, const double (&r)[4]) {
+  reinterpret_cast<double2*>(p)[0] = make_double2(r[0], r[1]);
+  reinterpret_cast<double2*>(p)[1] = make_double2(r[2], r[3]);
+}
+
 // Forward: out[i] = sum_{l<=i} a[l]. Reverse: out[l] = sum_{t>=l} (a[t] + b[t]). Scan position
-// k is memory position k (forward) or L-1-k (reverse).
-template <bool kReverse>
+// k is memory position k (forward) or L-1-k (reverse). OutT: float, or double for the fp64 c.
+template <bool kReverse, typename OutT>
 __global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(const float* __restrict__ a,
                                                                  const float* __restrict__ b,
-                                                                 float* __restrict__ out,
+                                                                 OutT* __restrict__ out,
                                                                  int64_t L) {
   __shared__ double wave_tot[2][kScanWaves];  // two copies: a pass never waits for the last reads
   const int64_t row = blockIdx.x;
@@ -105,15 +115,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(const float* __
     if (full) {
 #pragma unroll
       for (int g = 0; g < kScanPer / 4; ++g) {
-        float r[4];
+        OutT r[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = (float)v[kReverse ? kScanPer - 1 - (4 * g + e) : 4 * g + e];
-        *reinterpret_cast<float4*>(out + p0 + 4 * g) = make_float4(r[0], r[1], r[2], r[3]);
+        for (int e = 0; e < 4; ++e) r[e] = (OutT)v[kReverse ? kScanPer - 1 - (4 * g + e) : 4 * g + e];
+        store4(out + p0 + 4 * g, r);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kScanPer; ++j) {
-        if (j < cnt) out[kReverse ? (L - 1 - (k0 + j)) : (k0 + j)] = (float)v[j];
+        if (j < cnt) out[kReverse ? (L - 1 - (k0 + j)) : (k0 + j)] = (OutT)v[j];
       }
     }
   }
@@ -122,15 +132,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_rows_kernel(const float* __
 }  // namespace
 
 hipError_t launch_cumsum(const float* x, float* c, int64_t rows, int64_t L, hipStream_t s) {
-  hipLaunchKernelGGL(scan_rows_kernel<false>, dim3((unsigned)rows), dim3(kScanThreads), 0, s, x,
-                     (const float*)nullptr, c, L);
+  hipLaunchKernelGGL((scan_rows_kernel<false, float>), dim3((unsigned)rows), dim3(kScanThreads), 0,
+                     s, x, (const float*)nullptr, c, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_cumsum64(const float* x, double* c, int64_t rows, int64_t L, hipStream_t s) {
+  hipLaunchKernelGGL((scan_rows_kernel<false, double>), dim3((unsigned)rows), dim3(kScanThreads),
+                     0, s, x, (const float*)nullptr, c, L);
   return hipGetLastError();
 }
 
 hipError_t launch_rev_cumsum2(const float* a, const float* b, float* out, int64_t rows, int64_t L,
                               hipStream_t s) {
-  hipLaunchKernelGGL(scan_rows_kernel<true>, dim3((unsigned)rows), dim3(kScanThreads), 0, s, a, b,
-                     out, L);
+  hipLaunchKernelGGL((scan_rows_kernel<true, float>), dim3((unsigned)rows), dim3(kScanThreads), 0, s,
+                     a, b, out, L);
   return hipGetLastError();
 }
 

@@ -24,8 +24,14 @@
  *     not implement) and enqueues nothing; fox_last_error() then describes it. A failed
  *     launch returns FOX_E_LAUNCH. No C++ exception or abort crosses this boundary.
  *   - Preconditions not checked on the device: log f must be finite (the pages' log 0 = -inf
- *     would make c_i - c_j undefined; a hard reset is a large finite negative value such as
- *     -1e4); NaN inputs propagate to NaN outputs.
+ *     would make c_i - c_j undefined); NaN inputs propagate to NaN outputs. A hard reset is a
+ *     large finite negative log f: -200 already cuts every earlier weight exactly (exp
+ *     underflows in fp32). Deeper values only make |c| large, and fp32 c is spaced 2^-10 at
+ *     |c| ~ 2^14 and 2^-7 at 2^17, which then shows in the results; pass fp64 c (FOX_C_F64)
+ *     for resets of -1e4 and the like. Within one 256-position block, the kernels hold c
+ *     differences in fp32 relative to one reference, so a fall of c beyond ~1e5 inside a
+ *     single block (many consecutive resets of -1e4) leaves an error of about 2^-24 |fall| in
+ *     the weights next to it whatever the type of c.
  *   - Calls are reentrant: the library holds no mutable global state apart from the
  *     thread-local error message.
  */
@@ -48,16 +54,24 @@ typedef enum fox_status {
 
 typedef enum fox_dtype { FOX_F32 = 0, FOX_BF16 = 1 } fox_dtype;
 
-/* Flags of fox_attn_fwd / fox_attn_bwd. FOX_CAUSAL is required: the method is defined for
- * causal sequence modelling only (paperlayer.ai summary, section 6 "CONCLUSION", limitations:
- * the non-causal case is future work). */
-enum { FOX_CAUSAL = 1u };
+/* Flags of fox_attn_fwd / fox_attn_bwd and the backward steps. FOX_CAUSAL is required: the
+ * method is defined for causal sequence modelling only (paperlayer.ai summary, section 6
+ * "CONCLUSION", limitations: the non-causal case is future work).
+ * FOX_C_F64: c holds fp64 values (from fox_logf_cumsum_f64) instead of fp32. The kernels then
+ * form every c_i - c_j in fp64 and round the difference once, so it keeps full precision however
+ * far c has fallen; with fp32 c each value carries a rounding of up to half the fp32 spacing at
+ * |c| (2^-9 at |c| ~ 2^14, 2^-7 at |c| ~ 2^17), which hard resets (log f ~ -1e4) reach within a
+ * few positions. Not taken together with a skip plan (FOX_E_UNSUPPORTED). */
+enum { FOX_CAUSAL = 1u, FOX_C_F64 = 2u };
 
 /* Cumulative log decay (paper-graph-ui summary, "Hardware-Aware Implementation": c is the
  * cumulative sum of log f, computed once per head before attention and kept in HBM).
  *   log_f : [BH, L] fp32 input;  c : [BH, L] fp32 output, c[r, i] = sum_{l<=i} log_f[r, l].
  * Accumulates in fp64 and rounds once to fp32. c may not alias log_f. */
 fox_status fox_logf_cumsum(const float* log_f, float* c, int64_t BH, int64_t L, void* stream);
+/* The same prefix sum kept in fp64 (c : [BH, L] fp64 output; the accumulation is fp64 either
+ * way), for the attention calls with FOX_C_F64. */
+fox_status fox_logf_cumsum_f64(const float* log_f, double* c, int64_t BH, int64_t L, void* stream);
 
 /* Scalar per-head forget gate in log space (paper-graph-ui summary, "Forget Gate Computation";
  * Pro block Step 4): log_f[b, h, t] = log sigmoid(sum_d x[b, t, d] * w_f[h, d] + b_f[h]).
@@ -115,19 +129,23 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
  * results are bit-identical to those without a plan.
  * The bound: for a query i and an earlier key j,
  *   scale q_i.k_j + c_i - c_j - (scale q_i.k_i) <= scale |q_i| (|k_j| + |k_i|) - (c_j - c_i),
- * evaluated per tile with the largest row norms of q and k in each 64-row group and with c at
- * the tile ends (c does not increase), plus a slack for the fp32 rounding of c. The forward's
- * running maximum and the backward's LSE are never below the diagonal logit scale q_i.k_i.
+ * evaluated per tile with the largest row norms of q and k in each 64-row group, the smallest c
+ * of the key tile and the largest c of the query tile (with gates in (0, 1), c at the key tile's
+ * last and the query tile's first position), plus a slack for the fp32 rounding of c. The
+ * extremes are taken per 64-row group, so the plan is exact for any finite c, rising or not.
+ * The forward's running maximum and the backward's LSE are never below the diagonal logit
+ * scale q_i.k_i.
  *   fox_attn_skip_plan_bytes : bytes of device memory a plan takes for these sizes.
  *   fox_attn_skip_plan       : fills `plan` (256-byte aligned, at least that many bytes) from
  *                              q, k (bf16, [B, H, L, D]), c and scale. Reads q and k once.
  *                              Supports B*H <= 65535 (FOX_E_UNSUPPORTED beyond).
- * Plan layout (four arrays, each starting at the next 256-byte boundary, BH = B * H):
+ * Plan layout (arrays in this order, each starting at the next 256-byte boundary, BH = B * H):
  *   int32 q_skip[BH][ceil(L / 256)]   key tiles of 64 keys, counted from key 0, that the
  *                                     256-query tile skips (the forward and dq steps);
  *   int32 kv_tiles[BH][ceil(L / 128)] 64-query tiles, counted from the block's first key, that
  *                                     the 128-key block walks (the dk/dv step);
  *   fp32 qn[BH][ceil(L / 64)], kn[...] largest row norm of q and k in each 64-row group;
+ *   fp32 cmin[BH][ceil(L / 64)], cmax[...] smallest and largest c in each 64-row group;
  *   int32 q_order[BH * ceil(L / 256)]  launch order of the query tiles (entry bh * ceil(L / 256)
  *                                     + tile), most work first; entries of equal work may come
  *                                     in a different order on each call (results do not depend
@@ -191,14 +209,15 @@ fox_status fox_out_norm_gate_bwd(const void* o, fox_dtype o_dt, const void* g, f
  *   lse[i] = log sum_{j<=i} exp(scale * q_i . k_j + c_i - c_j)     (natural log, fp32)
  * The scale multiplies q.k only; the bias is added unscaled. Only differences of c matter,
  * so any per-(b,h) constant offset in c leaves O and lse unchanged.
- *   q, k, v : in_dt (FOX_BF16, or FOX_F32 for the full-fp32 path);  c : fp32
+ *   q, k, v : in_dt (FOX_BF16, or FOX_F32 for the full-fp32 path)
+ *   c       : fp32, or fp64 with FOX_C_F64 in flags
  *   o       : o_dt (FOX_BF16 or FOX_F32; must be FOX_F32 when in_dt is FOX_F32)
  *   lse     : fp32, may be NULL if not wanted.
  * bf16 inputs run on bf16 MFMA with fp32 accumulation and an fp32 online softmax; fp32
  * inputs run fully in fp32. flags must contain FOX_CAUSAL. skip_plan: NULL, or a plan from
  * fox_attn_skip_plan for these q, k, c and scale (bf16 inputs only). */
 fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                        const float* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
+                        const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
                         int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
                         const void* skip_plan, void* stream);
 
@@ -207,7 +226,7 @@ size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
 
 /* Backward of the loss sum(dO * O) (paper-graph-ui summary, "Hardware-Aware Implementation",
  * the backward pass; paperlayer.ai summary, section E): recomputes P from lse with the same
- * bias, and returns
+ * bias (c fp32, or fp64 with FOX_C_F64, as given to the forward), and returns
  *   dq, dk, dv : [B, H, L, D] fp32
  *   dlog_f     : [B, H, L] fp32, the reverse cumulative sum of dc = dc^q + dc^k with
  *                dc^q_i = sum_j dS_ij and dc^k_j = -sum_i dS_ij.
@@ -219,7 +238,7 @@ size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);
  * entry and clobbered. Deterministic: identical inputs give bit-identical outputs. skip_plan:
  * NULL, or the plan of these q, k, c and scale (see fox_attn_skip_plan). */
 fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                        const float* c, const float* o, const float* lse, const void* dO,
+                        const void* c, const float* o, const float* lse, const void* dO,
                         float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
                         size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
                         float scale, uint32_t flags, const void* skip_plan, void* stream);
@@ -234,26 +253,32 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
 fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, float* delta,
                               int64_t rows, int64_t D, void* stream);
 
-/* Step 2, query-stationary: dq ([B,H,L,D] fp32), dc_q[i] = sum_j dS_ij ([B,H,L] fp32), and
- * delta_out ([B,H,L] fp32, may equal delta): the row term refined so that each row of dS sums to
- * zero under the P and dP this library recomputes. The forward rounds P to bf16 before the PV
- * product, so dO . O matches sum_j P_ij dP_ij only to ~1e-3 relative; d log f sums that
- * residual over every row that attends across a position, hence the refinement.
+/* Step 2, query-stationary: dq ([B,H,L,D] fp32), dc_q[i] = sum_j dS_ij ([B,H,L] fp32),
+ * delta_out ([B,H,L] fp32, may equal delta) and lse_out ([B,H,L] fp32, must not alias lse).
+ * delta_out is the row term refined so that each row of dS sums to zero under the P and dP this
+ * library recomputes: the forward rounds P to bf16 before the PV product, so dO . O matches
+ * sum_j P_ij dP_ij only to ~1e-3 relative, and d log f sums that residual over every row that
+ * attends across a position. lse_out is the row offset that makes each recomputed row of P sum
+ * to one: the forward's lse is the log of the sum of the bf16-rounded weights that built O, which
+ * leaves exp(s - lse) summing to 1 + O(2^-9) over a row (most off where a few keys dominate, as
+ * after a hard reset); the step scales dq and dc_q by the inverse of that sum and returns
+ * lse + log(sum) for step 3. (The full-fp32 path's forward sums fp32 weights; it copies lse.)
  * The row term comes from delta (step 1's output) when it is not NULL, and o is then not read.
  * With delta = NULL, o ([B,H,L,D] fp32, the forward output) must be given and the step forms
  * Delta_i = dO_i . O_i itself, bit-identical to step 1 (the bf16 path in the same kernel; the
  * fp32 path as a launch of step 1 into delta_out first). Both NULL: FOX_E_INVALID. skip_plan as
  * for fox_attn_bwd. */
 fox_status fox_attn_bwd_dq(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                           const float* c, const float* lse, const void* dO, const float* o,
+                           const void* c, const float* lse, const void* dO, const float* o,
                            const float* delta, float* dq, float* dc_q, float* delta_out,
-                           int64_t B, int64_t H, int64_t L, int64_t D, float scale,
-                           uint32_t flags, const void* skip_plan, void* stream);
+                           float* lse_out, int64_t B, int64_t H, int64_t L, int64_t D,
+                           float scale, uint32_t flags, const void* skip_plan, void* stream);
 
 /* Step 3, key-stationary: dk, dv ([B,H,L,D] fp32) and dc_k[j] = -sum_i dS_ij ([B,H,L] fp32).
- * delta must be step 2's delta_out; the other inputs (skip_plan too) as for fox_attn_bwd. */
+ * lse must be step 2's lse_out and delta step 2's delta_out; the other inputs (skip_plan too)
+ * as for fox_attn_bwd. */
 fox_status fox_attn_bwd_dkv(const void* q, const void* k, const void* v, fox_dtype in_dt,
-                            const float* c, const float* lse, const void* dO, const float* delta,
+                            const void* c, const float* lse, const void* dO, const float* delta,
                             float* dk, float* dv, float* dc_k, int64_t B, int64_t H, int64_t L,
                             int64_t D, float scale, uint32_t flags, const void* skip_plan,
                             void* stream);
@@ -280,9 +305,10 @@ fox_status fox_dlogf_from_dc(const float* dc_q, const float* dc_k, float* dlog_f
  *             (fox_attn_decode_key_norms, kept current by fox_attn_decode_append), or NULL.
  *             With it, chunks of the cache whose every weight is provably below 2^-160 of the
  *             query's own-key weight (scale q.(k_j - k_t) - (c_j - c_t) <= scale |q| (|k_j| +
- *             |k_t|) - (c_end - c_t)) are not read; the result is bit-identical, since such a
- *             chunk would enter the combination scaled by exactly 0 in fp32. A stale k_norms
- *             gives wrong results.
+ *             |k_t|) - (c_min - c_t), c_min the chunk's smallest c, read from c_cache) have
+ *             their keys and values not read; the result is bit-identical for any finite c,
+ *             since such a chunk would enter the combination scaled by exactly 0 in fp32. A
+ *             stale k_norms gives wrong results.
  *   o       : [B, H, D] in o_dt (FOX_BF16 or FOX_F32);  lse : [B, H] fp32 or NULL
  *   workspace : at least fox_attn_decode_workspace_bytes(B, H, T_max, D) bytes, 256-byte
  *             aligned, contents ignored and clobbered.

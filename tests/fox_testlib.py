@@ -26,7 +26,11 @@ def dev(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    return t.detach().float().cpu().numpy().astype(np.float64)
+    """fp64 NumPy copy (bf16 widened exactly; fp64 kept as is)."""
+    t = t.detach()
+    if t.dtype != torch.float64:
+        t = t.float()
+    return t.cpu().numpy().astype(np.float64)
 
 
 def errors(got, ref):
@@ -38,7 +42,8 @@ def errors(got, ref):
     return maxabs, rel
 
 
-def check(name, got, ref, maxabs=BF16_MAXABS, rel_l2=BF16_RELL2):
+def check(name, got, ref, maxabs=BF16_MAXABS, rel_l2=BF16_RELL2, quiet=False):
+    """Assert max-abs and relative-L2 bars; quiet prints only on failure."""
     got = np.asarray(got, np.float64)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     m, r = errors(got, ref)
@@ -46,7 +51,9 @@ def check(name, got, ref, maxabs=BF16_MAXABS, rel_l2=BF16_RELL2):
     if rel_l2 is not None and np.linalg.norm(np.asarray(ref, np.float64)) < 1e-6:
         rel_l2 = None
     rl = "n/a" if rel_l2 is None else f"{rel_l2:g}"
-    say(f"  {name}: max-abs {m:.3e} (<= {maxabs:g})  rel-L2 {r:.3e} (<= {rl})")
+    bad = m > maxabs or (rel_l2 is not None and r > rel_l2)
+    if bad or not quiet:
+        say(f"  {name}: max-abs {m:.3e} (<= {maxabs:g})  rel-L2 {r:.3e} (<= {rl})")
     assert m <= maxabs, f"{name}: max-abs {m:.3e} > {maxabs:g}"
     if rel_l2 is not None:
         assert r <= rel_l2, f"{name}: rel-L2 {r:.3e} > {rel_l2:g}"

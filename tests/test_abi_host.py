@@ -46,9 +46,9 @@ def test_status_strings_and_version(lib):
 
 
 def test_workspace_size(lib):
-    # three fp32 [B*H*L] regions, each rounded up to 256 bytes
-    assert lib.fox_attn_bwd_workspace_bytes(1, 12, 16384, 128) == 3 * 12 * 16384 * 4
-    assert lib.fox_attn_bwd_workspace_bytes(1, 1, 1, 64) == 3 * 256
+    # four fp32 [B*H*L] regions (row term, dc^q, dc^k, row offset), each rounded up to 256 bytes
+    assert lib.fox_attn_bwd_workspace_bytes(1, 12, 16384, 128) == 4 * 12 * 16384 * 4
+    assert lib.fox_attn_bwd_workspace_bytes(1, 1, 1, 64) == 4 * 256
     assert lib.fox_attn_bwd_workspace_bytes(0, 1, 1, 64) == 0
 
 
@@ -70,8 +70,8 @@ def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o
     (dict(q=0), 1), (dict(k=P + 8), 1), (dict(c=0), 1), (dict(o=0), 1), (dict(lse=P + 4), 1),
     (dict(D=96), 1), (dict(D=256), 1), (dict(L=0), 1), (dict(L=(1 << 23) + 1), 1), (dict(B=0), 1),
     (dict(H=-1), 1), (dict(in_dt=7), 1), (dict(o_dt=3), 1), (dict(in_dt=0, o_dt=1), 1), (dict(scale=0.0), 1),
-    (dict(scale=float("nan")), 1), (dict(flags=0), 2), (dict(flags=3), 2),
-    (dict(plan=P + 16), 1), (dict(in_dt=0, o_dt=0, plan=P), 2),
+    (dict(scale=float("nan")), 1), (dict(flags=0), 2), (dict(flags=5), 2), (dict(flags=2), 2),
+    (dict(flags=3, plan=P), 2), (dict(plan=P + 16), 1), (dict(in_dt=0, o_dt=0, plan=P), 2),
 ])
 def test_forward_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
@@ -93,8 +93,8 @@ def test_backward_rejects(lib, kw, status):
 
 
 def _bwd_dq(lib, o=P, delta=P, in_dt=1, plan=None):
-    return lib.fox_attn_bwd_dq(P, P, P, in_dt, P, P, P, o, delta, P, P, P, 1, 2, 64, 128, 0.1, 1,
-                               plan, None)
+    return lib.fox_attn_bwd_dq(P, P, P, in_dt, P, P, P, o, delta, P, P, P, P + 1024, 1, 2, 64, 128,
+                               0.1, 1, plan, None)
 
 
 @host_only
@@ -122,10 +122,10 @@ def test_scan_gate_norm_reject(lib):
 
 
 def test_skip_plan_size(lib):
-    # int32 [12, 64] + int32 [12, 128] + 2 x fp32 [12, 256] + int32 [768] + int32 [1536], each
-    # rounded up to 256 bytes
-    assert lib.fox_attn_skip_plan_bytes(1, 12, 16384, 128) == 4 * 12 * (64 + 128 + 256 + 256 + 64 + 128)
-    assert lib.fox_attn_skip_plan_bytes(1, 1, 1, 64) == 6 * 256
+    # int32 [12, 64] + int32 [12, 128] + 4 x fp32 [12, 256] (q and k norms, smallest and largest
+    # c) + int32 [768] + int32 [1536], each rounded up to 256 bytes
+    assert lib.fox_attn_skip_plan_bytes(1, 12, 16384, 128) == 4 * 12 * (64 + 128 + 4 * 256 + 64 + 128)
+    assert lib.fox_attn_skip_plan_bytes(1, 1, 1, 64) == 8 * 256
     assert lib.fox_attn_skip_plan_bytes(1, 0, 1, 64) == 0
 
 
@@ -213,6 +213,7 @@ def test_binding_rejects_cpu_tensors(lib):
         fox.fox_attn_fwd(x, x, x, c)
 
 
+@host_only
 def test_pro_backward_rejects(lib):
     ws = 256 * 1024  # a 256-aligned stand-in address, never dereferenced
     f = lib.fox_gate_logf_bwd
@@ -230,3 +231,4 @@ def test_pro_backward_rejects(lib):
     assert g(P, 1, P, P, P, P, None, 0, 10, 128, ctypes.c_float(1e-6), None) == 1  # no workspace
     assert g(P, 1, P, P, None, None, None, 0, 10, 128, ctypes.c_float(-1.0), None) == 1  # eps
     assert lib.fox_qk_rmsnorm_bwd_workspace_bytes(10, 128) >= 1024 * 128 * 4
+

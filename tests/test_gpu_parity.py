@@ -29,9 +29,9 @@ def fox():
     return f
 
 
-def _run_fwd(fox, case, o_dtype):
+def _run_fwd(fox, case, o_dtype, c_dtype=torch.float32):
     q, k, v = (dev(getattr(case, n), case.dtype) for n in "qkv")
-    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"), dtype=c_dtype)
     o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=o_dtype)
     torch.cuda.synchronize()
     return host(c), host(o), host(lse)
@@ -120,47 +120,47 @@ def test_forward_structured_gates(fox, gate):
 
 
 def test_forward_config2(fox):
-    """B=4, H=12, L=2048, D=128 bf16: 8 whole heads plus sampled rows of every head."""
+    """B=4, H=12, L=2048, D=128 bf16: every row of all 48 heads, bf16 and fp32 O."""
     case = fi.config_case(2)
     say("fwd config2")
     c, o, lse = _run_fwd(fox, case, torch.bfloat16)
     _, o32, lse32 = _run_fwd(fox, case, torch.float32)
-    s = default_scale(case.D)
-    rng = np.random.default_rng(0)
-    heads = [(b, h) for b in range(case.B) for h in range(case.H)]
-    full = [heads[i] for i in rng.choice(len(heads), 8, replace=False)]
-    for b, h in full:
-        O, LSE = oracle.attn_fwd(case.q[b:b + 1, h:h + 1], case.k[b:b + 1, h:h + 1],
-                                 case.v[b:b + 1, h:h + 1], case.log_f[b:b + 1, h:h + 1], scale=s)
-        check(f"O bf16 (b{b},h{h})", o[b, h], O[0, 0])
-        check(f"O fp32 (b{b},h{h})", o32[b, h], O[0, 0])
-        check(f"LSE (b{b},h{h})", lse[b, h], LSE[0, 0])
-    cc = oracle.cumsum_logf(case.log_f)
-    got, ref, gl, rl = [], [], [], []
-    for b, h in heads:
-        rows = sample_rows(case.L, 12, seed=b * 100 + h)
-        O, LSE = oracle.attn_fwd_rows(case.q[b, h], case.k[b, h], case.v[b, h], cc[b, h], rows,
-                                      scale=s)
-        got.append(o[b, h, rows]); ref.append(O); gl.append(lse[b, h, rows]); rl.append(LSE)
-    check("O sampled rows, all heads", np.concatenate(got), np.concatenate(ref))
-    check("LSE sampled rows, all heads", np.concatenate(gl), np.concatenate(rl))
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=default_scale(case.D))
+    check("O bf16, all heads", o, O)
+    check("O fp32, all heads", o32, O)
+    check("LSE, all heads", lse, LSE)
+    check("LSE (fp32 O run), all heads", lse32, LSE)
+    for b in range(case.B):
+        for h in range(case.H):  # each head alone meets the bar too
+            check(f"O (b{b},h{h})", o[b, h], O[b, h], quiet=True)
+            check(f"LSE (b{b},h{h})", lse[b, h], LSE[b, h], quiet=True)
 
 
-def test_forward_config3_full_length(fox):
-    """B=1, H=12, L=16384, D=128 bf16 at the launch configuration the benchmark times."""
+@pytest.fixture(scope="module")
+def config3_oracle():
+    """The oracle's O and LSE of workload 3 (every row of all 12 heads), shared with the
+    full-length backward test, whose inputs are workload 3's plus dO."""
+    case = fi.config_case(3)
+    say("oracle forward of workload 3 (12 heads, L=16384) ...")
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=default_scale(case.D),
+                             block=1024)
+    return O, LSE
+
+
+def test_forward_config3_full_length(fox, config3_oracle):
+    """B=1, H=12, L=16384, D=128 bf16 at the launch configuration the benchmark times: every row
+    of every head against the oracle, each head separately and all together."""
     case = fi.config_case(3)
     say("fwd config3 (L=16384)")
     c, o, lse = _run_fwd(fox, case, torch.bfloat16)
-    s = default_scale(case.D)
-    cc = oracle.cumsum_logf(case.log_f)
-    got, ref, gl, rl = [], [], [], []
+    _, o32, lse32 = _run_fwd(fox, case, torch.float32)
+    O, LSE = config3_oracle
+    check("O bf16, all rows and heads", o, O)
+    check("O fp32, all rows and heads", o32, O)
+    check("LSE, all rows and heads", lse, LSE)
     for h in range(case.H):
-        rows = sample_rows(case.L, 40, seed=h, tile=128)
-        O, LSE = oracle.attn_fwd_rows(case.q[0, h], case.k[0, h], case.v[0, h], cc[0, h], rows,
-                                      scale=s)
-        got.append(o[0, h, rows]); ref.append(O); gl.append(lse[0, h, rows]); rl.append(LSE)
-    check("O sampled rows", np.concatenate(got), np.concatenate(ref))
-    check("LSE sampled rows", np.concatenate(gl), np.concatenate(rl))
+        check(f"O (h{h})", o[0, h], O[0, h])
+        check(f"LSE (h{h})", lse[0, h], LSE[0, h])
 
 
 @pytest.mark.parametrize("per_wg", [2, 3, 4, 5])
@@ -235,7 +235,8 @@ def test_qk_rmsnorm_matches_oracle(fox, D):
 
 
 def test_pro_pipeline_config4(fox):
-    """x -> gate -> scan, q,k -> QK-norm, then the forward; sampled rows at L = 16384."""
+    """x -> gate -> scan, q,k -> QK-norm, then the forward: every row of all 12 heads at
+    L = 16384."""
     case = fi.config_case(4)
     say("pro pipeline config4")
     lf = fox.fox_gate_logf(dev(case.x, "bf16"), dev(case.w_f, "f32"), dev(case.b_f, "f32"))
@@ -244,17 +245,16 @@ def test_pro_pipeline_config4(fox):
     kn = fox.fox_qk_rmsnorm(dev(case.k, "bf16"), eps=1e-6)
     o, lse = fox.fox_attn_fwd(qn, kn, dev(case.v, "bf16"), c, o_dtype=torch.bfloat16)
     o, lse = host(o), host(lse)
-    s = default_scale(case.D)
     cc = oracle.cumsum_logf(oracle.gate_logf(case.x, case.w_f, case.b_f))
     qh = oracle.rms_norm(case.q, 1e-6)
     kh = oracle.rms_norm(case.k, 1e-6)
-    got, ref, gl, rl = [], [], [], []
+    say("  oracle forward (12 heads, L=16384) ...")
+    O, LSE = oracle.attn_fwd(qh, kh, case.v, c=cc, scale=default_scale(case.D), block=1024)
+    check("O, all rows and heads", o, O)
+    check("LSE, all rows and heads", lse, LSE)
     for h in range(case.H):
-        rows = sample_rows(case.L, 24, seed=50 + h, tile=128)
-        O, LSE = oracle.attn_fwd_rows(qh[0, h], kh[0, h], case.v[0, h], cc[0, h], rows, scale=s)
-        got.append(o[0, h, rows]); ref.append(O); gl.append(lse[0, h, rows]); rl.append(LSE)
-    check("O sampled rows", np.concatenate(got), np.concatenate(ref))
-    check("LSE sampled rows", np.concatenate(gl), np.concatenate(rl))
+        check(f"O (h{h})", o[0, h], O[0, h], quiet=True)
+        check(f"LSE (h{h})", lse[0, h], LSE[0, h], quiet=True)
 
 
 # ------------------------------------------------------------------------------------- Pro backward
@@ -324,9 +324,9 @@ def test_qk_rmsnorm_backward(fox, rows, D, dt, weighted):
 
 
 # ------------------------------------------------------------------------------------- backward
-def _run_bwd(fox, case):
+def _run_bwd(fox, case, c_dtype=torch.float32):
     q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
-    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"), dtype=c_dtype)
     o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
     g = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
     torch.cuda.synchronize()
@@ -364,9 +364,9 @@ def test_head_counts_off_the_xcd_grid(fox, B, H, L, D):
     _check_grads(got, ref)
 
 
-def _run_bwd_f32(fox, case):
+def _run_bwd_f32(fox, case, c_dtype=torch.float32):
     q, k, v, do = (dev(getattr(case, n), "f32") for n in ("q", "k", "v", "do"))
-    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"), dtype=c_dtype)
     o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
     g = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
     torch.cuda.synchronize()
@@ -407,8 +407,8 @@ def test_backward_fp32_steps_match(fox):
     o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
     whole = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
     delta = fox.fox_attn_bwd_delta(do, o)
-    dq, dcq, delta = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta, delta_out=delta)
-    dk, dv, dck = fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, delta)
+    dq, dcq, delta, lse2 = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta, delta_out=delta)
+    dk, dv, dck = fox.fox_attn_bwd_dkv(q, k, v, c, lse2, do, delta)
     dlf = fox.fox_dlogf_from_dc(dcq, dck)
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), whole, (dq, dk, dv, dlf)):
@@ -435,46 +435,36 @@ def test_backward_row_term_from_o(fox, B, H, L, D, dtype, skip):
     delta = fox.fox_attn_bwd_delta(do, o)
     sep = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, delta, skip_plan=plan)
     fused = fox.fox_attn_bwd_dq(q, k, v, c, lse, do, None, o=o, skip_plan=plan)
-    dk, dv, dck = fox.fox_attn_bwd_dkv(q, k, v, c, lse, do, sep[2], skip_plan=plan)
+    dk, dv, dck = fox.fox_attn_bwd_dkv(q, k, v, c, sep[3], do, sep[2], skip_plan=plan)
     dlf = fox.fox_dlogf_from_dc(sep[1], dck)
     whole = fox.fox_attn_bwd(q, k, v, c, o, lse, do, skip_plan=plan)
     torch.cuda.synchronize()
-    for name, a, b in zip(("dQ", "dc_q", "delta_out"), sep, fused):
+    for name, a, b in zip(("dQ", "dc_q", "delta_out", "lse_out"), sep, fused):
         assert torch.equal(a, b), f"{name}: fused row term differs from the separate one"
     for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), whole, (sep[0], dk, dv, dlf)):
         assert torch.equal(a, b), f"{name}: fox_attn_bwd differs from the step calls"
 
 
 def test_backward_config2_shape(fox):
-    """B=4, H=12, L=2048 with config-5 statistics: 6 whole heads compared."""
+    """B=4, H=12, L=2048 with config-5 statistics: all 48 heads compared element by element."""
     case = fi.make_case(4, 12, 2048, 128, "bf16", seed=3, gate="per_head", with_do=True)
     say("bwd B4 H12 L2048")
     got = _run_bwd(fox, case)
-    s = default_scale(case.D)
-    for b, h in [(0, 0), (1, 5), (2, 7), (3, 11), (0, 3), (3, 9)]:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        ref = oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl],
-                              scale=s)[:4]
-        _check_grads([g[sl] for g in got], ref, f" (b{b},h{h})")
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do,
+                          scale=default_scale(case.D))[:4]
+    _check_grads(got, ref, " (all heads)")
+    for b in range(case.B):
+        for h in range(case.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            for name, a, r in zip(("dQ", "dK", "dV", "dlog f"), got, ref):
+                check(f"{name} (b{b},h{h})", a[sl], r[sl], quiet=True)
 
 
-def test_backward_config5_full_length(fox):
-    """L = 16384: the shortest- and longest-memory heads, whole, plus gradient invariants."""
-    case = fi.config_case(5)
-    say("bwd config5 (L=16384)")
-    got = _run_bwd(fox, case)
-    s = default_scale(case.D)
-    mu = case.log_f[0].mean(axis=-1)
-    for h in (int(np.argmin(mu)), int(np.argmax(mu))):
-        sl = (slice(0, 1), slice(h, h + 1))
-        ref = oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl],
-                              scale=s, block=1024)[:4]
-        _check_grads([g[sl] for g in got], ref, f" (h{h})")
-    dq, dk, dv, dlf = got
-    # Invariants for every head: sum_t dK_t = 0, sum_t dV_t = sum_t dO_t, d log f_0 = 0. If each
-    # column's elementwise error stays within the relative-L2 tolerance and errors are
-    # independent across rows, the error of a column sum has standard deviation at most
-    # BF16_RELL2 * ||column||_2; allow 6 of them (the max over 12 x 128 columns).
+def _grad_invariants(case, dk, dv, dlf):
+    """Invariants for every head: sum_t dK_t = 0, sum_t dV_t = sum_t dO_t, d log f_0 = 0. If each
+    column's elementwise error stays within the relative-L2 tolerance and errors are independent
+    across rows, the error of a column sum has standard deviation at most
+    BF16_RELL2 * ||column||_2; allow 6 of them."""
     dk_sum = np.abs(dk.sum(axis=2))
     dk_norm = np.linalg.norm(dk, axis=2)
     assert np.all(dk_sum <= 6 * BF16_RELL2 * dk_norm), float((dk_sum / dk_norm).max())
@@ -483,37 +473,130 @@ def test_backward_config5_full_length(fox):
     assert np.abs(dlf[..., 0]).max() <= BF16_MAXABS
 
 
+def test_backward_config5_full_length(fox, config3_oracle):
+    """L = 16384, all 12 heads compared element by element (dQ, dK, dV, d log f), each head
+    separately and all together, plus the gradient invariants. The oracle's forward is workload
+    3's (the same q, k, v, log f)."""
+    case = fi.config_case(5)
+    say("bwd config5 (L=16384)")
+    got = _run_bwd(fox, case)
+    O, LSE = config3_oracle
+    say("  oracle backward (12 heads, L=16384) ...")
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=default_scale(case.D),
+                          O=O, LSE=LSE, block=1024)[:4]
+    _check_grads(got, ref, " (all heads)")
+    for h in range(case.H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), got, ref):
+            check(f"{name} (h{h})", a[sl], b[sl], quiet=True)
+    _grad_invariants(case, got[1], got[2], got[3])
+
+
 def test_paper_head_shape_full_length(fox):
     """The FoX paper's head shape, B=1, H=24, L=16384, D=64, as the benchmark's paper-shape run
-    builds it: forward on sampled rows of every head, backward on the shortest- and
-    longest-memory heads whole, plus the column-sum invariants for every head."""
+    builds it: forward and backward on every row of all 24 heads, plus the gradient
+    invariants."""
     case = fi.make_case(1, 24, 16384, 64, "bf16", seed=6, gate="per_head", with_do=True,
                         name="paper_shape")
     say("fwd+bwd paper shape (H=24, L=16384, D=64)")
     s = default_scale(case.D)
     _, o, lse = _run_fwd(fox, case, torch.bfloat16)
-    cc = oracle.cumsum_logf(case.log_f)
-    got, ref, gl, rl = [], [], [], []
-    for h in range(case.H):
-        rows = sample_rows(case.L, 24, seed=500 + h, tile=128)
-        O, LSE = oracle.attn_fwd_rows(case.q[0, h], case.k[0, h], case.v[0, h], cc[0, h], rows,
-                                      scale=s)
-        got.append(o[0, h, rows]); ref.append(O); gl.append(lse[0, h, rows]); rl.append(LSE)
-    check("O sampled rows", np.concatenate(got), np.concatenate(ref))
-    check("LSE sampled rows", np.concatenate(gl), np.concatenate(rl))
     grads = _run_bwd(fox, case)
-    mu = case.log_f[0].mean(axis=-1)
-    for h in (int(np.argmin(mu)), int(np.argmax(mu))):
+    say("  oracle forward and backward (24 heads, L=16384) ...")
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s, block=1024)
+    check("O, all rows and heads", o, O)
+    check("LSE, all rows and heads", lse, LSE)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s, O=O, LSE=LSE,
+                          block=1024)[:4]
+    _check_grads(grads, ref, " (all heads)")
+    for h in range(case.H):
         sl = (slice(0, 1), slice(h, h + 1))
-        ref = oracle.attn_bwd(case.q[sl], case.k[sl], case.v[sl], case.log_f[sl], case.do[sl],
-                              scale=s, block=1024)[:4]
-        _check_grads([g[sl] for g in grads], ref, f" (h{h})")
-    _, dk, dv, dlf = grads
-    dk_norm = np.linalg.norm(dk, axis=2)
-    assert np.all(np.abs(dk.sum(axis=2)) <= 6 * BF16_RELL2 * dk_norm)
-    dv_err = np.abs(dv.sum(axis=2) - case.do.astype(np.float64).sum(axis=2))
-    assert np.all(dv_err <= 6 * BF16_RELL2 * np.linalg.norm(dv, axis=2))
-    assert np.abs(dlf[..., 0]).max() <= BF16_MAXABS
+        check(f"O (h{h})", o[sl], O[sl], quiet=True)
+        for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), grads, ref):
+            check(f"{name} (h{h})", a[sl], b[sl], quiet=True)
+    _grad_invariants(case, grads[1], grads[2], grads[3])
+
+
+def _structured_gate(case, gate):
+    B, H, L = case.B, case.H, case.L
+    if gate == "open":  # f = 1: plain causal attention
+        case.log_f = np.zeros((B, H, L), np.float32)
+    elif gate == "alibi":  # constant per-head gate: the ALiBi bias -m_h (i - j)
+        m = 2.0 ** (-8.0 * np.arange(1, H + 1) / H)
+        case.log_f = np.broadcast_to(-m[None, :, None], (B, H, L)).astype(np.float32).copy()
+    elif gate in ("reset", "reset_1e4"):  # hard resets (f ~ 0): a slab of ten, two singles
+        # Every one of these cuts all earlier keys exactly (exp(-300) underflows in fp32). With
+        # -300 c falls by about 3.6e3 in all, where fp32 c is spaced 2^-12; the single resets of
+        # -1e4 take it to 2.3e4, where the spacing of fp32 c (2^-10) alone moves d log f by about
+        # 1e-2, so those run with fp64 c.
+        single = -300.0 if gate == "reset" else -1e4
+        case.log_f[..., L // 5:L // 5 + 10] = -300.0
+        case.log_f[..., L // 2] = single
+        case.log_f[..., L - 3] = single
+    else:
+        raise ValueError(gate)
+    return case
+
+
+STRUCTURED = [(g, cd) for g in ("open", "alibi", "reset") for cd in ("f32", "f64")] + [
+    ("reset_1e4", "f64")]
+
+
+@pytest.mark.parametrize("gate,c_dtype", STRUCTURED)
+@pytest.mark.parametrize("B,H,L,D", [(1, 3, 1000, 64), (1, 2, 2000, 128), (1, 1, 1537, 128)])
+def test_backward_structured_gates(fox, gate, c_dtype, B, H, L, D):
+    """dQ, dK, dV and d log f against the oracle where the gates have a closed form: all open
+    (plain causal attention), constant per head (ALiBi), and hard resets, where c drops by 300 or
+    1e4 per position and the precision of c and of the backward's row terms matter most; with c
+    in fp32 and in fp64 (resets of -1e4: fp64 only). B*H = 1 in the last shape."""
+    case = _structured_gate(fi.make_case(B, H, L, D, "bf16", seed=60 + L + D, with_do=True), gate)
+    cdt = torch.float64 if c_dtype == "f64" else torch.float32
+    say(f"bwd structured gate={gate} c={c_dtype} B={B} H={H} L={L} D={D}")
+    s = default_scale(D)
+    _, o, lse = _run_fwd(fox, case, torch.float32, c_dtype=cdt)
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
+    check("O", o, O)
+    check("LSE", lse, LSE)
+    got = _run_bwd(fox, case, c_dtype=cdt)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s, O=O, LSE=LSE)[:4]
+    _check_grads(got, ref)
+    _grad_invariants(case, got[1], got[2], got[3])
+
+
+@pytest.mark.parametrize("L,D,dtype", [(1, 64, "bf16"), (300, 128, "bf16"), (1500, 64, "bf16"),
+                                       (77, 128, "f32"), (700, 64, "f32")])
+def test_fp64_c_matches_oracle(fox, L, D, dtype):
+    """fp64 c on ragged shapes, both paths: forward and backward against the oracle (the fp32
+    bar scaled by each output's size for fp32 inputs, as for fp32 c)."""
+    case = fi.make_case(1, 3, L, D, dtype, seed=1200 + L, with_do=True, gate="per_head")
+    say(f"fp64 c L={L} D={D} {dtype}")
+    s = default_scale(D)
+    c, o, lse = _run_fwd(fox, case, torch.float32, c_dtype=torch.float64)
+    assert np.array_equal(c, oracle.cumsum_logf(case.log_f)) or \
+        np.abs(c - oracle.cumsum_logf(case.log_f)).max() <= 1e-9
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s, O=O, LSE=LSE)[:4]
+    if dtype == "bf16":
+        check("O", o, O)
+        check("LSE", lse, LSE)
+        _check_grads(_run_bwd(fox, case, c_dtype=torch.float64), ref)
+    else:
+        check("O", o, O, maxabs=F32_MAXABS, rel_l2=None)
+        check("LSE", lse, LSE, maxabs=F32_MAXABS * max(1.0, float(np.abs(LSE).max())), rel_l2=None)
+        got = _run_bwd_f32(fox, case, c_dtype=torch.float64)
+        for name, a, b in zip(("dQ", "dK", "dV", "dlog f"), got, ref):
+            check(name, a, b, maxabs=F32_MAXABS * max(1.0, float(np.abs(b).max())), rel_l2=1e-5)
+
+
+def test_fp64_c_rejects_skip_plan(fox):
+    case = fi.make_case(1, 2, 300, 64, "bf16", seed=3)
+    q, k, v = (dev(getattr(case, n), "bf16") for n in "qkv")
+    c32 = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    c64 = fox.fox_logf_cumsum(dev(case.log_f, "f32"), dtype=torch.float64)
+    plan = fox.fox_attn_skip_plan(q, k, c32)
+    with pytest.raises(fox.FoxError, match="skip plan"):
+        fox.fox_attn_fwd(q, k, v, c64, skip_plan=plan)
+    torch.cuda.synchronize()
 
 
 def test_backward_deterministic(fox):
@@ -532,6 +615,11 @@ def _skip_case(L, D, kind, H=4, seed=0, B=1):
     elif kind == "mixed":  # per-head gates from strongly to barely forgetting
         case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="per_head",
                             head_mean_range=(-2.0, 6.0), with_do=True)
+    elif kind == "rising":  # strong decay with slabs of positive log f: c rises inside tiles
+        case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=0.0,
+                            with_do=True)
+        for a in (L // 4 + 17, L // 2 + 3, (3 * L) // 4 + 40):
+            case.log_f[..., a:a + 9] = 12.0
     else:  # hard resets inside otherwise open gates
         case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=6.0,
                             with_do=True)
@@ -553,8 +641,8 @@ def _check_plan_against_oracle(fox, case, plan, c):
     moves it outside that band. The group norms match the oracle's, and the launch orders list
     every item once, most work first."""
     B, H, L, D = case.B, case.H, case.L, case.D
-    q_skip, kv_tiles, qn, kn, q_order, kv_order = (host(a) for a in
-                                                   fox.skip_plan_arrays(plan, B, H, L))
+    q_skip, kv_tiles, qn, kn, cmin, cmax, q_order, kv_order = (
+        host(a) for a in fox.skip_plan_arrays(plan, B, H, L))
     n_qt, n_kb = q_skip.shape[1], kv_tiles.shape[1]
     q_work = np.minimum(np.arange(n_qt) * 256 + 255, L - 1) // 64 + 1 - q_skip  # [BH, n_qt]
     for order, work in ((q_order, q_work.reshape(-1)), (kv_order, kv_tiles.reshape(-1))):
@@ -570,12 +658,16 @@ def _check_plan_against_oracle(fox, case, plan, c):
     for got, x in ((qn, case.q), (kn, case.k)):
         ref = fox_oracle._group_max_norms(x, 64).reshape(B * H, -1)
         assert np.all(got >= ref * (1 - 1e-6)) and np.all(got <= ref * (1 + 1e-4) + 1e-30)
+    rmin, rmax = fox_oracle._group_extrema(cc, 64)  # exact: a min / max of the same fp32 values
+    assert np.array_equal(cmin, rmin.reshape(B * H, -1))
+    assert np.array_equal(cmax, rmax.reshape(B * H, -1))
     return q_skip, kv_tiles
 
 
 SKIP_CASES = [(3000, 128, "strong", 1), (1000, 64, "strong", 1), (2500, 128, "mixed", 1),
               (1500, 64, "reset", 1), (100, 128, "strong", 1), (4097, 128, "reset", 1),
-              (2000, 128, "mixed", 2), (1300, 64, "strong", 3)]
+              (2000, 128, "mixed", 2), (1300, 64, "strong", 3), (3000, 128, "rising", 1),
+              (1200, 64, "rising", 2)]
 
 
 @pytest.mark.parametrize("L,D,kind,B", SKIP_CASES)
@@ -891,3 +983,45 @@ def test_decode_append_keeps_key_norms(fox):
     fresh = fox.fox_attn_decode_key_norms(kc, lens)
     torch.cuda.synchronize()
     assert np.allclose(host(kn), host(fresh), rtol=1e-6, atol=0)
+
+
+# ------------------------------------------------------------------------------ binding checks
+def test_binding_rejects_wrong_shapes(fox):
+    """Tensors too small for the sizes q implies are refused in Python, before any launch: the
+    kernels index every element the sizes imply, so a short dO, o, c, lse, delta, plan or
+    workspace would be read past its end."""
+    B, H, L, D = 1, 2, 300, 64
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    q = torch.zeros(B, H, L, D, **bf)
+    c = torch.zeros(B, H, L, **f32)
+    o = torch.zeros(B, H, L, D, **f32)
+    lse = torch.zeros(B, H, L, **f32)
+    short4 = torch.zeros(B, H, L - 1, D, **bf)
+    short3 = torch.zeros(B, H, L - 1, **f32)
+    plan = fox.fox_attn_skip_plan(q, q, c)
+    cases = [
+        lambda: fox.fox_attn_fwd(q, q, q, short3),
+        lambda: fox.fox_attn_fwd(q, q, q, c, skip_plan=plan[:-256]),
+        lambda: fox.fox_attn_bwd(q, q, q, c, o, lse, short4),
+        lambda: fox.fox_attn_bwd(q, q, q, c, torch.zeros(B, H, L - 1, D, **f32), lse, q),
+        lambda: fox.fox_attn_bwd(q, q, q, c, o, short3, q),
+        lambda: fox.fox_attn_bwd(q, q, q, short3, o, lse, q),
+        lambda: fox.fox_attn_bwd(q, q, q, c, o, lse, q, workspace=torch.zeros(256, dtype=torch.uint8,
+                                                                             device="cuda")),
+        lambda: fox.fox_attn_bwd_dq(q, q, q, c, lse, short4, None, o=o),
+        lambda: fox.fox_attn_bwd_dq(q, q, q, c, lse, q, short3),
+        lambda: fox.fox_attn_bwd_dq(q, q, q, c, lse, q, None, o=o, delta_out=short3),
+        lambda: fox.fox_attn_bwd_dkv(q, q, q, c, short3, q, lse),
+        lambda: fox.fox_attn_bwd_dkv(q, q, q, c, lse, q, short3),
+        lambda: fox.fox_attn_bwd_dkv(q, q, q, c, lse, q, lse, skip_plan=plan[:100]),
+        lambda: fox.fox_logf_cumsum(c, torch.zeros(B, H, L - 1, **f32)),
+        lambda: fox.fox_qk_rmsnorm(q, out=short4),
+        lambda: fox.fox_kv_shift_bwd(q, short3, o),
+    ]
+    torch.cuda.synchronize()
+    for i, fn in enumerate(cases):
+        with pytest.raises(ValueError):
+            fn()
+        say(f"  case {i}: refused")
+    torch.cuda.synchronize()
