@@ -41,7 +41,7 @@ __all__ = [
     "fox_attn_decode_key_norms",
     "fox_shift_gate", "fox_shift_gate_bwd", "fox_kv_shift", "fox_kv_shift_bwd", "fox_out_norm_gate",
     "fox_out_norm_gate_bwd",
-    "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
+    "fox_attn_bwd_workspace_bytes", "fox_attn_bwd_noalloc", "fox_attn_bwd_delta", "fox_attn_bwd_dkv", "fox_attn_bwd_dq",
     "fox_dlogf_from_dc", "fox_version", "FOX_OK", "FOX_E_INVALID", "FOX_C_F64",
     "FOX_E_UNSUPPORTED", "FOX_E_LAUNCH", "FOX_F32", "FOX_BF16", "FOX_CAUSAL",
 ]
@@ -80,6 +80,10 @@ _SIGS = {
     "fox_attn_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64,
                                     _c_i64, _c_i64, _c_f32, _c_u32, _c_vp, _c_vp]),
+    "fox_attn_bwd_noalloc_max_bytes": (_c_sz, []),
+    "fox_attn_bwd_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                            _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                            _c_i64, _c_i64, _c_f32, _c_u32, _c_vp, _c_vp]),
     "fox_attn_bwd_delta": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp]),
     "fox_attn_bwd_dkv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
@@ -407,6 +411,41 @@ def fox_attn_bwd(q, k, v, c, o, lse, dO, scale: float | None = None, workspace=N
                             workspace.numel(), B, H, L, D, scale, _cflags(c),
                             _plan_ptr(skip_plan, B, H, L, D), _stream(q)),
            "fox_attn_bwd")
+    return dq, dk, dv, dlf
+
+
+def fox_attn_bwd_noalloc(q, k, v, c, o, lse, dO, scale: float | None = None,
+                         skip_plan: torch.Tensor | None = None, out=None):
+    """fox_attn_bwd on the library's static scratch (no workspace). out: optional
+    (dq, dk, dv, dlog_f) fp32 tensors to write; with them this call allocates nothing."""
+    lib = load_library()
+    B, H, L, D = _bhld(q, k, v)
+    pq = _dev(q, "q", (torch.bfloat16, torch.float32))
+    pk, pv = _dev(k, "k", (q.dtype,)), _dev(v, "v", (q.dtype,))
+    pdo = _dev(dO, "dO", (q.dtype,))
+    pc = _dev(c, "c", (torch.float32, torch.float64), 3)
+    po = _dev(o, "o", (torch.float32,), 4)
+    pl = _dev(lse, "lse", (torch.float32,), 3)
+    for t, name in ((dO, "dO"), (o, "o")):
+        _shape(t, name, (B, H, L, D))
+    for t, name in ((c, "c"), (lse, "lse")):
+        _shape(t, name, (B, H, L))
+    if out is None:
+        out = (torch.empty((B, H, L, D), dtype=torch.float32, device=q.device),
+               torch.empty((B, H, L, D), dtype=torch.float32, device=q.device),
+               torch.empty((B, H, L, D), dtype=torch.float32, device=q.device),
+               torch.empty((B, H, L), dtype=torch.float32, device=q.device))
+    dq, dk, dv, dlf = out
+    ptrs = []
+    for t, name, shp in ((dq, "dq", (B, H, L, D)), (dk, "dk", (B, H, L, D)),
+                         (dv, "dv", (B, H, L, D)), (dlf, "dlog_f", (B, H, L))):
+        ptrs.append(_dev(t, name, (torch.float32,)))
+        _shape(t, name, shp)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_bwd_noalloc(pq, pk, pv, _code(q.dtype), pc, po, pl, pdo, *ptrs, B, H, L, D,
+                                    scale, _cflags(c), _plan_ptr(skip_plan, B, H, L, D),
+                                    _stream(q)),
+           "fox_attn_bwd_noalloc")
     return dq, dk, dv, dlf
 
 

@@ -297,13 +297,15 @@ size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D) 
 
 namespace {
 
-// fox_attn_bwd's validation and launches (named `what` in messages).
+// fox_attn_bwd's validation and launches; the workspace comes from the caller or, with
+// scratch set, from the library's static array (fox_attn_bwd_noalloc, named `what` in
+// messages), whose address is looked up only once every argument has passed.
 fox_status attn_bwd_impl(const void* q, const void* k, const void* v, fox_dtype in_dt,
                          const void* c, const float* o, const float* lse, const void* dO,
                          float* dq, float* dk, float* dv, float* dlog_f, void* workspace,
                          size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
                          float scale, uint32_t flags, const void* skip_plan, void* stream,
-                         const char* what) {
+                         const char* what, bool scratch) {
   FOX_REQUIRE_PTR(q);
   FOX_REQUIRE_PTR(k);
   FOX_REQUIRE_PTR(v);
@@ -315,9 +317,11 @@ fox_status attn_bwd_impl(const void* q, const void* k, const void* v, fox_dtype 
   FOX_REQUIRE_PTR(dk);
   FOX_REQUIRE_PTR(dv);
   FOX_REQUIRE_PTR(dlog_f);
-  FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL");
-  FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
-              "workspace must be 256-byte aligned");
+  if (!scratch) {
+    FOX_REQUIRE(workspace != nullptr, "workspace must not be NULL");
+    FOX_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0,
+                "workspace must be 256-byte aligned");
+  }
   fox_status st = check_bhld(B, H, L, D);
   if (st != FOX_OK) return st;
   FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
@@ -325,8 +329,14 @@ fox_status attn_bwd_impl(const void* q, const void* k, const void* v, fox_dtype 
   if (st != FOX_OK) return st;
   FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
   const size_t need = fox::bwd_workspace_bytes(B * H, L);
-  FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
-              workspace_bytes, need);
+  if (scratch)
+    FOX_REQUIRE(need <= fox::noalloc_scratch_bytes(),
+                "B*H*L too large for the static scratch: %zu bytes needed, %zu held "
+                "(fox_attn_bwd_noalloc_max_bytes; use fox_attn_bwd with a workspace)",
+                need, fox::noalloc_scratch_bytes());
+  else
+    FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
   if (in_dt == FOX_F32 && skip_plan)
@@ -334,6 +344,11 @@ fox_status attn_bwd_impl(const void* q, const void* k, const void* v, fox_dtype 
   if (in_dt == FOX_F32 && B * H > 65535)
     return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)",
                 (long long)(B * H));
+  if (scratch) {
+    const hipError_t e = fox::noalloc_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(FOX_E_LAUNCH, "%s: scratch address: %s", what, hipGetErrorString(e));
+  }
   if (in_dt == FOX_F32) {
     return launched(fox::launch_bwd_f32((const float*)q, (const float*)k, (const float*)v,
                                         cptr(c, flags), o, lse, (const float*)dO, dq, dk, dv,
@@ -358,7 +373,18 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
                         float scale, uint32_t flags, const void* skip_plan, void* stream) {
   return attn_bwd_impl(q, k, v, in_dt, c, o, lse, dO, dq, dk, dv, dlog_f, workspace,
                        workspace_bytes, B, H, L, D, scale, flags, skip_plan, stream,
-                       "fox_attn_bwd");
+                       "fox_attn_bwd", false);
+}
+
+size_t fox_attn_bwd_noalloc_max_bytes(void) { return fox::noalloc_scratch_bytes(); }
+
+fox_status fox_attn_bwd_noalloc(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                                const void* c, const float* o, const float* lse, const void* dO,
+                                float* dq, float* dk, float* dv, float* dlog_f, int64_t B,
+                                int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
+                                const void* skip_plan, void* stream) {
+  return attn_bwd_impl(q, k, v, in_dt, c, o, lse, dO, dq, dk, dv, dlog_f, nullptr, 0, B, H, L, D,
+                       scale, flags, skip_plan, stream, "fox_attn_bwd_noalloc", true);
 }
 
 namespace {

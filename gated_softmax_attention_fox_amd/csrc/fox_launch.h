@@ -88,6 +88,10 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, CPtr c
                           float* lse, int64_t BH, int64_t L, int64_t D, float scale, hipStream_t s);
 // Workspace bytes of the bf16 backward.
 size_t bwd_workspace_bytes(int64_t BH, int64_t L);
+// The static scratch array of noalloc.hip: its size, and its device address on the current
+// device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 // Backward steps: Delta = rowsum(dO * O); query-stationary dQ, dc^q, the refined Delta
 // (delta_out may equal delta; with delta null the step forms Delta from o itself, bit-identical
 // to launch_bwd_delta) and the normalised row offset lse_out; key-stationary dK, dV, dc^k from

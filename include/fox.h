@@ -243,6 +243,22 @@ fox_status fox_attn_bwd(const void* q, const void* k, const void* v, fox_dtype i
                         size_t workspace_bytes, int64_t B, int64_t H, int64_t L, int64_t D,
                         float scale, uint32_t flags, const void* skip_plan, void* stream);
 
+/* fox_attn_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid an allocator). Same arguments, results and errors
+ * as fox_attn_bwd, minus the workspace: the row term and the dc partial sums live in a static
+ * device array of the library (32 MiB, fox_attn_bwd_noalloc_max_bytes()) that every GPU the
+ * library runs on holds from the library's load until the process ends. Sizes whose workspace
+ * (fox_attn_bwd_workspace_bytes) exceeds it, that is B*H*L above 2^21, return FOX_E_INVALID.
+ * Calls no allocator. Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on different streams, or from different threads) race and give wrong results;
+ * calls in order on one stream are safe. The array's contents are not read on entry. */
+size_t fox_attn_bwd_noalloc_max_bytes(void);
+fox_status fox_attn_bwd_noalloc(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                                const void* c, const float* o, const float* lse, const void* dO,
+                                float* dq, float* dk, float* dv, float* dlog_f, int64_t B,
+                                int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
+                                const void* skip_plan, void* stream);
+
 /* The four steps of fox_attn_bwd as separate calls, for callers that schedule them
  * themselves. Running them in this order with the same arguments gives exactly fox_attn_bwd's
  * results. fox_attn_bwd itself runs step 1 inside step 2 (step 2 with delta = NULL and o

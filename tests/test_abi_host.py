@@ -232,3 +232,18 @@ def test_pro_backward_rejects(lib):
     assert g(P, 1, P, P, None, None, None, 0, 10, 128, ctypes.c_float(-1.0), None) == 1  # eps
     assert lib.fox_qk_rmsnorm_bwd_workspace_bytes(10, 128) >= 1024 * 128 * 4
 
+
+@host_only
+def test_noalloc_backward_rejects(lib):
+    """fox_attn_bwd_noalloc: the size limit of its static scratch and the usual validation,
+    before any launch."""
+    assert lib.fox_attn_bwd_noalloc_max_bytes() == 4 * (1 << 21) * 4
+
+    def call(B=1, H=2, L=64, D=128, flags=1, in_dt=1):
+        return lib.fox_attn_bwd_noalloc(P, P, P, in_dt, P, P, P, P, P, P, P, P, B, H, L, D, 0.1,
+                                        flags, None, None)
+    assert call(H=2, L=(1 << 20) + 64) == 1  # B*H*L above 2^21
+    assert b"static scratch" in lib.fox_last_error()
+    assert call(flags=0) == 2
+    assert call(D=96) == 1
+    assert call(in_dt=7) == 1
