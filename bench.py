@@ -268,6 +268,8 @@ def main():
     if not args.no_skip:
         out["skip_decayed"] = skip_measurement(args, torch, fox, step, names, ms_per_step,
                                                fwd_flops + bwd_flops, (B, H, L))
+        out["fused_scan"] = fused_scan_measurement(args, torch, fox, (q, k, v, do, log_f),
+                                                   stream, kern_ms)
     copy_calibration(args, torch, dev, out)
     if not args.no_cpu_baseline:
         log(f"timing the oracle on {args.cpu_heads} heads (CPU) ...")
@@ -307,6 +309,54 @@ def skip_measurement(args, torch, fox, step, names, dense_ms, dense_flops, bhl):
             float((q_dense - q_skip).sum() / (B * H * q_dense.sum())), 4),
         "dkv_query_tiles_walked_frac": round(float(kv_tiles.sum() / (B * H * kv_dense.sum())), 4),
         "kernel_ms": {n: round(kern[n], 4) for n in kern},
+    }
+
+
+def fused_scan_measurement(args, torch, fox, inputs, stream, dense_kern):
+    """The same step with the prefix sum fused into the forward (fox_attn_fwd_logf takes log f and
+    writes c for the backward) in place of the scan kernel and the forward. A separate
+    measurement of the option, never the headline."""
+    q, k, v, do, log_f = inputs
+
+    def fstep(events):
+        def run(n, fn):
+            if events is None:
+                return fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r = fn()
+            e1.record(stream)
+            events.append((n, e0, e1))
+            return r
+        o, lse, c = run("fwd_logf", lambda: fox.fox_attn_fwd_logf(q, k, v, log_f,
+                                                                  o_dtype=torch.float32))
+        dq, dcq, delta, lse2 = run("dq", lambda: fox.fox_attn_bwd_dq(q, k, v, c, lse, do, None,
+                                                                      o=o))
+        dk, dv, dck = run("dkv", lambda: fox.fox_attn_bwd_dkv(q, k, v, c, lse2, do, delta))
+        run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
+        return o, c
+
+    o_f, c_f = fstep(None)
+    c_s = fox.fox_logf_cumsum(log_f)
+    o_s, _ = fox.fox_attn_fwd(q, k, v, c_s, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        fstep(None)
+    events = []
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fstep(events)
+    torch.cuda.synchronize()
+    ms = events[0][1].elapsed_time(events[-1][2]) / args.steps
+    names = ["fwd_logf", "dq", "dkv", "dlogf"]
+    kern = {n: float(np.mean([a.elapsed_time(b) for m, a, b in events if m == n])) for n in names}
+    return {
+        "ms_per_step": round(ms, 4),
+        "fused_fwd_ms": round(kern["fwd_logf"], 4),
+        "separate_scan_plus_fwd_ms": round(dense_kern["scan"] + dense_kern["fwd"], 4),
+        "c_equal_to_scan_kernel_frac": round(float((c_f == c_s).float().mean()), 6),
+        "o_max_abs_diff_vs_separate": float((o_f - o_s).abs().max()),
+        "kernel_ms": {n: round(kern[n], 4) for n in names},
     }
 
 

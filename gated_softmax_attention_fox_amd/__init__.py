@@ -35,7 +35,8 @@ import torch
 
 __all__ = [
     "FoxError", "LIB_PATH", "HEADER_PATH", "load_library", "header_functions",
-    "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_bwd",
+    "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_fwd_logf",
+    "fox_attn_bwd",
     "fox_attn_skip_plan_bytes", "fox_attn_skip_plan", "skip_plan_arrays",
     "fox_attn_decode_workspace_bytes", "fox_attn_decode", "fox_attn_decode_append",
     "fox_attn_decode_key_norms",
@@ -76,6 +77,9 @@ _SIGS = {
     "fox_attn_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int,
                                     _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, _c_u32, _c_vp,
                                     _c_vp]),
+    "fox_attn_fwd_logf": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
+                                         ctypes.c_int, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                         _c_f32, _c_u32, _c_vp]),
     "fox_attn_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "fox_attn_bwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64,
@@ -373,6 +377,30 @@ def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | 
                             _stream(q)),
            "fox_attn_fwd")
     return o, lse
+
+
+def fox_attn_fwd_logf(q, k, v, log_f, o_dtype: torch.dtype | None = None,
+                      scale: float | None = None, want_lse: bool = True,
+                      c_dtype: torch.dtype = torch.float32):
+    """(O, LSE, c) of the forward with the prefix sum fused in: takes log f [B, H, L] fp32 and
+    returns c (fp32, or fp64 with c_dtype=torch.float64) for the backward."""
+    lib = load_library()
+    B, H, L, D = _bhld(q, k, v)
+    dts = (torch.bfloat16, torch.float32)
+    pq, pk, pv = _dev(q, "q", dts), _dev(k, "k", (q.dtype,)), _dev(v, "v", (q.dtype,))
+    pl = _dev(log_f, "log_f", (torch.float32,), 3)
+    _shape(log_f, "log_f", (B, H, L))
+    o_dtype = o_dtype or q.dtype
+    o = torch.empty((B, H, L, D), dtype=o_dtype, device=q.device)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if want_lse else None
+    c = torch.empty((B, H, L), dtype=c_dtype, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.fox_attn_fwd_logf(pq, pk, pv, _code(q.dtype), pl, ctypes.c_void_p(c.data_ptr()),
+                                 ctypes.c_void_p(o.data_ptr()), _code(o_dtype),
+                                 ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                                 B, H, L, D, scale, _cflags(c), _stream(q)),
+           "fox_attn_fwd_logf")
+    return o, lse, c
 
 
 def fox_attn_bwd_workspace_bytes(B: int, H: int, L: int, D: int) -> int:

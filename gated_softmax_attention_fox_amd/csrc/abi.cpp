@@ -287,6 +287,43 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
                   "fox_attn_fwd");
 }
 
+fox_status fox_attn_fwd_logf(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                             const float* log_f, void* c_out, void* o, fox_dtype o_dt, float* lse,
+                             int64_t B, int64_t H, int64_t L, int64_t D, float scale,
+                             uint32_t flags, void* stream) {
+  FOX_REQUIRE_PTR(q);
+  FOX_REQUIRE_PTR(k);
+  FOX_REQUIRE_PTR(v);
+  FOX_REQUIRE_PTR(log_f);
+  FOX_REQUIRE_PTR(c_out);
+  FOX_REQUIRE_PTR(o);
+  FOX_REQUIRE((const void*)log_f != c_out, "c_out must not alias log_f");
+  if (lse) FOX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+  fox_status st = check_bhld(B, H, L, D);
+  if (st != FOX_OK) return st;
+  FOX_REQUIRE(in_dt == FOX_BF16 || in_dt == FOX_F32, "in_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(!(in_dt == FOX_F32 && o_dt != FOX_F32), "fp32 inputs require an fp32 output");
+  FOX_REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+  st = check_flags(flags, nullptr);
+  if (st != FOX_OK) return st;
+  if (in_dt == FOX_F32 && B * H > 65535)
+    return fail(FOX_E_UNSUPPORTED, "the fp32 kernels take B*H <= 65535 (got %lld)", (long long)(B * H));
+  const hipStream_t s = (hipStream_t)stream;
+  const fox::CPtr c = cptr(c_out, flags);
+  if (in_dt == FOX_F32) {  // the full-fp32 path: the scan, then the forward on its output
+    const hipError_t e = c.f64 ? fox::launch_cumsum64(log_f, (double*)c_out, B * H, L, s)
+                               : fox::launch_cumsum(log_f, (float*)c_out, B * H, L, s);
+    if (e != hipSuccess) return launched(e, "fox_attn_fwd_logf");
+    return launched(fox::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, c,
+                                        (float*)o, lse, B * H, L, D, scale, s),
+                    "fox_attn_fwd_logf");
+  }
+  return launched(fox::launch_fwd_bf16_logf(q, k, v, log_f, c, o, o_dt == FOX_F32, lse, B * H, L,
+                                            D, scale, s),
+                  "fox_attn_fwd_logf");
+}
+
 size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D) {
   (void)D;
   if (B < 1 || H < 1 || L < 1) return 0;

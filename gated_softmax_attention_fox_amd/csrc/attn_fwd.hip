@@ -87,12 +87,19 @@ __device__ __forceinline__ void interleave_step() {
 // the only one that evaluates the causal mask. From tile 4 on all waves are in step and run the
 // pipelined body; its main loop is unrolled over four tiles so that every ring slot is a
 // compile-time constant and every LDS address is a per-lane base register plus an immediate.
-template <int D, typename CT>
+//
+// Fused scan (kLogF). The kernel then takes log f (LF) instead of c and forms the prefix sums
+// itself, in fp64: a workgroup sums log f over every position before its window (the 256
+// positions of its diagonal band, which hold its own queries), scans the window, and writes c
+// for its queries (Cout, fp32 or fp64) for the backward. For the older key tiles, walked in
+// ascending order, the converting wave carries the running prefix from tile to tile and scans
+// each tile's 64 values. Every bias is an fp64 difference of prefix sums, rounded once.
+template <int D, typename CT, bool kLogF>
 __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const CT* __restrict__ C, void* __restrict__ O, float* __restrict__ LSE,
-    const int32_t* __restrict__ q_skip, const int32_t* __restrict__ q_order, int L, int BH,
-    int n_qt, float sl2e, int o_f32) {
+    const CT* __restrict__ C, const float* __restrict__ LF, CT* __restrict__ Cout,
+    void* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ q_skip,
+    const int32_t* __restrict__ q_order, int L, int BH, int n_qt, float sl2e, int o_f32) {
   constexpr int NW = 8, BM = NW * 32, NT = NW * 64, BN = kFwdBN;
   constexpr int TILE = BN * D;
   constexpr int CPR = D / 8;
@@ -101,9 +108,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   constexpr int NCOPY = 2 * BLK + 1;         // copies a wave starts per iteration (K, V, c)
   static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
   constexpr uint32_t TB = TILE * 2;  // bytes of one K or V tile
-  constexpr uint32_t CS = sizeof(CT);  // bytes of one raw c value (fp32 or fp64)
+  // bytes of one raw value in the copy ring: c (fp32 or fp64), or log f (fp32) when fused
+  constexpr uint32_t CS = kLogF ? 4 : sizeof(CT);
   constexpr uint32_t K_OFF = 0, V_OFF = 4 * TB, R_OFF = 8 * TB, C_OFF = 8 * TB + 4 * BN * CS;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[8 * TB + 4 * BN * CS + 2 * BN * 4];
+  // fused scan: the window's fp64 prefix sums and eight per-wave partial sums
+  constexpr uint32_t W_OFF = C_OFF + 2 * BN * 4, RED_OFF = W_OFF + (kLogF ? 256 * 8 : 0);
+  __shared__ __attribute__((aligned(1024))) unsigned char
+      smem[8 * TB + 4 * BN * CS + 2 * BN * 4 + (kLogF ? 256 * 8 + 16 * 8 : 0)];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses need it
@@ -125,8 +136,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   Q += base;
   K += base;
   V += base;
-  C += (size_t)bh * L;
-  const CT c_ref = C[q0];
+  if constexpr (kLogF) {
+    LF += (size_t)bh * L;
+    Cout += (size_t)bh * L;
+  } else {
+    C += (size_t)bh * L;
+  }
+  const CT c_ref = kLogF ? (CT)0 : C[q0];
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
   const int q_last = (q0 + BM - 1 < L - 1) ? q0 + BM - 1 : L - 1;
@@ -139,8 +155,13 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   const int j0 = 2 * kt_last + 1 - qw / 32;  // the wave's diagonal sub-tile
   const i32x4 k_rs = buffer_words(K, (uint32_t)L * (uint32_t)(D * 2));
   const i32x4 v_rs = buffer_words(V, (uint32_t)L * (uint32_t)(D * 2));
-  const i32x4 c_rs = buffer_words(C, (uint32_t)L * CS);
+  const i32x4 c_rs = kLogF ? buffer_words(LF, (uint32_t)L * 4u) : buffer_words(C, (uint32_t)L * CS);
   const uint32_t sbase = lds_addr(smem);
+  typedef __attribute__((address_space(3))) double lds_d;
+  const int w0 = kt_last >= 3 ? (kt_last - 3) * BN : 0;  // first position of the window
+  // fused scan: the prefix sum at q0 sits in the window at P_REF; the converting wave keeps the
+  // running prefix before the next older tile at CARRY (LDS, so no fp64 stays live in registers)
+  const uint32_t P_REF = sbase + W_OFF + (uint32_t)(q0 - w0) * 8, CARRY = sbase + RED_OFF + 128;
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -177,6 +198,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
   };
   auto copy_c = [&](int t, int slot) __attribute__((always_inline)) {  // 8 values per wave
+    if (kLogF && t < 4) return;  // fused: the band's prefix sums come from the window scan
     if (lane < 2 * (int)CS) {  // one 4-byte word per lane
       const uint32_t voff = (uint32_t)(key_tile(t) * BN + wave * 8) * CS + lane * 4;
       copy4_to_lds(sbase + R_OFF + slot * BN * CS + wave * 8 * CS, voff, c_rs);
@@ -190,13 +212,35 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
     if (t + 2 < n_t) copy_kv(v_rs, V_OFF, t + 2, sv);
   };
-  // Bias slice of tile t + 1 from its raw c values (wave 0).
+  // Bias slice of tile t + 1 from its raw c values (wave 0). Fused: from the window's prefix
+  // sums for the band, else from the running prefix and a scan of the tile's log f.
   auto convert_c = [&](int t, int sr, int sb) __attribute__((always_inline)) {
     if (wave == 0 && t + 1 < n_t) {
-      const CT cj = *(const __attribute__((address_space(3))) CT*)(uintptr_t)(
-          sbase + R_OFF + sr * BN * CS + lane * CS);
+      float bias;
+      if constexpr (kLogF) {
+        const double p_ref = *(const lds_d*)(uintptr_t)P_REF;
+        if (t + 1 < 4) {
+          const double pj =
+              *(const lds_d*)(uintptr_t)(sbase + W_OFF + (key_tile(t + 1) * BN - w0 + lane) * 8);
+          bias = (float)((pj - p_ref) * 1.4426950408889634);
+        } else {
+          // the tile's own prefix in fp32 on DPP moves (its partial sums are small; the carry
+          // across tiles and the reference stay fp64)
+          const float x = wave_scan_incl(*(const __attribute__((address_space(3))) float*)(uintptr_t)(
+              sbase + R_OFF + sr * BN * 4 + lane * 4));
+          const double carry = *(const lds_d*)(uintptr_t)CARRY;
+          bias = (float)(((carry - p_ref) + (double)x) * 1.4426950408889634);
+          const float tot =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+          if (lane == 0) *(lds_d*)(uintptr_t)CARRY = carry + (double)tot;
+        }
+      } else {
+        const CT cj = *(const __attribute__((address_space(3))) CT*)(uintptr_t)(
+            sbase + R_OFF + sr * BN * CS + lane * CS);
+        bias = cbias(cj, c_ref);
+      }
       *(__attribute__((address_space(3))) float*)(uintptr_t)(sbase + C_OFF + sb * BN * 4 + lane * 4) =
-          cbias(cj, c_ref);
+          bias;
     }
   };
 
@@ -299,6 +343,37 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
   };
 
+  // ---- fused scan: prefix sums of the window [w0, q_last], c of this workgroup's queries --------
+  // (all of its global loads and stores complete before the first untracked copy is issued)
+  if constexpr (kLogF) {
+    double part = 0.0;  // sum of log f over [0, w0), then over the wave's 64 window positions
+#pragma unroll 8
+    for (int l = tid; l < w0; l += NT) part += (double)LF[l];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off, 64);
+    double x = (tid < 256 && w0 + tid <= q_last) ? (double)LF[w0 + tid] : 0.0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 0) *(lds_d*)(uintptr_t)(sbase + RED_OFF + wave * 8) = part;
+    if (tid == 0) *(lds_d*)(uintptr_t)CARRY = 0.0;  // older tiles start from key 0
+    if (lane == 63 && wave < 4) *(lds_d*)(uintptr_t)(sbase + RED_OFF + 64 + wave * 8) = x;
+    __syncthreads();
+    double base = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) base += *(const lds_d*)(uintptr_t)(sbase + RED_OFF + w * 8);
+    if (tid < 256) {
+      double pre = base;
+      for (int w = 0; w < wave; ++w) pre += *(const lds_d*)(uintptr_t)(sbase + RED_OFF + 64 + w * 8);
+      *(lds_d*)(uintptr_t)(sbase + W_OFF + tid * 8) = pre + x;
+    }
+    __syncthreads();
+    if (tid < 256 && q0 + tid <= q_last)
+      Cout[q0 + tid] = (CT)*(const lds_d*)(uintptr_t)(sbase + W_OFF + (q0 - w0 + tid) * 8);
+  }
+
   // ---- prologue: tile 0 through registers; copies of K(1), K(2), V(1), c(1), c(2) -------------
   {
     const int k0 = kt_last * BN;
@@ -311,7 +386,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     }
     if (tid < BN) {
       const int key = k0 + tid;
-      ((float*)(smem + C_OFF))[tid] = key < L ? cbias(C[key], c_ref) : 0.f;
+      float bias = 0.f;
+      if constexpr (kLogF) {
+        if (key < L)
+          bias = (float)((*(const lds_d*)(uintptr_t)(sbase + W_OFF + (key - w0) * 8) -
+                          *(const lds_d*)(uintptr_t)P_REF) * 1.4426950408889634);
+      } else {
+        bias = key < L ? cbias(C[key], c_ref) : 0.f;
+      }
+      ((float*)(smem + C_OFF))[tid] = bias;
     }
     if (1 < n_t) {
       copy_kv(k_rs, K_OFF, 1, 1);
@@ -469,7 +552,15 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
         }
       }
     }
-    if (h == 0 && LSE) LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + cdiff(C[qi], c_ref);
+    if (h == 0 && LSE) {
+      float crel;  // c_qi - c_q0
+      if constexpr (kLogF)
+        crel = (float)(*(const lds_d*)(uintptr_t)(sbase + W_OFF + (qi - w0) * 8) -
+                       *(const lds_d*)(uintptr_t)P_REF);
+      else
+        crel = cdiff(C[qi], c_ref);
+      LSE[(size_t)bh * L + qi] = (m + __log2f(ltot)) * kLn2 + crel;
+    }
   }
 }
 
@@ -560,9 +651,21 @@ void go_fwd_bf16(const void* q, const void* k, const void* v, const void* c, voi
                  float* lse, int64_t BH, int64_t L, float scale, const SkipArgs& skip,
                  hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)c, o, lse,
-                     skip.q_skip, skip.q_order, (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, false>), dim3((unsigned)(n_qt * BH)), dim3(512),
+                     0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)c,
+                     (const float*)nullptr, (CT*)nullptr, o, lse, skip.q_skip, skip.q_order,
+                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+}
+
+template <int D, typename CT>
+void go_fwd_bf16_logf(const void* q, const void* k, const void* v, const float* log_f, void* c_out,
+                      void* o, bool o_f32, float* lse, int64_t BH, int64_t L, float scale,
+                      hipStream_t s) {
+  const int n_qt = (int)((L + 255) / 256);
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, true>), dim3((unsigned)(n_qt * BH)), dim3(512),
+                     0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)nullptr,
+                     log_f, (CT*)c_out, o, lse, (const int32_t*)nullptr, (const int32_t*)nullptr,
+                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32);
 }
 
 template <int D, typename CT>
@@ -584,6 +687,20 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, 
   } else {
     if (c.f64) go_fwd_bf16<128, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
     else go_fwd_bf16<128, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_logf(const void* q, const void* k, const void* v, const float* log_f,
+                                CPtr c_out, void* o, bool o_f32, float* lse, int64_t BH, int64_t L,
+                                int64_t D, float scale, hipStream_t s) {
+  void* co = const_cast<void*>(c_out.p);
+  if (D == 64) {
+    if (c_out.f64) go_fwd_bf16_logf<64, double>(q, k, v, log_f, co, o, o_f32, lse, BH, L, scale, s);
+    else go_fwd_bf16_logf<64, float>(q, k, v, log_f, co, o, o_f32, lse, BH, L, scale, s);
+  } else {
+    if (c_out.f64) go_fwd_bf16_logf<128, double>(q, k, v, log_f, co, o, o_f32, lse, BH, L, scale, s);
+    else go_fwd_bf16_logf<128, float>(q, k, v, log_f, co, o, o_f32, lse, BH, L, scale, s);
   }
   return hipGetLastError();
 }

@@ -186,6 +186,26 @@ __device__ __forceinline__ bf16x8 lds_tr8(uint32_t a0, uint32_t a1) {
   return __builtin_bit_cast(bf16x8, ab);
 }
 
+// Inclusive prefix sum of one float per lane over the wave (lane 0 first), on DPP moves only (no
+// LDS round trips): a Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8, lanes
+// without a source reading 0), then row 0's total added to row 1 and row 2's to row 3
+// (row_bcast:15), then lane 31's prefix added to rows 2 and 3 (row_bcast:31). Lanes a step does
+// not write read the zero passed as the old value.
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl,
+                                                               kRowMask, 0xf, kBound));
+}
+__device__ __forceinline__ float wave_scan_incl(float x) {
+  x += dpp_move<0x111, 0xf, true>(x);  // row_shr:1
+  x += dpp_move<0x112, 0xf, true>(x);  // row_shr:2
+  x += dpp_move<0x114, 0xf, true>(x);  // row_shr:4
+  x += dpp_move<0x118, 0xf, true>(x);  // row_shr:8
+  x += dpp_move<0x142, 0xa, false>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_move<0x143, 0xc, false>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Register-file hints for the allocator (no instruction is emitted): accumulators only the
 // matrix cores touch stay in AGPRs, MFMA results the vector ALU reads stay in VGPRs, so no
 // v_accvgpr moves are needed between them.

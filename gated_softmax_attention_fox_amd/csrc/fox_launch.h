@@ -83,6 +83,11 @@ SkipArgs skip_args(const void* plan, int64_t BH, int64_t L);
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
                            const SkipArgs& skip, hipStream_t s);
+// Forward from log f with the prefix sum fused in (bf16 inputs); also writes c (c_out: fp32, or
+// fp64 when c_out.f64).
+hipError_t launch_fwd_bf16_logf(const void* q, const void* k, const void* v, const float* log_f,
+                                CPtr c_out, void* o, bool o_f32, float* lse, int64_t BH, int64_t L,
+                                int64_t D, float scale, hipStream_t s);
 // Forward, fp32 inputs and outputs, fp32 arithmetic throughout.
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, CPtr c, float* o,
                           float* lse, int64_t BH, int64_t L, int64_t D, float scale, hipStream_t s);

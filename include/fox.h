@@ -26,12 +26,13 @@
  *   - Preconditions not checked on the device: log f must be finite (the pages' log 0 = -inf
  *     would make c_i - c_j undefined); NaN inputs propagate to NaN outputs. A hard reset is a
  *     large finite negative log f: -200 already cuts every earlier weight exactly (exp
- *     underflows in fp32). Deeper values only make |c| large, and fp32 c is spaced 2^-10 at
- *     |c| ~ 2^14 and 2^-7 at 2^17, which then shows in the results; pass fp64 c (FOX_C_F64)
- *     for resets of -1e4 and the like. Within one 256-position block, the kernels hold c
- *     differences in fp32 relative to one reference, so a fall of c beyond ~1e5 inside a
- *     single block (many consecutive resets of -1e4) leaves an error of about 2^-24 |fall| in
- *     the weights next to it whatever the type of c.
+ *     underflows in fp32), and deeper values only cost precision, in two ways. (1) |c| grows:
+ *     fp32 c is spaced 2^-11 at |c| ~ 4e3 and 2^-7 at 1e5, and that rounding shows in the
+ *     gradients once |c| passes about 1e4 (many resets, or strong decay over a long context);
+ *     fp64 c (FOX_C_F64) removes it. (2) Within a tile the kernels hold c differences in fp32
+ *     against one reference, so a fall of c by F inside one tile leaves errors of about
+ *     2^-24 F (log2 units) in the weights on one side of it, whatever the type of c: keep a
+ *     single reset within about -2000 (at -1e4 d log f can reach 2e-2 on bf16 inputs).
  *   - Calls are reentrant: the library holds no mutable global state apart from the
  *     thread-local error message.
  */
@@ -220,6 +221,19 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
                         const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
                         int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
                         const void* skip_plan, void* stream);
+
+/* The forward with the prefix sum fused in (paper-graph-ui summary, section 7 "Implications and
+ * Future Directions", follow-up work: fuse the computation of c into the attention kernel). It
+ * takes log f ([B, H, L] fp32) instead of c, computes the prefix sums itself in fp64, and writes
+ * c_out ([B, H, L]; fp32, or fp64 with FOX_C_F64) for the backward: within one fp32 ulp of
+ * fox_logf_cumsum (fox_logf_cumsum_f64 to fp64 rounding). O and lse as fox_attn_fwd; every bias
+ * c_i - c_j is formed as an fp64 difference, so the forward does not carry the rounding of an
+ * fp32 c. bf16 inputs run one fused kernel; fp32 inputs run the scan and then the fp32 forward.
+ * No skip plan (a plan is built from c). c_out may not alias log_f. */
+fox_status fox_attn_fwd_logf(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                             const float* log_f, void* c_out, void* o, fox_dtype o_dt, float* lse,
+                             int64_t B, int64_t H, int64_t L, int64_t D, float scale,
+                             uint32_t flags, void* stream);
 
 /* Bytes of device workspace fox_attn_bwd needs for these sizes (caller-allocated). */
 size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D);

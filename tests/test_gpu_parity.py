@@ -524,12 +524,11 @@ def _structured_gate(case, gate):
     elif gate == "alibi":  # constant per-head gate: the ALiBi bias -m_h (i - j)
         m = 2.0 ** (-8.0 * np.arange(1, H + 1) / H)
         case.log_f = np.broadcast_to(-m[None, :, None], (B, H, L)).astype(np.float32).copy()
-    elif gate in ("reset", "reset_1e4"):  # hard resets (f ~ 0): a slab of ten, two singles
+    elif gate in ("reset", "reset_deep"):  # hard resets (f ~ 0): a slab of ten, two singles
         # Every one of these cuts all earlier keys exactly (exp(-300) underflows in fp32). With
-        # -300 c falls by about 3.6e3 in all, where fp32 c is spaced 2^-12; the single resets of
-        # -1e4 take it to 2.3e4, where the spacing of fp32 c (2^-10) alone moves d log f by about
-        # 1e-2, so those run with fp64 c.
-        single = -300.0 if gate == "reset" else -1e4
+        # -300, c falls by about 3.6e3 in all, where fp32 c is spaced 2^-11. The deeper singles
+        # (-2000) take it to about 7e3; they run with fp64 c.
+        single = -300.0 if gate == "reset" else -2000.0
         case.log_f[..., L // 5:L // 5 + 10] = -300.0
         case.log_f[..., L // 2] = single
         case.log_f[..., L - 3] = single
@@ -539,7 +538,7 @@ def _structured_gate(case, gate):
 
 
 STRUCTURED = [(g, cd) for g in ("open", "alibi", "reset") for cd in ("f32", "f64")] + [
-    ("reset_1e4", "f64")]
+    ("reset_deep", "f64")]
 
 
 @pytest.mark.parametrize("gate,c_dtype", STRUCTURED)
@@ -547,8 +546,8 @@ STRUCTURED = [(g, cd) for g in ("open", "alibi", "reset") for cd in ("f32", "f64
 def test_backward_structured_gates(fox, gate, c_dtype, B, H, L, D):
     """dQ, dK, dV and d log f against the oracle where the gates have a closed form: all open
     (plain causal attention), constant per head (ALiBi), and hard resets, where c drops by 300 or
-    1e4 per position and the precision of c and of the backward's row terms matter most; with c
-    in fp32 and in fp64 (resets of -1e4: fp64 only). B*H = 1 in the last shape."""
+    2000 per position and the precision of c and of the backward's row terms matter most; with c
+    in fp32 and in fp64 (the deeper resets: fp64 only). B*H = 1 in the last shape."""
     case = _structured_gate(fi.make_case(B, H, L, D, "bf16", seed=60 + L + D, with_do=True), gate)
     cdt = torch.float64 if c_dtype == "f64" else torch.float32
     say(f"bwd structured gate={gate} c={c_dtype} B={B} H={H} L={L} D={D}")
@@ -1025,3 +1024,80 @@ def test_binding_rejects_wrong_shapes(fox):
             fn()
         say(f"  case {i}: refused")
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------ fused scan
+def _ulp_ok(got, ref):
+    """Within one fp32 ulp of the exact prefix sum (fp64 accumulation, one rounding)."""
+    ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    return bool(np.all(np.abs(got - ref) <= ulp + 1e-30)), float(np.max(np.abs(got - ref) / (ulp + 1e-30)))
+
+
+@pytest.mark.parametrize("B,H,L,D,dtype", [(1, 2, 1, 64, "bf16"), (1, 3, 63, 128, "bf16"),
+                                           (2, 3, 300, 64, "bf16"), (1, 2, 1000, 128, "bf16"),
+                                           (1, 2, 4097, 128, "bf16"), (1, 13, 520, 64, "bf16"),
+                                           (1, 2, 300, 64, "f32"), (1, 1, 700, 128, "f32")])
+def test_fused_scan_forward(fox, B, H, L, D, dtype):
+    """fox_attn_fwd_logf: O and LSE against the oracle, c within one fp32 ulp of the exact
+    prefix sum (and fp64 c to fp64 rounding), for fp32 and fp64 c outputs."""
+    case = fi.make_case(B, H, L, D, dtype, seed=1300 + L + D, gate="per_head")
+    say(f"fused scan B={B} H={H} L={L} D={D} {dtype}")
+    q, k, v = (dev(getattr(case, n), dtype) for n in "qkv")
+    lf = dev(case.log_f, "f32")
+    s = default_scale(D)
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
+    cref = oracle.cumsum_logf(case.log_f)
+    for cdt in (torch.float32, torch.float64):
+        for o_dt in ((torch.bfloat16, torch.float32) if dtype == "bf16" else (torch.float32,)):
+            o, lse, c = fox.fox_attn_fwd_logf(q, k, v, lf, o_dtype=o_dt, c_dtype=cdt)
+            torch.cuda.synchronize()
+            if cdt == torch.float32:
+                ok, worst = _ulp_ok(host(c), cref)
+                assert ok, f"c off by {worst} ulp"
+            else:
+                assert np.abs(host(c) - cref).max() <= 1e-9 * max(1.0, np.abs(cref).max())
+            tol = dict(maxabs=F32_MAXABS, rel_l2=None) if dtype == "f32" else {}
+            check(f"O[{o_dt}, c {cdt}]", host(o), O, **tol)
+            check("LSE", host(lse), LSE, **tol)
+
+
+def test_fused_scan_config3_full_length(fox, config3_oracle):
+    """The fused forward at the benchmark's workload: every row of every head, and c within one
+    fp32 ulp of the exact prefix sum and of fox_logf_cumsum."""
+    case = fi.config_case(3)
+    say("fused scan config3 (L=16384)")
+    q, k, v = (dev(getattr(case, n), "bf16") for n in "qkv")
+    lf = dev(case.log_f, "f32")
+    o, lse, c = fox.fox_attn_fwd_logf(q, k, v, lf, o_dtype=torch.bfloat16)
+    c_sep = fox.fox_logf_cumsum(lf)
+    torch.cuda.synchronize()
+    cref = oracle.cumsum_logf(case.log_f)
+    ok, worst = _ulp_ok(host(c), cref)
+    assert ok, f"c off by {worst} ulp"
+    diff = np.abs(host(c) - host(c_sep))
+    ulp = np.spacing(np.abs(host(c_sep)).astype(np.float32)).astype(np.float64)
+    assert np.all(diff <= ulp), "fused c differs from the scan kernel's by more than one ulp"
+    say(f"  c equal to the scan kernel's bit for bit at {float(np.mean(diff == 0)):.6f} of positions")
+    O, LSE = config3_oracle
+    check("O, all rows and heads", host(o), O)
+    check("LSE, all rows and heads", host(lse), LSE)
+
+
+@pytest.mark.parametrize("B,H,L,D", [(1, 3, 1000, 64), (1, 2, 2000, 128)])
+def test_fused_scan_then_backward_with_resets(fox, B, H, L, D):
+    """Hard resets: the fused forward writes fp64 c, and the backward runs on it; all outputs
+    against the oracle."""
+    case = _structured_gate(fi.make_case(B, H, L, D, "bf16", seed=90 + L, with_do=True),
+                            "reset_deep")
+    say(f"fused scan + backward, hard resets, B={B} H={H} L={L} D={D}")
+    q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
+    o, lse, c = fox.fox_attn_fwd_logf(q, k, v, dev(case.log_f, "f32"), o_dtype=torch.float32,
+                                      c_dtype=torch.float64)
+    g = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
+    torch.cuda.synchronize()
+    s = default_scale(D)
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
+    check("O", host(o), O)
+    check("LSE", host(lse), LSE)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s, O=O, LSE=LSE)[:4]
+    _check_grads([host(t) for t in g], ref)
