@@ -453,6 +453,47 @@ def decode_step(args, torch, fi, fox, dev):
     print(json.dumps(out), flush=True)
 
 
+def pro_fused_forward(args, torch, fox, q, k, v, x, w_f, b_f, stream):
+    """The Pro forward's q-norm and output norm + gate done inside the attention forward
+    (fox_attn_fwd_ex: q normalised as it is loaded, y = RMSNorm(O) * sigmoid(g) in the
+    epilogue, O still written for the backward) against the same work as separate passes
+    (q-norm, forward, output norm + gate); both take the same normalised keys and c."""
+    B, H, L, D = q.shape
+    rng = torch.Generator(device=q.device).manual_seed(47)
+    g = torch.randn(B, H, L, D, device=q.device, generator=rng).to(torch.bfloat16)
+    c = fox.fox_logf_cumsum(fox.fox_gate_logf(x, w_f, b_f))
+    kn = fox.fox_qk_rmsnorm(k, eps=1e-6)
+
+    def separate():
+        qn = fox.fox_qk_rmsnorm(q, eps=1e-6)
+        o, lse = fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32)
+        return o, lse, fox.fox_out_norm_gate(o, g, eps=1e-6)
+
+    def fused():
+        return fox.fox_attn_fwd_ex(q, kn, v, c, o_dtype=torch.float32, q_norm_eps=1e-6, gate=g,
+                                   out_norm_eps=1e-6)
+
+    res = {}
+    for name, fn in (("separate", separate), ("fused", fused)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(e0.elapsed_time(e1) / args.steps, 4)
+    so, sl, sy = separate()
+    fo, fl, fy = fused()
+    torch.cuda.synchronize()
+    res["o_max_abs_diff"] = float((so - fo).abs().max())
+    res["y_max_abs_diff"] = float((sy.float() - fy.float()).abs().max())
+    res["saved_ms"] = round(res["separate_ms"] - res["fused_ms"], 4)
+    return res
+
+
 def pro_extra_kernels(torch, fox, x, k, v, stream):
     """The Pro block's shift gates, token shift (keys with RMSNorm, values without) and output
     norm + gate, forward and backward, at the workload's shape: each timed alone, 20 calls,
@@ -581,6 +622,7 @@ def pro_step(args, torch, fi, fox, dev):
         "host_wall_ms_per_step": round(wall_ms, 4),
     }
     out["pro_shift_output_kernels"] = pro_extra_kernels(torch, fox, x, k, v, stream)
+    out["fused_forward"] = pro_fused_forward(args, torch, fox, q, k, v, x, w_f, b_f, stream)
     if not args.no_skip:  # the same step with exact tile skipping, a separate measurement
         ref = step(None)
         got = step(None, skip=True)

@@ -35,7 +35,8 @@ import torch
 
 __all__ = [
     "FoxError", "LIB_PATH", "HEADER_PATH", "load_library", "header_functions",
-    "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_fwd_logf",
+    "fox_logf_cumsum", "fox_gate_logf", "fox_qk_rmsnorm", "fox_attn_fwd", "fox_attn_fwd_ex",
+    "FoxFwdOpts", "fox_attn_fwd_logf",
     "fox_attn_bwd",
     "fox_attn_skip_plan_bytes", "fox_attn_skip_plan", "skip_plan_arrays",
     "fox_attn_decode_workspace_bytes", "fox_attn_decode", "fox_attn_decode_append",
@@ -53,7 +54,16 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fox.h")
 
 FOX_OK, FOX_E_INVALID, FOX_E_UNSUPPORTED, FOX_E_LAUNCH = 0, 1, 2, 3
 FOX_F32, FOX_BF16 = 0, 1
-FOX_CAUSAL, FOX_C_F64 = 1, 2
+FOX_CAUSAL, FOX_C_F64, FOX_QK_RMSNORM = 1, 2, 4
+
+
+class FoxFwdOpts(ctypes.Structure):
+    """fox_fwd_opts of include/fox.h (same field order; ctypes lays it out as the C compiler)."""
+    _fields_ = [("scale", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("q_norm_eps", ctypes.c_float), ("q_norm_weight", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p), ("gate_dt", ctypes.c_int),
+                ("out_norm_weight", ctypes.c_void_p), ("out_norm_eps", ctypes.c_float),
+                ("y", ctypes.c_void_p), ("skip_plan", ctypes.c_void_p)]
 
 _c_i64, _c_u32, _c_f32, _c_vp, _c_sz = (ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
@@ -77,6 +87,8 @@ _SIGS = {
     "fox_attn_fwd": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int,
                                     _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_f32, _c_u32, _c_vp,
                                     _c_vp]),
+    "fox_attn_fwd_ex": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, ctypes.c_int,
+                                       _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
     "fox_attn_fwd_logf": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp,
                                          ctypes.c_int, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                          _c_f32, _c_u32, _c_vp]),
@@ -377,6 +389,45 @@ def fox_attn_fwd(q, k, v, c, o_dtype: torch.dtype | None = None, scale: float | 
                             _stream(q)),
            "fox_attn_fwd")
     return o, lse
+
+
+def fox_attn_fwd_ex(q, k, v, c, o_dtype: torch.dtype | None = torch.float32,
+                    scale: float | None = None, want_lse: bool = True,
+                    q_norm_eps: float | None = None, q_norm_weight: torch.Tensor | None = None,
+                    gate: torch.Tensor | None = None, out_norm_weight: torch.Tensor | None = None,
+                    out_norm_eps: float = 1e-6, skip_plan: torch.Tensor | None = None):
+    """(O or None, LSE or None, y or None) of the forward with the Pro block's fusions: QK-norm
+    of q as it is loaded (q_norm_eps not None; k must come normalised), and the output norm and
+    gate y = RMSNorm(O) [* out_norm_weight] * sigmoid(gate) (gate [B, H, L, D] bf16 or fp32, y in
+    its type). o_dtype=None skips O (only with a gate)."""
+    lib = load_library()
+    B, H, L, D = _bhld(q, k, v)
+    pq, pk, pv = (_dev(q, "q", (torch.bfloat16,)), _dev(k, "k", (torch.bfloat16,)),
+                  _dev(v, "v", (torch.bfloat16,)))
+    pc = _dev(c, "c", (torch.float32, torch.float64), 3)
+    _shape(c, "c", (B, H, L))
+    opts = FoxFwdOpts()
+    opts.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    opts.flags = _cflags(c) | (FOX_QK_RMSNORM if q_norm_eps is not None else 0)
+    opts.q_norm_eps = 0.0 if q_norm_eps is None else float(q_norm_eps)
+    opts.q_norm_weight = _wptr(q_norm_weight, D).value
+    y = None
+    if gate is not None:
+        _dev(gate, "gate", (torch.bfloat16, torch.float32))
+        _shape(gate, "gate", (B, H, L, D))
+        y = torch.empty_like(gate)
+        opts.gate, opts.gate_dt, opts.y = gate.data_ptr(), _code(gate.dtype), y.data_ptr()
+        opts.out_norm_weight = _wptr(out_norm_weight, D).value
+        opts.out_norm_eps = float(out_norm_eps)
+    opts.skip_plan = _plan_ptr(skip_plan, B, H, L, D).value
+    o = None if o_dtype is None else torch.empty((B, H, L, D), dtype=o_dtype, device=q.device)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if want_lse else None
+    _check(lib.fox_attn_fwd_ex(pq, pk, pv, FOX_BF16, pc,
+                               ctypes.c_void_p(o.data_ptr() if o is not None else 0),
+                               _code(o_dtype or torch.float32),
+                               ctypes.c_void_p(lse.data_ptr() if lse is not None else 0),
+                               B, H, L, D, ctypes.byref(opts), _stream(q)), "fox_attn_fwd_ex")
+    return o, lse, y
 
 
 def fox_attn_fwd_logf(q, k, v, log_f, o_dtype: torch.dtype | None = None,

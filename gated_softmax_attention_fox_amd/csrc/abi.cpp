@@ -71,8 +71,10 @@ fox_status check_bhld(int64_t B, int64_t H, int64_t L, int64_t D) {
 fox_status check_flags(uint32_t flags, const void* skip_plan) {
   if (!(flags & FOX_CAUSAL))
     return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
-  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64))
+  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64 | FOX_QK_RMSNORM))
     return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if (flags & FOX_QK_RMSNORM)
+    return fail(FOX_E_UNSUPPORTED, "FOX_QK_RMSNORM is taken by fox_attn_fwd_ex only");
   if ((flags & FOX_C_F64) && skip_plan)
     return fail(FOX_E_UNSUPPORTED, "a skip plan is built from fp32 c; it is not taken with FOX_C_F64");
   return FOX_OK;
@@ -285,6 +287,64 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
                                        D, scale,
                                        fox::skip_args(skip_plan, B * H, L), s),
                   "fox_attn_fwd");
+}
+
+fox_status fox_attn_fwd_ex(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                           const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
+                           int64_t H, int64_t L, int64_t D, const fox_fwd_opts* opts,
+                           void* stream) {
+  FOX_REQUIRE(opts != nullptr, "opts must not be NULL");
+  const uint32_t flags = opts->flags;
+  const bool qnorm = (flags & FOX_QK_RMSNORM) != 0;
+  const bool gated = opts->gate != nullptr;
+  if (!qnorm && !gated)  // nothing fused: the plain forward
+    return fox_attn_fwd(q, k, v, in_dt, c, o, o_dt, lse, B, H, L, D, opts->scale, flags,
+                        opts->skip_plan, stream);
+  FOX_REQUIRE_PTR(q);
+  FOX_REQUIRE_PTR(k);
+  FOX_REQUIRE_PTR(v);
+  FOX_REQUIRE_PTR(c);
+  FOX_REQUIRE(o != nullptr || gated, "o may be NULL only when the output gate is given");
+  if (o) FOX_REQUIRE(aligned16(o), "o must be 16-byte aligned");
+  if (lse) FOX_REQUIRE(aligned16(lse), "lse must be 16-byte aligned");
+  fox_status st = check_bhld(B, H, L, D);
+  if (st != FOX_OK) return st;
+  if (in_dt != FOX_BF16)
+    return fail(FOX_E_UNSUPPORTED, "QK-norm and the output gate serve the bf16 kernels");
+  FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
+  FOX_REQUIRE(opts->scale > 0.f && opts->scale < 1e30f, "scale must be positive and finite");
+  if (!(flags & FOX_CAUSAL))
+    return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
+  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64 | FOX_QK_RMSNORM))
+    return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
+  if ((flags & FOX_C_F64) && opts->skip_plan)
+    return fail(FOX_E_UNSUPPORTED, "a skip plan is built from fp32 c; it is not taken with FOX_C_F64");
+  if (qnorm && opts->skip_plan)
+    return fail(FOX_E_UNSUPPORTED, "a skip plan is built from the normalised q; it is not taken "
+                                   "with FOX_QK_RMSNORM");
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(opts->skip_plan) & 255u) == 0,
+              "skip_plan must be 256-byte aligned");
+  if (qnorm) FOX_REQUIRE(opts->q_norm_eps >= 0.f, "q_norm_eps must be >= 0");
+  if (gated) {
+    FOX_REQUIRE(aligned16(opts->gate), "gate must be 16-byte aligned");
+    FOX_REQUIRE_PTR(opts->y);
+    FOX_REQUIRE(opts->gate_dt == FOX_BF16 || opts->gate_dt == FOX_F32,
+                "gate_dt must be FOX_BF16 or FOX_F32");
+    FOX_REQUIRE(opts->out_norm_eps >= 0.f, "out_norm_eps must be >= 0");
+  }
+  fox::ProFwdArgs pa;
+  pa.q_norm = qnorm;
+  pa.q_w = opts->q_norm_weight;
+  pa.q_eps = opts->q_norm_eps;
+  pa.g = opts->gate;
+  pa.g_f32 = opts->gate_dt == FOX_F32;
+  pa.out_w = opts->out_norm_weight;
+  pa.out_eps = opts->out_norm_eps;
+  pa.y = gated ? opts->y : nullptr;
+  return launched(fox::launch_fwd_bf16(q, k, v, cptr(c, flags), o, o_dt == FOX_F32, lse, B * H, L,
+                                       D, opts->scale, fox::skip_args(opts->skip_plan, B * H, L),
+                                       (hipStream_t)stream, &pa),
+                  "fox_attn_fwd_ex");
 }
 
 fox_status fox_attn_fwd_logf(const void* q, const void* k, const void* v, fox_dtype in_dt,

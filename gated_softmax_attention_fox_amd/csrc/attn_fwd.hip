@@ -94,12 +94,32 @@ __device__ __forceinline__ void interleave_step() {
 // for its queries (Cout, fp32 or fp64) for the backward. For the older key tiles, walked in
 // ascending order, the converting wave carries the running prefix from tile to tile and scans
 // each tile's 64 values. Every bias is an fp64 difference of prefix sums, rounded once.
+//
+// Pro-block options (runtime, outside the hot loop; the Pro Block Architecture of the
+// paper-graph-ui summary, section 3.4). FwdPro::q_norm: each query row is RMS-normalised in
+// registers when it is loaded (Step 1, QK-norm of the queries; the keys come normalised from the
+// key shift). FwdPro::y: the epilogue writes y = RMSNorm(O) [* out_w] * sigmoid(g) (Steps 5 and 7,
+// output norm and output gate) from the fp32 O still in registers; O itself may then be skipped.
+struct FwdPro {
+  const float* q_w = nullptr;  // QK-norm weight [D] or null (unit)
+  float q_eps = 0.f;
+  int q_norm = 0;
+  const void* g = nullptr;     // output gate pre-activation [B, H, L, D] (bf16 or fp32)
+  int g_f32 = 0;
+  const float* out_w = nullptr;  // output-norm weight [D] or null (unit)
+  float out_eps = 0.f;
+  void* y = nullptr;           // [B, H, L, D] in g's type, or null: no output gate
+};
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+
 template <int D, typename CT, bool kLogF>
 __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const CT* __restrict__ C, const float* __restrict__ LF, CT* __restrict__ Cout,
     void* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ q_skip,
-    const int32_t* __restrict__ q_order, int L, int BH, int n_qt, float sl2e, int o_f32) {
+    const int32_t* __restrict__ q_order, int L, int BH, int n_qt, float sl2e, int o_f32,
+    FwdPro pro) {
   constexpr int NW = 8, BM = NW * 32, NT = NW * 64, BN = kFwdBN;
   constexpr int TILE = BN * D;
   constexpr int CPR = D / 8;
@@ -171,6 +191,21 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[c][e] = (__bf16)0.f;
+    }
+  }
+  if (pro.q_norm) {  // QK-norm of the query: this lane holds half its row, the partner the rest
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf((float)qf[c][e], (float)qf[c][e], ss);
+    }
+    const float rs = 1.0f / sqrtf(xhalf_sum(ss) / (float)D + pro.q_eps);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        qf[c][e] = (__bf16)((float)qf[c][e] * rs * (pro.q_w ? pro.q_w[16 * c + 8 * h + e] : 1.0f));
     }
   }
   f32x16 oacc[D / 32];
@@ -534,10 +569,48 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   if (!active) return;
   const float ltot = xhalf_sum(lsum);
   const float inv = 1.0f / ltot;
-  if (qi < L) {
+  if (qi < L && pro.y) {  // output norm and gate (both halves of the row take this branch)
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ss = fmaf(oacc[d][e] * inv, oacc[d][e] * inv, ss);
+    }
+    const float rs = 1.0f / sqrtf(xhalf_sum(ss) / (float)D + pro.out_eps);
     const size_t orow = base + (size_t)qi * D;
 #pragma unroll
     for (int d = 0; d < D / 32; ++d) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = d * 32 + 8 * i + 4 * h;
+        float g4[4], y4[4];
+        if (pro.g_f32) {
+          const float4 t = *reinterpret_cast<const float4*>(static_cast<const float*>(pro.g) + orow + col);
+          g4[0] = t.x; g4[1] = t.y; g4[2] = t.z; g4[3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(pro.g) + orow + col);
+          g4[0] = __uint_as_float(t.x << 16); g4[1] = __uint_as_float(t.x & 0xffff0000u);
+          g4[2] = __uint_as_float(t.y << 16); g4[3] = __uint_as_float(t.y & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          y4[j] = oacc[d][4 * i + j] * inv * rs * (pro.out_w ? pro.out_w[col + j] : 1.0f) *
+                  sigmoid_f(g4[j]);
+        if (pro.g_f32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(pro.y) + orow + col) =
+              make_float4(y4[0], y4[1], y4[2], y4[3]);
+        } else {
+          const uint32_t lo = (uint32_t)f2bf(y4[0]) | ((uint32_t)f2bf(y4[1]) << 16);
+          const uint32_t hi = (uint32_t)f2bf(y4[2]) | ((uint32_t)f2bf(y4[3]) << 16);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(pro.y) + orow + col) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  if (qi < L) {
+    const size_t orow = base + (size_t)qi * D;
+#pragma unroll
+    for (int d = 0; d < D / 32 && O; ++d) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = d * 32 + 8 * i + 4 * h;
@@ -649,12 +722,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ Q
 template <int D, typename CT>
 void go_fwd_bf16(const void* q, const void* k, const void* v, const void* c, void* o, bool o_f32,
                  float* lse, int64_t BH, int64_t L, float scale, const SkipArgs& skip,
-                 hipStream_t s) {
+                 const FwdPro& pro, hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
   hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, false>), dim3((unsigned)(n_qt * BH)), dim3(512),
                      0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)c,
                      (const float*)nullptr, (CT*)nullptr, o, lse, skip.q_skip, skip.q_order,
-                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32, pro);
 }
 
 template <int D, typename CT>
@@ -665,7 +738,7 @@ void go_fwd_bf16_logf(const void* q, const void* k, const void* v, const float* 
   hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, true>), dim3((unsigned)(n_qt * BH)), dim3(512),
                      0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)nullptr,
                      log_f, (CT*)c_out, o, lse, (const int32_t*)nullptr, (const int32_t*)nullptr,
-                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32);
+                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32, FwdPro());
 }
 
 template <int D, typename CT>
@@ -680,13 +753,24 @@ void go_fwd_f32(const float* q, const float* k, const float* v, const void* c, f
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
-                           const SkipArgs& skip, hipStream_t s) {
+                           const SkipArgs& skip, hipStream_t s, const ProFwdArgs* pa) {
+  FwdPro pro;
+  if (pa) {
+    pro.q_w = pa->q_w;
+    pro.q_eps = pa->q_eps;
+    pro.q_norm = pa->q_norm ? 1 : 0;
+    pro.g = pa->g;
+    pro.g_f32 = pa->g_f32 ? 1 : 0;
+    pro.out_w = pa->out_w;
+    pro.out_eps = pa->out_eps;
+    pro.y = pa->y;
+  }
   if (D == 64) {
-    if (c.f64) go_fwd_bf16<64, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
-    else go_fwd_bf16<64, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+    if (c.f64) go_fwd_bf16<64, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, pro, s);
+    else go_fwd_bf16<64, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, pro, s);
   } else {
-    if (c.f64) go_fwd_bf16<128, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
-    else go_fwd_bf16<128, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, s);
+    if (c.f64) go_fwd_bf16<128, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, pro, s);
+    else go_fwd_bf16<128, float>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, pro, s);
   }
   return hipGetLastError();
 }

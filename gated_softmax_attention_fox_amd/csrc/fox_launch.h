@@ -79,10 +79,22 @@ struct SkipArgs {
   const int32_t* kv_order = nullptr;
 };
 SkipArgs skip_args(const void* plan, int64_t BH, int64_t L);
-// Forward, bf16 inputs on MFMA; O in bf16 or fp32.
+// Pro-block options of the bf16 forward: QK-norm of q on load, output norm and gate in the
+// epilogue (y = RMSNorm(O) [* out_w] * sigmoid(g), y in g's type).
+struct ProFwdArgs {
+  bool q_norm = false;
+  const float* q_w = nullptr;
+  float q_eps = 0.f;
+  const void* g = nullptr;
+  bool g_f32 = false;
+  const float* out_w = nullptr;
+  float out_eps = 0.f;
+  void* y = nullptr;
+};
+// Forward, bf16 inputs on MFMA; O in bf16 or fp32 (o may be null when pa->y is set).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, void* o,
                            bool o_f32, float* lse, int64_t BH, int64_t L, int64_t D, float scale,
-                           const SkipArgs& skip, hipStream_t s);
+                           const SkipArgs& skip, hipStream_t s, const ProFwdArgs* pa = nullptr);
 // Forward from log f with the prefix sum fused in (bf16 inputs); also writes c (c_out: fp32, or
 // fp64 when c_out.f64).
 hipError_t launch_fwd_bf16_logf(const void* q, const void* k, const void* v, const float* log_f,

@@ -63,7 +63,7 @@ typedef enum fox_dtype { FOX_F32 = 0, FOX_BF16 = 1 } fox_dtype;
  * far c has fallen; with fp32 c each value carries a rounding of up to half the fp32 spacing at
  * |c| (2^-9 at |c| ~ 2^14, 2^-7 at |c| ~ 2^17), which hard resets (log f ~ -1e4) reach within a
  * few positions. Not taken together with a skip plan (FOX_E_UNSUPPORTED). */
-enum { FOX_CAUSAL = 1u, FOX_C_F64 = 2u };
+enum { FOX_CAUSAL = 1u, FOX_C_F64 = 2u, FOX_QK_RMSNORM = 4u };
 
 /* Cumulative log decay (paper-graph-ui summary, "Hardware-Aware Implementation": c is the
  * cumulative sum of log f, computed once per head before attention and kept in HBM).
@@ -221,6 +221,36 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
                         const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
                         int64_t H, int64_t L, int64_t D, float scale, uint32_t flags,
                         const void* skip_plan, void* stream);
+
+/* The forward with the Pro block's fusions (paper-graph-ui summary, section 3.4, "The Pro Block
+ * Architecture": Step 1, QK-norm; Steps 5 and 7, output norm and output gate), through one options
+ * struct. Everything else as fox_attn_fwd.
+ *   flags: FOX_CAUSAL (required), FOX_C_F64, and FOX_QK_RMSNORM: each query row is normalised
+ *          as it is loaded, q / sqrt(mean_d q^2 + q_norm_eps) [* q_norm_weight], in fp32 with one
+ *          rounding to bf16, as fox_qk_rmsnorm would; k must come normalised (the Pro block's
+ *          key shift normalises it, fox_kv_shift with normalize = 1, or fox_qk_rmsnorm).
+ *   gate:  NULL, or the output gate's pre-activation g ([B, H, L, D], gate_dt FOX_BF16 or
+ *          FOX_F32). Then y ([B, H, L, D], gate_dt) = RMSNorm(O) [* out_norm_weight] *
+ *          sigmoid(g), RMSNorm over D with out_norm_eps, formed from the fp32 O in registers.
+ *   o:     may be NULL when gate is given (inference, O not wanted); lse may be NULL.
+ * bf16 inputs only for FOX_QK_RMSNORM or a gate (FOX_E_UNSUPPORTED otherwise); a skip plan is
+ * not taken with FOX_QK_RMSNORM (a plan is built from the normalised q). */
+typedef struct fox_fwd_opts {
+  float scale;
+  uint32_t flags;
+  float q_norm_eps;
+  const float* q_norm_weight;
+  const void* gate;
+  fox_dtype gate_dt;
+  const float* out_norm_weight;
+  float out_norm_eps;
+  void* y;
+  const void* skip_plan;
+} fox_fwd_opts;
+fox_status fox_attn_fwd_ex(const void* q, const void* k, const void* v, fox_dtype in_dt,
+                           const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B,
+                           int64_t H, int64_t L, int64_t D, const fox_fwd_opts* opts,
+                           void* stream);
 
 /* The forward with the prefix sum fused in (paper-graph-ui summary, section 7 "Implications and
  * Future Directions", follow-up work: fuse the computation of c into the attention kernel). It

@@ -247,3 +247,26 @@ def test_noalloc_backward_rejects(lib):
     assert call(flags=0) == 2
     assert call(D=96) == 1
     assert call(in_dt=7) == 1
+
+
+def test_fwd_opts_layout_matches_c():
+    """The binding's fox_fwd_opts mirror has the C struct's size and field offsets (gcc on the
+    header, CPU only)."""
+    import shutil
+    import subprocess
+    import tempfile
+    import gated_softmax_attention_fox_amd as fox
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    fields = [f for f, _ in fox.FoxFwdOpts._fields_]
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"fox.h\"\nint main(void){printf(\"%zu\", sizeof(fox_fwd_opts));" + "".join(
+        f"printf(\" %zu\", offsetof(fox_fwd_opts, {f}));" for f in fields) + "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "layout")
+        subprocess.run([gcc, "-I", os.path.dirname(fox.HEADER_PATH), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(fox.FoxFwdOpts)
+    assert got[1:] == [getattr(fox.FoxFwdOpts, f).offset for f in fields]

@@ -1101,3 +1101,63 @@ def test_fused_scan_then_backward_with_resets(fox, B, H, L, D):
     check("LSE", host(lse), LSE)
     ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s, O=O, LSE=LSE)[:4]
     _check_grads([host(t) for t in g], ref)
+
+
+# ------------------------------------------------------------------------------ Pro fusions
+@pytest.mark.parametrize("L,D,g_dt,weighted", [(300, 64, "bf16", False), (1000, 128, "f32", True),
+                                               (777, 128, "bf16", True), (1, 64, "f32", False)])
+def test_fwd_ex_qnorm_and_output_gate(fox, L, D, g_dt, weighted):
+    """fox_attn_fwd_ex: the query's QK-norm on load and the output norm and gate in the epilogue,
+    against the oracle (rms_norm, attn_fwd, out_norm_gate in fp64); with and without O."""
+    B, H = 1, 3
+    case = fi.make_case(B, H, L, D, "bf16", seed=1400 + L + D, gate="per_head")
+    rng = np.random.default_rng(L + D)
+    q3 = fi.bf16_round((case.q * rng.uniform(0.3, 3.0, size=(B, H, L, 1))).astype(np.float32))
+    g = rng.standard_normal((B, H, L, D)).astype(np.float32) * 2
+    g = fi.bf16_round(g) if g_dt == "bf16" else g
+    qw = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32) if weighted else None
+    ow = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32) if weighted else None
+    say(f"fwd_ex L={L} D={D} g={g_dt} weighted={weighted}")
+    q, v = dev(q3, "bf16"), dev(case.v, "bf16")
+    kn = fox.fox_qk_rmsnorm(dev(case.k, "bf16"), eps=1e-6)  # keys come normalised
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    o, lse, y = fox.fox_attn_fwd_ex(q, kn, v, c, o_dtype=torch.float32, q_norm_eps=1e-6,
+                                    q_norm_weight=None if qw is None else dev(qw, "f32"),
+                                    gate=dev(g, g_dt), out_norm_weight=None if ow is None else dev(ow, "f32"),
+                                    out_norm_eps=1e-6)
+    _, _, y2 = fox.fox_attn_fwd_ex(q, kn, v, c, o_dtype=None, want_lse=False, q_norm_eps=1e-6,
+                                   q_norm_weight=None if qw is None else dev(qw, "f32"),
+                                   gate=dev(g, g_dt), out_norm_weight=None if ow is None else dev(ow, "f32"),
+                                   out_norm_eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "y differs when O is not written"
+    qh = oracle.rms_norm(q3, 1e-6, qw)
+    kh = host(kn)  # the bits the kernel reads
+    O, LSE = oracle.attn_fwd(qh, kh, case.v, case.log_f, scale=default_scale(D))
+    Y = oracle.out_norm_gate(O, g, 1e-6, ow)
+    check("O", host(o), O)
+    check("LSE", host(lse), LSE)
+    check("y", host(y), Y)
+
+
+def test_fwd_ex_pro_pipeline_config4(fox):
+    """Workload 4 with the fusions: gate -> scan, k -> QK-norm, then fox_attn_fwd_ex normalising q
+    on load and applying an output gate; every row of all 12 heads."""
+    case = fi.config_case(4)
+    say("pro pipeline config4, fused q-norm and output gate")
+    rng = np.random.default_rng(404)
+    g = fi.bf16_round(rng.standard_normal(case.q.shape).astype(np.float32))
+    lf = fox.fox_gate_logf(dev(case.x, "bf16"), dev(case.w_f, "f32"), dev(case.b_f, "f32"))
+    c = fox.fox_logf_cumsum(lf)
+    kn = fox.fox_qk_rmsnorm(dev(case.k, "bf16"), eps=1e-6)
+    o, lse, y = fox.fox_attn_fwd_ex(dev(case.q, "bf16"), kn, dev(case.v, "bf16"), c,
+                                    o_dtype=torch.bfloat16, q_norm_eps=1e-6, gate=dev(g, "bf16"))
+    torch.cuda.synchronize()
+    cc = oracle.cumsum_logf(oracle.gate_logf(case.x, case.w_f, case.b_f))
+    qh = oracle.rms_norm(case.q, 1e-6)
+    kh = oracle.rms_norm(case.k, 1e-6)
+    say("  oracle forward (12 heads, L=16384) ...")
+    O, LSE = oracle.attn_fwd(qh, kh, case.v, c=cc, scale=default_scale(case.D), block=1024)
+    check("O, all rows and heads", host(o), O)
+    check("LSE, all rows and heads", host(lse), LSE)
+    check("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6))
