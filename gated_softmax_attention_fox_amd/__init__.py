@@ -49,7 +49,9 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfox.so")
+# FOX_LIBRARY names another build of the same library (the host tests use it to load a build
+# whose host code is compiled with address and undefined-behaviour sanitizers).
+LIB_PATH = os.environ.get("FOX_LIBRARY") or os.path.join(_PKG, "libfox.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fox.h")
 
 FOX_OK, FOX_E_INVALID, FOX_E_UNSUPPORTED, FOX_E_LAUNCH = 0, 1, 2, 3

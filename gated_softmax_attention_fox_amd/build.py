@@ -4,6 +4,10 @@
 
 Compiles every csrc/*.hip and csrc/*.cpp into _build/ and links
 gated_softmax_attention_fox_amd/libfox.so. Always recompiles.
+
+    python -m gated_softmax_attention_fox_amd.build --sanitized
+
+builds _build/libfox_san.so, the same library with its host code under ASan and UBSan.
 """
 from __future__ import annotations
 
@@ -69,5 +73,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "libfox_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer"]
+
+
+def build_sanitized() -> str:
+    """A CPU-side check build: the host code (abi.cpp) compiled by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the HIP kernel objects of build() (device code is
+    not instrumented). Written to _build/libfox_san.so; load it through FOX_LIBRARY with the
+    sanitizer runtimes preloaded (the host tests do)."""
+    objs = [os.path.join(BUILD, f.rsplit(".", 1)[0] + ".o")
+            for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+    san_obj = os.path.join(BUILD, "abi_san.o")
+    _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", *SAN_FLAGS, "-D__HIP_PLATFORM_AMD__",
+          f"-I{rocm}/include", f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, "abi.cpp"),
+          "-o", san_obj])
+    _run(["g++", "-shared", *SAN_FLAGS, san_obj, *objs, f"-L{rocm}/lib", f"-Wl,-rpath,{rocm}/lib",
+          "-lamdhip64", "-o", SAN_LIB])
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())
+    else:
+        build(verbose="-q" not in sys.argv)
