@@ -44,6 +44,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxL = int64_t(1) << 23;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
 
+// a * b <= lim for a, b >= 1, decided without forming a product that could overflow.
+bool prod_le(int64_t a, int64_t b, int64_t lim) { return a <= lim / b; }
+
 #define FOX_REQUIRE(cond, ...)                                   \
   do {                                                           \
     if (!(cond)) return fail(FOX_E_INVALID, __VA_ARGS__);        \
@@ -61,7 +64,7 @@ fox_status check_bhld(int64_t B, int64_t H, int64_t L, int64_t D) {
   FOX_REQUIRE(L >= 1 && L <= kMaxL, "L must be in [1, %lld] (got %lld)", (long long)kMaxL,
               (long long)L);
   FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
-  FOX_REQUIRE(B * H <= (int64_t(1) << 31) / 1024 && B * H * L * D <= kMaxElems,
+  FOX_REQUIRE(prod_le(B, H, (int64_t(1) << 31) / 1024) && B * H * L * D <= kMaxElems,
               "B*H*L*D too large");
   return FOX_OK;
 }
@@ -140,7 +143,7 @@ fox_status fox_gate_logf(const void* x, fox_dtype x_dt, const float* w_f, const 
   FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
   FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
               "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
-  FOX_REQUIRE(B * ((L + 63) / 64) < (int64_t(1) << 31), "B*L too large");
+  FOX_REQUIRE(prod_le(B, (L + 63) / 64, (int64_t(1) << 31) - 1), "B*L too large");
   return launched(fox::launch_gate(x, x_dt == FOX_BF16, w_f, b_f, log_f, B, L, d_model, H,
                                    fox::GateKind::kLogSigmoid, (hipStream_t)stream),
                   "fox_gate_logf");
@@ -151,8 +154,9 @@ fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, in
   FOX_REQUIRE_PTR(x);
   FOX_REQUIRE_PTR(y);
   FOX_REQUIRE(dt == FOX_BF16 || dt == FOX_F32, "dt must be FOX_BF16 or FOX_F32");
-  FOX_REQUIRE(rows >= 1 && rows * (D / 8) / 256 < (int64_t(1) << 31), "rows out of range");
   FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
+  FOX_REQUIRE(rows >= 1 && prod_le(rows, D, kMaxElems) && rows * (D / 8) / 256 < (int64_t(1) << 31),
+              "rows out of range");
   FOX_REQUIRE(eps >= 0.f, "eps must be >= 0");
   return launched(fox::launch_rmsnorm(x, y, dt == FOX_BF16, rows, D, eps, weight,
                                       (hipStream_t)stream),
@@ -160,7 +164,9 @@ fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, in
 }
 
 size_t fox_gate_logf_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H) {
-  if (B < 1 || L < 1 || d_model < 1 || H < 1) return 0;
+  if (B < 1 || L < 1 || L > kMaxL || d_model < 1 || d_model > 8192 || H < 1 || H > 64 ||
+      !prod_le(B, L, (int64_t(1) << 31) / 64))
+    return 0;
   return fox::gate_bwd_workspace_bytes(B, L, d_model, H);
 }
 
@@ -183,7 +189,7 @@ fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, co
   FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
   FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
               "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
-  FOX_REQUIRE(B * L <= (int64_t(1) << 31) / 64 && B * L * d_model <= kMaxElems,
+  FOX_REQUIRE(prod_le(B, L, (int64_t(1) << 31) / 64) && B * L * d_model <= kMaxElems,
               "B*L*d_model too large");
   const size_t need = fox::gate_bwd_workspace_bytes(B, L, d_model, H);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
@@ -195,7 +201,7 @@ fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, co
 }
 
 size_t fox_qk_rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D) {
-  if (rows < 1 || !(D == 64 || D == 128)) return 0;
+  if (rows < 1 || !(D == 64 || D == 128) || !prod_le(rows, D, kMaxElems)) return 0;
   return fox::rmsnorm_bwd_workspace_bytes(rows, D);
 }
 
@@ -208,7 +214,7 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
   FOX_REQUIRE_PTR(dx);
   FOX_REQUIRE(dt == FOX_BF16 || dt == FOX_F32, "dt must be FOX_BF16 or FOX_F32");
   FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
-  FOX_REQUIRE(rows >= 1 && rows * D <= kMaxElems, "rows out of range");
+  FOX_REQUIRE(rows >= 1 && prod_le(rows, D, kMaxElems), "rows out of range");
   FOX_REQUIRE(eps >= 0.f, "eps must be >= 0");
   FOX_REQUIRE(!(dweight && !weight), "dweight needs the weight it is the gradient of");
   if (dweight) {
@@ -226,7 +232,7 @@ fox_status fox_qk_rmsnorm_bwd(const void* x, fox_dtype dt, const float* dy, floa
 
 size_t fox_attn_skip_plan_bytes(int64_t B, int64_t H, int64_t L, int64_t D) {
   (void)D;
-  if (B < 1 || H < 1 || L < 1) return 0;
+  if (B < 1 || H < 1 || L < 1 || L > kMaxL || !prod_le(B, H, int64_t(1) << 31)) return 0;
   return fox::skip_plan_layout(B * H, L).bytes;
 }
 
@@ -386,7 +392,7 @@ fox_status fox_attn_fwd_logf(const void* q, const void* k, const void* v, fox_dt
 
 size_t fox_attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D) {
   (void)D;
-  if (B < 1 || H < 1 || L < 1) return 0;
+  if (B < 1 || H < 1 || L < 1 || L > kMaxL || !prod_le(B, H, int64_t(1) << 31)) return 0;
   return fox::bwd_workspace_bytes(B * H, L);
 }
 
@@ -514,7 +520,8 @@ fox_status fox_attn_bwd_delta(const void* dO, fox_dtype dO_dt, const float* o, f
   FOX_REQUIRE_PTR(delta);
   FOX_REQUIRE(dO_dt == FOX_BF16 || dO_dt == FOX_F32, "dO_dt must be FOX_BF16 or FOX_F32");
   FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
-  FOX_REQUIRE(rows >= 1 && rows * (D / 8) / 256 < (int64_t(1) << 31), "rows out of range");
+  FOX_REQUIRE(rows >= 1 && prod_le(rows, D, kMaxElems) && rows * (D / 8) / 256 < (int64_t(1) << 31),
+              "rows out of range");
   if (dO_dt == FOX_F32)
     return launched(fox::launch_bwd_delta_f32((const float*)dO, o, delta, rows, D,
                                               (hipStream_t)stream),
@@ -599,7 +606,7 @@ fox_status check_shift_gate(const void* x, fox_dtype x_dt, const float* w, int64
   FOX_REQUIRE(H >= 1 && H <= 64, "H must be in [1, 64] (got %lld)", (long long)H);
   FOX_REQUIRE(d_model >= 8 && d_model <= 8192 && d_model % 8 == 0,
               "d_model must be a multiple of 8 in [8, 8192] (got %lld)", (long long)d_model);
-  FOX_REQUIRE(B * L <= (int64_t(1) << 31) / 64 && B * L * d_model <= kMaxElems,
+  FOX_REQUIRE(prod_le(B, L, (int64_t(1) << 31) / 64) && B * L * d_model <= kMaxElems,
               "B*L*d_model too large");
   return FOX_OK;
 }
@@ -607,7 +614,7 @@ fox_status check_shift_gate(const void* x, fox_dtype x_dt, const float* w, int64
 fox_status check_rows(const void* x, int64_t rows, int64_t D, float eps) {
   FOX_REQUIRE_PTR(x);
   FOX_REQUIRE(D == 64 || D == 128, "D must be 64 or 128 (got %lld)", (long long)D);
-  FOX_REQUIRE(rows >= 1 && rows * D <= kMaxElems, "rows out of range");
+  FOX_REQUIRE(rows >= 1 && prod_le(rows, D, kMaxElems), "rows out of range");
   FOX_REQUIRE(eps >= 0.f, "eps must be >= 0");
   return FOX_OK;
 }
@@ -646,6 +653,8 @@ fox_status fox_shift_gate_bwd(const void* x, fox_dtype x_dt, const float* w, con
 fox_status fox_kv_shift(const void* x, fox_dtype dt, const float* alpha, void* y, int normalize,
                         float eps, const float* weight, int64_t BH, int64_t L, int64_t D,
                         void* stream) {
+  FOX_REQUIRE(BH >= 1 && L >= 1 && L <= kMaxL && prod_le(BH, L, kMaxElems),
+              "BH >= 1, 1 <= L <= 2^23 and BH*L*D <= 2^40 required");
   fox_status st = check_rows(x, BH * L, D, eps);
   if (st != FOX_OK) return st;
   FOX_REQUIRE_PTR(alpha);
@@ -661,6 +670,8 @@ fox_status fox_kv_shift(const void* x, fox_dtype dt, const float* alpha, void* y
 fox_status fox_kv_shift_bwd(const void* x, fox_dtype dt, const float* alpha, const float* dy,
                             float* dx, float* dalpha, int normalize, float eps,
                             const float* weight, int64_t BH, int64_t L, int64_t D, void* stream) {
+  FOX_REQUIRE(BH >= 1 && L >= 1 && L <= kMaxL && prod_le(BH, L, kMaxElems),
+              "BH >= 1, 1 <= L <= 2^23 and BH*L*D <= 2^40 required");
   fox_status st = check_rows(x, BH * L, D, eps);
   if (st != FOX_OK) return st;
   FOX_REQUIRE_PTR(alpha);
@@ -708,7 +719,9 @@ fox_status fox_out_norm_gate_bwd(const void* o, fox_dtype o_dt, const void* g, f
 }
 
 size_t fox_attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t T_max, int64_t D) {
-  if (B < 1 || H < 1 || T_max < 1 || (D != 64 && D != 128)) return 0;
+  if (B < 1 || H < 1 || T_max < 1 || T_max > kMaxL || (D != 64 && D != 128) ||
+      !prod_le(B, H, int64_t(1) << 31))
+    return 0;
   return fox::decode_workspace_bytes(B * H, T_max, D);
 }
 

@@ -33,8 +33,10 @@
  *     against one reference, so a fall of c by F inside one tile leaves errors of about
  *     2^-24 F (log2 units) in the weights on one side of it, whatever the type of c: keep a
  *     single reset within about -2000 (at -1e4 d log f can reach 2e-2 on bf16 inputs).
+ *   - Size queries (the *_bytes calls) return 0 for sizes outside these limits; every size
+ *     check is made without an intermediate product that could overflow.
  *   - Calls are reentrant: the library holds no mutable global state apart from the
- *     thread-local error message.
+ *     thread-local error message and the per-device scratch array of fox_attn_bwd_noalloc.
  */
 #ifndef FOX_H
 #define FOX_H

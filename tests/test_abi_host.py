@@ -270,3 +270,48 @@ def test_fwd_opts_layout_matches_c():
         got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
     assert got[0] == ctypes.sizeof(fox.FoxFwdOpts)
     assert got[1:] == [getattr(fox.FoxFwdOpts, f).offset for f in fields]
+
+
+BIG = 1 << 62  # sizes whose products overflow int64
+
+
+def test_size_queries_reject_extreme_sizes(lib):
+    """Size queries answer 0 for sizes beyond the limits, without overflowing on the way (the
+    sanitized build of this file checks the arithmetic with UBSan)."""
+    for b, h, l in ((BIG, BIG, 16), (BIG, 2, 16), (2, BIG, 16), (1, 1, BIG)):
+        assert lib.fox_attn_skip_plan_bytes(b, h, l, 128) == 0
+        assert lib.fox_attn_bwd_workspace_bytes(b, h, l, 128) == 0
+        assert lib.fox_attn_decode_workspace_bytes(b, h, l, 128) == 0
+    assert lib.fox_gate_logf_bwd_workspace_bytes(BIG, 16, 128, 4) == 0
+    assert lib.fox_gate_logf_bwd_workspace_bytes(1, BIG, 128, 4) == 0
+    assert lib.fox_gate_logf_bwd_workspace_bytes(1, 16, BIG, 4) == 0
+    assert lib.fox_qk_rmsnorm_bwd_workspace_bytes(BIG, 128) == 0
+    assert lib.fox_attn_bwd_workspace_bytes(1, 12, 16384, 128) > 0  # a valid size still answers
+
+
+@host_only
+def test_calls_reject_extreme_sizes(lib):
+    """Every entry point with int64 sizes rejects products beyond its limits with
+    FOX_E_INVALID, before forming a product that could overflow."""
+    e = 1e-6
+    for b, h in ((BIG, BIG), (BIG, 1), (1, BIG)):
+        assert _fwd(lib, B=b, H=h) == 1
+        assert lib.fox_attn_skip_plan(P, P, 1, P, P, 1 << 20, b, h, 64, 128, 0.1, None) == 1
+        assert lib.fox_attn_decode(P, P, P, 1, P, P, None, P, 1, P, P, 1 << 20, b, h, 64, 128,
+                                   0.1, 1, None) == 1
+        assert lib.fox_attn_decode_key_norms(P, 1, P, P, b, h, 64, 128, None) == 1
+    assert lib.fox_gate_logf(P, 1, P, P, P, BIG, 64, 128, 4, None) == 1
+    assert lib.fox_gate_logf_bwd(P, 1, P, P, P, P, P, P, P, 1 << 20, BIG, 64, 128, 4, None) == 1
+    assert lib.fox_shift_gate(P, 1, P, P, BIG, 64, 128, 4, None) == 1
+    assert lib.fox_shift_gate_bwd(P, 1, P, P, P, P, P, 1 << 20, BIG, 64, 128, 4, None) == 1
+    assert lib.fox_qk_rmsnorm(P, P, 1, BIG, 128, e, None, None) == 1
+    assert lib.fox_qk_rmsnorm(P, P, 1, BIG, BIG, e, None, None) == 1
+    assert lib.fox_qk_rmsnorm_bwd(P, 1, P, P, None, None, None, 0, BIG, 128, e, None) == 1
+    assert lib.fox_attn_bwd_delta(P, 1, P, P, BIG, 128, None) == 1
+    assert lib.fox_out_norm_gate(P, 1, P, 1, None, e, P, BIG, 128, None) == 1
+    assert lib.fox_out_norm_gate_bwd(P, 1, P, 1, None, e, P, P, P, BIG, 128, None) == 1
+    for bh, l in ((BIG, 16), (BIG, BIG), (1 << 40, 1 << 20)):
+        assert lib.fox_kv_shift(P, 1, P, P, 1, e, None, bh, l, 128, None) == 1
+        assert lib.fox_kv_shift_bwd(P, 1, P, P, P, P, 1, e, None, bh, l, 128, None) == 1
+    assert lib.fox_logf_cumsum(P, P + 1024, BIG, 16, None) == 1
+    assert lib.fox_dlogf_from_dc(P, P + 1024, P + 2048, BIG, 16, None) == 1

@@ -35,7 +35,7 @@ def test_host_abi_under_asan_and_ubsan():
     env = dict(os.environ, FOX_LIBRARY=lib, LD_PRELOAD=f"{asan}:{ubsan}",
                ASAN_OPTIONS="detect_leaks=0:alloc_dealloc_mismatch=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-s", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_abi_host.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                        text=True, timeout=600)
