@@ -578,7 +578,7 @@ def pro_step(args, torch, fi, fox, dev):
         dlf = run("dlogf", lambda: fox.fox_dlogf_from_dc(dcq, dck))
         dq, _ = run("qnorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(q, dqn, eps=1e-6))
         dk, _ = run("knorm_bwd", lambda: fox.fox_qk_rmsnorm_bwd(k, dkn, eps=1e-6))
-        dx, dw, db = run("gate_bwd", lambda: fox.fox_gate_logf_bwd(x, w_f, b_f, dlf))
+        dx, dw, db = run("gate_bwd", lambda: fox.fox_gate_logf_bwd(x, w_f, b_f, dlf, log_f=lf))
         return dq, dk, dv, dx, dw, db
 
     for _ in range(args.warmup):
@@ -600,7 +600,7 @@ def pro_step(args, torch, fi, fox, dev):
         "gate": n_tok * dm * 2 + B * H * L * 4,
         "qnorm": n_qk * 2 * 2, "knorm": n_qk * 2 * 2,
         "qnorm_bwd": n_qk * (2 + 4 + 4), "knorm_bwd": n_qk * (2 + 4 + 4),
-        "gate_bwd": n_tok * dm * (2 + 4) + B * H * L * 4,
+        "gate_bwd": n_tok * dm * (2 + 4) + B * H * L * 8,  # x, dx; dlog_f and log f
     }
     hbm = {n: {"ms": round(kern_ms[n], 4), "bytes": int(b),
                "GB_per_s": round(b / (kern_ms[n] * 1e-3) / 1e9, 1),

@@ -78,8 +78,8 @@ _SIGS = {
                                       _c_vp]),
     "fox_gate_logf_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "fox_gate_logf_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
-                                         _c_vp, _c_vp, _c_sz, _c_i64, _c_i64, _c_i64, _c_i64,
-                                         _c_vp]),
+                                         _c_vp, _c_vp, _c_vp, _c_sz, _c_i64, _c_i64, _c_i64,
+                                         _c_i64, _c_vp]),
     "fox_qk_rmsnorm_bwd_workspace_bytes": (_c_sz, [_c_i64, _c_i64]),
     "fox_qk_rmsnorm_bwd": (ctypes.c_int, [_c_vp, ctypes.c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                           _c_sz, _c_i64, _c_i64, _c_f32, _c_vp]),
@@ -262,8 +262,10 @@ def fox_qk_rmsnorm(x: torch.Tensor, eps: float = 1e-6, weight: torch.Tensor | No
 
 
 def fox_gate_logf_bwd(x: torch.Tensor, w_f: torch.Tensor, b_f: torch.Tensor,
-                      dlog_f: torch.Tensor):
-    """(dx [B, L, d_model], dw_f [H, d_model], db_f [H]), all fp32, given dlog_f [B, H, L]."""
+                      dlog_f: torch.Tensor, log_f: torch.Tensor | None = None):
+    """(dx [B, L, d_model], dw_f [H, d_model], db_f [H]), all fp32, given dlog_f [B, H, L].
+    log_f: the forward's output (fox_gate_logf of the same inputs), from which the backward
+    takes sigmoid(-z) instead of recomputing z from x; None recomputes."""
     lib = load_library()
     px = _dev(x, "x", (torch.bfloat16, torch.float32), 3)
     pw = _dev(w_f, "w_f", (torch.float32,), 2)
@@ -273,12 +275,16 @@ def fox_gate_logf_bwd(x: torch.Tensor, w_f: torch.Tensor, b_f: torch.Tensor,
     H = w_f.shape[0]
     if w_f.shape[1] != dm or b_f.shape[0] != H or tuple(dlog_f.shape) != (B, H, L):
         raise ValueError("w_f must be [H, d_model], b_f [H] and dlog_f [B, H, L]")
+    pl = ctypes.c_void_p(0)
+    if log_f is not None:
+        pl = _dev(log_f, "log_f", (torch.float32,), 3)
+        _shape(log_f, "log_f", (B, H, L))
     dx = torch.empty((B, L, dm), dtype=torch.float32, device=x.device)
     dw = torch.empty((H, dm), dtype=torch.float32, device=x.device)
     db = torch.empty((H,), dtype=torch.float32, device=x.device)
     need = int(lib.fox_gate_logf_bwd_workspace_bytes(B, L, dm, H))
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
-    _check(lib.fox_gate_logf_bwd(px, _code(x.dtype), pw, pb, pg, ctypes.c_void_p(dx.data_ptr()),
+    _check(lib.fox_gate_logf_bwd(px, _code(x.dtype), pw, pb, pg, pl, ctypes.c_void_p(dx.data_ptr()),
                                  ctypes.c_void_p(dw.data_ptr()), ctypes.c_void_p(db.data_ptr()),
                                  ctypes.c_void_p(ws.data_ptr()), ws.numel(), B, L, dm, H,
                                  _stream(x)), "fox_gate_logf_bwd")

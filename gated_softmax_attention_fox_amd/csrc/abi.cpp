@@ -171,13 +171,14 @@ size_t fox_gate_logf_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, 
 }
 
 fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
-                             const float* dlog_f, float* dx, float* dw_f, float* db_f,
-                             void* workspace, size_t workspace_bytes, int64_t B, int64_t L,
-                             int64_t d_model, int64_t H, void* stream) {
+                             const float* dlog_f, const float* log_f, float* dx, float* dw_f,
+                             float* db_f, void* workspace, size_t workspace_bytes, int64_t B,
+                             int64_t L, int64_t d_model, int64_t H, void* stream) {
   FOX_REQUIRE_PTR(x);
   FOX_REQUIRE_PTR(w_f);
   FOX_REQUIRE(b_f != nullptr, "b_f must not be NULL");
   FOX_REQUIRE_PTR(dlog_f);
+  if (log_f) FOX_REQUIRE(aligned16(log_f), "log_f must be 16-byte aligned");
   FOX_REQUIRE_PTR(dx);
   FOX_REQUIRE_PTR(dw_f);
   FOX_REQUIRE(db_f != nullptr, "db_f must not be NULL");
@@ -194,8 +195,8 @@ fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, co
   const size_t need = fox::gate_bwd_workspace_bytes(B, L, d_model, H);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
-  return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w_f, b_f, dlog_f, dx, dw_f, db_f,
-                                       workspace, B, L, d_model, H, fox::GateKind::kLogSigmoid,
+  return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w_f, b_f, dlog_f, log_f, dx, dw_f,
+                                       db_f, workspace, B, L, d_model, H, fox::GateKind::kLogSigmoid,
                                        (hipStream_t)stream),
                   "fox_gate_logf_bwd");
 }
@@ -644,8 +645,8 @@ fox_status fox_shift_gate_bwd(const void* x, fox_dtype x_dt, const float* w, con
   const size_t need = fox::gate_bwd_workspace_bytes(B, L, d_model, H);
   FOX_REQUIRE(workspace_bytes >= need, "workspace too small: %zu bytes given, %zu needed",
               workspace_bytes, need);
-  return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w, nullptr, dalpha, dx, dw, nullptr,
-                                       workspace, B, L, d_model, H, fox::GateKind::kSigmoid,
+  return launched(fox::launch_gate_bwd(x, x_dt == FOX_BF16, w, nullptr, dalpha, nullptr, dx, dw,
+                                       nullptr, workspace, B, L, d_model, H, fox::GateKind::kSigmoid,
                                        (hipStream_t)stream),
                   "fox_shift_gate_bwd");
 }

@@ -27,16 +27,18 @@ enum class GateKind { kLogSigmoid, kSigmoid };
 hipError_t launch_gate(const void* x, bool x_bf16, const float* w_f, const float* b_f, float* out,
                        int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
                        hipStream_t s);
-// Backward of the gate's output: dz[b, t, h] = dout[b, h, t] * (d out / dz) (token-major).
+// Backward of the gate's output: dz[b, h, t] = dout[b, h, t] * (d out / dz).
 hipError_t launch_gate_dz(const void* x, bool x_bf16, const float* w_f, const float* b_f,
                           const float* dout, float* dz, int64_t B, int64_t L, int64_t d_model,
                           int64_t H, GateKind kind, hipStream_t s);
 // Backward of the gate: dx, dw_f and (when not null) db_f (workspace: gate_bwd_workspace_bytes).
+// log_f (forget gate only, may be null): the forward's output, from which dz is formed without
+// a pass over x.
 size_t gate_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H);
 hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const float* b_f,
-                           const float* dout, float* dx, float* dw_f, float* db_f, void* ws,
-                           int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
-                           hipStream_t s);
+                           const float* dout, const float* log_f, float* dx, float* dw_f,
+                           float* db_f, void* ws, int64_t B, int64_t L, int64_t d_model, int64_t H,
+                           GateKind kind, hipStream_t s);
 // Backward of the QK-norm: dx and, when dw is not null, the weight gradient.
 size_t rmsnorm_bwd_workspace_bytes(int64_t rows, int64_t D);
 hipError_t launch_rmsnorm_bwd(const void* x, bool bf16, const float* dy, const float* w, float* dx,

@@ -11,8 +11,8 @@
 // per-wave partial sums meet in LDS and lane t writes log f for token t, evaluated stably as
 // -log1p(exp(-z)) for z >= 0 and z - log1p(exp(z)) otherwise.
 //
-// The same kernel serves the backward (kBwd): it recomputes z and writes, token-major,
-// dz[b, t, h] = dlog_f[b, h, t] * sigma(-z), since d log sigma(z) / dz = 1 - sigma(z) = sigma(-z);
+// The same kernel serves the backward (kBwd): it recomputes z and writes
+// dz[b, h, t] = dlog_f[b, h, t] * sigma(-z), since d log sigma(z) / dz = 1 - sigma(z) = sigma(-z);
 // sigma(-z) = 1 / (1 + exp(z)) goes to 0 or 1 in the limits without a NaN.
 //
 // With kSig the output is sigma(z) itself and the bias may be absent: the Pro block's shift gates
@@ -27,6 +27,7 @@ constexpr int kGateTok = 64;       // tokens per workgroup
 constexpr int kGateSlab = 256;     // x columns staged per step
 constexpr int kGatePitch = kGateSlab + 8;
 constexpr int kGateHeads = 16;     // heads handled per workgroup (blockIdx.y walks head groups)
+constexpr int kGateSB = 3;         // 32-column steps per load batch of the matrix-core gate
 
 __device__ __forceinline__ float log_sigmoid(float z) {
   return z >= 0.f ? -log1pf(expf(-z)) : z - log1pf(expf(z));
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
       if (t < L) {
         if constexpr (kBwd) {
           const float g = dlog_f[((size_t)b * H + h0 + h) * L + t];
-          out[((size_t)b * L + t) * H + h0 + h] =
+          out[((size_t)b * H + h0 + h) * L + t] =
               kSig ? g * sigmoid(z) / (1.0f + expf(z)) : g / (1.0f + expf(z));
         } else {
           out[((size_t)b * H + h0 + h) * L + t] = kSig ? sigmoid(z) : log_sigmoid(z);
@@ -129,22 +130,28 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 }
 
 // bf16 x on the matrix cores: z[16 tokens][16 heads] = x[16 tokens][:] . w_f[16 heads][:]^T with
-// v_mfma_f32_16x16x32_bf16. A workgroup takes NTT tiles of 16 tokens (blockIdx.y picks the group
-// of 16 heads); its 4 waves take every 4th 32-column step, load and split that step's w_f once
-// for all NTT tiles, and their partial sums meet in LDS. Lane l supplies A = x[token l % 16][8 (l / 16) .. +7] of each 32-column step
-// straight from HBM and B = w_f[head l % 16][same columns]; w_f is split into bf16 hi and lo
-// parts (hi = bf16(w), lo = bf16(w - hi)) and both are multiplied, so z keeps about 16
-// significant bits of w on top of exact products and fp32 accumulation. Lane l receives z for
-// head l % 16 and tokens 4 (l / 16) .. +3. Needs d_model % 32 == 0.
+// v_mfma_f32_16x16x32_bf16. A workgroup of 8 waves takes NTT tiles of 16 tokens (blockIdx.y picks
+// the group of 16 heads). Wave w takes the 32-column steps d0 = 32 (w + 8 s); lane l supplies
+// A = x[token l % 16][d0 + 8 (l / 16) .. +7] straight from HBM and B = w_f[head l % 16][same
+// columns]. w_f is split into bf16 hi and lo parts (hi = bf16(w), lo = bf16(w - hi)) and both are
+// multiplied, so z keeps about 16 significant bits of w on top of exact products and fp32
+// accumulation; lane l receives z for head l % 16 and tokens 4 (l / 16) .. +3. Needs
+// d_model % 32 == 0.
+// Measured on the Pro shape (x [16384, 1536]), the costs beyond the bare x stream were the w_f
+// reads (each workgroup reads all of w_f for its heads: with 64 tokens per workgroup that stream
+// is half of what 32 tokens cost) and a one-wave epilogue of scattered stores. So every load of a
+// batch of kGateSB steps is issued before its first product, padded heads load nothing, and the
+// epilogue spreads the (head, token) outputs over all 512 threads, each head's 64 tokens stored
+// contiguously.
 template <bool kBwd, bool kSig, int NTT>
-__global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict__ x,
+__global__ __launch_bounds__(512) void gate_mfma_kernel(const bf16_t* __restrict__ x,
                                                         const float* __restrict__ w_f,
                                                         const float* __restrict__ b_f,
                                                         const float* __restrict__ dlog_f,
                                                         float* __restrict__ out, int L, int dm,
                                                         int H, int tiles_per_b, int n_tiles) {
   typedef float f32x4v __attribute__((ext_vector_type(4)));
-  __shared__ f32x4v part[4][NTT][64];
+  __shared__ f32x4v part[8][NTT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int h0 = blockIdx.y * 16;
@@ -166,57 +173,76 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(const bf16_t* __restrict
 #pragma unroll
   for (int u = 0; u < NTT; ++u) acc[u] = f32x4v{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-#pragma unroll 2
-  for (int d0 = 32 * wave; d0 < dm; d0 += 128) {
-    const float4 w0 = *reinterpret_cast<const float4*>(wr + d0);
-    const float4 w1 = *reinterpret_cast<const float4*>(wr + d0 + 4);
-    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-    bf16x8 bh, bl;
+  const int n_steps = (dm / 32 - wave + 7) / 8;  // this wave's 32-column steps
+  for (int s0 = 0; s0 < n_steps; s0 += kGateSB) {
+    u32x4 xa[kGateSB][NTT];
+    float4 wa[kGateSB][2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float w = head_ok ? wv[e] : 0.f;
-      const __bf16 hi = (__bf16)w;
-      bh[e] = hi;
-      bl[e] = (__bf16)(w - (float)hi);
+    for (int j = 0; j < kGateSB; ++j) {
+      if (s0 + j < n_steps) {  // wave-uniform
+        const int d0 = 32 * (wave + 8 * (s0 + j));
+#pragma unroll
+        for (int u = 0; u < NTT; ++u) xa[j][u] = *reinterpret_cast<const u32x4*>(xr[u] + d0);
+        if (head_ok) {
+          wa[j][0] = *reinterpret_cast<const float4*>(wr + d0);
+          wa[j][1] = *reinterpret_cast<const float4*>(wr + d0 + 4);
+        } else {
+          wa[j][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+          wa[j][1] = wa[j][0];
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < NTT; ++u) {  // one load and split of w_f serves all the tiles
-      const u32x4 xa = *reinterpret_cast<const u32x4*>(xr[u] + d0);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok[u] ? xa : zero4);
-      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[u], 0, 0, 0);
-      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[u], 0, 0, 0);
+    for (int j = 0; j < kGateSB; ++j) {
+      if (s0 + j >= n_steps) break;
+      const float wv[8] = {wa[j][0].x, wa[j][0].y, wa[j][0].z, wa[j][0].w,
+                           wa[j][1].x, wa[j][1].y, wa[j][1].z, wa[j][1].w};
+      bf16x8 bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 hi = (__bf16)wv[e];
+        bh[e] = hi;
+        bl[e] = (__bf16)(wv[e] - (float)hi);
+      }
+#pragma unroll
+      for (int u = 0; u < NTT; ++u) {  // one load and split of w_f serves all the tiles
+        const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok[u] ? xa[j][u] : zero4);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[u], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
   for (int u = 0; u < NTT; ++u) part[wave][u][lane] = acc[u];
   __syncthreads();
-  if (wave != 0) return;
-  const int hc = h0 + r;  // the head of this lane's output column
-  if (hc >= H) return;
-  const float bias = b_f ? b_f[hc] : 0.f;
-#pragma unroll
-  for (int u = 0; u < NTT; ++u) {
+  // Output (head h, token tok) of the workgroup's 16 NTT tokens: tile u = tok / 16; inside the
+  // tile, accumulator lane h + 16 g holds tokens 4 g .. 4 g + 3 in its four slots. The eight wave
+  // sums are added in wave order.
+  const int nh = H - h0 < 16 ? H - h0 : 16;
+  constexpr int kTok = 16 * NTT;
+  const float* pf = reinterpret_cast<const float*>(part);
+  for (int i = threadIdx.x; i < nh * kTok; i += 512) {
+    const int h = i / kTok, tok = i % kTok;
+    const int u = tok >> 4, tin = tok & 15, g = tin >> 2, j = tin & 3;
     const int tile = blockIdx.x * NTT + u;
-    if (tile >= n_tiles) break;
-    const int b = tile / tiles_per_b, t0 = (tile % tiles_per_b) * 16;
-    const f32x4v z4 = (part[0][u][lane] + part[1][u][lane]) + (part[2][u][lane] + part[3][u][lane]);
+    if (tile >= n_tiles) continue;
+    const int b = tile / tiles_per_b, tt = (tile % tiles_per_b) * 16 + tin;
+    if (tt >= L) continue;
+    float zs = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tt = t0 + 4 * grp + j;
-      if (tt >= L) break;
-      const float z = z4[j] + bias;
-      if constexpr (kBwd) {
-        const float g = dlog_f[((size_t)b * H + hc) * L + tt];
-        out[((size_t)b * L + tt) * H + hc] =
-            kSig ? g * sigmoid(z) / (1.0f + expf(z)) : g / (1.0f + expf(z));
-      } else {
-        out[((size_t)b * H + hc) * L + tt] = kSig ? sigmoid(z) : log_sigmoid(z);
-      }
+    for (int w = 0; w < 8; ++w) zs += pf[((w * NTT + u) * 64 + h + 16 * g) * 4 + j];
+    const float z = zs + (b_f ? b_f[h0 + h] : 0.f);
+    const size_t o = ((size_t)b * H + h0 + h) * L + tt;
+    if constexpr (kBwd) {
+      const float gd = dlog_f[o];
+      out[o] = kSig ? gd * sigmoid(z) / (1.0f + expf(z)) : gd / (1.0f + expf(z));
+    } else {
+      out[o] = kSig ? sigmoid(z) : log_sigmoid(z);
     }
   }
 }
 
-constexpr int kGateTiles = 2;  // token tiles per workgroup of the matrix-core gate
+constexpr int kGateTiles = 4;  // token tiles per workgroup of the matrix-core gate
 
 template <bool kBwd, bool kSig>
 void go_gate_mfma(const void* x, const float* w_f, const float* b_f, const float* dlog_f,
@@ -224,7 +250,7 @@ void go_gate_mfma(const void* x, const float* w_f, const float* b_f, const float
   const int tiles_per_b = (int)((L + 15) / 16);
   const int64_t n_tiles = B * tiles_per_b;
   const dim3 grid((unsigned)((n_tiles + kGateTiles - 1) / kGateTiles), (unsigned)((H + 15) / 16));
-  hipLaunchKernelGGL((gate_mfma_kernel<kBwd, kSig, kGateTiles>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((gate_mfma_kernel<kBwd, kSig, kGateTiles>), grid, dim3(512), 0, s,
                      static_cast<const bf16_t*>(x), w_f, b_f, dlog_f, out, (int)L, (int)d_model,
                      (int)H, tiles_per_b, (int)n_tiles);
 }

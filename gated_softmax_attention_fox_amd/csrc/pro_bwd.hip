@@ -3,7 +3,9 @@
 // "The Pro Block Architecture", Steps 1-2 and 4). Both are HBM-bound; every reduction runs in a
 // fixed order (per-chunk partials, then a second pass), so the results are deterministic.
 //
-// Gate: given dz[b, t, h] (gate.hip, backward mode),
+// Gate: given dz[b, h, t] (from gate.hip's backward mode, which recomputes z from x; or, for the
+// forget gate, from the forward's own output: d log sigma(z) / dz = 1 - sigma(z) = 1 - f, so
+// dz = dlog_f (1 - f) = -dlog_f expm1(log f), which needs no pass over x),
 //   dx[b, t, :] = sum_h dz[b, t, h] w_f[h, :]        (one pass over the tokens; on the matrix
 //                                                    cores when H <= 16, d_model % 128 == 0)
 //   dw_f[h, :]  = sum_{b,t} dz[b, t, h] x[b, t, :]   (partials per 256-token chunk, then a sum;
@@ -25,8 +27,22 @@ __device__ __forceinline__ float load_x(const void* x, bool bf16, size_t i) {
   return bf16 ? bf2f(static_cast<const bf16_t*>(x)[i]) : static_cast<const float*>(x)[i];
 }
 
+// dz[b, h, t] for the flattened token row = b L + t: stored, or formed from dlog_f and log f.
+struct DzSrc {
+  const float* dz;    // [B, H, L], or null
+  const float* dout;  // dlog_f [B, H, L] (used with logf)
+  const float* logf;  // the forward's log f [B, H, L]
+  int64_t L;
+  int H;
+  __device__ __forceinline__ float operator()(int64_t row, int h) const {
+    const int64_t b = row / L;
+    const size_t i = (size_t)(b * H + h) * L + (row - b * L);
+    return dz ? dz[i] : dout[i] * -expm1f(logf[i]);
+  }
+};
+
 // dx[r, d .. d+7] for token r (one thread per 8 columns).
-__global__ __launch_bounds__(256) void gate_dx_kernel(const float* __restrict__ dz,
+__global__ __launch_bounds__(256) void gate_dx_kernel(const DzSrc dz,
                                                       const float* __restrict__ w_f,
                                                       float* __restrict__ dx, int64_t rows, int dm,
                                                       int H) {
@@ -39,7 +55,7 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(const float* __restrict__ 
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   for (int h = 0; h < H; ++h) {
-    const float g = dz[r * H + h];
+    const float g = dz(r, h);
     const float4 w0 = *reinterpret_cast<const float4*>(w_f + (size_t)h * dm + d);
     const float4 w1 = *reinterpret_cast<const float4*>(w_f + (size_t)h * dm + d + 4);
     acc[0] = fmaf(g, w0.x, acc[0]); acc[1] = fmaf(g, w0.y, acc[1]);
@@ -53,7 +69,7 @@ __global__ __launch_bounds__(256) void gate_dx_kernel(const float* __restrict__ 
 
 // dx for up to 16 heads: a workgroup owns 16 tokens and thread c the columns 8c .. 8c + 7 of all
 // of them, so its slice of w_f (16 heads x 8 columns) is read once and stays in registers.
-__global__ __launch_bounds__(256) void gate_dx16_kernel(const float* __restrict__ dz,
+__global__ __launch_bounds__(256) void gate_dx16_kernel(const DzSrc dz,
                                                         const float* __restrict__ w_f,
                                                         float* __restrict__ dx, int64_t rows,
                                                         int dm, int H) {
@@ -80,7 +96,7 @@ __global__ __launch_bounds__(256) void gate_dx16_kernel(const float* __restrict_
 #pragma unroll
       for (int h = 0; h < 16; ++h) {
         if (h < H) {
-          const float g = dz[r * H + h];
+          const float g = dz(r, h);
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] = fmaf(g, w[h][e], acc[e]);
         }
@@ -94,19 +110,25 @@ __global__ __launch_bounds__(256) void gate_dx16_kernel(const float* __restrict_
 // Partial dw_f and db_f of one 256-token chunk, one 256-column slab and up to 16 heads: thread c
 // owns column slab * 256 + c and walks the chunk's tokens (coalesced rows of x).
 // dx on the matrix cores (d_model a multiple of 128, H <= 16): workgroup (token block, slab) owns
-// 128 tokens x 128 columns, each wave 32 columns. dx^T[32 columns x 32 tokens] is one
+// 128 tokens x 128 columns, each wave 32 columns; the workgroup's dz goes through LDS first. dx^T[32 columns x 32 tokens] is one
 // v_mfma_f32_32x32x16_bf16 per operand pair, k = the (zero-padded) 16 heads: A = w_f^T (the
 // wave's columns, loaded once), B = dz^T of 32 tokens. Both are split into three bf16 parts and
 // the six products that reach fp32 accuracy are summed smallest first; the hi x hi product is
 // exact, so the result matches an fp32 dot product of 16 terms to its rounding.
-__global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const float* __restrict__ dz,
+__global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const DzSrc dz,
                                                            const float* __restrict__ w_f,
                                                            float* __restrict__ dx, int64_t rows,
                                                            int dm, int H) {
   constexpr int TB = 128;  // tokens per workgroup
+  __shared__ float zs[16][TB + 1];  // dz of the workgroup's tokens, loaded once by all threads
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hl = lane >> 5, l32 = lane & 31;
   const int64_t t_blk = (int64_t)blockIdx.x * TB;
   const int d0 = blockIdx.y * 128 + 32 * wave;
+  for (int i = threadIdx.x; i < 16 * TB; i += 256) {  // token fastest: coalesced per head
+    const int h = i / TB, tt = i % TB;
+    const int64_t t = t_blk + tt;
+    zs[h][tt] = (h < H && t < rows) ? dz(t, h) : 0.f;
+  }
   auto split3 = [](const float (&v)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -129,14 +151,12 @@ __global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const float* __restri
     }
     split3(v, wa0, wa1, wa2);
   }
+  __syncthreads();
   for (int tb = 0; tb < TB; tb += 32) {
     const int64_t t = t_blk + tb + l32;  // B[k = head 8 hl + e][n = token t]
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int h = 8 * hl + e;
-      v[e] = (t < rows && h < H) ? dz[t * H + h] : 0.f;
-    }
+    for (int e = 0; e < 8; ++e) v[e] = zs[8 * hl + e][tb + l32];
     bf16x8 b0, b1, b2;
     split3(v, b0, b1, b2);
     f32x16 acc = zero16();
@@ -157,19 +177,19 @@ __global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const float* __restri
 
 template <bool kBf16>
 __global__ __launch_bounds__(256) void gate_dw_partial_kernel(const void* __restrict__ x,
-                                                              const float* __restrict__ dz,
+                                                              const DzSrc dz,
                                                               float* __restrict__ part,
                                                               float* __restrict__ part_db,
                                                               int64_t rows, int dm, int H) {
-  __shared__ float dzs[kChunk][kHGroup];
+  __shared__ float dzs[kChunk][kHGroup + 1];
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x, slab = blockIdx.y, h0 = blockIdx.z * kHGroup;
   const int nh = H - h0 < kHGroup ? H - h0 : kHGroup;
   const int64_t r0 = (int64_t)chunk * kChunk;
   const int n = rows - r0 < kChunk ? (int)(rows - r0) : kChunk;
-  for (int i = tid; i < kChunk * kHGroup; i += 256) {
-    const int r = i / kHGroup, h = i % kHGroup;
-    dzs[r][h] = (r < n && h < nh) ? dz[(r0 + r) * H + h0 + h] : 0.f;
+  for (int i = tid; i < kChunk * kHGroup; i += 256) {  // token fastest: coalesced per head
+    const int r = i % kChunk, h = i / kChunk;
+    dzs[r][h] = (r < n && h < nh) ? dz(r0 + r, h0 + h) : 0.f;
   }
   __syncthreads();
   const int d = slab * 256 + tid;
@@ -201,7 +221,7 @@ __global__ __launch_bounds__(256) void gate_dw_partial_kernel(const void* __rest
 // (hi + mid + lo carries all 24 bits of the fp32 value), so every product is exact and only the
 // fp32 accumulation rounds. The partials have gate_dw_partial_kernel's layout.
 __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restrict__ x,
-                                                           const float* __restrict__ dz,
+                                                           const DzSrc dz,
                                                            float* __restrict__ part,
                                                            float* __restrict__ part_db,
                                                            int64_t rows, int dm, int H) {
@@ -210,7 +230,10 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
   constexpr int XV = TS * 16 / 256;  // 16-byte pieces of x per thread and stage
   constexpr int DV = TS * HG / 256;  // dz values per thread and stage
   __shared__ __attribute__((aligned(16))) bf16_t xs[TS * 128];
-  __shared__ float dzs[TS][HG];
+  // dz of the stage, split once into three bf16 parts (hi + mid + lo carries all 24 bits) and
+  // stored in B-operand order: part p, 16-token block ks, half hl, head n -> the 8 bf16 of B's k
+  // slots, so the product loop reads each part with one 16-byte read.
+  __shared__ __attribute__((aligned(16))) bf16_t dzp[3][TS / 16][2][HG][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5;
   const int chunk = blockIdx.x, slab = blockIdx.y, h0 = blockIdx.z * HG;
   const int nh = H - h0 < HG ? H - h0 : HG;
@@ -235,15 +258,20 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
       xv[q] = ok ? v : zero4;
     }
 #pragma unroll
-    for (int q = 0; q < DV; ++q) {
-      const int i = tid + 256 * q, row = i / HG, hh = i % HG;
+    for (int q = 0; q < DV; ++q) {  // token fastest: coalesced per head
+      const int i = tid + 256 * q, row = i % TS, hh = i / TS;
       const int tok = st * TS + row;
-      dv[q] = (tok < n && hh < nh) ? dz[(r0 + tok) * H + h0 + hh] : 0.f;
+      dv[q] = (tok < n && hh < nh) ? dz(r0 + tok, h0 + hh) : 0.f;
     }
   };
 
   f32x16 acc = zero16();
-  float db = 0.f;
+  // db partial: thread tid holds dz of token tid % TS and heads tid / TS + 4 q (q < DV) in every
+  // stage, so each wave sums its lanes' values over the stages and reduces across lanes at the
+  // end (a fixed butterfly order).
+  float dba[DV];
+#pragma unroll
+  for (int q = 0; q < DV; ++q) dba[q] = 0.f;
   load_stage(0);
   for (int st = 0; st < n_st; ++st) {
 #pragma unroll
@@ -253,29 +281,29 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
     }
 #pragma unroll
     for (int q = 0; q < DV; ++q) {
-      const int i = tid + 256 * q;
-      dzs[i / HG][i % HG] = dv[q];
+      const int i = tid + 256 * q, row = i % TS, hh = i / TS;
+      // token row of the stage sits in k slot e of half hb of block ks (the slot order of the
+      // transposed x reads: tokens 16 ks + 4 hb + 0..3 in slots 0..3, 16 ks + 8 + 4 hb + 0..3 in 4..7)
+      const int ks = row >> 4, tin = row & 15, hb = (tin >> 2) & 1, e = (tin & 3) + ((tin >> 3) << 2);
+      const float v = dv[q];
+      const __bf16 p1 = (__bf16)v;
+      const float r1 = v - (float)p1;
+      const __bf16 p2 = (__bf16)r1;
+      dzp[0][ks][hb][hh][e] = __builtin_bit_cast(bf16_t, p1);
+      dzp[1][ks][hb][hh][e] = __builtin_bit_cast(bf16_t, p2);
+      dzp[2][ks][hb][hh][e] = __builtin_bit_cast(bf16_t, (__bf16)(r1 - (float)p2));
+      dba[q] += v;
     }
     __syncthreads();
     if (st + 1 < n_st) load_stage(st + 1);
-    if (slab == 0 && tid < HG) {
-      for (int row = 0; row < TS; ++row) db += dzs[row][tid];
-    }
 #pragma unroll
     for (int ks = 0; ks < TS / 16; ++ks) {
       const uint32_t ro = (uint32_t)ks * 16 * 128 * 2;  // 16-row blocks keep the swizzle key
       const bf16x8 a = lds_tr8(a0 + ro, a1 + ro);
-      bf16x8 bh, bm, bl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {  // the token of B's k slot e matches A's (transposed read)
-        const float v = dzs[16 * ks + (e < 4 ? 4 * hl + e : 8 + 4 * hl + (e - 4))][lane & 31];
-        const __bf16 p1 = (__bf16)v;
-        const float r1 = v - (float)p1;
-        const __bf16 p2 = (__bf16)r1;
-        bh[e] = p1;
-        bm[e] = p2;
-        bl[e] = (__bf16)(r1 - (float)p2);
-      }
+      const int hd = lane & 31;
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&dzp[0][ks][hl][hd][0]);
+      const bf16x8 bm = *reinterpret_cast<const bf16x8*>(&dzp[1][ks][hl][hd][0]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&dzp[2][ks][hl][hd][0]);
       acc = mfma32(a, bh, acc);
       acc = mfma32(a, bm, acc);
       acc = mfma32(a, bl, acc);
@@ -291,26 +319,48 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
           make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
     }
   }
-  if (slab == 0 && tid < nh) part_db[(size_t)chunk * H + h0 + tid] = db;
+  if (slab == 0) {
+    static_assert(TS == 64, "one wave holds one head's tokens of a stage");
+#pragma unroll
+    for (int q = 0; q < DV; ++q) {
+      float v = dba[q];
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      const int hh = wave + 4 * q;  // (tid + 256 q) / TS
+      if (lane == 0 && hh < nh) part_db[(size_t)chunk * H + h0 + hh] = v;
+    }
+  }
 }
 
+// dw_f[h, d] and db_f[h]: the chunk partials summed in a fixed order. A workgroup owns 64
+// consecutive entries of the flattened [H, d_model] array; wave w sums the chunks
+// [w n / 4, (w + 1) n / 4) of every entry (16 loads in flight), and the four wave sums are added
+// in wave order. The last workgroup sums the db_f partials the same way.
 __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __restrict__ part,
                                                              const float* __restrict__ part_db,
                                                              float* __restrict__ dw_f,
                                                              float* __restrict__ db_f, int n_chunk,
                                                              int dm, int H) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n_w = (int64_t)H * dm;
-  if (gid < n_w) {
-    float s = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < n_chunk; ++c) s += part[(size_t)c * n_w + gid];  // 8 loads in flight
-    dw_f[gid] = s;
-  } else if (gid < n_w + H) {
-    const int h = (int)(gid - n_w);
-    float s = 0.f;
-    for (int c = 0; c < n_chunk; ++c) s += part_db[(size_t)c * H + h];
-    if (db_f) db_f[h] = s;
+  const bool db_blk = blockIdx.x == gridDim.x - 1;
+  const int64_t e = db_blk ? lane : (int64_t)blockIdx.x * 64 + lane;
+  const int64_t n_e = db_blk ? H : n_w;
+  const float* src = db_blk ? part_db : part;
+  const int64_t stride = db_blk ? H : n_w;
+  const int c0 = (int)((int64_t)n_chunk * wave / 4), c1 = (int)((int64_t)n_chunk * (wave + 1) / 4);
+  float s = 0.f;
+  if (e < n_e) {
+#pragma unroll 16
+    for (int c = c0; c < c1; ++c) s += src[(size_t)c * stride + e];
+  }
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && e < n_e) {
+    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if (!db_blk) dw_f[e] = t;
+    else if (db_f) db_f[e] = t;
   }
 }
 
@@ -417,16 +467,20 @@ size_t gate_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H
 }
 
 hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const float* b_f,
-                           const float* dout, float* dx, float* dw_f, float* db_f, void* ws,
-                           int64_t B, int64_t L, int64_t d_model, int64_t H, GateKind kind,
-                           hipStream_t s) {
+                           const float* dout, const float* log_f, float* dx, float* dw_f,
+                           float* db_f, void* ws, int64_t B, int64_t L, int64_t d_model, int64_t H,
+                           GateKind kind, hipStream_t s) {
   const int64_t rows = B * L;
   const int n_chunk = (int)((rows + kChunk - 1) / kChunk);
-  float* dz = static_cast<float*>(ws);
-  float* part = dz + granule((size_t)(rows * H));
+  float* dzbuf = static_cast<float*>(ws);
+  float* part = dzbuf + granule((size_t)(rows * H));
   float* part_db = part + granule((size_t)((int64_t)n_chunk * H * d_model));
-  hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dout, dz, B, L, d_model, H, kind, s);
-  if (e != hipSuccess) return e;
+  DzSrc dz{nullptr, dout, log_f, L, (int)H};
+  if (kind != GateKind::kLogSigmoid || log_f == nullptr) {  // recompute z from x
+    hipError_t e = launch_gate_dz(x, x_bf16, w_f, b_f, dout, dzbuf, B, L, d_model, H, kind, s);
+    if (e != hipSuccess) return e;
+    dz.dz = dzbuf;
+  }
   if (H <= 16 && d_model % 128 == 0) {
     hipLaunchKernelGGL(gate_dx_mfma_kernel, dim3((unsigned)((rows + 127) / 128), (unsigned)(d_model / 128)),
                        dim3(256), 0, s, dz, w_f, dx, rows, (int)d_model, (int)H);
@@ -451,8 +505,8 @@ hipError_t launch_gate_bwd(const void* x, bool x_bf16, const float* w_f, const f
   else
     hipLaunchKernelGGL((gate_dw_partial_kernel<false>), pg, dim3(256), 0, s, x, dz, part, part_db,
                        rows, (int)d_model, (int)H);
-  const int64_t red = H * d_model + H;
-  hipLaunchKernelGGL(gate_dw_reduce_kernel, dim3((unsigned)((red + 255) / 256)), dim3(256), 0, s,
+  const int64_t n_w = H * d_model;
+  hipLaunchKernelGGL(gate_dw_reduce_kernel, dim3((unsigned)((n_w + 63) / 64 + 1)), dim3(256), 0, s,
                      part, part_db, dw_f, db_f, n_chunk, (int)d_model, (int)H);
   return hipGetLastError();
 }

@@ -96,18 +96,21 @@ fox_status fox_qk_rmsnorm(const void* x, void* y, fox_dtype dt, int64_t rows, in
 
 /* Backward of the gate (paper-graph-ui summary, "Forget Gate Computation"; Pro block Step 4),
  * for the loss whose gradient with respect to log_f is dlog_f ([B, H, L] fp32):
- *   dz[b, h, t] = dlog_f[b, h, t] * sigmoid(-z[b, h, t])   (z recomputed from x, w_f, b_f)
+ *   dz[b, h, t] = dlog_f[b, h, t] * sigmoid(-z[b, h, t])
  *   dx[b, t, :] = sum_h dz[b, h, t] w_f[h, :]              [B, L, d_model] fp32 output
  *   dw_f[h, :]  = sum_{b,t} dz[b, h, t] x[b, t, :]         [H, d_model] fp32 output
  *   db_f[h]     = sum_{b,t} dz[b, h, t]                    [H] fp32 output
+ * log_f: the forward's output [B, H, L] fp32 (fox_gate_logf of the same x, w_f, b_f), or NULL.
+ * With it, sigmoid(-z) = 1 - f = -expm1(log f) comes from log_f and x is read once (for dw_f);
+ * with NULL, z is recomputed from x, w_f and b_f (a second pass over x).
  * x, w_f, b_f, shapes and limits as for fox_gate_logf. workspace: device memory of at least
  * fox_gate_logf_bwd_workspace_bytes(B, L, d_model, H) bytes, 256-byte aligned, contents ignored.
  * fp32 arithmetic; sums over tokens run in a fixed order (deterministic, no atomics). */
 size_t fox_gate_logf_bwd_workspace_bytes(int64_t B, int64_t L, int64_t d_model, int64_t H);
 fox_status fox_gate_logf_bwd(const void* x, fox_dtype x_dt, const float* w_f, const float* b_f,
-                             const float* dlog_f, float* dx, float* dw_f, float* db_f,
-                             void* workspace, size_t workspace_bytes, int64_t B, int64_t L,
-                             int64_t d_model, int64_t H, void* stream);
+                             const float* dlog_f, const float* log_f, float* dx, float* dw_f,
+                             float* db_f, void* workspace, size_t workspace_bytes, int64_t B,
+                             int64_t L, int64_t d_model, int64_t H, void* stream);
 
 /* Backward of the QK-norm (Pro block Steps 1-2), y = x / sqrt(mean x^2 + eps) * weight:
  *   x  : [rows, D] in dtype dt (the norm's input);  dy : [rows, D] fp32 (gradient of y)

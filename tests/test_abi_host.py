@@ -218,11 +218,12 @@ def test_pro_backward_rejects(lib):
     ws = 256 * 1024  # a 256-aligned stand-in address, never dereferenced
     f = lib.fox_gate_logf_bwd
     # d_model % 8, H > 64, dtype, unaligned workspace, short workspace
-    assert f(P, 1, P, P, P, P, P, P, ws, 1 << 30, 1, 8, 12, 2, None) == 1
-    assert f(P, 1, P, P, P, P, P, P, ws, 1 << 30, 1, 8, 16, 65, None) == 1
-    assert f(P, 2, P, P, P, P, P, P, ws, 1 << 30, 1, 8, 16, 2, None) == 1
-    assert f(P, 1, P, P, P, P, P, P, ws + 16, 1 << 30, 1, 8, 16, 2, None) == 1
-    assert f(P, 1, P, P, P, P, P, P, ws, 16, 1, 8, 16, 2, None) == 1
+    assert f(P, 1, P, P, P, None, P, P, P, ws, 1 << 30, 1, 8, 12, 2, None) == 1
+    assert f(P, 1, P, P, P, None, P, P, P, ws, 1 << 30, 1, 8, 16, 65, None) == 1
+    assert f(P, 2, P, P, P, None, P, P, P, ws, 1 << 30, 1, 8, 16, 2, None) == 1
+    assert f(P, 1, P, P, P, None, P, P, P, ws + 16, 1 << 30, 1, 8, 16, 2, None) == 1
+    assert f(P, 1, P, P, P, None, P, P, P, ws, 16, 1, 8, 16, 2, None) == 1
+    assert f(P, 1, P, P, P, P + 4, P, P, P, ws, 1 << 30, 1, 8, 16, 2, None) == 1  # log_f unaligned
     assert lib.fox_gate_logf_bwd_workspace_bytes(1, 16384, 1536, 12) >= 4 * 16384 * 12
     assert lib.fox_gate_logf_bwd_workspace_bytes(0, 8, 16, 2) == 0
     g = lib.fox_qk_rmsnorm_bwd
@@ -301,7 +302,7 @@ def test_calls_reject_extreme_sizes(lib):
                                    0.1, 1, None) == 1
         assert lib.fox_attn_decode_key_norms(P, 1, P, P, b, h, 64, 128, None) == 1
     assert lib.fox_gate_logf(P, 1, P, P, P, BIG, 64, 128, 4, None) == 1
-    assert lib.fox_gate_logf_bwd(P, 1, P, P, P, P, P, P, P, 1 << 20, BIG, 64, 128, 4, None) == 1
+    assert lib.fox_gate_logf_bwd(P, 1, P, P, P, P, P, P, P, P, 1 << 20, BIG, 64, 128, 4, None) == 1
     assert lib.fox_shift_gate(P, 1, P, P, BIG, 64, 128, 4, None) == 1
     assert lib.fox_shift_gate_bwd(P, 1, P, P, P, P, P, 1 << 20, BIG, 64, 128, 4, None) == 1
     assert lib.fox_qk_rmsnorm(P, P, 1, BIG, 128, e, None, None) == 1

@@ -266,15 +266,18 @@ def _check_tight(name, got, ref, rel=1e-5):
     assert rl <= rel, f"{name}: relative L2 {rl:.3e} > {rel:g} (fp32 arithmetic)"
 
 
-@pytest.mark.parametrize("x_dt", ["bf16", "f32"])
-def test_gate_backward_config4(fox, x_dt):
-    """dx, dw_f, db_f of the gate at config 4's shape (x [1, 16384, 1536], 12 heads)."""
+@pytest.mark.parametrize("x_dt,src", [("bf16", "x"), ("f32", "x"), ("bf16", "log_f"),
+                                      ("f32", "log_f")])
+def test_gate_backward_config4(fox, x_dt, src):
+    """dx, dw_f, db_f of the gate at config 4's shape (x [1, 16384, 1536], 12 heads), with
+    sigmoid(-z) recomputed from x or taken from the forward's log f."""
     case = fi.config_case(4)
     x = case.x if x_dt == "bf16" else case.x.astype(np.float32)
     g = np.random.default_rng(44).standard_normal((case.B, case.H, case.L)).astype(np.float32)
-    say(f"gate backward config4 x={x_dt}")
-    dx, dw, db = fox.fox_gate_logf_bwd(dev(x, x_dt), dev(case.w_f, "f32"), dev(case.b_f, "f32"),
-                                       dev(g, "f32"))
+    say(f"gate backward config4 x={x_dt} dz from {src}")
+    xd, wd, bd = dev(x, x_dt), dev(case.w_f, "f32"), dev(case.b_f, "f32")
+    lf = fox.fox_gate_logf(xd, wd, bd) if src == "log_f" else None
+    dx, dw, db = fox.fox_gate_logf_bwd(xd, wd, bd, dev(g, "f32"), log_f=lf)
     torch.cuda.synchronize()
     rdx, rdw, rdb = oracle.gate_logf_bwd(x, case.w_f, case.b_f, g)
     _check_tight("dx", host(dx), rdx)
@@ -293,12 +296,15 @@ def test_gate_backward_ragged(fox, B, L, dm, H):
     w = (0.1 * rng.standard_normal((H, dm))).astype(np.float32)
     b = rng.uniform(-6, 6, size=H).astype(np.float32)
     g = rng.standard_normal((B, H, L)).astype(np.float32)
-    dx, dw, db = fox.fox_gate_logf_bwd(dev(x, "bf16"), dev(w, "f32"), dev(b, "f32"), dev(g, "f32"))
-    torch.cuda.synchronize()
+    xd, wd, bd = dev(x, "bf16"), dev(w, "f32"), dev(b, "f32")
     rdx, rdw, rdb = oracle.gate_logf_bwd(x, w, b, g)
-    _check_tight("dx", host(dx), rdx)
-    _check_tight("dw_f", host(dw), rdw)
-    _check_tight("db_f", host(db), rdb)
+    for src in ("x", "log_f"):
+        lf = fox.fox_gate_logf(xd, wd, bd) if src == "log_f" else None
+        dx, dw, db = fox.fox_gate_logf_bwd(xd, wd, bd, dev(g, "f32"), log_f=lf)
+        torch.cuda.synchronize()
+        _check_tight(f"dx ({src})", host(dx), rdx)
+        _check_tight(f"dw_f ({src})", host(dw), rdw)
+        _check_tight(f"db_f ({src})", host(db), rdb)
 
 
 @pytest.mark.parametrize("rows,D,dt,weighted", [(1, 64, "bf16", False), (37, 128, "f32", True),
