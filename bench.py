@@ -15,7 +15,9 @@ per-kernel averages and the step time come from the same K steps.
 The roofline object covers the kernel with the longest average duration. Its "traffic" (HBM bytes
 per launch) is read from profiles/hbm_traffic.txt, which holds FETCH_SIZE / WRITE_SIZE counter
 readings scaled by a copy kernel of known size; it is null when the kernel's source has changed
-since the counters were taken (the file records a hash of the sources).
+since the counters were taken (the file records a hash of the sources). "clock_ghz" is the
+shader clock each attention kernel ran at in the committed counter passes
+(profiles/counters_L16384_D128.txt), under the same rule.
 """
 from __future__ import annotations
 
@@ -63,6 +65,36 @@ def source_hash(kernel: str) -> str:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+COUNTER_FILE = os.path.join(ROOT, "profiles", "counters_L16384_D128.txt")
+
+
+def read_profile_value(path: str, kernel: str, key: str):
+    """`key` of section [kernel] in a committed counter summary, or None if the file is absent
+    or was taken from other kernel sources (its source_sha256 differs from the current one)."""
+    if not os.path.exists(path):
+        return None
+    sec, vals = None, {}
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("[") and line.endswith("]"):
+            sec = line[1:-1]
+        elif "=" in line and not line.startswith("#") and sec == kernel:
+            k, v = (s.strip() for s in line.split("=", 1))
+            vals[k] = v
+    if not vals or vals.get("source_sha256") != source_hash(kernel) or key not in vals:
+        return None
+    return float(vals[key])
+
+
+def counter_clock():
+    """Shader clock (GHz) of each attention kernel from the committed counter passes
+    (GRBM_GUI_ACTIVE per XCD over the dispatch's duration), null where stale."""
+    return {"fwd": read_profile_value(COUNTER_FILE, "fwd", "clock_ghz"),
+            "dq": read_profile_value(COUNTER_FILE, "dq", "clock_ghz"),
+            "dkv": read_profile_value(COUNTER_FILE, "dkv", "clock_ghz"),
+            "source": "profiles/counters_L16384_D128.txt"}
 
 
 def read_traffic(kernel: str):
@@ -263,6 +295,7 @@ def main():
         "ms_per_step_median": step_med,
         "fwd_frac_of_peak_median": round(kernel_flops["fwd"] / (kern_med["fwd"] * 1e-3) / 1e12
                                          / PEAK_BF16_TFLOPS, 4),
+        "clock_ghz": counter_clock() if not args.paper_shape else None,
         "host_wall_ms_per_step": round(wall_ms, 4),
     }
     if not args.no_skip:
