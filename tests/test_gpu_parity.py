@@ -1167,3 +1167,123 @@ def test_fwd_ex_pro_pipeline_config4(fox):
     check("O, all rows and heads", host(o), O)
     check("LSE, all rows and heads", host(lse), LSE)
     check("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6))
+
+
+# ------------------------------------------------------------------------------ randomized sweep
+def _sweep_case(i):
+    """Seeded random shape, gate and option mix (case i of the sweep)."""
+    rng = np.random.default_rng(7000 + i)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    L = int(rng.choice([1, 2, 63, 64, 65, 255, 256, 257, 511, 700, 1023, 1500, 2100]))
+    D = int(rng.choice([64, 128]))
+    gate = str(rng.choice(["normal", "per_head", "zero", "strong", "reset", "rising"]))
+    if gate == "strong":
+        case = fi.make_case(B, H, L, D, "bf16", seed=7100 + i, gate="normal", gate_mean=-2.0,
+                            with_do=True)
+    elif gate in ("reset", "rising"):
+        case = fi.make_case(B, H, L, D, "bf16", seed=7100 + i, gate="normal", gate_mean=4.0,
+                            with_do=True)
+        for a in sorted(set(int(x) for x in rng.integers(0, L, size=3))):
+            case.log_f[..., a:a + 5] = -300.0 if gate == "reset" else 12.0
+    else:
+        case = fi.make_case(B, H, L, D, "bf16", seed=7100 + i, gate=gate, with_do=True)
+    opts = dict(o_dtype=str(rng.choice(["f32", "bf16"])), c_dtype=str(rng.choice(["f32", "f64"])),
+                fused_scan=bool(rng.integers(0, 2)), skip=bool(rng.integers(0, 2)))
+    if opts["c_dtype"] == "f64":
+        opts["skip"] = False  # a skip plan is built from fp32 c
+    return case, gate, opts
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_sweep_against_oracle(fox, i):
+    """24 seeded random cases: shapes (ragged L, D, B, H), gates (plain, per-head, open, strong
+    decay, hard resets, rising c), O in bf16 or fp32, c in fp32 or fp64, the scan fused into the
+    forward or separate, and tile skipping; the forward against the oracle, the backward (from
+    an fp32 forward) against the oracle, and skipping bit-identical to the dense path."""
+    case, gate, opts = _sweep_case(i)
+    say(f"sweep {i}: B={case.B} H={case.H} L={case.L} D={case.D} gate={gate} {opts}")
+    s = default_scale(case.D)
+    q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
+    cdt = torch.float64 if opts["c_dtype"] == "f64" else torch.float32
+    odt = torch.float32 if opts["o_dtype"] == "f32" else torch.bfloat16
+    if opts["fused_scan"]:
+        o, lse, c = fox.fox_attn_fwd_logf(q, k, v, dev(case.log_f, "f32"), o_dtype=odt, c_dtype=cdt)
+    else:
+        c = fox.fox_logf_cumsum(dev(case.log_f, "f32"), dtype=cdt)
+        o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=odt)
+    o32, lse32 = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    g = fox.fox_attn_bwd(q, k, v, c, o32, lse32, do)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
+    check(f"O ({opts['o_dtype']})", host(o), O)
+    check("LSE", host(lse), LSE)
+    ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s)[:4]
+    _check_grads([host(t) for t in g], ref, f" sweep {i}")
+    if opts["skip"]:
+        plan = fox.fox_attn_skip_plan(q, k, c)
+        o2, lse2 = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32, skip_plan=plan)
+        g2 = fox.fox_attn_bwd(q, k, v, c, o2, lse2, do, skip_plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o32) and torch.equal(lse2, lse32), "skip forward differs from dense"
+        assert all(torch.equal(a, b) for a, b in zip(g, g2)), "skip backward differs from dense"
+
+
+# ------------------------------------------------------------------------------ streams and graphs
+def test_two_streams_run_concurrently(fox):
+    """The calls keep no shared mutable state: forward and backward of two different problems
+    enqueued on two streams at once give the same bits as the same calls one after another."""
+    cases = [fi.make_case(1, 3, 1500, 128, "bf16", seed=7300 + n, with_do=True) for n in range(2)]
+    ins = [[dev(getattr(cs, n), "bf16") for n in ("q", "k", "v", "do")] +
+           [fox.fox_logf_cumsum(dev(cs.log_f, "f32"))] for cs in cases]
+
+    def run(q, k, v, do, c):
+        o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+        return (o, lse) + tuple(fox.fox_attn_bwd(q, k, v, c, o, lse, do))
+
+    serial = [run(*x) for x in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for x in ins:
+        for t in x:
+            t.record_stream(streams[0]); t.record_stream(streams[1])
+    for rep in range(3):
+        outs = [None, None]
+        torch.cuda.synchronize()
+        for n in range(2):
+            with torch.cuda.stream(streams[n]):
+                outs[n] = run(*ins[n])
+        torch.cuda.synchronize()
+        for n in range(2):
+            assert all(torch.equal(a, b) for a, b in zip(outs[n], serial[n])), (rep, n)
+
+
+def test_graph_capture_replays_match_eager(fox):
+    """Forward and backward captured in a HIP graph (through torch.cuda.graph): every replay,
+    with eager work and synchronisations between replays, gives the eager bits."""
+    case = fi.make_case(1, 2, 900, 128, "bf16", seed=7400, with_do=True)
+    q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
+    lf = dev(case.log_f, "f32")
+
+    def run():
+        c = fox.fox_logf_cumsum(lf)
+        o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+        return (o, lse) + tuple(fox.fox_attn_bwd(q, k, v, c, o, lse, do))
+
+    eager = run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as graph capture expects
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = run()
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager result"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
