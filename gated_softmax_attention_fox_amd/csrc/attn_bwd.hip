@@ -306,6 +306,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       sb[t] = pack_c_half(dp, t);
     }
   };
+  auto grad_h = [&](f32x16& s, f32x16& dp, const f32x4 (&m4)[4], const f32x4 (&d4)[4], int hf,
+                    bf16x8 (&pb)[2], bf16x8 (&sb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * hf + ii;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = fmaf(s[4 * i + e], sl2e, -(kterm + m4[i][e]));
+        const float p = __builtin_amdgcn_exp2f(x);
+        const float ds = p * (dp[4 * i + e] - d4[i][e]);
+        dck -= ds;
+        s[4 * i + e] = p;
+        dp[4 * i + e] = ds;
+      }
+    }
+    pb[hf] = pack_c_half(s, hf);
+    sb[hf] = pack_c_half(dp, hf);
+  };
   auto dvdk = [&](uint32_t ro, const bf16x8 (&pb)[2], const bf16x8 (&sb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -364,9 +382,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     bar_vm<0>();
   };
   // Steady tile t (slot S = t % 4), software-pipelined so that the vector work of one sub-tile runs
-  // under the matrix products of its neighbours: S, dP of sub-tile 2t; then (step A) the gradient
-  // arithmetic of 2t under dV, dK of 2t - 1 (carried from the previous tile in pc, sc) and S, dP
-  // of 2t + 1; then (step B) the gradient arithmetic of 2t + 1 under dV, dK of 2t. The P and dS of
+  // under the matrix products of its neighbours: S, dP of sub-tile 2t under the second half of
+  // the gradient arithmetic of 2t - 1; then (step A) the arithmetic of 2t under dV, dK of 2t - 1
+  // (from pc, sc) and S, dP of 2t + 1; then (step B) the first half of the arithmetic of 2t + 1
+  // under dV, dK of 2t. Each of the three product blocks then carries about 3-4 vector
+  // instructions per product (before, the first carried none and the last 8). The P and dS of
   // 2t + 1 are carried to the next tile. Every tile read here (t - 1 and t) has landed.
   bf16x8 pc[2], sc[2];
 #pragma unroll
@@ -377,39 +397,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       sc[i][e] = (__bf16)0.f;
     }
   }
-  auto steady_tile = [&](int t, auto slot_tag) __attribute__((always_inline)) {
+  // The second half of sub-tile 2t + 1's arithmetic runs under the next tile's first products
+  // (its S and dP, which carry no vector work otherwise); s1c, dp1c and the row terms m4c, d4c
+  // carry it across the barrier (the row-term slot is rewritten by the next conversion).
+  f32x16 s1c, dp1c;
+  f32x4 m4c[4], d4c[4];
+  auto steady_tile = [&](int t, auto slot_tag, auto first_tag) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;  // t % 4
+    constexpr bool kFirst = decltype(first_tag)::value;
     constexpr uint32_t cur = S * TB, prev = ((S + 3) & 3) * TB, half = 32 * D * 2;
     constexpr uint32_t mo0 = (S & 1) * 2 * BQ * 4, mo1 = mo0 + 32 * 4;
     start_copies(t, (S + 2) & 3, (S + 3) & 3);
     convert_rows(t, (S + 1) & 3, (S + 1) & 1);
     if (active) {
-      f32x16 s0, dp0, s1, dp1;
+      f32x16 s0, dp0;
       bf16x8 p0[2], q0[2];
       f32x4 m4[4], d4[4];
       sd(s0, dp0, cur);
-      readahead<8, 16>();
+      if constexpr (kFirst) {
+        readahead<8, 16>();
+      } else {
+        grad_h(s1c, dp1c, m4c, d4c, 1, pc, sc);
+        interleave_bwd<8, 1, 3, 8, 16>();
+      }
       __builtin_amdgcn_sched_barrier(0);
       rows(m4, d4, mo0);
       dvdk(prev + half, pc, sc);
-      sd(s1, dp1, cur + half);
+      sd(s1c, dp1c, cur + half);
       grad(s0, dp0, m4, d4, 0, std::false_type{}, p0, q0);
       interleave_bwd<14, 2, 4, 21, 32>();
       __builtin_amdgcn_sched_barrier(0);
-      rows(m4, d4, mo1);
+      rows(m4c, d4c, mo1);
       dvdk(cur, p0, q0);
-      grad(s1, dp1, m4, d4, 0, std::false_type{}, pc, sc);
-      interleave_bwd<14, 2, 7, 13, 16>();
+      grad_h(s1c, dp1c, m4c, d4c, 0, pc, sc);
+      interleave_bwd<14, 2, 4, 13, 16>();
     }
     bar_vm<NCOPY>();
   };
   int t = 0;
   for (; t < n_t && t < 2; ++t) generic_tile(t, std::true_type{});
-  for (; t + 6 < n_t; t += 4) {  // t % 4 == 2; every copy of the four iterations exists
-    steady_tile(t, std::integral_constant<int, 2>{});
-    steady_tile(t + 1, std::integral_constant<int, 3>{});
-    steady_tile(t + 2, std::integral_constant<int, 0>{});
-    steady_tile(t + 3, std::integral_constant<int, 1>{});
+  const bool ran = t + 6 < n_t;
+  if (ran) {
+    steady_tile(t, std::integral_constant<int, 2>{}, std::true_type{});
+    ++t;
+    for (; t + 6 < n_t; t += 4) {  // t % 4 == 3; every copy of the four iterations exists
+      steady_tile(t, std::integral_constant<int, 3>{}, std::false_type{});
+      steady_tile(t + 1, std::integral_constant<int, 0>{}, std::false_type{});
+      steady_tile(t + 2, std::integral_constant<int, 1>{}, std::false_type{});
+      steady_tile(t + 3, std::integral_constant<int, 2>{}, std::false_type{});
+    }
+    if (active) grad_h(s1c, dp1c, m4c, d4c, 1, pc, sc);  // the carried half
   }
   // the last steady tile's carried sub-tile (zero operands when the loop did not run)
   if (active) dvdk((uint32_t)((t + 3) & 3) * TB + 32 * D * 2, pc, sc);
