@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256) void gate_dx16_kernel(const DzSrc dz,
 // Partial dw_f and db_f of one 256-token chunk, one 256-column slab and up to 16 heads: thread c
 // owns column slab * 256 + c and walks the chunk's tokens (coalesced rows of x).
 // dx on the matrix cores (d_model a multiple of 128, H <= 16): workgroup (token block, slab) owns
-// 128 tokens x 128 columns, each wave 32 columns; the workgroup's dz goes through LDS first. dx^T[32 columns x 32 tokens] is one
+// 128 tokens x 128 columns, each wave 32 columns; the workgroup's dz goes through LDS first,
+// already split into its bf16 parts. dx^T[32 columns x 32 tokens] is one
 // v_mfma_f32_32x32x16_bf16 per operand pair, k = the (zero-padded) 16 heads: A = w_f^T (the
 // wave's columns, loaded once), B = dz^T of 32 tokens. Both are split into three bf16 parts and
 // the six products that reach fp32 accuracy are summed smallest first; the hi x hi product is
@@ -120,15 +121,9 @@ __global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const DzSrc dz,
                                                            float* __restrict__ dx, int64_t rows,
                                                            int dm, int H) {
   constexpr int TB = 128;  // tokens per workgroup
-  __shared__ float zs[16][TB + 1];  // dz of the workgroup's tokens, loaded once by all threads
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hl = lane >> 5, l32 = lane & 31;
   const int64_t t_blk = (int64_t)blockIdx.x * TB;
   const int d0 = blockIdx.y * 128 + 32 * wave;
-  for (int i = threadIdx.x; i < 16 * TB; i += 256) {  // token fastest: coalesced per head
-    const int h = i / TB, tt = i % TB;
-    const int64_t t = t_blk + tt;
-    zs[h][tt] = (h < H && t < rows) ? dz(t, h) : 0.f;
-  }
   auto split3 = [](const float (&v)[8], bf16x8& p0, bf16x8& p1, bf16x8& p2) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -140,6 +135,25 @@ __global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const DzSrc dz,
       p2[e] = (__bf16)(r1 - (float)b);
     }
   };
+  // The workgroup's dz as B operands, split once: thread (token tt, half hb) loads the 8 heads
+  // 8 hb .. 8 hb + 7 of its token (coalesced over tokens) and stores their three bf16 parts in
+  // operand order, so each wave's step reads one 16-byte chunk per part instead of splitting.
+  __shared__ __attribute__((aligned(16))) bf16x8 dzp[3][TB / 32][2][32];
+  {
+    const int tt = threadIdx.x % TB, hb = threadIdx.x / TB;  // 256 threads: 128 tokens x 2 halves
+    const int64_t t = t_blk + tt;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int h = 8 * hb + e;
+      v[e] = (h < H && t < rows) ? dz(t, h) : 0.f;
+    }
+    bf16x8 p0, p1, p2;
+    split3(v, p0, p1, p2);
+    dzp[0][tt >> 5][hb][tt & 31] = p0;
+    dzp[1][tt >> 5][hb][tt & 31] = p1;
+    dzp[2][tt >> 5][hb][tt & 31] = p2;
+  }
   // A[m = column d0 + l32][k = head 8 hl + e]
   bf16x8 wa0, wa1, wa2;
   {
@@ -154,11 +168,8 @@ __global__ __launch_bounds__(256) void gate_dx_mfma_kernel(const DzSrc dz,
   __syncthreads();
   for (int tb = 0; tb < TB; tb += 32) {
     const int64_t t = t_blk + tb + l32;  // B[k = head 8 hl + e][n = token t]
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = zs[8 * hl + e][tb + l32];
-    bf16x8 b0, b1, b2;
-    split3(v, b0, b1, b2);
+    const bf16x8 b0 = dzp[0][tb >> 5][hl][l32], b1 = dzp[1][tb >> 5][hl][l32],
+                 b2 = dzp[2][tb >> 5][hl][l32];
     f32x16 acc = zero16();
     acc = mfma32(wa2, b0, acc);
     acc = mfma32(wa1, b1, acc);
