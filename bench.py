@@ -487,27 +487,42 @@ def decode_step(args, torch, fi, fox, dev):
 
 
 def pro_fused_forward(args, torch, fox, q, k, v, x, w_f, b_f, stream):
-    """The Pro forward's q-norm and output norm + gate done inside the attention forward
-    (fox_attn_fwd_ex: q normalised as it is loaded, y = RMSNorm(O) * sigmoid(g) in the
-    epilogue, O still written for the backward) against the same work as separate passes
-    (q-norm, forward, output norm + gate); both take the same normalised keys and c."""
+    """The Pro forward from the raw key and value candidates, three ways, all with the same
+    shift gates, c and output-gate input, and O still written for the backward:
+    - separate: key shift + RMSNorm and value shift passes, q-norm pass, forward, output norm +
+      gate pass;
+    - fused: the two shift passes, then fox_attn_fwd_ex normalising q as it is loaded and
+      applying the output norm + gate in its epilogue;
+    - fused_prologue: fox_attn_fwd_ex alone, shifting and normalising the key and value tiles as
+      they are loaded as well (no shifted keys or values are written)."""
     B, H, L, D = q.shape
+    dm = x.shape[-1]
     rng = torch.Generator(device=q.device).manual_seed(47)
     g = torch.randn(B, H, L, D, device=q.device, generator=rng).to(torch.bfloat16)
+    ak = fox.fox_shift_gate(x, 0.02 * torch.randn(H, dm, device=q.device, generator=rng))
+    av = fox.fox_shift_gate(x, 0.02 * torch.randn(H, dm, device=q.device, generator=rng))
     c = fox.fox_logf_cumsum(fox.fox_gate_logf(x, w_f, b_f))
-    kn = fox.fox_qk_rmsnorm(k, eps=1e-6)
 
     def separate():
+        kn = fox.fox_kv_shift(k, ak, normalize=True, eps=1e-6)
+        vs = fox.fox_kv_shift(v, av)
         qn = fox.fox_qk_rmsnorm(q, eps=1e-6)
-        o, lse = fox.fox_attn_fwd(qn, kn, v, c, o_dtype=torch.float32)
+        o, lse = fox.fox_attn_fwd(qn, kn, vs, c, o_dtype=torch.float32)
         return o, lse, fox.fox_out_norm_gate(o, g, eps=1e-6)
 
     def fused():
-        return fox.fox_attn_fwd_ex(q, kn, v, c, o_dtype=torch.float32, q_norm_eps=1e-6, gate=g,
+        kn = fox.fox_kv_shift(k, ak, normalize=True, eps=1e-6)
+        vs = fox.fox_kv_shift(v, av)
+        return fox.fox_attn_fwd_ex(q, kn, vs, c, o_dtype=torch.float32, q_norm_eps=1e-6, gate=g,
                                    out_norm_eps=1e-6)
 
+    def fused_prologue():
+        return fox.fox_attn_fwd_ex(q, k, v, c, o_dtype=torch.float32, q_norm_eps=1e-6, gate=g,
+                                   out_norm_eps=1e-6, k_shift_alpha=ak, v_shift_alpha=av,
+                                   k_norm_eps=1e-6)
+
     res = {}
-    for name, fn in (("separate", separate), ("fused", fused)):
+    for name, fn in (("separate", separate), ("fused", fused), ("fused_prologue", fused_prologue)):
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
@@ -520,10 +535,14 @@ def pro_fused_forward(args, torch, fox, q, k, v, x, w_f, b_f, stream):
         res[name + "_ms"] = round(e0.elapsed_time(e1) / args.steps, 4)
     so, sl, sy = separate()
     fo, fl, fy = fused()
+    po, pl, py = fused_prologue()
     torch.cuda.synchronize()
     res["o_max_abs_diff"] = float((so - fo).abs().max())
     res["y_max_abs_diff"] = float((sy.float() - fy.float()).abs().max())
+    res["prologue_bit_identical_to_fused"] = bool(torch.equal(po, fo) and torch.equal(pl, fl)
+                                                  and torch.equal(py, fy))
     res["saved_ms"] = round(res["separate_ms"] - res["fused_ms"], 4)
+    res["prologue_saved_ms"] = round(res["fused_ms"] - res["fused_prologue_ms"], 4)
     return res
 
 

@@ -56,7 +56,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fox.h")
 
 FOX_OK, FOX_E_INVALID, FOX_E_UNSUPPORTED, FOX_E_LAUNCH = 0, 1, 2, 3
 FOX_F32, FOX_BF16 = 0, 1
-FOX_CAUSAL, FOX_C_F64, FOX_QK_RMSNORM = 1, 2, 4
+FOX_CAUSAL, FOX_C_F64, FOX_QK_RMSNORM, FOX_K_RMSNORM = 1, 2, 4, 8
 
 
 class FoxFwdOpts(ctypes.Structure):
@@ -65,7 +65,9 @@ class FoxFwdOpts(ctypes.Structure):
                 ("q_norm_eps", ctypes.c_float), ("q_norm_weight", ctypes.c_void_p),
                 ("gate", ctypes.c_void_p), ("gate_dt", ctypes.c_int),
                 ("out_norm_weight", ctypes.c_void_p), ("out_norm_eps", ctypes.c_float),
-                ("y", ctypes.c_void_p), ("skip_plan", ctypes.c_void_p)]
+                ("y", ctypes.c_void_p), ("skip_plan", ctypes.c_void_p),
+                ("k_shift_alpha", ctypes.c_void_p), ("v_shift_alpha", ctypes.c_void_p),
+                ("k_norm_eps", ctypes.c_float), ("k_norm_weight", ctypes.c_void_p)]
 
 _c_i64, _c_u32, _c_f32, _c_vp, _c_sz = (ctypes.c_int64, ctypes.c_uint32, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
@@ -403,11 +405,16 @@ def fox_attn_fwd_ex(q, k, v, c, o_dtype: torch.dtype | None = torch.float32,
                     scale: float | None = None, want_lse: bool = True,
                     q_norm_eps: float | None = None, q_norm_weight: torch.Tensor | None = None,
                     gate: torch.Tensor | None = None, out_norm_weight: torch.Tensor | None = None,
-                    out_norm_eps: float = 1e-6, skip_plan: torch.Tensor | None = None):
+                    out_norm_eps: float = 1e-6, skip_plan: torch.Tensor | None = None,
+                    k_shift_alpha: torch.Tensor | None = None,
+                    v_shift_alpha: torch.Tensor | None = None,
+                    k_norm_eps: float | None = None, k_norm_weight: torch.Tensor | None = None):
     """(O or None, LSE or None, y or None) of the forward with the Pro block's fusions: QK-norm
-    of q as it is loaded (q_norm_eps not None; k must come normalised), and the output norm and
-    gate y = RMSNorm(O) [* out_norm_weight] * sigmoid(gate) (gate [B, H, L, D] bf16 or fp32, y in
-    its type). o_dtype=None skips O (only with a gate)."""
+    of q as it is loaded (q_norm_eps not None); the token shift of the raw keys and values
+    (k_shift_alpha, v_shift_alpha [B, H, L] fp32) and the key norm (k_norm_eps not None) as their
+    tiles are loaded; and the output norm and gate y = RMSNorm(O) [* out_norm_weight] *
+    sigmoid(gate) (gate [B, H, L, D] bf16 or fp32, y in its type). o_dtype=None skips O (only
+    with a gate)."""
     lib = load_library()
     B, H, L, D = _bhld(q, k, v)
     pq, pk, pv = (_dev(q, "q", (torch.bfloat16,)), _dev(k, "k", (torch.bfloat16,)),
@@ -416,9 +423,17 @@ def fox_attn_fwd_ex(q, k, v, c, o_dtype: torch.dtype | None = torch.float32,
     _shape(c, "c", (B, H, L))
     opts = FoxFwdOpts()
     opts.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    opts.flags = _cflags(c) | (FOX_QK_RMSNORM if q_norm_eps is not None else 0)
+    opts.flags = (_cflags(c) | (FOX_QK_RMSNORM if q_norm_eps is not None else 0)
+                  | (FOX_K_RMSNORM if k_norm_eps is not None else 0))
     opts.q_norm_eps = 0.0 if q_norm_eps is None else float(q_norm_eps)
     opts.q_norm_weight = _wptr(q_norm_weight, D).value
+    opts.k_norm_eps = 0.0 if k_norm_eps is None else float(k_norm_eps)
+    opts.k_norm_weight = _wptr(k_norm_weight, D).value
+    for name, a in (("k_shift_alpha", k_shift_alpha), ("v_shift_alpha", v_shift_alpha)):
+        if a is not None:
+            _dev(a, name, (torch.float32,), 3)
+            _shape(a, name, (B, H, L))
+            setattr(opts, name, a.data_ptr())
     y = None
     if gate is not None:
         _dev(gate, "gate", (torch.bfloat16, torch.float32))

@@ -8,6 +8,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "fox.h"
@@ -74,10 +75,10 @@ fox_status check_bhld(int64_t B, int64_t H, int64_t L, int64_t D) {
 fox_status check_flags(uint32_t flags, const void* skip_plan) {
   if (!(flags & FOX_CAUSAL))
     return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
-  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64 | FOX_QK_RMSNORM))
+  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64 | FOX_QK_RMSNORM | FOX_K_RMSNORM))
     return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
-  if (flags & FOX_QK_RMSNORM)
-    return fail(FOX_E_UNSUPPORTED, "FOX_QK_RMSNORM is taken by fox_attn_fwd_ex only");
+  if (flags & (FOX_QK_RMSNORM | FOX_K_RMSNORM))
+    return fail(FOX_E_UNSUPPORTED, "FOX_QK_RMSNORM and FOX_K_RMSNORM are taken by fox_attn_fwd_ex only");
   if ((flags & FOX_C_F64) && skip_plan)
     return fail(FOX_E_UNSUPPORTED, "a skip plan is built from fp32 c; it is not taken with FOX_C_F64");
   return FOX_OK;
@@ -304,7 +305,9 @@ fox_status fox_attn_fwd_ex(const void* q, const void* k, const void* v, fox_dtyp
   const uint32_t flags = opts->flags;
   const bool qnorm = (flags & FOX_QK_RMSNORM) != 0;
   const bool gated = opts->gate != nullptr;
-  if (!qnorm && !gated)  // nothing fused: the plain forward
+  const bool knorm = (flags & FOX_K_RMSNORM) != 0;
+  const bool staged = knorm || opts->k_shift_alpha || opts->v_shift_alpha;  // K/V via registers
+  if (!qnorm && !gated && !staged)  // nothing fused: the plain forward
     return fox_attn_fwd(q, k, v, in_dt, c, o, o_dt, lse, B, H, L, D, opts->scale, flags,
                         opts->skip_plan, stream);
   FOX_REQUIRE_PTR(q);
@@ -317,26 +320,37 @@ fox_status fox_attn_fwd_ex(const void* q, const void* k, const void* v, fox_dtyp
   fox_status st = check_bhld(B, H, L, D);
   if (st != FOX_OK) return st;
   if (in_dt != FOX_BF16)
-    return fail(FOX_E_UNSUPPORTED, "QK-norm and the output gate serve the bf16 kernels");
+    return fail(FOX_E_UNSUPPORTED, "QK-norm, the token shift and the output gate serve the bf16 kernels");
   FOX_REQUIRE(o_dt == FOX_BF16 || o_dt == FOX_F32, "o_dt must be FOX_BF16 or FOX_F32");
   FOX_REQUIRE(opts->scale > 0.f && opts->scale < 1e30f, "scale must be positive and finite");
   if (!(flags & FOX_CAUSAL))
     return fail(FOX_E_UNSUPPORTED, "only causal attention is defined (pass FOX_CAUSAL)");
-  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64 | FOX_QK_RMSNORM))
+  if (flags & ~uint32_t(FOX_CAUSAL | FOX_C_F64 | FOX_QK_RMSNORM | FOX_K_RMSNORM))
     return fail(FOX_E_UNSUPPORTED, "unknown flag bits 0x%x", flags);
   if ((flags & FOX_C_F64) && opts->skip_plan)
     return fail(FOX_E_UNSUPPORTED, "a skip plan is built from fp32 c; it is not taken with FOX_C_F64");
   if (qnorm && opts->skip_plan)
     return fail(FOX_E_UNSUPPORTED, "a skip plan is built from the normalised q; it is not taken "
                                    "with FOX_QK_RMSNORM");
+  if (staged && opts->skip_plan)
+    return fail(FOX_E_UNSUPPORTED, "a skip plan is built from the keys the attention sees; it is "
+                                   "not taken with the key shift or FOX_K_RMSNORM");
+  if (knorm) FOX_REQUIRE(opts->k_norm_eps >= 0.f, "k_norm_eps must be >= 0");
+  FOX_REQUIRE((reinterpret_cast<uintptr_t>(opts->k_shift_alpha) & 3u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(opts->v_shift_alpha) & 3u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(opts->k_norm_weight) & 3u) == 0,
+              "the shift gates and k_norm_weight must be 4-byte aligned");
   FOX_REQUIRE((reinterpret_cast<uintptr_t>(opts->skip_plan) & 255u) == 0,
               "skip_plan must be 256-byte aligned");
   if (qnorm) FOX_REQUIRE(opts->q_norm_eps >= 0.f, "q_norm_eps must be >= 0");
+  // the caller's struct may hold any int in gate_dt: read its bits, not an enum value
+  static_assert(sizeof(fox_dtype) == sizeof(int), "fox_dtype is an int-sized enum");
+  int gate_dt = 0;
+  std::memcpy(&gate_dt, &opts->gate_dt, sizeof gate_dt);
   if (gated) {
     FOX_REQUIRE(aligned16(opts->gate), "gate must be 16-byte aligned");
     FOX_REQUIRE_PTR(opts->y);
-    FOX_REQUIRE(opts->gate_dt == FOX_BF16 || opts->gate_dt == FOX_F32,
-                "gate_dt must be FOX_BF16 or FOX_F32");
+    FOX_REQUIRE(gate_dt == FOX_BF16 || gate_dt == FOX_F32, "gate_dt must be FOX_BF16 or FOX_F32");
     FOX_REQUIRE(opts->out_norm_eps >= 0.f, "out_norm_eps must be >= 0");
   }
   fox::ProFwdArgs pa;
@@ -344,10 +358,15 @@ fox_status fox_attn_fwd_ex(const void* q, const void* k, const void* v, fox_dtyp
   pa.q_w = opts->q_norm_weight;
   pa.q_eps = opts->q_norm_eps;
   pa.g = opts->gate;
-  pa.g_f32 = opts->gate_dt == FOX_F32;
+  pa.g_f32 = gate_dt == FOX_F32;
   pa.out_w = opts->out_norm_weight;
   pa.out_eps = opts->out_norm_eps;
   pa.y = gated ? opts->y : nullptr;
+  pa.k_alpha = opts->k_shift_alpha;
+  pa.v_alpha = opts->v_shift_alpha;
+  pa.k_norm = knorm;
+  pa.k_w = opts->k_norm_weight;
+  pa.k_eps = opts->k_norm_eps;
   return launched(fox::launch_fwd_bf16(q, k, v, cptr(c, flags), o, o_dt == FOX_F32, lse, B * H, L,
                                        D, opts->scale, fox::skip_args(opts->skip_plan, B * H, L),
                                        (hipStream_t)stream, &pa),

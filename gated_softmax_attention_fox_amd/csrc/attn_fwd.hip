@@ -100,6 +100,12 @@ __device__ __forceinline__ void interleave_step() {
 // registers when it is loaded (Step 1, QK-norm of the queries; the keys come normalised from the
 // key shift). FwdPro::y: the epilogue writes y = RMSNorm(O) [* out_w] * sigmoid(g) (Steps 5 and 7,
 // output norm and output gate) from the fp32 O still in registers; O itself may then be skipped.
+// FwdPro::k_alpha, v_alpha, k_norm (the kPre instantiation; Steps 2-3, token shift, and Step 1 for
+// the keys): K and V arrive as the raw key and value candidates, and every tile goes through
+// registers on its way to LDS, where each row t becomes a_t x_{t-1} + (1 - a_t) x_t (x_{-1} = 0)
+// and, for keys, is RMS-normalised: the arithmetic of the separate shift pass, element for
+// element, so the tiles hold the bits that pass would have written. Every workgroup whose queries
+// see a key tile repeats that work for it.
 struct FwdPro {
   const float* q_w = nullptr;  // QK-norm weight [D] or null (unit)
   float q_eps = 0.f;
@@ -109,11 +115,16 @@ struct FwdPro {
   const float* out_w = nullptr;  // output-norm weight [D] or null (unit)
   float out_eps = 0.f;
   void* y = nullptr;           // [B, H, L, D] in g's type, or null: no output gate
+  const float* k_alpha = nullptr;  // key shift gate [B, H, L] or null (no key shift)
+  const float* v_alpha = nullptr;  // value shift gate [B, H, L] or null (no value shift)
+  int k_norm = 0;                  // RMS-normalise each key row (after its shift)
+  const float* k_w = nullptr;      // its weight [D] or null (unit)
+  float k_eps = 0.f;
 };
 
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-template <int D, typename CT, bool kLogF>
+template <int D, typename CT, bool kLogF, bool kPre>
 __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const CT* __restrict__ C, const float* __restrict__ LF, CT* __restrict__ Cout,
@@ -125,7 +136,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   constexpr int CPR = D / 8;
   constexpr int CPT = TILE / 8 / NT;         // 16-byte chunks per thread per tensor (register path)
   constexpr int BLK = TILE * 2 / 1024 / NW;  // 1 KiB copies per wave per tensor and tile
-  constexpr int NCOPY = 2 * BLK + 1;         // copies a wave starts per iteration (K, V, c)
+  // untracked copies a wave starts per iteration: K, V and c, or only c when K and V go through
+  // registers (kPre)
+  constexpr int NCOPY = kPre ? 1 : 2 * BLK + 1;
   static_assert(CPT >= 1 && BLK >= 1, "tile must split evenly over the waves");
   constexpr uint32_t TB = TILE * 2;  // bytes of one K or V tile
   // bytes of one raw value in the copy ring: c (fp32 or fp64), or log f (fp32) when fused
@@ -162,6 +175,8 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   } else {
     C += (size_t)bh * L;
   }
+  const float* k_alpha = (kPre && pro.k_alpha) ? pro.k_alpha + (size_t)bh * L : nullptr;
+  const float* v_alpha = (kPre && pro.v_alpha) ? pro.v_alpha + (size_t)bh * L : nullptr;
   const CT c_ref = kLogF ? (CT)0 : C[q0];
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
@@ -239,13 +254,51 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
       copy4_to_lds(sbase + R_OFF + slot * BN * CS + wave * 8 * CS, voff, c_rs);
     }
   };
-  // Iteration t's copies: K(t + 3), V(t + 2), c(t + 3) (full tiles only: t >= 1).
-  auto start_copies = [&](int t, int sk, int sv, int sc) __attribute__((always_inline)) {
-    if (t + 3 < n_t) {
-      copy_kv(k_rs, K_OFF, t + 3, sk);
-      copy_c(t + 3, sc);
+  // kPre: tile t of K or V through registers into ring slot `slot`, shifted (A non-null) and,
+  // for keys, normalised (rows past the sequence end are zero, as in the copies).
+  auto stage_tile = [&](const bf16_t* X, const float* A, bool norm, uint32_t region, int t,
+                        int slot) __attribute__((always_inline)) {
+    const int k0 = key_tile(t) * BN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / CPR, cc = idx % CPR, key = k0 + r;
+      float x[8];
+      unpack8(ld16_or_zero<D>(X, key, L, cc * 8), x);
+      if (A) {
+        const bool has_prev = key >= 1 && key < L;  // x_{-1} = 0; rows past the end stay zero
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 pv = *reinterpret_cast<const u32x4*>(X + (size_t)(has_prev ? key - 1 : 0) * D + cc * 8);
+        float p[8];
+        unpack8(has_prev ? pv : z, p);
+        const float a = key < L ? A[key] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = shift_mix(a, p[e], x[e]);
+      }
+      if (norm) {
+        rms_norm8<D>(x, pro.k_w, cc * 8, pro.k_eps);
+        if (key >= L) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+      }
+      lds_store8<D>((bf16_t*)(smem + region + slot * TB), r, cc * 8, pack8(x));
     }
-    if (t + 2 < n_t) copy_kv(v_rs, V_OFF, t + 2, sv);
+  };
+  // Iteration t's copies: K(t + 3), V(t + 2), c(t + 3) (full tiles only: t >= 1). kPre: the
+  // staged tiles first, so that no tracked load follows the untracked copy of c.
+  auto start_copies = [&](int t, int sk, int sv, int sc) __attribute__((always_inline)) {
+    if constexpr (kPre) {
+      if (t + 3 < n_t) stage_tile(K, k_alpha, pro.k_norm != 0, K_OFF, t + 3, sk);
+      if (t + 2 < n_t) stage_tile(V, v_alpha, false, V_OFF, t + 2, sv);
+      if (t + 3 < n_t) copy_c(t + 3, sc);
+    } else {
+      if (t + 3 < n_t) {
+        copy_kv(k_rs, K_OFF, t + 3, sk);
+        copy_c(t + 3, sc);
+      }
+      if (t + 2 < n_t) copy_kv(v_rs, V_OFF, t + 2, sv);
+    }
   };
   // Bias slice of tile t + 1 from its raw c values (wave 0). Fused: from the window's prefix
   // sums for the band, else from the running prefix and a scan of the tile's log f.
@@ -412,12 +465,17 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
   // ---- prologue: tile 0 through registers; copies of K(1), K(2), V(1), c(1), c(2) -------------
   {
     const int k0 = kt_last * BN;
+    if constexpr (kPre) {
+      stage_tile(K, k_alpha, pro.k_norm != 0, K_OFF, 0, 0);
+      stage_tile(V, v_alpha, false, V_OFF, 0, 0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int idx = tid + i * NT;
-      const int key = k0 + idx / CPR, cc = idx % CPR;
-      lds_store8<D>((bf16_t*)(smem + K_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(K, key, L, cc * 8));
-      lds_store8<D>((bf16_t*)(smem + V_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(V, key, L, cc * 8));
+      for (int i = 0; i < CPT; ++i) {
+        const int idx = tid + i * NT;
+        const int key = k0 + idx / CPR, cc = idx % CPR;
+        lds_store8<D>((bf16_t*)(smem + K_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(K, key, L, cc * 8));
+        lds_store8<D>((bf16_t*)(smem + V_OFF), idx / CPR, cc * 8, ld16_or_zero<D>(V, key, L, cc * 8));
+      }
     }
     if (tid < BN) {
       const int key = k0 + tid;
@@ -431,14 +489,24 @@ __global__ __launch_bounds__(512) void fwd_bf16_pipe_kernel(
       }
       ((float*)(smem + C_OFF))[tid] = bias;
     }
-    if (1 < n_t) {
-      copy_kv(k_rs, K_OFF, 1, 1);
-      copy_kv(v_rs, V_OFF, 1, 1);
-      copy_c(1, 1);
-    }
-    if (2 < n_t) {
-      copy_kv(k_rs, K_OFF, 2, 2);
-      copy_c(2, 2);
+    if constexpr (kPre) {
+      if (1 < n_t) {
+        stage_tile(K, k_alpha, pro.k_norm != 0, K_OFF, 1, 1);
+        stage_tile(V, v_alpha, false, V_OFF, 1, 1);
+      }
+      if (2 < n_t) stage_tile(K, k_alpha, pro.k_norm != 0, K_OFF, 2, 2);
+      if (1 < n_t) copy_c(1, 1);
+      if (2 < n_t) copy_c(2, 2);
+    } else {
+      if (1 < n_t) {
+        copy_kv(k_rs, K_OFF, 1, 1);
+        copy_kv(v_rs, V_OFF, 1, 1);
+        copy_c(1, 1);
+      }
+      if (2 < n_t) {
+        copy_kv(k_rs, K_OFF, 2, 2);
+        copy_c(2, 2);
+      }
     }
     bar_vm<0>();
   }
@@ -724,10 +792,16 @@ void go_fwd_bf16(const void* q, const void* k, const void* v, const void* c, voi
                  float* lse, int64_t BH, int64_t L, float scale, const SkipArgs& skip,
                  const FwdPro& pro, hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, false>), dim3((unsigned)(n_qt * BH)), dim3(512),
-                     0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)c,
-                     (const float*)nullptr, (CT*)nullptr, o, lse, skip.q_skip, skip.q_order,
-                     (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32, pro);
+  if (pro.k_alpha || pro.v_alpha || pro.k_norm)
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, false, true>), dim3((unsigned)(n_qt * BH)),
+                       dim3(512), 0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                       (const CT*)c, (const float*)nullptr, (CT*)nullptr, o, lse, skip.q_skip,
+                       skip.q_order, (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32, pro);
+  else
+    hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, false, false>), dim3((unsigned)(n_qt * BH)),
+                       dim3(512), 0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v,
+                       (const CT*)c, (const float*)nullptr, (CT*)nullptr, o, lse, skip.q_skip,
+                       skip.q_order, (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32, pro);
 }
 
 template <int D, typename CT>
@@ -735,7 +809,7 @@ void go_fwd_bf16_logf(const void* q, const void* k, const void* v, const float* 
                       void* o, bool o_f32, float* lse, int64_t BH, int64_t L, float scale,
                       hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, true>), dim3((unsigned)(n_qt * BH)), dim3(512),
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, CT, true, false>), dim3((unsigned)(n_qt * BH)), dim3(512),
                      0, s, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const CT*)nullptr,
                      log_f, (CT*)c_out, o, lse, (const int32_t*)nullptr, (const int32_t*)nullptr,
                      (int)L, (int)BH, n_qt, scale * kLog2e, (int)o_f32, FwdPro());
@@ -764,6 +838,11 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, 
     pro.out_w = pa->out_w;
     pro.out_eps = pa->out_eps;
     pro.y = pa->y;
+    pro.k_alpha = pa->k_alpha;
+    pro.v_alpha = pa->v_alpha;
+    pro.k_norm = pa->k_norm ? 1 : 0;
+    pro.k_w = pa->k_w;
+    pro.k_eps = pa->k_eps;
   }
   if (D == 64) {
     if (c.f64) go_fwd_bf16<64, double>(q, k, v, c.p, o, o_f32, lse, BH, L, scale, skip, pro, s);

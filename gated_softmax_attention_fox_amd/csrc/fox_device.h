@@ -110,6 +110,47 @@ __device__ __forceinline__ void lds_store8(bf16_t* base, int row, int col, const
   *reinterpret_cast<u32x4*>(base + swz<D>(row, col)) = v;
 }
 
+// The Pro block's token shift and key RMSNorm on one 8-element chunk of a row. The separate
+// shift pass and the forward's fused tile loads both use these, so their rows hold the same bits:
+// the shifted row is a prev + (1 - a) cur, and the norm multiplies it by
+// 1 / sqrt(mean of squares + eps) [* w], the sum of squares taken over the D / 8 consecutive
+// lanes that hold the row (a butterfly, which leaves the same sum in every lane of the group).
+__device__ __forceinline__ float shift_mix(float a, float prev, float cur) {
+  return fmaf(a, prev, (1.0f - a) * cur);
+}
+template <int D>
+__device__ __forceinline__ float row_group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < D / 8; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+template <int D>
+__device__ __forceinline__ float rms_scale(float ss_row, float eps) {
+  return rsqrtf(fmaf(ss_row, 1.0f / D, eps));
+}
+template <int D>
+__device__ __forceinline__ void rms_norm8(float (&v)[8], const float* w, int col, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+  const float r = rms_scale<D>(row_group_sum<D>(ss), eps);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] *= r * (w ? w[col + e] : 1.0f);
+}
+__device__ __forceinline__ void unpack8(const u32x4& x, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(x[i] << 16);
+    v[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float (&v)[8]) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  return r;
+}
+
 // acc + sum of the 8 bf16 values of v, with v_dot2_f32_bf16 against packed ones (fp32 sums).
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float rowsum_bf16x8(const bf16x8& v, float acc) {
@@ -218,8 +259,10 @@ __device__ __forceinline__ void pin_agpr(bf16x8& x) { asm volatile("" : "+a"(x))
 // inserts the conservative vmcnt(0) it would place before every LDS read that might alias a
 // tracked copy; the kernel instead waits explicitly with bar_vm<N>(), which lets the N most
 // recently issued copies stay in flight across the barrier (vector memory loads complete in
-// issue order). A kernel using these must issue no compiler-visible vector memory load between
-// a copy and the wait that covers it.
+// issue order). A compiler-visible vector memory load issued after a copy leaves this correct,
+// since the loads still complete in order, but the compiler's wait for that load's data then
+// also waits for the copy; the kernels keep such loads out of their pipelined loops, or issue
+// them before the iteration's copies.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor: `bytes` bytes from `base`, reads at or past the end return zero.

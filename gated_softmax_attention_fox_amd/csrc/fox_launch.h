@@ -92,6 +92,11 @@ struct ProFwdArgs {
   const float* out_w = nullptr;
   float out_eps = 0.f;
   void* y = nullptr;
+  const float* k_alpha = nullptr;  // key shift gate [B, H, L] (k holds the raw candidates)
+  const float* v_alpha = nullptr;  // value shift gate [B, H, L]
+  bool k_norm = false;             // RMS-normalise the (shifted) key rows on load
+  const float* k_w = nullptr;
+  float k_eps = 0.f;
 };
 // Forward, bf16 inputs on MFMA; O in bf16 or fp32 (o may be null when pa->y is set).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, CPtr c, void* o,

@@ -76,15 +76,8 @@ __global__ __launch_bounds__(256) void kv_shift_kernel(const T* __restrict__ x,
   const float a = alpha[row];
   float v[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = a * prev[e] + (1.0f - a) * cur[e];
-  if constexpr (kNorm) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-    const float r = rsqrtf(row_sum<D>(ss) / D + eps);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= r * (w ? w[c + e] : 1.0f);
-  }
+  for (int e = 0; e < 8; ++e) v[e] = shift_mix(a, prev[e], cur[e]);
+  if constexpr (kNorm) rms_norm8<D>(v, w, c, eps);
   store_row8(y + row * D + c, v);
 }
 
@@ -96,7 +89,7 @@ __device__ __forceinline__ void pre_norm_grad(const float (&v)[8], const float (
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-    const float r = rsqrtf(row_sum<D>(ss) / D + eps);
+    const float r = rms_scale<D>(row_sum<D>(ss), eps);
     float gw[8], dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -131,7 +124,7 @@ __global__ __launch_bounds__(256) void kv_shift_bwd_kernel(
   const float a = alpha[row];
   float v[8], g0[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = a * prev[e] + (1.0f - a) * cur[e];
+  for (int e = 0; e < 8; ++e) v[e] = shift_mix(a, prev[e], cur[e]);
   pre_norm_grad<D, kNorm>(v, d0, w, c, eps, g0);
   float out[8], da = 0.f;
 #pragma unroll
@@ -145,7 +138,7 @@ __global__ __launch_bounds__(256) void kv_shift_bwd_kernel(
     load_row8(dy + (row + 1) * D + c, d1);
     const float a1 = alpha[row + 1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v1[e] = a1 * cur[e] + (1.0f - a1) * nxt[e];
+    for (int e = 0; e < 8; ++e) v1[e] = shift_mix(a1, cur[e], nxt[e]);
     pre_norm_grad<D, kNorm>(v1, d1, w, c, eps, g1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = fmaf(a1, g1[e], out[e]);

@@ -65,7 +65,7 @@ typedef enum fox_dtype { FOX_F32 = 0, FOX_BF16 = 1 } fox_dtype;
  * far c has fallen; with fp32 c each value carries a rounding of up to half the fp32 spacing at
  * |c| (2^-9 at |c| ~ 2^14, 2^-7 at |c| ~ 2^17), which hard resets (log f ~ -1e4) reach within a
  * few positions. Not taken together with a skip plan (FOX_E_UNSUPPORTED). */
-enum { FOX_CAUSAL = 1u, FOX_C_F64 = 2u, FOX_QK_RMSNORM = 4u };
+enum { FOX_CAUSAL = 1u, FOX_C_F64 = 2u, FOX_QK_RMSNORM = 4u, FOX_K_RMSNORM = 8u };
 
 /* Cumulative log decay (paper-graph-ui summary, "Hardware-Aware Implementation": c is the
  * cumulative sum of log f, computed once per head before attention and kept in HBM).
@@ -228,18 +228,30 @@ fox_status fox_attn_fwd(const void* q, const void* k, const void* v, fox_dtype i
                         const void* skip_plan, void* stream);
 
 /* The forward with the Pro block's fusions (paper-graph-ui summary, section 3.4, "The Pro Block
- * Architecture": Step 1, QK-norm; Steps 5 and 7, output norm and output gate), through one options
- * struct. Everything else as fox_attn_fwd.
- *   flags: FOX_CAUSAL (required), FOX_C_F64, and FOX_QK_RMSNORM: each query row is normalised
- *          as it is loaded, q / sqrt(mean_d q^2 + q_norm_eps) [* q_norm_weight], in fp32 with one
- *          rounding to bf16, as fox_qk_rmsnorm would; k must come normalised (the Pro block's
- *          key shift normalises it, fox_kv_shift with normalize = 1, or fox_qk_rmsnorm).
+ * Architecture": Step 1, QK-norm; Steps 2-3, the token shift of keys and values; Steps 5 and 7,
+ * output norm and output gate), through one options struct. Everything else as fox_attn_fwd.
+ *   flags: FOX_CAUSAL (required), FOX_C_F64, FOX_QK_RMSNORM and FOX_K_RMSNORM.
+ *          FOX_QK_RMSNORM: each query row is normalised as it is loaded,
+ *          q / sqrt(mean_d q^2 + q_norm_eps) [* q_norm_weight], in fp32 with one rounding to bf16,
+ *          as fox_qk_rmsnorm would. FOX_K_RMSNORM: each key row (after its shift, if any) is
+ *          normalised the same way with k_norm_eps [* k_norm_weight] as its tile is loaded.
+ *   k_shift_alpha, v_shift_alpha: NULL, or the shift gate alpha ([B, H, L] fp32, from
+ *          fox_shift_gate); k (v) then holds the raw candidates, and row t of the keys (values)
+ *          the attention uses is alpha_t x_{t-1} + (1 - alpha_t) x_t, with x_{-1} = 0.
+ *          With FOX_K_RMSNORM and k_shift_alpha, the keys are exactly the rows fox_kv_shift
+ *          (normalize = 1, the same eps and weight) writes, and v_shift_alpha gives the rows of
+ *          fox_kv_shift (normalize = 0): O, lse and y are bit-identical to that pass followed by
+ *          this call without them. Every workgroup whose queries see a key tile repeats the shift
+ *          and norm of that tile (its loads go through registers instead of direct copies), so
+ *          this serves callers that must not write the shifted keys and values; the separate
+ *          pass is faster.
  *   gate:  NULL, or the output gate's pre-activation g ([B, H, L, D], gate_dt FOX_BF16 or
  *          FOX_F32). Then y ([B, H, L, D], gate_dt) = RMSNorm(O) [* out_norm_weight] *
  *          sigmoid(g), RMSNorm over D with out_norm_eps, formed from the fp32 O in registers.
  *   o:     may be NULL when gate is given (inference, O not wanted); lse may be NULL.
- * bf16 inputs only for FOX_QK_RMSNORM or a gate (FOX_E_UNSUPPORTED otherwise); a skip plan is
- * not taken with FOX_QK_RMSNORM (a plan is built from the normalised q). */
+ * bf16 inputs only for any of these (FOX_E_UNSUPPORTED otherwise); a skip plan is not taken with
+ * FOX_QK_RMSNORM, FOX_K_RMSNORM or a shift (a plan is built from the q and k the attention
+ * sees). The shift gates and k_norm_weight must be 4-byte aligned. */
 typedef struct fox_fwd_opts {
   float scale;
   uint32_t flags;
@@ -251,6 +263,10 @@ typedef struct fox_fwd_opts {
   float out_norm_eps;
   void* y;
   const void* skip_plan;
+  const float* k_shift_alpha;
+  const float* v_shift_alpha;
+  float k_norm_eps;
+  const float* k_norm_weight;
 } fox_fwd_opts;
 fox_status fox_attn_fwd_ex(const void* q, const void* k, const void* v, fox_dtype in_dt,
                            const void* c, void* o, fox_dtype o_dt, float* lse, int64_t B,

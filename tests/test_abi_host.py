@@ -72,9 +72,43 @@ def _bwd(lib, ws=P, ws_bytes=1 << 30, in_dt=1, B=1, H=2, L=64, D=128, flags=1, o
     (dict(H=-1), 1), (dict(in_dt=7), 1), (dict(o_dt=3), 1), (dict(in_dt=0, o_dt=1), 1), (dict(scale=0.0), 1),
     (dict(scale=float("nan")), 1), (dict(flags=0), 2), (dict(flags=5), 2), (dict(flags=2), 2),
     (dict(flags=3, plan=P), 2), (dict(plan=P + 16), 1), (dict(in_dt=0, o_dt=0, plan=P), 2),
+    (dict(flags=9), 2),
 ])
 def test_forward_rejects(lib, kw, status):
     assert _fwd(lib, **kw) == status
+    assert lib.fox_last_error().decode() != ""
+
+
+def _fwd_ex(lib, opts=None, in_dt=1, o=P, L=64, D=128, **fields):
+    o_ = fox.FoxFwdOpts()
+    o_.scale, o_.flags = 0.1, fox.FOX_CAUSAL
+    for f, val in fields.items():
+        setattr(o_, f, val)
+    ref = ctypes.byref(o_) if opts is None else opts
+    return lib.fox_attn_fwd_ex(P, P, P, in_dt, P, o, 1, P, 1, 2, L, D, ref, None)
+
+
+@host_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(opts=ctypes.c_void_p(0)), 1),
+    (dict(flags=1 | 16), 2),
+    (dict(flags=1 | 8, k_norm_eps=-1.0), 1),
+    (dict(flags=1 | 8, skip_plan=P), 2),
+    (dict(k_shift_alpha=P, skip_plan=P), 2),
+    (dict(v_shift_alpha=P + 2), 1),
+    (dict(flags=1 | 8, k_norm_weight=P + 1), 1),
+    (dict(k_shift_alpha=P, in_dt=0), 2),
+    (dict(k_shift_alpha=P, o=0), 1),
+    (dict(flags=1 | 4, q_norm_eps=-1.0), 1),
+    (dict(gate=P, y=0), 1),
+    (dict(gate=P, y=P, gate_dt=5), 1),
+    (dict(k_shift_alpha=P, D=96), 1),
+    (dict(k_shift_alpha=P, flags=0), 2),
+])
+def test_forward_ex_rejects(lib, kw, status):
+    """fox_attn_fwd_ex validates its options (the fused q-norm, key norm, token shift and output
+    gate) before any launch."""
+    assert _fwd_ex(lib, **kw) == status
     assert lib.fox_last_error().decode() != ""
 
 

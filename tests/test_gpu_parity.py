@@ -164,17 +164,16 @@ def test_forward_config3_full_length(fox, config3_oracle):
 
 
 @pytest.mark.parametrize("per_wg", [2, 3, 4, 5])
-def test_forward_balanced_schedule(fox, per_wg):
-    """Head counts that give every compute unit the same number of (head, 256-query tile) items,
-    so the forward walks its balanced item lists; L = 300 leaves the second query tile partial
-    (waves past the end idle). Two rows of every item are checked against the oracle."""
+def test_forward_many_heads(fox, per_wg):
+    """Hundreds of heads (per_wg (head, 256-query tile) items per compute unit): the XCD-aware
+    work order with many heads at home on each XCD and left-over heads spread over the levels;
+    L = 300 leaves the second query tile partial (waves past the end idle). Up to five rows of every
+    item's head, in both query tiles, are checked against the oracle."""
     P = torch.cuda.get_device_properties(0).multi_processor_count
-    if P % 2:
-        pytest.skip("balanced lists need an even number of compute units")
     L, D = 300, 128
     H = per_wg * P // 2  # n_qt = 2 query tiles per head
     case = fi.make_case(1, H, L, D, "bf16", seed=40 + per_wg, gate="per_head")
-    say(f"fwd balanced schedule: {per_wg} items per workgroup, H={H}, L={L}")
+    say(f"fwd many heads: {per_wg} items per compute unit, H={H}, L={L}")
     c, o, lse = _run_fwd(fox, case, torch.float32)
     s = default_scale(D)
     cc = oracle.cumsum_logf(case.log_f)
@@ -1164,6 +1163,96 @@ def test_fwd_ex_pro_pipeline_config4(fox):
     kh = oracle.rms_norm(case.k, 1e-6)
     say("  oracle forward (12 heads, L=16384) ...")
     O, LSE = oracle.attn_fwd(qh, kh, case.v, c=cc, scale=default_scale(case.D), block=1024)
+    check("O, all rows and heads", host(o), O)
+    check("LSE, all rows and heads", host(lse), LSE)
+    check("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6))
+
+
+PROLOGUE_CASES = [  # L, D, k shift, v shift, k norm (weighted?), q norm, gate dtype, c dtype
+    (300, 64, True, True, "unit", True, "bf16", "f32"),
+    (1000, 128, True, True, "weighted", False, None, "f32"),
+    (1, 128, True, True, "unit", True, "f32", "f32"),
+    (257, 128, False, False, "unit", False, "f32", "f32"),
+    (700, 64, False, True, None, False, None, "f32"),
+    (1500, 128, True, False, "weighted", True, "bf16", "f64"),
+    (64, 64, True, True, "unit", False, None, "f32"),
+]
+
+
+@pytest.mark.parametrize("L,D,ks,vs,kn,qn,g_dt,c_dt", PROLOGUE_CASES)
+def test_fwd_ex_shift_prologue(fox, L, D, ks, vs, kn, qn, g_dt, c_dt):
+    """The key and value token shift and the key norm fused into the forward's tile loads: O, LSE
+    and y bit-identical to the separate fox_kv_shift passes followed by the forward, and against
+    the oracle (kv_shift, rms_norm, attn_fwd, out_norm_gate in fp64)."""
+    B, H = 1, 3
+    case = fi.make_case(B, H, L, D, "bf16", seed=1500 + L + D, gate="per_head")
+    rng = np.random.default_rng(L * 3 + D)
+    ak = rng.uniform(0.0, 1.0, size=(B, H, L)).astype(np.float32)
+    av = rng.uniform(0.0, 1.0, size=(B, H, L)).astype(np.float32)
+    kw = (1 + 0.2 * rng.standard_normal(D)).astype(np.float32) if kn == "weighted" else None
+    g = rng.standard_normal((B, H, L, D)).astype(np.float32) * 2
+    g = (fi.bf16_round(g) if g_dt == "bf16" else g) if g_dt else None
+    say(f"fwd_ex prologue L={L} D={D} kshift={ks} vshift={vs} knorm={kn} qnorm={qn} g={g_dt} c={c_dt}")
+    q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
+    lf = dev(case.log_f, "f32")
+    c = fox.fox_logf_cumsum(lf, dtype=torch.float64 if c_dt == "f64" else torch.float32)
+    tak, tav = dev(ak, "f32"), dev(av, "f32")
+    tkw = None if kw is None else dev(kw, "f32")
+    common = dict(o_dtype=torch.float32, q_norm_eps=1e-6 if qn else None,
+                  gate=None if g is None else dev(g, g_dt), out_norm_eps=1e-6)
+    o, lse, y = fox.fox_attn_fwd_ex(q, k, v, c, k_shift_alpha=tak if ks else None,
+                                    v_shift_alpha=tav if vs else None,
+                                    k_norm_eps=1e-6 if kn else None, k_norm_weight=tkw, **common)
+    # the separate passes: a shift with alpha = 0 is the identity, so it also gives the plain norm
+    k2 = fox.fox_kv_shift(k, tak if ks else torch.zeros_like(tak), normalize=kn is not None,
+                          eps=1e-6, weight=tkw) if (ks or kn) else k
+    v2 = fox.fox_kv_shift(v, tav) if vs else v
+    o2, lse2, y2 = fox.fox_attn_fwd_ex(q, k2, v2, c, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "fused prologue differs from the passes"
+    if g is not None:
+        assert torch.equal(y, y2), "fused prologue differs from the passes (y)"
+    kk = oracle.kv_shift(case.k, ak) if ks else case.k
+    kk = oracle.rms_norm(kk, 1e-6, kw) if kn else kk
+    vv = oracle.kv_shift(case.v, av) if vs else case.v
+    qq = oracle.rms_norm(case.q, 1e-6) if qn else case.q
+    O, LSE = oracle.attn_fwd(qq, kk, vv, case.log_f, scale=default_scale(D))
+    check("O", host(o), O)
+    check("LSE", host(lse), LSE)
+    if g is not None:
+        check("y", host(y), oracle.out_norm_gate(O, g, 1e-6))
+
+
+def test_fwd_ex_shift_prologue_config4(fox):
+    """Workload 4 with the whole Pro prologue fused: shift gates from x (fox_shift_gate), the raw
+    key and value candidates shifted, keys and queries normalised and the output gate applied
+    inside one forward; bit-identical to the separate passes, and every row of all 12 heads
+    against the oracle."""
+    case = fi.config_case(4)
+    say("pro pipeline config4, shift, norms and output gate fused")
+    rng = np.random.default_rng(405)
+    g = rng.standard_normal(case.q.shape).astype(np.float32)  # fp32 gate: y in fp32
+    wk = (0.02 * rng.standard_normal((case.H, case.x.shape[-1]))).astype(np.float32)
+    wv = (0.02 * rng.standard_normal((case.H, case.x.shape[-1]))).astype(np.float32)
+    x = dev(case.x, "bf16")
+    lf = fox.fox_gate_logf(x, dev(case.w_f, "f32"), dev(case.b_f, "f32"))
+    c = fox.fox_logf_cumsum(lf)
+    ak, av = fox.fox_shift_gate(x, dev(wk, "f32")), fox.fox_shift_gate(x, dev(wv, "f32"))
+    q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
+    common = dict(o_dtype=torch.float32, q_norm_eps=1e-6, gate=dev(g, "f32"))
+    o, lse, y = fox.fox_attn_fwd_ex(q, k, v, c, k_shift_alpha=ak, v_shift_alpha=av,
+                                    k_norm_eps=1e-6, **common)
+    o2, lse2, y2 = fox.fox_attn_fwd_ex(q, fox.fox_kv_shift(k, ak, normalize=True, eps=1e-6),
+                                       fox.fox_kv_shift(v, av), c, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2) and torch.equal(y, y2)
+    cc = oracle.cumsum_logf(oracle.gate_logf(case.x, case.w_f, case.b_f))
+    ak_r, av_r = oracle.shift_gate(case.x, wk), oracle.shift_gate(case.x, wv)
+    qh = oracle.rms_norm(case.q, 1e-6)
+    kh = oracle.rms_norm(oracle.kv_shift(case.k, ak_r), 1e-6)
+    vh = oracle.kv_shift(case.v, av_r)
+    say("  oracle forward (12 heads, L=16384) ...")
+    O, LSE = oracle.attn_fwd(qh, kh, vh, c=cc, scale=default_scale(case.D), block=1024)
     check("O, all rows and heads", host(o), O)
     check("LSE, all rows and heads", host(lse), LSE)
     check("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6))
