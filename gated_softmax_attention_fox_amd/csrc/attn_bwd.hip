@@ -115,8 +115,11 @@ __device__ __forceinline__ void readahead() {
 // dc^k_j -= sum_i dS_ij from the fp32 dS, and dV^T += dO^T P, dK^T += Q^T dS with the transposes
 // read from the row-major tiles. Tiles 0 and 1 hold every wave's diagonal and evaluate the
 // causal mask; from tile 2 on the loop is unrolled over four tiles for compile-time slots.
+// Occupancy: at D = 128 a wave needs about 400 registers, so each SIMD runs one. At D = 64 the
+// kernel fits in 256 (128 VGPRs and 128 AGPRs, no spill) and its LDS in 69 KB, so two
+// workgroups share a compute unit and each SIMD interleaves two waves.
 template <int D, typename CT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dkv_pipe_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1))) void dkv_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const CT* __restrict__ C, const float* __restrict__ LSE,
     const float* __restrict__ Delta, float* __restrict__ dK, float* __restrict__ dV,
@@ -472,9 +475,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // Query-stationary step with the forward kernel's memory pipeline. NB 32-query blocks per wave
 // share every K / V operand read; 8 / NB waves cover 256 queries (NB = 1: 8 waves, two per
-// SIMD, within 256 registers each; NB = 2: 4 waves, one per SIMD, up to 512). Keys are walked in 64-key tiles (two 32-key sub-tiles): the diagonal band (the
-// last four key tiles, where sub-tile j is key block 2 kt_last + 1 - j) from the diagonal
-// backwards, then the older tiles in ascending order. K, V and raw c of tile t sit in LDS
+// SIMD, within 256 registers each; NB = 2: 4 waves, within 256 registers at D = 64, where two
+// workgroups share a compute unit). Keys are walked in 64-key tiles (two 32-key sub-tiles):
+// the diagonal band (the last four key tiles, where sub-tile j is key block
+// 2 kt_last + 1 - j) from the diagonal backwards, then the older tiles in ascending order.
+// K, V and raw c of tile t sit in LDS
 // ring slot t % 4 (the bias slice (c_j - c_ref) log2 e of tile t in slot t % 2); iteration t
 // reads K(t), V(t) and the bias of tile t, starts the untracked copies of K(t + 2), V(t + 2)
 // and c(t + 3), converts c(t + 1) into the bias of tile t + 1, and its barrier waits only for
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Tiles 0..3 hold every wave's diagonal and evaluate the causal mask; from tile 4 on the loop
 // is unrolled over four tiles so that every LDS address is a per-lane base plus an immediate.
 template <int D, int NB, typename CT>
-__global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB))) void dq_pipe_kernel(
+__global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 3 - NB, D == 64 ? 2 : 3 - NB))) void dq_pipe_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const CT* __restrict__ C, const float* __restrict__ LSE,
     const float* Delta, const float* __restrict__ O, float* __restrict__ dQ,
@@ -1020,9 +1025,13 @@ void go_dq(const bf16_t* q, const bf16_t* k, const bf16_t* v, const void* c, con
            const SkipArgs& skip,
            hipStream_t s) {
   const int n_qt = (int)((L + 255) / 256);
-  // one 32-query block per wave, 8 waves (two per SIMD): measured 18% faster than 4 waves with
-  // two blocks each, whose halved LDS traffic does not make up for the lost latency hiding
-  hipLaunchKernelGGL((dq_pipe_kernel<D, 1, CT>), dim3((unsigned)(n_qt * BH)), dim3(512), 0, s, q, k,
+  // D = 128: one 32-query block per wave, 8 waves (two per SIMD): measured 18% faster than 4
+  // waves with two blocks each, whose halved LDS traffic does not make up for the lost latency
+  // hiding. D = 64: two blocks per wave, 4 waves in 253 registers and 67 KB of LDS, so two
+  // workgroups share a compute unit and each SIMD still runs two waves, each K and V operand
+  // read now feeding two products (6% faster than one block per wave).
+  constexpr int NB = D == 64 ? 2 : 1;
+  hipLaunchKernelGGL((dq_pipe_kernel<D, NB, CT>), dim3((unsigned)(n_qt * BH)), dim3(512 / NB), 0, s, q, k,
                      v, dO, (const CT*)c, lse, delta, o, dq, dcq, delta_out, lse_out, skip.q_skip,
                      skip.q_order, (int)L, (int)BH, n_qt, scale * kLog2e, scale);
 }
