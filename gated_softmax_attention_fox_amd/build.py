@@ -3,7 +3,8 @@
     python -m gated_softmax_attention_fox_amd.build
 
 Compiles every csrc/*.hip and csrc/*.cpp into _build/ and links
-gated_softmax_attention_fox_amd/libfox.so. Always recompiles.
+gated_softmax_attention_fox_amd/libfox.so, then the plain-C test driver tests/c_abi/fox_c_smoke
+against it. Always recompiles.
 
     python -m gated_softmax_attention_fox_amd.build --sanitized
 
@@ -68,9 +69,25 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp])
     os.replace(tmp, LIB)
+    build_c_smoke(hipcc)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", C_SMOKE)
     return LIB
+
+
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c_abi", "fox_c_smoke.c")
+C_SMOKE = os.path.join(ROOT, "tests", "c_abi", "fox_c_smoke")
+
+
+def build_c_smoke(hipcc: str) -> str:
+    """The plain-C driver of the attention path (a GPU test runs it): gcc, C11, linked against
+    libfox.so (found next to the package through its run path) and the HIP runtime."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{rocm}/include", f"-I{INCLUDE}", C_SMOKE_SRC, "-o", C_SMOKE, f"-L{PKG}", "-lfox",
+          f"-L{rocm}/lib", "-lamdhip64", "-lm",
+          "-Wl,-rpath,$ORIGIN/../../gated_softmax_attention_fox_amd", f"-Wl,-rpath,{rocm}/lib"])
+    return C_SMOKE
 
 
 SAN_LIB = os.path.join(BUILD, "libfox_san.so")
