@@ -345,6 +345,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     }
   };
   auto sub_tile = [&](uint32_t ro, uint32_t mo, int q0s, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
     f32x16 s, dp;
     bf16x8 pb[2], sb[2];
     f32x4 m4[4], d4[4];
@@ -354,6 +355,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     __builtin_amdgcn_sched_barrier(0);
     grad(s, dp, m4, d4, q0s, mask_tag, pb, sb);
     dvdk(ro, pb, sb);
+    if constexpr (kMask) {
+      // The diagonal tiles hold the queries that give a key its largest weights whenever a few
+      // keys dominate their rows, and there P and dS are large: their bf16 rounding alone can
+      // move dV and dK by ~2^-9 of their size. These products therefore also take the rounding
+      // remainders P - bf16(P) and dS - bf16(dS), so they see both to ~2^-17.
+      bf16x8 pl[2], sl[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pl[t][e] = (__bf16)(s[8 * t + e] - (float)pb[t][e]);
+          sl[t][e] = (__bf16)(dp[8 * t + e] - (float)sb[t][e]);
+        }
+      }
+      dvdk(ro, pl, sl);
+    }
   };
 
   // prologue: copies of Q(0), dO(0), Q(1), dO(1) and the raw rows of tiles 0..2; convert tile 0
@@ -705,13 +722,28 @@ __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(D == 6
       sb[b][0] = pack_c_half(s[b], 0);
       sb[b][1] = pack_c_half(s[b], 1);
     }
+    // The diagonal band (the masked sub-tiles) holds the keys that carry a row's largest weights
+    // whenever a few keys dominate it (early rows, strong decay), and there dS is large: its
+    // bf16 rounding alone can move dQ by ~2^-9 |dQ|. The band's products therefore also take the
+    // rounding remainder dS - bf16(dS), so they see dS to ~2^-17.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      bf16x8 sl[NB];
+      if constexpr (kMask) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sl[b][e] = (__bf16)(s[b][8 * t + e] - (float)sb[b][t][e]);
+        }
+      }
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) {
         const bf16x8 a = lds_tr8(kt[d][0] + ro + t * 16 * D * 2, kt[d][1] + ro + t * 16 * D * 2);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) dqacc[b][d] = mfma32(a, sb[b][t], dqacc[b][d]);
+        for (int b = 0; b < NB; ++b) {
+          dqacc[b][d] = mfma32(a, sb[b][t], dqacc[b][d]);
+          if constexpr (kMask) dqacc[b][d] = mfma32(a, sl[b], dqacc[b][d]);
+        }
       }
     }
   };
