@@ -1301,6 +1301,19 @@ def test_random_sweep_against_oracle(fox, i):
     decay, hard resets, rising c), O in bf16 or fp32, c in fp32 or fp64, the scan fused into the
     forward or separate, and tile skipping; the forward against the oracle, the backward (from
     an fp32 forward) against the oracle, and skipping bit-identical to the dense path."""
+    _run_sweep_case(fox, i)
+
+
+@pytest.mark.parametrize("i", [79, 337, 372, 1953])
+def test_sweep_cases_from_wider_search(fox, i):
+    """Seeds of the same generator that a 3600-case search flagged: 1953 (gates in (0, 1), a row
+    dominated by two keys, |dQ| = 5.7, where the bf16 rounding of dS alone moved dQ by 1.6e-2
+    before the diagonal tiles took the remainder products), and three with rising c (large dK,
+    dV; one-hot rows at L = 2; a vanishing d log f)."""
+    _run_sweep_case(fox, i)
+
+
+def _run_sweep_case(fox, i):
     case, gate, opts = _sweep_case(i)
     say(f"sweep {i}: B={case.B} H={case.H} L={case.L} D={case.D} gate={gate} {opts}")
     s = default_scale(case.D)
