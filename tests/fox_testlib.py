@@ -70,3 +70,28 @@ def sample_rows(L, n, seed, tile=64):
 
 def default_scale(D):
     return 1.0 / math.sqrt(D)
+
+
+def check_y(name, got, Y, O, g, eps, weight=None, y_bf16=False):
+    """Check the fused output gate y = RMSNorm(O) [* w] * sigmoid(g) against the oracle's Y, where
+    O is the oracle's attention output. An error e in O reaches y as r (1 + r |O_j|) |w_j|
+    sigmoid(g_j) e per element (r = 1 / sqrt(mean O^2 + eps) of the row: the element's own term
+    and the change of the row's RMS), so the max-abs bar is the attention bar carried through
+    that factor, element by element, plus half a bf16 ulp of y when y is stored in bf16. Relative
+    L2 keeps the attention bar."""
+    got = np.asarray(got, np.float64)
+    Y = np.asarray(Y, np.float64)
+    O = np.asarray(O, np.float64)
+    g = np.asarray(g, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    r = 1.0 / np.sqrt(np.mean(O * O, axis=-1, keepdims=True) + eps)
+    w = np.ones(O.shape[-1]) if weight is None else np.abs(np.asarray(weight, np.float64))
+    bound = BF16_MAXABS * r * (1.0 + r * np.abs(O)) * w / (1.0 + np.exp(-g))
+    if y_bf16:
+        bound = bound + 2.0 ** -9 * np.abs(Y)
+    d = np.abs(got - Y)
+    worst = float(np.max(d / bound))
+    m, rel = errors(got, Y)
+    say(f"  {name}: max-abs {m:.3e}, at most {worst:.2f} of the carried bar  rel-L2 {rel:.3e} (<= {BF16_RELL2:g})")
+    assert worst <= 1.0, f"{name}: error {worst:.2f} times the bar carried from O"
+    assert rel <= BF16_RELL2, f"{name}: rel-L2 {rel:.3e} > {BF16_RELL2:g}"

@@ -14,8 +14,8 @@ import torch
 import fox_inputs as fi
 import oracle
 from oracle import fox_oracle
-from tests.fox_testlib import (BF16_MAXABS, BF16_RELL2, F32_MAXABS, check, default_scale, dev,
-                               host, sample_rows, say)
+from tests.fox_testlib import (BF16_MAXABS, BF16_RELL2, F32_MAXABS, check, check_y,
+                               default_scale, dev, host, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -1142,7 +1142,7 @@ def test_fwd_ex_qnorm_and_output_gate(fox, L, D, g_dt, weighted):
     Y = oracle.out_norm_gate(O, g, 1e-6, ow)
     check("O", host(o), O)
     check("LSE", host(lse), LSE)
-    check("y", host(y), Y)
+    check_y("y", host(y), Y, O, g, 1e-6, ow, y_bf16=g_dt == "bf16")
 
 
 def test_fwd_ex_pro_pipeline_config4(fox):
@@ -1165,7 +1165,8 @@ def test_fwd_ex_pro_pipeline_config4(fox):
     O, LSE = oracle.attn_fwd(qh, kh, case.v, c=cc, scale=default_scale(case.D), block=1024)
     check("O, all rows and heads", host(o), O)
     check("LSE, all rows and heads", host(lse), LSE)
-    check("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6))
+    check_y("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6), O, g, 1e-6,
+            y_bf16=True)
 
 
 PROLOGUE_CASES = [  # L, D, k shift, v shift, k norm (weighted?), q norm, gate dtype, c dtype
@@ -1220,7 +1221,7 @@ def test_fwd_ex_shift_prologue(fox, L, D, ks, vs, kn, qn, g_dt, c_dt):
     check("O", host(o), O)
     check("LSE", host(lse), LSE)
     if g is not None:
-        check("y", host(y), oracle.out_norm_gate(O, g, 1e-6))
+        check_y("y", host(y), oracle.out_norm_gate(O, g, 1e-6), O, g, 1e-6, y_bf16=g_dt == "bf16")
 
 
 def test_fwd_ex_shift_prologue_config4(fox):
@@ -1231,7 +1232,7 @@ def test_fwd_ex_shift_prologue_config4(fox):
     case = fi.config_case(4)
     say("pro pipeline config4, shift, norms and output gate fused")
     rng = np.random.default_rng(405)
-    g = rng.standard_normal(case.q.shape).astype(np.float32)  # fp32 gate: y in fp32
+    g = fi.bf16_round(rng.standard_normal(case.q.shape).astype(np.float32))
     wk = (0.02 * rng.standard_normal((case.H, case.x.shape[-1]))).astype(np.float32)
     wv = (0.02 * rng.standard_normal((case.H, case.x.shape[-1]))).astype(np.float32)
     x = dev(case.x, "bf16")
@@ -1239,7 +1240,7 @@ def test_fwd_ex_shift_prologue_config4(fox):
     c = fox.fox_logf_cumsum(lf)
     ak, av = fox.fox_shift_gate(x, dev(wk, "f32")), fox.fox_shift_gate(x, dev(wv, "f32"))
     q, k, v = dev(case.q, "bf16"), dev(case.k, "bf16"), dev(case.v, "bf16")
-    common = dict(o_dtype=torch.float32, q_norm_eps=1e-6, gate=dev(g, "f32"))
+    common = dict(o_dtype=torch.bfloat16, q_norm_eps=1e-6, gate=dev(g, "bf16"))
     o, lse, y = fox.fox_attn_fwd_ex(q, k, v, c, k_shift_alpha=ak, v_shift_alpha=av,
                                     k_norm_eps=1e-6, **common)
     o2, lse2, y2 = fox.fox_attn_fwd_ex(q, fox.fox_kv_shift(k, ak, normalize=True, eps=1e-6),
@@ -1255,7 +1256,8 @@ def test_fwd_ex_shift_prologue_config4(fox):
     O, LSE = oracle.attn_fwd(qh, kh, vh, c=cc, scale=default_scale(case.D), block=1024)
     check("O, all rows and heads", host(o), O)
     check("LSE, all rows and heads", host(lse), LSE)
-    check("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6))
+    check_y("y, all rows and heads", host(y), oracle.out_norm_gate(O, g, 1e-6), O, g, 1e-6,
+            y_bf16=True)
 
 
 # ------------------------------------------------------------------------------ randomized sweep
