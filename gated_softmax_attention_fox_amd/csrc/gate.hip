@@ -133,9 +133,11 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
 // v_mfma_f32_16x16x32_bf16. A workgroup of 8 waves takes NTT tiles of 16 tokens (blockIdx.y picks
 // the group of 16 heads). Wave w takes the 32-column steps d0 = 32 (w + 8 s); lane l supplies
 // A = x[token l % 16][d0 + 8 (l / 16) .. +7] straight from HBM and B = w_f[head l % 16][same
-// columns]. w_f is split into bf16 hi and lo parts (hi = bf16(w), lo = bf16(w - hi)) and both are
-// multiplied, so z keeps about 16 significant bits of w on top of exact products and fp32
-// accumulation; lane l receives z for head l % 16 and tokens 4 (l / 16) .. +3. Needs
+// columns]. w_f is split into three bf16 parts (hi = bf16(w), mid = bf16(w - hi),
+// lo = bf16(w - hi - mid)) that together hold all 24 bits of its significand, and all three are
+// multiplied: the products are exact, so z carries only the fp32 accumulation's rounding (two
+// parts, 16 bits of w, leave z off by up to 2^-17 of sum |x w|: 4e-5 in log f at d_model 1536
+// and |w| ~ 0.1). Lane l receives z for head l % 16 and tokens 4 (l / 16) .. +3. Needs
 // d_model % 32 == 0.
 // Measured on the Pro shape (x [16384, 1536]), the costs beyond the bare x stream were the w_f
 // reads (each workgroup reads all of w_f for its heads: with 64 tokens per workgroup that stream
@@ -197,17 +199,21 @@ __global__ __launch_bounds__(512) void gate_mfma_kernel(const bf16_t* __restrict
       if (s0 + j >= n_steps) break;
       const float wv[8] = {wa[j][0].x, wa[j][0].y, wa[j][0].z, wa[j][0].w,
                            wa[j][1].x, wa[j][1].y, wa[j][1].z, wa[j][1].w};
-      bf16x8 bh, bl;
+      bf16x8 bh, bm, bl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const __bf16 hi = (__bf16)wv[e];
+        const float r1 = wv[e] - (float)hi;
+        const __bf16 mid = (__bf16)r1;
         bh[e] = hi;
-        bl[e] = (__bf16)(wv[e] - (float)hi);
+        bm[e] = mid;
+        bl[e] = (__bf16)(r1 - (float)mid);
       }
 #pragma unroll
       for (int u = 0; u < NTT; ++u) {  // one load and split of w_f serves all the tiles
         const bf16x8 a = __builtin_bit_cast(bf16x8, tok_ok[u] ? xa[j][u] : zero4);
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm, acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc[u], 0, 0, 0);
       }
     }
