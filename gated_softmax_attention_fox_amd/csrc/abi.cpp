@@ -95,7 +95,7 @@ fox::CPtr cptr(const void* c, uint32_t flags) {
 
 extern "C" {
 
-const char* fox_version(void) { return "0.1.0"; }
+const char* fox_version(void) { return "0.2.0"; }
 
 const char* fox_status_str(fox_status s) {
   switch (s) {

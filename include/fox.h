@@ -426,7 +426,9 @@ const char* fox_status_str(fox_status s);
 /* Thread-local detail of the last non-OK status returned on this thread ("" if none). */
 const char* fox_last_error(void);
 
-/* Library version, e.g. "0.1.0". */
+/* Library version, "major.minor.patch". The minor number rises when a struct of this header
+ * changes layout (0.2.0: fox_fwd_opts gained the key and value shift and the key norm fields at
+ * its end), so a caller built against another layout can check it before passing one. */
 const char* fox_version(void);
 
 #ifdef __cplusplus
