@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="single-token decode against a full KV cache instead: B=8 sequences of "
                          "12 heads, 16384 cached positions, D=128 (a separate, HBM-bound line)")
+    ap.add_argument("--lengths", action="store_true",
+                    help="forward and backward at other batch and sequence shapes instead (one "
+                         "JSON line per shape; a separate measurement, not the headline line)")
     ap.add_argument("--no-skip", action="store_true",
                     help="leave out the second measurement with exact tile skipping")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -190,6 +193,8 @@ def main():
         return pro_step(args, torch, fi, fox, dev)
     if args.decode:
         return decode_step(args, torch, fi, fox, dev)
+    if args.lengths:
+        return length_sweep(args, torch, fi, fox, dev)
     if args.paper_shape:
         case = fi.make_case(1, 24, 16384, 64, "bf16", seed=6, gate="per_head", with_do=True,
                             name="paper_shape")
@@ -405,6 +410,54 @@ def copy_calibration(args, torch, dev, out):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = n
+
+
+# (B, H, L, D): the bench workload, shorter sequences at the same or larger batch, and the
+# paper's head shape
+LENGTH_SHAPES = [(1, 12, 16384, 128), (2, 12, 8192, 128), (1, 12, 4096, 128), (4, 12, 2048, 128),
+                 (1, 48, 2048, 128), (8, 12, 1024, 128), (1, 24, 16384, 64)]
+
+
+def length_sweep(args, torch, fi, fox, dev):
+    """fox_attn_fwd (fp32 O) and fox_attn_bwd at each of LENGTH_SHAPES, timed separately over
+    args.steps calls each with HIP events on the library's stream, inputs resident in HBM. One
+    JSON line per shape; the forward's fraction of the bf16 peak uses its causal FLOPs."""
+    stream = torch.cuda.current_stream()
+    for B, H, L, D in LENGTH_SHAPES:
+        case = fi.make_case(B, H, L, D, "bf16", seed=1, gate="per_head", with_do=True)
+        up = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+        q, k, v, do = (up(getattr(case, n), torch.bfloat16) for n in ("q", "k", "v", "do"))
+        c = fox.fox_logf_cumsum(up(case.log_f, torch.float32))
+        ws = torch.empty(fox.fox_attn_bwd_workspace_bytes(B, H, L, D), dtype=torch.uint8,
+                         device=dev)
+        o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+        for _ in range(args.warmup):
+            fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+            fox.fox_attn_bwd(q, k, v, c, o, lse, do, workspace=ws)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+        ev[1].record(stream)
+        for _ in range(args.steps):
+            fox.fox_attn_bwd(q, k, v, c, o, lse, do, workspace=ws)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_f = ev[0].elapsed_time(ev[1]) / args.steps
+        t_b = ev[1].elapsed_time(ev[2]) / args.steps
+        one = contraction_flops(B, H, L, D)
+        print(json.dumps({
+            "shape": {"B": B, "H": H, "L": L, "D": D},
+            "fwd_ms": round(t_f, 4),
+            "fwd_tflops": round(2 * one / (t_f * 1e-3) / 1e12, 1),
+            "fwd_frac_of_peak": round(2 * one / (t_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_ms": round(t_b, 4),
+            "bwd_tflops_credited": round(5 * one / (t_b * 1e-3) / 1e12, 1),
+            "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+        }), flush=True)
+        del q, k, v, do, c, ws, o, lse
+        torch.cuda.empty_cache()
 
 
 def decode_step(args, torch, fi, fox, dev):
