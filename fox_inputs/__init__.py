@@ -18,8 +18,8 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "bf16_bits", "bf16_round", "bits_to_f32", "FoxCase", "make_case", "CONFIGS",
-    "config_case", "logsigmoid_input",
+    "bf16_bits", "bf16_round", "bits_to_f32", "FoxCase", "make_case", "make_periodic_case",
+    "repeat_rows", "CONFIGS", "config_case", "logsigmoid_input",
 ]
 
 
@@ -89,6 +89,23 @@ def _qkv(rng: np.random.Generator, shape, dtype: str):
     return out
 
 
+def _draw_log_f(rng: np.random.Generator, B: int, H: int, L: int, gate: str, gate_mean: float,
+                gate_std: float, head_mean_range: tuple[float, float]) -> np.ndarray:
+    """log f [B, H, L] fp32 by the named gate recipe (see make_case)."""
+    if gate == "normal":
+        z = rng.normal(gate_mean, gate_std, size=(B, H, L))
+        return logsigmoid_input(z)
+    if gate == "per_head":
+        mu = rng.uniform(head_mean_range[0], head_mean_range[1], size=(H,))
+        z = mu[None, :, None] + rng.standard_normal((B, H, L))
+        return logsigmoid_input(z)
+    if gate == "zero":
+        return np.zeros((B, H, L), np.float32)
+    if gate == "quarter_steps":
+        return np.where(rng.random((B, H, L)) < 0.5, -0.25, 0.0).astype(np.float32)
+    raise ValueError(gate)
+
+
 def make_case(B: int, H: int, L: int, D: int, dtype: str = "bf16", *, seed: int = 0,
               gate: str = "normal", gate_mean: float = 3.0, gate_std: float = 1.5,
               head_mean_range: tuple[float, float] = (1.0, 6.0), with_do: bool = False,
@@ -98,27 +115,44 @@ def make_case(B: int, H: int, L: int, D: int, dtype: str = "bf16", *, seed: int 
     gate = "normal": z ~ N(gate_mean, gate_std^2) per (b, h, t).
     gate = "per_head": mu_h ~ U[head_mean_range] per head, z ~ N(mu_h, 1) per (b, h, t).
     gate = "zero": log f = 0 (f = 1, plain causal attention).
+    gate = "quarter_steps": log f = -1/4 or 0 with equal odds per (b, h, t); every prefix sum is
+        a multiple of 1/4 below 2^21 in size up to L = 2^23, so fp32 holds c exactly.
     """
     assert dtype in ("bf16", "f32")
     rng = np.random.default_rng(seed)
     q, k, v = _qkv(rng, (B, H, L, D), dtype)
-    if gate == "normal":
-        z = rng.normal(gate_mean, gate_std, size=(B, H, L))
-        log_f = logsigmoid_input(z)
-    elif gate == "per_head":
-        mu = rng.uniform(head_mean_range[0], head_mean_range[1], size=(H,))
-        z = mu[None, :, None] + rng.standard_normal((B, H, L))
-        log_f = logsigmoid_input(z)
-    elif gate == "zero":
-        log_f = np.zeros((B, H, L), np.float32)
-    else:
-        raise ValueError(gate)
+    log_f = _draw_log_f(rng, B, H, L, gate, gate_mean, gate_std, head_mean_range)
     do = None
     if with_do:
         r2 = np.random.default_rng(seed + 1000)
         do = r2.standard_normal((B, H, L, D), dtype=np.float32)
         do = bf16_round(do) if dtype == "bf16" else do
     return FoxCase(name, B, H, L, D, dtype, q, k, v, log_f=log_f, do=do, seed=seed)
+
+
+def repeat_rows(a: np.ndarray, L: int) -> np.ndarray:
+    """a [..., P, D] repeated along its row axis and cut to [..., L, D] (row r is row r mod P)."""
+    P = a.shape[-2]
+    reps = -(-L // P)
+    return np.concatenate([a] * reps, axis=-2)[..., :L, :] if reps > 1 else a[..., :L, :].copy()
+
+
+def make_periodic_case(B: int, H: int, L: int, D: int, *, period: int, seed: int = 0,
+                       gate: str = "normal", with_do: bool = False,
+                       name: str = "periodic") -> tuple[FoxCase, FoxCase]:
+    """A long bf16 case whose q, k, v (and dO) rows repeat with the given period, for lengths at
+    which drawing every value would take minutes: the rows of make_case(B, H, period, D) repeated
+    along the sequence (row r is row r mod period), and log f drawn for all L positions by the
+    same gate recipe from its own stream (seed + 2000), so no two positions share their decay.
+    Returns (case, base): base is the period-length case whose rows repeat (its bf16 bits,
+    repeated with repeat_rows, are the upload of the long case without re-rounding)."""
+    base = make_case(B, H, period, D, "bf16", seed=seed, gate="zero", with_do=with_do)
+    rng = np.random.default_rng(seed + 2000)
+    log_f = _draw_log_f(rng, B, H, L, gate, 3.0, 1.5, (1.0, 6.0))
+    q, k, v = (repeat_rows(getattr(base, n), L) for n in ("q", "k", "v"))
+    do = repeat_rows(base.do, L) if with_do else None
+    case = FoxCase(name, B, H, L, D, "bf16", q, k, v, log_f=log_f, do=do, seed=seed)
+    return case, base
 
 
 def make_pro_case(B: int, H: int, L: int, D: int, d_model: int, *, seed: int = 4,

@@ -19,9 +19,9 @@ a Forget Gate"):
 Two independent tiers compute attention:
   T1 (``*_bruteforce``): explicit range sums D_ij = sum_{l=j+1..i} log f_l and per-row loops;
       supports log f = -inf (f = 0). For tiny L only.
-  T2 (``attn_fwd`` / ``attn_bwd`` / ``attn_fwd_rows``): D_ij = c_i - c_j with c = cumsum(log f),
-      vectorised over blocks of query rows (the blocking only groups rows; every row still sees
-      all of its keys at once).
+  T2 (``attn_fwd`` / ``attn_bwd`` / ``attn_fwd_rows`` / ``attn_bwd_tail``): D_ij = c_i - c_j
+      with c = cumsum(log f), vectorised over blocks of query rows (the blocking only groups
+      rows; every row still sees all of its keys at once).
 
 Conventions (readings taken where the pages are silent or ambiguous): positions are 0-indexed and
 c is the inclusive prefix sum; the softmax scale multiplies q.k only, never the bias; the
@@ -342,6 +342,37 @@ def attn_fwd_rows(q, k, v, c, rows, *, scale):
         O[n] = (p @ v[:i + 1]) / ell
         LSE[n] = m + np.log(ell)
     return O, LSE
+
+
+def attn_bwd_tail(q, k, v, c, do, n, *, scale):
+    """Forward and backward of the last n positions of one (b, h): q, k, v, dO [L, D], c [L].
+
+    Only the last n query rows reach the gradients of the last n positions: key j is seen by
+    queries i >= j, and d log f_l = sum_{t >= l} dc_t sums over positions t >= l. So the
+    definition written for rows i in [L - n, L) alone gives, exactly, O and LSE of those rows,
+    their dQ, and dK, dV and d log f of those positions, whatever L is. Returns
+    (O, LSE, dQ, dK, dV, dlog_f), each for the last n positions.
+    """
+    k, v, c = _f64(k), _f64(v), _f64(c)
+    L = k.shape[0]
+    i0 = L - n
+    qt, dot = _f64(q[i0:]), _f64(do[i0:])
+    rows = np.arange(i0, L)
+    s = _rows_logits(qt, k, c[i0:], c, rows, scale)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    ell = p.sum(axis=1)
+    P = p / ell[:, None]
+    O = P @ v
+    LSE = m + np.log(ell)
+    Delta = np.sum(dot * O, axis=1)
+    dP = dot @ v.T
+    dS = P * (dP - Delta[:, None])
+    dQ = scale * (dS @ k)
+    dV = P[:, i0:].T @ dot
+    dK = scale * (dS[:, i0:].T @ qt)
+    dc = dS.sum(axis=1) - dS[:, i0:].sum(axis=0)  # dc^q_t + dc^k_t of the tail positions
+    return O, LSE, dQ, dK, dV, reverse_cumsum(dc)
 
 
 def attn_bwd(q, k, v, log_f=None, do=None, *, c=None, scale, O=None, LSE=None, block=512):

@@ -1,8 +1,8 @@
 """GPU parity: every entry point of libfox against the fp64 oracle on the same seeded inputs.
 
-Sizes the oracle finishes in seconds are compared element by element; the full-size workloads
-(L = 16384) are compared on sampled rows (forward) or on whole heads (backward), which the
-oracle computes independently of the rest. Tolerances: max-abs 2e-2 and relative L2 5e-3 for
+Sizes the oracle finishes in seconds are compared element by element, and so are the full-size
+workloads (L = 16384, every row of every head); the longest sequence the library takes
+(L = 2^23) is compared on rows the oracle computes independently of the rest. Tolerances: max-abs 2e-2 and relative L2 5e-3 for
 bf16 inputs with fp32 accumulation, 1e-5 max-abs for the fp32 workload.
 """
 import math
@@ -727,6 +727,53 @@ def test_skip_config5_full_length(fox):
     torch.cuda.synchronize()
     for name, a, b in zip(("dq", "dk", "dv", "dlog f"), g0, g1):
         assert torch.equal(a, b), name
+
+
+MAX_L = 1 << 23  # the longest sequence the library takes
+
+
+def test_maximum_length(fox):
+    """L = 2^23 at D = 128 (B = H = 1): one K or V buffer then spans 2^31 bytes, the most the
+    kernels' 32-bit buffer offsets address. q, k, v and dO repeat with a period of 65537 rows
+    (drawing 2^30 values each would take minutes); log f is -1/4 or 0 at random per position, so
+    every prefix sum is exact in fp32 (a gate of the usual kind would reach |c| ~ 1e6 here, where
+    an fp32 ulp is 0.06 and only fp64 c keeps the bias) and the memory is a few hundred tokens.
+    The forward and backward run with a skip plan, which leaves out the fully decayed tiles and
+    returns the dense path's bits (the skip tests), so the kernels reach every offset quickly.
+    Checked against the oracle: c everywhere, O and LSE of rows spread over the sequence, and O,
+    LSE, dQ, dK, dV and d log f of the last 16 positions (which only the last 16 rows reach)."""
+    L, D = MAX_L, 128
+    s = default_scale(D)
+    say(f"max length L={L} D={D}: inputs")
+    case, base = fi.make_periodic_case(1, 1, L, D, period=65537, seed=81, gate="quarter_steps",
+                                       with_do=True)
+
+    def up(name):
+        bits = fi.repeat_rows(fi.bf16_bits(getattr(base, name)), L)
+        return torch.from_numpy(bits).view(torch.bfloat16).cuda()
+
+    q, k, v, do = (up(n) for n in ("q", "k", "v", "do"))
+    say("  scan, plan, forward, backward")
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    plan = fox.fox_attn_skip_plan(q, k, c)
+    o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32, skip_plan=plan)
+    dq, dk, dv, dlf = fox.fox_attn_bwd(q, k, v, c, o, lse, do, skip_plan=plan)
+    torch.cuda.synchronize()
+    cc = oracle.cumsum_logf(case.log_f)[0, 0]
+    assert np.array_equal(host(c)[0, 0], cc), "c is exact in fp32 for these gates"
+    rows = np.array([0, 1, 63, 64, 65535, 65536, 65537, (L >> 1) - 1, L >> 1, L - 257])
+    say("  oracle rows")
+    O, LSE = oracle.attn_fwd_rows(case.q[0, 0], case.k[0, 0], case.v[0, 0], cc, rows, scale=s)
+    ri = torch.from_numpy(rows).cuda()
+    check("O rows", host(o[0, 0].index_select(0, ri)), O)
+    check("LSE rows", host(lse[0, 0].index_select(0, ri)), LSE)
+    say("  oracle tail")
+    n = 16
+    To, Tl, TdQ, TdK, TdV, TdL = oracle.attn_bwd_tail(case.q[0, 0], case.k[0, 0], case.v[0, 0],
+                                                      cc, case.do[0, 0], n, scale=s)
+    for name, got, ref in (("O tail", o, To), ("LSE tail", lse, Tl), ("dQ tail", dq, TdQ),
+                           ("dK tail", dk, TdK), ("dV tail", dv, TdV), ("d log f tail", dlf, TdL)):
+        check(name, host(got[0, 0, L - n:]), ref)
 
 
 # ---------------------------------------------------------------------------- single-token decode

@@ -259,6 +259,40 @@ def test_gradients_against_finite_differences():
             assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (which, fd, an)
 
 
+@pytest.mark.parametrize("n", [1, 5, 40, 64])
+@pytest.mark.parametrize("gate", ["normal", "zero"])
+def test_tail_backward_against_torch_autograd(n, gate):
+    """attn_bwd_tail (the last n positions alone) against torch autograd of the whole sequence,
+    and its forward part against torch's attention: exact where only the tail rows reach."""
+    c = _case(B=1, H=1, L=64, D=16, seed=71, gate=gate)
+    s = 1 / math.sqrt(c.D)
+    dq, dk, dv, dlf = _torch_grads(c, s)
+    cc = oracle.cumsum_logf(c.log_f)[0, 0]
+    O, LSE, dQ, dK, dV, dLF = oracle.attn_bwd_tail(c.q[0, 0], c.k[0, 0], c.v[0, 0], cc,
+                                                   c.do[0, 0], n, scale=s)
+    bias = cc[:, None] - cc[None, :]
+    ref_o = _sdpa_causal(c.q, c.k, c.v, s, bias)[0, 0, -n:]
+    ref_lse = _lse_ref(c.q, c.k, s, bias)[0, 0, -n:]
+    tol = 1e-11
+    assert np.abs(O - ref_o).max() < tol and np.abs(LSE - ref_lse).max() < tol
+    for got, ref in ((dQ, dq), (dK, dk), (dV, dv), (dLF, dlf)):
+        ref = ref[0, 0, -n:]
+        assert np.abs(got - ref).max() < tol * max(1.0, np.abs(ref).max())
+
+
+def test_tail_backward_with_a_hard_reset():
+    """A reset (log f = -1e4) inside the tail: rows after it see nothing before it."""
+    c = _case(B=1, H=1, L=48, D=8, seed=72)
+    c.log_f[0, 0, 40] = -1e4
+    s = 0.3
+    dq, dk, dv, dlf = _torch_grads(c, s)
+    cc = oracle.cumsum_logf(c.log_f)[0, 0]
+    got = oracle.attn_bwd_tail(c.q[0, 0], c.k[0, 0], c.v[0, 0], cc, c.do[0, 0], 12, scale=s)
+    for g, r in zip(got[2:], (dq, dk, dv, dlf)):
+        r = r[0, 0, -12:]
+        assert np.abs(g - r).max() < 1e-10 * max(1.0, np.abs(r).max())
+
+
 def test_gradient_invariants():
     c = _case()
     s = 1 / math.sqrt(c.D)
@@ -318,6 +352,43 @@ def test_unmutated_oracle_passes_the_pin_harness():
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(name):
     assert not _pins_hold(_mutant(name))
+
+
+TAIL_MUTATIONS = {
+    "tail_drops_dck": ("dc = dS.sum(axis=1) - dS[:, i0:].sum(axis=0)", "dc = dS.sum(axis=1)"),
+    "tail_dk_unscaled": ("dK = scale * (dS[:, i0:].T @ qt)", "dK = dS[:, i0:].T @ qt"),
+    "tail_dv_keys_shifted": ("dV = P[:, i0:].T @ dot", "dV = P[:, i0 - 1:-1].T @ dot"),
+    "tail_row_term_unnormalised": ("P = p / ell[:, None]", "P = p"),
+}
+
+
+def _tail_pins_hold(mod):
+    """The tail of a 40-position sequence (n = 9, with a reset inside it) against autograd."""
+    c = _case(B=1, H=1, L=40, D=8, seed=73)
+    c.log_f[0, 0, 35] = -30.0
+    s = 0.4
+    ref = _torch_grads(c, s)
+    cc = oracle.cumsum_logf(c.log_f)[0, 0]
+    try:
+        got = mod.attn_bwd_tail(c.q[0, 0], c.k[0, 0], c.v[0, 0], cc, c.do[0, 0], 9, scale=s)
+    except ValueError:
+        return False
+    return all(g.shape == r[0, 0, -9:].shape and np.abs(g - r[0, 0, -9:]).max() < 1e-9
+               for g, r in zip(got[2:], ref))
+
+
+def test_tail_pin_harness():
+    assert _tail_pins_hold(fox_oracle)
+
+
+@pytest.mark.parametrize("name", sorted(TAIL_MUTATIONS))
+def test_planted_tail_mistake_is_caught(name):
+    old, new = TAIL_MUTATIONS[name]
+    src = open(fox_oracle.__file__).read()
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mod.__dict__)
+    assert not _tail_pins_hold(mod)
 
 
 # ---------------------------------------------------------------- Pro block backward (gate, QK-norm)
