@@ -776,6 +776,38 @@ def test_maximum_length(fox):
         check(name, host(got[0, 0, L - n:]), ref)
 
 
+def test_maximum_head_count(fox):
+    """B*H = 2^21, the most heads the attention entry points take, at L = 1 and D = 64: the
+    largest grids the kernels launch and the work order at that many heads. A one-position
+    sequence attends only to itself, so at every head O = v, LSE = scale q.k, dV = dO, and dQ,
+    dK and d log f vanish (row 0's closed form, which pins the oracle); 4096 random heads are
+    also compared with the oracle itself."""
+    B, H, L, D = 2048, 1024, 1, 64
+    s = default_scale(D)
+    say(f"max heads B*H={B * H} L={L} D={D}")
+    case = fi.make_case(B, H, L, D, "bf16", seed=82, gate="normal", with_do=True)
+    q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    o, lse = fox.fox_attn_fwd(q, k, v, c, o_dtype=torch.float32)
+    dq, dk, dv, dlf = fox.fox_attn_bwd(q, k, v, c, o, lse, do)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv, dlf = (host(t) for t in (o, lse, dq, dk, dv, dlf))
+    check("O = v, every head", o, case.v)
+    check("LSE = scale q.k, every head", lse, s * np.sum(case.q.astype(np.float64) * case.k, -1))
+    check("dV = dO, every head", dv, case.do)
+    for name, g in (("dQ", dq), ("dK", dk), ("d log f", dlf)):
+        check(f"{name} = 0, every head", g, np.zeros_like(g), rel_l2=None)
+    pick = np.random.default_rng(82).choice(B * H, size=4096, replace=False)
+    b, h = pick // H, pick % H
+    sub = lambda a: a[b, h][None]
+    O, LSE = oracle.attn_fwd(sub(case.q), sub(case.k), sub(case.v), sub(case.log_f), scale=s)
+    dQ, dK, dV, dLF = oracle.attn_bwd(sub(case.q), sub(case.k), sub(case.v), sub(case.log_f),
+                                      sub(case.do), scale=s)[:4]
+    for name, got, ref in (("O", o, O), ("LSE", lse, LSE), ("dQ", dq, dQ), ("dK", dk, dK),
+                           ("dV", dv, dV), ("d log f", dlf, dLF)):
+        check(f"{name}, 4096 heads against the oracle", sub(got), ref)
+
+
 # ---------------------------------------------------------------------------- single-token decode
 def _decode_ref(q, k, v, log_f, lens, scale):
     """Oracle rows: the query of sequence b sits at position lens[b] - 1 of its cache."""
