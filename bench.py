@@ -161,7 +161,7 @@ def main():
                     help="the FoX paper's own head shape instead: B=1, H=24, L=16384, D=64 "
                          "(same input recipe); a second measurement, not the headline line")
     ap.add_argument("--pro", action="store_true",
-                    help="the Pro block's whole attention step instead (workload 4 plus dO): gate, "
+                    help="the Pro block's whole attention step instead (x [1, 16384, 1536], 12 heads of D=128, plus dO): gate, "
                          "scan, QK-norm, attention forward and backward, QK-norm and gate backward")
     ap.add_argument("--decode", action="store_true",
                     help="single-token decode against a full KV cache instead: B=8 sequences of "
@@ -645,7 +645,8 @@ def pro_extra_kernels(torch, fox, x, k, v, stream):
 
 
 def pro_step(args, torch, fi, fox, dev):
-    """One training step of the Pro block's attention path (workload 4 plus a seeded dO)."""
+    """One training step of the Pro block's attention path (x [1, 16384, 1536], q, k, v
+    [1, 12, 16384, 128], plus a seeded dO)."""
     case = fi.config_case(4)
     B, H, L, D, dm = case.B, case.H, case.L, case.D, case.x.shape[-1]
     up = lambda a, dt: (torch.from_numpy(fi.bf16_bits(a)).view(torch.bfloat16) if dt == "bf16"

@@ -138,10 +138,10 @@ def test_forward_config2(fox):
 
 @pytest.fixture(scope="module")
 def config3_oracle():
-    """The oracle's O and LSE of workload 3 (every row of all 12 heads), shared with the
-    full-length backward test, whose inputs are workload 3's plus dO."""
+    """The oracle's O and LSE of the B=1, H=12, L=16384, D=128 bf16 workload (every row of all
+    12 heads), shared with the full-length backward test, whose inputs are the same plus dO."""
     case = fi.config_case(3)
-    say("oracle forward of workload 3 (12 heads, L=16384) ...")
+    say("oracle forward of the L=16384, 12-head workload ...")
     O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=default_scale(case.D),
                              block=1024)
     return O, LSE
@@ -379,7 +379,8 @@ def _run_bwd_f32(fox, case, c_dtype=torch.float32):
 
 
 def test_backward_config1_fp32(fox):
-    """The full-fp32 backward at workload 1's shape and recipe, to the fp32 bar."""
+    """The full-fp32 backward at the small fp32 workload's shape and recipe (B=1, H=2, L=256,
+    D=64), to the fp32 bar."""
     case = fi.make_case(1, 2, 256, 64, "f32", seed=1, gate_mean=3.0, gate_std=1.5, with_do=True)
     say("bwd config1 fp32")
     got = _run_bwd_f32(fox, case)
@@ -1225,8 +1226,9 @@ def test_fwd_ex_qnorm_and_output_gate(fox, L, D, g_dt, weighted):
 
 
 def test_fwd_ex_pro_pipeline_config4(fox):
-    """Workload 4 with the fusions: gate -> scan, k -> QK-norm, then fox_attn_fwd_ex normalising q
-    on load and applying an output gate; every row of all 12 heads."""
+    """The Pro workload (x [1, 16384, 1536], 12 heads) with the fusions: gate -> scan,
+    k -> QK-norm, then fox_attn_fwd_ex normalising q on load and applying an output gate; every
+    row of all 12 heads."""
     case = fi.config_case(4)
     say("pro pipeline config4, fused q-norm and output gate")
     rng = np.random.default_rng(404)
@@ -1304,10 +1306,10 @@ def test_fwd_ex_shift_prologue(fox, L, D, ks, vs, kn, qn, g_dt, c_dt):
 
 
 def test_fwd_ex_shift_prologue_config4(fox):
-    """Workload 4 with the whole Pro prologue fused: shift gates from x (fox_shift_gate), the raw
-    key and value candidates shifted, keys and queries normalised and the output gate applied
-    inside one forward; bit-identical to the separate passes, and every row of all 12 heads
-    against the oracle."""
+    """The Pro workload (x [1, 16384, 1536], 12 heads) with the whole Pro prologue fused: shift
+    gates from x (fox_shift_gate), the raw key and value candidates shifted, keys and queries
+    normalised and the output gate applied inside one forward; bit-identical to the separate
+    passes, and every row of all 12 heads against the oracle."""
     case = fi.config_case(4)
     say("pro pipeline config4, shift, norms and output gate fused")
     rng = np.random.default_rng(405)
