@@ -2,8 +2,9 @@
 
 Sizes the oracle finishes in seconds are compared element by element, and so are the full-size
 workloads (L = 16384, every row of every head); the longest sequence the library takes
-(L = 2^23) is compared on rows the oracle computes independently of the rest. Tolerances: max-abs 2e-2 and relative L2 5e-3 for
-bf16 inputs with fp32 accumulation, 1e-5 max-abs for the fp32 workload.
+(L = 2^23) is compared on rows the oracle computes independently of the rest. Tolerances:
+max-abs 2e-2 and relative L2 5e-3 for bf16 inputs with fp32 accumulation, 1e-5 max-abs for the
+fp32 workload.
 """
 import math
 
