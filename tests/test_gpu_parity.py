@@ -924,6 +924,49 @@ def test_decode_append_after_prefill(fox):
     assert all(torch.equal(a, b) for a, b in zip(before, (kc, vc, c)))
 
 
+def test_decode_maximum_length(fox):
+    """A 2^23-position cache at D = 128 (one sequence, one head: a 2^31-byte K or V cache),
+    filled to T - 1, then the last position appended and decoded: the append writes k, v and c
+    of position T - 1 exactly (the gate keeps c exact in fp32, as in test_maximum_length), the
+    dense decode and the key-norm skip give the same bits, and both match the oracle's row."""
+    T, D = MAX_L, 128
+    s = default_scale(D)
+    say(f"decode at T={T} D={D}")
+    case, base = fi.make_periodic_case(1, 1, T, D, period=65537, seed=83, gate="quarter_steps")
+    q = fi.bf16_round(np.random.default_rng(83).standard_normal((1, 1, D), dtype=np.float32))
+
+    def up(name):
+        bits = fi.repeat_rows(fi.bf16_bits(getattr(base, name)), T)
+        return torch.from_numpy(bits).view(torch.bfloat16).cuda()
+
+    kc, vc = up("k"), up("v")
+    last_k, last_v = kc[:, :, T - 1].clone(), vc[:, :, T - 1].clone()
+    kc[:, :, T - 1].zero_()
+    vc[:, :, T - 1].zero_()
+    c = fox.fox_logf_cumsum(dev(case.log_f, "f32"))
+    c[:, :, T - 1] = 0.0
+    lens = torch.full((1,), T - 1, dtype=torch.int32, device="cuda")
+    kn = fox.fox_attn_decode_key_norms(kc, lens)
+    fox.fox_attn_decode_append(last_k, last_v, dev(case.log_f[:, :, T - 1], "f32"), kc, vc, c,
+                               lens, k_norms=kn)
+    o0, l0 = fox.fox_attn_decode(dev(q, "bf16"), kc, vc, c, lens, o_dtype=torch.float32)
+    o1, l1 = fox.fox_attn_decode(dev(q, "bf16"), kc, vc, c, lens, o_dtype=torch.float32,
+                                 k_norms=kn)
+    torch.cuda.synchronize()
+    assert host(lens).tolist() == [T]
+    assert torch.equal(kc[:, :, T - 1], last_k) and torch.equal(vc[:, :, T - 1], last_v)
+    cc = oracle.cumsum_logf(case.log_f)[0, 0]
+    assert host(c[0, 0, T - 2:]).tolist() == cc[T - 2:].tolist()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    say("  oracle row")
+    q_rows = np.broadcast_to(q[0, 0], (T, D))  # the query sits at position T - 1
+    no_do = np.broadcast_to(np.zeros(D, np.float32), (T, D))
+    O, LSE = oracle.attn_bwd_tail(q_rows, case.k[0, 0], case.v[0, 0], cc, no_do, 1, scale=s)[:2]
+    # c is exact here, so the fp32 arithmetic bound is the plain fp32 floor
+    _check_tight("decode O at T = 2^23", host(o0)[0], O, rel=1e-5)
+    _check_tight("decode LSE at T = 2^23", host(l0)[0], LSE, rel=1e-5)
+
+
 # ------------------------------------------------------ Pro block: shift gate, KV-shift, output gate
 @pytest.mark.parametrize("x_dt,dm", [("bf16", 1536), ("f32", 1536), ("bf16", 40)])
 def test_shift_gate_forward_backward(fox, x_dt, dm):
