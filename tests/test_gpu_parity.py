@@ -1394,8 +1394,12 @@ def test_fwd_ex_shift_prologue_config4(fox):
 # can also turn one-hot (weights 1 - 6e-6 and 6e-6 at L = 2): dQ and d log f are then differences
 # of nearly equal terms and shrink to ~1e-5, their error set by the terms' size rather than their
 # own, so the relative-L2 bar applies there only where the reference's RMS reaches RISING_RMS.
+# That cancellation also leaves d log f small beside the terms it sums (the rectangle sums of
+# |dS|, up to 500 times its RMS), and the bf16 path is accurate to 2-5e-5 of those terms (errors
+# of 0.7-1.1e-5 RMS in the sweep), where a 5e-3 relative bar holds only for an RMS above
+# 1.4-2.2e-3: RISING_RMS is five times that.
 RISING_SCALE = 5.0
-RISING_RMS = 1e-3
+RISING_RMS = 1e-2
 
 
 def _sweep_case(i):
@@ -1431,12 +1435,13 @@ def test_random_sweep_against_oracle(fox, i):
     _run_sweep_case(fox, i)
 
 
-@pytest.mark.parametrize("i", [79, 337, 372, 1953])
+@pytest.mark.parametrize("i", [79, 337, 372, 1953, 10716, 11308])
 def test_sweep_cases_from_wider_search(fox, i):
-    """Seeds of the same generator that a 3600-case search flagged: 1953 (gates in (0, 1), a row
-    dominated by two keys, |dQ| = 5.7, where the bf16 rounding of dS alone moved dQ by 1.6e-2
-    before the diagonal tiles took the remainder products), and three with rising c (large dK,
-    dV; one-hot rows at L = 2; a vanishing d log f)."""
+    """Seeds of the same generator that wider searches (18600 cases) flagged: 1953 (gates in
+    (0, 1), a row dominated by two keys, |dQ| = 5.7, where the bf16 rounding of dS alone moved dQ
+    by 1.6e-2 before the diagonal tiles took the remainder products), and five with rising c
+    (large dK, dV; one-hot rows at L = 2; a vanishing d log f; d log f of RMS 1e-3 summing terms
+    of RMS 0.14-0.55)."""
     _run_sweep_case(fox, i)
 
 
