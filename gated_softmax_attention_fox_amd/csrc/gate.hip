@@ -7,9 +7,13 @@
 // HBM-bound contraction with H (~12) outputs per token, done on the vector ALU: a workgroup owns
 // 64 tokens, stages x through LDS in coalesced 256-column slabs, and each of its 4 waves walks a
 // quarter of every slab with one token per lane. The gate weights are read with wave-uniform
-// addresses (scalar loads), so the inner loop is one FMA per (token, head, column). The four
-// per-wave partial sums meet in LDS and lane t writes log f for token t, evaluated stably as
-// -log1p(exp(-z)) for z >= 0 and z - log1p(exp(z)) otherwise.
+// addresses (scalar loads), so the inner loop is one FMA per (token, head, column). It runs in
+// fp64: the products of fp32 x and w are exact there and the sum rounds only at fp64, so z is
+// the fp64 sum rounded once to fp32 whatever d_model and sum |x w| are (an fp32 running sum over
+// a wave's 384 columns at d_model 1536 moved log f by up to 1.5e-5 where sum |x w| reached ~200).
+// The
+// four per-wave partial sums meet in LDS and lane t writes log f for token t, evaluated stably
+// as -log1p(exp(-z)) for z >= 0 and z - log1p(exp(z)) otherwise.
 //
 // The same kernel serves the backward (kBwd): it recomputes z and writes
 // dz[b, h, t] = dlog_f[b, h, t] * sigma(-z), since d log sigma(z) / dz = 1 - sigma(z) = sigma(-z);
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
                                                    int tok_blocks) {
   __shared__ bf16_t xs_b[kBf16 ? kGateTok * kGatePitch : 1];
   __shared__ float xs_f[kBf16 ? 1 : kGateTok * kGatePitch];
-  __shared__ float red[4][kGateHeads][kGateTok];
+  __shared__ double red[4][kGateHeads][kGateTok];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x / tok_blocks;
@@ -52,9 +56,9 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   const int h0 = blockIdx.y * kGateHeads;
   const int nh = H - h0 < kGateHeads ? H - h0 : kGateHeads;
 
-  float acc[kGateHeads];
+  double acc[kGateHeads];
 #pragma unroll
-  for (int h = 0; h < kGateHeads; ++h) acc[h] = 0.f;
+  for (int h = 0; h < kGateHeads; ++h) acc[h] = 0.0;
 
   for (int d0 = 0; d0 < dm; d0 += kGateSlab) {
     const int width = dm - d0 < kGateSlab ? dm - d0 : kGateSlab;  // multiple of 8
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
         if (h < nh) {
           const float* wr = w_f + (size_t)(h0 + h) * dm + d0 + col;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h] = fmaf(xv8[e], wr[e], acc[h]);
+          for (int e = 0; e < 8; ++e) acc[h] = fma((double)xv8[e], (double)wr[e], acc[h]);
         }
       }
     }
@@ -114,8 +118,9 @@ __global__ __launch_bounds__(256) void gate_kernel(const void* __restrict__ xv,
   if (wave == 0) {
     const int t = t0 + lane;
     for (int h = 0; h < nh; ++h) {
-      const float z = ((red[0][h][lane] + red[1][h][lane]) + (red[2][h][lane] + red[3][h][lane])) +
-                      (b_f ? b_f[h0 + h] : 0.f);
+      const float z = (float)(((red[0][h][lane] + red[1][h][lane]) +
+                               (red[2][h][lane] + red[3][h][lane])) +
+                              (b_f ? (double)b_f[h0 + h] : 0.0));
       if (t < L) {
         if constexpr (kBwd) {
           const float g = dlog_f[((size_t)b * H + h0 + h) * L + t];

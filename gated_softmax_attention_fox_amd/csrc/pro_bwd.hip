@@ -216,9 +216,9 @@ __global__ __launch_bounds__(256) void gate_dw_partial_kernel(const void* __rest
     for (int h = 0; h < nh; ++h) part[((size_t)chunk * H + h0 + h) * dm + d] = acc[h];
   }
   if (slab == 0 && tid < nh) {
-    float sum = 0.f;
-    for (int r = 0; r < n; ++r) sum += dzs[r][tid];
-    part_db[(size_t)chunk * H + h0 + tid] = sum;
+    double sum = 0.0;  // fp64, as in the matrix-core kernel
+    for (int r = 0; r < n; ++r) sum += (double)dzs[r][tid];
+    part_db[(size_t)chunk * H + h0 + tid] = (float)sum;
   }
 }
 
@@ -279,10 +279,11 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
   f32x16 acc = zero16();
   // db partial: thread tid holds dz of token tid % TS and heads tid / TS + 4 q (q < DV) in every
   // stage, so each wave sums its lanes' values over the stages and reduces across lanes at the
-  // end (a fixed butterfly order).
-  float dba[DV];
+  // end (a fixed butterfly order). The sums run in fp64: db_f is a sum over every token whose
+  // terms may cancel, and an fp32 running sum left it off by 1.4-1.9e-5 relative where it did.
+  double dba[DV];
 #pragma unroll
-  for (int q = 0; q < DV; ++q) dba[q] = 0.f;
+  for (int q = 0; q < DV; ++q) dba[q] = 0.0;
   load_stage(0);
   for (int st = 0; st < n_st; ++st) {
 #pragma unroll
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
       dzp[0][ks][hb][hh][e] = __builtin_bit_cast(bf16_t, p1);
       dzp[1][ks][hb][hh][e] = __builtin_bit_cast(bf16_t, p2);
       dzp[2][ks][hb][hh][e] = __builtin_bit_cast(bf16_t, (__bf16)(r1 - (float)p2));
-      dba[q] += v;
+      dba[q] += (double)v;
     }
     __syncthreads();
     if (st + 1 < n_st) load_stage(st + 1);
@@ -334,17 +335,17 @@ __global__ __launch_bounds__(256) void gate_dw_mfma_kernel(const bf16_t* __restr
     static_assert(TS == 64, "one wave holds one head's tokens of a stage");
 #pragma unroll
     for (int q = 0; q < DV; ++q) {
-      float v = dba[q];
+      double v = dba[q];
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
       const int hh = wave + 4 * q;  // (tid + 256 q) / TS
-      if (lane == 0 && hh < nh) part_db[(size_t)chunk * H + h0 + hh] = v;
+      if (lane == 0 && hh < nh) part_db[(size_t)chunk * H + h0 + hh] = (float)v;
     }
   }
 }
 
-// dw_f[h, d] and db_f[h]: the chunk partials summed in a fixed order. A workgroup owns 64
-// consecutive entries of the flattened [H, d_model] array; wave w sums the chunks
+// dw_f[h, d] and db_f[h]: the chunk partials summed in a fixed order, in fp64. A workgroup owns
+// 64 consecutive entries of the flattened [H, d_model] array; wave w sums the chunks
 // [w n / 4, (w + 1) n / 4) of every entry (16 loads in flight), and the four wave sums are added
 // in wave order. The last workgroup sums the db_f partials the same way.
 __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __restrict__ part,
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __rest
                                                              float* __restrict__ dw_f,
                                                              float* __restrict__ db_f, int n_chunk,
                                                              int dm, int H) {
-  __shared__ float red[4][64];
+  __shared__ double red[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n_w = (int64_t)H * dm;
   const bool db_blk = blockIdx.x == gridDim.x - 1;
@@ -361,15 +362,15 @@ __global__ __launch_bounds__(256) void gate_dw_reduce_kernel(const float* __rest
   const float* src = db_blk ? part_db : part;
   const int64_t stride = db_blk ? H : n_w;
   const int c0 = (int)((int64_t)n_chunk * wave / 4), c1 = (int)((int64_t)n_chunk * (wave + 1) / 4);
-  float s = 0.f;
+  double s = 0.0;
   if (e < n_e) {
 #pragma unroll 16
-    for (int c = c0; c < c1; ++c) s += src[(size_t)c * stride + e];
+    for (int c = c0; c < c1; ++c) s += (double)src[(size_t)c * stride + e];
   }
   red[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && e < n_e) {
-    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    const float t = (float)(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
     if (!db_blk) dw_f[e] = t;
     else if (db_f) db_f[e] = t;
   }
