@@ -1445,8 +1445,41 @@ def test_sweep_cases_from_wider_search(fox, i):
     _run_sweep_case(fox, i)
 
 
-def _run_sweep_case(fox, i):
-    case, gate, opts = _sweep_case(i)
+def _long_sweep_case(i):
+    """The sweep's gate kinds and options at long sequences (L from 3000 to 16384)."""
+    rng = np.random.default_rng(50000 + i)
+    B, H = 1, int(rng.integers(1, 3))
+    L = int(rng.choice([3000, 4096, 8191, 12288, 16384]))
+    D = int(rng.choice([64, 128]))
+    gate = str(rng.choice(["normal", "per_head", "zero", "strong", "reset", "rising"]))
+    if gate == "strong":
+        case = fi.make_case(B, H, L, D, "bf16", seed=51000 + i, gate="normal", gate_mean=-2.0,
+                            with_do=True)
+    elif gate in ("reset", "rising"):
+        case = fi.make_case(B, H, L, D, "bf16", seed=51000 + i, gate="normal", gate_mean=4.0,
+                            with_do=True)
+        for a in sorted(set(int(x) for x in rng.integers(0, L, size=3))):
+            case.log_f[..., a:a + 5] = -300.0 if gate == "reset" else 12.0
+    else:
+        case = fi.make_case(B, H, L, D, "bf16", seed=51000 + i, gate=gate, with_do=True)
+    opts = dict(o_dtype=str(rng.choice(["f32", "bf16"])), c_dtype=str(rng.choice(["f32", "f64"])),
+                fused_scan=bool(rng.integers(0, 2)), skip=bool(rng.integers(0, 2)))
+    if opts["c_dtype"] == "f64":
+        opts["skip"] = False
+    return case, gate, opts
+
+
+@pytest.mark.parametrize("i", [1, 2, 7, 31, 32])
+def test_long_sequence_sweep_cases(fox, i):
+    """Cases of the long-sequence generator (200 of which pass in a one-off run), each with its
+    drawn options, against the oracle at every element: rising c at L = 16384, D = 64 (fp64 c,
+    the scan fused); open gates at 16384; strong decay at 16384 (fp32 c); hard resets at 12288
+    and rising c at 12288, both with fp32 c and tile skipping."""
+    _run_sweep_case(fox, i, _long_sweep_case)
+
+
+def _run_sweep_case(fox, i, gen=None):
+    case, gate, opts = (gen or _sweep_case)(i)
     say(f"sweep {i}: B={case.B} H={case.H} L={case.L} D={case.D} gate={gate} {opts}")
     s = default_scale(case.D)
     q, k, v, do = (dev(getattr(case, n), "bf16") for n in ("q", "k", "v", "do"))
