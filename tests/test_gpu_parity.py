@@ -924,6 +924,66 @@ def test_decode_append_after_prefill(fox):
     assert all(torch.equal(a, b) for a, b in zip(before, (kc, vc, c)))
 
 
+def test_pro_decode_steps_match_the_full_forward(fox):
+    """Pro block decoding, built from the library's calls: a prefill of 300 positions through the
+    sequence passes (shift gates, token shift with the key norm, forget gate, scan), then four
+    tokens each through the same calls on one position (the token shift takes the previous
+    position's candidates), an append, the q-norm, a decode and the output norm and gate. Every
+    decoded row must match the oracle's full-sequence Pro forward at that position."""
+    B, H, D, dm, T0, N = 2, 3, 128, 96, 300, 4
+    L, eps = T0 + N, 1e-6
+    rng = np.random.default_rng(84)
+    bf = lambda *shape: fi.bf16_round(rng.standard_normal(shape, dtype=np.float32))
+    x, q, kc, vc, g = bf(B, L, dm), bf(B, H, L, D), bf(B, H, L, D), bf(B, H, L, D), bf(B, H, L, D)
+    w_f = (0.02 * rng.standard_normal((H, dm))).astype(np.float32)
+    b_f = rng.uniform(1.0, 6.0, H).astype(np.float32)
+    w_k, w_v = ((0.05 * rng.standard_normal((H, dm))).astype(np.float32) for _ in range(2))
+    say("pro decode: prefill 300, then 4 tokens")
+    xt, wf, bfv, wk, wv = dev(x, "bf16"), dev(w_f, "f32"), dev(b_f, "f32"), dev(w_k, "f32"), dev(w_v, "f32")
+    qt, kct, vct, gt = (dev(a, "bf16") for a in (q, kc, vc, g))
+    # prefill: the sequence passes over positions 0 .. T0 - 1, into a cache of L positions
+    pre = lambda a: a[:, :, :T0].contiguous()
+    k0 = fox.fox_kv_shift(pre(kct), fox.fox_shift_gate(xt[:, :T0].contiguous(), wk),
+                          normalize=True, eps=eps)
+    v0 = fox.fox_kv_shift(pre(vct), fox.fox_shift_gate(xt[:, :T0].contiguous(), wv))
+    k_cache = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device="cuda")
+    v_cache = torch.zeros_like(k_cache)
+    c_cache = torch.zeros((B, H, L), dtype=torch.float32, device="cuda")
+    k_cache[:, :, :T0] = k0
+    v_cache[:, :, :T0] = v0
+    c_cache[:, :, :T0] = fox.fox_logf_cumsum(fox.fox_gate_logf(xt[:, :T0].contiguous(), wf, bfv))
+    lens = torch.full((B,), T0, dtype=torch.int32, device="cuda")
+    got_o, got_y = [], []
+    for n in range(N):
+        p = T0 + n
+        xp = xt[:, p:p + 1].contiguous()
+        a_k = fox.fox_shift_gate(xp, wk)  # [B, H, 1]
+        a_v = fox.fox_shift_gate(xp, wv)
+        pair = lambda cand, a: (cand[:, :, p - 1:p + 1].contiguous(),
+                                torch.cat([torch.zeros_like(a), a], dim=2))
+        k_t = fox.fox_kv_shift(*pair(kct, a_k), normalize=True, eps=eps)[:, :, 1].contiguous()
+        v_t = fox.fox_kv_shift(*pair(vct, a_v))[:, :, 1].contiguous()
+        lf_t = fox.fox_gate_logf(xp, wf, bfv)[:, :, 0].contiguous()
+        fox.fox_attn_decode_append(k_t, v_t, lf_t, k_cache, v_cache, c_cache, lens)
+        q_t = fox.fox_qk_rmsnorm(qt[:, :, p].contiguous(), eps=eps)
+        o_t, _ = fox.fox_attn_decode(q_t, k_cache, v_cache, c_cache, lens, o_dtype=torch.float32)
+        got_o.append(o_t)
+        got_y.append(fox.fox_out_norm_gate(o_t, gt[:, :, p].contiguous(), eps=eps))
+    torch.cuda.synchronize()
+    assert host(lens).tolist() == [L] * B
+    # the oracle: the Pro forward over the whole sequence, rows T0 .. L - 1
+    kk = oracle.rms_norm(oracle.kv_shift(kc, oracle.shift_gate(x, w_k)), eps)
+    vv = oracle.kv_shift(vc, oracle.shift_gate(x, w_v))
+    O, _ = oracle.attn_fwd(oracle.rms_norm(q, eps), kk, vv, oracle.gate_logf(x, w_f, b_f),
+                           scale=default_scale(D))
+    Y = oracle.out_norm_gate(O, g, eps)
+    for n in range(N):
+        p = T0 + n
+        check(f"decoded O at position {p}", host(got_o[n]), O[:, :, p])
+        check_y(f"decoded y at position {p}", host(got_y[n]), Y[:, :, p], O[:, :, p], g[:, :, p],
+                eps, y_bf16=True)
+
+
 def test_decode_maximum_length(fox):
     """A 2^23-position cache at D = 128 (one sequence, one head: a 2^31-byte K or V cache),
     filled to T - 1, then the last position appended and decoded: the append writes k, v and c
