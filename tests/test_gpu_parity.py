@@ -924,6 +924,56 @@ def test_decode_append_after_prefill(fox):
     assert all(torch.equal(a, b) for a, b in zip(before, (kc, vc, c)))
 
 
+def test_pro_training_step_gradients(fox):
+    """The Pro block's attention training step as the benchmark runs it (gate, scan, QK-norm of q
+    and k, forward, the two backward steps, d log f, the QK-norm backward of q and k, the gate
+    backward from the forward's log f) against the oracle's functions chained the same way,
+    for the gradients of the raw inputs q, k, v, x, w_f and b_f. dq, dk, dv and d log f take
+    the attention bar. The gate's gradients are linear in d log f (dz = d log f (1 - f)), so their
+    bar is d log f's (2e-2) carried through that map element by element: dx[t, :] sums over
+    heads of (1 - f) |w_f|, dw_f over tokens of (1 - f) |x|, db_f over tokens of (1 - f)."""
+    B, H, L, D, dm, eps = 1, 4, 700, 128, 256, 1e-6
+    rng = np.random.default_rng(85)
+    bf = lambda *shape: fi.bf16_round(rng.standard_normal(shape, dtype=np.float32))
+    x, q, k, v, do = bf(B, L, dm), bf(B, H, L, D), bf(B, H, L, D), bf(B, H, L, D), bf(B, H, L, D)
+    w_f = (0.05 * rng.standard_normal((H, dm))).astype(np.float32)
+    b_f = rng.uniform(1.0, 6.0, H).astype(np.float32)
+    say("pro training step: gradients of the raw inputs")
+    xt, qt, kt, vt, dot = dev(x, "bf16"), dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+    wf, bfv = dev(w_f, "f32"), dev(b_f, "f32")
+    lf = fox.fox_gate_logf(xt, wf, bfv)
+    c = fox.fox_logf_cumsum(lf)
+    qn, kn = fox.fox_qk_rmsnorm(qt, eps=eps), fox.fox_qk_rmsnorm(kt, eps=eps)
+    o, lse = fox.fox_attn_fwd(qn, kn, vt, c, o_dtype=torch.float32)
+    dqn, dcq, delta, lse2 = fox.fox_attn_bwd_dq(qn, kn, vt, c, lse, dot, None, o=o)
+    dkn, dv, dck = fox.fox_attn_bwd_dkv(qn, kn, vt, c, lse2, dot, delta)
+    dlf = fox.fox_dlogf_from_dc(dcq, dck)
+    dq, _ = fox.fox_qk_rmsnorm_bwd(qt, dqn, eps=eps)
+    dk, _ = fox.fox_qk_rmsnorm_bwd(kt, dkn, eps=eps)
+    dx, dw, db = fox.fox_gate_logf_bwd(xt, wf, bfv, dlf, log_f=lf)
+    torch.cuda.synchronize()
+    LF = oracle.gate_logf(x, w_f, b_f)
+    # the step stores the normalised q and k in bf16, the attention's input type; the oracle's
+    # chain rounds its fp64 values at the same point (reading r27)
+    qh, kh = (fi.bf16_round(oracle.rms_norm(a, eps)) for a in (q, k))
+    dQn, dKn, dV, dLF = oracle.attn_bwd(qh, kh, v, LF, do, scale=default_scale(D))[:4]
+    check("d log f", host(dlf), dLF)
+    check("dq", host(dq), oracle.rms_norm_bwd(q, dQn, eps)[0])
+    check("dk", host(dk), oracle.rms_norm_bwd(k, dKn, eps)[0])
+    check("dv", host(dv), dV)
+    DX, DW, DB = oracle.gate_logf_bwd(x, w_f, b_f, dLF)
+    one_minus_f = -np.expm1(LF[0])  # [H, L]
+    bars = {"dx": BF16_MAXABS * (one_minus_f.T @ np.abs(w_f.astype(np.float64)))[None],
+            "dw_f": BF16_MAXABS * (one_minus_f @ np.abs(x[0].astype(np.float64))),
+            "db_f": BF16_MAXABS * one_minus_f.sum(axis=1)}
+    for name, got, ref in (("dx", dx, DX), ("dw_f", dw, DW), ("db_f", db, DB)):
+        err = np.abs(host(got) - ref)
+        worst = float(np.max(err / bars[name]))
+        say(f"  {name}: max-abs {float(err.max()):.3e}, at most {worst:.3f} of the carried bar")
+        assert worst <= 1.0, f"{name}: {worst:.2f} times the bar carried from d log f"
+        check(name, host(got), ref, maxabs=float("inf"))
+
+
 def test_pro_decode_steps_match_the_full_forward(fox):
     """Pro block decoding, built from the library's calls: a prefill of 300 positions through the
     sequence passes (shift gates, token shift with the key norm, forget gate, scan), then four
