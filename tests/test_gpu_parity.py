@@ -931,7 +931,9 @@ def test_pro_training_step_gradients(fox):
     for the gradients of the raw inputs q, k, v, x, w_f and b_f. dq, dk, dv and d log f take
     the attention bar. The gate's gradients are linear in d log f (dz = d log f (1 - f)), so their
     bar is d log f's (2e-2) carried through that map element by element: dx[t, :] sums over
-    heads of (1 - f) |w_f|, dw_f over tokens of (1 - f) |x|, db_f over tokens of (1 - f)."""
+    heads of (1 - f) |w_f|, dw_f over tokens of (1 - f) |x|, db_f over tokens of (1 - f).
+    dx and dw_f also take the 5e-3 relative L2; db_f does not (a random sweep found one head's
+    db_f of 0.48 from terms whose carried bar sums to 4.7: 9.5e-3 off, 2% of itself)."""
     B, H, L, D, dm, eps = 1, 4, 700, 128, 256, 1e-6
     rng = np.random.default_rng(85)
     bf = lambda *shape: fi.bf16_round(rng.standard_normal(shape, dtype=np.float32))
@@ -971,7 +973,8 @@ def test_pro_training_step_gradients(fox):
         worst = float(np.max(err / bars[name]))
         say(f"  {name}: max-abs {float(err.max()):.3e}, at most {worst:.3f} of the carried bar")
         assert worst <= 1.0, f"{name}: {worst:.2f} times the bar carried from d log f"
-        check(name, host(got), ref, maxabs=float("inf"))
+        if name != "db_f":  # db_f: H sums over every token, whose terms may cancel
+            check(name, host(got), ref, maxabs=float("inf"))
 
 
 def test_pro_decode_steps_match_the_full_forward(fox):
