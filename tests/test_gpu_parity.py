@@ -1515,28 +1515,44 @@ RISING_SCALE = 5.0
 RISING_RMS = 1e-2
 
 
+def _gate_kind_case(rng, B, H, L, D, gate, seed):
+    """A case of the named gate kind: plain, per-head and open gates by make_case's recipes;
+    strong decay (z ~ N(-2, 1.5^2)); hard resets (-300) or rising c (+12) over five positions at
+    three places drawn from rng, on long-memory gates (z ~ N(4, 1.5^2))."""
+    if gate == "strong":
+        return fi.make_case(B, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=-2.0,
+                            with_do=True)
+    if gate in ("reset", "rising"):
+        case = fi.make_case(B, H, L, D, "bf16", seed=seed, gate="normal", gate_mean=4.0,
+                            with_do=True)
+        for a in sorted(set(int(x) for x in rng.integers(0, L, size=3))):
+            case.log_f[..., a:a + 5] = -300.0 if gate == "reset" else 12.0
+        return case
+    return fi.make_case(B, H, L, D, "bf16", seed=seed, gate=gate, with_do=True)
+
+
+def _sweep_opts(rng):
+    """O in fp32 or bf16, c in fp32 or fp64, the scan fused or separate, tile skipping (fp32 c
+    only: a skip plan is built from fp32 c)."""
+    opts = dict(o_dtype=str(rng.choice(["f32", "bf16"])), c_dtype=str(rng.choice(["f32", "f64"])),
+                fused_scan=bool(rng.integers(0, 2)), skip=bool(rng.integers(0, 2)))
+    if opts["c_dtype"] == "f64":
+        opts["skip"] = False
+    return opts
+
+
+GATE_KINDS = ["normal", "per_head", "zero", "strong", "reset", "rising"]
+
+
 def _sweep_case(i):
     """Seeded random shape, gate and option mix (case i of the sweep)."""
     rng = np.random.default_rng(7000 + i)
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
     L = int(rng.choice([1, 2, 63, 64, 65, 255, 256, 257, 511, 700, 1023, 1500, 2100]))
     D = int(rng.choice([64, 128]))
-    gate = str(rng.choice(["normal", "per_head", "zero", "strong", "reset", "rising"]))
-    if gate == "strong":
-        case = fi.make_case(B, H, L, D, "bf16", seed=7100 + i, gate="normal", gate_mean=-2.0,
-                            with_do=True)
-    elif gate in ("reset", "rising"):
-        case = fi.make_case(B, H, L, D, "bf16", seed=7100 + i, gate="normal", gate_mean=4.0,
-                            with_do=True)
-        for a in sorted(set(int(x) for x in rng.integers(0, L, size=3))):
-            case.log_f[..., a:a + 5] = -300.0 if gate == "reset" else 12.0
-    else:
-        case = fi.make_case(B, H, L, D, "bf16", seed=7100 + i, gate=gate, with_do=True)
-    opts = dict(o_dtype=str(rng.choice(["f32", "bf16"])), c_dtype=str(rng.choice(["f32", "f64"])),
-                fused_scan=bool(rng.integers(0, 2)), skip=bool(rng.integers(0, 2)))
-    if opts["c_dtype"] == "f64":
-        opts["skip"] = False  # a skip plan is built from fp32 c
-    return case, gate, opts
+    gate = str(rng.choice(GATE_KINDS))
+    case = _gate_kind_case(rng, B, H, L, D, gate, 7100 + i)
+    return case, gate, _sweep_opts(rng)
 
 
 @pytest.mark.parametrize("i", range(24))
@@ -1564,22 +1580,9 @@ def _long_sweep_case(i):
     B, H = 1, int(rng.integers(1, 3))
     L = int(rng.choice([3000, 4096, 8191, 12288, 16384]))
     D = int(rng.choice([64, 128]))
-    gate = str(rng.choice(["normal", "per_head", "zero", "strong", "reset", "rising"]))
-    if gate == "strong":
-        case = fi.make_case(B, H, L, D, "bf16", seed=51000 + i, gate="normal", gate_mean=-2.0,
-                            with_do=True)
-    elif gate in ("reset", "rising"):
-        case = fi.make_case(B, H, L, D, "bf16", seed=51000 + i, gate="normal", gate_mean=4.0,
-                            with_do=True)
-        for a in sorted(set(int(x) for x in rng.integers(0, L, size=3))):
-            case.log_f[..., a:a + 5] = -300.0 if gate == "reset" else 12.0
-    else:
-        case = fi.make_case(B, H, L, D, "bf16", seed=51000 + i, gate=gate, with_do=True)
-    opts = dict(o_dtype=str(rng.choice(["f32", "bf16"])), c_dtype=str(rng.choice(["f32", "f64"])),
-                fused_scan=bool(rng.integers(0, 2)), skip=bool(rng.integers(0, 2)))
-    if opts["c_dtype"] == "f64":
-        opts["skip"] = False
-    return case, gate, opts
+    gate = str(rng.choice(GATE_KINDS))
+    case = _gate_kind_case(rng, B, H, L, D, gate, 51000 + i)
+    return case, gate, _sweep_opts(rng)
 
 
 @pytest.mark.parametrize("i", [1, 2, 7, 31, 32])
