@@ -1513,6 +1513,12 @@ def test_fwd_ex_shift_prologue_config4(fox):
 # 1.4-2.2e-3: RISING_RMS is five times that.
 RISING_SCALE = 5.0
 RISING_RMS = 1e-2
+# LSE is a logarithm, and its error is absolute: the forward's LSE is the log of the sum of the
+# bf16-rounded weights that built O, up to 2^-9 (about 2e-3) from the exact one, and a single
+# position's LSE is one fp32 dot product. A 5e-3 relative bar over the one or two values of a
+# sequence of length 1 or 2 can then fail near zero (LSE of 9e-6 off by 6e-8; of 0.16 off by
+# 1e-3), so the relative bar applies where the reference's RMS is at least 2e-3 / 5e-3 = 0.4.
+LSE_RMS = 0.4
 
 
 def _gate_kind_case(rng, B, H, L, D, gate, seed):
@@ -1564,13 +1570,13 @@ def test_random_sweep_against_oracle(fox, i):
     _run_sweep_case(fox, i)
 
 
-@pytest.mark.parametrize("i", [79, 337, 372, 1953, 10716, 11308])
+@pytest.mark.parametrize("i", [79, 337, 372, 1953, 10716, 11308, 33426, 36764])
 def test_sweep_cases_from_wider_search(fox, i):
-    """Seeds of the same generator that wider searches (18600 cases) flagged: 1953 (gates in
+    """Seeds of the same generator that wider searches (38600 cases) flagged: 1953 (gates in
     (0, 1), a row dominated by two keys, |dQ| = 5.7, where the bf16 rounding of dS alone moved dQ
-    by 1.6e-2 before the diagonal tiles took the remainder products), and five with rising c
-    (large dK, dV; one-hot rows at L = 2; a vanishing d log f; d log f of RMS 1e-3 summing terms
-    of RMS 0.14-0.55)."""
+    by 1.6e-2 before the diagonal tiles took the remainder products), five with rising c (large
+    dK, dV; one-hot rows at L = 2; a vanishing d log f; d log f of RMS 1e-3 summing terms of RMS
+    0.14-0.55), and two whose one or two LSE values lie near zero (L = 1 and 2; see LSE_RMS)."""
     _run_sweep_case(fox, i)
 
 
@@ -1611,16 +1617,20 @@ def _run_sweep_case(fox, i, gen=None):
     torch.cuda.synchronize()
     O, LSE = oracle.attn_fwd(case.q, case.k, case.v, case.log_f, scale=s)
 
-    def bars(ref):
+    def bars(ref, lse=False):
+        r = np.asarray(ref, np.float64)
+        if lse and float(np.sqrt(np.mean(r * r))) < LSE_RMS:
+            # reading r28: LSE's error is absolute; near zero only the max-abs bar holds it
+            return dict(maxabs=BF16_MAXABS if gate != "rising" else bars(ref)["maxabs"],
+                        rel_l2=None)
         # gates outside (0, 1) (rising c): see RISING_SCALE
         if gate != "rising":
             return dict(maxabs=BF16_MAXABS, rel_l2=BF16_RELL2)
-        r = np.asarray(ref, np.float64)
         return dict(maxabs=max(BF16_MAXABS, BF16_MAXABS / RISING_SCALE * float(np.max(np.abs(r)))),
                     rel_l2=BF16_RELL2 if float(np.sqrt(np.mean(r * r))) >= RISING_RMS else None)
 
     check(f"O ({opts['o_dtype']})", host(o), O, **bars(O))
-    check("LSE", host(lse), LSE, **bars(LSE))
+    check("LSE", host(lse), LSE, **bars(LSE, lse=True))
     ref = oracle.attn_bwd(case.q, case.k, case.v, case.log_f, case.do, scale=s)[:4]
     for name, a, r in zip(("dQ", "dK", "dV", "dlog f"), (host(t) for t in g), ref):
         check(f"{name} sweep {i}", a, r, **bars(r))
