@@ -1672,6 +1672,55 @@ def test_two_streams_run_concurrently(fox):
             assert all(torch.equal(a, b) for a, b in zip(outs[n], serial[n])), (rep, n)
 
 
+def test_graph_capture_decode_loop(fox):
+    """A serving loop's step captured once in a HIP graph: append the new token (k, v, log f from
+    fixed input buffers) to the cache, then decode (q from a fixed buffer). Each replay, after
+    the next token is copied into the input buffers, must give the bits of the same step run
+    eagerly on a second copy of the cache; lens advances on the device at every replay."""
+    B, H, T, D, T0, N = 2, 3, 700, 128, 400, 6
+    case, _ = _decode_case(B, H, T, D, seed=7500)
+    qs = fi.bf16_round(np.random.default_rng(7501).standard_normal((N, B, H, D), dtype=np.float32))
+    kc, vc = dev(case.k, "bf16"), dev(case.v, "bf16")
+    kc[:, :, T0:].zero_()
+    vc[:, :, T0:].zero_()
+    c = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    c[:, :, :T0] = fox.fox_logf_cumsum(dev(np.ascontiguousarray(case.log_f[:, :, :T0]), "f32"))
+    lens = torch.full((B,), T0, dtype=torch.int32, device="cuda")
+    kn = fox.fox_attn_decode_key_norms(kc, lens)
+    ref = [t.clone() for t in (kc, vc, c, lens, kn)]  # the eager loop's own cache
+    tok = lambda a, p: dev(np.ascontiguousarray(a[:, :, p]), "bf16" if a.ndim == 4 else "f32")
+    k_in, v_in, lf_in, q_in = tok(case.k, T0), tok(case.v, T0), tok(case.log_f, T0), dev(qs[0], "bf16")
+
+    def step(kk, vv, cc, ll, nn):
+        fox.fox_attn_decode_append(k_in, v_in, lf_in, kk, vv, cc, ll, k_norms=nn)
+        return fox.fox_attn_decode(q_in, kk, vv, cc, ll, o_dtype=torch.float32, k_norms=nn)
+
+    side = torch.cuda.Stream()  # warm-up on a throwaway copy of the cache, on a side stream
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(*[t.clone() for t in (kc, vc, c, lens, kn)])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        o_g, lse_g = step(kc, vc, c, lens, kn)
+    # capture records the step without running it: the cache is still at T0
+    torch.cuda.synchronize()
+    assert host(lens).tolist() == [T0] * B
+    for n in range(N):
+        p = T0 + n
+        k_in.copy_(tok(case.k, p)); v_in.copy_(tok(case.v, p)); lf_in.copy_(tok(case.log_f, p))
+        q_in.copy_(dev(qs[n], "bf16"))
+        graph.replay()
+        o_e, lse_e = step(*ref)
+        torch.cuda.synchronize()
+        assert host(lens).tolist() == [p + 1] * B
+        assert torch.equal(o_g, o_e) and torch.equal(lse_g, lse_e), f"replay {n} differs"
+        assert all(torch.equal(a, b) for a, b in zip((kc, vc, c, lens, kn), ref)), f"cache {n}"
+    O, LSE = _decode_ref(qs[N - 1], case.k, case.v, case.log_f, np.full(B, T0 + N), default_scale(D))
+    _check_decode("decode O after the replays", host(o_g), O, case.log_f[:, :, :T0 + N])
+
+
 def test_graph_capture_replays_match_eager(fox):
     """Forward and backward captured in a HIP graph (through torch.cuda.graph): every replay,
     with eager work and synchronisations between replays, gives the eager bits."""
