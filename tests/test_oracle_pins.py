@@ -85,6 +85,11 @@ def test_rows_match_full_forward():
     rows = np.array([0, 1, 63, 64, 200, 299])
     Or, Lr = oracle.attn_fwd_rows(c.q[0, 0], c.k[0, 0], c.v[0, 0], cc[0, 0], rows, scale=s)
     assert np.abs(Or - O[0, 0, rows]).max() < 1e-12 and np.abs(Lr - LSE[0, 0, rows]).max() < 1e-12
+    # and against torch's attention with the explicit bias c_i - c_j, independently of attn_fwd
+    bias = cc[0, 0][:, None] - cc[0, 0][None, :]
+    ref = _sdpa_causal(c.q[:, :1], c.k[:, :1], c.v[:, :1], s, bias)[0, 0, rows]
+    assert np.abs(Or - ref).max() < 1e-12
+    assert np.abs(Lr - _lse_ref(c.q[:, :1], c.k[:, :1], s, bias)[0, 0, rows]).max() < 1e-12
 
 
 # ---------------------------------------------------------------- closed forms and library routines
