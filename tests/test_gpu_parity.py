@@ -1593,7 +1593,7 @@ def _long_sweep_case(i):
 
 @pytest.mark.parametrize("i", [1, 2, 7, 31, 32])
 def test_long_sequence_sweep_cases(fox, i):
-    """Cases of the long-sequence generator (200 of which pass in a one-off run), each with its
+    """Cases of the long-sequence generator (520 of which pass in a one-off run), each with its
     drawn options, against the oracle at every element: rising c at L = 16384, D = 64 (fp64 c,
     the scan fused); open gates at 16384; strong decay at 16384 (fp32 c); hard resets at 12288
     and rising c at 12288, both with fp32 c and tile skipping."""
